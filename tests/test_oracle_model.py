@@ -1,0 +1,228 @@
+"""Whole-step pins of the fp64 oracle and determinism pins of the generator.
+
+* special case: with W_o = W_down = 0 the residual stream stays E[tok], so
+  logits = W_lm * rmsnorm(E[tok]) * g_out in closed form;
+* composition: the oracle's step against Hugging Face transformers'
+  LlamaForCausalLM run in fp64 on the same dequantised weights and the same
+  prefilled cache (an independent implementation of the architecture; its
+  rotate-half RoPE is matched by the standard per-head row permutation of
+  W_q / W_k, and it keeps the new token's k/v in fp64 where the oracle rounds
+  them to fp16, hence the 1e-4 relative bound instead of exact agreement);
+* generator: Philox4x32-10 known-answer vectors and identical bytes for any
+  thread count.
+"""
+import hashlib
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth import Q4_0, Q8_0
+from tests.test_oracle_pins import _numpy_dequant
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _load_oracle(model, n_seq=1, ctx=None):
+    cfg = model.cfg
+    om = oracle.OracleModel(model, max_seqs=n_seq)
+    for s in range(n_seq):
+        for l in range(cfg.n_layers):
+            k, v = synth.make_kv(cfg, s, l, ctx)
+            om.load_kv(s, l, k, v)
+    return om
+
+
+def test_zero_wo_wdown_closed_form():
+    cfg = synth.variant("tiny", qtype=Q8_0)
+    model = synth.make_model(cfg)
+    for w in model.layers:
+        w.wo[:] = 0
+        w.w_down[:] = 0
+    om = _load_oracle(model)
+    tok = int(synth.start_tokens(cfg)[0])
+    logits, am = om.step([tok])
+    e = model.tok_embd[tok].view(np.float16).astype(np.float64)
+    xf = torch.nn.functional.rms_norm(torch.from_numpy(e), (cfg.hidden,),
+                                      weight=torch.from_numpy(model.out_norm.astype(np.float64)),
+                                      eps=cfg.rms_eps).numpy()
+    W = _numpy_dequant(cfg.qtype, model.lm_head, cfg.vocab, cfg.hidden)
+    expect = W @ xf
+    assert np.allclose(logits[0], expect, rtol=1e-12, atol=1e-14)
+    assert am[0] == int(np.argmax(expect.astype(np.float32)))
+
+
+def _hf_model(model):
+    from transformers import LlamaConfig, LlamaForCausalLM
+    cfg = model.cfg
+    hc = LlamaConfig(vocab_size=cfg.vocab, hidden_size=cfg.hidden, intermediate_size=cfg.ffn,
+                     num_hidden_layers=cfg.n_layers, num_attention_heads=cfg.n_heads,
+                     num_key_value_heads=cfg.n_kv_heads, head_dim=cfg.head_dim,
+                     rms_norm_eps=cfg.rms_eps, rope_theta=cfg.rope_theta,
+                     tie_word_embeddings=False, attention_bias=False, mlp_bias=False,
+                     max_position_embeddings=8192)
+    hc._attn_implementation = "eager"
+    hf = LlamaForCausalLM(hc).double().eval()
+    hd = cfg.head_dim
+    # adjacent pairs (2i, 2i+1) <-> rotate-half pairs (i, i + hd/2)
+    perm = np.concatenate([np.arange(0, hd, 2), np.arange(1, hd, 2)])
+
+    def rows_perm(W, n_heads):
+        return W.reshape(n_heads, hd, -1)[:, perm, :].reshape(n_heads * hd, -1)
+
+    def T(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))
+
+    H, F = cfg.hidden, cfg.ffn
+    qt = cfg.qtype
+    with torch.no_grad():
+        hf.model.embed_tokens.weight.copy_(T(model.tok_embd.view(np.float16)))
+        hf.model.norm.weight.copy_(T(model.out_norm))
+        hf.lm_head.weight.copy_(T(_numpy_dequant(qt, model.lm_head, cfg.vocab, H)))
+        for l, w in enumerate(model.layers):
+            L = hf.model.layers[l]
+            L.input_layernorm.weight.copy_(T(w.attn_norm))
+            L.post_attention_layernorm.weight.copy_(T(w.ffn_norm))
+            L.self_attn.q_proj.weight.copy_(T(rows_perm(_numpy_dequant(qt, w.wq, cfg.n_heads * hd, H), cfg.n_heads)))
+            L.self_attn.k_proj.weight.copy_(T(rows_perm(_numpy_dequant(qt, w.wk, cfg.n_kv_heads * hd, H), cfg.n_kv_heads)))
+            L.self_attn.v_proj.weight.copy_(T(_numpy_dequant(qt, w.wv, cfg.n_kv_heads * hd, H)))
+            L.self_attn.o_proj.weight.copy_(T(_numpy_dequant(qt, w.wo, H, cfg.n_heads * hd)))
+            L.mlp.gate_proj.weight.copy_(T(_numpy_dequant(qt, w.w_gate, F, H)))
+            L.mlp.up_proj.weight.copy_(T(_numpy_dequant(qt, w.w_up, F, H)))
+            L.mlp.down_proj.weight.copy_(T(_numpy_dequant(qt, w.w_down, H, F)))
+    return hf, perm, hc
+
+
+@pytest.mark.parametrize("name,qtype", [("tiny", Q8_0), ("tiny", Q4_0)])
+def test_oracle_matches_transformers_llama(name, qtype):
+    from transformers.cache_utils import DynamicCache
+    cfg = synth.variant(name, qtype=qtype)
+    model = synth.make_model(cfg)
+    om = _load_oracle(model)
+    hf, perm, hc = _hf_model(model)
+    cache = DynamicCache(config=hc)
+    for l in range(cfg.n_layers):
+        k, v = synth.make_kv(cfg, 0, l)
+        kf = k.view(np.float16).astype(np.float64)[:, :, perm]
+        vf = v.view(np.float16).astype(np.float64)
+        cache.update(torch.from_numpy(kf[None].copy()), torch.from_numpy(vf[None].copy()), l)
+    tok = int(synth.start_tokens(cfg)[0])
+    for step in range(cfg.steps):
+        p = cfg.ctx + step
+        logits, am = om.step([tok])
+        with torch.no_grad():
+            out = hf(input_ids=torch.tensor([[tok]]), position_ids=torch.tensor([[p]]),
+                     cache_position=torch.tensor([p]), past_key_values=cache, use_cache=True)
+        ref = out.logits[0, -1].numpy()
+        err = np.max(np.abs(logits[0] - ref))
+        assert err <= 1e-4 * np.max(np.abs(ref)), (step, err)
+        # the token the oracle appended at p equals the library's k (fp16-rounded, <= 1 ulp)
+        for l in range(cfg.n_layers):
+            ko, vo = om.get_kv(0, l, p + 1)
+            kh = cache.layers[l].keys[0, :, p, :].numpy()[:, np.argsort(perm)]
+            vh = cache.layers[l].values[0, :, p, :].numpy()
+            for got, want in ((ko[:, p], kh), (vo[:, p], vh)):
+                g = got.view(np.float16).astype(np.float64)
+                if l == 0:
+                    # same inputs on both sides: fp16 rounding is the only difference
+                    ulp = np.abs(np.spacing(want.astype(np.float16)).astype(np.float64))
+                    assert np.all(np.abs(g - want) <= ulp), (step, l)
+                else:
+                    # deeper layers also carry layer 0's fp16-vs-fp64 new-token difference
+                    assert np.max(np.abs(g - want)) <= 2e-3 * np.max(np.abs(want)), (step, l)
+        tok = int(am[0])
+
+
+def test_oracle_positions_and_context_limit():
+    cfg = synth.variant("tiny", steps=2)
+    model = synth.make_model(cfg)
+    om = _load_oracle(model)
+    assert om.position(0) == cfg.ctx
+    om.step([1])
+    om.step([2])
+    assert om.position(0) == cfg.ctx + 2
+    with pytest.raises(ValueError):
+        om.step([3])                      # max_ctx = ctx + steps reached
+    om.set_position(0, cfg.ctx)
+    om.step([1])
+
+
+def test_oracle_step_is_repeatable_after_rewind():
+    cfg = synth.CONFIGS["tiny"]
+    model = synth.make_model(cfg)
+    om = _load_oracle(model)
+    a, _ = om.step([7])
+    om.set_position(0, cfg.ctx)
+    b, _ = om.step([7])
+    assert np.array_equal(a, b)
+
+
+def test_batch_sequences_are_independent():
+    cfg = synth.variant("tiny", batch=2)
+    model = synth.make_model(cfg)
+    om2 = _load_oracle(model, n_seq=2)
+    lg2, am2 = om2.step([11, 300])
+    for s, t in ((0, 11), (1, 300)):
+        om1 = oracle.OracleModel(model, max_seqs=1)
+        for l in range(cfg.n_layers):
+            k, v = synth.make_kv(cfg, s, l)
+            om1.load_kv(0, l, k, v)
+        lg1, am1 = om1.step([t])
+        assert np.array_equal(lg1[0], lg2[s]) and am1[0] == am2[s]
+
+
+# ---------------------------------------------------------------------------
+# generator
+# ---------------------------------------------------------------------------
+
+def test_philox_known_answer_vectors():
+    # known-answer vectors published with Philox4x32-10 (Salmon et al., SC'11)
+    kat = [
+        ([0, 0, 0, 0], [0, 0], [0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8]),
+        ([0xFFFFFFFF] * 4, [0xFFFFFFFF] * 2, [0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD]),
+        ([0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344], [0xA4093822, 0x299F31D0],
+         [0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1]),
+    ]
+    for ctr, key, out in kat:
+        assert list(synth.philox4x32_10(ctr, key)) == out
+
+
+_DIGEST_SNIPPET = r"""
+import hashlib, sys
+sys.path.insert(0, {root!r})
+import synth
+h = hashlib.sha256()
+h.update(synth.quant_matrix(1, 77, 96, 512, 0.02, 8).tobytes())
+h.update(synth.quant_matrix(1, 78, 40, 256, 0.02, 2).tobytes())
+h.update(synth.normal_f16_bits(1, 79, 10001, 0.0, 1.0).tobytes())
+h.update(synth.normal_f32(1, 80, 999, 1.0, 0.1).tobytes())
+print(h.hexdigest())
+"""
+
+
+def test_generator_bytes_independent_of_thread_count():
+    code = _DIGEST_SNIPPET.format(root=ROOT)
+    digests = []
+    for n in ("1", "3", "8"):
+        env = dict(os.environ, OMP_NUM_THREADS=n)
+        digests.append(subprocess.check_output([sys.executable, "-c", code], env=env).strip())
+    assert len(set(digests)) == 1
+
+
+def test_generator_distributions():
+    w = synth.normal_f32(9, 1, 200000, 0.0, 1.0).astype(np.float64)
+    assert abs(w.mean()) < 0.01 and abs(w.std() - 1.0) < 0.01
+    g = synth.normal_f32(9, 2, 100000, 1.0, 0.1).astype(np.float64)
+    assert abs(g.mean() - 1.0) < 0.002 and abs(g.std() - 0.1) < 0.002
+    t = synth.uniform_int(9, 3, 50000, 512)
+    assert t.min() >= 0 and t.max() < 512 and abs(t.mean() - 255.5) < 5
+    cfg = synth.CONFIGS["tiny"]
+    blocks = synth.quant_matrix(0, 5, 64, 256, 0.02, Q8_0)
+    W = _numpy_dequant(Q8_0, blocks, 64, 256)
+    assert abs(W.std() - 0.02) < 0.001
+    assert cfg.max_ctx == 20
