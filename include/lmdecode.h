@@ -1,0 +1,208 @@
+/*
+ * lmdecode.h - C ABI of the MI355X (gfx950) batch-1 decode step of a
+ * Llama-architecture transformer with block-quantised weights.
+ *
+ * What one decode step computes (per sequence s, token t at position p):
+ *   x = E[t]                                   fp16 embedding row -> fp32
+ *   for each layer:
+ *     xn = x / sqrt(mean(x^2) + eps) * g_attn  RMSNorm
+ *     q, k, v = W_q xn, W_k xn, W_v xn         dequant-GEMV over Q8_0/Q4_0 blocks
+ *     rotate q, k by RoPE at p; K[p] = fp16(k), V[p] = fp16(v)
+ *     o_h = softmax_t(q_h . K[g][t] / sqrt(hd)) V[g][t], t = 0..p, g = h / (nq/nkv)
+ *     x += W_o o
+ *     xn = RMSNorm(x) * g_ffn;  x += W_down (silu(W_gate xn) * (W_up xn))
+ *   logits = W_lm (RMSNorm(x) * g_out);  next token = argmax (lowest index on ties)
+ * Sources: the C/CUDA Llama engine page (rskf.cn/news/15116) lists the Llama
+ * features and the Q8_0/Q4_0 formats in section 1 and the operators in
+ * section 4.4 (GEMV for single-token products, fused RMSNorm, RoPE from a
+ * precomputed sin/cos table, SwiGLU fused with the FC product, causal-masked
+ * softmax); the SwarmKV page ("Prefill once, fan out", ideipro.ru) gives the
+ * KV size in section 3 and positions that continue after the prefix in
+ * section 4; the weight-streaming mode follows the double-buffered pipeline
+ * of the same engine page (sections 2.3, 3.3, 4.2) and the pinned-host /
+ * two-stream / ping-pong-buffer design of "3 Agents. 3 LLMs. 1 Aging GPU"
+ * (section on loading only the layers you need).
+ *
+ * Conventions for every call:
+ *   - Host pointers passed in are read during the call only; the library
+ *     copies what it keeps.  Device pointers (the *_dev call) stay owned by
+ *     the caller.
+ *   - The library owns all device memory (weights, KV cache, scratch, the two
+ *     streaming buffers) and the pinned host arena of streaming mode.
+ *   - No C++ exception crosses this boundary.  Every call returns a status;
+ *     lm_last_error() returns a message with the numbers involved.
+ *   - All-or-nothing: a failed call leaves the model as it was, and a failed
+ *     lm_model_create leaks nothing.
+ *   - A model is not thread-safe: the caller serialises calls on one model.
+ *     Different models (on different streams) are independent.
+ */
+#ifndef LMDECODE_H
+#define LMDECODE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct lm_model lm_model;
+
+typedef enum {
+    LM_OK = 0,
+    LM_E_ARG = 1,    /* invalid argument (shape, index, null pointer, size) */
+    LM_E_STATE = 2,  /* call not legal in the model's current state */
+    LM_E_OOM = 3,    /* device or pinned-host allocation failed */
+    LM_E_HIP = 4,    /* a HIP runtime call failed (message names it) */
+    LM_E_CTX = 5     /* the step would run past max_ctx */
+} lm_status;
+
+/* GGUF type ids of the two block formats.
+ * Q8_0: 34-byte block = fp16 d (little endian) + 32 int8 q; w = d * q.
+ * Q4_0: 18-byte block = fp16 d + 16 bytes; byte j holds element j in its low
+ *       nibble and element j+16 in its high nibble; w = (nibble - 8) * d. */
+typedef enum { LM_Q4_0 = 2, LM_Q8_0 = 8 } lm_qtype;
+
+typedef struct {
+    int32_t vocab;       /* rows of the LM head, rows of the embedding table */
+    int32_t hidden;      /* H, a multiple of 32 */
+    int32_t n_layers;
+    int32_t n_heads;     /* query heads nq */
+    int32_t n_kv_heads;  /* KV heads nkv; nq % nkv == 0 */
+    int32_t head_dim;    /* hd: even, 32 <= hd <= 256, nq*hd a multiple of 32 */
+    int32_t ffn;         /* F, a multiple of 32 */
+    double rms_eps;      /* RMSNorm epsilon (inside the square root) */
+    double rope_theta;   /* RoPE base: pair i turns by p * theta^(-2i/hd) */
+    int32_t max_ctx;     /* KV positions per sequence */
+    int32_t max_seqs;    /* sequences decoded together (1..4) */
+    int32_t qtype;       /* LM_Q8_0 or LM_Q4_0, for every weight matrix */
+} lm_config;
+
+/* One decoder layer's weights.  Norm gains: fp32 [hidden].  Matrices: GGUF
+ * block bytes, row-major [out rows][in/32 blocks]:
+ *   wq [nq*hd][H], wk [nkv*hd][H], wv [nkv*hd][H], wo [H][nq*hd],
+ *   w_gate [F][H], w_up [F][H], w_down [H][F]. */
+typedef struct {
+    const float* attn_norm;
+    const float* ffn_norm;
+    const void* wq;
+    const void* wk;
+    const void* wv;
+    const void* wo;
+    const void* w_gate;
+    const void* w_up;
+    const void* w_down;
+} lm_layer_weights;
+
+/* Validates cfg, then allocates every device buffer the model needs (KV
+ * cache for max_seqs x max_ctx, weights, scratch).  hip_stream: a hipStream_t
+ * the model launches on (borrowed, never destroyed), or NULL for a stream the
+ * library creates.  On failure *out is NULL and nothing is left allocated.
+ * Errors: LM_E_ARG (bad config, with the offending field), LM_E_OOM, LM_E_HIP. */
+lm_status lm_model_create(const lm_config* cfg, void* hip_stream, lm_model** out);
+
+/* Waits for the model's work, then frees everything it owns.  NULL is a no-op. */
+void lm_model_destroy(lm_model* m);
+
+/* Copies one layer's weights (host memory) into the model, repacking the
+ * blocks into the library's device layout.  Byte counts follow from the
+ * config.  Errors: LM_E_ARG (layer out of range, NULL pointer), LM_E_HIP. */
+lm_status lm_load_layer_weights(lm_model* m, int32_t layer, const lm_layer_weights* w);
+
+/* Embedding table fp16 bits [vocab][hidden], output norm gain fp32 [hidden],
+ * LM head GGUF blocks [vocab][hidden/32].  The model is ready to decode once
+ * this and every layer are loaded. */
+lm_status lm_load_global_weights(lm_model* m, const uint16_t* tok_embd_f16,
+                                 const float* out_norm, const void* lm_head_blocks);
+
+/* Installs n_pos cached (already rotated) keys and values of one (sequence,
+ * layer): fp16 bits [n_kv][n_pos][head_dim] each.  Sets the sequence's next
+ * position to n_pos (its next decode step runs at position n_pos, 0-based).
+ * Errors: LM_E_ARG (index or n_pos > max_ctx), LM_E_HIP. */
+lm_status lm_load_kv(lm_model* m, int32_t seq, int32_t layer, const uint16_t* k,
+                     const uint16_t* v, int32_t n_pos);
+
+/* Copies cached rows 0..n_pos-1 of one (sequence, layer) out, same layout. */
+lm_status lm_get_kv(lm_model* m, int32_t seq, int32_t layer, uint16_t* k, uint16_t* v,
+                    int32_t n_pos);
+
+/* Rewinds (or advances) a sequence: its next step runs at position pos and
+ * overwrites cache rows >= pos. 0 <= pos <= max_ctx. */
+lm_status lm_set_position(lm_model* m, int32_t seq, int32_t pos);
+lm_status lm_get_position(const lm_model* m, int32_t seq, int32_t* pos);
+
+/* Weight residency.  enable = 1: the decoder layers' weights move to a pinned
+ * host arena and each step copies layer l+1 into one of two HBM layer buffers
+ * on a copy stream while layer l computes from the other (events order both
+ * the copy->compute and the compute->overwrite edges).  enable = 0: weights
+ * move back to HBM.  Embedding, norms, LM head and KV stay in HBM either way.
+ * Legal only between steps.  Outputs are bit-identical in both modes.
+ * Errors: LM_E_OOM (pinned or device memory), LM_E_HIP. */
+lm_status lm_stream_mode(lm_model* m, int32_t enable);
+
+/* One decode step for sequences 0..n_seq-1 (1 <= n_seq <= max_seqs):
+ * tokens host int32 [n_seq]; logits host fp32 [n_seq][vocab] or NULL;
+ * argmax host int32 [n_seq].  Blocks until the results are on the host.
+ * Every sequence advances by one position.
+ * Errors: LM_E_STATE (weights not all loaded), LM_E_ARG (token out of range,
+ * n_seq out of range), LM_E_CTX (a sequence at max_ctx; checked before any
+ * device work), LM_E_HIP. */
+lm_status lm_decode_step(lm_model* m, const int32_t* tokens, int32_t n_seq, float* logits,
+                         int32_t* argmax);
+
+/* The same step on device buffers, asynchronous on the model's stream:
+ * d_tokens int32 [n_seq], d_logits fp32 [n_seq][vocab] or NULL, d_argmax int32
+ * [n_seq].  Token ids are not range-checked on the host (the kernel clamps an
+ * out-of-range id to 0).  d_argmax may equal d_tokens to feed the greedy loop
+ * on the device. */
+lm_status lm_decode_step_dev(lm_model* m, const int32_t* d_tokens, int32_t n_seq,
+                             float* d_logits, int32_t* d_argmax);
+
+/* 1 (default): replay each step from a captured HIP graph; 0: launch eagerly. */
+lm_status lm_set_graph(lm_model* m, int32_t enable);
+
+/* The hipStream_t the model launches on. */
+void* lm_stream(const lm_model* m);
+
+/* Last error message of this model, or of the calling thread's last failed
+ * lm_model_create when m is NULL.  Never NULL; "" when there is none. */
+const char* lm_last_error(const lm_model* m);
+
+/* ---- measurement and inspection ---------------------------------------- */
+
+/* Kernel families of one step (for timing and profiling). */
+typedef enum {
+    LM_K_EMBED = 0, LM_K_QKV = 1, LM_K_ATTN = 2, LM_K_WO = 3, LM_K_GATEUP = 4,
+    LM_K_DOWN = 5, LM_K_LMHEAD = 6, LM_K_COUNT = 7
+} lm_kernel_kind;
+
+/* enable = 1: eager steps record HIP events around every kernel of every
+ * kind on the model's stream and accumulate their durations; graph replay is
+ * suspended while timing is on.  Resets the totals. */
+lm_status lm_kernel_timing(lm_model* m, int32_t enable);
+
+/* Launch count and summed duration (ms) of one kernel kind since timing was
+ * enabled (events are read after the step's final synchronisation). */
+lm_status lm_kernel_stats(lm_model* m, int32_t kind, int64_t* count, double* total_ms);
+
+/* Algorithmic bytes one launch of `kind` moves (weights + activations + KV,
+ * at the sequences' current positions for attention), summed over the
+ * launches of one step. */
+lm_status lm_kernel_bytes(const lm_model* m, int32_t kind, int32_t n_seq, double* bytes);
+
+/* Dequantises rows [row0, row0 + n_rows) of one loaded matrix with a GPU
+ * kernel that reads the library's device layout, into host fp32 [n_rows][cols].
+ * which: 0 wq, 1 wk, 2 wv, 3 wo, 4 w_gate, 5 w_up, 6 w_down (layer >= 0) or
+ * 7 the LM head (layer ignored).  Values are exact (d * q fits fp32). */
+lm_status lm_debug_dequant(lm_model* m, int32_t layer, int32_t which, int32_t row0,
+                           int32_t n_rows, float* out);
+
+/* A plain read-only kernel over n_bytes of device memory (sum of 16-byte
+ * words), for calibrating HBM counters and the read ceiling; *ms = average
+ * duration over iters launches. */
+lm_status lm_debug_read_bw(lm_model* m, int64_t n_bytes, int32_t iters, double* ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LMDECODE_H */

@@ -1,0 +1,69 @@
+"""The C-ABI library loads, exports every symbol its header declares, and
+rejects bad configurations before touching the GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import token_decode_llama_amd as lm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lmdecode.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lm_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declarations_match_binding_list():
+    assert _declared_functions() == sorted(lm.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = lm.load()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+def _good():
+    return dict(vocab=512, hidden=256, n_layers=2, n_heads=4, n_kv_heads=2, head_dim=64,
+                ffn=704, rms_eps=1e-5, rope_theta=5e5, max_ctx=20, max_seqs=1, qtype=8)
+
+
+@pytest.mark.parametrize("field,value,needle", [
+    ("qtype", 3, "qtype"),
+    ("vocab", 511, "vocab"),
+    ("hidden", 100, "hidden"),
+    ("n_layers", 0, "n_layers"),
+    ("n_kv_heads", 3, "n_kv_heads"),
+    ("head_dim", 96, "head_dim"),
+    ("ffn", 30, "ffn"),
+    ("max_ctx", 0, "max_ctx"),
+    ("max_seqs", 5, "max_seqs"),
+    ("rope_theta", 0.0, "rope_theta"),
+    ("rms_eps", float("nan"), "rms_eps"),
+    ("ffn", 64 * 1024, "LDS"),
+])
+def test_create_rejects_bad_config_before_any_device_call(field, value, needle):
+    L = lm.load()
+    d = _good()
+    d[field] = value
+    c = lm.Config(**d)
+    h = ctypes.c_void_p(123)
+    st = L.lm_model_create(ctypes.byref(c), None, ctypes.byref(h))
+    assert st == lm.LM_E_ARG
+    assert not h.value
+    msg = L.lm_last_error(None).decode()
+    assert needle in msg and "expected" in msg
+
+
+def test_null_arguments():
+    L = lm.load()
+    assert L.lm_model_create(None, None, None) == lm.LM_E_ARG
+    h = ctypes.c_void_p()
+    assert L.lm_model_create(None, None, ctypes.byref(h)) == lm.LM_E_ARG
+    L.lm_model_destroy(None)   # no-op
+    assert L.lm_last_error(None) is not None

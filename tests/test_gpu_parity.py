@@ -1,0 +1,231 @@
+"""GPU parity: the HIP decode step (through the C ABI) against the fp64 oracle
+on identical seeded inputs.
+
+Bars: dequantised weights bit-exact; argmax identical; per step and
+sequence max|d logit| <= 1e-3 * max|logit|; appended fp16 K/V within one
+fp16 ulp plus 2e-5 * max|K or V row| (the GPU rounds an fp32 value carrying
+the fp32 GEMV's absolute error, the oracle an fp64 one).
+Steps are teacher-forced with the oracle's token so one near-tie cannot
+cascade; a mismatch reports the oracle's top-2 gap.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth import Q4_0, Q8_0
+from tests.helpers import compare_step, f16_close, log, open_gpu, open_oracle
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "tiny_q8": synth.CONFIGS["tiny"],
+    "tiny_q4": synth.variant("tiny", qtype=Q4_0),
+    # the multi-model shapes: ragged block counts (28, 30 blocks/row), GQA groups 7 and 3
+    "qwen05b_2layers": synth.variant("multi_qwen05b", n_layers=2, ctx=130, steps=3),
+    "smol360m_2layers": synth.variant("multi_smol360m", n_layers=2, ctx=70, steps=3),
+    "llama1b_2layers": synth.variant("multi_llama1b", n_layers=2, ctx=64, steps=3),
+    # 8B layer shapes in Q4_0 with a long context (65 attention chunks)
+    "llama8b_q4_2layers_ctx4k": synth.variant("llama8b_q8", n_layers=2, qtype=Q4_0, ctx=4090,
+                                              steps=3, batch=1),
+}
+
+_models = {}
+
+
+def get_model(name):
+    if name not in _models:
+        log("generate", name)
+        _models[name] = synth.make_model(CASES[name])
+    return _models[name]
+
+
+def run_parity(model, n_seq, steps=None):
+    cfg = model.cfg
+    steps = steps or cfg.steps
+    g = open_gpu(model, max_seqs=n_seq)
+    om = open_oracle(model, n_seq)
+    toks = synth.start_tokens(cfg, n_seq)
+    worst = 0.0
+    try:
+        for st in range(steps):
+            p = cfg.ctx + st
+            log(f"{cfg.name}: step {st} pos {p} n_seq {n_seq}")
+            lg_o, am_o = om.step(toks)
+            lg_g, am_g = g.step(toks)
+            worst = max(worst, compare_step(lg_g, am_g, lg_o, am_o, f"{cfg.name} step {st}"))
+            for s in range(n_seq):
+                for l in range(cfg.n_layers):
+                    kg, vg = g.get_kv(s, l, p + 1)
+                    ko, vo = om.get_kv(s, l, p + 1)
+                    c0 = cfg.ctx
+                    assert np.array_equal(kg[:, :c0], ko[:, :c0]), "prefilled K rows changed"
+                    assert np.array_equal(vg[:, :c0], vo[:, :c0]), "prefilled V rows changed"
+                    # rows appended by this and earlier steps: fp16 of fp32 vs of fp64
+                    assert f16_close(kg[:, c0:p + 1], ko[:, c0:p + 1]), (s, l, "K append")
+                    assert f16_close(vg[:, c0:p + 1], vo[:, c0:p + 1]), (s, l, "V append")
+            toks = am_o
+            assert g.position(0) == p + 1
+    finally:
+        g.close()
+        om.close()
+    log(f"{cfg.name}: worst max|dlogit|/max|logit| = {worst:.3e}")
+    return worst
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_decode_parity(name):
+    run_parity(get_model(name), n_seq=1)
+
+
+@pytest.mark.parametrize("name,n_seq", [("tiny_q8", 3), ("tiny_q4", 4)])
+def test_decode_parity_batch(name, n_seq):
+    cfg = synth.variant(CASES[name].name, qtype=CASES[name].qtype, batch=n_seq)
+    run_parity(synth.make_model(cfg), n_seq=n_seq)
+
+
+def _bb(qt):
+    return synth.BLOCK_BYTES[qt]
+
+
+@pytest.mark.parametrize("name", ["tiny_q8", "tiny_q4", "qwen05b_2layers"])
+def test_dequant_bit_exact_all_rows(name):
+    model = get_model(name)
+    cfg = model.cfg
+    g = open_gpu(model, max_seqs=1)
+    try:
+        H, F, Q, KV = cfg.hidden, cfg.ffn, cfg.n_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
+        for l, w in enumerate(model.layers):
+            for which, (arr, rows, cols) in enumerate([(w.wq, Q, H), (w.wk, KV, H), (w.wv, KV, H),
+                                                       (w.wo, H, Q), (w.w_gate, F, H),
+                                                       (w.w_up, F, H), (w.w_down, H, F)]):
+                got = g.debug_dequant(l, which, 0, rows, cols)
+                ref = oracle.dequant(cfg.qtype, arr, rows, cols)
+                assert np.array_equal(got.astype(np.float64), ref), (l, which)
+        got = g.debug_dequant(0, 7, 0, cfg.vocab, H)
+        assert np.array_equal(got.astype(np.float64), oracle.dequant(cfg.qtype, model.lm_head, cfg.vocab, H))
+    finally:
+        g.close()
+
+
+def test_graph_replay_equals_eager():
+    model = get_model("llama1b_2layers")
+    cfg = model.cfg
+    g = open_gpu(model, max_seqs=1)
+    try:
+        toks = synth.start_tokens(cfg, 1)
+        outs = {}
+        for mode in (True, False, True):
+            g.set_graph(mode)
+            g.set_position(0, cfg.ctx)
+            seq = []
+            t = toks
+            for _ in range(3):
+                lg, am = g.step(t)
+                seq.append((lg.copy(), am.copy()))
+                t = am
+            outs.setdefault(mode, []).append(seq)
+        ref = outs[True][0]
+        for runs in outs.values():
+            for seq in runs:
+                for (a, b), (c, d) in zip(seq, ref):
+                    assert np.array_equal(a, c) and np.array_equal(b, d)
+    finally:
+        g.close()
+
+
+@pytest.mark.parametrize("name", ["tiny_q8", "llama1b_2layers"])
+def test_stream_mode_bit_identical(name):
+    model = get_model(name)
+    cfg = model.cfg
+    g = open_gpu(model, max_seqs=1)
+    try:
+        toks = synth.start_tokens(cfg, 1)
+
+        def run():
+            g.set_position(0, cfg.ctx)
+            res = []
+            t = toks
+            for _ in range(cfg.steps):
+                lg, am = g.step(t)
+                res.append((lg.copy(), am.copy()))
+                t = am
+            return res
+
+        resident = run()
+        g.stream_mode(True)
+        streamed = run()
+        streamed2 = run()
+        g.stream_mode(False)
+        back = run()
+        for other in (streamed, streamed2, back):
+            for (a, b), (c, d) in zip(resident, other):
+                assert np.array_equal(a, c) and np.array_equal(b, d)
+    finally:
+        g.close()
+
+
+def test_state_and_context_errors():
+    import token_decode_llama_amd as lm
+    cfg = CASES["tiny_q8"]
+    model = get_model("tiny_q8")
+    m = lm.Model(cfg, max_seqs=1)
+    try:
+        with pytest.raises(lm.LMError) as e:
+            m.step([1])
+        assert e.value.status == lm.LM_E_STATE
+        m.load_model(model)
+        for l in range(cfg.n_layers):
+            k, v = synth.make_kv(cfg, 0, l)
+            m.load_kv(0, l, k, v)
+        with pytest.raises(lm.LMError) as e:
+            m.step([cfg.vocab])
+        assert e.value.status == lm.LM_E_ARG
+        with pytest.raises(lm.LMError) as e:
+            m.step([1, 2])
+        assert e.value.status == lm.LM_E_ARG
+        first = m.step([5])
+        for _ in range(cfg.steps - 1):
+            m.step([5])
+        assert m.position(0) == cfg.max_ctx
+        with pytest.raises(lm.LMError) as e:
+            m.step([5])
+        assert e.value.status == lm.LM_E_CTX and "max_ctx" in str(e.value)
+        m.set_position(0, cfg.ctx)
+        again = m.step([5])
+        assert np.array_equal(first[0], again[0]) and np.array_equal(first[1], again[1])
+        with pytest.raises(lm.LMError) as e:
+            m.set_position(0, cfg.max_ctx + 1)
+        assert e.value.status == lm.LM_E_ARG
+    finally:
+        m.close()
+
+
+@pytest.mark.slow
+def test_llama8b_q8_full_size_parity():
+    """The full 8B-shape Q8_0 model at context 512, the launch configuration
+    the benchmark times: two teacher-forced steps against the oracle, plus
+    sampled rows of every matrix dequantised bit-exactly."""
+    cfg = synth.CONFIGS["llama8b_q8"]
+    log("generate llama8b_q8 (~8 GB)")
+    model = synth.make_model(cfg)
+    log("run parity")
+    run_parity(model, n_seq=1, steps=2)
+    g = open_gpu(model, max_seqs=1)
+    try:
+        H, F, Q, KV = cfg.hidden, cfg.ffn, cfg.n_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
+        rng = np.random.default_rng(0)
+        for l in (0, cfg.n_layers - 1):
+            w = model.layers[l]
+            for which, (arr, rows, cols) in enumerate([(w.wq, Q, H), (w.wk, KV, H), (w.wv, KV, H),
+                                                       (w.wo, H, Q), (w.w_gate, F, H),
+                                                       (w.w_up, F, H), (w.w_down, H, F)]):
+                for r in (0, rows - 1, int(rng.integers(rows))):
+                    got = g.debug_dequant(l, which, r, 1, cols)
+                    ref = oracle.dequant(cfg.qtype, arr[r:r + 1], 1, cols)
+                    assert np.array_equal(got.astype(np.float64), ref), (l, which, r)
+        for r in (0, cfg.vocab - 1, 77777):
+            got = g.debug_dequant(0, 7, r, 1, H)
+            assert np.array_equal(got.astype(np.float64), oracle.dequant(cfg.qtype, model.lm_head[r:r + 1], 1, H))
+    finally:
+        g.close()

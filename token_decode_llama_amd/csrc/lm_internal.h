@@ -1,0 +1,84 @@
+// lm_internal.h - shared declarations between the host runtime and the
+// gfx950 kernels of the decode step (not part of the public C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace lmk {
+
+constexpr int kQ4_0 = 2;
+constexpr int kQ8_0 = 8;
+constexpr int kAttnChunk = 64;     // KV positions per attention workgroup
+
+// Device layout of one quantised matrix [N rows][K cols], nb = K/32 blocks/row.
+//   Q8_0: quants row-major, each row = [first 16 bytes of every block]
+//         [last 16 bytes of every block] (int8), so a wavefront reading
+//         block b of consecutive lanes makes fully coalesced 16-byte loads;
+//   Q4_0: quants row-major, each row = nb x 16 nibble bytes in GGUF order
+//         (byte j: element j low nibble, element j+16 high nibble);
+//   scales: fp16 [N][nb] in a separate plane.
+struct QMat {
+    const uint8_t* q;
+    const uint16_t* sc;
+    int N, K;
+};
+
+inline int64_t qmat_qbytes(int qtype, int64_t N, int64_t K) {
+    return qtype == kQ8_0 ? N * K : N * K / 2;
+}
+inline int64_t qmat_sbytes(int64_t N, int64_t K) { return N * (K / 32) * 2; }
+
+enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
+
+struct GemvArgs {
+    QMat w;
+    int qtype;
+    const float* xin;      // [n_seq][x_stride] input activations
+    int x_stride;
+    const float* norm_g;   // RMSNorm gain applied to xin first, or nullptr
+    float eps;
+    // epilogue outputs
+    float* out;            // QKV: q [n_seq][nq*hd]; RESID: x [n_seq][N] (+=);
+                           // SWIGLU: h [n_seq][N/2]; LOGITS: logits [n_seq][N] or nullptr
+    int out_stride;
+    // QKV epilogue
+    int q_rows, kv_rows, head_dim, max_ctx;
+    __half* kcache;        // layer base [max_seqs][nkv][max_ctx][hd]
+    __half* vcache;
+    int64_t kv_seq_stride; // elements per sequence in one layer's cache
+    const int* pos;        // [n_seq] current position of each sequence
+    const float* rope_cos; // [max_ctx][hd/2]
+    const float* rope_sin;
+    // LOGITS epilogue: per-workgroup (max, index) partials and the final argmax
+    float* part_val;       // [n_seq][gridDim.x]
+    int* part_idx;
+    int* counter;          // [n_seq], zero between launches
+    int* argmax_out;       // [n_seq]
+    int* pos_inc;          // [n_seq] positions advanced by one after the argmax
+};
+
+struct AttnArgs {
+    const float* q;        // [n_seq][nq*hd], rotated
+    const __half* kcache;  // layer base [max_seqs][nkv][max_ctx][hd]
+    const __half* vcache;
+    int64_t kv_seq_stride;
+    const int* pos;
+    int nq, nkv, hd, max_ctx, max_chunks;
+    float scale;           // 1/sqrt(hd)
+    float* part;           // [n_seq][nq][max_chunks][hd + 2] partial o, m, l
+    int* counter;          // [n_seq][nkv], zero between launches
+    float* out;            // [n_seq][nq*hd]
+};
+
+// launchers (lm_kernels.hip); all asynchronous on `st`
+hipError_t launch_embed(const uint16_t* tok_embd, const int* tokens, int vocab, int hidden,
+                        float* x, int n_seq, hipStream_t st);
+hipError_t launch_gemv(const GemvArgs& a, int epi, int n_seq, int max_blocks, hipStream_t st);
+hipError_t launch_attention(const AttnArgs& a, int n_seq, hipStream_t st);
+hipError_t launch_dequant(const QMat& w, int qtype, int row0, int n_rows, float* out,
+                          hipStream_t st);
+hipError_t launch_read_bw(const void* buf, int64_t n_bytes, float* sink, hipStream_t st);
+
+}  // namespace lmk

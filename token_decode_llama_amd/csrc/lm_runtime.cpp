@@ -1,0 +1,1091 @@
+// lm_runtime.cpp - host runtime behind the C ABI in include/lmdecode.h.
+//
+// One model = one HIP stream (plus a copy stream for weight streaming).  All
+// device memory is allocated in lm_model_create, so a decode step allocates
+// nothing.  Weight matrices are repacked at load into the layout the GEMV
+// kernels read (lm_internal.h); one layer's four matrices form one
+// contiguous "layer blob", which is also the unit the streaming mode copies.
+//
+// Streaming mode follows the double-buffered layer pipeline of the C/CUDA
+// Llama engine page (rskf.cn/news/15116, sections 2.3, 3.3 and 4.2: compute
+// layer n from one buffer while layer n+1 loads into the other, then swap)
+// and the pinned host region + two device ping-pong buffers + two streams +
+// per-layer events of "3 Agents. 3 LLMs. 1 Aging GPU" (section on loading
+// only the layers you need).  Both ordering edges are explicit events: a
+// layer's compute waits for its copy, and the copy that overwrites a buffer
+// waits for the compute that last read it.
+#include "lm_internal.h"
+
+#include "../../include/lmdecode.h"
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <thread>
+#include <vector>
+
+using namespace lmk;
+
+namespace {
+
+thread_local std::string g_create_error;
+std::atomic<long> g_alloc_count{0};
+
+constexpr int64_t kAlign = 256;
+inline int64_t align_up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Matrices of one layer blob, in order.
+enum { M_QKV = 0, M_WO = 1, M_GU = 2, M_DOWN = 3, M_COUNT = 4 };
+
+struct MatOff {
+    int64_t q, sc;   // byte offsets within the blob
+    int N, K;
+};
+
+template <class F>
+void parallel_rows(int64_t n, F&& fn) {
+    unsigned nt = std::min<unsigned>(std::max(1u, std::thread::hardware_concurrency()), 16u);
+    if (n < 64 || nt <= 1) { fn(0, n); return; }
+    std::vector<std::thread> th;
+    const int64_t per = (n + nt - 1) / nt;
+    for (unsigned t = 0; t < nt; ++t) {
+        const int64_t a = t * per, b = std::min(n, a + per);
+        if (a >= b) break;
+        th.emplace_back([&fn, a, b] { fn(a, b); });
+    }
+    for (auto& t : th) t.join();
+}
+
+// GGUF row (nb blocks) -> device layout row (quants + scales)
+void repack_row(int qtype, const uint8_t* src, int K, uint8_t* dq, uint16_t* dsc) {
+    const int nb = K / 32;
+    if (qtype == kQ8_0) {
+        for (int b = 0; b < nb; ++b) {
+            const uint8_t* blk = src + (int64_t)b * 34;
+            dsc[b] = (uint16_t)(blk[0] | (blk[1] << 8));
+            std::memcpy(dq + (int64_t)b * 16, blk + 2, 16);
+            std::memcpy(dq + (int64_t)nb * 16 + (int64_t)b * 16, blk + 18, 16);
+        }
+    } else {
+        for (int b = 0; b < nb; ++b) {
+            const uint8_t* blk = src + (int64_t)b * 18;
+            dsc[b] = (uint16_t)(blk[0] | (blk[1] << 8));
+            std::memcpy(dq + (int64_t)b * 16, blk + 2, 16);
+        }
+    }
+}
+
+int block_bytes(int qtype) { return qtype == kQ8_0 ? 34 : 18; }
+
+}  // namespace
+
+struct lm_model {
+    lm_config cfg{};
+    hipStream_t stream = nullptr;
+    bool own_stream = false;
+    hipStream_t copy_stream = nullptr;
+    std::string err;
+
+    int64_t H = 0, F = 0, V = 0, nq = 0, nkv = 0, hd = 0, qrows = 0, kvrows = 0;
+    int64_t blob_bytes = 0;
+    MatOff mo[M_COUNT]{};
+    int64_t lm_q_bytes = 0, lm_sc_bytes = 0;
+    int max_chunks = 0;
+    int gemv_max_blocks = 1024;
+    int lm_grid = 0;
+
+    // device memory
+    uint8_t* d_layers = nullptr;          // resident blobs [L][blob]
+    uint8_t* d_sbuf[2] = {nullptr, nullptr};
+    uint8_t* h_arena = nullptr;           // pinned blobs (stream mode)
+    uint8_t* h_stage = nullptr;           // pinned staging for uploads
+    int64_t stage_bytes = 0;
+    float* d_norms = nullptr;             // [L][2][H]
+    uint16_t* d_embd = nullptr;
+    float* d_out_norm = nullptr;
+    uint8_t* d_lm_q = nullptr;
+    uint16_t* d_lm_sc = nullptr;
+    __half* d_k = nullptr;                // [L][S][nkv][max_ctx][hd]
+    __half* d_v = nullptr;
+    float *d_x = nullptr, *d_q = nullptr, *d_o = nullptr, *d_h = nullptr, *d_logits = nullptr;
+    int *d_tokens = nullptr, *d_argmax = nullptr, *d_pos = nullptr;
+    float *d_cos = nullptr, *d_sin = nullptr;
+    float* d_attn_part = nullptr;
+    int* d_attn_cnt = nullptr;
+    float* d_lm_pval = nullptr;
+    int* d_lm_pidx = nullptr;
+    int* d_lm_cnt = nullptr;
+    float* d_sink = nullptr;
+    float* d_dbg = nullptr;               // debug dequant rows
+    int64_t dbg_floats = 0;
+
+    std::vector<uint8_t> layer_loaded;
+    bool global_loaded = false;
+    std::vector<int> pos;
+    bool streaming = false;
+    bool use_graph = true;
+
+    // streaming pipeline state
+    hipEvent_t ev_copied[2] = {nullptr, nullptr};
+    hipEvent_t ev_consumed[2] = {nullptr, nullptr};
+    bool prefetched[2] = {false, false};   // slot holds layer 0/1 for the next step
+
+    struct GraphEntry {
+        int n_seq;
+        const int* tok;
+        float* logits;
+        int* argmax;
+        hipGraphExec_t exec;
+    };
+    std::vector<GraphEntry> graphs;
+
+    // kernel timing
+    bool timing = false;
+    int64_t kcount[LM_K_COUNT] = {};
+    double kms[LM_K_COUNT] = {};
+    struct Pending { int kind; hipEvent_t a, b; };
+    std::vector<Pending> pending;
+    std::vector<hipEvent_t> ev_pool;
+    size_t ev_used = 0;
+
+    std::vector<void*> dev_allocs;
+    std::vector<void*> host_allocs;
+};
+
+// ---------------------------------------------------------------------------
+// error helpers
+// ---------------------------------------------------------------------------
+static lm_status fail(lm_model* m, lm_status st, const char* fmt, ...) {
+    char buf[1024];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    if (m) m->err = buf;
+    else g_create_error = buf;
+    return st;
+}
+
+#define HIPTRY(m, call)                                                                    \
+    do {                                                                                   \
+        hipError_t _e = (call);                                                            \
+        if (_e != hipSuccess)                                                              \
+            return fail((m), LM_E_HIP, "%s failed: %s (%d)", #call, hipGetErrorString(_e), \
+                        (int)_e);                                                          \
+    } while (0)
+
+static bool fault_alloc_now() {
+    static long at = [] {
+        const char* s = std::getenv("LM_FAULT_ALLOC_AT");
+        return s ? std::atol(s) : 0L;
+    }();
+    const long n = ++g_alloc_count;
+    return at > 0 && n == at;
+}
+
+static lm_status dev_alloc(lm_model* m, void** p, int64_t bytes, const char* what) {
+    *p = nullptr;
+    if (bytes <= 0) bytes = kAlign;
+    if (fault_alloc_now())
+        return fail(m, LM_E_OOM, "device allocation of %s (%lld bytes) failed: injected by LM_FAULT_ALLOC_AT",
+                    what, (long long)bytes);
+    hipError_t e = hipMalloc(p, (size_t)bytes);
+    if (e != hipSuccess) {
+        *p = nullptr;
+        (void)hipGetLastError();
+        return fail(m, LM_E_OOM, "hipMalloc of %s (%lld bytes) failed: %s", what, (long long)bytes,
+                    hipGetErrorString(e));
+    }
+    m->dev_allocs.push_back(*p);
+    return LM_OK;
+}
+
+static lm_status host_alloc(lm_model* m, void** p, int64_t bytes, const char* what) {
+    *p = nullptr;
+    if (fault_alloc_now())
+        return fail(m, LM_E_OOM, "pinned host allocation of %s (%lld bytes) failed: injected by LM_FAULT_ALLOC_AT",
+                    what, (long long)bytes);
+    hipError_t e = hipHostMalloc(p, (size_t)bytes, hipHostMallocDefault);
+    if (e != hipSuccess) {
+        *p = nullptr;
+        (void)hipGetLastError();
+        return fail(m, LM_E_OOM, "hipHostMalloc of %s (%lld bytes) failed: %s", what, (long long)bytes,
+                    hipGetErrorString(e));
+    }
+    m->host_allocs.push_back(*p);
+    return LM_OK;
+}
+
+static void dev_free(lm_model* m, void* p) {
+    if (!p) return;
+    (void)hipFree(p);
+    m->dev_allocs.erase(std::remove(m->dev_allocs.begin(), m->dev_allocs.end(), p), m->dev_allocs.end());
+}
+
+static void host_free(lm_model* m, void* p) {
+    if (!p) return;
+    (void)hipHostFree(p);
+    m->host_allocs.erase(std::remove(m->host_allocs.begin(), m->host_allocs.end(), p), m->host_allocs.end());
+}
+
+static void release_all(lm_model* m) {
+    if (m->stream) (void)hipStreamSynchronize(m->stream);
+    if (m->copy_stream) (void)hipStreamSynchronize(m->copy_stream);
+    for (auto& g : m->graphs) (void)hipGraphExecDestroy(g.exec);
+    m->graphs.clear();
+    for (auto e : m->ev_pool) (void)hipEventDestroy(e);
+    m->ev_pool.clear();
+    for (int i = 0; i < 2; ++i) {
+        if (m->ev_copied[i]) (void)hipEventDestroy(m->ev_copied[i]);
+        if (m->ev_consumed[i]) (void)hipEventDestroy(m->ev_consumed[i]);
+        m->ev_copied[i] = m->ev_consumed[i] = nullptr;
+    }
+    for (void* p : m->dev_allocs) (void)hipFree(p);
+    m->dev_allocs.clear();
+    for (void* p : m->host_allocs) (void)hipHostFree(p);
+    m->host_allocs.clear();
+    if (m->copy_stream) (void)hipStreamDestroy(m->copy_stream);
+    m->copy_stream = nullptr;
+    if (m->own_stream && m->stream) (void)hipStreamDestroy(m->stream);
+    m->stream = nullptr;
+}
+
+// ---------------------------------------------------------------------------
+// configuration checks (no HIP call before these pass)
+// ---------------------------------------------------------------------------
+static lm_status check_config(const lm_config* c) {
+    auto bad = [](const char* what, long long got, const char* expect) {
+        return fail(nullptr, LM_E_ARG, "bad config: %s = %lld; expected %s", what, got, expect);
+    };
+    if (!c) return fail(nullptr, LM_E_ARG, "bad config: NULL pointer");
+    if (c->qtype != LM_Q8_0 && c->qtype != LM_Q4_0) return bad("qtype", c->qtype, "2 (Q4_0) or 8 (Q8_0)");
+    if (c->vocab < 2 || c->vocab % 2) return bad("vocab", c->vocab, "an even number >= 2");
+    if (c->hidden < 32 || c->hidden % 32) return bad("hidden", c->hidden, "a positive multiple of 32");
+    if (c->n_layers < 1) return bad("n_layers", c->n_layers, ">= 1");
+    if (c->n_heads < 1) return bad("n_heads", c->n_heads, ">= 1");
+    if (c->n_kv_heads < 1 || c->n_heads % c->n_kv_heads)
+        return bad("n_kv_heads", c->n_kv_heads, "a divisor of n_heads");
+    if (c->n_heads / c->n_kv_heads > 8) return bad("n_heads / n_kv_heads", c->n_heads / c->n_kv_heads, "<= 8");
+    if (c->head_dim != 64 && c->head_dim != 128) return bad("head_dim", c->head_dim, "64 or 128");
+    if (c->ffn < 32 || c->ffn % 32) return bad("ffn", c->ffn, "a positive multiple of 32");
+    if (c->max_ctx < 1) return bad("max_ctx", c->max_ctx, ">= 1");
+    if (c->max_seqs < 1 || c->max_seqs > 4) return bad("max_seqs", c->max_seqs, "1..4");
+    if (!(c->rms_eps >= 0.0) || !std::isfinite(c->rms_eps))
+        return fail(nullptr, LM_E_ARG, "bad config: rms_eps = %g; expected a finite value >= 0", c->rms_eps);
+    if (!(c->rope_theta > 0.0) || !std::isfinite(c->rope_theta))
+        return fail(nullptr, LM_E_ARG, "bad config: rope_theta = %g; expected a finite value > 0", c->rope_theta);
+    const int64_t kmax = std::max<int64_t>({c->hidden, c->ffn, (int64_t)c->n_heads * c->head_dim});
+    const int64_t lds = kmax * 4 + kmax / 32 * 4;
+    if (lds > 150 * 1024)
+        return fail(nullptr, LM_E_ARG, "bad config: widest GEMV input has %lld columns (%lld bytes of LDS); "
+                    "expected at most %d bytes", (long long)kmax, (long long)lds, 150 * 1024);
+    return LM_OK;
+}
+
+static void layout(lm_model* m) {
+    const lm_config& c = m->cfg;
+    m->H = c.hidden; m->F = c.ffn; m->V = c.vocab;
+    m->nq = c.n_heads; m->nkv = c.n_kv_heads; m->hd = c.head_dim;
+    m->qrows = m->nq * m->hd;
+    m->kvrows = m->nkv * m->hd;
+    const int qt = c.qtype;
+    int64_t off = 0;
+    const int64_t NK[M_COUNT][2] = {{m->qrows + 2 * m->kvrows, m->H},
+                                    {m->H, m->qrows},
+                                    {2 * m->F, m->H},
+                                    {m->H, m->F}};
+    for (int i = 0; i < M_COUNT; ++i) {
+        m->mo[i].N = (int)NK[i][0];
+        m->mo[i].K = (int)NK[i][1];
+        m->mo[i].q = off;
+        off = align_up(off + qmat_qbytes(qt, NK[i][0], NK[i][1]));
+        m->mo[i].sc = off;
+        off = align_up(off + qmat_sbytes(NK[i][0], NK[i][1]));
+    }
+    m->blob_bytes = off;
+    m->lm_q_bytes = align_up(qmat_qbytes(qt, m->V, m->H));
+    m->lm_sc_bytes = align_up(qmat_sbytes(m->V, m->H));
+    m->max_chunks = (c.max_ctx + kAttnChunk - 1) / kAttnChunk;
+}
+
+static QMat mat_at(const lm_model* m, const uint8_t* blob, int which) {
+    QMat w;
+    w.q = blob + m->mo[which].q;
+    w.sc = (const uint16_t*)(blob + m->mo[which].sc);
+    w.N = m->mo[which].N;
+    w.K = m->mo[which].K;
+    return w;
+}
+
+static QMat lm_head_mat(const lm_model* m) {
+    QMat w;
+    w.q = m->d_lm_q;
+    w.sc = m->d_lm_sc;
+    w.N = (int)m->V;
+    w.K = (int)m->H;
+    return w;
+}
+
+static int64_t kv_layer_elems(const lm_model* m) {
+    return (int64_t)m->cfg.max_seqs * m->nkv * m->cfg.max_ctx * m->hd;
+}
+
+static int64_t kv_seq_elems(const lm_model* m) { return m->nkv * (int64_t)m->cfg.max_ctx * m->hd; }
+
+// ---------------------------------------------------------------------------
+// create / destroy
+// ---------------------------------------------------------------------------
+extern "C" lm_status lm_model_create(const lm_config* cfg, void* hip_stream, lm_model** out) {
+    g_create_error.clear();
+    if (!out) return fail(nullptr, LM_E_ARG, "lm_model_create: out is NULL");
+    *out = nullptr;
+    lm_status st = check_config(cfg);
+    if (st != LM_OK) return st;
+
+    lm_model* m = new (std::nothrow) lm_model();
+    if (!m) return fail(nullptr, LM_E_OOM, "lm_model_create: host allocation failed");
+    m->cfg = *cfg;
+    layout(m);
+    m->layer_loaded.assign(cfg->n_layers, 0);
+    m->pos.assign(cfg->max_seqs, 0);
+
+    auto bail = [&](lm_status s) {
+        g_create_error = m->err;
+        release_all(m);
+        delete m;
+        return s;
+    };
+#define CREATE_TRY(expr)                      \
+    do {                                      \
+        lm_status _s = (expr);                \
+        if (_s != LM_OK) return bail(_s);     \
+    } while (0)
+#define CREATE_HIP(call)                                                                   \
+    do {                                                                                   \
+        hipError_t _e = (call);                                                            \
+        if (_e != hipSuccess) {                                                            \
+            fail(m, LM_E_HIP, "%s failed: %s (%d)", #call, hipGetErrorString(_e), (int)_e); \
+            return bail(LM_E_HIP);                                                         \
+        }                                                                                  \
+    } while (0)
+
+    int ndev = 0;
+    CREATE_HIP(hipGetDeviceCount(&ndev));
+    if (hip_stream) {
+        m->stream = (hipStream_t)hip_stream;
+        m->own_stream = false;
+    } else {
+        CREATE_HIP(hipStreamCreateWithFlags(&m->stream, hipStreamNonBlocking));
+        m->own_stream = true;
+    }
+    CREATE_HIP(hipStreamCreateWithFlags(&m->copy_stream, hipStreamNonBlocking));
+    for (int i = 0; i < 2; ++i) {
+        CREATE_HIP(hipEventCreateWithFlags(&m->ev_copied[i], hipEventDisableTiming));
+        CREATE_HIP(hipEventCreateWithFlags(&m->ev_consumed[i], hipEventDisableTiming));
+    }
+    {
+        int dev = 0, ncu = 0;
+        CREATE_HIP(hipGetDevice(&dev));
+        CREATE_HIP(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
+        m->gemv_max_blocks = std::max(64, ncu * 4);
+    }
+
+    const lm_config& c = *cfg;
+    const int S = c.max_seqs;
+    const int64_t L = c.n_layers;
+    CREATE_TRY(dev_alloc(m, (void**)&m->d_layers, L * m->blob_bytes, "layer weights"));
+    CREATE_TRY(dev_alloc(m, (void**)&m->d_norms, L * 2 * m->H * 4, "norm gains"));
+    CREATE_TRY(dev_alloc(m, (void**)&m->d_embd, m->V * m->H * 2, "token embedding"));
+    CREATE_TRY(dev_alloc(m, (void**)&m->d_out_norm, m->H * 4, "output norm"));
+    CREATE_TRY(dev_alloc(m, (void**)&m->d_lm_q, m->lm_q_bytes, "LM head quants"));
+    CREATE_TRY(dev_alloc(m, (void**)&m->d_lm_sc, m->lm_sc_bytes, "LM head scales"));
+    CREATE_TRY(dev_alloc(m, (void**)&m->d_k, L * kv_layer_elems(m) * 2, "K cache"));
+    CREATE_TRY(dev_alloc(m, (void**)&m->d_v, L * kv_layer_elems(m) * 2, "V cache"));
+    CREATE_TRY(dev_alloc(m, (void**)&m->d_x, S * m->H * 4, "residual"));
+    CREATE_TRY(dev_alloc(m, (void**)&m->d_q, S * m->qrows * 4, "q"));
+    CREATE_TRY(dev_alloc(m, (void**)&m->d_o, S * m->qrows * 4, "attention output"));
+    CREATE_TRY(dev_alloc(m, (void**)&m->d_h, S * m->F * 4, "ffn hidden"));
+    CREATE_TRY(dev_alloc(m, (void**)&m->d_logits, S * m->V * 4, "logits"));
+    CREATE_TRY(dev_alloc(m, (void**)&m->d_tokens, S * 4, "tokens"));
+    CREATE_TRY(dev_alloc(m, (void**)&m->d_argmax, S * 4, "argmax"));
+    CREATE_TRY(dev_alloc(m, (void**)&m->d_pos, S * 4, "positions"));
+    CREATE_TRY(dev_alloc(m, (void**)&m->d_cos, (int64_t)c.max_ctx * (m->hd / 2) * 4, "rope cos"));
+    CREATE_TRY(dev_alloc(m, (void**)&m->d_sin, (int64_t)c.max_ctx * (m->hd / 2) * 4, "rope sin"));
+    CREATE_TRY(dev_alloc(m, (void**)&m->d_attn_part,
+                         (int64_t)S * m->nq * m->max_chunks * (m->hd + 2) * 4, "attention partials"));
+    CREATE_TRY(dev_alloc(m, (void**)&m->d_attn_cnt, (int64_t)S * m->nkv * 4, "attention counters"));
+    CREATE_TRY(dev_alloc(m, (void**)&m->d_lm_pval, (int64_t)S * m->gemv_max_blocks * 4, "argmax partials"));
+    CREATE_TRY(dev_alloc(m, (void**)&m->d_lm_pidx, (int64_t)S * m->gemv_max_blocks * 4, "argmax partial ids"));
+    CREATE_TRY(dev_alloc(m, (void**)&m->d_lm_cnt, (int64_t)S * 4, "argmax counters"));
+    CREATE_TRY(dev_alloc(m, (void**)&m->d_sink, 4096 * 4, "sink"));
+    m->dbg_floats = std::max<int64_t>({m->H, m->F, m->qrows}) * 64;
+    CREATE_TRY(dev_alloc(m, (void**)&m->d_dbg, m->dbg_floats * 4, "debug rows"));
+    m->stage_bytes = std::min<int64_t>(64ll << 20, std::max<int64_t>(m->blob_bytes, m->lm_q_bytes + m->lm_sc_bytes));
+    m->stage_bytes = std::max<int64_t>(m->stage_bytes, 4 * (m->H * 34 / 32 + 64));
+    CREATE_TRY(host_alloc(m, (void**)&m->h_stage, m->stage_bytes, "upload staging"));
+
+    // zero what must start at zero (counters, caches, positions)
+    CREATE_HIP(hipMemsetAsync(m->d_attn_cnt, 0, (size_t)S * m->nkv * 4, m->stream));
+    CREATE_HIP(hipMemsetAsync(m->d_lm_cnt, 0, (size_t)S * 4, m->stream));
+    CREATE_HIP(hipMemsetAsync(m->d_pos, 0, (size_t)S * 4, m->stream));
+    CREATE_HIP(hipMemsetAsync(m->d_k, 0, (size_t)(L * kv_layer_elems(m) * 2), m->stream));
+    CREATE_HIP(hipMemsetAsync(m->d_v, 0, (size_t)(L * kv_layer_elems(m) * 2), m->stream));
+
+    // RoPE table: angle p * theta^(-2i/hd) evaluated in fp64, stored fp32
+    {
+        const int half = (int)(m->hd / 2);
+        std::vector<float> cs((size_t)c.max_ctx * half), sn((size_t)c.max_ctx * half);
+        for (int p = 0; p < c.max_ctx; ++p)
+            for (int i = 0; i < half; ++i) {
+                const double f = std::pow(c.rope_theta, -2.0 * i / (double)m->hd);
+                const double a = (double)p * f;
+                cs[(size_t)p * half + i] = (float)std::cos(a);
+                sn[(size_t)p * half + i] = (float)std::sin(a);
+            }
+        CREATE_HIP(hipMemcpy(m->d_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice));
+        CREATE_HIP(hipMemcpy(m->d_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice));
+    }
+    CREATE_HIP(hipStreamSynchronize(m->stream));
+#undef CREATE_TRY
+#undef CREATE_HIP
+    *out = m;
+    return LM_OK;
+}
+
+extern "C" void lm_model_destroy(lm_model* m) {
+    if (!m) return;
+    release_all(m);
+    delete m;
+}
+
+extern "C" const char* lm_last_error(const lm_model* m) {
+    return m ? m->err.c_str() : g_create_error.c_str();
+}
+
+extern "C" void* lm_stream(const lm_model* m) { return m ? (void*)m->stream : nullptr; }
+
+// ---------------------------------------------------------------------------
+// weight upload
+// ---------------------------------------------------------------------------
+// Repacks rows [0, N) of one matrix, whose row r comes from src_row(r), into
+// the device layout at (dq, dsc).  dst_host: the destination is host memory
+// (the pinned arena) and is written directly; otherwise rows go through the
+// pinned staging buffer in chunks.
+template <class RowFn>
+static lm_status upload_matrix(lm_model* m, int N, int K, RowFn src_row, uint8_t* dq, uint16_t* dsc,
+                               bool dst_host) {
+    const int qt = m->cfg.qtype;
+    const int64_t rq = qmat_qbytes(qt, 1, K), rs = (K / 32) * 2;
+    if (dst_host) {
+        parallel_rows(N, [&](int64_t a, int64_t b) {
+            for (int64_t r = a; r < b; ++r) repack_row(qt, src_row(r), K, dq + r * rq, dsc + r * (K / 32));
+        });
+        return LM_OK;
+    }
+    const int64_t rows_per = std::max<int64_t>(1, m->stage_bytes / (rq + rs));
+    for (int64_t r0 = 0; r0 < N; r0 += rows_per) {
+        const int64_t n = std::min<int64_t>(rows_per, N - r0);
+        uint8_t* sq = m->h_stage;
+        uint16_t* ss = (uint16_t*)(m->h_stage + n * rq);
+        parallel_rows(n, [&](int64_t a, int64_t b) {
+            for (int64_t r = a; r < b; ++r) repack_row(qt, src_row(r0 + r), K, sq + r * rq, ss + r * (K / 32));
+        });
+        HIPTRY(m, hipMemcpyAsync(dq + r0 * rq, sq, (size_t)(n * rq), hipMemcpyHostToDevice, m->stream));
+        HIPTRY(m, hipMemcpyAsync(dsc + r0 * (K / 32), ss, (size_t)(n * rs), hipMemcpyHostToDevice, m->stream));
+        HIPTRY(m, hipStreamSynchronize(m->stream));
+    }
+    return LM_OK;
+}
+
+static void invalidate_graphs(lm_model* m) {
+    for (auto& g : m->graphs) (void)hipGraphExecDestroy(g.exec);
+    m->graphs.clear();
+}
+
+extern "C" lm_status lm_load_layer_weights(lm_model* m, int32_t layer, const lm_layer_weights* w) {
+    if (!m) return LM_E_ARG;
+    if (layer < 0 || layer >= m->cfg.n_layers)
+        return fail(m, LM_E_ARG, "lm_load_layer_weights: layer = %d; expected 0..%d", layer, m->cfg.n_layers - 1);
+    if (!w || !w->attn_norm || !w->ffn_norm || !w->wq || !w->wk || !w->wv || !w->wo || !w->w_gate ||
+        !w->w_up || !w->w_down)
+        return fail(m, LM_E_ARG, "lm_load_layer_weights: a weight pointer is NULL (layer %d)", layer);
+    HIPTRY(m, hipStreamSynchronize(m->stream));
+    HIPTRY(m, hipStreamSynchronize(m->copy_stream));
+    const int qt = m->cfg.qtype, bb = block_bytes(qt);
+    const int64_t H = m->H, F = m->F;
+    const int64_t rowH = H / 32 * bb, rowQ = m->qrows / 32 * bb, rowF = F / 32 * bb;
+    const uint8_t *wq = (const uint8_t*)w->wq, *wk = (const uint8_t*)w->wk, *wv = (const uint8_t*)w->wv;
+    const uint8_t *wo = (const uint8_t*)w->wo, *wg = (const uint8_t*)w->w_gate, *wu = (const uint8_t*)w->w_up;
+    const uint8_t* wd = (const uint8_t*)w->w_down;
+    const int64_t qr = m->qrows, kr = m->kvrows;
+    uint8_t* blob = m->streaming ? m->h_arena + (int64_t)layer * m->blob_bytes
+                                 : m->d_layers + (int64_t)layer * m->blob_bytes;
+    const bool host = m->streaming;
+    auto dq = [&](int i) { return blob + m->mo[i].q; };
+    auto ds = [&](int i) { return (uint16_t*)(blob + m->mo[i].sc); };
+    lm_status st;
+    st = upload_matrix(m, m->mo[M_QKV].N, (int)H, [&](int64_t r) {
+        if (r < qr) return wq + r * rowH;
+        if (r < qr + kr) return wk + (r - qr) * rowH;
+        return wv + (r - qr - kr) * rowH;
+    }, dq(M_QKV), ds(M_QKV), host);
+    if (st != LM_OK) return st;
+    st = upload_matrix(m, (int)H, (int)m->qrows, [&](int64_t r) { return wo + r * rowQ; }, dq(M_WO), ds(M_WO), host);
+    if (st != LM_OK) return st;
+    // gate and up rows interleaved: device row 2i = gate i, 2i+1 = up i
+    st = upload_matrix(m, (int)(2 * F), (int)H, [&](int64_t r) {
+        return (r & 1) ? wu + (r >> 1) * rowH : wg + (r >> 1) * rowH;
+    }, dq(M_GU), ds(M_GU), host);
+    if (st != LM_OK) return st;
+    st = upload_matrix(m, (int)H, (int)F, [&](int64_t r) { return wd + r * rowF; }, dq(M_DOWN), ds(M_DOWN), host);
+    if (st != LM_OK) return st;
+    HIPTRY(m, hipMemcpy(m->d_norms + (int64_t)layer * 2 * H, w->attn_norm, H * 4, hipMemcpyHostToDevice));
+    HIPTRY(m, hipMemcpy(m->d_norms + ((int64_t)layer * 2 + 1) * H, w->ffn_norm, H * 4, hipMemcpyHostToDevice));
+    m->layer_loaded[layer] = 1;
+    m->prefetched[0] = m->prefetched[1] = false;
+    return LM_OK;
+}
+
+extern "C" lm_status lm_load_global_weights(lm_model* m, const uint16_t* tok_embd_f16, const float* out_norm,
+                                            const void* lm_head_blocks) {
+    if (!m) return LM_E_ARG;
+    if (!tok_embd_f16 || !out_norm || !lm_head_blocks)
+        return fail(m, LM_E_ARG, "lm_load_global_weights: a pointer is NULL");
+    HIPTRY(m, hipStreamSynchronize(m->stream));
+    HIPTRY(m, hipMemcpy(m->d_embd, tok_embd_f16, (size_t)(m->V * m->H * 2), hipMemcpyHostToDevice));
+    HIPTRY(m, hipMemcpy(m->d_out_norm, out_norm, (size_t)(m->H * 4), hipMemcpyHostToDevice));
+    const int64_t rowH = m->H / 32 * block_bytes(m->cfg.qtype);
+    const uint8_t* src = (const uint8_t*)lm_head_blocks;
+    lm_status st = upload_matrix(m, (int)m->V, (int)m->H, [&](int64_t r) { return src + r * rowH; },
+                                 m->d_lm_q, m->d_lm_sc, false);
+    if (st != LM_OK) return st;
+    m->global_loaded = true;
+    return LM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// KV cache and positions
+// ---------------------------------------------------------------------------
+static lm_status check_seq_layer(lm_model* m, const char* fn, int seq, int layer) {
+    if (seq < 0 || seq >= m->cfg.max_seqs)
+        return fail(m, LM_E_ARG, "%s: seq = %d; expected 0..%d", fn, seq, m->cfg.max_seqs - 1);
+    if (layer < 0 || layer >= m->cfg.n_layers)
+        return fail(m, LM_E_ARG, "%s: layer = %d; expected 0..%d", fn, layer, m->cfg.n_layers - 1);
+    return LM_OK;
+}
+
+extern "C" lm_status lm_load_kv(lm_model* m, int32_t seq, int32_t layer, const uint16_t* k, const uint16_t* v,
+                                int32_t n_pos) {
+    if (!m) return LM_E_ARG;
+    lm_status st = check_seq_layer(m, "lm_load_kv", seq, layer);
+    if (st != LM_OK) return st;
+    if (n_pos < 0 || n_pos > m->cfg.max_ctx)
+        return fail(m, LM_E_ARG, "lm_load_kv: n_pos = %d; expected 0..%d (max_ctx)", n_pos, m->cfg.max_ctx);
+    if (n_pos > 0 && (!k || !v)) return fail(m, LM_E_ARG, "lm_load_kv: k or v is NULL");
+    HIPTRY(m, hipStreamSynchronize(m->stream));
+    const int64_t base = (int64_t)layer * kv_layer_elems(m) + (int64_t)seq * kv_seq_elems(m);
+    const size_t row = (size_t)n_pos * m->hd * 2;
+    for (int g = 0; g < m->nkv && n_pos > 0; ++g) {
+        const int64_t off = base + (int64_t)g * m->cfg.max_ctx * m->hd;
+        HIPTRY(m, hipMemcpy(m->d_k + off, k + (int64_t)g * n_pos * m->hd, row, hipMemcpyHostToDevice));
+        HIPTRY(m, hipMemcpy(m->d_v + off, v + (int64_t)g * n_pos * m->hd, row, hipMemcpyHostToDevice));
+    }
+    int p = n_pos;
+    HIPTRY(m, hipMemcpy(m->d_pos + seq, &p, 4, hipMemcpyHostToDevice));
+    m->pos[seq] = n_pos;
+    return LM_OK;
+}
+
+extern "C" lm_status lm_get_kv(lm_model* m, int32_t seq, int32_t layer, uint16_t* k, uint16_t* v, int32_t n_pos) {
+    if (!m) return LM_E_ARG;
+    lm_status st = check_seq_layer(m, "lm_get_kv", seq, layer);
+    if (st != LM_OK) return st;
+    if (n_pos < 0 || n_pos > m->cfg.max_ctx)
+        return fail(m, LM_E_ARG, "lm_get_kv: n_pos = %d; expected 0..%d (max_ctx)", n_pos, m->cfg.max_ctx);
+    if (n_pos > 0 && (!k || !v)) return fail(m, LM_E_ARG, "lm_get_kv: k or v is NULL");
+    HIPTRY(m, hipStreamSynchronize(m->stream));
+    const int64_t base = (int64_t)layer * kv_layer_elems(m) + (int64_t)seq * kv_seq_elems(m);
+    const size_t row = (size_t)n_pos * m->hd * 2;
+    for (int g = 0; g < m->nkv && n_pos > 0; ++g) {
+        const int64_t off = base + (int64_t)g * m->cfg.max_ctx * m->hd;
+        HIPTRY(m, hipMemcpy(k + (int64_t)g * n_pos * m->hd, m->d_k + off, row, hipMemcpyDeviceToHost));
+        HIPTRY(m, hipMemcpy(v + (int64_t)g * n_pos * m->hd, m->d_v + off, row, hipMemcpyDeviceToHost));
+    }
+    return LM_OK;
+}
+
+extern "C" lm_status lm_set_position(lm_model* m, int32_t seq, int32_t pos) {
+    if (!m) return LM_E_ARG;
+    if (seq < 0 || seq >= m->cfg.max_seqs)
+        return fail(m, LM_E_ARG, "lm_set_position: seq = %d; expected 0..%d", seq, m->cfg.max_seqs - 1);
+    if (pos < 0 || pos > m->cfg.max_ctx)
+        return fail(m, LM_E_ARG, "lm_set_position: pos = %d; expected 0..%d (max_ctx)", pos, m->cfg.max_ctx);
+    HIPTRY(m, hipStreamSynchronize(m->stream));
+    int p = pos;
+    HIPTRY(m, hipMemcpy(m->d_pos + seq, &p, 4, hipMemcpyHostToDevice));
+    m->pos[seq] = pos;
+    return LM_OK;
+}
+
+extern "C" lm_status lm_get_position(const lm_model* m, int32_t seq, int32_t* pos) {
+    if (!m || !pos || seq < 0 || seq >= m->cfg.max_seqs) return LM_E_ARG;
+    *pos = m->pos[seq];
+    return LM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// the step
+// ---------------------------------------------------------------------------
+static hipEvent_t pool_event(lm_model* m) {
+    if (m->ev_used == m->ev_pool.size()) {
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        m->ev_pool.push_back(e);
+    }
+    return m->ev_pool[m->ev_used++];
+}
+
+struct KTimer {
+    lm_model* m;
+    int kind;
+    hipEvent_t a = nullptr;
+    KTimer(lm_model* mm, int k) : m(mm), kind(k) {
+        if (m->timing) {
+            a = pool_event(m);
+            if (a) (void)hipEventRecord(a, m->stream);
+        }
+    }
+    ~KTimer() {
+        if (m->timing && a) {
+            hipEvent_t b = pool_event(m);
+            if (b) {
+                (void)hipEventRecord(b, m->stream);
+                m->pending.push_back({kind, a, b});
+            }
+        }
+    }
+};
+
+static lm_status collect_timing(lm_model* m) {
+    if (m->pending.empty()) return LM_OK;
+    HIPTRY(m, hipStreamSynchronize(m->stream));
+    for (auto& p : m->pending) {
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, p.a, p.b) == hipSuccess) {
+            m->kcount[p.kind] += 1;
+            m->kms[p.kind] += ms;
+        }
+    }
+    m->pending.clear();
+    m->ev_used = 0;
+    return LM_OK;
+}
+
+static const uint8_t* layer_blob(lm_model* m, int l) {
+    return m->streaming ? m->d_sbuf[l & 1] : m->d_layers + (int64_t)l * m->blob_bytes;
+}
+
+static lm_status stream_copy(lm_model* m, int layer) {
+    const int slot = layer & 1;
+    HIPTRY(m, hipStreamWaitEvent(m->copy_stream, m->ev_consumed[slot], 0));
+    HIPTRY(m, hipMemcpyAsync(m->d_sbuf[slot], m->h_arena + (int64_t)layer * m->blob_bytes,
+                             (size_t)m->blob_bytes, hipMemcpyHostToDevice, m->copy_stream));
+    HIPTRY(m, hipEventRecord(m->ev_copied[slot], m->copy_stream));
+    return LM_OK;
+}
+
+static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d_logits, int* d_argmax) {
+    const lm_config& c = m->cfg;
+    const int L = c.n_layers;
+    hipStream_t st = m->stream;
+    {
+        KTimer t(m, LM_K_EMBED);
+        HIPTRY(m, launch_embed(m->d_embd, d_tok, (int)m->V, (int)m->H, m->d_x, n_seq, st));
+    }
+    GemvArgs base{};
+    base.qtype = c.qtype;
+    base.eps = (float)c.rms_eps;
+    base.head_dim = (int)m->hd;
+    base.max_ctx = c.max_ctx;
+    base.q_rows = (int)m->qrows;
+    base.kv_rows = (int)m->kvrows;
+    base.kv_seq_stride = kv_seq_elems(m);
+    base.pos = m->d_pos;
+    base.rope_cos = m->d_cos;
+    base.rope_sin = m->d_sin;
+
+    AttnArgs at{};
+    at.q = m->d_q;
+    at.kv_seq_stride = kv_seq_elems(m);
+    at.pos = m->d_pos;
+    at.nq = (int)m->nq;
+    at.nkv = (int)m->nkv;
+    at.hd = (int)m->hd;
+    at.max_ctx = c.max_ctx;
+    at.max_chunks = m->max_chunks;
+    at.scale = (float)(1.0 / std::sqrt((double)m->hd));
+    at.part = m->d_attn_part;
+    at.counter = m->d_attn_cnt;
+    at.out = m->d_o;
+
+    if (m->streaming) {
+        for (int l = 0; l < std::min(L, 2); ++l)
+            if (!m->prefetched[l]) {
+                lm_status s = stream_copy(m, l);
+                if (s != LM_OK) return s;
+            }
+        m->prefetched[0] = m->prefetched[1] = false;
+    }
+
+    for (int l = 0; l < L; ++l) {
+        if (m->streaming) HIPTRY(m, hipStreamWaitEvent(st, m->ev_copied[l & 1], 0));
+        const uint8_t* blob = layer_blob(m, l);
+        const float* g_attn = m->d_norms + (int64_t)l * 2 * m->H;
+        const float* g_ffn = g_attn + m->H;
+        __half* kc = m->d_k + (int64_t)l * kv_layer_elems(m);
+        __half* vc = m->d_v + (int64_t)l * kv_layer_elems(m);
+        {   // RMSNorm -> QKV GEMV -> RoPE -> KV append
+            KTimer t(m, LM_K_QKV);
+            GemvArgs a = base;
+            a.w = mat_at(m, blob, M_QKV);
+            a.xin = m->d_x; a.x_stride = (int)m->H;
+            a.norm_g = g_attn;
+            a.out = m->d_q; a.out_stride = (int)m->qrows;
+            a.kcache = kc; a.vcache = vc;
+            HIPTRY(m, launch_gemv(a, EPI_QKV, n_seq, m->gemv_max_blocks, st));
+        }
+        {   // GQA attention with causal softmax
+            KTimer t(m, LM_K_ATTN);
+            AttnArgs b = at;
+            b.kcache = kc; b.vcache = vc;
+            HIPTRY(m, launch_attention(b, n_seq, st));
+        }
+        {   // x += Wo o
+            KTimer t(m, LM_K_WO);
+            GemvArgs a = base;
+            a.w = mat_at(m, blob, M_WO);
+            a.xin = m->d_o; a.x_stride = (int)m->qrows;
+            a.out = m->d_x; a.out_stride = (int)m->H;
+            HIPTRY(m, launch_gemv(a, EPI_RESID, n_seq, m->gemv_max_blocks, st));
+        }
+        {   // RMSNorm -> gate/up GEMV -> SwiGLU
+            KTimer t(m, LM_K_GATEUP);
+            GemvArgs a = base;
+            a.w = mat_at(m, blob, M_GU);
+            a.xin = m->d_x; a.x_stride = (int)m->H;
+            a.norm_g = g_ffn;
+            a.out = m->d_h; a.out_stride = (int)m->F;
+            HIPTRY(m, launch_gemv(a, EPI_SWIGLU, n_seq, m->gemv_max_blocks, st));
+        }
+        {   // x += Wdown h
+            KTimer t(m, LM_K_DOWN);
+            GemvArgs a = base;
+            a.w = mat_at(m, blob, M_DOWN);
+            a.xin = m->d_h; a.x_stride = (int)m->F;
+            a.out = m->d_x; a.out_stride = (int)m->H;
+            HIPTRY(m, launch_gemv(a, EPI_RESID, n_seq, m->gemv_max_blocks, st));
+        }
+        if (m->streaming) {
+            HIPTRY(m, hipEventRecord(m->ev_consumed[l & 1], st));
+            if (l + 2 < L) {
+                lm_status s = stream_copy(m, l + 2);
+                if (s != LM_OK) return s;
+            }
+        }
+    }
+    if (m->streaming) {
+        // start the next step's first two layers while the LM head runs
+        for (int l = 0; l < std::min(L, 2); ++l) {
+            lm_status s = stream_copy(m, l);
+            if (s != LM_OK) return s;
+            m->prefetched[l] = true;
+        }
+    }
+    {   // final RMSNorm -> LM head GEMV -> argmax (and positions += 1)
+        KTimer t(m, LM_K_LMHEAD);
+        GemvArgs a = base;
+        a.w = lm_head_mat(m);
+        a.xin = m->d_x; a.x_stride = (int)m->H;
+        a.norm_g = m->d_out_norm;
+        a.out = d_logits; a.out_stride = (int)m->V;
+        a.part_val = m->d_lm_pval;
+        a.part_idx = m->d_lm_pidx;
+        a.counter = m->d_lm_cnt;
+        a.argmax_out = d_argmax;
+        a.pos_inc = m->d_pos;
+        HIPTRY(m, launch_gemv(a, EPI_LOGITS, n_seq, m->gemv_max_blocks, st));
+    }
+    return LM_OK;
+}
+
+static lm_status run_step(lm_model* m, int n_seq, const int* d_tok, float* d_logits, int* d_argmax) {
+    const bool graph_ok = m->use_graph && !m->timing && !m->streaming;
+    if (!graph_ok) return enqueue_step(m, n_seq, d_tok, d_logits, d_argmax);
+    for (auto& g : m->graphs)
+        if (g.n_seq == n_seq && g.tok == d_tok && g.logits == d_logits && g.argmax == d_argmax) {
+            HIPTRY(m, hipGraphLaunch(g.exec, m->stream));
+            return LM_OK;
+        }
+    hipGraph_t graph = nullptr;
+    HIPTRY(m, hipStreamBeginCapture(m->stream, hipStreamCaptureModeThreadLocal));
+    lm_status s = enqueue_step(m, n_seq, d_tok, d_logits, d_argmax);
+    hipError_t e = hipStreamEndCapture(m->stream, &graph);
+    if (s != LM_OK) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return s;
+    }
+    if (e != hipSuccess) return fail(m, LM_E_HIP, "hipStreamEndCapture failed: %s", hipGetErrorString(e));
+    hipGraphExec_t exec = nullptr;
+    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (e != hipSuccess) return fail(m, LM_E_HIP, "hipGraphInstantiate failed: %s", hipGetErrorString(e));
+    if (m->graphs.size() >= 8) {
+        (void)hipGraphExecDestroy(m->graphs.front().exec);
+        m->graphs.erase(m->graphs.begin());
+    }
+    m->graphs.push_back({n_seq, d_tok, d_logits, d_argmax, exec});
+    HIPTRY(m, hipGraphLaunch(exec, m->stream));
+    return LM_OK;
+}
+
+static lm_status check_ready(lm_model* m, const char* fn, int n_seq) {
+    if (!m->global_loaded)
+        return fail(m, LM_E_STATE, "%s: global weights not loaded (lm_load_global_weights)", fn);
+    for (int l = 0; l < m->cfg.n_layers; ++l)
+        if (!m->layer_loaded[l]) return fail(m, LM_E_STATE, "%s: layer %d weights not loaded", fn, l);
+    if (n_seq < 1 || n_seq > m->cfg.max_seqs)
+        return fail(m, LM_E_ARG, "%s: n_seq = %d; expected 1..%d (max_seqs)", fn, n_seq, m->cfg.max_seqs);
+    for (int s = 0; s < n_seq; ++s)
+        if (m->pos[s] + 1 > m->cfg.max_ctx)
+            return fail(m, LM_E_CTX, "%s: sequence %d is at position %d; max_ctx = %d leaves no room for a step",
+                        fn, s, m->pos[s], m->cfg.max_ctx);
+    return LM_OK;
+}
+
+extern "C" lm_status lm_decode_step(lm_model* m, const int32_t* tokens, int32_t n_seq, float* logits,
+                                    int32_t* argmax) {
+    if (!m) return LM_E_ARG;
+    lm_status st = check_ready(m, "lm_decode_step", n_seq);
+    if (st != LM_OK) return st;
+    if (!tokens || !argmax) return fail(m, LM_E_ARG, "lm_decode_step: tokens or argmax is NULL");
+    for (int s = 0; s < n_seq; ++s)
+        if (tokens[s] < 0 || tokens[s] >= m->cfg.vocab)
+            return fail(m, LM_E_ARG, "lm_decode_step: tokens[%d] = %d; expected 0..%d", s, tokens[s],
+                        m->cfg.vocab - 1);
+    HIPTRY(m, hipMemcpyAsync(m->d_tokens, tokens, (size_t)n_seq * 4, hipMemcpyHostToDevice, m->stream));
+    st = run_step(m, n_seq, m->d_tokens, logits ? m->d_logits : nullptr, m->d_argmax);
+    if (st != LM_OK) return st;
+    for (int s = 0; s < n_seq; ++s) m->pos[s] += 1;
+    HIPTRY(m, hipMemcpyAsync(argmax, m->d_argmax, (size_t)n_seq * 4, hipMemcpyDeviceToHost, m->stream));
+    if (logits)
+        HIPTRY(m, hipMemcpyAsync(logits, m->d_logits, (size_t)(n_seq * m->V * 4), hipMemcpyDeviceToHost,
+                                 m->stream));
+    HIPTRY(m, hipStreamSynchronize(m->stream));
+    return collect_timing(m);
+}
+
+extern "C" lm_status lm_decode_step_dev(lm_model* m, const int32_t* d_tokens, int32_t n_seq, float* d_logits,
+                                        int32_t* d_argmax) {
+    if (!m) return LM_E_ARG;
+    lm_status st = check_ready(m, "lm_decode_step_dev", n_seq);
+    if (st != LM_OK) return st;
+    if (!d_tokens || !d_argmax) return fail(m, LM_E_ARG, "lm_decode_step_dev: d_tokens or d_argmax is NULL");
+    st = run_step(m, n_seq, d_tokens, d_logits, d_argmax);
+    if (st != LM_OK) return st;
+    for (int s = 0; s < n_seq; ++s) m->pos[s] += 1;
+    return LM_OK;
+}
+
+extern "C" lm_status lm_set_graph(lm_model* m, int32_t enable) {
+    if (!m) return LM_E_ARG;
+    m->use_graph = enable != 0;
+    if (!m->use_graph) {
+        HIPTRY(m, hipStreamSynchronize(m->stream));
+        invalidate_graphs(m);
+    }
+    return LM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// streaming mode
+// ---------------------------------------------------------------------------
+extern "C" lm_status lm_stream_mode(lm_model* m, int32_t enable) {
+    if (!m) return LM_E_ARG;
+    const bool want = enable != 0;
+    if (want == m->streaming) return LM_OK;
+    HIPTRY(m, hipStreamSynchronize(m->stream));
+    HIPTRY(m, hipStreamSynchronize(m->copy_stream));
+    const int64_t L = m->cfg.n_layers;
+    if (want) {
+        uint8_t* arena = nullptr;
+        uint8_t* b0 = nullptr;
+        uint8_t* b1 = nullptr;
+        lm_status st = host_alloc(m, (void**)&arena, L * m->blob_bytes, "streaming host arena");
+        if (st != LM_OK) return st;
+        st = dev_alloc(m, (void**)&b0, m->blob_bytes, "streaming buffer 0");
+        if (st == LM_OK) st = dev_alloc(m, (void**)&b1, m->blob_bytes, "streaming buffer 1");
+        if (st == LM_OK) {
+            hipError_t e = hipMemcpy(arena, m->d_layers, (size_t)(L * m->blob_bytes), hipMemcpyDeviceToHost);
+            if (e != hipSuccess) st = fail(m, LM_E_HIP, "hipMemcpy (weights to host arena) failed: %s",
+                                           hipGetErrorString(e));
+        }
+        if (st != LM_OK) {
+            host_free(m, arena);
+            dev_free(m, b0);
+            dev_free(m, b1);
+            return st;
+        }
+        dev_free(m, m->d_layers);
+        m->d_layers = nullptr;
+        m->h_arena = arena;
+        m->d_sbuf[0] = b0;
+        m->d_sbuf[1] = b1;
+        m->streaming = true;
+    } else {
+        uint8_t* d = nullptr;
+        lm_status st = dev_alloc(m, (void**)&d, L * m->blob_bytes, "layer weights");
+        if (st != LM_OK) return st;
+        hipError_t e = hipMemcpy(d, m->h_arena, (size_t)(L * m->blob_bytes), hipMemcpyHostToDevice);
+        if (e != hipSuccess) {
+            dev_free(m, d);
+            return fail(m, LM_E_HIP, "hipMemcpy (weights to HBM) failed: %s", hipGetErrorString(e));
+        }
+        host_free(m, m->h_arena);
+        dev_free(m, m->d_sbuf[0]);
+        dev_free(m, m->d_sbuf[1]);
+        m->h_arena = nullptr;
+        m->d_sbuf[0] = m->d_sbuf[1] = nullptr;
+        m->d_layers = d;
+        m->streaming = false;
+    }
+    m->prefetched[0] = m->prefetched[1] = false;
+    invalidate_graphs(m);
+    return LM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// measurement and inspection
+// ---------------------------------------------------------------------------
+extern "C" lm_status lm_kernel_timing(lm_model* m, int32_t enable) {
+    if (!m) return LM_E_ARG;
+    lm_status st = collect_timing(m);
+    if (st != LM_OK) return st;
+    m->timing = enable != 0;
+    for (int k = 0; k < LM_K_COUNT; ++k) { m->kcount[k] = 0; m->kms[k] = 0.0; }
+    return LM_OK;
+}
+
+extern "C" lm_status lm_kernel_stats(lm_model* m, int32_t kind, int64_t* count, double* total_ms) {
+    if (!m || kind < 0 || kind >= LM_K_COUNT || !count || !total_ms) return LM_E_ARG;
+    lm_status st = collect_timing(m);
+    if (st != LM_OK) return st;
+    *count = m->kcount[kind];
+    *total_ms = m->kms[kind];
+    return LM_OK;
+}
+
+extern "C" lm_status lm_kernel_bytes(const lm_model* m, int32_t kind, int32_t n_seq, double* bytes) {
+    if (!m || !bytes || kind < 0 || kind >= LM_K_COUNT || n_seq < 1 || n_seq > m->cfg.max_seqs) return LM_E_ARG;
+    const double bpw = m->cfg.qtype == LM_Q8_0 ? 34.0 / 32.0 : 18.0 / 32.0;
+    const double H = (double)m->H, F = (double)m->F, V = (double)m->V, Q = (double)m->qrows,
+                 KV = (double)m->kvrows, L = m->cfg.n_layers, S = n_seq;
+    double b = 0.0;
+    switch (kind) {
+        case LM_K_EMBED: b = S * H * (2 + 4); break;
+        case LM_K_QKV: b = L * ((Q + 2 * KV) * H * bpw + H * 4 + S * (H * 4 + Q * 4 + 2 * KV * 2)); break;
+        case LM_K_ATTN: {
+            double kv = 0.0;
+            for (int s = 0; s < n_seq; ++s) kv += (double)(m->pos[s] + 1) * KV * 2 * 2;
+            b = L * (kv + S * Q * 4 * 2);
+            break;
+        }
+        case LM_K_WO: b = L * (H * Q * bpw + S * (Q * 4 + H * 8)); break;
+        case LM_K_GATEUP: b = L * (2 * F * H * bpw + H * 4 + S * (H * 4 + F * 4)); break;
+        case LM_K_DOWN: b = L * (H * F * bpw + S * (F * 4 + H * 8)); break;
+        case LM_K_LMHEAD: b = V * H * bpw + H * 4 + S * H * 4; break;
+    }
+    *bytes = b;
+    return LM_OK;
+}
+
+extern "C" lm_status lm_debug_dequant(lm_model* m, int32_t layer, int32_t which, int32_t row0, int32_t n_rows,
+                                      float* out) {
+    if (!m || !out) return LM_E_ARG;
+    if (which < 0 || which > 7) return fail(m, LM_E_ARG, "lm_debug_dequant: which = %d; expected 0..7", which);
+    if (which < 7 && (layer < 0 || layer >= m->cfg.n_layers))
+        return fail(m, LM_E_ARG, "lm_debug_dequant: layer = %d; expected 0..%d", layer, m->cfg.n_layers - 1);
+    // (matrix, first device row, row stride, rows available)
+    int mat = -1;
+    int64_t dr0 = 0, stride = 1, avail = 0;
+    switch (which) {
+        case 0: mat = M_QKV; dr0 = 0; avail = m->qrows; break;
+        case 1: mat = M_QKV; dr0 = m->qrows; avail = m->kvrows; break;
+        case 2: mat = M_QKV; dr0 = m->qrows + m->kvrows; avail = m->kvrows; break;
+        case 3: mat = M_WO; avail = m->H; break;
+        case 4: mat = M_GU; dr0 = 0; stride = 2; avail = m->F; break;
+        case 5: mat = M_GU; dr0 = 1; stride = 2; avail = m->F; break;
+        case 6: mat = M_DOWN; avail = m->H; break;
+        default: avail = m->V; break;
+    }
+    if (row0 < 0 || n_rows < 0 || row0 + (int64_t)n_rows > avail)
+        return fail(m, LM_E_ARG, "lm_debug_dequant: rows [%d, %d) outside 0..%lld", row0, row0 + n_rows,
+                    (long long)avail);
+    HIPTRY(m, hipStreamSynchronize(m->stream));
+    HIPTRY(m, hipStreamSynchronize(m->copy_stream));
+    QMat w;
+    if (mat < 0) w = lm_head_mat(m);
+    else if (m->streaming) {
+        HIPTRY(m, hipMemcpy(m->d_sbuf[0], m->h_arena + (int64_t)layer * m->blob_bytes, (size_t)m->blob_bytes,
+                            hipMemcpyHostToDevice));
+        m->prefetched[0] = m->prefetched[1] = false;
+        w = mat_at(m, m->d_sbuf[0], mat);
+    } else {
+        w = mat_at(m, m->d_layers + (int64_t)layer * m->blob_bytes, mat);
+    }
+    const int K = w.K;
+    const int64_t per = std::max<int64_t>(1, m->dbg_floats / K);
+    std::vector<float> tmp;
+    for (int64_t r = 0; r < n_rows;) {
+        // device rows for logical rows r.. (stride 1 or 2)
+        const int64_t n = std::min<int64_t>(n_rows - r, per / stride);
+        const int64_t first = dr0 + (row0 + r) * stride;
+        const int64_t span = (n - 1) * stride + 1;
+        HIPTRY(m, launch_dequant(w, m->cfg.qtype, (int)first, (int)span, m->d_dbg, m->stream));
+        tmp.resize((size_t)(span * K));
+        HIPTRY(m, hipMemcpyAsync(tmp.data(), m->d_dbg, (size_t)(span * K * 4), hipMemcpyDeviceToHost, m->stream));
+        HIPTRY(m, hipStreamSynchronize(m->stream));
+        for (int64_t i = 0; i < n; ++i)
+            std::memcpy(out + (r + i) * K, tmp.data() + i * stride * K, (size_t)K * 4);
+        r += n;
+    }
+    return LM_OK;
+}
+
+extern "C" lm_status lm_debug_read_bw(lm_model* m, int64_t n_bytes, int32_t iters, double* ms) {
+    if (!m || !ms || iters < 1) return LM_E_ARG;
+    const uint8_t* buf = m->streaming ? nullptr : m->d_layers;
+    const int64_t avail = m->streaming ? 0 : (int64_t)m->cfg.n_layers * m->blob_bytes;
+    if (!buf || n_bytes < 16 || n_bytes > avail || n_bytes % 16)
+        return fail(m, LM_E_ARG, "lm_debug_read_bw: n_bytes = %lld; expected a multiple of 16 in 16..%lld "
+                    "(resident weight arena)", (long long)n_bytes, (long long)avail);
+    hipEvent_t a = nullptr, b = nullptr;
+    HIPTRY(m, hipEventCreate(&a));
+    HIPTRY(m, hipEventCreate(&b));
+    hipError_t e = launch_read_bw(buf, n_bytes, m->d_sink, m->stream);  // warm-up
+    if (e == hipSuccess) e = hipEventRecord(a, m->stream);
+    for (int i = 0; i < iters && e == hipSuccess; ++i) e = launch_read_bw(buf, n_bytes, m->d_sink, m->stream);
+    if (e == hipSuccess) e = hipEventRecord(b, m->stream);
+    if (e == hipSuccess) e = hipEventSynchronize(b);
+    float t = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, a, b);
+    (void)hipEventDestroy(a);
+    (void)hipEventDestroy(b);
+    if (e != hipSuccess) return fail(m, LM_E_HIP, "lm_debug_read_bw: %s", hipGetErrorString(e));
+    *ms = (double)t / iters;
+    return LM_OK;
+}
