@@ -37,15 +37,6 @@ constexpr int kWaves = kBlock / 64;
 // ---------------------------------------------------------------------------
 // helpers
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int xswz(int i) {
-    // column i -> LDS slot: block b = i/32 keeps its 32 floats, its eight
-    // 16-byte chunks are permuted by XOR with (b & 7)
-    const int b = i >> 5, j = (i >> 2) & 7;
-    return (b << 5) | ((j ^ (b & 7)) << 2) | (i & 3);
-}
-
-__device__ __forceinline__ float i8f(uint32_t v, int k) { return (float)(int8_t)(v >> (8 * k)); }
-__device__ __forceinline__ float u8f(uint32_t v, int k) { return (float)((v >> (8 * k)) & 0xFFu); }
 
 // 16-byte streaming load (weights are read once per token: non-temporal hint)
 typedef int v4i_t __attribute__((ext_vector_type(4)));
@@ -78,62 +69,52 @@ __device__ __forceinline__ void better(float& bv, int& bi, float v, int i) {
     if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
 }
 
-__device__ __forceinline__ float dot4(float4 x, float a, float b, float c, float d, float acc) {
-    acc = fmaf(a, x.x, acc);
-    acc = fmaf(b, x.y, acc);
-    acc = fmaf(c, x.z, acc);
-    acc = fmaf(d, x.w, acc);
-    return acc;
+// Activations enter the integer dot products as 24-bit fixed point: per
+// 32-column block b, X_i = rint(x_i * 127*2^16 / max|x_b|), split into three
+// balanced signed 8-bit digits X = D2*2^16 + D1*2^8 + D0 (two's-complement
+// bytes: D0 = low byte of X, D1 = low byte of (X+128)>>8, D2 = (X+2^15+128)>>16).
+// sum_i q_i x_i = sx_b * (2^16 S2 + 2^8 S1 + S0), S_k = sum_i q_i D_k,i, with
+// sx_b = max|x_b| / (127*2^16).  The S_k are exact int32 sums of v_dot4 products;
+// the only rounding is X's (relative 2^-24 of the block maximum) and the fp32
+// combination, the same order as an fp32 dot product.
+__device__ __forceinline__ int sdot4(int a, int b, int c) { return __builtin_amdgcn_sdot4(a, b, c, false); }
+
+__device__ __forceinline__ float combine_digits(int s0, int s1, int s2) {
+    return fmaf((float)(s2 * 256 + s1), 256.f, (float)s0);
 }
 
-// 32 int8 weights (two 16-byte halves) against the block's 32 activations
-__device__ __forceinline__ float dot_q8(const int4 A, const int4 B, const float* xb, int sw) {
-    const float4 x0 = *(const float4*)(xb + ((0 ^ sw) << 2));
-    const float4 x1 = *(const float4*)(xb + ((1 ^ sw) << 2));
-    const float4 x2 = *(const float4*)(xb + ((2 ^ sw) << 2));
-    const float4 x3 = *(const float4*)(xb + ((3 ^ sw) << 2));
-    const float4 x4 = *(const float4*)(xb + ((4 ^ sw) << 2));
-    const float4 x5 = *(const float4*)(xb + ((5 ^ sw) << 2));
-    const float4 x6 = *(const float4*)(xb + ((6 ^ sw) << 2));
-    const float4 x7 = *(const float4*)(xb + ((7 ^ sw) << 2));
-    const uint32_t a0 = A.x, a1 = A.y, a2 = A.z, a3 = A.w;
-    const uint32_t b0 = B.x, b1 = B.y, b2 = B.z, b3 = B.w;
-    float t0 = dot4(x0, i8f(a0, 0), i8f(a0, 1), i8f(a0, 2), i8f(a0, 3), 0.f);
-    float t1 = dot4(x1, i8f(a1, 0), i8f(a1, 1), i8f(a1, 2), i8f(a1, 3), 0.f);
-    float t2 = dot4(x2, i8f(a2, 0), i8f(a2, 1), i8f(a2, 2), i8f(a2, 3), 0.f);
-    float t3 = dot4(x3, i8f(a3, 0), i8f(a3, 1), i8f(a3, 2), i8f(a3, 3), 0.f);
-    t0 = dot4(x4, i8f(b0, 0), i8f(b0, 1), i8f(b0, 2), i8f(b0, 3), t0);
-    t1 = dot4(x5, i8f(b1, 0), i8f(b1, 1), i8f(b1, 2), i8f(b1, 3), t1);
-    t2 = dot4(x6, i8f(b2, 0), i8f(b2, 1), i8f(b2, 2), i8f(b2, 3), t2);
-    t3 = dot4(x7, i8f(b3, 0), i8f(b3, 1), i8f(b3, 2), i8f(b3, 3), t3);
-    return (t0 + t1) + (t2 + t3);
+// Q8_0 block: A = elements 0..15, B = 16..31 (int8); D = the block's digit
+// planes [D0 0..15][D0 16..31][D1 ..][D1 ..][D2 ..][D2 ..] as int4s.
+__device__ __forceinline__ float dot_q8(const int4 A, const int4 B, const int4* D) {
+    const int4 e0 = D[0], e1 = D[1], f0 = D[2], f1 = D[3], g0 = D[4], g1 = D[5];
+    int s0 = sdot4(A.x, e0.x, 0), s1 = sdot4(A.x, f0.x, 0), s2 = sdot4(A.x, g0.x, 0);
+    s0 = sdot4(A.y, e0.y, s0); s1 = sdot4(A.y, f0.y, s1); s2 = sdot4(A.y, g0.y, s2);
+    s0 = sdot4(A.z, e0.z, s0); s1 = sdot4(A.z, f0.z, s1); s2 = sdot4(A.z, g0.z, s2);
+    s0 = sdot4(A.w, e0.w, s0); s1 = sdot4(A.w, f0.w, s1); s2 = sdot4(A.w, g0.w, s2);
+    s0 = sdot4(B.x, e1.x, s0); s1 = sdot4(B.x, f1.x, s1); s2 = sdot4(B.x, g1.x, s2);
+    s0 = sdot4(B.y, e1.y, s0); s1 = sdot4(B.y, f1.y, s1); s2 = sdot4(B.y, g1.y, s2);
+    s0 = sdot4(B.z, e1.z, s0); s1 = sdot4(B.z, f1.z, s1); s2 = sdot4(B.z, g1.z, s2);
+    s0 = sdot4(B.w, e1.w, s0); s1 = sdot4(B.w, f1.w, s1); s2 = sdot4(B.w, g1.w, s2);
+    return combine_digits(s0, s1, s2);
 }
 
-// 32 4-bit weights (16 bytes, GGUF nibble order) against the block's
-// activations; returns sum(n_j * x_j), the caller subtracts 8 * sum(x)
-__device__ __forceinline__ float dot_q4(const int4 A, const float* xb, int sw) {
-    const float4 x0 = *(const float4*)(xb + ((0 ^ sw) << 2));
-    const float4 x1 = *(const float4*)(xb + ((1 ^ sw) << 2));
-    const float4 x2 = *(const float4*)(xb + ((2 ^ sw) << 2));
-    const float4 x3 = *(const float4*)(xb + ((3 ^ sw) << 2));
-    const float4 x4 = *(const float4*)(xb + ((4 ^ sw) << 2));
-    const float4 x5 = *(const float4*)(xb + ((5 ^ sw) << 2));
-    const float4 x6 = *(const float4*)(xb + ((6 ^ sw) << 2));
-    const float4 x7 = *(const float4*)(xb + ((7 ^ sw) << 2));
-    const uint32_t w0 = A.x, w1 = A.y, w2 = A.z, w3 = A.w;
-    const uint32_t l0 = w0 & 0x0F0F0F0Fu, h0 = (w0 >> 4) & 0x0F0F0F0Fu;
-    const uint32_t l1 = w1 & 0x0F0F0F0Fu, h1 = (w1 >> 4) & 0x0F0F0F0Fu;
-    const uint32_t l2 = w2 & 0x0F0F0F0Fu, h2 = (w2 >> 4) & 0x0F0F0F0Fu;
-    const uint32_t l3 = w3 & 0x0F0F0F0Fu, h3 = (w3 >> 4) & 0x0F0F0F0Fu;
-    float t0 = dot4(x0, u8f(l0, 0), u8f(l0, 1), u8f(l0, 2), u8f(l0, 3), 0.f);
-    float t1 = dot4(x1, u8f(l1, 0), u8f(l1, 1), u8f(l1, 2), u8f(l1, 3), 0.f);
-    float t2 = dot4(x2, u8f(l2, 0), u8f(l2, 1), u8f(l2, 2), u8f(l2, 3), 0.f);
-    float t3 = dot4(x3, u8f(l3, 0), u8f(l3, 1), u8f(l3, 2), u8f(l3, 3), 0.f);
-    t0 = dot4(x4, u8f(h0, 0), u8f(h0, 1), u8f(h0, 2), u8f(h0, 3), t0);
-    t1 = dot4(x5, u8f(h1, 0), u8f(h1, 1), u8f(h1, 2), u8f(h1, 3), t1);
-    t2 = dot4(x6, u8f(h2, 0), u8f(h2, 1), u8f(h2, 2), u8f(h2, 3), t2);
-    t3 = dot4(x7, u8f(h3, 0), u8f(h3, 1), u8f(h3, 2), u8f(h3, 3), t3);
-    return (t0 + t1) + (t2 + t3);
+// Q4_0 block: 16 bytes, byte j = element j (low nibble) | element j+16 (high).
+// The nibbles n = q + 8 enter the dot products unsigned; T = the block's digit
+// sums (T0, T1, T2) remove the 8 offset.
+__device__ __forceinline__ float dot_q4(const int4 A, const int4* D, const int4 T) {
+    const int4 e0 = D[0], e1 = D[1], f0 = D[2], f1 = D[3], g0 = D[4], g1 = D[5];
+    const int w[4] = {A.x, A.y, A.z, A.w};
+    const int E0[4] = {e0.x, e0.y, e0.z, e0.w}, E1[4] = {e1.x, e1.y, e1.z, e1.w};
+    const int F0[4] = {f0.x, f0.y, f0.z, f0.w}, F1[4] = {f1.x, f1.y, f1.z, f1.w};
+    const int G0[4] = {g0.x, g0.y, g0.z, g0.w}, G1[4] = {g1.x, g1.y, g1.z, g1.w};
+    int s0 = -8 * T.x, s1 = -8 * T.y, s2 = -8 * T.z;
+    #pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int lo = w[u] & 0x0F0F0F0F, hi = (int)(((unsigned)w[u] >> 4) & 0x0F0F0F0Fu);
+        s0 = sdot4(lo, E0[u], s0); s1 = sdot4(lo, F0[u], s1); s2 = sdot4(lo, G0[u], s2);
+        s0 = sdot4(hi, E1[u], s0); s1 = sdot4(hi, F1[u], s1); s2 = sdot4(hi, G1[u], s2);
+    }
+    return combine_digits(s0, s1, s2);
 }
 
 __device__ __forceinline__ float block_sum(float v, float* red) {
@@ -181,7 +162,7 @@ hipError_t launch_embed(const uint16_t* tok_embd, const int* tokens, int vocab, 
 // Tuning knobs (compile-time): blocks per lane per pipeline stage, and
 // whether weight loads carry the non-temporal hint.
 #ifndef LMK_CB_Q8
-#define LMK_CB_Q8 2
+#define LMK_CB_Q8 1
 #endif
 #ifndef LMK_CB_Q4
 #define LMK_CB_Q4 4
@@ -189,6 +170,56 @@ hipError_t launch_embed(const uint16_t* tok_embd, const int* tokens, int vocab, 
 #ifndef LMK_WEIGHT_NT
 #define LMK_WEIGHT_NT 1
 #endif
+
+// Reductions over the 8 lanes i..i|7 with DPP moves (no LDS round trip):
+// xor 1 and xor 2 inside a quad, then the mirror inside each half row (lane
+// i <-> 7 - i) brings the other quad's result.
+__device__ __forceinline__ float max8(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));  // quad_perm [1,0,3,2]
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));  // quad_perm [2,3,0,1]
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false))); // row_half_mirror
+    return v;
+}
+__device__ __forceinline__ int sum8(int v) {
+    v += __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
+    v += __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
+    v += __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);
+    return v;
+}
+
+// Four consecutive activations (columns i..i+3 of a 32-column block) -> their
+// three digit bytes; the block maximum comes from the 8 lanes sharing the block.
+__device__ __forceinline__ void stage_digits(float4 v, int i, int K, int8_t* xq, float* xsc, int4* dsum,
+                                             bool sums) {
+    const float m = max8(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    if (i >= K) return;
+    const float f = m > 0.f ? 8323072.0f / m : 0.f;       // 127 * 2^16 / max|x_b|
+    const int X[4] = {(int)rintf(v.x * f), (int)rintf(v.y * f), (int)rintf(v.z * f), (int)rintf(v.w * f)};
+    uint32_t w0 = 0, w1 = 0, w2 = 0;
+    int t0 = 0, t1 = 0, t2 = 0;
+    #pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int x1 = (X[e] + 128) >> 8, x2 = (x1 + 128) >> 8;
+        w0 |= (uint32_t)(X[e] & 255) << (8 * e);
+        w1 |= (uint32_t)(x1 & 255) << (8 * e);
+        w2 |= (uint32_t)(x2 & 255) << (8 * e);
+        t0 += (int)(int8_t)(X[e] & 255);
+        t1 += (int)(int8_t)(x1 & 255);
+        t2 += x2;
+    }
+    const int b = i >> 5, j = (i >> 2) & 7;
+    int* dst = (int*)(xq + b * 96);
+    dst[j] = (int)w0;
+    dst[8 + j] = (int)w1;
+    dst[16 + j] = (int)w2;
+    if (j == 0) xsc[b] = m * (1.0f / 8323072.0f);
+    if (sums) {
+        t0 = sum8(t0);
+        t1 = sum8(t1);
+        t2 = sum8(t2);
+        if (j == 0) dsum[b] = make_int4(t0, t1, t2, 0);
+    }
+}
 
 // Weight blocks one lane loads per pipeline stage (per row of its row pair).
 template <int QT> struct ChunkBlocks { static constexpr int value = LMK_CB_Q8; };
@@ -220,9 +251,14 @@ __global__ __launch_bounds__(kBlock, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a
     constexpr int kRowsPerStep = 2 * kGroups;
 
     const int K = a.w.K, N = a.w.N, nb = K >> 5;
-    float* xs = smem;            // K floats, swizzled
-    float* bsum = smem + K;      // nb block sums (Q4_0)
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // LDS: per 32-column block, the activation digit planes (96 bytes), its
+    // scale, and (Q4_0) the digit sums
+    int8_t* xq = (int8_t*)smem;                       // [nb][3][32] int8
+    float* xsc = (float*)(xq + nb * 96);              // [nb]
+    int4* dsum = (int4*)(xsc + ((nb + 3) & ~3));      // [nb] (T0, T1, T2, 0)
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave-uniform by construction; readfirstlane lets the row bases live in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int s = blockIdx.y;
     const float* x = a.xin + (int64_t)s * a.x_stride;
     const int rg = lane / LPR, li = lane % LPR;
@@ -263,15 +299,15 @@ __global__ __launch_bounds__(kBlock, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a
         #pragma unroll
         for (int u = 0; u < CB; ++u) {
             const int b = li + LPR * (k * CB + u);
-            const int bc = min(b, nb - 1);
-            w.a0[u] = ld16_stream(q0 + bc * 16);
-            w.a1[u] = ld16_stream(q1 + bc * 16);
+            const uint32_t bc = (uint32_t)min(b, nb - 1);   // unsigned 32-bit offsets: scalar base + vector offset
+            w.a0[u] = ld16_stream(q0 + bc * 16u);
+            w.a1[u] = ld16_stream(q1 + bc * 16u);
             if (QT == kQ8_0) {
-                w.b0[u] = ld16_stream(q0 + (int64_t)nb * 16 + bc * 16);
-                w.b1[u] = ld16_stream(q1 + (int64_t)nb * 16 + bc * 16);
+                w.b0[u] = ld16_stream(q0 + (uint32_t)nb * 16u + bc * 16u);
+                w.b1[u] = ld16_stream(q1 + (uint32_t)nb * 16u + bc * 16u);
             }
             w.d0[u] = s0[bc];          // used only in compute(): consuming a load here
-            w.d1[u] = s0[nb + bc];     // would wait on every load issued before it
+            w.d1[u] = s0[(uint32_t)nb + bc];     // would wait on every load issued before it
         }
     };
 
@@ -284,15 +320,15 @@ __global__ __launch_bounds__(kBlock, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a
             const int b = min(braw, nb - 1);
             const float d0 = braw < nb ? h2f(w.d0[u]) : 0.f;   // past the row end: no contribution
             const float d1 = braw < nb ? h2f(w.d1[u]) : 0.f;
-            const float* xb = xs + (b << 5);
-            const int sw = b & 7;
+            const int4* D = (const int4*)(xq + b * 96);
+            const float sx = xsc[b];
             if (QT == kQ8_0) {
-                acc0 = fmaf(d0, dot_q8(w.a0[u], w.b0[u], xb, sw), acc0);
-                acc1 = fmaf(d1, dot_q8(w.a1[u], w.b1[u], xb, sw), acc1);
+                acc0 = fmaf(d0 * sx, dot_q8(w.a0[u], w.b0[u], D), acc0);
+                acc1 = fmaf(d1 * sx, dot_q8(w.a1[u], w.b1[u], D), acc1);
             } else {
-                const float c8 = 8.f * bsum[b];
-                acc0 = fmaf(d0, dot_q4(w.a0[u], xb, sw) - c8, acc0);
-                acc1 = fmaf(d1, dot_q4(w.a1[u], xb, sw) - c8, acc1);
+                const int4 T = dsum[b];
+                acc0 = fmaf(d0 * sx, dot_q4(w.a0[u], D, T), acc0);
+                acc1 = fmaf(d1 * sx, dot_q4(w.a1[u], D, T), acc1);
             }
         }
     };
@@ -373,7 +409,8 @@ __global__ __launch_bounds__(kBlock, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a
         if (has_g) gr[u] = *(const float4*)(a.norm_g + i);
     }
     WChunk<QT> wa, wb;
-    load(0, wa);          // unconditional: rows are clamped, so this is always in bounds
+    load(0, wa);          // unconditional: rows are clamped, so these are always in bounds
+    load(1, wb);
 
     float ss = 0.f;
     for (int base = 0; base < K; base += kXr * kBlock * 4) {
@@ -387,60 +424,56 @@ __global__ __launch_bounds__(kBlock, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a
         }
         #pragma unroll
         for (int u = 0; u < kXr; ++u) {
+            // the 8 threads tid..tid|7 hold one 32-column block (K % 32 == 0, so a
+            // block is either wholly inside K or wholly past it: uniform per group)
             const int i = base + (tid + u * kBlock) * 4;
-            if (i < K) {
-                float4 v = xr[u];
-                if (has_g) {
+            float4 v = xr[u];
+            if (has_g) {
+                if (i < K) {
                     ss = fmaf(v.x, v.x, ss);
                     ss = fmaf(v.y, v.y, ss);
                     ss = fmaf(v.z, v.z, ss);
                     ss = fmaf(v.w, v.w, ss);
-                    v.x *= gr[u].x;
-                    v.y *= gr[u].y;
-                    v.z *= gr[u].z;
-                    v.w *= gr[u].w;
                 }
-                *(float4*)(xs + xswz(i)) = v;
+                v.x *= gr[u].x;
+                v.y *= gr[u].y;
+                v.z *= gr[u].z;
+                v.w *= gr[u].w;
             }
+            stage_digits(v, i, K, xq, xsc, dsum, QT == kQ4_0);
         }
     }
     // block_sum's barriers also order the LDS stores above before any reads
     if (has_g) rscale = 1.0f / sqrtf(block_sum(ss, red) / (float)K + a.eps);
     __syncthreads();
-    if (QT == kQ4_0) {
-        for (int b = tid; b < nb; b += kBlock) {
-            const float* xb = xs + (b << 5);
-            float t = 0.f;
-            #pragma unroll
-            for (int e = 0; e < 32; ++e) t += xb[e];
-            bsum[b] = t;
-        }
-        __syncthreads();
-    }
 
-    // ---- two-stage pipeline: chunk c+1's loads are in flight while c computes.
-    // The steady-state body issues its loads unconditionally (exact load
-    // counters); the last one or two chunks are peeled off.
+    // ---- pipeline: a chunk's registers are refilled (chunk c+2) as soon as
+    // chunk c has been consumed, before c's cross-lane reduction and
+    // epilogue, so two chunks stay in flight.  The steady-state body issues
+    // its loads unconditionally (exact load counters); the tail is peeled.
     int c = 0;
-    for (; c + 2 < n_chunks; c += 2) {
-        load(c + 1, wb);
+    for (; c + 3 < n_chunks; c += 2) {
         compute(c, wa);
-        finish(c);
         load(c + 2, wa);
+        finish(c);
         compute(c + 1, wb);
+        load(c + 3, wb);
         finish(c + 1);
+    }
+    // at most three chunks left: c (in wa), c+1 (in wb), c+2 (not loaded)
+    if (c < n_chunks) {
+        compute(c, wa);
+        if (c + 2 < n_chunks) load(c + 2, wa);
+        finish(c);
     }
     if (c + 1 < n_chunks) {
-        load(c + 1, wb);
-        compute(c, wa);
-        finish(c);
         compute(c + 1, wb);
         finish(c + 1);
-    } else if (c < n_chunks) {
-        compute(c, wa);
-        finish(c);
     }
-
+    if (c + 2 < n_chunks) {
+        compute(c + 2, wa);
+        finish(c + 2);
+    }
     if (EPI == EPI_LOGITS) {
         // workgroup maximum, then the last workgroup of the sequence reduces
         #pragma unroll
@@ -495,9 +528,7 @@ static int pick_lpr(int nb) {
     return 8;
 }
 
-template <int QT, int LPR, int EPI>
-static int resident_blocks(size_t lds) {
-    // workgroups of this instantiation that fit on the whole device at once
+static int device_cus() {
     static int cached_cus = 0;
     if (!cached_cus) {
         int dev = 0;
@@ -505,23 +536,41 @@ static int resident_blocks(size_t lds) {
             hipDeviceGetAttribute(&cached_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             cached_cus = 256;
     }
+    return cached_cus;
+}
+
+template <int QT, int LPR, int EPI>
+static int resident_blocks(size_t lds) {
+    // workgroups of this instantiation that fit on the whole device at once
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemv<QT, LPR, EPI>, kBlock, lds) != hipSuccess ||
         per_cu < 1)
         per_cu = 1;
-    return per_cu * cached_cus;
+    return per_cu * device_cus();
 }
 
 template <int QT, int LPR, int EPI>
 static hipError_t launch_one(const GemvArgs& a, int n_seq, int max_blocks, size_t lds, hipStream_t st) {
     constexpr int rows_per_step = 2 * (64 / LPR);
     const int n_steps = (a.w.N + rows_per_step - 1) / rows_per_step;
-    int g = (n_steps + kWaves - 1) / kWaves;
+    const int need = (n_steps + kWaves - 1) / kWaves;
+    const int cus = device_cus();
     const int cap = std::min(max_blocks, resident_blocks<QT, LPR, EPI>(lds));
-    if (g > cap) {
-        // equal work per workgroup: the fewest blocks that keep the grid-stride rounds balanced
-        const int rounds = (g + cap - 1) / cap;
-        g = (g + rounds - 1) / rounds;
+    int g = need;
+    if (need > cap) {
+        // Several rounds per wavefront.  Busiest CU decides: cost = (row-pair rounds
+        // per wavefront) x (workgroups on the busiest CU), over whole multiples of the
+        // CU count.  Measured on gfx950: beyond two workgroups per CU a long GEMV
+        // slows down (the 128256-row LM head: 101 us at 1-2 per CU, 131 us at 3-4),
+        // so at most two.
+        int64_t best = -1;
+        for (int per = 1; per <= 2 && per * cus <= cap; ++per) {
+            const int cand = per * cus;
+            const int64_t rounds = ((int64_t)n_steps + (int64_t)cand * kWaves - 1) / ((int64_t)cand * kWaves);
+            const int64_t cost = rounds * per;
+            if (best < 0 || cost <= best) { best = cost; g = cand; }
+        }
+        if (best < 0) g = cap;
     }
     if (g < 1) g = 1;
     hipLaunchKernelGGL((k_gemv<QT, LPR, EPI>), dim3(g, n_seq), dim3(kBlock), lds, st, a);
@@ -553,150 +602,188 @@ static hipError_t launch_gemv_epi(const GemvArgs& a, int epi, int lpr, int n_seq
 hipError_t launch_gemv(const GemvArgs& a, int epi, int n_seq, int max_blocks, hipStream_t st) {
     const int nb = a.w.K / 32;
     const int lpr = pick_lpr(nb);
-    const size_t lds = (size_t)(a.w.K + (a.qtype == kQ4_0 ? nb : 0)) * sizeof(float);
+    const size_t lds = (size_t)nb * 96 + (size_t)((nb + 3) & ~3) * 4 + (a.qtype == kQ4_0 ? (size_t)nb * 16 : 0);
     if (a.qtype == kQ8_0) return launch_gemv_epi<kQ8_0>(a, epi, lpr, n_seq, max_blocks, lds, st);
     return launch_gemv_epi<kQ4_0>(a, epi, lpr, n_seq, max_blocks, lds, st);
 }
 
 // ---------------------------------------------------------------------------
-// GQA decode attention, split over context, combined by the last workgroup
+// GQA decode attention with causal softmax, split over context
 // ---------------------------------------------------------------------------
 constexpr int kMaxGroup = 8;   // query heads per KV head
 
+// Phase 1: one workgroup per (64-position chunk, KV head, sequence).  The
+// chunk's K/V tile and the group's q are requested before the position is
+// known (rows clamped to the cache), staged in LDS, and every query head of
+// the group is scored against the tile (causal mask: keys 0..pos).  Writes
+// the chunk's softmax state: row max m, sum l = sum exp(s - m), and the
+// unnormalised o = sum exp(s - m) v.
 template <int HD>
 __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
     constexpr int CH = kAttnChunk;
-    __shared__ __align__(16) __half Ks[CH][HD + 2];   // +2 halves: row stride of an odd word count
+    constexpr int KP = HD + 8;   // K row stride in halves: 16-byte aligned, conflict-free 16-byte reads
+    __shared__ __align__(16) __half Ks[CH][KP];
     __shared__ __align__(16) __half Vs[CH][HD];
     __shared__ __align__(16) float Qs[kMaxGroup][HD];
     __shared__ __align__(16) float Ps[kMaxGroup][CH];
-    __shared__ int s_last;
+    __shared__ __align__(16) float Os[kWaves][kMaxGroup * HD];
 
     const int chunk = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int G = a.nq / a.nkv;
-    const int n_ctx = a.pos[s] + 1;                 // keys 0..pos inclusive
     const int t0 = chunk * CH;
     const int64_t stride = HD + 2;
+
+    // ---- loads (independent of the position)
+    const __half* Kg = a.kcache + (int64_t)s * a.kv_seq_stride + (int64_t)g * a.max_ctx * HD;
+    const __half* Vg = a.vcache + (int64_t)s * a.kv_seq_stride + (int64_t)g * a.max_ctx * HD;
+    constexpr int kPer = CH * (HD / 8) / kBlock;     // 16-byte pieces per thread
+    uint4 kr[kPer], vr[kPer];
+    #pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const int c = tid + u * kBlock;
+        const int t = min(t0 + c / (HD / 8), a.max_ctx - 1), d8 = (c % (HD / 8)) * 8;
+        kr[u] = *(const uint4*)(Kg + (int64_t)t * HD + d8);
+        vr[u] = *(const uint4*)(Vg + (int64_t)t * HD + d8);
+    }
+    const float* qg = a.q + (int64_t)s * a.nq * HD + (int64_t)g * G * HD;
+    constexpr int kQ = (kMaxGroup * HD / 4 + kBlock - 1) / kBlock;  // float4 pieces of q per thread
+    float4 qv[kQ];
+    #pragma unroll
+    for (int u = 0; u < kQ; ++u) {
+        const int i = min((tid + u * kBlock) * 4, G * HD - 4);
+        qv[u] = *(const float4*)(qg + i);
+    }
+    const int n_ctx = a.pos[s] + 1;                 // keys 0..pos inclusive
+    if (t0 >= n_ctx) return;                        // chunk past the causal horizon
+    const int nt = min(CH, n_ctx - t0);
+
+    #pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const int c = tid + u * kBlock;
+        const int t = c / (HD / 8), d8 = (c % (HD / 8)) * 8;
+        *(uint4*)&Ks[t][d8] = kr[u];
+        *(uint4*)&Vs[t][d8] = vr[u];
+    }
+    #pragma unroll
+    for (int u = 0; u < kQ; ++u) {
+        const int i = (tid + u * kBlock) * 4;
+        if (i < G * HD) *(float4*)&Qs[i / HD][i % HD] = qv[u];
+    }
+    __syncthreads();
+
     float* part_s = a.part + (int64_t)s * a.nq * a.max_chunks * stride;
-
-    if (t0 < n_ctx) {
-        const int nt = min(CH, n_ctx - t0);
-        const __half* Kg = a.kcache + (int64_t)s * a.kv_seq_stride + ((int64_t)g * a.max_ctx + t0) * HD;
-        const __half* Vg = a.vcache + (int64_t)s * a.kv_seq_stride + ((int64_t)g * a.max_ctx + t0) * HD;
-        // every 16-byte load of the tile (and q) is issued before any is used
-        constexpr int kPer = CH * (HD / 8) / kBlock;     // 16-byte pieces per thread
-        uint4 kr[kPer], vr[kPer];
-        #pragma unroll
-        for (int u = 0; u < kPer; ++u) {
-            const int c = tid + u * kBlock;
-            const int t = c / (HD / 8), d8 = (c % (HD / 8)) * 8;
-            if (t < nt) {
-                kr[u] = *(const uint4*)(Kg + (int64_t)t * HD + d8);
-                vr[u] = *(const uint4*)(Vg + (int64_t)t * HD + d8);
+    // ---- scores: a wavefront per query head, a lane per key
+    for (int j = wave; j < G; j += kWaves) {
+        float sc = -FLT_MAX;
+        if (lane < nt) {
+            float acc0 = 0.f, acc1 = 0.f;
+            #pragma unroll
+            for (int d = 0; d < HD; d += 8) {
+                const uint4 kk = *(const uint4*)&Ks[lane][d];
+                const float4 q0 = *(const float4*)&Qs[j][d];
+                const float4 q1 = *(const float4*)&Qs[j][d + 4];
+                const float2 k01 = __half22float2(*(const __half2*)&kk.x);
+                const float2 k23 = __half22float2(*(const __half2*)&kk.y);
+                const float2 k45 = __half22float2(*(const __half2*)&kk.z);
+                const float2 k67 = __half22float2(*(const __half2*)&kk.w);
+                acc0 = fmaf(q0.x, k01.x, acc0);
+                acc1 = fmaf(q0.y, k01.y, acc1);
+                acc0 = fmaf(q0.z, k23.x, acc0);
+                acc1 = fmaf(q0.w, k23.y, acc1);
+                acc0 = fmaf(q1.x, k45.x, acc0);
+                acc1 = fmaf(q1.y, k45.y, acc1);
+                acc0 = fmaf(q1.z, k67.x, acc0);
+                acc1 = fmaf(q1.w, k67.y, acc1);
             }
+            sc = (acc0 + acc1) * a.scale;
         }
-        const float* qg = a.q + (int64_t)s * a.nq * HD + (int64_t)g * G * HD;
-        float qv[kMaxGroup * HD / kBlock];
-        #pragma unroll
-        for (int u = 0; u < kMaxGroup * HD / kBlock; ++u) {
-            const int i = tid + u * kBlock;
-            if (i < G * HD) qv[u] = qg[i];
-        }
-        #pragma unroll
-        for (int u = 0; u < kPer; ++u) {
-            const int c = tid + u * kBlock;
-            const int t = c / (HD / 8), d8 = (c % (HD / 8)) * 8;
-            if (t < nt) {
-                uint32_t* kd = (uint32_t*)&Ks[t][d8];
-                kd[0] = kr[u].x; kd[1] = kr[u].y; kd[2] = kr[u].z; kd[3] = kr[u].w;
-                *(uint4*)&Vs[t][d8] = vr[u];
-            }
-        }
-        #pragma unroll
-        for (int u = 0; u < kMaxGroup * HD / kBlock; ++u) {
-            const int i = tid + u * kBlock;
-            if (i < G * HD) Qs[i / HD][i % HD] = qv[u];
-        }
-        __syncthreads();
-
-        // scores and the chunk's softmax state, one head per wavefront pass
-        for (int j = wave; j < G; j += kWaves) {
-            float sc = -FLT_MAX;
-            if (lane < nt) {
-                float acc0 = 0.f, acc1 = 0.f;
-                #pragma unroll 8
-                for (int d = 0; d < HD; d += 2) {
-                    const float2 kk = __half22float2(*(const __half2*)&Ks[lane][d]);
-                    acc0 = fmaf(Qs[j][d], kk.x, acc0);
-                    acc1 = fmaf(Qs[j][d + 1], kk.y, acc1);
-                }
-                sc = (acc0 + acc1) * a.scale;
-            }
-            const float m = wave_max(sc);
-            const float p = lane < nt ? __expf(sc - m) : 0.f;
-            const float l = wave_sum(p);
-            Ps[j][lane] = p;
-            if (lane == 0) {
-                float* ph = part_s + ((int64_t)(g * G + j) * a.max_chunks + chunk) * stride;
-                ph[HD] = m;
-                ph[HD + 1] = l;
-            }
-        }
-        __syncthreads();
-        for (int i = tid; i < G * HD; i += kBlock) {
-            const int j = i / HD, d = i % HD;
-            float o0 = 0.f, o1 = 0.f;
-            int t = 0;
-            for (; t + 1 < nt; t += 2) {
-                o0 = fmaf(Ps[j][t], __half2float(Vs[t][d]), o0);
-                o1 = fmaf(Ps[j][t + 1], __half2float(Vs[t + 1][d]), o1);
-            }
-            if (t < nt) o0 = fmaf(Ps[j][t], __half2float(Vs[t][d]), o0);
-            part_s[((int64_t)(g * G + j) * a.max_chunks + chunk) * stride + d] = o0 + o1;
+        const float m = wave_max(sc);
+        const float p = lane < nt ? __expf(sc - m) : 0.f;
+        const float l = wave_sum(p);
+        Ps[j][lane] = p;
+        if (lane == 0) {
+            float* ph = part_s + ((int64_t)(g * G + j) * a.max_chunks + chunk) * stride;
+            ph[HD] = m;
+            ph[HD + 1] = l;
         }
     }
+    __syncthreads();
 
-    // completion count; the last workgroup of (s, g) merges the chunks.  The
-    // barrier completes every thread's stores; one agent-scope fence per
-    // workgroup then publishes them before the counter moves.
-    __syncthreads();
-    if (tid == 0) {
-        __threadfence();
-        const int old = atomicAdd(&a.counter[s * a.nkv + g], 1);
-        s_last = (old == (int)gridDim.x - 1);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    if (tid == 0) __threadfence();
-    __syncthreads();
-    const int n_act = (n_ctx + CH - 1) / CH;
-    for (int i = tid; i < G * HD; i += kBlock) {
-        const int j = i / HD, d = i % HD;
-        const int h = g * G + j;
-        const float* ph = part_s + (int64_t)h * a.max_chunks * stride;
-        // one pass with running rescaling: (M, L, O) merge chunk by chunk
-        float M = -FLT_MAX, L = 0.f, O = 0.f;
-        for (int c = 0; c < n_act; ++c) {
-            const float mc = ph[c * stride + HD];
-            const float lc = ph[c * stride + HD + 1];
-            const float oc = ph[c * stride + d];
-            const float Mn = fmaxf(M, mc);
-            const float r = __expf(M - Mn), e = __expf(mc - Mn);
-            L = fmaf(L, r, lc * e);
-            O = fmaf(O, r, oc * e);
-            M = Mn;
+    // ---- o = sum_t p_t v_t: thread (head j, 8 dims, quarter of the keys)
+    constexpr int D8 = HD / 8;
+    for (int idx = tid; idx < G * D8 * kWaves; idx += kBlock) {
+        const int w = idx / (G * D8), r = idx % (G * D8);
+        const int j = r / D8, d8 = (r % D8) * 8;
+        float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        const int tb = w * (CH / kWaves), te = min(tb + CH / kWaves, nt);
+        for (int t = tb; t < te; ++t) {
+            const float pt = Ps[j][t];
+            const uint4 vv = *(const uint4*)&Vs[t][d8];
+            const float2 v01 = __half22float2(*(const __half2*)&vv.x);
+            const float2 v23 = __half22float2(*(const __half2*)&vv.y);
+            const float2 v45 = __half22float2(*(const __half2*)&vv.z);
+            const float2 v67 = __half22float2(*(const __half2*)&vv.w);
+            o[0] = fmaf(pt, v01.x, o[0]);
+            o[1] = fmaf(pt, v01.y, o[1]);
+            o[2] = fmaf(pt, v23.x, o[2]);
+            o[3] = fmaf(pt, v23.y, o[3]);
+            o[4] = fmaf(pt, v45.x, o[4]);
+            o[5] = fmaf(pt, v45.y, o[5]);
+            o[6] = fmaf(pt, v67.x, o[6]);
+            o[7] = fmaf(pt, v67.y, o[7]);
         }
-        a.out[(int64_t)s * a.nq * HD + (int64_t)h * HD + d] = O / L;
+        float* dst = &Os[w][j * HD + d8];
+        *(float4*)dst = make_float4(o[0], o[1], o[2], o[3]);
+        *(float4*)(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
     }
-    if (tid == 0) a.counter[s * a.nkv + g] = 0;
+    __syncthreads();
+    for (int i = tid; i < G * HD / 4; i += kBlock) {
+        float4 v = *(const float4*)&Os[0][i * 4];
+        #pragma unroll
+        for (int w = 1; w < kWaves; ++w) {
+            const float4 u = *(const float4*)&Os[w][i * 4];
+            v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+        }
+        const int j = (i * 4) / HD, d = (i * 4) % HD;
+        float* ph = part_s + ((int64_t)(g * G + j) * a.max_chunks + chunk) * stride + d;
+        ph[0] = v.x; ph[1] = v.y; ph[2] = v.z; ph[3] = v.w;
+    }
+}
+
+// Phase 2: merge the chunks of each (sequence, query head): with
+// M = max_c m_c, o = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c.
+// A thread per output element; the loads of all chunks are independent.
+template <int HD>
+__global__ __launch_bounds__(HD) void k_attn_merge(AttnArgs a) {
+    const int h = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
+    const int64_t stride = HD + 2;
+    const int n_act = (a.pos[s] + 1 + kAttnChunk - 1) / kAttnChunk;
+    const float* ph = a.part + ((int64_t)s * a.nq + h) * a.max_chunks * stride;
+    float M = -FLT_MAX;
+    for (int c = 0; c < n_act; ++c) M = fmaxf(M, ph[c * stride + HD]);
+    float L = 0.f, O = 0.f;
+    #pragma unroll 4
+    for (int c = 0; c < n_act; ++c) {
+        const float e = __expf(ph[c * stride + HD] - M);
+        L = fmaf(ph[c * stride + HD + 1], e, L);
+        O = fmaf(ph[c * stride + d], e, O);
+    }
+    a.out[(int64_t)s * a.nq * HD + (int64_t)h * HD + d] = O / L;
 }
 
 hipError_t launch_attention(const AttnArgs& a, int n_seq, hipStream_t st) {
     dim3 grid(a.max_chunks, a.nkv, n_seq);
-    if (a.hd == 128) hipLaunchKernelGGL(k_attn<128>, grid, dim3(kBlock), 0, st, a);
-    else if (a.hd == 64) hipLaunchKernelGGL(k_attn<64>, grid, dim3(kBlock), 0, st, a);
-    else return hipErrorInvalidValue;
+    dim3 mgrid(a.nq, n_seq);
+    if (a.hd == 128) {
+        hipLaunchKernelGGL(k_attn<128>, grid, dim3(kBlock), 0, st, a);
+        hipLaunchKernelGGL(k_attn_merge<128>, mgrid, dim3(128), 0, st, a);
+    } else if (a.hd == 64) {
+        hipLaunchKernelGGL(k_attn<64>, grid, dim3(kBlock), 0, st, a);
+        hipLaunchKernelGGL(k_attn_merge<64>, mgrid, dim3(64), 0, st, a);
+    } else {
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -116,7 +116,6 @@ struct lm_model {
     int *d_tokens = nullptr, *d_argmax = nullptr, *d_pos = nullptr;
     float *d_cos = nullptr, *d_sin = nullptr;
     float* d_attn_part = nullptr;
-    int* d_attn_cnt = nullptr;
     float* d_lm_pval = nullptr;
     int* d_lm_pidx = nullptr;
     int* d_lm_cnt = nullptr;
@@ -418,7 +417,6 @@ extern "C" lm_status lm_model_create(const lm_config* cfg, void* hip_stream, lm_
     CREATE_TRY(dev_alloc(m, (void**)&m->d_sin, (int64_t)c.max_ctx * (m->hd / 2) * 4, "rope sin"));
     CREATE_TRY(dev_alloc(m, (void**)&m->d_attn_part,
                          (int64_t)S * m->nq * m->max_chunks * (m->hd + 2) * 4, "attention partials"));
-    CREATE_TRY(dev_alloc(m, (void**)&m->d_attn_cnt, (int64_t)S * m->nkv * 4, "attention counters"));
     CREATE_TRY(dev_alloc(m, (void**)&m->d_lm_pval, (int64_t)S * m->gemv_max_blocks * 4, "argmax partials"));
     CREATE_TRY(dev_alloc(m, (void**)&m->d_lm_pidx, (int64_t)S * m->gemv_max_blocks * 4, "argmax partial ids"));
     CREATE_TRY(dev_alloc(m, (void**)&m->d_lm_cnt, (int64_t)S * 4, "argmax counters"));
@@ -430,7 +428,6 @@ extern "C" lm_status lm_model_create(const lm_config* cfg, void* hip_stream, lm_
     CREATE_TRY(host_alloc(m, (void**)&m->h_stage, m->stage_bytes, "upload staging"));
 
     // zero what must start at zero (counters, caches, positions)
-    CREATE_HIP(hipMemsetAsync(m->d_attn_cnt, 0, (size_t)S * m->nkv * 4, m->stream));
     CREATE_HIP(hipMemsetAsync(m->d_lm_cnt, 0, (size_t)S * 4, m->stream));
     CREATE_HIP(hipMemsetAsync(m->d_pos, 0, (size_t)S * 4, m->stream));
     CREATE_HIP(hipMemsetAsync(m->d_k, 0, (size_t)(L * kv_layer_elems(m) * 2), m->stream));
@@ -730,7 +727,6 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
     at.max_chunks = m->max_chunks;
     at.scale = (float)(1.0 / std::sqrt((double)m->hd));
     at.part = m->d_attn_part;
-    at.counter = m->d_attn_cnt;
     at.out = m->d_o;
 
     if (m->streaming) {
