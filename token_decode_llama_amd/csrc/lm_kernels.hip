@@ -753,21 +753,46 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
 
 // Phase 2: merge the chunks of each (sequence, query head): with
 // M = max_c m_c, o = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c.
-// A thread per output element; the loads of all chunks are independent.
+// A thread per output element.  Chunks are read in batches of 8 whose loads
+// are all independent; the first batch is requested together with the
+// position (chunks past the causal horizon are loaded, then ignored).
 template <int HD>
 __global__ __launch_bounds__(HD) void k_attn_merge(AttnArgs a) {
+    constexpr int B = 8;
     const int h = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
     const int64_t stride = HD + 2;
-    const int n_act = (a.pos[s] + 1 + kAttnChunk - 1) / kAttnChunk;
     const float* ph = a.part + ((int64_t)s * a.nq + h) * a.max_chunks * stride;
-    float M = -FLT_MAX;
-    for (int c = 0; c < n_act; ++c) M = fmaxf(M, ph[c * stride + HD]);
-    float L = 0.f, O = 0.f;
-    #pragma unroll 4
-    for (int c = 0; c < n_act; ++c) {
-        const float e = __expf(ph[c * stride + HD] - M);
-        L = fmaf(ph[c * stride + HD + 1], e, L);
-        O = fmaf(ph[c * stride + d], e, O);
+    float mv[B], lv[B], ov[B];
+    auto fetch = [&](int base) {
+        #pragma unroll
+        for (int u = 0; u < B; ++u) {
+            const int c = min(base + u, a.max_chunks - 1);
+            mv[u] = ph[c * stride + HD];
+            lv[u] = ph[c * stride + HD + 1];
+            ov[u] = ph[c * stride + d];
+        }
+    };
+    fetch(0);
+    const int n_act = (a.pos[s] + 1 + kAttnChunk - 1) / kAttnChunk;
+    float M = -FLT_MAX, L = 0.f, O = 0.f;
+    for (int base = 0; base < n_act; base += B) {
+        if (base > 0) fetch(base);
+        float bm = -FLT_MAX;
+        #pragma unroll
+        for (int u = 0; u < B; ++u)
+            if (base + u < n_act) bm = fmaxf(bm, mv[u]);
+        const float Mn = fmaxf(M, bm);
+        const float r = __expf(M - Mn);
+        L *= r;
+        O *= r;
+        #pragma unroll
+        for (int u = 0; u < B; ++u)
+            if (base + u < n_act) {
+                const float e = __expf(mv[u] - Mn);
+                L = fmaf(lv[u], e, L);
+                O = fmaf(ov[u], e, O);
+            }
+        M = Mn;
     }
     a.out[(int64_t)s * a.nq * HD + (int64_t)h * HD + d] = O / L;
 }
