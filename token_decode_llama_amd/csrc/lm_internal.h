@@ -22,6 +22,8 @@ constexpr int kAttnChunk = 64;     // KV positions per attention workgroup
 struct QMat {
     const uint8_t* q;
     const uint16_t* sc;
+    const uint16_t* sct;   // scales again, transposed per 16-row tile: [N/16][nb][16]
+                           // (present when the model decodes several sequences at once)
     int N, K;
 };
 
@@ -57,6 +59,9 @@ struct GemvArgs {
     int* counter;          // [n_seq], zero between launches
     int* argmax_out;       // [n_seq]
     int* pos_inc;          // [n_seq] positions advanced by one after the argmax
+    // several sequences at once (MFMA path)
+    int n_seq;
+    uint4* xfrag;          // activation B-fragments, [nb][hi|lo][4 k-groups][4 seqs] x 16 bytes
 };
 
 struct AttnArgs {
@@ -75,6 +80,9 @@ struct AttnArgs {
 hipError_t launch_embed(const uint16_t* tok_embd, const int* tokens, int vocab, int hidden,
                         float* x, int n_seq, hipStream_t st);
 hipError_t launch_gemv(const GemvArgs& a, int epi, int n_seq, int max_blocks, hipStream_t st);
+// 2..4 sequences: activation fragments (RMSNorm applied), then the MFMA GEMV
+hipError_t launch_gemv_batched(const GemvArgs& a, int epi, int n_seq, int max_blocks, hipStream_t st);
+inline int64_t xfrag_bytes(int64_t K) { return K / 32 * 512; }
 hipError_t launch_attention(const AttnArgs& a, int n_seq, hipStream_t st);
 hipError_t launch_dequant(const QMat& w, int qtype, int row0, int n_rows, float* out,
                           hipStream_t st);

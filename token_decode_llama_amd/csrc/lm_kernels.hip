@@ -608,6 +608,304 @@ hipError_t launch_gemv(const GemvArgs& a, int epi, int n_seq, int max_blocks, hi
 }
 
 // ---------------------------------------------------------------------------
+// 2..4 sequences: dequant-GEMV as a dense contraction on the matrix cores
+// ---------------------------------------------------------------------------
+// v_mfma_f32_16x16x32_f16 contracts a 16-row x 32-column weight tile (one quant
+// block) with a 32 x 16 activation tile whose columns are the sequences.
+// Operand layout (lane l, group g = l/16, index j = l%16):
+//   A: row j, columns 8g..8g+7;  B: column (sequence) j, rows 8g..8g+7;
+//   D: rows 4g..4g+3, column j.
+// Weights enter as exact fp16 integers (q, or nibble - 8); activations as an
+// exact pair x = hi + lo of fp16 values (two accumulating MFMAs), so each
+// block's 16x16 result is the block dot product in fp32; it is then scaled by
+// the row's block scale and accumulated in fp32.
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+
+// One workgroup per sequence: RMSNorm (optional) and the hi/lo fp16 split of
+// every activation, written as B fragments: frag[b][part][g][s] = 8 halves
+// (block b, columns 8g..8g+7, sequence s; part 0 = hi, 1 = lo).
+__global__ __launch_bounds__(kBlock) void k_xfrag(const float* __restrict__ xin, int x_stride,
+                                                 const float* __restrict__ g, float eps, int K,
+                                                 uint4* __restrict__ frag) {
+    __shared__ float red[kWaves];
+    const int s = blockIdx.x, tid = threadIdx.x;
+    const float* x = xin + (int64_t)s * x_stride;
+    float scale = 1.f;
+    if (g) {
+        float ss = 0.f;
+        for (int i = tid * 4; i < K; i += kBlock * 4) {
+            const float4 v = *(const float4*)(x + i);
+            ss = fmaf(v.x, v.x, ss);
+            ss = fmaf(v.y, v.y, ss);
+            ss = fmaf(v.z, v.z, ss);
+            ss = fmaf(v.w, v.w, ss);
+        }
+        scale = 1.0f / sqrtf(block_sum(ss, red) / (float)K + eps);
+    }
+    for (int c = tid; c < K / 8; c += kBlock) {            // 8 columns per piece
+        const float4 v0 = *(const float4*)(x + 8 * c), v1 = *(const float4*)(x + 8 * c + 4);
+        float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        if (g) {
+            const float4 g0 = *(const float4*)(g + 8 * c), g1 = *(const float4*)(g + 8 * c + 4);
+            const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+            #pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = v[e] * scale * gg[e];
+        }
+        h8_t hi, lo;
+        #pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            hi[e] = (_Float16)v[e];
+            lo[e] = (_Float16)(v[e] - (float)hi[e]);
+        }
+        const int b = c >> 2, gq = c & 3;
+        frag[((b * 2 + 0) * 4 + gq) * 4 + s] = *(const uint4*)&hi;
+        frag[((b * 2 + 1) * 4 + gq) * 4 + s] = *(const uint4*)&lo;
+    }
+}
+
+template <int QT>
+__device__ __forceinline__ h8_t weights_f16(uint2 raw, int g) {
+    h8_t a;
+    if (QT == kQ8_0) {
+        #pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            a[e] = (_Float16)(float)(int8_t)(raw.x >> (8 * e));
+            a[4 + e] = (_Float16)(float)(int8_t)(raw.y >> (8 * e));
+        }
+    } else {
+        const int sh = g >= 2 ? 4 : 0;     // groups 2, 3: high nibbles (columns 16..31)
+        #pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            a[e] = (_Float16)(float)((int)((raw.x >> (8 * e + sh)) & 15u) - 8);
+            a[4 + e] = (_Float16)(float)((int)((raw.y >> (8 * e + sh)) & 15u) - 8);
+        }
+    }
+    return a;
+}
+
+constexpr int kMbDepth = 4;   // blocks per lane whose loads are in flight together
+
+// One 16-row tile per workgroup at a time (grid-stride over tiles); the W
+// wavefronts of the workgroup split the tile's K blocks and reduce through LDS.
+template <int QT, int EPI, int W>
+__global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
+    __shared__ __align__(16) float part[W][64][4];
+    __shared__ float wv_best[4][W];
+    __shared__ int wi_best[4][W];
+    __shared__ int s_last;
+
+    const int K = a.w.K, N = a.w.N, nb = K >> 5;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, j = lane & 15;
+    const int n_tiles = (N + 15) >> 4;
+    const int nbq = (nb + W - 1) / W;
+    const int b_lo = min(wave * nbq, nb), b_hi = min(b_lo + nbq, nb);
+    const int64_t rowq = (QT == kQ8_0) ? (int64_t)K : (int64_t)(K >> 1);
+    const bool col_ok = j < a.n_seq;
+
+    float best_v = -FLT_MAX;
+    int best_i = INT_MAX;
+
+    for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+        const int row = min(tile * 16 + j, N - 1);      // this lane's A row (clamped in a ragged tile)
+        const uint8_t* qrow = a.w.q + (int64_t)row * rowq;
+        const uint16_t* sct = a.w.sct + (int64_t)tile * nb * 16 + 4 * g;
+        f4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (int b0 = b_lo; b0 < b_hi; b0 += kMbDepth) {
+            uint2 wr[kMbDepth], sr[kMbDepth];
+            uint4 xh[kMbDepth], xl[kMbDepth];
+            #pragma unroll
+            for (int u = 0; u < kMbDepth; ++u) {
+                const int b = min(b0 + u, b_hi - 1);
+                const uint8_t* p = (QT == kQ8_0)
+                    ? qrow + (int64_t)(g >> 1) * nb * 16 + (uint32_t)b * 16u + (g & 1) * 8
+                    : qrow + (uint32_t)b * 16u + (g & 1) * 8;
+                wr[u] = *(const uint2*)p;
+                sr[u] = *(const uint2*)(sct + (int64_t)b * 16);
+                const int fi = (b * 8 + g) * 4 + (col_ok ? j : 0);
+                xh[u] = a.xfrag[fi];
+                xl[u] = a.xfrag[fi + 16];
+            }
+            #pragma unroll
+            for (int u = 0; u < kMbDepth; ++u) {
+                if (b0 + u >= b_hi) break;
+                const h8_t wa = weights_f16<QT>(wr[u], g);
+                h8_t bh = *(const h8_t*)&xh[u], bl = *(const h8_t*)&xl[u];
+                if (!col_ok) { bh = (h8_t)0; bl = (h8_t)0; }
+                f4_t c = {0.f, 0.f, 0.f, 0.f};
+                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa, bh, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa, bl, c, 0, 0, 0);
+                acc[0] = fmaf(h2f((uint16_t)(sr[u].x & 0xFFFF)), c[0], acc[0]);
+                acc[1] = fmaf(h2f((uint16_t)(sr[u].x >> 16)), c[1], acc[1]);
+                acc[2] = fmaf(h2f((uint16_t)(sr[u].y & 0xFFFF)), c[2], acc[2]);
+                acc[3] = fmaf(h2f((uint16_t)(sr[u].y >> 16)), c[3], acc[3]);
+            }
+        }
+        *(float4*)&part[wave][lane][0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        __syncthreads();
+        if (wave == 0 && col_ok) {
+            float y[4] = {0.f, 0.f, 0.f, 0.f};
+            #pragma unroll
+            for (int w = 0; w < W; ++w) {
+                const float4 v = *(const float4*)&part[w][lane][0];
+                y[0] += v.x; y[1] += v.y; y[2] += v.z; y[3] += v.w;
+            }
+            const int s = j;
+            #pragma unroll
+            for (int pr = 0; pr < 2; ++pr) {
+                const int r0 = tile * 16 + 4 * g + 2 * pr;   // rows r0, r0 + 1 (a RoPE / gate-up pair)
+                const float y0 = y[2 * pr], y1 = y[2 * pr + 1];
+                if (EPI == EPI_QKV) {
+                    const int p = a.pos[s];
+                    const int hd = a.head_dim;
+                    if (r0 < a.q_rows + a.kv_rows) {
+                        const int rr = r0 < a.q_rows ? r0 : r0 - a.q_rows;
+                        const int pi = (rr % hd) >> 1;
+                        const float cs = a.rope_cos[(int64_t)p * (hd >> 1) + pi];
+                        const float sn = a.rope_sin[(int64_t)p * (hd >> 1) + pi];
+                        const float z0 = y0 * cs - y1 * sn;
+                        const float z1 = y0 * sn + y1 * cs;
+                        if (r0 < a.q_rows) {
+                            *(float2*)(a.out + (int64_t)s * a.out_stride + r0) = make_float2(z0, z1);
+                        } else {
+                            __half2* dst = (__half2*)(a.kcache + (int64_t)s * a.kv_seq_stride +
+                                                      ((int64_t)(rr / hd) * a.max_ctx + p) * hd + (rr % hd));
+                            *dst = __floats2half2_rn(z0, z1);
+                        }
+                    } else {
+                        const int rr = r0 - a.q_rows - a.kv_rows;
+                        __half2* dst = (__half2*)(a.vcache + (int64_t)s * a.kv_seq_stride +
+                                                  ((int64_t)(rr / hd) * a.max_ctx + p) * hd + (rr % hd));
+                        *dst = __floats2half2_rn(y0, y1);
+                    }
+                } else if (EPI == EPI_RESID) {
+                    float* xo = a.out + (int64_t)s * a.out_stride + r0;
+                    float2 v = *(float2*)xo;
+                    v.x += y0;
+                    v.y += y1;
+                    *(float2*)xo = v;
+                } else if (EPI == EPI_SWIGLU) {
+                    const float sg = y0 / (1.0f + __expf(-y0));
+                    a.out[(int64_t)s * a.out_stride + (r0 >> 1)] = sg * y1;
+                } else {  // EPI_LOGITS: the vocabulary may end inside a tile or a pair
+                    if (r0 < N) {
+                        if (a.out) a.out[(int64_t)s * a.out_stride + r0] = y0;
+                        better(best_v, best_i, y0, r0);
+                    }
+                    if (r0 + 1 < N) {
+                        if (a.out) a.out[(int64_t)s * a.out_stride + r0 + 1] = y1;
+                        better(best_v, best_i, y1, r0 + 1);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    if (EPI == EPI_LOGITS) {
+        // sequence j's candidates sit in lanes j, j+16, j+32, j+48 of wavefront 0
+        if (wave == 0) {
+            float bv = best_v;
+            int bi = best_i;
+            #pragma unroll
+            for (int off = 16; off < 64; off <<= 1) {
+                const float ov = __shfl_xor(bv, off, 64);
+                const int oi = __shfl_xor(bi, off, 64);
+                better(bv, bi, ov, oi);
+            }
+            if (lane < a.n_seq) {
+                a.part_val[(int64_t)lane * gridDim.x + blockIdx.x] = bv;
+                a.part_idx[(int64_t)lane * gridDim.x + blockIdx.x] = bi;
+            }
+        }
+        __syncthreads();
+        if (tid == 0) {
+            __threadfence();
+            const int old = atomicAdd(&a.counter[0], 1);
+            s_last = (old == (int)gridDim.x - 1);
+        }
+        __syncthreads();
+        if (s_last) {
+            if (tid == 0) __threadfence();
+            __syncthreads();
+            for (int s = 0; s < a.n_seq; ++s) {
+                float bv = -FLT_MAX;
+                int bi = INT_MAX;
+                for (int i = tid; i < (int)gridDim.x; i += 64 * W)
+                    better(bv, bi, a.part_val[(int64_t)s * gridDim.x + i], a.part_idx[(int64_t)s * gridDim.x + i]);
+                #pragma unroll
+                for (int off = 32; off > 0; off >>= 1) {
+                    const float ov = __shfl_xor(bv, off, 64);
+                    const int oi = __shfl_xor(bi, off, 64);
+                    better(bv, bi, ov, oi);
+                }
+                if (lane == 0) { wv_best[s][wave] = bv; wi_best[s][wave] = bi; }
+            }
+            __syncthreads();
+            if (tid == 0) {
+                for (int s = 0; s < a.n_seq; ++s) {
+                    float bv = wv_best[s][0];
+                    int bi = wi_best[s][0];
+                    for (int w = 1; w < W; ++w) better(bv, bi, wv_best[s][w], wi_best[s][w]);
+                    a.argmax_out[s] = bi;
+                    if (a.pos_inc) a.pos_inc[s] += 1;
+                }
+                a.counter[0] = 0;
+            }
+        }
+    }
+}
+
+template <int QT, int EPI, int W>
+static hipError_t launch_mfma_w(const GemvArgs& a, int max_blocks, hipStream_t st) {
+    const int n_tiles = (a.w.N + 15) / 16;
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemv_mfma<QT, EPI, W>, 64 * W, 0) != hipSuccess ||
+        per_cu < 1)
+        per_cu = 1;
+    const int cap = std::min(max_blocks, per_cu * device_cus());
+    const int grid = std::max(1, std::min(n_tiles, cap));
+    hipLaunchKernelGGL((k_gemv_mfma<QT, EPI, W>), dim3(grid), dim3(64 * W), 0, st, a);
+    return hipGetLastError();
+}
+
+// wavefronts per tile: enough K splitting that every CU holds ~16 wavefronts
+template <int QT, int EPI>
+static hipError_t launch_mfma(const GemvArgs& a, int max_blocks, hipStream_t st) {
+    const int n_tiles = (a.w.N + 15) / 16;
+    const int64_t target = (int64_t)device_cus() * 16;
+    if ((int64_t)n_tiles * 4 >= target) return launch_mfma_w<QT, EPI, 4>(a, max_blocks, st);
+    if ((int64_t)n_tiles * 8 >= target) return launch_mfma_w<QT, EPI, 8>(a, max_blocks, st);
+    return launch_mfma_w<QT, EPI, 16>(a, max_blocks, st);
+}
+
+hipError_t launch_gemv_batched(const GemvArgs& a0, int epi, int n_seq, int max_blocks, hipStream_t st) {
+    if (n_seq < 1 || n_seq > 4 || !a0.w.sct || !a0.xfrag) return hipErrorInvalidValue;
+    GemvArgs a = a0;
+    a.n_seq = n_seq;
+    hipLaunchKernelGGL(k_xfrag, dim3(n_seq), dim3(kBlock), 0, st, a.xin, a.x_stride, a.norm_g, a.eps, a.w.K,
+                       a.xfrag);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.qtype == kQ8_0) {
+        switch (epi) {
+            case EPI_QKV: return launch_mfma<kQ8_0, EPI_QKV>(a, max_blocks, st);
+            case EPI_RESID: return launch_mfma<kQ8_0, EPI_RESID>(a, max_blocks, st);
+            case EPI_SWIGLU: return launch_mfma<kQ8_0, EPI_SWIGLU>(a, max_blocks, st);
+            default: return launch_mfma<kQ8_0, EPI_LOGITS>(a, max_blocks, st);
+        }
+    }
+    switch (epi) {
+        case EPI_QKV: return launch_mfma<kQ4_0, EPI_QKV>(a, max_blocks, st);
+        case EPI_RESID: return launch_mfma<kQ4_0, EPI_RESID>(a, max_blocks, st);
+        case EPI_SWIGLU: return launch_mfma<kQ4_0, EPI_SWIGLU>(a, max_blocks, st);
+        default: return launch_mfma<kQ4_0, EPI_LOGITS>(a, max_blocks, st);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // GQA decode attention with causal softmax, split over context
 // ---------------------------------------------------------------------------
 constexpr int kMaxGroup = 8;   // query heads per KV head

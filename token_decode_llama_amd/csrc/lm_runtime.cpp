@@ -44,8 +44,12 @@ enum { M_QKV = 0, M_WO = 1, M_GU = 2, M_DOWN = 3, M_COUNT = 4 };
 
 struct MatOff {
     int64_t q, sc;   // byte offsets within the blob
+    int64_t sct;     // transposed scales [ceil(N/16)][nb][16], or -1 (single-sequence models)
     int N, K;
 };
+
+// bytes of a tile-transposed scale plane
+inline int64_t sct_bytes(int64_t N, int64_t K) { return (N + 15) / 16 * 16 * (K / 32) * 2; }
 
 template <class F>
 void parallel_rows(int64_t n, F&& fn) {
@@ -94,7 +98,8 @@ struct lm_model {
     int64_t H = 0, F = 0, V = 0, nq = 0, nkv = 0, hd = 0, qrows = 0, kvrows = 0;
     int64_t blob_bytes = 0;
     MatOff mo[M_COUNT]{};
-    int64_t lm_q_bytes = 0, lm_sc_bytes = 0;
+    int64_t lm_q_bytes = 0, lm_sc_bytes = 0, lm_sct_bytes = 0;
+    bool batched = false;                 // max_seqs >= 2: MFMA path for 2..4 sequences
     int max_chunks = 0;
     int gemv_max_blocks = 1024;
     int lm_grid = 0;
@@ -110,6 +115,8 @@ struct lm_model {
     float* d_out_norm = nullptr;
     uint8_t* d_lm_q = nullptr;
     uint16_t* d_lm_sc = nullptr;
+    uint16_t* d_lm_sct = nullptr;
+    uint4* d_xfrag = nullptr;             // activation fragments of the MFMA path
     __half* d_k = nullptr;                // [L][S][nkv][max_ctx][hd]
     __half* d_v = nullptr;
     float *d_x = nullptr, *d_q = nullptr, *d_o = nullptr, *d_h = nullptr, *d_logits = nullptr;
@@ -305,10 +312,16 @@ static void layout(lm_model* m) {
         off = align_up(off + qmat_qbytes(qt, NK[i][0], NK[i][1]));
         m->mo[i].sc = off;
         off = align_up(off + qmat_sbytes(NK[i][0], NK[i][1]));
+        m->mo[i].sct = -1;
+        if (m->batched) {
+            m->mo[i].sct = off;
+            off = align_up(off + sct_bytes(NK[i][0], NK[i][1]));
+        }
     }
     m->blob_bytes = off;
     m->lm_q_bytes = align_up(qmat_qbytes(qt, m->V, m->H));
     m->lm_sc_bytes = align_up(qmat_sbytes(m->V, m->H));
+    m->lm_sct_bytes = m->batched ? align_up(sct_bytes(m->V, m->H)) : 0;
     m->max_chunks = (c.max_ctx + kAttnChunk - 1) / kAttnChunk;
 }
 
@@ -316,6 +329,7 @@ static QMat mat_at(const lm_model* m, const uint8_t* blob, int which) {
     QMat w;
     w.q = blob + m->mo[which].q;
     w.sc = (const uint16_t*)(blob + m->mo[which].sc);
+    w.sct = m->mo[which].sct >= 0 ? (const uint16_t*)(blob + m->mo[which].sct) : nullptr;
     w.N = m->mo[which].N;
     w.K = m->mo[which].K;
     return w;
@@ -325,6 +339,7 @@ static QMat lm_head_mat(const lm_model* m) {
     QMat w;
     w.q = m->d_lm_q;
     w.sc = m->d_lm_sc;
+    w.sct = m->d_lm_sct;
     w.N = (int)m->V;
     w.K = (int)m->H;
     return w;
@@ -349,6 +364,7 @@ extern "C" lm_status lm_model_create(const lm_config* cfg, void* hip_stream, lm_
     lm_model* m = new (std::nothrow) lm_model();
     if (!m) return fail(nullptr, LM_E_OOM, "lm_model_create: host allocation failed");
     m->cfg = *cfg;
+    m->batched = cfg->max_seqs >= 2;
     layout(m);
     m->layer_loaded.assign(cfg->n_layers, 0);
     m->pos.assign(cfg->max_seqs, 0);
@@ -403,6 +419,11 @@ extern "C" lm_status lm_model_create(const lm_config* cfg, void* hip_stream, lm_
     CREATE_TRY(dev_alloc(m, (void**)&m->d_out_norm, m->H * 4, "output norm"));
     CREATE_TRY(dev_alloc(m, (void**)&m->d_lm_q, m->lm_q_bytes, "LM head quants"));
     CREATE_TRY(dev_alloc(m, (void**)&m->d_lm_sc, m->lm_sc_bytes, "LM head scales"));
+    if (m->batched) {
+        CREATE_TRY(dev_alloc(m, (void**)&m->d_lm_sct, m->lm_sct_bytes, "LM head transposed scales"));
+        const int64_t kmax = std::max<int64_t>({m->H, m->qrows, m->F});
+        CREATE_TRY(dev_alloc(m, (void**)&m->d_xfrag, xfrag_bytes(kmax), "activation fragments"));
+    }
     CREATE_TRY(dev_alloc(m, (void**)&m->d_k, L * kv_layer_elems(m) * 2, "K cache"));
     CREATE_TRY(dev_alloc(m, (void**)&m->d_v, L * kv_layer_elems(m) * 2, "V cache"));
     CREATE_TRY(dev_alloc(m, (void**)&m->d_x, S * m->H * 4, "residual"));
@@ -499,6 +520,36 @@ static lm_status upload_matrix(lm_model* m, int N, int K, RowFn src_row, uint8_t
     return LM_OK;
 }
 
+// The tile-transposed copy of a matrix's block scales used by the MFMA path:
+// dst[t][b][i] = scale of row 16t+i, block b (zero past the last row).
+template <class RowFn>
+static lm_status upload_sct(lm_model* m, int N, int K, RowFn src_row, uint16_t* dst, bool dst_host) {
+    const int64_t nb = K / 32, tiles = (N + 15) / 16, bb = block_bytes(m->cfg.qtype);
+    std::vector<uint16_t> tmp;
+    uint16_t* t = dst;
+    if (!dst_host) {
+        tmp.assign((size_t)(tiles * nb * 16), 0);
+        t = tmp.data();
+    }
+    parallel_rows(tiles, [&](int64_t a, int64_t b) {
+        for (int64_t tile = a; tile < b; ++tile)
+            for (int i = 0; i < 16; ++i) {
+                const int64_t r = tile * 16 + i;
+                uint16_t* col = t + tile * nb * 16 + i;
+                if (r >= N) {
+                    for (int64_t k = 0; k < nb; ++k) col[k * 16] = 0;
+                    continue;
+                }
+                const uint8_t* src = src_row(r);
+                for (int64_t k = 0; k < nb; ++k)
+                    col[k * 16] = (uint16_t)(src[k * bb] | (src[k * bb + 1] << 8));
+            }
+    });
+    if (!dst_host)
+        HIPTRY(m, hipMemcpy(dst, t, (size_t)(tiles * nb * 16 * 2), hipMemcpyHostToDevice));
+    return LM_OK;
+}
+
 static void invalidate_graphs(lm_model* m) {
     for (auto& g : m->graphs) (void)hipGraphExecDestroy(g.exec);
     m->graphs.clear();
@@ -525,22 +576,31 @@ extern "C" lm_status lm_load_layer_weights(lm_model* m, int32_t layer, const lm_
     const bool host = m->streaming;
     auto dq = [&](int i) { return blob + m->mo[i].q; };
     auto ds = [&](int i) { return (uint16_t*)(blob + m->mo[i].sc); };
-    lm_status st;
-    st = upload_matrix(m, m->mo[M_QKV].N, (int)H, [&](int64_t r) {
+    auto src_qkv = [&](int64_t r) {
         if (r < qr) return wq + r * rowH;
         if (r < qr + kr) return wk + (r - qr) * rowH;
         return wv + (r - qr - kr) * rowH;
-    }, dq(M_QKV), ds(M_QKV), host);
-    if (st != LM_OK) return st;
-    st = upload_matrix(m, (int)H, (int)m->qrows, [&](int64_t r) { return wo + r * rowQ; }, dq(M_WO), ds(M_WO), host);
-    if (st != LM_OK) return st;
+    };
+    auto src_wo = [&](int64_t r) { return wo + r * rowQ; };
     // gate and up rows interleaved: device row 2i = gate i, 2i+1 = up i
-    st = upload_matrix(m, (int)(2 * F), (int)H, [&](int64_t r) {
-        return (r & 1) ? wu + (r >> 1) * rowH : wg + (r >> 1) * rowH;
-    }, dq(M_GU), ds(M_GU), host);
+    auto src_gu = [&](int64_t r) { return (r & 1) ? wu + (r >> 1) * rowH : wg + (r >> 1) * rowH; };
+    auto src_down = [&](int64_t r) { return wd + r * rowF; };
+    lm_status st;
+    st = upload_matrix(m, m->mo[M_QKV].N, (int)H, src_qkv, dq(M_QKV), ds(M_QKV), host);
     if (st != LM_OK) return st;
-    st = upload_matrix(m, (int)H, (int)F, [&](int64_t r) { return wd + r * rowF; }, dq(M_DOWN), ds(M_DOWN), host);
+    st = upload_matrix(m, (int)H, (int)m->qrows, src_wo, dq(M_WO), ds(M_WO), host);
     if (st != LM_OK) return st;
+    st = upload_matrix(m, (int)(2 * F), (int)H, src_gu, dq(M_GU), ds(M_GU), host);
+    if (st != LM_OK) return st;
+    st = upload_matrix(m, (int)H, (int)F, src_down, dq(M_DOWN), ds(M_DOWN), host);
+    if (st != LM_OK) return st;
+    if (m->batched) {
+        auto dt = [&](int i) { return (uint16_t*)(blob + m->mo[i].sct); };
+        if ((st = upload_sct(m, m->mo[M_QKV].N, (int)H, src_qkv, dt(M_QKV), host)) != LM_OK) return st;
+        if ((st = upload_sct(m, (int)H, (int)m->qrows, src_wo, dt(M_WO), host)) != LM_OK) return st;
+        if ((st = upload_sct(m, (int)(2 * F), (int)H, src_gu, dt(M_GU), host)) != LM_OK) return st;
+        if ((st = upload_sct(m, (int)H, (int)F, src_down, dt(M_DOWN), host)) != LM_OK) return st;
+    }
     HIPTRY(m, hipMemcpy(m->d_norms + (int64_t)layer * 2 * H, w->attn_norm, H * 4, hipMemcpyHostToDevice));
     HIPTRY(m, hipMemcpy(m->d_norms + ((int64_t)layer * 2 + 1) * H, w->ffn_norm, H * 4, hipMemcpyHostToDevice));
     m->layer_loaded[layer] = 1;
@@ -558,9 +618,10 @@ extern "C" lm_status lm_load_global_weights(lm_model* m, const uint16_t* tok_emb
     HIPTRY(m, hipMemcpy(m->d_out_norm, out_norm, (size_t)(m->H * 4), hipMemcpyHostToDevice));
     const int64_t rowH = m->H / 32 * block_bytes(m->cfg.qtype);
     const uint8_t* src = (const uint8_t*)lm_head_blocks;
-    lm_status st = upload_matrix(m, (int)m->V, (int)m->H, [&](int64_t r) { return src + r * rowH; },
-                                 m->d_lm_q, m->d_lm_sc, false);
+    auto src_row = [&](int64_t r) { return src + r * rowH; };
+    lm_status st = upload_matrix(m, (int)m->V, (int)m->H, src_row, m->d_lm_q, m->d_lm_sc, false);
     if (st != LM_OK) return st;
+    if (m->batched && (st = upload_sct(m, (int)m->V, (int)m->H, src_row, m->d_lm_sct, false)) != LM_OK) return st;
     m->global_loaded = true;
     return LM_OK;
 }
@@ -696,6 +757,16 @@ static lm_status stream_copy(lm_model* m, int layer) {
     return LM_OK;
 }
 
+// One sequence: the integer-digit VALU GEMV.  Two to four: activation
+// fragments plus the MFMA GEMV (one read of the weights for all sequences).
+static hipError_t gemv(lm_model* m, GemvArgs a, int epi, int n_seq, hipStream_t st) {
+    if (n_seq >= 2) {
+        a.xfrag = m->d_xfrag;
+        return launch_gemv_batched(a, epi, n_seq, m->gemv_max_blocks, st);
+    }
+    return launch_gemv(a, epi, n_seq, m->gemv_max_blocks, st);
+}
+
 static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d_logits, int* d_argmax) {
     const lm_config& c = m->cfg;
     const int L = c.n_layers;
@@ -753,7 +824,7 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
             a.norm_g = g_attn;
             a.out = m->d_q; a.out_stride = (int)m->qrows;
             a.kcache = kc; a.vcache = vc;
-            HIPTRY(m, launch_gemv(a, EPI_QKV, n_seq, m->gemv_max_blocks, st));
+            HIPTRY(m, gemv(m, a, EPI_QKV, n_seq, st));
         }
         {   // GQA attention with causal softmax
             KTimer t(m, LM_K_ATTN);
@@ -767,7 +838,7 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
             a.w = mat_at(m, blob, M_WO);
             a.xin = m->d_o; a.x_stride = (int)m->qrows;
             a.out = m->d_x; a.out_stride = (int)m->H;
-            HIPTRY(m, launch_gemv(a, EPI_RESID, n_seq, m->gemv_max_blocks, st));
+            HIPTRY(m, gemv(m, a, EPI_RESID, n_seq, st));
         }
         {   // RMSNorm -> gate/up GEMV -> SwiGLU
             KTimer t(m, LM_K_GATEUP);
@@ -776,7 +847,7 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
             a.xin = m->d_x; a.x_stride = (int)m->H;
             a.norm_g = g_ffn;
             a.out = m->d_h; a.out_stride = (int)m->F;
-            HIPTRY(m, launch_gemv(a, EPI_SWIGLU, n_seq, m->gemv_max_blocks, st));
+            HIPTRY(m, gemv(m, a, EPI_SWIGLU, n_seq, st));
         }
         {   // x += Wdown h
             KTimer t(m, LM_K_DOWN);
@@ -784,7 +855,7 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
             a.w = mat_at(m, blob, M_DOWN);
             a.xin = m->d_h; a.x_stride = (int)m->F;
             a.out = m->d_x; a.out_stride = (int)m->H;
-            HIPTRY(m, launch_gemv(a, EPI_RESID, n_seq, m->gemv_max_blocks, st));
+            HIPTRY(m, gemv(m, a, EPI_RESID, n_seq, st));
         }
         if (m->streaming) {
             HIPTRY(m, hipEventRecord(m->ev_consumed[l & 1], st));
@@ -814,7 +885,7 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
         a.counter = m->d_lm_cnt;
         a.argmax_out = d_argmax;
         a.pos_inc = m->d_pos;
-        HIPTRY(m, launch_gemv(a, EPI_LOGITS, n_seq, m->gemv_max_blocks, st));
+        HIPTRY(m, gemv(m, a, EPI_LOGITS, n_seq, st));
     }
     return LM_OK;
 }
