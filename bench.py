@@ -1,19 +1,29 @@
 #!/usr/bin/env python3
 """Decode-step benchmark of the MI355X quantized Llama decode library.
 
-One "step" = one greedy batch-1 decode step of the whole model (embedding,
-every layer's RMSNorm + QKV + RoPE/KV-append, GQA attention, Wo, RMSNorm +
+One "step" = one greedy decode step of the whole model (embedding, every
+layer's RMSNorm + QKV + RoPE/KV-append, GQA attention, Wo, RMSNorm +
 gate/up + SwiGLU, down, then final norm + LM head + argmax) on synthetic
-seeded weights already resident in HBM.  The default workload is the
-Llama-3.1-8B-shaped Q8_0 model at KV context 512 (+64 steps), batch 1.
+seeded weights.  The default workload (the headline line) is the
+Llama-3.1-8B-shaped Q8_0 model at KV context 512 (+64 steps), batch 1, with
+every weight resident in HBM.
 
-Prints ONE JSON line:
+Other workloads (--workload), each printing one JSON line of its own:
+  llama8b_q4   8B shape, Q4_0, four sequences decoded together at KV context
+               4096 (+32 steps): the multi-sequence (MFMA) path
+  multi        Llama-3.2-1B, Qwen2-0.5B and SmolLM2-360M shapes (Q8_0, KV
+               context 2048, 32 steps each) decoded round-robin, each model on
+               its own HIP stream; value = aggregate tokens/s
+  llama70b_q4  70B shape, Q4_0, KV context 1024, 16 steps: (a) all weights
+               resident in HBM, then (b) layer streaming from pinned host
+               memory through two HBM layer buffers
+
+Every line carries:
   value           decode tokens/s over the timed steps (whole job; one GPU)
-  roofline        the dominant kernel (gate/up dequant-GEMV): algorithmic bytes
-                  per launch / average launch time from HIP events on the
-                  model's stream, against 8 TB/s
+  roofline        the dominant kernel: algorithmic bytes per launch / average
+                  launch duration from HIP events on the model's stream
   cpu_baseline    the fp64 oracle on this host's cores, on a bounded sample
-Usage: python bench.py [--gpus 1] [--steps 64] [--warmup 2] [--workload llama8b_q8]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 from __future__ import annotations
 
@@ -28,11 +38,28 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-DOMINANT = "gateup"
+HEADLINE_METRIC = "decode tokens/s + achieved HBM GB/s (% of peak), 8B-shape Q8_0 batch 1"
+SHAPE_8B = "vocab 128256, hidden 4096, 32 layers, 32/8 heads, hd 128, ffn 14336"
 WORKLOAD_TEXT = {
-    "llama8b_q8": "Llama-3.1-8B-shaped synthetic decoder (vocab 128256, hidden 4096, 32 layers, "
-                  "32/8 heads, hd 128, ffn 14336), Q8_0 weights resident in HBM, batch 1, "
-                  "KV context 512 (+steps), greedy decode",
+    "llama8b_q8": f"Llama-3.1-8B-shaped synthetic decoder ({SHAPE_8B}), Q8_0 weights resident "
+                  "in HBM, batch 1, KV context 512 (+steps), greedy decode",
+    "llama8b_q4": f"Llama-3.1-8B-shaped synthetic decoder ({SHAPE_8B}), Q4_0 weights resident "
+                  "in HBM, 4 independent sequences decoded together, KV context 4096 (+steps)",
+    "multi": "three concurrently resident Q8_0 models decoded round-robin on three HIP streams: "
+             "Llama-3.2-1B shape (hidden 2048, 16 layers, 32/8 heads, hd 64, ffn 8192, vocab 128256), "
+             "Qwen2-0.5B shape (hidden 896, 24 layers, 14/2 heads, hd 64, ffn 4864, vocab 151936), "
+             "SmolLM2-360M shape (hidden 960, 32 layers, 15/5 heads, hd 64, ffn 2560, vocab 49152); "
+             "KV context 2048 (+steps) each, batch 1",
+    "llama70b_q4": "Llama-3.1-70B-shaped synthetic decoder (vocab 128256, hidden 8192, 80 layers, "
+                   "64/8 heads, hd 128, ffn 28672), Q4_0 weights, batch 1, KV context 1024 (+steps)",
+}
+KERNEL_NAMES = {
+    "qkv": "k_gemv<QKV, RMSNorm prologue, RoPE + KV-append epilogue>",
+    "attn": "k_attn + k_attn_merge (GQA decode attention)",
+    "wo": "k_gemv<Wo, residual epilogue>",
+    "gateup": "k_gemv<gate/up, RMSNorm prologue, SwiGLU epilogue>",
+    "down": "k_gemv<down, residual epilogue>",
+    "lmhead": "k_gemv<LM head, RMSNorm prologue, argmax epilogue>",
 }
 
 
@@ -64,39 +91,366 @@ def traffic_from_profiles(kind: str, workload: str):
         return None
 
 
-def cpu_baseline(model, cfg, budget_s: float):
+def host_threads() -> int:
+    return int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(model, cfg, n_seq: int, budget_s: float, max_steps: int = 64):
     """The oracle as it stands, timed on this host on the same workload."""
-    import numpy as np
     import oracle
     import synth
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    om = oracle.OracleModel(model, max_seqs=1, max_ctx=cfg.ctx + 64)
-    for l in range(cfg.n_layers):
-        om.load_kv(0, l, *synth.make_kv(cfg, 0, l))
-    tok = synth.start_tokens(cfg, 1)
+    om = oracle.OracleModel(model, max_seqs=n_seq, max_ctx=cfg.ctx + max_steps)
+    for s in range(n_seq):
+        for l in range(cfg.n_layers):
+            om.load_kv(s, l, *synth.make_kv(cfg, s, l))
+    tok = synth.start_tokens(cfg, n_seq)
     n = 0
     t0 = time.perf_counter()
     while True:
         _, am = om.step(tok)
         tok = am
         n += 1
-        if time.perf_counter() - t0 >= budget_s or n >= 64:
+        if time.perf_counter() - t0 >= budget_s or n >= max_steps:
             break
     dt = time.perf_counter() - t0
     om.close()
-    return {"value": round(n / dt, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} greedy decode steps of the same model from context {cfg.ctx} "
-                      f"({dt:.1f} s, fp64, OpenMP over output rows)"}
+    what = "sequence" if n_seq == 1 else f"batch of {n_seq} sequences"
+    return {"value": round(n * n_seq / dt, 4), "unit": "tokens/s", "cores": host_threads(), "kind": "oracle",
+            "sample": f"{n} greedy decode steps ({what}) of the same model from context {cfg.ctx} "
+                      f"({dt:.1f} s, fp64, OpenMP over output rows)",
+            "_tokens": n * n_seq, "_seconds": dt}
+
+
+def public(d):
+    return {k: v for k, v in d.items() if not k.startswith("_")}
+
+
+class Runner:
+    """One opened model with its torch stream and device token buffers."""
+
+    def __init__(self, model, n_seq: int, kv_fn=None, loader=None):
+        import torch
+        import synth
+        import token_decode_llama_amd as lm
+        self.cfg = cfg = model.cfg
+        self.n_seq = n_seq
+        self.stream = torch.cuda.Stream()          # the model's stream (default priority)
+        kv_fn = kv_fn or (lambda s, l: synth.make_kv(cfg, s, l))
+        if loader is None:
+            self.g = lm.open_model(model, kv_fn, max_seqs=n_seq, kv_seqs=n_seq,
+                                   stream=self.stream.cuda_stream)
+        else:
+            self.g = loader(self.stream.cuda_stream)
+        dev = torch.device("cuda:0")
+        with torch.cuda.stream(self.stream):
+            self.tok = torch.from_numpy(synth.start_tokens(cfg, n_seq)).to(dev)
+            self.d_tok = self.tok.clone()
+        torch.cuda.synchronize()
+
+    def rewind(self):
+        import torch
+        torch.cuda.synchronize()
+        for s in range(self.n_seq):
+            self.g.set_position(s, self.cfg.ctx)
+        with torch.cuda.stream(self.stream):
+            self.d_tok.copy_(self.tok)
+        torch.cuda.synchronize()
+
+    def step(self):
+        self.g.step_dev(self.d_tok, self.n_seq, self.d_tok)
+
+    def warm(self, n: int):
+        import torch
+        for _ in range(n):
+            self.step()
+        torch.cuda.synchronize()
+        self.rewind()
+
+    def timed(self, n: int) -> float:
+        """ms per step over n steps, HIP events on the model's stream."""
+        import torch
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(self.stream)
+        for _ in range(n):
+            self.step()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    def kernel_profile(self, timing_steps: int):
+        """Per-kind (launches, total ms) over eager steps with events around every
+        kernel, and the algorithmic bytes of one step at those steps' mean position."""
+        import torch
+        import token_decode_llama_amd as lm
+        self.rewind()
+        self.g.kernel_timing(True)
+        for _ in range(timing_steps):
+            self.step()
+        torch.cuda.synchronize()
+        kstats = {k: self.g.kernel_stats(k) for k in lm.KERNEL_KINDS}
+        self.g.kernel_timing(False)
+        for s in range(self.n_seq):
+            self.g.set_position(s, self.cfg.ctx + timing_steps // 2)
+        kbytes = {k: self.g.kernel_bytes(k, self.n_seq) for k in lm.KERNEL_KINDS}
+        self.rewind()
+        return kstats, kbytes
+
+    def step_bytes(self, at_step: int) -> float:
+        import token_decode_llama_amd as lm
+        for s in range(self.n_seq):
+            self.g.set_position(s, self.cfg.ctx + at_step)
+        b = sum(self.g.kernel_bytes(k, self.n_seq) for k in lm.KERNEL_KINDS if k != "copy")
+        self.rewind()
+        return b
+
+    def close(self):
+        self.g.close()
+
+
+def per_launch(kind: str, n_layers: int) -> int:
+    return 1 if kind in ("embed", "lmhead") else n_layers
+
+
+def kernel_table(kstats, kbytes, n_layers):
+    out = {}
+    for k, (n, ms) in kstats.items():
+        if not n:
+            continue
+        avg_ms = ms / n
+        launches_per_step = per_launch(k, n_layers)
+        out[k] = {"launches": n, "avg_us": round(1e3 * avg_ms, 3),
+                  "algorithmic_GBps": round((kbytes[k] / launches_per_step) / (avg_ms * 1e-3) / 1e9, 1)
+                  if kbytes[k] else None}
+    return out
+
+
+def roofline_for(kind, kstats, kbytes, n_layers, workload):
+    n, ms = kstats[kind]
+    per_launch_bytes = kbytes[kind] / per_launch(kind, n_layers)
+    avg_ms = ms / max(n, 1)
+    achieved = per_launch_bytes / (avg_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_from_profiles(kind, workload),
+            "kernel": KERNEL_NAMES.get(kind, kind), "bytes_per_launch": int(per_launch_bytes),
+            "avg_launch_us": round(avg_ms * 1e3, 3)}
+
+
+def dominant(kstats):
+    """The compute kind with the largest summed duration."""
+    return max((k for k in kstats if k not in ("copy", "embed")), key=lambda k: kstats[k][1])
+
+
+def base_line(metric, tps, ms_per_step, steps, warmup, step_bytes, config, dtype="f32"):
+    gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+    return {"metric": metric, "value": round(tps, 2), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+            "warmup": warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+            "achieved_hbm_GBps": round(gbps, 1), "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+            "step_bytes": int(step_bytes), "config": config}
+
+
+# ---------------------------------------------------------------------------
+def run_single(args, name: str, n_seq: int):
+    """llama8b_q8 (headline, batch 1) and llama8b_q4 (four sequences)."""
+    import synth
+    base = synth.CONFIGS[name]
+    extra = max(args.steps, args.warmup, args.timing_steps, 1)
+    cfg = synth.variant(name, steps=extra)
+    log(f"generating {name} ({cfg.weight_bytes() / 1e9:.2f} GB of quantized weights)")
+    model = synth.make_model(cfg)
+    log("loading into HBM")
+    r = Runner(model, n_seq)
+    r.warm(args.warmup)                                     # also captures the step graph
+    ms_per_step = None
+    if not args.only_kernels:
+        ms_per_step = r.timed(args.steps)
+        log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step")
+    kstats, kbytes = r.kernel_profile(args.timing_steps)
+    L = cfg.n_layers
+    dom = "gateup" if name == "llama8b_q8" else dominant(kstats)
+    roofline = roofline_for(dom, kstats, kbytes, L, name)
+    step_bytes = r.step_bytes(args.steps // 2)
+    read_ms = r.g.debug_read_bw(4 << 30, 5)
+    if args.calibrate:
+        r.g.debug_read_bw(1 << 30, 1)
+        r.g.debug_dequant(0, 6, 0, 64, cfg.ffn)
+        log(f"calibration: read {1 << 30} bytes; dequant wrote {64 * cfg.ffn * 4} bytes")
+    qt = "Q8_0" if cfg.qtype == synth.Q8_0 else "Q4_0"
+    config = {"workload": WORKLOAD_TEXT[name], "name": name, "batch": n_seq, "ctx": base.ctx, "qtype": qt,
+              "weights": "random N(0,0.02), quantized, resident in HBM"}
+    metric = HEADLINE_METRIC if name == "llama8b_q8" else \
+        f"decode tokens/s (aggregate over {n_seq} sequences) + achieved HBM GB/s, 8B-shape {qt} batch {n_seq}"
+    if ms_per_step is not None:
+        out = base_line(metric, 1000.0 * n_seq / ms_per_step, ms_per_step, args.steps, args.warmup,
+                        step_bytes, config)
+    else:
+        out = {"metric": metric, "config": config}
+    out["roofline"] = roofline
+    out["read_ceiling_GBps"] = round((4 << 30) / (read_ms * 1e-3) / 1e9, 1)
+    out["kernels"] = kernel_table(kstats, kbytes, L)
+    r.close()
+    if not args.no_cpu_baseline and not args.only_kernels:
+        log("oracle baseline")
+        out["cpu_baseline"] = public(cpu_baseline(model, cfg, n_seq, args.cpu_budget))
+    return out
+
+
+def run_multi(args):
+    """Three models resident together, decoded round-robin on three streams."""
+    import torch
+    import synth
+    names = ["multi_llama1b", "multi_qwen05b", "multi_smol360m"]
+    extra = max(args.steps, args.warmup, args.timing_steps, 1)
+    cfgs = [synth.variant(n, steps=extra) for n in names]
+    models, runners = [], []
+    for c in cfgs:
+        log(f"generating {c.name} ({c.weight_bytes() / 1e9:.2f} GB)")
+        models.append(synth.make_model(c))
+        runners.append(Runner(models[-1], 1))
+    for r in runners:
+        r.warm(args.warmup)
+    # each model alone
+    solo = {}
+    for r in runners:
+        solo[r.cfg.name] = r.timed(args.steps)
+        r.rewind()
+    # round-robin on three streams
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for r in runners:
+            r.step()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    ms_per_round = wall_ms / args.steps
+    log(f"round-robin: {ms_per_round:.4f} ms per round of 3 tokens; solo ms/step {solo}")
+    for r in runners:
+        r.rewind()
+    round_bytes = sum(r.step_bytes(args.steps // 2) for r in runners)
+    # kernel profile of the largest model (eager, alone)
+    kstats, kbytes = runners[0].kernel_profile(args.timing_steps)
+    dom = dominant(kstats)
+    config = {"workload": WORKLOAD_TEXT["multi"], "name": "multi", "batch": 1, "ctx": 2048, "qtype": "Q8_0",
+              "models": names, "weights": "random N(0,0.02), quantized, resident in HBM"}
+    out = base_line("decode tokens/s aggregate over three concurrently resident Q8_0 models "
+                    "(round-robin, one HIP stream each)", 3000.0 / ms_per_round, ms_per_round, args.steps,
+                    args.warmup, round_bytes, config)
+    out["per_model_solo_tokens_per_s"] = {k: round(1000.0 / v, 2) for k, v in solo.items()}
+    out["roofline"] = roofline_for(dom, kstats, kbytes, cfgs[0].n_layers, "multi_llama1b")
+    out["roofline"]["model"] = names[0]
+    out["kernels"] = kernel_table(kstats, kbytes, cfgs[0].n_layers)
+    for r in runners:
+        r.close()
+    if not args.no_cpu_baseline:
+        log("oracle baseline (the three models in turn)")
+        per = [cpu_baseline(m, c, 1, args.cpu_budget / 3, max_steps=32) for m, c in zip(models, cfgs)]
+        tot_s = sum(p["_seconds"] for p in per)
+        n_tok = sum(p["_tokens"] for p in per)
+        out["cpu_baseline"] = {"value": round(n_tok / tot_s, 4), "unit": "tokens/s", "cores": host_threads(),
+                               "kind": "oracle",
+                               "sample": "; ".join(f"{n}: {p['sample']}" for n, p in zip(names, per))}
+    return out
+
+
+def run_70b(args):
+    """(a) resident in HBM, (b) layer streaming from pinned host memory."""
+    import numpy as np
+    import synth
+    import token_decode_llama_amd as lm
+    name = "llama70b_q4"
+    extra = max(args.steps, args.warmup, args.timing_steps, 1)
+    cfg = synth.variant(name, steps=extra)
+    s, H, V = cfg.seed, cfg.hidden, cfg.vocab
+    log(f"generating {name} ({cfg.weight_bytes() / 1e9:.2f} GB of quantized weights), layer by layer")
+    model = synth.Model(cfg=cfg,
+                        tok_embd=synth.normal_f16_bits(s, synth.tensor_id(cfg, synth.T_EMBD), V * H, 0.0,
+                                                       0.02).reshape(V, H),
+                        out_norm=synth.normal_f32(s, synth.tensor_id(cfg, synth.T_OUT_NORM), H, 1.0, 0.1),
+                        lm_head=synth.quant_matrix(s, synth.tensor_id(cfg, synth.T_LM_HEAD), V, H, 0.02,
+                                                   cfg.qtype))
+    keep = not args.no_cpu_baseline
+
+    def loader(stream):
+        g = lm.Model(cfg, max_seqs=1, stream=stream)
+        for l in range(cfg.n_layers):
+            w = synth.make_layer(cfg, l)
+            g.load_layer(l, w)
+            if keep:
+                model.layers.append(w)
+            if l % 10 == 9:
+                log(f"  layer {l + 1}/{cfg.n_layers} loaded")
+        g.load_global(model.tok_embd, model.out_norm, model.lm_head)
+        for l in range(cfg.n_layers):
+            g.load_kv(0, l, *synth.make_kv(cfg, 0, l))
+        return g
+
+    r = Runner(model, 1, loader=loader)
+    r.warm(args.warmup)
+    ms_res = r.timed(args.steps)
+    log(f"resident: {ms_res:.3f} ms/step")
+    kstats, kbytes = r.kernel_profile(args.timing_steps)
+    step_bytes = r.step_bytes(args.steps // 2)
+    dom = dominant(kstats)
+    roof = roofline_for(dom, kstats, kbytes, cfg.n_layers, name)
+    ktab = kernel_table(kstats, kbytes, cfg.n_layers)
+    # the resident step's compute time per step (eager, from the kernel events)
+    compute_ms = sum(ms for k, (n, ms) in kstats.items() if k != "copy") / args.timing_steps
+
+    log("switching to layer streaming")
+    r.g.stream_mode(True)
+    r.warm(1)
+    n_st = args.stream_steps
+    ms_st = r.timed(n_st)
+    log(f"streaming: {ms_st:.3f} ms/step")
+    # copy and compute event totals over streamed steps
+    r.rewind()
+    r.g.kernel_timing(True)
+    ms_st_timed = r.timed(n_st)          # wall time of the same instrumented steps
+    sk = {k: r.g.kernel_stats(k) for k in lm.KERNEL_KINDS}
+    r.g.kernel_timing(False)
+    copy_bytes = r.g.kernel_bytes("copy", 1)
+    r.rewind()
+    t_copy = sk["copy"][1] / n_st
+    t_comp = sum(ms for k, (n, ms) in sk.items() if k != "copy") / n_st
+    overlap = (t_copy + t_comp - ms_st_timed) / min(t_copy, t_comp) if min(t_copy, t_comp) > 0 else None
+    config = {"workload": WORKLOAD_TEXT[name], "name": name, "batch": 1, "ctx": cfg.ctx, "qtype": "Q4_0",
+              "weights": "random N(0,0.02), quantized; (a) resident in HBM, (b) streamed per layer from "
+                         "pinned host memory"}
+    out = base_line("decode tokens/s + achieved HBM GB/s, 70B-shape Q4_0 batch 1, weights resident in HBM",
+                    1000.0 / ms_res, ms_res, args.steps, args.warmup, step_bytes, config)
+    out["roofline"] = roof
+    out["kernels"] = ktab
+    out["streaming"] = {
+        "value": round(1000.0 / ms_st, 4), "unit": "tokens/s", "steps": n_st, "ms_per_step": round(ms_st, 2),
+        "host_link_GBps": round(copy_bytes / (ms_st * 1e-3) / 1e9, 2),
+        "copy_only_GBps": round(copy_bytes / (t_copy * 1e-3) / 1e9, 2) if t_copy else None,
+        "layer_blob_bytes": int(copy_bytes / cfg.n_layers),
+        "sum_copy_ms": round(t_copy, 2), "sum_compute_ms": round(t_comp, 3),
+        "instrumented_wall_ms": round(ms_st_timed, 2),
+        "serial_copy_then_compute_ms": round(t_copy + t_comp, 2),
+        "overlap_fraction": round(overlap, 4) if overlap is not None else None,
+        "overlap_definition": "(sum copy + sum compute - wall) / min(sum copy, sum compute), per step, all "
+                              "three from the same steps with HIP events around every copy and kernel",
+        "resident_compute_ms_eager": round(compute_ms, 3)}
+    r.close()
+    if keep:
+        log("oracle baseline (bounded sample)")
+        out["cpu_baseline"] = public(cpu_baseline(model, cfg, 1, args.cpu_budget, max_steps=2))
+    return out
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default: the workload's own)")
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="llama8b_q8")
+    ap.add_argument("--workload", default="llama8b_q8",
+                    choices=["llama8b_q8", "llama8b_q4", "multi", "llama70b_q4"])
     ap.add_argument("--timing-steps", type=int, default=8,
                     help="eager steps with per-kernel HIP events for the roofline")
+    ap.add_argument("--stream-steps", type=int, default=16, help="timed steps in layer-streaming mode (70B)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-kernels", action="store_true",
@@ -111,120 +465,22 @@ def main():
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the per-GPU throughput is the --gpus 1 figure)", file=sys.stderr)
         sys.exit(2)
+    if args.steps is None:
+        args.steps = {"llama8b_q8": 64, "llama8b_q4": 32, "multi": 32, "llama70b_q4": 16}[args.workload]
 
-    import numpy as np
     import torch
-    import synth
-    import token_decode_llama_amd as lm
-
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
-    base = synth.CONFIGS[args.workload]
-    extra = max(args.steps, args.warmup, args.timing_steps, 1)
-    cfg = synth.variant(args.workload, steps=extra)
-    log(f"generating {args.workload} ({cfg.weight_bytes() / 1e9:.2f} GB of quantized weights)")
-    model = synth.make_model(cfg)
-    stream = torch.cuda.Stream()          # the model's stream (default priority)
-    log("loading into HBM")
-    g = lm.open_model(model, lambda s, l: synth.make_kv(cfg, s, l), max_seqs=1, kv_seqs=1,
-                      stream=stream.cuda_stream)
-    dev = torch.device("cuda:0")
-    with torch.cuda.stream(stream):
-        tok = torch.from_numpy(synth.start_tokens(cfg, 1)).to(dev)
-        d_tok = tok.clone()
-    torch.cuda.synchronize()
-
-    # warm-up (also captures the step graph), then rewind to the prefill length
-    for _ in range(args.warmup):
-        g.step_dev(d_tok, 1, d_tok)
-    torch.cuda.synchronize()
-    g.set_position(0, cfg.ctx)
-    with torch.cuda.stream(stream):
-        d_tok.copy_(tok)
-    torch.cuda.synchronize()
-
-    ms_per_step = None
-    if not args.only_kernels:
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(args.steps):
-            g.step_dev(d_tok, 1, d_tok)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms_per_step = e0.elapsed_time(e1) / args.steps
-        log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step")
-
-    # per-kernel durations from HIP events on the model's stream (eager steps)
-    g.set_position(0, cfg.ctx)
-    with torch.cuda.stream(stream):
-        d_tok.copy_(tok)
-    torch.cuda.synchronize()
-    g.kernel_timing(True)
-    for _ in range(args.timing_steps):
-        g.step_dev(d_tok, 1, d_tok)
-    torch.cuda.synchronize()
-    kstats = {}
-    for k in lm.KERNEL_KINDS:
-        n, ms = g.kernel_stats(k)
-        kstats[k] = (n, ms)
-    g.kernel_timing(False)
-    L = cfg.n_layers
-    # bytes at the positions the timing steps ran at (their mean position)
-    g.set_position(0, cfg.ctx + args.timing_steps // 2)
-    kbytes = {k: g.kernel_bytes(k, 1) for k in lm.KERNEL_KINDS}
-    g.set_position(0, cfg.ctx + args.steps // 2)
-    step_bytes = sum(g.kernel_bytes(k, 1) for k in lm.KERNEL_KINDS)
-    g.set_position(0, cfg.ctx)
-
-    n_dom, ms_dom = kstats[DOMINANT]
-    per_launch_bytes = kbytes[DOMINANT] / L
-    avg_ms = ms_dom / max(n_dom, 1)
-    achieved = per_launch_bytes / (avg_ms * 1e-3) / 1e9
-    kernels = {k: {"launches": kstats[k][0],
-                   "avg_us": round(1e3 * kstats[k][1] / max(kstats[k][0], 1), 3),
-                   "algorithmic_GBps": round((kbytes[k] / (L if k not in ("embed", "lmhead") else 1))
-                                             / (kstats[k][1] / max(kstats[k][0], 1) * 1e-3) / 1e9, 1)
-                   if kstats[k][0] else None}
-               for k in lm.KERNEL_KINDS}
-    read_ms = g.debug_read_bw(4 << 30, 5)
-    read_ceiling = (4 << 30) / (read_ms * 1e-3) / 1e9
-
-    if args.calibrate:
-        g.debug_read_bw(1 << 30, 1)
-        g.debug_dequant(0, 6, 0, 64, cfg.ffn)
-        torch.cuda.synchronize()
-        log(f"calibration: read {1 << 30} bytes; dequant wrote {64 * cfg.ffn * 4} bytes")
-    traffic = traffic_from_profiles(DOMINANT, args.workload)
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": "k_gemv<Q8_0, gate/up, SwiGLU epilogue>",
-                "bytes_per_launch": int(per_launch_bytes), "avg_launch_us": round(avg_ms * 1e3, 3)}
-
-    out = {"metric": "decode tokens/s + achieved HBM GB/s (% of peak), 8B-shape Q8_0 batch 1"}
-    if ms_per_step is not None:
-        tps = 1000.0 / ms_per_step
-        gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
-        out.update({"value": round(tps, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-                    "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-                    "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-                    "dtype": "f32", "data": "synthetic",
-                    "achieved_hbm_GBps": round(gbps, 1),
-                    "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
-                    "step_bytes": int(step_bytes)})
-    out["config"] = {"workload": WORKLOAD_TEXT.get(args.workload, args.workload), "name": args.workload,
-                     "batch": 1, "ctx": base.ctx, "qtype": "Q8_0" if cfg.qtype == synth.Q8_0 else "Q4_0",
-                     "weights": "random N(0,0.02), quantized, resident in HBM"}
-    out["roofline"] = roofline
-    out["read_ceiling_GBps"] = round(read_ceiling, 1)
-    out["kernels"] = kernels
-    if not args.no_cpu_baseline and not args.only_kernels:
-        log("oracle baseline")
-        out["cpu_baseline"] = cpu_baseline(model, cfg, args.cpu_budget)
-    g.close()
+    if args.workload == "llama8b_q8":
+        out = run_single(args, "llama8b_q8", 1)
+    elif args.workload == "llama8b_q4":
+        out = run_single(args, "llama8b_q4", 4)
+    elif args.workload == "multi":
+        out = run_multi(args)
+    else:
+        out = run_70b(args)
     print(json.dumps(out), flush=True)
 
 

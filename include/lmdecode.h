@@ -169,14 +169,18 @@ const char* lm_last_error(const lm_model* m);
 
 /* ---- measurement and inspection ---------------------------------------- */
 
-/* Kernel families of one step (for timing and profiling). */
+/* Kernel families of one step (for timing and profiling).  LM_K_COPY is the
+ * host-to-HBM copy of one layer blob on the copy stream in streaming mode
+ * (its durations are those copies' events; its bytes are the blobs copied per
+ * step, zero when the weights are resident). */
 typedef enum {
     LM_K_EMBED = 0, LM_K_QKV = 1, LM_K_ATTN = 2, LM_K_WO = 3, LM_K_GATEUP = 4,
-    LM_K_DOWN = 5, LM_K_LMHEAD = 6, LM_K_COUNT = 7
+    LM_K_DOWN = 5, LM_K_LMHEAD = 6, LM_K_COPY = 7, LM_K_COUNT = 8
 } lm_kernel_kind;
 
 /* enable = 1: eager steps record HIP events around every kernel of every
- * kind on the model's stream and accumulate their durations; graph replay is
+ * kind on the model's stream (and around every layer copy on the copy stream
+ * in streaming mode) and accumulate their durations; graph replay is
  * suspended while timing is on.  Resets the totals. */
 lm_status lm_kernel_timing(lm_model* m, int32_t enable);
 

@@ -28,6 +28,8 @@ CASES = {
     # 8B layer shapes in Q4_0 with a long context (65 attention chunks)
     "llama8b_q4_2layers_ctx4k": synth.variant("llama8b_q8", n_layers=2, qtype=Q4_0, ctx=4090,
                                               steps=3, batch=1),
+    # the 70B shape's layers (hidden 8192, ffn 28672, 64/8 heads) in Q4_0 at its context length
+    "llama70b_q4_2layers": synth.variant("llama70b_q4", n_layers=2, steps=2),
 }
 
 _models = {}
@@ -134,7 +136,7 @@ def test_graph_replay_equals_eager():
         g.close()
 
 
-@pytest.mark.parametrize("name", ["tiny_q8", "llama1b_2layers"])
+@pytest.mark.parametrize("name", ["tiny_q8", "llama1b_2layers", "llama70b_q4_2layers"])
 def test_stream_mode_bit_identical(name):
     model = get_model(name)
     cfg = model.cfg

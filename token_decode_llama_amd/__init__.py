@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(HERE, "liblmdecode.so")
 
 LM_OK, LM_E_ARG, LM_E_STATE, LM_E_OOM, LM_E_HIP, LM_E_CTX = range(6)
 LM_Q4_0, LM_Q8_0 = 2, 8
-KERNEL_KINDS = ("embed", "qkv", "attn", "wo", "gateup", "down", "lmhead")
+KERNEL_KINDS = ("embed", "qkv", "attn", "wo", "gateup", "down", "lmhead", "copy")
 
 # every symbol include/lmdecode.h declares
 EXPORTS = (

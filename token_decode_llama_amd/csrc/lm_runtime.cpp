@@ -123,6 +123,7 @@ struct lm_model {
     int *d_tokens = nullptr, *d_argmax = nullptr, *d_pos = nullptr;
     float *d_cos = nullptr, *d_sin = nullptr;
     float* d_attn_part = nullptr;
+    int* d_attn_cnt = nullptr;            // [max_seqs][nkv] attention chunk counters
     float* d_lm_pval = nullptr;
     int* d_lm_pidx = nullptr;
     int* d_lm_cnt = nullptr;
@@ -441,6 +442,7 @@ extern "C" lm_status lm_model_create(const lm_config* cfg, void* hip_stream, lm_
     CREATE_TRY(dev_alloc(m, (void**)&m->d_lm_pval, (int64_t)S * m->gemv_max_blocks * 4, "argmax partials"));
     CREATE_TRY(dev_alloc(m, (void**)&m->d_lm_pidx, (int64_t)S * m->gemv_max_blocks * 4, "argmax partial ids"));
     CREATE_TRY(dev_alloc(m, (void**)&m->d_lm_cnt, (int64_t)S * 4, "argmax counters"));
+    CREATE_TRY(dev_alloc(m, (void**)&m->d_attn_cnt, (int64_t)S * m->nkv * 4, "attention chunk counters"));
     CREATE_TRY(dev_alloc(m, (void**)&m->d_sink, 4096 * 4, "sink"));
     m->dbg_floats = std::max<int64_t>({m->H, m->F, m->qrows}) * 64;
     CREATE_TRY(dev_alloc(m, (void**)&m->d_dbg, m->dbg_floats * 4, "debug rows"));
@@ -450,6 +452,7 @@ extern "C" lm_status lm_model_create(const lm_config* cfg, void* hip_stream, lm_
 
     // zero what must start at zero (counters, caches, positions)
     CREATE_HIP(hipMemsetAsync(m->d_lm_cnt, 0, (size_t)S * 4, m->stream));
+    CREATE_HIP(hipMemsetAsync(m->d_attn_cnt, 0, (size_t)(S * m->nkv * 4), m->stream));
     CREATE_HIP(hipMemsetAsync(m->d_pos, 0, (size_t)S * 4, m->stream));
     CREATE_HIP(hipMemsetAsync(m->d_k, 0, (size_t)(L * kv_layer_elems(m) * 2), m->stream));
     CREATE_HIP(hipMemsetAsync(m->d_v, 0, (size_t)(L * kv_layer_elems(m) * 2), m->stream));
@@ -732,6 +735,7 @@ struct KTimer {
 static lm_status collect_timing(lm_model* m) {
     if (m->pending.empty()) return LM_OK;
     HIPTRY(m, hipStreamSynchronize(m->stream));
+    HIPTRY(m, hipStreamSynchronize(m->copy_stream));
     for (auto& p : m->pending) {
         float ms = 0.f;
         if (hipEventElapsedTime(&ms, p.a, p.b) == hipSuccess) {
@@ -751,8 +755,17 @@ static const uint8_t* layer_blob(lm_model* m, int l) {
 static lm_status stream_copy(lm_model* m, int layer) {
     const int slot = layer & 1;
     HIPTRY(m, hipStreamWaitEvent(m->copy_stream, m->ev_consumed[slot], 0));
+    hipEvent_t a = m->timing ? pool_event(m) : nullptr;
+    if (a) HIPTRY(m, hipEventRecord(a, m->copy_stream));
     HIPTRY(m, hipMemcpyAsync(m->d_sbuf[slot], m->h_arena + (int64_t)layer * m->blob_bytes,
                              (size_t)m->blob_bytes, hipMemcpyHostToDevice, m->copy_stream));
+    if (a) {
+        hipEvent_t b = pool_event(m);
+        if (b) {
+            HIPTRY(m, hipEventRecord(b, m->copy_stream));
+            m->pending.push_back({LM_K_COPY, a, b});
+        }
+    }
     HIPTRY(m, hipEventRecord(m->ev_copied[slot], m->copy_stream));
     return LM_OK;
 }
@@ -798,6 +811,7 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
     at.max_chunks = m->max_chunks;
     at.scale = (float)(1.0 / std::sqrt((double)m->hd));
     at.part = m->d_attn_part;
+    at.counter = m->d_attn_cnt;
     at.out = m->d_o;
 
     if (m->streaming) {
@@ -1075,6 +1089,7 @@ extern "C" lm_status lm_kernel_bytes(const lm_model* m, int32_t kind, int32_t n_
         case LM_K_GATEUP: b = L * (2 * F * H * bpw + H * 4 + S * (H * 4 + F * 4)); break;
         case LM_K_DOWN: b = L * (H * F * bpw + S * (F * 4 + H * 8)); break;
         case LM_K_LMHEAD: b = V * H * bpw + H * 4 + S * H * 4; break;
+        case LM_K_COPY: b = m->streaming ? L * (double)m->blob_bytes : 0.0; break;
     }
     *bytes = b;
     return LM_OK;
