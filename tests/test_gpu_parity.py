@@ -25,6 +25,9 @@ CASES = {
     "qwen05b_2layers": synth.variant("multi_qwen05b", n_layers=2, ctx=130, steps=3),
     "smol360m_2layers": synth.variant("multi_smol360m", n_layers=2, ctx=70, steps=3),
     "llama1b_2layers": synth.variant("multi_llama1b", n_layers=2, ctx=64, steps=3),
+    # the attention context crosses a 256-position chunk: one chunk, then a
+    # second chunk holding a single key (wavefronts with no valid key)
+    "llama1b_2layers_ctx255": synth.variant("multi_llama1b", n_layers=2, ctx=255, steps=3),
     # 8B layer shapes in Q4_0 with a long context (65 attention chunks)
     "llama8b_q4_2layers_ctx4k": synth.variant("llama8b_q8", n_layers=2, qtype=Q4_0, ctx=4090,
                                               steps=3, batch=1),

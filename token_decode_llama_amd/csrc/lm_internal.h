@@ -73,6 +73,7 @@ struct AttnArgs {
     int nq, nkv, hd, max_ctx, max_chunks;
     float scale;           // 1/sqrt(hd)
     float* part;           // [n_seq][nq][max_chunks][hd + 2] partial o, m, l
+    int* counter;          // [n_seq][nkv] chunks finished, zero between launches
     float* out;            // [n_seq][nq*hd]
 };
 

@@ -908,23 +908,41 @@ hipError_t launch_gemv_batched(const GemvArgs& a0, int epi, int n_seq, int max_b
 // ---------------------------------------------------------------------------
 // GQA decode attention with causal softmax, split over context
 // ---------------------------------------------------------------------------
+// One workgroup per (64-position chunk, KV head, sequence).  The chunk's K and
+// V tiles are read with coalesced 16-byte loads (issued before anything
+// else), staged in LDS (K rows padded so that a lane per key reads
+// conflict-free), and every query head of the group is scored against them:
+// a wavefront per head, a lane per key, causal mask = keys 0..pos.  PV runs
+// as thread = (head, 8 dimensions, quarter of the keys) with a reduction
+// over the quarters in LDS.  A context that fits one chunk writes o
+// directly; otherwise each chunk publishes its softmax state (m, l, o) with
+// device-coherent stores, and the last chunk of the (sequence, KV head) to
+// finish merges all of them (log-sum-exp) within the same launch.
 constexpr int kMaxGroup = 8;   // query heads per KV head
 
-// Phase 1: one workgroup per (64-position chunk, KV head, sequence).  The
-// chunk's K/V tile and the group's q are requested before the position is
-// known (rows clamped to the cache), staged in LDS, and every query head of
-// the group is scored against the tile (causal mask: keys 0..pos).  Writes
-// the chunk's softmax state: row max m, sum l = sum exp(s - m), and the
-// unnormalised o = sum exp(s - m) v.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// this wavefront's outstanding memory operations have completed (gfx9 vmcnt(0))
+__device__ __forceinline__ void drain_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 template <int HD>
 __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
     constexpr int CH = kAttnChunk;
-    constexpr int KP = HD + 8;   // K row stride in halves: 16-byte aligned, conflict-free 16-byte reads
+    constexpr int KP = HD + 8;                  // padded K row (halves)
+    constexpr int PCS = CH * HD / 8 / kBlock;   // 16-byte pieces per thread per tile
+    // the K tile is dead once the scores are taken: the PV partial sums reuse it
+    static_assert(sizeof(float) * kWaves * kMaxGroup * HD <= sizeof(__half) * CH * KP, "Os fits in Ks");
     __shared__ __align__(16) __half Ks[CH][KP];
     __shared__ __align__(16) __half Vs[CH][HD];
     __shared__ __align__(16) float Qs[kMaxGroup][HD];
     __shared__ __align__(16) float Ps[kMaxGroup][CH];
-    __shared__ __align__(16) float Os[kWaves][kMaxGroup * HD];
+    __shared__ float Ms[kMaxGroup], Ls[kMaxGroup];
+    __shared__ int s_last;
+    float (*Os)[kMaxGroup * HD] = reinterpret_cast<float (*)[kMaxGroup * HD]>(&Ks[0][0]);
 
     const int chunk = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -932,32 +950,32 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
     const int t0 = chunk * CH;
     const int64_t stride = HD + 2;
 
-    // ---- loads (independent of the position)
+    // ---- every load first (rows clamped to the cache; masked below)
     const __half* Kg = a.kcache + (int64_t)s * a.kv_seq_stride + (int64_t)g * a.max_ctx * HD;
     const __half* Vg = a.vcache + (int64_t)s * a.kv_seq_stride + (int64_t)g * a.max_ctx * HD;
-    constexpr int kPer = CH * (HD / 8) / kBlock;     // 16-byte pieces per thread
-    uint4 kr[kPer], vr[kPer];
+    uint4 kr[PCS], vr[PCS];
     #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
+    for (int u = 0; u < PCS; ++u) {
         const int c = tid + u * kBlock;
         const int t = min(t0 + c / (HD / 8), a.max_ctx - 1), d8 = (c % (HD / 8)) * 8;
         kr[u] = *(const uint4*)(Kg + (int64_t)t * HD + d8);
         vr[u] = *(const uint4*)(Vg + (int64_t)t * HD + d8);
     }
     const float* qg = a.q + (int64_t)s * a.nq * HD + (int64_t)g * G * HD;
-    constexpr int kQ = (kMaxGroup * HD / 4 + kBlock - 1) / kBlock;  // float4 pieces of q per thread
+    constexpr int kQ = (kMaxGroup * HD / 4 + kBlock - 1) / kBlock;
     float4 qv[kQ];
     #pragma unroll
     for (int u = 0; u < kQ; ++u) {
         const int i = min((tid + u * kBlock) * 4, G * HD - 4);
         qv[u] = *(const float4*)(qg + i);
     }
-    const int n_ctx = a.pos[s] + 1;                 // keys 0..pos inclusive
-    if (t0 >= n_ctx) return;                        // chunk past the causal horizon
+    const int n_ctx = a.pos[s] + 1;                       // keys 0..pos inclusive
+    const int n_act = (n_ctx + CH - 1) / CH;
+    if (chunk >= n_act) return;                           // chunk past the causal horizon
     const int nt = min(CH, n_ctx - t0);
 
     #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
+    for (int u = 0; u < PCS; ++u) {
         const int c = tid + u * kBlock;
         const int t = c / (HD / 8), d8 = (c % (HD / 8)) * 8;
         *(uint4*)&Ks[t][d8] = kr[u];
@@ -970,7 +988,6 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
     }
     __syncthreads();
 
-    float* part_s = a.part + (int64_t)s * a.nq * a.max_chunks * stride;
     // ---- scores: a wavefront per query head, a lane per key
     for (int j = wave; j < G; j += kWaves) {
         float sc = -FLT_MAX;
@@ -1000,15 +1017,11 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
         const float p = lane < nt ? __expf(sc - m) : 0.f;
         const float l = wave_sum(p);
         Ps[j][lane] = p;
-        if (lane == 0) {
-            float* ph = part_s + ((int64_t)(g * G + j) * a.max_chunks + chunk) * stride;
-            ph[HD] = m;
-            ph[HD + 1] = l;
-        }
+        if (lane == 0) { Ms[j] = m; Ls[j] = l; }
     }
     __syncthreads();
 
-    // ---- o = sum_t p_t v_t: thread (head j, 8 dims, quarter of the keys)
+    // ---- o = sum_t p_t v_t: thread (head j, 8 dims, quarter w of the keys)
     constexpr int D8 = HD / 8;
     for (int idx = tid; idx < G * D8 * kWaves; idx += kBlock) {
         const int w = idx / (G * D8), r = idx % (G * D8);
@@ -1036,77 +1049,80 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
         *(float4*)(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
     }
     __syncthreads();
-    for (int i = tid; i < G * HD / 4; i += kBlock) {
-        float4 v = *(const float4*)&Os[0][i * 4];
-        #pragma unroll
-        for (int w = 1; w < kWaves; ++w) {
-            const float4 u = *(const float4*)&Os[w][i * 4];
-            v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
-        }
-        const int j = (i * 4) / HD, d = (i * 4) % HD;
-        float* ph = part_s + ((int64_t)(g * G + j) * a.max_chunks + chunk) * stride + d;
-        ph[0] = v.x; ph[1] = v.y; ph[2] = v.z; ph[3] = v.w;
-    }
-}
 
-// Phase 2: merge the chunks of each (sequence, query head): with
-// M = max_c m_c, o = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c.
-// A thread per output element.  Chunks are read in batches of 8 whose loads
-// are all independent; the first batch is requested together with the
-// position (chunks past the causal horizon are loaded, then ignored).
-template <int HD>
-__global__ __launch_bounds__(HD) void k_attn_merge(AttnArgs a) {
-    constexpr int B = 8;
-    const int h = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
-    const int64_t stride = HD + 2;
-    const float* ph = a.part + ((int64_t)s * a.nq + h) * a.max_chunks * stride;
-    float mv[B], lv[B], ov[B];
-    auto fetch = [&](int base) {
-        #pragma unroll
-        for (int u = 0; u < B; ++u) {
-            const int c = min(base + u, a.max_chunks - 1);
-            mv[u] = ph[c * stride + HD];
-            lv[u] = ph[c * stride + HD + 1];
-            ov[u] = ph[c * stride + d];
+    float* part_s = a.part + (int64_t)s * a.nq * a.max_chunks * stride;
+    float* out_s = a.out + (int64_t)s * a.nq * HD + (int64_t)g * G * HD;
+    if (n_act == 1) {
+        for (int i = tid; i < G * HD; i += kBlock) {
+            float v = Os[0][i];
+            #pragma unroll
+            for (int w = 1; w < kWaves; ++w) v += Os[w][i];
+            out_s[i] = v / Ls[i / HD];
         }
-    };
-    fetch(0);
-    const int n_act = (a.pos[s] + 1 + kAttnChunk - 1) / kAttnChunk;
-    float M = -FLT_MAX, L = 0.f, O = 0.f;
-    for (int base = 0; base < n_act; base += B) {
-        if (base > 0) fetch(base);
-        float bm = -FLT_MAX;
-        #pragma unroll
-        for (int u = 0; u < B; ++u)
-            if (base + u < n_act) bm = fmaxf(bm, mv[u]);
-        const float Mn = fmaxf(M, bm);
-        const float r = __expf(M - Mn);
-        L *= r;
-        O *= r;
-        #pragma unroll
-        for (int u = 0; u < B; ++u)
-            if (base + u < n_act) {
-                const float e = __expf(mv[u] - Mn);
-                L = fmaf(lv[u], e, L);
-                O = fmaf(ov[u], e, O);
-            }
-        M = Mn;
+        return;
     }
-    a.out[(int64_t)s * a.nq * HD + (int64_t)h * HD + d] = O / L;
+    for (int i = tid; i < G * HD; i += kBlock) {
+        float v = Os[0][i];
+        #pragma unroll
+        for (int w = 1; w < kWaves; ++w) v += Os[w][i];
+        const int j = i / HD, d = i % HD;
+        float* ph = part_s + ((int64_t)(g * G + j) * a.max_chunks + chunk) * stride;
+        st_dev(ph + d, v);
+        if (d == 0) { st_dev(ph + HD, Ms[j]); st_dev(ph + HD + 1, Ls[j]); }
+    }
+
+    // ---- the last chunk of this (sequence, KV head) merges every chunk.  The
+    // partials are device-coherent stores, each wavefront waits for its own
+    // to complete before the count is taken.
+    drain_vm();
+    __syncthreads();
+    if (tid == 0) {
+        const int old = __hip_atomic_fetch_add(&a.counter[s * a.nkv + g], 1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (old == n_act - 1);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    constexpr int B = 8;
+    for (int idx = tid; idx < G * HD; idx += kBlock) {
+        const int j = idx / HD, d = idx % HD;
+        const float* ph = part_s + (int64_t)(g * G + j) * a.max_chunks * stride;
+        float M = -FLT_MAX, L = 0.f, O = 0.f;
+        for (int base = 0; base < n_act; base += B) {
+            float mv[B], lv[B], ov[B];
+            #pragma unroll
+            for (int u = 0; u < B; ++u) {
+                const int c = min(base + u, n_act - 1);
+                mv[u] = ld_dev(ph + c * stride + HD);
+                lv[u] = ld_dev(ph + c * stride + HD + 1);
+                ov[u] = ld_dev(ph + c * stride + d);
+            }
+            float bm = M;
+            #pragma unroll
+            for (int u = 0; u < B; ++u)
+                if (base + u < n_act) bm = fmaxf(bm, mv[u]);
+            const float r = __expf(M - bm);
+            L *= r;
+            O *= r;
+            #pragma unroll
+            for (int u = 0; u < B; ++u)
+                if (base + u < n_act) {
+                    const float e = __expf(mv[u] - bm);
+                    L = fmaf(lv[u], e, L);
+                    O = fmaf(ov[u], e, O);
+                }
+            M = bm;
+        }
+        out_s[idx] = O / L;
+    }
+    if (tid == 0) __hip_atomic_store(&a.counter[s * a.nkv + g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 hipError_t launch_attention(const AttnArgs& a, int n_seq, hipStream_t st) {
     dim3 grid(a.max_chunks, a.nkv, n_seq);
-    dim3 mgrid(a.nq, n_seq);
-    if (a.hd == 128) {
-        hipLaunchKernelGGL(k_attn<128>, grid, dim3(kBlock), 0, st, a);
-        hipLaunchKernelGGL(k_attn_merge<128>, mgrid, dim3(128), 0, st, a);
-    } else if (a.hd == 64) {
-        hipLaunchKernelGGL(k_attn<64>, grid, dim3(kBlock), 0, st, a);
-        hipLaunchKernelGGL(k_attn_merge<64>, mgrid, dim3(64), 0, st, a);
-    } else {
-        return hipErrorInvalidValue;
-    }
+    if (a.hd == 128) hipLaunchKernelGGL(k_attn<128>, grid, dim3(kBlock), 0, st, a);
+    else if (a.hd == 64) hipLaunchKernelGGL(k_attn<64>, grid, dim3(kBlock), 0, st, a);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
