@@ -60,6 +60,7 @@ KERNEL_NAMES = {
     "gateup": "k_gemv<gate/up, RMSNorm prologue, SwiGLU epilogue>",
     "down": "k_gemv<down, residual epilogue>",
     "lmhead": "k_gemv<LM head, RMSNorm prologue, argmax epilogue>",
+    "step": "k_step (persistent one-kernel decode step: LDS weight ring + operator chain)",
 }
 
 
@@ -69,7 +70,7 @@ def log(*a):
 
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("lm_kernels.hip", "lm_internal.h"):
+    for f in ("lm_kernels.hip", "lm_internal.h", "lm_step.hip", "lm_step.h", "lm_device.h"):
         with open(os.path.join(ROOT, "token_decode_llama_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -201,7 +202,7 @@ class Runner:
         import token_decode_llama_amd as lm
         for s in range(self.n_seq):
             self.g.set_position(s, self.cfg.ctx + at_step)
-        b = sum(self.g.kernel_bytes(k, self.n_seq) for k in lm.KERNEL_KINDS if k != "copy")
+        b = sum(self.g.kernel_bytes(k, self.n_seq) for k in lm.KERNEL_KINDS if k not in ("copy", "step"))
         self.rewind()
         return b
 
@@ -210,7 +211,7 @@ class Runner:
 
 
 def per_launch(kind: str, n_layers: int) -> int:
-    return 1 if kind in ("embed", "lmhead") else n_layers
+    return 1 if kind in ("embed", "lmhead", "step") else n_layers
 
 
 def kernel_table(kstats, kbytes, n_layers):
@@ -269,7 +270,7 @@ def run_single(args, name: str, n_seq: int):
         log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step")
     kstats, kbytes = r.kernel_profile(args.timing_steps)
     L = cfg.n_layers
-    dom = "gateup" if name == "llama8b_q8" else dominant(kstats)
+    dom = dominant(kstats)
     roofline = roofline_for(dom, kstats, kbytes, L, name)
     step_bytes = r.step_bytes(args.steps // 2)
     read_ms = r.g.debug_read_bw(4 << 30, 5)
@@ -309,6 +310,9 @@ def run_multi(args):
         log(f"generating {c.name} ({c.weight_bytes() / 1e9:.2f} GB)")
         models.append(synth.make_model(c))
         runners.append(Runner(models[-1], 1))
+        # the models' steps overlap on the GPU: per-operator kernels (the
+        # persistent step needs every CU for itself)
+        runners[-1].g.set_persistent(False)
     for r in runners:
         r.warm(args.warmup)
     # each model alone

@@ -160,6 +160,22 @@ lm_status lm_decode_step_dev(lm_model* m, const int32_t* d_tokens, int32_t n_seq
 /* 1 (default): replay each step from a captured HIP graph; 0: launch eagerly. */
 lm_status lm_set_graph(lm_model* m, int32_t enable);
 
+/* One-sequence steps as one persistent kernel (available on models created
+ * with max_seqs = 1 whose widest GEMV input fits the kernel's LDS plan;
+ * weights resident, not in streaming mode; off by default).  One workgroup per CU
+ * streams that CU's share of every weight matrix through an LDS ring while
+ * its other wavefronts follow the step's operator chain (the C/CUDA Llama
+ * engine page, section 4.4: GEMV, RMSNorm, RoPE + KV append, causal softmax
+ * attention, SwiGLU, LM head, argmax), with grid-wide barriers between
+ * operators.  It keeps a tile-major copy of the weights in HBM (made at load).
+ * The kernel needs every CU: steps of two models must not overlap on one GPU
+ * while it is on (a wait that times out fails the step with LM_E_HIP when the
+ * step is synchronous).  enable = 0 selects the per-operator kernels; enable =
+ * 1 on a model without the kernel returns LM_E_STATE.  Results agree with the
+ * per-operator kernels within the same logit bound (different summation
+ * order), not bit for bit. */
+lm_status lm_set_persistent(lm_model* m, int32_t enable);
+
 /* The hipStream_t the model launches on. */
 void* lm_stream(const lm_model* m);
 
@@ -172,10 +188,11 @@ const char* lm_last_error(const lm_model* m);
 /* Kernel families of one step (for timing and profiling).  LM_K_COPY is the
  * host-to-HBM copy of one layer blob on the copy stream in streaming mode
  * (its durations are those copies' events; its bytes are the blobs copied per
- * step, zero when the weights are resident). */
+ * step, zero when the weights are resident).  LM_K_STEP is the persistent
+ * one-kernel step (lm_set_persistent); its bytes are those of the whole step. */
 typedef enum {
     LM_K_EMBED = 0, LM_K_QKV = 1, LM_K_ATTN = 2, LM_K_WO = 3, LM_K_GATEUP = 4,
-    LM_K_DOWN = 5, LM_K_LMHEAD = 6, LM_K_COPY = 7, LM_K_COUNT = 8
+    LM_K_DOWN = 5, LM_K_LMHEAD = 6, LM_K_COPY = 7, LM_K_STEP = 8, LM_K_COUNT = 9
 } lm_kernel_kind;
 
 /* enable = 1: eager steps record HIP events around every kernel of every
@@ -199,6 +216,18 @@ lm_status lm_kernel_bytes(const lm_model* m, int32_t kind, int32_t n_seq, double
  * 7 the LM head (layer ignored).  Values are exact (d * q fits fp32). */
 lm_status lm_debug_dequant(lm_model* m, int32_t layer, int32_t which, int32_t row0,
                            int32_t n_rows, float* out);
+
+/* One persistent step (as lm_decode_step_dev with d_argmax internal, no
+ * logits) that records timestamps of the 100 MHz constant clock into
+ * out[cu][phase][8] (host, capacity in uint64 words): [0] the phase starts
+ * (after the barrier), [1] the input vector is staged, [2] the first consumer
+ * wavefront has finished its tiles, [3] every consumer has finished (barrier
+ * arrival), [4] the first producer wavefront stores the phase's first tile;
+ * unused words are 0.  Phases: 5 per layer (QKV, attention, Wo, gate/up,
+ * down), then the LM head.  *n_cus and *n_phases give the extents.  Advances
+ * the position like a step.  For profiling the persistent kernel. */
+lm_status lm_debug_step_trace(lm_model* m, const int32_t* d_tokens, uint64_t* out, int64_t capacity,
+                              int32_t* n_cus, int32_t* n_phases);
 
 /* A plain read-only kernel over n_bytes of device memory (sum of 16-byte
  * words), for calibrating HBM counters and the read ceiling; *ms = average

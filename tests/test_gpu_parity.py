@@ -45,10 +45,12 @@ def get_model(name):
     return _models[name]
 
 
-def run_parity(model, n_seq, steps=None):
+def run_parity(model, n_seq, steps=None, persistent=False):
     cfg = model.cfg
     steps = steps or cfg.steps
     g = open_gpu(model, max_seqs=n_seq)
+    if persistent:
+        g.set_persistent(True)
     om = open_oracle(model, n_seq)
     toks = synth.start_tokens(cfg, n_seq)
     worst = 0.0
@@ -81,6 +83,12 @@ def run_parity(model, n_seq, steps=None):
 @pytest.mark.parametrize("name", list(CASES))
 def test_decode_parity(name):
     run_parity(get_model(name), n_seq=1)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_decode_parity_persistent(name):
+    """The same steps through the persistent one-kernel step."""
+    run_parity(get_model(name), n_seq=1, persistent=True)
 
 
 @pytest.mark.parametrize("name,n_seq", [("tiny_q8", 3), ("tiny_q4", 4)])
@@ -157,6 +165,8 @@ def test_stream_mode_bit_identical(name):
                 t = am
             return res
 
+        # streaming uses the per-operator kernels: compare against the same kernels resident
+        g.set_persistent(False)
         resident = run()
         g.stream_mode(True)
         streamed = run()

@@ -17,15 +17,16 @@ LIB_PATH = os.path.join(HERE, "liblmdecode.so")
 
 LM_OK, LM_E_ARG, LM_E_STATE, LM_E_OOM, LM_E_HIP, LM_E_CTX = range(6)
 LM_Q4_0, LM_Q8_0 = 2, 8
-KERNEL_KINDS = ("embed", "qkv", "attn", "wo", "gateup", "down", "lmhead", "copy")
+KERNEL_KINDS = ("embed", "qkv", "attn", "wo", "gateup", "down", "lmhead", "copy", "step")
 
 # every symbol include/lmdecode.h declares
 EXPORTS = (
     "lm_model_create", "lm_model_destroy", "lm_load_layer_weights", "lm_load_global_weights",
     "lm_load_kv", "lm_get_kv", "lm_set_position", "lm_get_position", "lm_stream_mode",
-    "lm_decode_step", "lm_decode_step_dev", "lm_set_graph", "lm_stream", "lm_last_error",
+    "lm_decode_step", "lm_decode_step_dev", "lm_set_graph", "lm_set_persistent", "lm_stream",
+    "lm_last_error",
     "lm_kernel_timing", "lm_kernel_stats", "lm_kernel_bytes", "lm_debug_dequant",
-    "lm_debug_read_bw",
+    "lm_debug_read_bw", "lm_debug_step_trace",
 )
 
 
@@ -76,6 +77,7 @@ def load():
         "lm_decode_step": ([vp, vp, i32, vp, vp], st),
         "lm_decode_step_dev": ([vp, vp, i32, vp, vp], st),
         "lm_set_graph": ([vp, i32], st),
+        "lm_set_persistent": ([vp, i32], st),
         "lm_stream": ([vp], vp),
         "lm_last_error": ([vp], ctypes.c_char_p),
         "lm_kernel_timing": ([vp, i32], st),
@@ -83,6 +85,7 @@ def load():
         "lm_kernel_bytes": ([vp, i32, i32, ctypes.POINTER(dbl)], st),
         "lm_debug_dequant": ([vp, i32, i32, i32, i32, vp], st),
         "lm_debug_read_bw": ([vp, i64, i32, ctypes.POINTER(dbl)], st),
+        "lm_debug_step_trace": ([vp, vp, vp, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)], st),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -209,6 +212,9 @@ class Model:
     def set_graph(self, enable: bool):
         self._check(self._lib.lm_set_graph(self._h, 1 if enable else 0))
 
+    def set_persistent(self, enable: bool):
+        self._check(self._lib.lm_set_persistent(self._h, 1 if enable else 0))
+
     # -- measurement ---------------------------------------------------------
     def kernel_timing(self, enable: bool):
         self._check(self._lib.lm_kernel_timing(self._h, 1 if enable else 0))
@@ -229,6 +235,16 @@ class Model:
         out = np.empty((n_rows, cols), np.float32)
         self._check(self._lib.lm_debug_dequant(self._h, layer, which, row0, n_rows, _p(out)))
         return out
+
+    def debug_step_trace(self, d_tokens) -> np.ndarray:
+        """Timestamps (100 MHz ticks) of one traced persistent step: [cu][phase][8]."""
+        ncu, nph = ctypes.c_int32(), ctypes.c_int32()
+        cap = 1024 * (5 * self.cfg.n_layers + 1) * 8
+        out = np.zeros(cap, np.uint64)
+        ptr = d_tokens if isinstance(d_tokens, int) else d_tokens.data_ptr()
+        self._check(self._lib.lm_debug_step_trace(self._h, ptr, _p(out), cap, ctypes.byref(ncu),
+                                                  ctypes.byref(nph)))
+        return out[:ncu.value * nph.value * 8].reshape(ncu.value, nph.value, 8)
 
     def debug_read_bw(self, n_bytes: int, iters: int = 10) -> float:
         ms = ctypes.c_double()

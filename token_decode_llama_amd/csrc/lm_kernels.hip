@@ -23,6 +23,7 @@
 //    last workgroup of a (sequence, KV head) to finish merges the chunks'
 //    partial softmax states (log-sum-exp) - no second launch.
 #include "lm_internal.h"
+#include "lm_device.h"
 
 #include <float.h>
 #include <limits.h>
@@ -30,104 +31,6 @@
 #include <algorithm>
 
 namespace lmk {
-
-constexpr int kBlock = 256;   // threads per workgroup (4 wavefronts)
-constexpr int kWaves = kBlock / 64;
-
-// ---------------------------------------------------------------------------
-// helpers
-// ---------------------------------------------------------------------------
-
-// 16-byte streaming load (weights are read once per token: non-temporal hint)
-typedef int v4i_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ int4 ld16_stream(const uint8_t* p) {
-#if LMK_WEIGHT_NT
-    const v4i_t v = __builtin_nontemporal_load((const v4i_t*)p);
-#else
-    const v4i_t v = *(const v4i_t*)p;
-#endif
-    return make_int4(v.x, v.y, v.z, v.w);
-}
-
-__device__ __forceinline__ float h2f(uint16_t h) {
-    return __half2float(__ushort_as_half(h));
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-    #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-    #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
-}
-
-// (value, index) maximum with the lowest index winning ties
-__device__ __forceinline__ void better(float& bv, int& bi, float v, int i) {
-    if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
-}
-
-// Activations enter the integer dot products as 24-bit fixed point: per
-// 32-column block b, X_i = rint(x_i * 127*2^16 / max|x_b|), split into three
-// balanced signed 8-bit digits X = D2*2^16 + D1*2^8 + D0 (two's-complement
-// bytes: D0 = low byte of X, D1 = low byte of (X+128)>>8, D2 = (X+2^15+128)>>16).
-// sum_i q_i x_i = sx_b * (2^16 S2 + 2^8 S1 + S0), S_k = sum_i q_i D_k,i, with
-// sx_b = max|x_b| / (127*2^16).  The S_k are exact int32 sums of v_dot4 products;
-// the only rounding is X's (relative 2^-24 of the block maximum) and the fp32
-// combination, the same order as an fp32 dot product.
-__device__ __forceinline__ int sdot4(int a, int b, int c) { return __builtin_amdgcn_sdot4(a, b, c, false); }
-
-__device__ __forceinline__ float combine_digits(int s0, int s1, int s2) {
-    return fmaf((float)(s2 * 256 + s1), 256.f, (float)s0);
-}
-
-// Q8_0 block: A = elements 0..15, B = 16..31 (int8); D = the block's digit
-// planes [D0 0..15][D0 16..31][D1 ..][D1 ..][D2 ..][D2 ..] as int4s.
-__device__ __forceinline__ float dot_q8(const int4 A, const int4 B, const int4* D) {
-    const int4 e0 = D[0], e1 = D[1], f0 = D[2], f1 = D[3], g0 = D[4], g1 = D[5];
-    int s0 = sdot4(A.x, e0.x, 0), s1 = sdot4(A.x, f0.x, 0), s2 = sdot4(A.x, g0.x, 0);
-    s0 = sdot4(A.y, e0.y, s0); s1 = sdot4(A.y, f0.y, s1); s2 = sdot4(A.y, g0.y, s2);
-    s0 = sdot4(A.z, e0.z, s0); s1 = sdot4(A.z, f0.z, s1); s2 = sdot4(A.z, g0.z, s2);
-    s0 = sdot4(A.w, e0.w, s0); s1 = sdot4(A.w, f0.w, s1); s2 = sdot4(A.w, g0.w, s2);
-    s0 = sdot4(B.x, e1.x, s0); s1 = sdot4(B.x, f1.x, s1); s2 = sdot4(B.x, g1.x, s2);
-    s0 = sdot4(B.y, e1.y, s0); s1 = sdot4(B.y, f1.y, s1); s2 = sdot4(B.y, g1.y, s2);
-    s0 = sdot4(B.z, e1.z, s0); s1 = sdot4(B.z, f1.z, s1); s2 = sdot4(B.z, g1.z, s2);
-    s0 = sdot4(B.w, e1.w, s0); s1 = sdot4(B.w, f1.w, s1); s2 = sdot4(B.w, g1.w, s2);
-    return combine_digits(s0, s1, s2);
-}
-
-// Q4_0 block: 16 bytes, byte j = element j (low nibble) | element j+16 (high).
-// The nibbles n = q + 8 enter the dot products unsigned; T = the block's digit
-// sums (T0, T1, T2) remove the 8 offset.
-__device__ __forceinline__ float dot_q4(const int4 A, const int4* D, const int4 T) {
-    const int4 e0 = D[0], e1 = D[1], f0 = D[2], f1 = D[3], g0 = D[4], g1 = D[5];
-    const int w[4] = {A.x, A.y, A.z, A.w};
-    const int E0[4] = {e0.x, e0.y, e0.z, e0.w}, E1[4] = {e1.x, e1.y, e1.z, e1.w};
-    const int F0[4] = {f0.x, f0.y, f0.z, f0.w}, F1[4] = {f1.x, f1.y, f1.z, f1.w};
-    const int G0[4] = {g0.x, g0.y, g0.z, g0.w}, G1[4] = {g1.x, g1.y, g1.z, g1.w};
-    int s0 = -8 * T.x, s1 = -8 * T.y, s2 = -8 * T.z;
-    #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int lo = w[u] & 0x0F0F0F0F, hi = (int)(((unsigned)w[u] >> 4) & 0x0F0F0F0Fu);
-        s0 = sdot4(lo, E0[u], s0); s1 = sdot4(lo, F0[u], s1); s2 = sdot4(lo, G0[u], s2);
-        s0 = sdot4(hi, E1[u], s0); s1 = sdot4(hi, F1[u], s1); s2 = sdot4(hi, G1[u], s2);
-    }
-    return combine_digits(s0, s1, s2);
-}
-
-__device__ __forceinline__ float block_sum(float v, float* red) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    v = wave_sum(v);
-    __syncthreads();
-    if (lane == 0) red[wave] = v;
-    __syncthreads();
-    float t = 0.f;
-    #pragma unroll
-    for (int w = 0; w < kWaves; ++w) t += red[w];
-    return t;
-}
 
 // ---------------------------------------------------------------------------
 // embedding: x[s] = fp32(E[token[s]])
@@ -154,71 +57,6 @@ hipError_t launch_embed(const uint16_t* tok_embd, const int* tokens, int vocab, 
     dim3 grid((hidden / 4 + kBlock - 1) / kBlock, n_seq);
     hipLaunchKernelGGL(k_embed, grid, dim3(kBlock), 0, st, tok_embd, tokens, vocab, hidden, x);
     return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// dequant-GEMV with fused prologue / epilogue
-// ---------------------------------------------------------------------------
-// Tuning knobs (compile-time): blocks per lane per pipeline stage, and
-// whether weight loads carry the non-temporal hint.
-#ifndef LMK_CB_Q8
-#define LMK_CB_Q8 1
-#endif
-#ifndef LMK_CB_Q4
-#define LMK_CB_Q4 4
-#endif
-#ifndef LMK_WEIGHT_NT
-#define LMK_WEIGHT_NT 1
-#endif
-
-// Reductions over the 8 lanes i..i|7 with DPP moves (no LDS round trip):
-// xor 1 and xor 2 inside a quad, then the mirror inside each half row (lane
-// i <-> 7 - i) brings the other quad's result.
-__device__ __forceinline__ float max8(float v) {
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));  // quad_perm [1,0,3,2]
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));  // quad_perm [2,3,0,1]
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false))); // row_half_mirror
-    return v;
-}
-__device__ __forceinline__ int sum8(int v) {
-    v += __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
-    v += __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
-    v += __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);
-    return v;
-}
-
-// Four consecutive activations (columns i..i+3 of a 32-column block) -> their
-// three digit bytes; the block maximum comes from the 8 lanes sharing the block.
-__device__ __forceinline__ void stage_digits(float4 v, int i, int K, int8_t* xq, float* xsc, int4* dsum,
-                                             bool sums) {
-    const float m = max8(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-    if (i >= K) return;
-    const float f = m > 0.f ? 8323072.0f / m : 0.f;       // 127 * 2^16 / max|x_b|
-    const int X[4] = {(int)rintf(v.x * f), (int)rintf(v.y * f), (int)rintf(v.z * f), (int)rintf(v.w * f)};
-    uint32_t w0 = 0, w1 = 0, w2 = 0;
-    int t0 = 0, t1 = 0, t2 = 0;
-    #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int x1 = (X[e] + 128) >> 8, x2 = (x1 + 128) >> 8;
-        w0 |= (uint32_t)(X[e] & 255) << (8 * e);
-        w1 |= (uint32_t)(x1 & 255) << (8 * e);
-        w2 |= (uint32_t)(x2 & 255) << (8 * e);
-        t0 += (int)(int8_t)(X[e] & 255);
-        t1 += (int)(int8_t)(x1 & 255);
-        t2 += x2;
-    }
-    const int b = i >> 5, j = (i >> 2) & 7;
-    int* dst = (int*)(xq + b * 96);
-    dst[j] = (int)w0;
-    dst[8 + j] = (int)w1;
-    dst[16 + j] = (int)w2;
-    if (j == 0) xsc[b] = m * (1.0f / 8323072.0f);
-    if (sums) {
-        t0 = sum8(t0);
-        t1 = sum8(t1);
-        t2 = sum8(t2);
-        if (j == 0) dsum[b] = make_int4(t0, t1, t2, 0);
-    }
 }
 
 // Weight blocks one lane loads per pipeline stage (per row of its row pair).

@@ -15,6 +15,7 @@
 // layer's compute waits for its copy, and the copy that overwrites a buffer
 // waits for the compute that last read it.
 #include "lm_internal.h"
+#include "lm_step.h"
 
 #include "../../include/lmdecode.h"
 
@@ -129,6 +130,20 @@ struct lm_model {
     int* d_lm_cnt = nullptr;
     float* d_sink = nullptr;
     float* d_dbg = nullptr;               // debug dequant rows
+
+    // persistent one-kernel step (one sequence, weights resident)
+    bool step_capable = false;            // the step kernel's LDS plan fits this shape
+    bool persistent = false;              // use it for one-sequence steps
+    int n_cus = 0;
+    TileGeom tgeo[5]{};                   // QKV, Wo, gate/up, down, LM head
+    int64_t tile_layer_stride = 0;
+    int64_t tile_off[4] = {};
+    uint8_t* d_tiles = nullptr;           // tile-major layer matrices [L][...]
+    uint8_t* d_lm_tiles = nullptr;
+    StepArgs step_h{};
+    StepArgs* d_step_args = nullptr;      // the step kernel's arguments
+    uint32_t* d_bar = nullptr;            // grid-barrier counts
+    uint32_t* d_step_misc = nullptr;      // [0] epoch [1] error [2] argmax count [3] pad [4..] attention counts
     int64_t dbg_floats = 0;
 
     std::vector<uint8_t> layer_loaded;
@@ -409,6 +424,7 @@ extern "C" lm_status lm_model_create(const lm_config* cfg, void* hip_stream, lm_
         CREATE_HIP(hipGetDevice(&dev));
         CREATE_HIP(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
         m->gemv_max_blocks = std::max(64, ncu * 4);
+        m->n_cus = ncu;
     }
 
     const lm_config& c = *cfg;
@@ -470,6 +486,77 @@ extern "C" lm_status lm_model_create(const lm_config* cfg, void* hip_stream, lm_
             }
         CREATE_HIP(hipMemcpy(m->d_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice));
         CREATE_HIP(hipMemcpy(m->d_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice));
+    }
+    // persistent one-kernel step (one sequence): tile-major weight copies,
+    // its argument block in device memory, barrier counts
+    if (S == 1) {
+        const int qt = c.qtype;
+        const int64_t kmax = std::max<int64_t>({m->H, m->F, m->qrows});
+        const int xb = step_xbytes(qt, (int)kmax, (int)m->hd);
+        const int slots = step_ring_slots(xb);
+        if (slots >= 4 && m->n_cus >= 1) {
+            m->tgeo[0] = tile_geom(qt, (int)(m->qrows + 2 * m->kvrows), (int)m->H);
+            m->tgeo[1] = tile_geom(qt, (int)m->H, (int)m->qrows);
+            m->tgeo[2] = tile_geom(qt, (int)(2 * m->F), (int)m->H);
+            m->tgeo[3] = tile_geom(qt, (int)m->H, (int)m->F);
+            m->tgeo[4] = tile_geom(qt, (int)m->V, (int)m->H);
+            int64_t off = 0;
+            for (int i = 0; i < 4; ++i) {
+                m->tile_off[i] = off;
+                off = align_up(off + tile_matrix_bytes(m->tgeo[i]));
+            }
+            m->tile_layer_stride = off;
+            CREATE_TRY(dev_alloc(m, (void**)&m->d_tiles, L * off, "tile-major layer weights"));
+            CREATE_TRY(dev_alloc(m, (void**)&m->d_lm_tiles, tile_matrix_bytes(m->tgeo[4]), "tile-major LM head"));
+            CREATE_TRY(dev_alloc(m, (void**)&m->d_step_args, sizeof(StepArgs), "step arguments"));
+            CREATE_TRY(dev_alloc(m, (void**)&m->d_bar, step_bar_words(c.n_layers) * 4, "step barrier counts"));
+            CREATE_TRY(dev_alloc(m, (void**)&m->d_step_misc, (4 + m->nkv) * 4, "step counters"));
+            CREATE_HIP(hipMemsetAsync(m->d_bar, 0, (size_t)(step_bar_words(c.n_layers) * 4), m->stream));
+            CREATE_HIP(hipMemsetAsync(m->d_step_misc, 0, (size_t)((4 + m->nkv) * 4), m->stream));
+            StepArgs& a = m->step_h;
+            a.L = c.n_layers;
+            a.H = (int)m->H;
+            a.F = (int)m->F;
+            a.V = (int)m->V;
+            a.nq = (int)m->nq;
+            a.nkv = (int)m->nkv;
+            a.hd = (int)m->hd;
+            a.max_ctx = c.max_ctx;
+            a.eps = (float)c.rms_eps;
+            a.scale = (float)(1.0 / std::sqrt((double)m->hd));
+            a.tiles = m->d_tiles;
+            a.layer_stride = m->tile_layer_stride;
+            for (int i = 0; i < 4; ++i) a.mat_off[i] = m->tile_off[i];
+            a.lm_tiles = m->d_lm_tiles;
+            for (int i = 0; i < 5; ++i) a.geo[i] = m->tgeo[i];
+            a.embd = m->d_embd;
+            a.norms = m->d_norms;
+            a.out_norm = m->d_out_norm;
+            a.kcache = m->d_k;
+            a.vcache = m->d_v;
+            a.kv_layer = kv_layer_elems(m);
+            a.rope_cos = m->d_cos;
+            a.rope_sin = m->d_sin;
+            a.pos = m->d_pos;
+            a.x = m->d_x;
+            a.q = m->d_q;
+            a.o = m->d_o;
+            a.h = m->d_h;
+            a.attn_part = m->d_attn_part;
+            a.attn_cnt = m->d_step_misc + 4;
+            a.max_chunks = m->max_chunks;
+            a.part_val = m->d_lm_pval;
+            a.part_idx = m->d_lm_pidx;
+            a.done_cnt = m->d_step_misc + 2;
+            a.bar = m->d_bar;
+            a.epoch = m->d_step_misc + 0;
+            a.err = (int*)(m->d_step_misc + 1);
+            a.ring_slots = slots;
+            a.xbytes = xb;
+            CREATE_HIP(hipMemcpy(m->d_step_args, &a, sizeof a, hipMemcpyHostToDevice));
+            m->step_capable = true;
+            m->persistent = false;        // opt-in (lm_set_persistent) until it beats the per-operator kernels
+        }
     }
     CREATE_HIP(hipStreamSynchronize(m->stream));
 #undef CREATE_TRY
@@ -553,6 +640,52 @@ static lm_status upload_sct(lm_model* m, int N, int K, RowFn src_row, uint16_t* 
     return LM_OK;
 }
 
+// Tile-major copy of one matrix for the persistent step (layout: lm_step.h):
+// row groups of 16 (rows past N are zero), each group's column chunks as
+// contiguous tiles in the matrix-core operand order, scales after the quants.
+template <class RowFn>
+static lm_status upload_tiles(lm_model* m, const TileGeom& g, RowFn src_row, uint8_t* dst) {
+    const int qt = m->cfg.qtype, bb = block_bytes(qt);
+    const int NBK = qt == kQ8_0 ? kTileBlocksQ8 : kTileBlocksQ4;
+    const int QBB = qt == kQ8_0 ? 512 : 256;      // quant bytes of one block of 16 rows
+    const int64_t per = std::max<int64_t>(1, m->stage_bytes / g.gbytes);
+    for (int64_t g0 = 0; g0 < g.ng; g0 += per) {
+        const int64_t n = std::min<int64_t>(per, g.ng - g0);
+        uint8_t* stg = m->h_stage;
+        parallel_rows(n, [&](int64_t a, int64_t b) {
+            for (int64_t gi = a; gi < b; ++gi) {
+                uint8_t* gd = stg + gi * g.gbytes;
+                std::memset(gd, 0, (size_t)g.gbytes);
+                for (int ch = 0; ch < g.nch; ++ch) {
+                    const int nbk = ch == g.nch - 1 ? g.nbk_last : NBK;
+                    uint8_t* t = gd + (int64_t)ch * g.tfull;
+                    uint8_t* sc = t + (int64_t)nbk * QBB;
+                    for (int j = 0; j < kTileRows; ++j) {
+                        const int64_t row = (g0 + gi) * kTileRows + j;
+                        if (row >= g.N) continue;
+                        const uint8_t* src = src_row(row);
+                        for (int bk = 0; bk < nbk; ++bk) {
+                            const uint8_t* blk = src + (int64_t)(ch * NBK + bk) * bb;
+                            sc[(bk * kTileRows + j) * 2] = blk[0];
+                            sc[(bk * kTileRows + j) * 2 + 1] = blk[1];
+                            uint8_t* q = t + (int64_t)bk * QBB;
+                            if (qt == kQ8_0) {
+                                for (int gq = 0; gq < 4; ++gq) std::memcpy(q + gq * 128 + j * 8, blk + 2 + 8 * gq, 8);
+                            } else {
+                                for (int h = 0; h < 2; ++h) std::memcpy(q + h * 128 + j * 8, blk + 2 + 8 * h, 8);
+                            }
+                        }
+                    }
+                }
+            }
+        });
+        HIPTRY(m, hipMemcpyAsync(dst + g0 * g.gbytes, stg, (size_t)(n * g.gbytes), hipMemcpyHostToDevice,
+                                 m->stream));
+        HIPTRY(m, hipStreamSynchronize(m->stream));
+    }
+    return LM_OK;
+}
+
 static void invalidate_graphs(lm_model* m) {
     for (auto& g : m->graphs) (void)hipGraphExecDestroy(g.exec);
     m->graphs.clear();
@@ -604,6 +737,13 @@ extern "C" lm_status lm_load_layer_weights(lm_model* m, int32_t layer, const lm_
         if ((st = upload_sct(m, (int)(2 * F), (int)H, src_gu, dt(M_GU), host)) != LM_OK) return st;
         if ((st = upload_sct(m, (int)H, (int)F, src_down, dt(M_DOWN), host)) != LM_OK) return st;
     }
+    if (m->step_capable) {
+        uint8_t* tl = m->d_tiles + (int64_t)layer * m->tile_layer_stride;
+        if ((st = upload_tiles(m, m->tgeo[0], src_qkv, tl + m->tile_off[0])) != LM_OK) return st;
+        if ((st = upload_tiles(m, m->tgeo[1], src_wo, tl + m->tile_off[1])) != LM_OK) return st;
+        if ((st = upload_tiles(m, m->tgeo[2], src_gu, tl + m->tile_off[2])) != LM_OK) return st;
+        if ((st = upload_tiles(m, m->tgeo[3], src_down, tl + m->tile_off[3])) != LM_OK) return st;
+    }
     HIPTRY(m, hipMemcpy(m->d_norms + (int64_t)layer * 2 * H, w->attn_norm, H * 4, hipMemcpyHostToDevice));
     HIPTRY(m, hipMemcpy(m->d_norms + ((int64_t)layer * 2 + 1) * H, w->ffn_norm, H * 4, hipMemcpyHostToDevice));
     m->layer_loaded[layer] = 1;
@@ -625,6 +765,7 @@ extern "C" lm_status lm_load_global_weights(lm_model* m, const uint16_t* tok_emb
     lm_status st = upload_matrix(m, (int)m->V, (int)m->H, src_row, m->d_lm_q, m->d_lm_sc, false);
     if (st != LM_OK) return st;
     if (m->batched && (st = upload_sct(m, (int)m->V, (int)m->H, src_row, m->d_lm_sct, false)) != LM_OK) return st;
+    if (m->step_capable && (st = upload_tiles(m, m->tgeo[4], src_row, m->d_lm_tiles)) != LM_OK) return st;
     m->global_loaded = true;
     return LM_OK;
 }
@@ -780,10 +921,19 @@ static hipError_t gemv(lm_model* m, GemvArgs a, int epi, int n_seq, hipStream_t 
     return launch_gemv(a, epi, n_seq, m->gemv_max_blocks, st);
 }
 
+static bool use_step(const lm_model* m, int n_seq) {
+    return m->persistent && m->step_capable && n_seq == 1 && !m->streaming;
+}
+
 static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d_logits, int* d_argmax) {
     const lm_config& c = m->cfg;
     const int L = c.n_layers;
     hipStream_t st = m->stream;
+    if (use_step(m, n_seq)) {
+        KTimer t(m, LM_K_STEP);
+        HIPTRY(m, launch_step(m->step_h, m->d_step_args, c.qtype, d_tok, d_logits, d_argmax, m->n_cus, st));
+        return LM_OK;
+    }
     {
         KTimer t(m, LM_K_EMBED);
         HIPTRY(m, launch_embed(m->d_embd, d_tok, (int)m->V, (int)m->H, m->d_x, n_seq, st));
@@ -934,6 +1084,18 @@ static lm_status run_step(lm_model* m, int n_seq, const int* d_tok, float* d_log
     return LM_OK;
 }
 
+// The step kernel sets an error flag when a wait between workgroups times
+// out (another kernel holding CUs for seconds); its counts are then reset.
+static lm_status check_step_error(lm_model* m) {
+    uint32_t err = 0;
+    HIPTRY(m, hipMemcpy(&err, m->d_step_misc + 1, 4, hipMemcpyDeviceToHost));
+    if (!err) return LM_OK;
+    HIPTRY(m, hipMemset(m->d_bar, 0, (size_t)(step_bar_words(m->cfg.n_layers) * 4)));
+    HIPTRY(m, hipMemset(m->d_step_misc, 0, (size_t)((4 + m->nkv) * 4)));
+    return fail(m, LM_E_HIP, "persistent decode step: a wait between workgroups timed out (every CU must be "
+                "free for the step kernel); the step's outputs are invalid");
+}
+
 static lm_status check_ready(lm_model* m, const char* fn, int n_seq) {
     if (!m->global_loaded)
         return fail(m, LM_E_STATE, "%s: global weights not loaded (lm_load_global_weights)", fn);
@@ -967,6 +1129,10 @@ extern "C" lm_status lm_decode_step(lm_model* m, const int32_t* tokens, int32_t 
         HIPTRY(m, hipMemcpyAsync(logits, m->d_logits, (size_t)(n_seq * m->V * 4), hipMemcpyDeviceToHost,
                                  m->stream));
     HIPTRY(m, hipStreamSynchronize(m->stream));
+    if (use_step(m, n_seq)) {
+        lm_status es = check_step_error(m);
+        if (es != LM_OK) return es;
+    }
     return collect_timing(m);
 }
 
@@ -980,6 +1146,50 @@ extern "C" lm_status lm_decode_step_dev(lm_model* m, const int32_t* d_tokens, in
     if (st != LM_OK) return st;
     for (int s = 0; s < n_seq; ++s) m->pos[s] += 1;
     return LM_OK;
+}
+
+extern "C" lm_status lm_set_persistent(lm_model* m, int32_t enable) {
+    if (!m) return LM_E_ARG;
+    if (enable && !m->step_capable)
+        return fail(m, LM_E_STATE, "lm_set_persistent: the one-kernel step is not available for this model "
+                    "(it needs max_seqs = 1 and an LDS plan that fits: widest GEMV input %lld columns)",
+                    (long long)std::max<int64_t>({m->H, m->F, m->qrows}));
+    HIPTRY(m, hipStreamSynchronize(m->stream));
+    m->persistent = enable != 0;
+    invalidate_graphs(m);
+    return LM_OK;
+}
+
+extern "C" lm_status lm_debug_step_trace(lm_model* m, const int32_t* d_tokens, uint64_t* out, int64_t capacity,
+                                         int32_t* n_cus, int32_t* n_phases) {
+    if (!m || !d_tokens || !out || !n_cus || !n_phases) return LM_E_ARG;
+    if (!m->step_capable || !m->persistent || m->streaming)
+        return fail(m, LM_E_STATE, "lm_debug_step_trace: the persistent step is not in use");
+    lm_status st = check_ready(m, "lm_debug_step_trace", 1);
+    if (st != LM_OK) return st;
+    const int64_t np = 5 * (int64_t)m->cfg.n_layers + 1;
+    const int64_t words = (int64_t)m->n_cus * np * kTraceWords;
+    *n_cus = m->n_cus;
+    *n_phases = (int32_t)np;
+    if (capacity < words)
+        return fail(m, LM_E_ARG, "lm_debug_step_trace: capacity = %lld words; expected >= %lld", (long long)capacity,
+                    (long long)words);
+    uint64_t* d = nullptr;
+    HIPTRY(m, hipStreamSynchronize(m->stream));
+    HIPTRY(m, hipMalloc(&d, (size_t)words * 8));
+    StepArgs a = m->step_h;
+    a.trace = d;
+    hipError_t e = hipMemsetAsync(d, 0, (size_t)words * 8, m->stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(m->d_step_args, &a, sizeof a, hipMemcpyHostToDevice, m->stream);
+    if (e == hipSuccess)
+        e = launch_step(a, m->d_step_args, m->cfg.qtype, d_tokens, nullptr, m->d_argmax, m->n_cus, m->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(m->stream);
+    if (e == hipSuccess) e = hipMemcpy(out, d, (size_t)words * 8, hipMemcpyDeviceToHost);
+    (void)hipMemcpy(m->d_step_args, &m->step_h, sizeof m->step_h, hipMemcpyHostToDevice);
+    (void)hipFree(d);
+    if (e != hipSuccess) return fail(m, LM_E_HIP, "lm_debug_step_trace: %s", hipGetErrorString(e));
+    m->pos[0] += 1;
+    return check_step_error(m);
 }
 
 extern "C" lm_status lm_set_graph(lm_model* m, int32_t enable) {
@@ -1090,6 +1300,13 @@ extern "C" lm_status lm_kernel_bytes(const lm_model* m, int32_t kind, int32_t n_
         case LM_K_DOWN: b = L * (H * F * bpw + S * (F * 4 + H * 8)); break;
         case LM_K_LMHEAD: b = V * H * bpw + H * 4 + S * H * 4; break;
         case LM_K_COPY: b = m->streaming ? L * (double)m->blob_bytes : 0.0; break;
+        case LM_K_STEP:
+            for (int k = LM_K_EMBED; k <= LM_K_LMHEAD; ++k) {
+                double kb = 0.0;
+                (void)lm_kernel_bytes(m, k, n_seq, &kb);
+                b += kb;
+            }
+            break;
     }
     *bytes = b;
     return LM_OK;
