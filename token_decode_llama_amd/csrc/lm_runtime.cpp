@@ -642,7 +642,7 @@ static lm_status upload_sct(lm_model* m, int N, int K, RowFn src_row, uint16_t* 
 
 // Tile-major copy of one matrix for the persistent step (layout: lm_step.h):
 // row groups of 16 (rows past N are zero), each group's column chunks as
-// contiguous tiles in the matrix-core operand order, scales after the quants.
+// contiguous tiles: [block][row] quants, then [block][row] scales.
 template <class RowFn>
 static lm_status upload_tiles(lm_model* m, const TileGeom& g, RowFn src_row, uint8_t* dst) {
     const int qt = m->cfg.qtype, bb = block_bytes(qt);
@@ -668,12 +668,8 @@ static lm_status upload_tiles(lm_model* m, const TileGeom& g, RowFn src_row, uin
                             const uint8_t* blk = src + (int64_t)(ch * NBK + bk) * bb;
                             sc[(bk * kTileRows + j) * 2] = blk[0];
                             sc[(bk * kTileRows + j) * 2 + 1] = blk[1];
-                            uint8_t* q = t + (int64_t)bk * QBB;
-                            if (qt == kQ8_0) {
-                                for (int gq = 0; gq < 4; ++gq) std::memcpy(q + gq * 128 + j * 8, blk + 2 + 8 * gq, 8);
-                            } else {
-                                for (int h = 0; h < 2; ++h) std::memcpy(q + h * 128 + j * 8, blk + 2 + 8 * h, 8);
-                            }
+                            const int qb = qt == kQ8_0 ? 32 : 16;    // quant bytes of one row's block
+                            std::memcpy(t + (int64_t)bk * QBB + j * qb, blk + 2, qb);
                         }
                     }
                 }

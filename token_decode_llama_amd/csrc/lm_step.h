@@ -18,19 +18,18 @@ constexpr int kPartBufs = 16;          // row-group partial-sum buffers (K split
 constexpr int kStepCtlBytes = 512 + kPartBufs * 4 * kTileRowsFwd * 4;   // LDS control block + partials
 constexpr int kStepLdsMax = 163840;    // LDS per workgroup on gfx950
 
-// Tile-major layout of one quantised matrix [N rows][K cols], in the operand
-// order of the matrix-core instruction that consumes it:
+// Tile-major layout of one quantised matrix [N rows][K cols]:
 //   rows in groups of 16 (zero rows pad the last group), each group's
 //   columns in chunks of NBK blocks; tile (group, chunk) is contiguous:
-//     Q8_0: for each block b: for g = 0..3: for row j = 0..15: the 8 quants
-//           of columns 8g..8g+7 (512 bytes per block); then the fp16 scales
-//           [b][j]
-//     Q4_0: for each block b: for h = 0..1: for row j = 0..15: bytes
-//           8h..8h+7 of the block's 16 nibble bytes (GGUF order: byte i
-//           holds column i low, column i+16 high; 256 bytes per block); then
-//           the fp16 scales [b][j]
+//     Q8_0: for each block b: for row j = 0..15: the row's 32 quants of the
+//           block (512 bytes per block); then the fp16 scales [b][j]
+//     Q4_0: for each block b: for row j = 0..15: the row's 16 nibble bytes
+//           of the block in GGUF order (byte i: column i low, column i+16
+//           high; 256 bytes per block); then the fp16 scales [b][j]
 //   a group's chunks follow each other, groups follow each other.  Bytes per
-//   weight are exactly the GGUF ones.
+//   weight are exactly the GGUF ones.  Four consecutive blocks of a tile are
+//   one matrix-core operand set: lane l of a wavefront reads row l mod 16 of
+//   block l / 16 at offset 32 l (Q8_0) or 16 l (Q4_0).
 struct TileGeom {
     int N, K;
     int ng;         // row groups

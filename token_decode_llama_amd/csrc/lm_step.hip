@@ -411,59 +411,61 @@ __device__ float stage_input(Cons& cs, const float* src, const uint16_t* emb, co
 }
 
 // ---- one tile on the matrix cores ------------------------------------------
-// v_mfma_i32_16x16x32_i8 with A = the input's digit planes (A row i = digit
-// i mod 3, 32 columns of one block) and B = 16 weight rows x the same 32
-// columns: D[i][j] = sum_k digit_i[k] * q_j[k], exact in int32.  Lane
-// l = 16 g + j supplies A[j][8g..8g+7] and B[8g..8g+7][j] and receives
-// D[4g..4g+3][j], so lanes 0..15 hold the three digit sums of row j.  Each
-// block's sums are combined and scaled (weight scale x input block scale)
-// into lane j's fp32 accumulator, block by block in column order.
+// v_mfma_i32_4x4x4i8 computes 16 independent 4x4x4 products; lane l = 4m + j
+// supplies A_m[j][0..3] and B_m[0..3][j] and receives D_m[0..3][j].  Product
+// m here is (input block l / 16 of four, weight row l mod 16): A_m row i =
+// digit i of the input's block (row 3 repeats digit 0 and is ignored), B_m
+// column j = the weight row, and eight products over k = 4c..4c+3 (c = 0..7)
+// accumulate the whole 32-column block.  Lane l ends with the three exact
+// digit sums of its (row, block) pair, combines them and scales them by
+// weight scale x input block scale into its fp32 accumulator; the four
+// lanes of a row (l, l+16, l+32, l+48) are added at the end of the row group.
 typedef int v4i_mf __attribute__((ext_vector_type(4)));
 
 template <int QT>
 __device__ __forceinline__ void tile_mfma(const uint8_t* T, int nbk, int b0, const int8_t* xq, const float* xsc,
                                           const int4* dsum, int lane, float& acc) {
-    constexpr int QBB = QT == kQ8_0 ? 512 : 256;
-    constexpr int U = 8;                              // blocks whose operands / MFMAs are in flight together
-    const int g = lane >> 4, j = lane & 15;
+    constexpr int QBB = QT == kQ8_0 ? 512 : 256;      // quant bytes of one block of 16 rows
     const uint16_t* sc = (const uint16_t*)(T + nbk * QBB);
-    const int8_t* xa = xq + (j % 3) * 32 + g * 8;     // this lane's A bytes within a block's digits
+    const int dig = (lane & 3) == 3 ? 0 : (lane & 3);  // A row of this lane: digit plane
+    const int bq = lane >> 4;                          // this lane's block within a set of four
     const v4i_mf zero = {0, 0, 0, 0};
-    for (int b = 0; b < nbk; b += U) {
-        long xa8[U], w8[U];
-        #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int bb = min(b + u, nbk - 1);
-            xa8[u] = *(const long*)(xa + (int64_t)(b0 + bb) * 96);
-            if (QT == kQ8_0) {
-                w8[u] = *(const long*)(T + bb * QBB + lane * 8);
-            } else {
-                const unsigned long raw = *(const unsigned long*)(T + bb * QBB + (g & 1) * 128 + j * 8);
-                w8[u] = (long)((raw >> (g >= 2 ? 4 : 0)) & 0x0F0F0F0F0F0F0F0Full);
+    for (int b = 0; b < nbk; b += 4) {
+        const int bl = min(b + bq, nbk - 1);           // clamped: a block past the chunk adds 0
+        const int gb = b0 + bl;
+        const int4 a0 = *(const int4*)(xq + (int64_t)gb * 96 + dig * 32);
+        const int4 a1 = *(const int4*)(xq + (int64_t)gb * 96 + dig * 32 + 16);
+        int w[8];
+        if (QT == kQ8_0) {
+            const int4 w0 = *(const int4*)(T + b * QBB + lane * 32);
+            const int4 w1 = *(const int4*)(T + b * QBB + lane * 32 + 16);
+            w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
+            w[4] = w1.x; w[5] = w1.y; w[6] = w1.z; w[7] = w1.w;
+        } else {
+            const int4 q = *(const int4*)(T + b * QBB + lane * 16);
+            const int qv[4] = {q.x, q.y, q.z, q.w};
+            #pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                w[c] = qv[c] & 0x0F0F0F0F;                             // columns 4c..4c+3 (low nibbles)
+                w[4 + c] = (int)(((uint32_t)qv[c] >> 4) & 0x0F0F0F0Fu);  // columns 16+4c.. (high nibbles)
             }
         }
-        float f[U];
+        const float f = (b + bq < nbk ? h2f(sc[b * kTileRows + (lane & 63)]) : 0.f) * xsc[gb];
+        const int av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        v4i_mf d0 = zero, d1 = zero;                    // two chains: even and odd column quads
         #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int bb = min(b + u, nbk - 1);
-            f[u] = h2f(sc[bb * kTileRows + j]) * xsc[b0 + bb];
+        for (int c = 0; c < 8; c += 2) {
+            d0 = __builtin_amdgcn_mfma_i32_4x4x4i8(av[c], w[c], d0, 0, 0, 0);
+            d1 = __builtin_amdgcn_mfma_i32_4x4x4i8(av[c + 1], w[c + 1], d1, 0, 0, 0);
         }
-        v4i_mf d[U];
-        #pragma unroll
-        for (int u = 0; u < U; ++u) d[u] = __builtin_amdgcn_mfma_i32_16x16x32_i8(xa8[u], w8[u], zero, 0, 0, 0);
-        #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (b + u < nbk) {
-                int s0 = d[u][0], s1 = d[u][1], s2 = d[u][2];
-                if (QT == kQ4_0) {                    // nibbles n = q + 8: remove 8 x the digit sums
-                    const int4 Ts = dsum[b0 + b + u];
-                    s0 -= 8 * Ts.x;
-                    s1 -= 8 * Ts.y;
-                    s2 -= 8 * Ts.z;
-                }
-                acc = fmaf(f[u], combine_digits(s0, s1, s2), acc);
-            }
+        int s0 = d0[0] + d1[0], s1 = d0[1] + d1[1], s2 = d0[2] + d1[2];
+        if (QT == kQ4_0) {                              // nibbles n = q + 8: remove 8 x the digit sums
+            const int4 Ts = dsum[gb];
+            s0 -= 8 * Ts.x;
+            s1 -= 8 * Ts.y;
+            s2 -= 8 * Ts.z;
         }
+        acc = fmaf(f, combine_digits(s0, s1, s2), acc);
     }
 }
 
@@ -481,6 +483,13 @@ enum { PH_QKV = 0, PH_ATTN = 1, PH_WO = 2, PH_GU = 3, PH_DOWN = 4, PH_LM = 5 };
 struct GroupCtx {
     int gbase;        // cumulative row-group index of the phase's first group (buffer ownership)
 };
+
+// lanes l, l+16, l+32, l+48 hold partial sums of row l mod 16 (four input blocks)
+__device__ __forceinline__ float row_sum(float v) {
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
 
 __device__ __forceinline__ bool part_wait(Cons& cs, const int* p, int want_ge) {
     if (lds_get(p) >= want_ge) return true;
@@ -523,7 +532,7 @@ __device__ void gemv_phase(Cons& cs, int type, int l, const PhaseMat& pm, int kb
     for (int t = cs.cw; t < nt; t += kNC) {
         const int i = t / nch, c = t - i * nch;
         if (i != cur) {
-            if (cur >= 0 && !part_store(cs, gbase + cur, acc)) return;
+            if (cur >= 0 && !part_store(cs, gbase + cur, row_sum(acc))) return;
             cur = i;
             acc = 0.f;
         }
@@ -550,7 +559,7 @@ __device__ void gemv_phase(Cons& cs, int type, int l, const PhaseMat& pm, int kb
 
         // finish row group i: every wavefront that took one of its chunks has stored a partial
         const int gi = gbase + i, s = gi % kPartBufs;
-        if (!part_store(cs, gi, acc)) return;
+        if (!part_store(cs, gi, row_sum(acc))) return;
         cur = -1;
         const int np = nch < kNC ? nch : kNC;             // wavefronts that took a chunk of the group
         if (!part_wait(cs, &C->pcnt[s], np)) return;
@@ -606,7 +615,7 @@ __device__ void gemv_phase(Cons& cs, int type, int l, const PhaseMat& pm, int kb
             }
         }
     }
-    if (cur >= 0) part_store(cs, gbase + cur, acc);
+    if (cur >= 0) part_store(cs, gbase + cur, row_sum(acc));
 }
 
 // ---- attention: items (KV head, 64-position chunk) over the CUs --------------
