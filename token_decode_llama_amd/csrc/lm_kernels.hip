@@ -76,7 +76,10 @@ struct WChunk {
 #define LMK_GEMV_MIN_BLOCKS 1     // workgroups per CU the register budget must allow
 #endif
 
-template <int QT, int LPR, int EPI>
+// XR: float4s of the input each thread requests per prologue batch (4, 8 or
+// 16: K up to 4096, 8192 or 16384 columns in one round trip); a template
+// parameter so the register budget of the short-K kernels stays small.
+template <int QT, int LPR, int EPI, int XR>
 __global__ __launch_bounds__(kBlock, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a) {
     extern __shared__ __align__(16) float smem[];
     __shared__ float red[kWaves];
@@ -111,19 +114,8 @@ __global__ __launch_bounds__(kBlock, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a
     const int cps = (bpl + CB - 1) / CB;
     const int n_chunks = my_steps * cps;
 
-    // ---- RoPE inputs of this wavefront's first row pair, fetched early
-    int rope_p = 0;
-    float pre_cs = 1.f, pre_sn = 0.f;
-    if (EPI == EPI_QKV) {
-        rope_p = a.pos[s];
-        const int r0 = step0 * kRowsPerStep + rg * 2;
-        if (n_chunks > 0 && li == 0 && r0 < a.q_rows + a.kv_rows) {
-            const int rr = r0 < a.q_rows ? r0 : r0 - a.q_rows;
-            const int pi = (rr % a.head_dim) >> 1;
-            pre_cs = a.rope_cos[(int64_t)rope_p * (a.head_dim >> 1) + pi];
-            pre_sn = a.rope_sin[(int64_t)rope_p * (a.head_dim >> 1) + pi];
-        }
-    }
+    int rope_p = 0;                       // the position (read after the weight requests)
+    float pre_cs = 1.f, pre_sn = 0.f;     // RoPE cos/sin of the first row pair (below)
 
     // Branch-free loads (clamped addresses; a block past the row end gets
     // scale 0) so the compiler's in-order load counters stay exact and the
@@ -235,48 +227,50 @@ __global__ __launch_bounds__(kBlock, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a
     // ---- prologue.  RMSNorm(x) * g = s * (x . g) with the scalar
     // s = 1/sqrt(mean(x^2) + eps): x . g is staged into LDS and s multiplies
     // each row's finished dot product, so no element waits for the reduction.
-    // The first x batch is requested before the first weight chunk; in-order
-    // load counters then let it be consumed while the weights are in flight.
-    constexpr int kXr = 4;                       // float4s per thread per batch
-    float4 xr[kXr], gr[kXr];
-    const bool has_g = a.norm_g != nullptr;
-    #pragma unroll
-    for (int u = 0; u < kXr; ++u) {
-        const int i = min((tid + u * kBlock) * 4, K - 4);
-        xr[u] = *(const float4*)(x + i);
-        if (has_g) gr[u] = *(const float4*)(a.norm_g + i);
-    }
+    // The x batch is requested before the first weight chunks (XR float4s
+    // per thread, chosen from K at launch); in-order load counters let it be
+    // consumed while the weights are still in flight.  The residual
+    // projections (Wo, down) take no gain.
+    constexpr bool kGain = EPI != EPI_RESID;
+    constexpr int GR = kGain ? XR : 1;
+    const bool has_g = kGain && a.norm_g != nullptr;
+    float4 xr[XR], gr[GR];
+    auto fetch = [&](int base) {
+        #pragma unroll
+        for (int u = 0; u < XR; ++u) {
+            const int i = min(base + (tid + u * kBlock) * 4, K - 4);
+            xr[u] = *(const float4*)(x + i);
+            if (kGain && has_g) gr[u % GR] = *(const float4*)(a.norm_g + i);
+        }
+    };
+    fetch(0);
+    // keep the input loads ahead of the weight loads: the in-order counters
+    // then release x while the weights are still arriving
+    __builtin_amdgcn_sched_barrier(0);
     WChunk<QT> wa, wb;
     load(0, wa);          // unconditional: rows are clamped, so these are always in bounds
     load(1, wb);
-
     float ss = 0.f;
-    for (int base = 0; base < K; base += kXr * kBlock * 4) {
-        if (base > 0) {
-            #pragma unroll
-            for (int u = 0; u < kXr; ++u) {
-                const int i = min(base + (tid + u * kBlock) * 4, K - 4);
-                xr[u] = *(const float4*)(x + i);
-                if (has_g) gr[u] = *(const float4*)(a.norm_g + i);
-            }
-        }
+    for (int base = 0; base < K; base += XR * kBlock * 4) {
+        if (base > 0) fetch(base);
         #pragma unroll
-        for (int u = 0; u < kXr; ++u) {
+        for (int u = 0; u < XR; ++u) {
             // the 8 threads tid..tid|7 hold one 32-column block (K % 32 == 0, so a
             // block is either wholly inside K or wholly past it: uniform per group)
             const int i = base + (tid + u * kBlock) * 4;
             float4 v = xr[u];
-            if (has_g) {
+            if (kGain && has_g) {
                 if (i < K) {
                     ss = fmaf(v.x, v.x, ss);
                     ss = fmaf(v.y, v.y, ss);
                     ss = fmaf(v.z, v.z, ss);
                     ss = fmaf(v.w, v.w, ss);
                 }
-                v.x *= gr[u].x;
-                v.y *= gr[u].y;
-                v.z *= gr[u].z;
-                v.w *= gr[u].w;
+                const float4 gv = gr[u % GR];
+                v.x *= gv.x;
+                v.y *= gv.y;
+                v.z *= gv.z;
+                v.w *= gv.w;
             }
             stage_digits(v, i, K, xq, xsc, dsum, QT == kQ4_0);
         }
@@ -284,6 +278,20 @@ __global__ __launch_bounds__(kBlock, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a
     // block_sum's barriers also order the LDS stores above before any reads
     if (has_g) rscale = 1.0f / sqrtf(block_sum(ss, red) / (float)K + a.eps);
     __syncthreads();
+
+    // ---- the position and the RoPE inputs of this wavefront's first row pair.
+    // Requested only now, behind the weights: the position is a scalar load,
+    // and scalar loads are waited for all together, so reading it before the
+    // weight requests would hold the whole stream for its round trip.  The
+    // table loads are unconditional (clamped row): exact load counters.
+    if (EPI == EPI_QKV) {
+        rope_p = a.pos[s];
+        const int r0 = min(step0 * kRowsPerStep + rg * 2, a.q_rows + a.kv_rows - 2);
+        const int rr = r0 < a.q_rows ? r0 : r0 - a.q_rows;
+        const int pi = (rr % a.head_dim) >> 1;
+        pre_cs = a.rope_cos[(int64_t)rope_p * (a.head_dim >> 1) + pi];
+        pre_sn = a.rope_sin[(int64_t)rope_p * (a.head_dim >> 1) + pi];
+    }
 
     // ---- pipeline: a chunk's registers are refilled (chunk c+2) as soon as
     // chunk c has been consumed, before c's cross-lane reduction and
@@ -377,23 +385,23 @@ static int device_cus() {
     return cached_cus;
 }
 
-template <int QT, int LPR, int EPI>
+template <int QT, int LPR, int EPI, int XR>
 static int resident_blocks(size_t lds) {
     // workgroups of this instantiation that fit on the whole device at once
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemv<QT, LPR, EPI>, kBlock, lds) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemv<QT, LPR, EPI, XR>, kBlock, lds) != hipSuccess ||
         per_cu < 1)
         per_cu = 1;
     return per_cu * device_cus();
 }
 
-template <int QT, int LPR, int EPI>
+template <int QT, int LPR, int EPI, int XR>
 static hipError_t launch_one(const GemvArgs& a, int n_seq, int max_blocks, size_t lds, hipStream_t st) {
     constexpr int rows_per_step = 2 * (64 / LPR);
     const int n_steps = (a.w.N + rows_per_step - 1) / rows_per_step;
     const int need = (n_steps + kWaves - 1) / kWaves;
     const int cus = device_cus();
-    const int cap = std::min(max_blocks, resident_blocks<QT, LPR, EPI>(lds));
+    const int cap = std::min(max_blocks, resident_blocks<QT, LPR, EPI, XR>(lds));
     int g = need;
     if (need > cap) {
         // Several rounds per wavefront.  Busiest CU decides: cost = (row-pair rounds
@@ -411,18 +419,22 @@ static hipError_t launch_one(const GemvArgs& a, int n_seq, int max_blocks, size_
         if (best < 0) g = cap;
     }
     if (g < 1) g = 1;
-    hipLaunchKernelGGL((k_gemv<QT, LPR, EPI>), dim3(g, n_seq), dim3(kBlock), lds, st, a);
+    hipLaunchKernelGGL((k_gemv<QT, LPR, EPI, XR>), dim3(g, n_seq), dim3(kBlock), lds, st, a);
     return hipGetLastError();
 }
 
 template <int QT, int EPI>
 static hipError_t launch_gemv_lpr(const GemvArgs& a, int lpr, int n_seq, int max_blocks, size_t lds,
                                   hipStream_t st) {
+    // K < 2048 (the narrower lane groups) always fits the 4-float4 batch
     switch (lpr) {
-        case 64: return launch_one<QT, 64, EPI>(a, n_seq, max_blocks, lds, st);
-        case 32: return launch_one<QT, 32, EPI>(a, n_seq, max_blocks, lds, st);
-        case 16: return launch_one<QT, 16, EPI>(a, n_seq, max_blocks, lds, st);
-        default: return launch_one<QT, 8, EPI>(a, n_seq, max_blocks, lds, st);
+        case 64:
+            if (a.w.K <= 4 * kBlock * 4) return launch_one<QT, 64, EPI, 4>(a, n_seq, max_blocks, lds, st);
+            if (a.w.K <= 8 * kBlock * 4) return launch_one<QT, 64, EPI, 8>(a, n_seq, max_blocks, lds, st);
+            return launch_one<QT, 64, EPI, 16>(a, n_seq, max_blocks, lds, st);
+        case 32: return launch_one<QT, 32, EPI, 4>(a, n_seq, max_blocks, lds, st);
+        case 16: return launch_one<QT, 16, EPI, 4>(a, n_seq, max_blocks, lds, st);
+        default: return launch_one<QT, 8, EPI, 4>(a, n_seq, max_blocks, lds, st);
     }
 }
 
@@ -438,6 +450,7 @@ static hipError_t launch_gemv_epi(const GemvArgs& a, int epi, int lpr, int n_seq
 }
 
 hipError_t launch_gemv(const GemvArgs& a, int epi, int n_seq, int max_blocks, hipStream_t st) {
+    if (epi == EPI_RESID && a.norm_g) return hipErrorInvalidValue;   // the residual products take no gain
     const int nb = a.w.K / 32;
     const int lpr = pick_lpr(nb);
     const size_t lds = (size_t)nb * 96 + (size_t)((nb + 3) & ~3) * 4 + (a.qtype == kQ4_0 ? (size_t)nb * 16 : 0);
@@ -921,7 +934,7 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
     }
     __syncthreads();
     if (!s_last) return;
-    constexpr int B = 8;
+    constexpr int B = 16;                     // partials fetched per round trip
     for (int idx = tid; idx < G * HD; idx += kBlock) {
         const int j = idx / HD, d = idx % HD;
         const float* ph = part_s + (int64_t)(g * G + j) * a.max_chunks * stride;
