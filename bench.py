@@ -61,6 +61,7 @@ KERNEL_NAMES = {
     "down": "k_gemv<down, residual epilogue>",
     "lmhead": "k_gemv<LM head, RMSNorm prologue, argmax epilogue>",
     "step": "k_step (persistent one-kernel decode step: LDS weight ring + operator chain)",
+    "flow": "k_flow (dataflow launch of all layers: QKV, attention, Wo, gate/up, down workgroups in dependency order)",
 }
 
 
@@ -70,7 +71,8 @@ def log(*a):
 
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("lm_kernels.hip", "lm_internal.h", "lm_step.hip", "lm_step.h", "lm_device.h"):
+    for f in ("lm_kernels.hip", "lm_internal.h", "lm_step.hip", "lm_step.h", "lm_device.h", "lm_flow.hip",
+              "lm_flow.h"):
         with open(os.path.join(ROOT, "token_decode_llama_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -202,7 +204,7 @@ class Runner:
         import token_decode_llama_amd as lm
         for s in range(self.n_seq):
             self.g.set_position(s, self.cfg.ctx + at_step)
-        b = sum(self.g.kernel_bytes(k, self.n_seq) for k in lm.KERNEL_KINDS if k not in ("copy", "step"))
+        b = sum(self.g.kernel_bytes(k, self.n_seq) for k in lm.KERNEL_KINDS if k not in ("copy", "step", "flow"))
         self.rewind()
         return b
 
@@ -211,7 +213,7 @@ class Runner:
 
 
 def per_launch(kind: str, n_layers: int) -> int:
-    return 1 if kind in ("embed", "lmhead", "step") else n_layers
+    return 1 if kind in ("embed", "lmhead", "step", "flow") else n_layers
 
 
 def kernel_table(kstats, kbytes, n_layers):

@@ -176,6 +176,31 @@ lm_status lm_set_graph(lm_model* m, int32_t enable);
  * order), not bit for bit. */
 lm_status lm_set_persistent(lm_model* m, int32_t enable);
 
+/* One-sequence steps with every layer in one launch (mode 1 or 2; off by
+ * default; available for Q8_0/Q4_0, head_dim 128, at most 8 query heads per KV
+ * head, hidden and FFN widths >= 2048; weights resident, not in streaming mode).
+ * The same operators as the per-operator kernels (the C/CUDA Llama engine
+ * page, section 4.4), computed the same way: the launch's workgroups are the
+ * operators' workgroups in dependency order, and each waits for the operator
+ * before it through a device counter instead of a kernel boundary, after
+ * requesting the weights it multiplies.  The embedding and the LM head stay
+ * separate launches.  A wait that times out (seconds) fails the step with
+ * LM_E_HIP (lm_decode_step; lm_check_error after lm_decode_step_dev).
+ * Mode 1 (dataflow): one workgroup per (operator, share); workgroups are
+ * dispatched in index order, so the chain always progresses, also beside
+ * other work on the GPU.  Mode 2 (resident): two workgroups per CU take their
+ * share of every operator in turn; it needs every CU (steps of two models
+ * must not overlap on one GPU).  enable = 0 selects the per-operator kernels;
+ * enable = 1 or 2 on a model without it returns LM_E_STATE.
+ * lm_set_persistent(m, 1) takes precedence.  Measured on the 8B shape it is
+ * slower than the per-operator kernels: a device-wide count across XCDs costs
+ * more than a kernel boundary. */
+lm_status lm_set_dataflow(lm_model* m, int32_t enable);
+
+/* Waits for the model's stream, then reports (LM_E_HIP) and clears a timed-out
+ * wait of the dataflow or persistent step since the last check. */
+lm_status lm_check_error(lm_model* m);
+
 /* The hipStream_t the model launches on. */
 void* lm_stream(const lm_model* m);
 
@@ -189,10 +214,12 @@ const char* lm_last_error(const lm_model* m);
  * host-to-HBM copy of one layer blob on the copy stream in streaming mode
  * (its durations are those copies' events; its bytes are the blobs copied per
  * step, zero when the weights are resident).  LM_K_STEP is the persistent
- * one-kernel step (lm_set_persistent); its bytes are those of the whole step. */
+ * one-kernel step (lm_set_persistent); its bytes are those of the whole step.
+ * LM_K_FLOW is the dataflow launch of all layers (lm_set_dataflow); its bytes
+ * are those of the QKV .. down kinds together. */
 typedef enum {
     LM_K_EMBED = 0, LM_K_QKV = 1, LM_K_ATTN = 2, LM_K_WO = 3, LM_K_GATEUP = 4,
-    LM_K_DOWN = 5, LM_K_LMHEAD = 6, LM_K_COPY = 7, LM_K_STEP = 8, LM_K_COUNT = 9
+    LM_K_DOWN = 5, LM_K_LMHEAD = 6, LM_K_COPY = 7, LM_K_STEP = 8, LM_K_FLOW = 9, LM_K_COUNT = 10
 } lm_kernel_kind;
 
 /* enable = 1: eager steps record HIP events around every kernel of every
@@ -228,6 +255,17 @@ lm_status lm_debug_dequant(lm_model* m, int32_t layer, int32_t which, int32_t ro
  * the position like a step.  For profiling the persistent kernel. */
 lm_status lm_debug_step_trace(lm_model* m, const int32_t* d_tokens, uint64_t* out, int64_t capacity,
                               int32_t* n_cus, int32_t* n_phases);
+
+/* The embedding and the dataflow launch of one step (lm_set_dataflow; no LM
+ * head, the position is not advanced; the K/V row of the current position is
+ * written as a step writes it), recording per workgroup into
+ * out[wg][4] (host, capacity in uint64 words): [0] start, [1] its wait passed
+ * (0 for workgroups that do not wait), [2] its work is done (100 MHz constant
+ * clock), [3] hardware ids (HW_ID in the high half, XCC_ID in the low half).
+ * Workgroups are layer-major, phases QKV, attention, Wo, gate/up, down with
+ * wg_per_phase[5] workgroups each; *n_wg gives the total.  For profiling. */
+lm_status lm_debug_flow_trace(lm_model* m, const int32_t* d_tokens, uint64_t* out, int64_t capacity,
+                              int32_t* n_wg, int32_t* wg_per_phase);
 
 /* A plain read-only kernel over n_bytes of device memory (sum of 16-byte
  * words), for calibrating HBM counters and the read ceiling; *ms = average

@@ -33,7 +33,13 @@ CASES = {
                                               steps=3, batch=1),
     # the 70B shape's layers (hidden 8192, ffn 28672, 64/8 heads) in Q4_0 at its context length
     "llama70b_q4_2layers": synth.variant("llama70b_q4", n_layers=2, steps=2),
+    # 8B layer shapes in Q8_0; positions 127, 128, 129: the new key ends a
+    # 64-position attention chunk, then is alone in a fresh chunk, then second
+    "llama8b_q8_2layers_ctx127": synth.variant("llama8b_q8", n_layers=2, ctx=127, steps=3, batch=1),
 }
+
+# shapes the one-launch step supports (head_dim 128, hidden and FFN >= 2048)
+FLOW_CASES = ["llama8b_q8_2layers_ctx127", "llama8b_q4_2layers_ctx4k", "llama70b_q4_2layers"]
 
 _models = {}
 
@@ -45,12 +51,23 @@ def get_model(name):
     return _models[name]
 
 
-def run_parity(model, n_seq, steps=None, persistent=False):
+def set_mode(g, mode):
+    """default | ops (per-operator kernels) | flow (dataflow step) | persistent"""
+    if mode == "persistent":
+        g.set_persistent(True)
+    elif mode == "ops":
+        g.set_dataflow(False)
+    elif mode == "flow":
+        g.set_dataflow(1)
+    elif mode == "resident":
+        g.set_dataflow(2)
+
+
+def run_parity(model, n_seq, steps=None, mode="default"):
     cfg = model.cfg
     steps = steps or cfg.steps
     g = open_gpu(model, max_seqs=n_seq)
-    if persistent:
-        g.set_persistent(True)
+    set_mode(g, mode)
     om = open_oracle(model, n_seq)
     toks = synth.start_tokens(cfg, n_seq)
     worst = 0.0
@@ -88,7 +105,93 @@ def test_decode_parity(name):
 @pytest.mark.parametrize("name", list(CASES))
 def test_decode_parity_persistent(name):
     """The same steps through the persistent one-kernel step."""
-    run_parity(get_model(name), n_seq=1, persistent=True)
+    run_parity(get_model(name), n_seq=1, mode="persistent")
+
+
+@pytest.mark.parametrize("name", FLOW_CASES)
+def test_decode_parity_flow(name):
+    """The dataflow step (all layers in one launch) against the oracle."""
+    run_parity(get_model(name), n_seq=1, mode="flow")
+
+
+@pytest.mark.parametrize("name", FLOW_CASES)
+def test_decode_parity_resident(name):
+    """The resident variant of the one-launch step (two workgroups per CU
+    through every operator) against the oracle."""
+    run_parity(get_model(name), n_seq=1, mode="resident")
+
+
+@pytest.mark.parametrize("name", FLOW_CASES)
+def test_decode_parity_ops(name):
+    """The per-operator kernels, selected explicitly, on the one-launch shapes."""
+    run_parity(get_model(name), n_seq=1, mode="ops")
+
+
+def _steps(g, cfg, n):
+    g.set_position(0, cfg.ctx)
+    t = synth.start_tokens(cfg, 1)
+    out = []
+    for _ in range(n):
+        lg, am = g.step(t)
+        out.append((lg.copy(), am.copy()))
+        t = am
+    return out
+
+
+@pytest.mark.parametrize("name", ["llama8b_q8_2layers_ctx127", "llama8b_q4_2layers_ctx4k"])
+@pytest.mark.parametrize("mode", [1, 2])
+def test_flow_equals_ops_bitwise(name, mode):
+    """The one-launch step (dataflow grid or resident workgroups) runs the
+    per-operator arithmetic in the same order (same per-row lane split, digit
+    staging, reductions and merge order), so its logits equal the per-operator
+    kernels' bit for bit."""
+    model = get_model(name)
+    cfg = model.cfg
+    g = open_gpu(model, max_seqs=1)
+    try:
+        g.set_dataflow(0)
+        ops = _steps(g, cfg, cfg.steps)
+        g.set_dataflow(mode)
+        flow = _steps(g, cfg, cfg.steps)
+        for st, ((a, b), (c, d)) in enumerate(zip(ops, flow)):
+            assert np.array_equal(b, d), (st, b, d)
+            assert np.array_equal(a, c), (st, float(np.max(np.abs(a - c))))
+    finally:
+        g.close()
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_flow_graph_and_eager_launches_agree(mode):
+    """Launch counting across graph replays and eager launches: the phase
+    counters grow every launch, so a wrong launch number would either hang a
+    wait (reported as an error) or let a phase start early (different logits)."""
+    model = get_model("llama8b_q8_2layers_ctx127")
+    cfg = model.cfg
+    g = open_gpu(model, max_seqs=1)
+    try:
+        g.set_dataflow(mode)
+        runs = []
+        for mode in (True, False, True, True, False):
+            g.set_graph(mode)
+            runs.append(_steps(g, cfg, 3))
+        g.check_error()
+        for other in runs[1:]:
+            for (a, b), (c, d) in zip(runs[0], other):
+                assert np.array_equal(a, c) and np.array_equal(b, d)
+    finally:
+        g.close()
+
+
+def test_flow_unsupported_shape_is_rejected():
+    import token_decode_llama_amd as lm
+    g = open_gpu(get_model("tiny_q8"), max_seqs=1)
+    try:
+        with pytest.raises(lm.LMError) as e:
+            g.set_dataflow(True)
+        assert e.value.status == lm.LM_E_STATE
+        g.set_dataflow(False)
+    finally:
+        g.close()
 
 
 @pytest.mark.parametrize("name,n_seq", [("tiny_q8", 3), ("tiny_q4", 4)])
@@ -167,6 +270,7 @@ def test_stream_mode_bit_identical(name):
 
         # streaming uses the per-operator kernels: compare against the same kernels resident
         g.set_persistent(False)
+        g.set_dataflow(False)
         resident = run()
         g.stream_mode(True)
         streamed = run()

@@ -17,16 +17,16 @@ LIB_PATH = os.path.join(HERE, "liblmdecode.so")
 
 LM_OK, LM_E_ARG, LM_E_STATE, LM_E_OOM, LM_E_HIP, LM_E_CTX = range(6)
 LM_Q4_0, LM_Q8_0 = 2, 8
-KERNEL_KINDS = ("embed", "qkv", "attn", "wo", "gateup", "down", "lmhead", "copy", "step")
+KERNEL_KINDS = ("embed", "qkv", "attn", "wo", "gateup", "down", "lmhead", "copy", "step", "flow")
 
 # every symbol include/lmdecode.h declares
 EXPORTS = (
     "lm_model_create", "lm_model_destroy", "lm_load_layer_weights", "lm_load_global_weights",
     "lm_load_kv", "lm_get_kv", "lm_set_position", "lm_get_position", "lm_stream_mode",
-    "lm_decode_step", "lm_decode_step_dev", "lm_set_graph", "lm_set_persistent", "lm_stream",
-    "lm_last_error",
+    "lm_decode_step", "lm_decode_step_dev", "lm_set_graph", "lm_set_persistent", "lm_set_dataflow",
+    "lm_check_error", "lm_stream", "lm_last_error",
     "lm_kernel_timing", "lm_kernel_stats", "lm_kernel_bytes", "lm_debug_dequant",
-    "lm_debug_read_bw", "lm_debug_step_trace",
+    "lm_debug_read_bw", "lm_debug_step_trace", "lm_debug_flow_trace",
 )
 
 
@@ -78,6 +78,8 @@ def load():
         "lm_decode_step_dev": ([vp, vp, i32, vp, vp], st),
         "lm_set_graph": ([vp, i32], st),
         "lm_set_persistent": ([vp, i32], st),
+        "lm_set_dataflow": ([vp, i32], st),
+        "lm_check_error": ([vp], st),
         "lm_stream": ([vp], vp),
         "lm_last_error": ([vp], ctypes.c_char_p),
         "lm_kernel_timing": ([vp, i32], st),
@@ -86,6 +88,7 @@ def load():
         "lm_debug_dequant": ([vp, i32, i32, i32, i32, vp], st),
         "lm_debug_read_bw": ([vp, i64, i32, ctypes.POINTER(dbl)], st),
         "lm_debug_step_trace": ([vp, vp, vp, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)], st),
+        "lm_debug_flow_trace": ([vp, vp, vp, i64, ctypes.POINTER(i32), vp], st),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -215,6 +218,13 @@ class Model:
     def set_persistent(self, enable: bool):
         self._check(self._lib.lm_set_persistent(self._h, 1 if enable else 0))
 
+    def set_dataflow(self, mode):
+        """False/0: per-operator kernels; True/1: dataflow grid; 2: resident workgroups."""
+        self._check(self._lib.lm_set_dataflow(self._h, int(mode)))
+
+    def check_error(self):
+        self._check(self._lib.lm_check_error(self._h))
+
     # -- measurement ---------------------------------------------------------
     def kernel_timing(self, enable: bool):
         self._check(self._lib.lm_kernel_timing(self._h, 1 if enable else 0))
@@ -245,6 +255,15 @@ class Model:
         self._check(self._lib.lm_debug_step_trace(self._h, ptr, _p(out), cap, ctypes.byref(ncu),
                                                   ctypes.byref(nph)))
         return out[:ncu.value * nph.value * 8].reshape(ncu.value, nph.value, 8)
+
+    def debug_flow_trace(self, d_tokens, max_wg: int = 1 << 20):
+        """One traced dataflow launch: ([wg][4] uint64 trace, workgroups per phase)."""
+        n = ctypes.c_int32()
+        per = np.zeros(5, np.int32)
+        out = np.zeros(max_wg * 4, np.uint64)
+        ptr = d_tokens if isinstance(d_tokens, int) else d_tokens.data_ptr()
+        self._check(self._lib.lm_debug_flow_trace(self._h, ptr, _p(out), out.size, ctypes.byref(n), _p(per)))
+        return out[:n.value * 4].reshape(n.value, 4), per
 
     def debug_read_bw(self, n_bytes: int, iters: int = 10) -> float:
         ms = ctypes.c_double()

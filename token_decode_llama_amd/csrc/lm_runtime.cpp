@@ -16,6 +16,7 @@
 // waits for the compute that last read it.
 #include "lm_internal.h"
 #include "lm_step.h"
+#include "lm_flow.h"
 
 #include "../../include/lmdecode.h"
 
@@ -130,6 +131,13 @@ struct lm_model {
     int* d_lm_cnt = nullptr;
     float* d_sink = nullptr;
     float* d_dbg = nullptr;               // debug dequant rows
+
+    // dataflow step (one sequence, weights resident): every layer in one launch
+    bool flow_capable = false;
+    int flow_mode = 0;                    // 0 off (per-operator kernels: measured faster), 1 dataflow
+                                          // grid, 2 resident workgroups (lm_set_dataflow)
+    FlowArgs flow_h{};
+    uint32_t* d_flow_ctl = nullptr;       // [L * 5] phase counts, then epoch, error flag
 
     // persistent one-kernel step (one sequence, weights resident)
     bool step_capable = false;            // the step kernel's LDS plan fits this shape
@@ -486,6 +494,51 @@ extern "C" lm_status lm_model_create(const lm_config* cfg, void* hip_stream, lm_
             }
         CREATE_HIP(hipMemcpy(m->d_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice));
         CREATE_HIP(hipMemcpy(m->d_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice));
+    }
+    // dataflow step: its phase counters and arguments
+    if (flow_supported(c.qtype, (int)m->H, (int)m->F, (int)m->hd, (int)m->nq, (int)m->nkv) && m->n_cus >= 1) {
+        const int64_t words = flow_ctl_words(c.n_layers);
+        CREATE_TRY(dev_alloc(m, (void**)&m->d_flow_ctl, words * 4, "dataflow step counters"));
+        CREATE_HIP(hipMemsetAsync(m->d_flow_ctl, 0, (size_t)(words * 4), m->stream));
+        FlowArgs& a = m->flow_h;
+        a.L = c.n_layers;
+        a.H = (int)m->H;
+        a.F = (int)m->F;
+        a.nq = (int)m->nq;
+        a.nkv = (int)m->nkv;
+        a.hd = (int)m->hd;
+        a.max_ctx = c.max_ctx;
+        a.max_chunks = m->max_chunks;
+        a.eps = (float)c.rms_eps;
+        a.scale = (float)(1.0 / std::sqrt((double)m->hd));
+        a.blobs = m->d_layers;
+        a.blob_stride = m->blob_bytes;
+        const int which[4] = {M_QKV, M_WO, M_GU, M_DOWN};
+        for (int i = 0; i < 4; ++i) {
+            a.mat[i].q_off = m->mo[which[i]].q;
+            a.mat[i].sc_off = m->mo[which[i]].sc;
+            a.mat[i].N = m->mo[which[i]].N;
+            a.mat[i].K = m->mo[which[i]].K;
+        }
+        a.norms = m->d_norms;
+        a.kcache = m->d_k;
+        a.vcache = m->d_v;
+        a.kv_layer = kv_layer_elems(m);
+        a.pos = m->d_pos;
+        a.rope_cos = m->d_cos;
+        a.rope_sin = m->d_sin;
+        a.x = m->d_x;
+        a.q = m->d_q;
+        a.o = m->d_o;
+        a.h = m->d_h;
+        a.attn_part = m->d_attn_part;
+        a.attn_cnt = m->d_attn_cnt;
+        a.done = m->d_flow_ctl;
+        a.epoch = m->d_flow_ctl + (int64_t)c.n_layers * kFlowOps * (kFlowSub + 1) * kFlowLine;
+        a.err = a.epoch + kFlowLine;
+        a.resident = m->flow_mode == 2;
+        flow_plan(a, c.qtype, m->n_cus);
+        m->flow_capable = true;
     }
     // persistent one-kernel step (one sequence): tile-major weight copies,
     // its argument block in device memory, barrier counts
@@ -921,6 +974,10 @@ static bool use_step(const lm_model* m, int n_seq) {
     return m->persistent && m->step_capable && n_seq == 1 && !m->streaming;
 }
 
+static bool use_flow(const lm_model* m, int n_seq) {
+    return m->flow_mode != 0 && m->flow_capable && n_seq == 1 && !m->streaming && !use_step(m, n_seq);
+}
+
 static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d_logits, int* d_argmax) {
     const lm_config& c = m->cfg;
     const int L = c.n_layers;
@@ -933,6 +990,11 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
     {
         KTimer t(m, LM_K_EMBED);
         HIPTRY(m, launch_embed(m->d_embd, d_tok, (int)m->V, (int)m->H, m->d_x, n_seq, st));
+    }
+    const bool flow = use_flow(m, n_seq);
+    if (flow) {
+        KTimer t(m, LM_K_FLOW);
+        HIPTRY(m, launch_flow(m->flow_h, c.qtype, st));
     }
     GemvArgs base{};
     base.qtype = c.qtype;
@@ -969,7 +1031,7 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
         m->prefetched[0] = m->prefetched[1] = false;
     }
 
-    for (int l = 0; l < L; ++l) {
+    for (int l = 0; l < (flow ? 0 : L); ++l) {
         if (m->streaming) HIPTRY(m, hipStreamWaitEvent(st, m->ev_copied[l & 1], 0));
         const uint8_t* blob = layer_blob(m, l);
         const float* g_attn = m->d_norms + (int64_t)l * 2 * m->H;
@@ -1092,6 +1154,28 @@ static lm_status check_step_error(lm_model* m) {
                 "free for the step kernel); the step's outputs are invalid");
 }
 
+// The dataflow step sets its error flag when a wait between workgroups timed
+// out; the counters are then reset so the next step starts clean.
+static lm_status check_flow_error(lm_model* m) {
+    uint32_t err = 0;
+    HIPTRY(m, hipMemcpy(&err, m->flow_h.err, 4, hipMemcpyDeviceToHost));
+    if (!err) return LM_OK;
+    HIPTRY(m, hipMemset(m->d_flow_ctl, 0, (size_t)(flow_ctl_words(m->cfg.n_layers) * 4)));
+    return fail(m, LM_E_HIP, "dataflow decode step: a wait between workgroups timed out; the step's outputs "
+                "are invalid");
+}
+
+extern "C" lm_status lm_check_error(lm_model* m) {
+    if (!m) return LM_E_ARG;
+    HIPTRY(m, hipStreamSynchronize(m->stream));
+    if (m->flow_capable) {
+        lm_status s = check_flow_error(m);
+        if (s != LM_OK) return s;
+    }
+    if (m->step_capable) return check_step_error(m);
+    return LM_OK;
+}
+
 static lm_status check_ready(lm_model* m, const char* fn, int n_seq) {
     if (!m->global_loaded)
         return fail(m, LM_E_STATE, "%s: global weights not loaded (lm_load_global_weights)", fn);
@@ -1129,6 +1213,10 @@ extern "C" lm_status lm_decode_step(lm_model* m, const int32_t* tokens, int32_t 
         lm_status es = check_step_error(m);
         if (es != LM_OK) return es;
     }
+    if (use_flow(m, n_seq)) {
+        lm_status es = check_flow_error(m);
+        if (es != LM_OK) return es;
+    }
     return collect_timing(m);
 }
 
@@ -1154,6 +1242,53 @@ extern "C" lm_status lm_set_persistent(lm_model* m, int32_t enable) {
     m->persistent = enable != 0;
     invalidate_graphs(m);
     return LM_OK;
+}
+
+extern "C" lm_status lm_set_dataflow(lm_model* m, int32_t enable) {
+    if (!m) return LM_E_ARG;
+    if (enable && !m->flow_capable)
+        return fail(m, LM_E_STATE, "lm_set_dataflow: the dataflow step is not available for this model (it needs "
+                    "Q8_0/Q4_0, head_dim 128, at most 8 query heads per KV head, hidden and FFN widths >= 2048)");
+    if (enable < 0 || enable > 2) return fail(m, LM_E_ARG, "lm_set_dataflow: mode = %d; expected 0, 1 or 2", enable);
+    HIPTRY(m, hipStreamSynchronize(m->stream));
+    if (m->flow_capable && (enable == 2) != (m->flow_h.resident != 0)) {
+        // the counters' launch totals depend on the plan: start them afresh
+        m->flow_h.resident = enable == 2;
+        flow_plan(m->flow_h, m->cfg.qtype, m->n_cus);
+        HIPTRY(m, hipMemset(m->d_flow_ctl, 0, (size_t)(flow_ctl_words(m->cfg.n_layers) * 4)));
+    }
+    m->flow_mode = enable;
+    invalidate_graphs(m);
+    return LM_OK;
+}
+
+extern "C" lm_status lm_debug_flow_trace(lm_model* m, const int32_t* d_tokens, uint64_t* out, int64_t capacity,
+                                         int32_t* n_wg, int32_t* wg_per_phase) {
+    if (!m || !d_tokens || !out || !n_wg || !wg_per_phase) return LM_E_ARG;
+    if (!use_flow(m, 1)) return fail(m, LM_E_STATE, "lm_debug_flow_trace: the dataflow step is not in use");
+    lm_status st = check_ready(m, "lm_debug_flow_trace", 1);
+    if (st != LM_OK) return st;
+    const int64_t grid = m->flow_h.resident ? (int64_t)m->cfg.n_layers * kFlowOps * m->flow_h.wg[0]
+                                            : (int64_t)m->cfg.n_layers * m->flow_h.wg_off[kFlowOps];
+    const int64_t words = grid * kFlowTraceWords;
+    *n_wg = (int32_t)grid;
+    for (int i = 0; i < kFlowOps; ++i) wg_per_phase[i] = m->flow_h.wg[i];
+    if (capacity < words)
+        return fail(m, LM_E_ARG, "lm_debug_flow_trace: capacity = %lld words; expected >= %lld", (long long)capacity,
+                    (long long)words);
+    uint64_t* d = nullptr;
+    HIPTRY(m, hipStreamSynchronize(m->stream));
+    HIPTRY(m, hipMalloc(&d, (size_t)words * 8));
+    FlowArgs a = m->flow_h;
+    a.trace = d;
+    hipError_t e = hipMemsetAsync(d, 0, (size_t)words * 8, m->stream);
+    if (e == hipSuccess) e = launch_embed(m->d_embd, d_tokens, (int)m->V, (int)m->H, m->d_x, 1, m->stream);
+    if (e == hipSuccess) e = launch_flow(a, m->cfg.qtype, m->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(m->stream);
+    if (e == hipSuccess) e = hipMemcpy(out, d, (size_t)words * 8, hipMemcpyDeviceToHost);
+    (void)hipFree(d);
+    if (e != hipSuccess) return fail(m, LM_E_HIP, "lm_debug_flow_trace: %s", hipGetErrorString(e));
+    return check_flow_error(m);
 }
 
 extern "C" lm_status lm_debug_step_trace(lm_model* m, const int32_t* d_tokens, uint64_t* out, int64_t capacity,
@@ -1296,6 +1431,13 @@ extern "C" lm_status lm_kernel_bytes(const lm_model* m, int32_t kind, int32_t n_
         case LM_K_DOWN: b = L * (H * F * bpw + S * (F * 4 + H * 8)); break;
         case LM_K_LMHEAD: b = V * H * bpw + H * 4 + S * H * 4; break;
         case LM_K_COPY: b = m->streaming ? L * (double)m->blob_bytes : 0.0; break;
+        case LM_K_FLOW:
+            for (int k = LM_K_QKV; k <= LM_K_DOWN; ++k) {
+                double kb = 0.0;
+                (void)lm_kernel_bytes(m, k, n_seq, &kb);
+                b += kb;
+            }
+            break;
         case LM_K_STEP:
             for (int k = LM_K_EMBED; k <= LM_K_LMHEAD; ++k) {
                 double kb = 0.0;
