@@ -183,17 +183,19 @@ class Runner:
         return e0.elapsed_time(e1) / n
 
     def kernel_profile(self, timing_steps: int):
-        """Per-kind (launches, total ms) over eager steps with events around every
-        kernel, and the algorithmic bytes of one step at those steps' mean position."""
+        """Per-kind (launches, total ms) over graph-replayed steps with HIP events
+        captured around every kernel inside the step graph, and the algorithmic
+        bytes of one step at those steps' mean position."""
         import torch
         import token_decode_llama_amd as lm
         self.rewind()
-        self.g.kernel_timing(True)
+        # events captured into the step graph: the kernels as the replayed step runs them
+        self.g.kernel_timing(2)
         for _ in range(timing_steps):
             self.step()
         torch.cuda.synchronize()
         kstats = {k: self.g.kernel_stats(k) for k in lm.KERNEL_KINDS}
-        self.g.kernel_timing(False)
+        self.g.kernel_timing(0)
         for s in range(self.n_seq):
             self.g.set_position(s, self.cfg.ctx + timing_steps // 2)
         kbytes = {k: self.g.kernel_bytes(k, self.n_seq) for k in lm.KERNEL_KINDS}
@@ -229,10 +231,14 @@ def kernel_table(kstats, kbytes, n_layers):
     return out
 
 
-def roofline_for(kind, kstats, kbytes, n_layers, workload):
+def roofline_for(kind, kstats, kbytes, n_layers, workload, us_graph=None):
+    """Algorithmic bytes per launch / average launch duration.  The duration is
+    the family's launches replayed as the step graph runs them, between two HIP
+    events on the model's stream (us_graph); without it, the per-launch events
+    of the timing steps (which add the events' own cost to every launch)."""
     n, ms = kstats[kind]
     per_launch_bytes = kbytes[kind] / per_launch(kind, n_layers)
-    avg_ms = ms / max(n, 1)
+    avg_ms = us_graph * 1e-3 if us_graph else ms / max(n, 1)
     achieved = per_launch_bytes / (avg_ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_from_profiles(kind, workload),
@@ -255,6 +261,31 @@ def base_line(metric, tps, ms_per_step, steps, warmup, step_bytes, config, dtype
 
 
 # ---------------------------------------------------------------------------
+def alternatives(r, args) -> dict:
+    """The same workload through the library's other one-sequence step paths
+    (opt-in; the headline uses the default per-operator kernels), timed the
+    same way, for comparison."""
+    import token_decode_llama_amd as lm
+    res = {}
+    for label, on, off in (("one_launch_dataflow", lambda: r.g.set_dataflow(1), lambda: r.g.set_dataflow(0)),
+                           ("one_launch_resident", lambda: r.g.set_dataflow(2), lambda: r.g.set_dataflow(0)),
+                           ("persistent_step", lambda: r.g.set_persistent(True), lambda: r.g.set_persistent(False))):
+        try:
+            on()
+        except lm.LMError as e:
+            res[label] = None
+            log(f"{label}: not available ({e})")
+            continue
+        r.rewind()
+        r.warm(args.warmup)
+        res[label] = round(r.timed(min(args.steps, 32)), 4)
+        r.g.check_error()
+        off()
+        r.rewind()
+        log(f"{label}: {res[label]:.4f} ms/step")
+    return res
+
+
 def run_single(args, name: str, n_seq: int):
     """llama8b_q8 (headline, batch 1) and llama8b_q4 (four sequences)."""
     import synth
@@ -273,7 +304,13 @@ def run_single(args, name: str, n_seq: int):
     kstats, kbytes = r.kernel_profile(args.timing_steps)
     L = cfg.n_layers
     dom = dominant(kstats)
-    roofline = roofline_for(dom, kstats, kbytes, L, name)
+    r.rewind()
+    us_graph = r.g.time_kind(dom, n_seq, 20)
+    r.rewind()
+    roofline = roofline_for(dom, kstats, kbytes, L, name, us_graph)
+    roofline["timing"] = ("the family's launches of one step captured alone as a HIP graph and replayed 20 "
+                          "times between two HIP events on the model's stream")
+    roofline["avg_launch_us_events_in_step"] = round(1e3 * kstats[dom][1] / max(kstats[dom][0], 1), 3)
     step_bytes = r.step_bytes(args.steps // 2)
     read_ms = r.g.debug_read_bw(4 << 30, 5)
     if args.calibrate:
@@ -293,6 +330,8 @@ def run_single(args, name: str, n_seq: int):
     out["roofline"] = roofline
     out["read_ceiling_GBps"] = round((4 << 30) / (read_ms * 1e-3) / 1e9, 1)
     out["kernels"] = kernel_table(kstats, kbytes, L)
+    if n_seq == 1 and not args.only_kernels and not args.no_alternatives:
+        out["alternatives_ms_per_step"] = alternatives(r, args)
     r.close()
     if not args.no_cpu_baseline and not args.only_kernels:
         log("oracle baseline")
@@ -459,6 +498,8 @@ def main():
     ap.add_argument("--stream-steps", type=int, default=16, help="timed steps in layer-streaming mode (70B)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-alternatives", action="store_true",
+                    help="skip timing the opt-in one-launch and persistent step paths")
     ap.add_argument("--only-kernels", action="store_true",
                     help="skip the timed loop: run the per-kernel timing steps only (for profilers)")
     ap.add_argument("--calibrate", action="store_true",

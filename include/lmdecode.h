@@ -225,8 +225,22 @@ typedef enum {
 /* enable = 1: eager steps record HIP events around every kernel of every
  * kind on the model's stream (and around every layer copy on the copy stream
  * in streaming mode) and accumulate their durations; graph replay is
- * suspended while timing is on.  Resets the totals. */
+ * suspended.  enable = 2: the same events are captured into the step's HIP
+ * graph (event-record nodes beside the kernels), and every replay waits for
+ * the step and accumulates them - kernel times as the replayed step runs them
+ * (streaming mode, which does not replay graphs, times eagerly).  0: off.
+ * Resets the totals; changing the mode drops captured graphs. */
 lm_status lm_kernel_timing(lm_model* m, int32_t enable);
+
+/* Average duration of one launch of kernel family `kind` as the step graph
+ * runs it: the step's launches of that family alone (same arguments and
+ * order; an LM-head-only replay does not advance positions) are captured as
+ * one graph and replayed `reps` times between two HIP events on the model's
+ * stream; result = elapsed / (reps x the family's launches per step).  It
+ * overwrites activations
+ * and the current position's K/V row like a step (the next step rewrites
+ * them).  Resident weights only.  For the roofline of a kernel family. */
+lm_status lm_time_kind(lm_model* m, int32_t kind, int32_t n_seq, int32_t reps, double* us_per_launch);
 
 /* Launch count and summed duration (ms) of one kernel kind since timing was
  * enabled (events are read after the step's final synchronisation). */

@@ -182,6 +182,53 @@ def test_flow_graph_and_eager_launches_agree(mode):
         g.close()
 
 
+@pytest.mark.parametrize("mode", [1, 2])
+def test_kernel_timing_modes(mode):
+    """Per-kernel timing, eager (1) or with events captured inside the step
+    graph (2): the outputs are those of untimed steps, and every launch of the
+    step is counted once per step."""
+    model = get_model("llama1b_2layers")
+    cfg = model.cfg
+    g = open_gpu(model, max_seqs=1)
+    try:
+        ref = _steps(g, cfg, 3)
+        g.kernel_timing(mode)
+        got = _steps(g, cfg, 3)
+        counts = {k: g.kernel_stats(k) for k in ("embed", "qkv", "attn", "wo", "gateup", "down", "lmhead")}
+        g.kernel_timing(0)
+        again = _steps(g, cfg, 3)
+        for other in (got, again):
+            for (a, b), (c, d) in zip(ref, other):
+                assert np.array_equal(a, c) and np.array_equal(b, d)
+        for k, (n, ms) in counts.items():
+            per_step = 1 if k in ("embed", "lmhead") else cfg.n_layers
+            assert n == 3 * per_step, (k, n)
+            assert ms > 0.0, k
+    finally:
+        g.close()
+
+
+def test_time_kind_graph_replay():
+    """lm_time_kind: every family's launches replayed alone as a graph give a
+    positive per-launch time, leave the position where it was, and the steps
+    after it equal those before."""
+    model = get_model("llama1b_2layers")
+    cfg = model.cfg
+    g = open_gpu(model, max_seqs=1)
+    try:
+        ref = _steps(g, cfg, 2)
+        g.set_position(0, cfg.ctx)
+        for k in ("embed", "qkv", "attn", "wo", "gateup", "down", "lmhead"):
+            us = g.time_kind(k, 1, 3)
+            assert us > 0.0, k
+            assert g.position(0) == cfg.ctx, k
+        again = _steps(g, cfg, 2)
+        for (a, b), (c, d) in zip(ref, again):
+            assert np.array_equal(a, c) and np.array_equal(b, d)
+    finally:
+        g.close()
+
+
 def test_flow_unsupported_shape_is_rejected():
     import token_decode_llama_amd as lm
     g = open_gpu(get_model("tiny_q8"), max_seqs=1)

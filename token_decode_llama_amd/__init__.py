@@ -25,7 +25,7 @@ EXPORTS = (
     "lm_load_kv", "lm_get_kv", "lm_set_position", "lm_get_position", "lm_stream_mode",
     "lm_decode_step", "lm_decode_step_dev", "lm_set_graph", "lm_set_persistent", "lm_set_dataflow",
     "lm_check_error", "lm_stream", "lm_last_error",
-    "lm_kernel_timing", "lm_kernel_stats", "lm_kernel_bytes", "lm_debug_dequant",
+    "lm_kernel_timing", "lm_kernel_stats", "lm_time_kind", "lm_kernel_bytes", "lm_debug_dequant",
     "lm_debug_read_bw", "lm_debug_step_trace", "lm_debug_flow_trace",
 )
 
@@ -85,6 +85,7 @@ def load():
         "lm_kernel_timing": ([vp, i32], st),
         "lm_kernel_stats": ([vp, i32, ctypes.POINTER(i64), ctypes.POINTER(dbl)], st),
         "lm_kernel_bytes": ([vp, i32, i32, ctypes.POINTER(dbl)], st),
+        "lm_time_kind": ([vp, i32, i32, i32, ctypes.POINTER(dbl)], st),
         "lm_debug_dequant": ([vp, i32, i32, i32, i32, vp], st),
         "lm_debug_read_bw": ([vp, i64, i32, ctypes.POINTER(dbl)], st),
         "lm_debug_step_trace": ([vp, vp, vp, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)], st),
@@ -226,8 +227,15 @@ class Model:
         self._check(self._lib.lm_check_error(self._h))
 
     # -- measurement ---------------------------------------------------------
-    def kernel_timing(self, enable: bool):
-        self._check(self._lib.lm_kernel_timing(self._h, 1 if enable else 0))
+    def kernel_timing(self, mode):
+        """0/False off; 1/True eager steps with events; 2 events inside the replayed graph."""
+        self._check(self._lib.lm_kernel_timing(self._h, int(mode)))
+
+    def time_kind(self, kind: str, n_seq: int = 1, reps: int = 20) -> float:
+        """Microseconds per launch of one kernel family, replayed as the step graph runs it."""
+        us = ctypes.c_double()
+        self._check(self._lib.lm_time_kind(self._h, KERNEL_KINDS.index(kind), n_seq, reps, ctypes.byref(us)))
+        return us.value
 
     def kernel_stats(self, kind: str):
         c = ctypes.c_int64()

@@ -165,20 +165,28 @@ struct lm_model {
     hipEvent_t ev_consumed[2] = {nullptr, nullptr};
     bool prefetched[2] = {false, false};   // slot holds layer 0/1 for the next step
 
+    struct Pending { int kind; hipEvent_t a, b; };
     struct GraphEntry {
         int n_seq;
         const int* tok;
         float* logits;
         int* argmax;
         hipGraphExec_t exec;
+        std::vector<Pending> timers;      // event pairs recorded inside the graph (timing mode 2)
+        std::vector<hipEvent_t> owned;    // those events, destroyed with the graph
     };
     std::vector<GraphEntry> graphs;
 
     // kernel timing
-    bool timing = false;
+    int timing = 0;                       // 0 off, 1 eager steps with events, 2 events inside the graph
+    hipError_t timer_err = hipSuccess;    // first failed timing call (reported by the step)
+    int only_kind = -1;                   // >= 0 while capturing a one-family timing graph
+    // timing mode 2: the graph nodes each timed scope captured (its last node and
+    // the node before it); event-record nodes are inserted around them afterwards
+    struct CapScope { int kind; hipGraphNode_t before, last; };
+    std::vector<CapScope> cap_scopes;
     int64_t kcount[LM_K_COUNT] = {};
     double kms[LM_K_COUNT] = {};
-    struct Pending { int kind; hipEvent_t a, b; };
     std::vector<Pending> pending;
     std::vector<hipEvent_t> ev_pool;
     size_t ev_used = 0;
@@ -736,7 +744,10 @@ static lm_status upload_tiles(lm_model* m, const TileGeom& g, RowFn src_row, uin
 }
 
 static void invalidate_graphs(lm_model* m) {
-    for (auto& g : m->graphs) (void)hipGraphExecDestroy(g.exec);
+    for (auto& g : m->graphs) {
+        (void)hipGraphExecDestroy(g.exec);
+        for (hipEvent_t e : g.owned) (void)hipEventDestroy(e);
+    }
     m->graphs.clear();
 }
 
@@ -901,28 +912,124 @@ static hipEvent_t pool_event(lm_model* m) {
     return m->ev_pool[m->ev_used++];
 }
 
+// The node the model's stream would attach the next captured operation to
+// (nullptr when nothing has been captured yet); false when not capturing.
+static bool capture_tail(lm_model* m, hipGraphNode_t* tail) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    const hipGraphNode_t* deps = nullptr;
+    size_t nd = 0;
+    if (hipStreamGetCaptureInfo_v2(m->stream, &cs, nullptr, nullptr, &deps, &nd) != hipSuccess ||
+        cs != hipStreamCaptureStatusActive)
+        return false;
+    *tail = nd ? deps[nd - 1] : nullptr;
+    return true;
+}
+
+// Timing of one kernel family's launches.  Eager (mode 1): HIP events on the
+// model's stream around the launches.  Inside a graph capture (mode 2): the
+// captured nodes are noted, and event-record nodes are put around them when
+// the capture ends (events recorded on a capturing stream are not supported by
+// every HIP runtime this library meets).
 struct KTimer {
     lm_model* m;
     int kind;
     hipEvent_t a = nullptr;
+    bool captured = false;
+    hipGraphNode_t before = nullptr;
     KTimer(lm_model* mm, int k) : m(mm), kind(k) {
-        if (m->timing) {
-            a = pool_event(m);
-            if (a) (void)hipEventRecord(a, m->stream);
+        if (!m->timing) return;
+        if (m->timing == 2 && capture_tail(m, &before)) {
+            captured = true;
+            return;
         }
+        a = pool_event(m);
+        if (a && hipEventRecord(a, m->stream) != hipSuccess && m->timer_err == hipSuccess)
+            m->timer_err = hipErrorUnknown;
     }
     ~KTimer() {
-        if (m->timing && a) {
+        if (!m->timing) return;
+        if (captured) {
+            hipGraphNode_t last = nullptr;
+            if (capture_tail(m, &last) && last && last != before) m->cap_scopes.push_back({kind, before, last});
+            return;
+        }
+        if (a) {
             hipEvent_t b = pool_event(m);
             if (b) {
-                (void)hipEventRecord(b, m->stream);
+                if (hipEventRecord(b, m->stream) != hipSuccess && m->timer_err == hipSuccess)
+                    m->timer_err = hipErrorUnknown;
                 m->pending.push_back({kind, a, b});
             }
         }
     }
 };
 
+// Puts an event-record node before the first and after the last node of every
+// timed scope of a captured (linear) step graph.  Scopes are handled last to
+// first, so each one's own edges are still those of the capture.
+static hipError_t insert_timers(lm_model* m, hipGraph_t graph, std::vector<lm_model::Pending>& timers,
+                                std::vector<hipEvent_t>& owned) {
+    hipError_t e = hipSuccess;
+    auto deps_of = [](hipGraphNode_t n, std::vector<hipGraphNode_t>& out) {
+        size_t nd = 0;
+        hipError_t r = hipGraphNodeGetDependencies(n, nullptr, &nd);
+        out.resize(nd);
+        if (r == hipSuccess && nd) r = hipGraphNodeGetDependencies(n, out.data(), &nd);
+        return r;
+    };
+    auto dependents_of = [](hipGraphNode_t n, std::vector<hipGraphNode_t>& out) {
+        size_t nd = 0;
+        hipError_t r = hipGraphNodeGetDependentNodes(n, nullptr, &nd);
+        out.resize(nd);
+        if (r == hipSuccess && nd) r = hipGraphNodeGetDependentNodes(n, out.data(), &nd);
+        return r;
+    };
+    std::vector<lm_model::Pending> found;
+    for (size_t i = m->cap_scopes.size(); i-- > 0;) {
+        const auto& sc = m->cap_scopes[i];
+        // the scope's first node: walk back from its last to the node after `before`
+        hipGraphNode_t first = sc.last;
+        std::vector<hipGraphNode_t> d;
+        for (;;) {
+            if ((e = deps_of(first, d)) != hipSuccess) return e;
+            if (d.empty() || (d.size() == 1 && d[0] == sc.before)) break;
+            if (d.size() != 1) return hipErrorInvalidValue;     // not a linear chain
+            first = d[0];
+        }
+        hipEvent_t ea = nullptr, eb = nullptr;
+        if ((e = hipEventCreate(&ea)) != hipSuccess) return e;
+        owned.push_back(ea);
+        if ((e = hipEventCreate(&eb)) != hipSuccess) return e;
+        owned.push_back(eb);
+        // after the last node: last -> B -> (what followed last)
+        std::vector<hipGraphNode_t> next;
+        if ((e = dependents_of(sc.last, next)) != hipSuccess) return e;
+        hipGraphNode_t nb = nullptr;
+        if ((e = hipGraphAddEventRecordNode(&nb, graph, &sc.last, 1, eb)) != hipSuccess) return e;
+        for (hipGraphNode_t n : next) {
+            if ((e = hipGraphRemoveDependencies(graph, &sc.last, &n, 1)) != hipSuccess) return e;
+            if ((e = hipGraphAddDependencies(graph, &nb, &n, 1)) != hipSuccess) return e;
+        }
+        // before the first node: (its dependency) -> A -> first
+        hipGraphNode_t na = nullptr;
+        if ((e = hipGraphAddEventRecordNode(&na, graph, d.empty() ? nullptr : d.data(), d.size(), ea)) != hipSuccess)
+            return e;
+        for (hipGraphNode_t n : d)
+            if ((e = hipGraphRemoveDependencies(graph, &n, &first, 1)) != hipSuccess) return e;
+        if ((e = hipGraphAddDependencies(graph, &na, &first, 1)) != hipSuccess) return e;
+        found.push_back({sc.kind, ea, eb});
+    }
+    timers.assign(found.rbegin(), found.rend());
+    return hipSuccess;
+}
+
 static lm_status collect_timing(lm_model* m) {
+    if (m->timer_err != hipSuccess) {
+        m->timer_err = hipSuccess;
+        m->pending.clear();
+        m->ev_used = 0;
+        return fail(m, LM_E_HIP, "recording a kernel-timing event failed");
+    }
     if (m->pending.empty()) return LM_OK;
     HIPTRY(m, hipStreamSynchronize(m->stream));
     HIPTRY(m, hipStreamSynchronize(m->copy_stream));
@@ -978,23 +1085,28 @@ static bool use_flow(const lm_model* m, int n_seq) {
     return m->flow_mode != 0 && m->flow_capable && n_seq == 1 && !m->streaming && !use_step(m, n_seq);
 }
 
+// Launch this family's kernels?  All of them, unless a timing-only graph of
+// one family is being captured (lm_time_kind).
+static bool want(const lm_model* m, int kind) { return m->only_kind < 0 || m->only_kind == kind; }
+
 static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d_logits, int* d_argmax) {
     const lm_config& c = m->cfg;
     const int L = c.n_layers;
     hipStream_t st = m->stream;
     if (use_step(m, n_seq)) {
         KTimer t(m, LM_K_STEP);
-        HIPTRY(m, launch_step(m->step_h, m->d_step_args, c.qtype, d_tok, d_logits, d_argmax, m->n_cus, st));
+        if (want(m, LM_K_STEP))
+            HIPTRY(m, launch_step(m->step_h, m->d_step_args, c.qtype, d_tok, d_logits, d_argmax, m->n_cus, st));
         return LM_OK;
     }
     {
         KTimer t(m, LM_K_EMBED);
-        HIPTRY(m, launch_embed(m->d_embd, d_tok, (int)m->V, (int)m->H, m->d_x, n_seq, st));
+        if (want(m, LM_K_EMBED)) HIPTRY(m, launch_embed(m->d_embd, d_tok, (int)m->V, (int)m->H, m->d_x, n_seq, st));
     }
     const bool flow = use_flow(m, n_seq);
     if (flow) {
         KTimer t(m, LM_K_FLOW);
-        HIPTRY(m, launch_flow(m->flow_h, c.qtype, st));
+        if (want(m, LM_K_FLOW)) HIPTRY(m, launch_flow(m->flow_h, c.qtype, st));
     }
     GemvArgs base{};
     base.qtype = c.qtype;
@@ -1046,13 +1158,13 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
             a.norm_g = g_attn;
             a.out = m->d_q; a.out_stride = (int)m->qrows;
             a.kcache = kc; a.vcache = vc;
-            HIPTRY(m, gemv(m, a, EPI_QKV, n_seq, st));
+            if (want(m, LM_K_QKV)) HIPTRY(m, gemv(m, a, EPI_QKV, n_seq, st));
         }
         {   // GQA attention with causal softmax
             KTimer t(m, LM_K_ATTN);
             AttnArgs b = at;
             b.kcache = kc; b.vcache = vc;
-            HIPTRY(m, launch_attention(b, n_seq, st));
+            if (want(m, LM_K_ATTN)) HIPTRY(m, launch_attention(b, n_seq, st));
         }
         {   // x += Wo o
             KTimer t(m, LM_K_WO);
@@ -1060,7 +1172,7 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
             a.w = mat_at(m, blob, M_WO);
             a.xin = m->d_o; a.x_stride = (int)m->qrows;
             a.out = m->d_x; a.out_stride = (int)m->H;
-            HIPTRY(m, gemv(m, a, EPI_RESID, n_seq, st));
+            if (want(m, LM_K_WO)) HIPTRY(m, gemv(m, a, EPI_RESID, n_seq, st));
         }
         {   // RMSNorm -> gate/up GEMV -> SwiGLU
             KTimer t(m, LM_K_GATEUP);
@@ -1069,7 +1181,7 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
             a.xin = m->d_x; a.x_stride = (int)m->H;
             a.norm_g = g_ffn;
             a.out = m->d_h; a.out_stride = (int)m->F;
-            HIPTRY(m, gemv(m, a, EPI_SWIGLU, n_seq, st));
+            if (want(m, LM_K_GATEUP)) HIPTRY(m, gemv(m, a, EPI_SWIGLU, n_seq, st));
         }
         {   // x += Wdown h
             KTimer t(m, LM_K_DOWN);
@@ -1077,7 +1189,7 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
             a.w = mat_at(m, blob, M_DOWN);
             a.xin = m->d_h; a.x_stride = (int)m->F;
             a.out = m->d_x; a.out_stride = (int)m->H;
-            HIPTRY(m, gemv(m, a, EPI_RESID, n_seq, st));
+            if (want(m, LM_K_DOWN)) HIPTRY(m, gemv(m, a, EPI_RESID, n_seq, st));
         }
         if (m->streaming) {
             HIPTRY(m, hipEventRecord(m->ev_consumed[l & 1], st));
@@ -1106,40 +1218,63 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
         a.part_idx = m->d_lm_pidx;
         a.counter = m->d_lm_cnt;
         a.argmax_out = d_argmax;
-        a.pos_inc = m->d_pos;
-        HIPTRY(m, gemv(m, a, EPI_LOGITS, n_seq, st));
+        // a timing-only replay of the LM head must not advance the positions
+        a.pos_inc = m->only_kind < 0 ? m->d_pos : nullptr;
+        if (want(m, LM_K_LMHEAD)) HIPTRY(m, gemv(m, a, EPI_LOGITS, n_seq, st));
     }
     return LM_OK;
 }
 
+// Launch a captured step; with timers (timing mode 2) wait for it and add the
+// durations of the event pairs recorded inside the graph.
+static lm_status launch_graph(lm_model* m, const lm_model::GraphEntry& g) {
+    HIPTRY(m, hipGraphLaunch(g.exec, m->stream));
+    if (g.timers.empty()) return LM_OK;
+    for (const auto& t : g.timers) m->pending.push_back(t);
+    return collect_timing(m);
+}
+
 static lm_status run_step(lm_model* m, int n_seq, const int* d_tok, float* d_logits, int* d_argmax) {
-    const bool graph_ok = m->use_graph && !m->timing && !m->streaming;
+    const bool graph_ok = m->use_graph && m->timing != 1 && !m->streaming;
     if (!graph_ok) return enqueue_step(m, n_seq, d_tok, d_logits, d_argmax);
     for (auto& g : m->graphs)
-        if (g.n_seq == n_seq && g.tok == d_tok && g.logits == d_logits && g.argmax == d_argmax) {
-            HIPTRY(m, hipGraphLaunch(g.exec, m->stream));
-            return LM_OK;
-        }
+        if (g.n_seq == n_seq && g.tok == d_tok && g.logits == d_logits && g.argmax == d_argmax)
+            return launch_graph(m, g);
+    lm_status cs = collect_timing(m);
+    if (cs != LM_OK) return cs;
+    m->cap_scopes.clear();
     hipGraph_t graph = nullptr;
     HIPTRY(m, hipStreamBeginCapture(m->stream, hipStreamCaptureModeThreadLocal));
     lm_status s = enqueue_step(m, n_seq, d_tok, d_logits, d_argmax);
     hipError_t e = hipStreamEndCapture(m->stream, &graph);
-    if (s != LM_OK) {
-        if (graph) (void)hipGraphDestroy(graph);
-        return s;
+    std::vector<lm_model::Pending> timers;
+    std::vector<hipEvent_t> owned;
+    if (s == LM_OK && e == hipSuccess && m->timing == 2) {
+        const hipError_t te = insert_timers(m, graph, timers, owned);
+        if (te != hipSuccess)
+            s = fail(m, LM_E_HIP, "placing timing events in the step graph failed: %s", hipGetErrorString(te));
     }
-    if (e != hipSuccess) return fail(m, LM_E_HIP, "hipStreamEndCapture failed: %s", hipGetErrorString(e));
+    m->cap_scopes.clear();
+    if (s != LM_OK || e != hipSuccess) {
+        if (graph) (void)hipGraphDestroy(graph);
+        for (hipEvent_t ev : owned) (void)hipEventDestroy(ev);
+        if (s != LM_OK) return s;
+        return fail(m, LM_E_HIP, "hipStreamEndCapture failed: %s", hipGetErrorString(e));
+    }
     hipGraphExec_t exec = nullptr;
     e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
     (void)hipGraphDestroy(graph);
-    if (e != hipSuccess) return fail(m, LM_E_HIP, "hipGraphInstantiate failed: %s", hipGetErrorString(e));
+    if (e != hipSuccess) {
+        for (hipEvent_t ev : owned) (void)hipEventDestroy(ev);
+        return fail(m, LM_E_HIP, "hipGraphInstantiate failed: %s", hipGetErrorString(e));
+    }
     if (m->graphs.size() >= 8) {
         (void)hipGraphExecDestroy(m->graphs.front().exec);
+        for (hipEvent_t ev : m->graphs.front().owned) (void)hipEventDestroy(ev);
         m->graphs.erase(m->graphs.begin());
     }
-    m->graphs.push_back({n_seq, d_tok, d_logits, d_argmax, exec});
-    HIPTRY(m, hipGraphLaunch(exec, m->stream));
-    return LM_OK;
+    m->graphs.push_back({n_seq, d_tok, d_logits, d_argmax, exec, std::move(timers), std::move(owned)});
+    return launch_graph(m, m->graphs.back());
 }
 
 // The step kernel sets an error flag when a wait between workgroups times
@@ -1397,8 +1532,70 @@ extern "C" lm_status lm_kernel_timing(lm_model* m, int32_t enable) {
     if (!m) return LM_E_ARG;
     lm_status st = collect_timing(m);
     if (st != LM_OK) return st;
-    m->timing = enable != 0;
+    if (enable < 0 || enable > 2) return fail(m, LM_E_ARG, "lm_kernel_timing: mode = %d; expected 0, 1 or 2", enable);
+    if (enable != m->timing) {
+        // graphs captured with (or without) timing events do not serve the other mode
+        HIPTRY(m, hipStreamSynchronize(m->stream));
+        invalidate_graphs(m);
+    }
+    m->timing = enable;
     for (int k = 0; k < LM_K_COUNT; ++k) { m->kcount[k] = 0; m->kms[k] = 0.0; }
+    return LM_OK;
+}
+
+extern "C" lm_status lm_time_kind(lm_model* m, int32_t kind, int32_t n_seq, int32_t reps, double* us_per_launch) {
+    if (!m || !us_per_launch || kind < 0 || kind >= LM_K_COUNT || kind == LM_K_COPY || reps < 1) return LM_E_ARG;
+    lm_status st = check_ready(m, "lm_time_kind", n_seq);
+    if (st != LM_OK) return st;
+    if (m->streaming) return fail(m, LM_E_STATE, "lm_time_kind: not in streaming mode (steps there are not graphs)");
+    // the step's launches of this family alone, captured as one graph (same
+    // arguments and order as in the step), replayed between two events
+    HIPTRY(m, hipStreamSynchronize(m->stream));
+    const int saved_timing = m->timing;
+    m->timing = 0;
+    m->only_kind = kind;
+    hipGraph_t graph = nullptr;
+    hipError_t e = hipStreamBeginCapture(m->stream, hipStreamCaptureModeThreadLocal);
+    if (e == hipSuccess) {
+        st = enqueue_step(m, n_seq, m->d_tokens, nullptr, m->d_argmax);
+        e = hipStreamEndCapture(m->stream, &graph);
+    }
+    m->only_kind = -1;
+    m->timing = saved_timing;
+    if (st != LM_OK) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return st;
+    }
+    if (e != hipSuccess) return fail(m, LM_E_HIP, "lm_time_kind: capture failed: %s", hipGetErrorString(e));
+    size_t n_nodes = 0;
+    (void)hipGraphGetNodes(graph, nullptr, &n_nodes);
+    hipGraphExec_t exec = nullptr;
+    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (e != hipSuccess) return fail(m, LM_E_HIP, "lm_time_kind: instantiate failed: %s", hipGetErrorString(e));
+    if (n_nodes == 0) {
+        (void)hipGraphExecDestroy(exec);
+        return fail(m, LM_E_STATE, "lm_time_kind: kind %d launches nothing in this model's step", kind);
+    }
+    hipEvent_t a = nullptr, b = nullptr;
+    float ms = 0.f;
+    e = hipEventCreate(&a);
+    if (e == hipSuccess) e = hipEventCreate(&b);
+    if (e == hipSuccess) e = hipGraphLaunch(exec, m->stream);          // warm
+    if (e == hipSuccess) e = hipEventRecord(a, m->stream);
+    for (int r = 0; r < reps && e == hipSuccess; ++r) e = hipGraphLaunch(exec, m->stream);
+    if (e == hipSuccess) e = hipEventRecord(b, m->stream);
+    if (e == hipSuccess) e = hipEventSynchronize(b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, a, b);
+    if (a) (void)hipEventDestroy(a);
+    if (b) (void)hipEventDestroy(b);
+    (void)hipGraphExecDestroy(exec);
+    if (e != hipSuccess) return fail(m, LM_E_HIP, "lm_time_kind: %s", hipGetErrorString(e));
+    // launches of the family per step (a launch may be more than one graph node:
+    // the several-sequence GEMV stages its activations first)
+    const bool once = kind == LM_K_EMBED || kind == LM_K_LMHEAD || kind == LM_K_FLOW || kind == LM_K_STEP;
+    const double launches = once ? 1.0 : (double)m->cfg.n_layers;
+    *us_per_launch = 1e3 * (double)ms / ((double)reps * launches);
     return LM_OK;
 }
 
