@@ -461,27 +461,37 @@ hipError_t launch_gemv(const GemvArgs& a, int epi, int n_seq, int max_blocks, hi
 // ---------------------------------------------------------------------------
 // 2..4 sequences: dequant-GEMV as a dense contraction on the matrix cores
 // ---------------------------------------------------------------------------
-// v_mfma_f32_16x16x32_f16 contracts a 16-row x 32-column weight tile (one quant
-// block) with a 32 x 16 activation tile whose columns are the sequences.
-// Operand layout (lane l, group g = l/16, index j = l%16):
-//   A: row j, columns 8g..8g+7;  B: column (sequence) j, rows 8g..8g+7;
+// v_mfma_i32_16x16x32_i8 contracts a 16-row x 32-column weight tile (one quant
+// block, its int8 quants - or Q4_0 nibbles as unsigned bytes - taken as they
+// are in HBM) with a 32 x 16 int8 activation tile.  The activations enter as
+// the integer digits of the one-sequence GEMV (per block b and sequence s,
+// X = rint(x * 127 * 2^16 / max|x_b|) = D2 * 2^16 + D1 * 2^8 + D0, signed
+// bytes), and the tile's 16 columns are (sequence, digit) pairs: column
+// j = 3 s + d, so one MFMA gives every digit's exact int32 dot product for up
+// to four sequences.  Operand layout (lane l, group g = l/16, index j = l%16):
+//   A: row j, columns 8g..8g+7;  B: column j, rows 8g..8g+7;
 //   D: rows 4g..4g+3, column j.
-// Weights enter as exact fp16 integers (q, or nibble - 8); activations as an
-// exact pair x = hi + lo of fp16 values (two accumulating MFMAs), so each
-// block's 16x16 result is the block dot product in fp32; it is then scaled by
-// the row's block scale and accumulated in fp32.
-typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
-typedef float f4_t __attribute__((ext_vector_type(4)));
+// Each lane keeps an fp32 sum per (row, column): the block's int32 result
+// (Q4_0: minus 8 x the block's digit sum) times the row's block scale and the
+// block's activation scale.  After the K loop the three digit columns of a
+// sequence are combined (2^16 D2 + 2^8 D1 + D0) across lanes.
+typedef int v4i_t __attribute__((ext_vector_type(4)));
 
-// One workgroup per sequence: RMSNorm (optional) and the hi/lo fp16 split of
-// every activation, written as B fragments: frag[b][part][g][s] = 8 halves
-// (block b, columns 8g..8g+7, sequence s; part 0 = hi, 1 = lo).
-__global__ __launch_bounds__(kBlock) void k_xfrag(const float* __restrict__ xin, int x_stride,
-                                                 const float* __restrict__ g, float eps, int K,
-                                                 uint4* __restrict__ frag) {
+// Activation fragments of the several-sequence GEMV (at a.xfrag):
+//   [nb][4 groups g][16 columns j] x 16 bytes: digit d of sequence s (j = 3s+d)
+//   for the block's columns 8g..8g+7 (8 bytes), the block's activation scale
+//   max|x_b| / (127 x 2^16) of sequence s (fp32), and the digit sum of column j
+//   over the block's 32 columns (int32); columns j >= 3 x n_seq are unused.
+// One workgroup per sequence: RMSNorm (optional), then the digits of every
+// activation.  Four consecutive threads hold one 32-column block.
+__global__ __launch_bounds__(kBlock) void k_xdigits(const float* __restrict__ xin, int x_stride,
+                                                   const float* __restrict__ g, float eps, int K,
+                                                   uint8_t* __restrict__ xb) {
     __shared__ float red[kWaves];
     const int s = blockIdx.x, tid = threadIdx.x;
+    const int nb = K >> 5;
     const float* x = xin + (int64_t)s * x_stride;
+    uint4* frag = (uint4*)xb;
     float scale = 1.f;
     if (g) {
         float ss = 0.f;
@@ -494,48 +504,57 @@ __global__ __launch_bounds__(kBlock) void k_xfrag(const float* __restrict__ xin,
         }
         scale = 1.0f / sqrtf(block_sum(ss, red) / (float)K + eps);
     }
-    for (int c = tid; c < K / 8; c += kBlock) {            // 8 columns per piece
-        const float4 v0 = *(const float4*)(x + 8 * c), v1 = *(const float4*)(x + 8 * c + 4);
-        float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    // K % 32 == 0 and kBlock % 4 == 0: the four threads of a block are all in or all out
+    for (int c0 = 0; c0 < K / 8; c0 += kBlock) {
+        const int c = c0 + tid;                     // 8 columns per thread
+        const bool in = c < K / 8;
+        float v[8];
+        const int cc = in ? c : 0;
+        const float4 v0 = *(const float4*)(x + 8 * cc), v1 = *(const float4*)(x + 8 * cc + 4);
+        v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
+        v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
         if (g) {
-            const float4 g0 = *(const float4*)(g + 8 * c), g1 = *(const float4*)(g + 8 * c + 4);
+            const float4 g0 = *(const float4*)(g + 8 * cc), g1 = *(const float4*)(g + 8 * cc + 4);
             const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
             #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = v[e] * scale * gg[e];
         }
-        h8_t hi, lo;
+        float m = 0.f;
+        #pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
+        m = fmaxf(m, __shfl_xor(m, 1, 64));         // the block's four threads
+        m = fmaxf(m, __shfl_xor(m, 2, 64));
+        const float f = m > 0.f ? 8323072.0f / m : 0.f;     // 127 * 2^16 / max|x_b|
+        uint32_t w[3][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}};
+        int t[3] = {0, 0, 0};
         #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            hi[e] = (_Float16)v[e];
-            lo[e] = (_Float16)(v[e] - (float)hi[e]);
+            const int X = (int)rintf(v[e] * f);
+            const int x1 = (X + 128) >> 8, x2 = (x1 + 128) >> 8;
+            const int d0 = (int)(int8_t)(X & 255), d1 = (int)(int8_t)(x1 & 255);
+            w[0][e >> 2] |= (uint32_t)(d0 & 255) << (8 * (e & 3));
+            w[1][e >> 2] |= (uint32_t)(d1 & 255) << (8 * (e & 3));
+            w[2][e >> 2] |= (uint32_t)(x2 & 255) << (8 * (e & 3));
+            t[0] += d0;
+            t[1] += d1;
+            t[2] += x2;
         }
-        const int b = c >> 2, gq = c & 3;
-        frag[((b * 2 + 0) * 4 + gq) * 4 + s] = *(const uint4*)&hi;
-        frag[((b * 2 + 1) * 4 + gq) * 4 + s] = *(const uint4*)&lo;
+        #pragma unroll
+        for (int d = 0; d < 3; ++d) {
+            t[d] += __shfl_xor(t[d], 1, 64);
+            t[d] += __shfl_xor(t[d], 2, 64);
+        }
+        if (in) {
+            const int b = c >> 2, gq = c & 3;
+            const uint32_t sxb = __float_as_uint(m * (1.0f / 8323072.0f));
+            #pragma unroll
+            for (int d = 0; d < 3; ++d)
+                frag[(b * 4 + gq) * 16 + 3 * s + d] = make_uint4(w[d][0], w[d][1], sxb, (uint32_t)t[d]);
+        }
     }
 }
 
-template <int QT>
-__device__ __forceinline__ h8_t weights_f16(uint2 raw, int g) {
-    h8_t a;
-    if (QT == kQ8_0) {
-        #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            a[e] = (_Float16)(float)(int8_t)(raw.x >> (8 * e));
-            a[4 + e] = (_Float16)(float)(int8_t)(raw.y >> (8 * e));
-        }
-    } else {
-        const int sh = g >= 2 ? 4 : 0;     // groups 2, 3: high nibbles (columns 16..31)
-        #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            a[e] = (_Float16)(float)((int)((raw.x >> (8 * e + sh)) & 15u) - 8);
-            a[4 + e] = (_Float16)(float)((int)((raw.y >> (8 * e + sh)) & 15u) - 8);
-        }
-    }
-    return a;
-}
-
-constexpr int kMbDepth = 4;   // blocks per lane whose loads are in flight together
+constexpr int kMbDepth = 4;   // blocks per lane per pipeline stage (two stages in flight)
 
 // One 16-row tile per workgroup at a time (grid-stride over tiles); the W
 // wavefronts of the workgroup split the tile's K blocks and reduce through LDS.
@@ -550,60 +569,102 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, j = lane & 15;
+    const int sq = min(j / 3, 3), dg = j - 3 * (j / 3);   // this lane's column: sequence, digit
     const int n_tiles = (N + 15) >> 4;
     const int nbq = (nb + W - 1) / W;
     const int b_lo = min(wave * nbq, nb), b_hi = min(b_lo + nbq, nb);
     const int64_t rowq = (QT == kQ8_0) ? (int64_t)K : (int64_t)(K >> 1);
-    const bool col_ok = j < a.n_seq;
+    const uint4* frag = (const uint4*)a.xfrag;
 
     float best_v = -FLT_MAX;
     int best_i = INT_MAX;
 
+    // one pipeline stage: kMbDepth blocks of this lane's row (weights, the 4
+    // rows' scales of its D rows, its B column's digits with scale and sum)
+    struct Stage {
+        uint2 w[kMbDepth], sc[kMbDepth];
+        uint4 x[kMbDepth];
+    };
     for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
         const int row = min(tile * 16 + j, N - 1);      // this lane's A row (clamped in a ragged tile)
         const uint8_t* qrow = a.w.q + (int64_t)row * rowq;
         const uint16_t* sct = a.w.sct + (int64_t)tile * nb * 16 + 4 * g;
-        f4_t acc = {0.f, 0.f, 0.f, 0.f};
-        for (int b0 = b_lo; b0 < b_hi; b0 += kMbDepth) {
-            uint2 wr[kMbDepth], sr[kMbDepth];
-            uint4 xh[kMbDepth], xl[kMbDepth];
+        auto load = [&](int b0, Stage& st) {
             #pragma unroll
             for (int u = 0; u < kMbDepth; ++u) {
-                const int b = min(b0 + u, b_hi - 1);
+                const int b = min(b0 + u, b_hi - 1);     // clamped: always in bounds
                 const uint8_t* p = (QT == kQ8_0)
                     ? qrow + (int64_t)(g >> 1) * nb * 16 + (uint32_t)b * 16u + (g & 1) * 8
                     : qrow + (uint32_t)b * 16u + (g & 1) * 8;
-                wr[u] = *(const uint2*)p;
-                sr[u] = *(const uint2*)(sct + (int64_t)b * 16);
-                const int fi = (b * 8 + g) * 4 + (col_ok ? j : 0);
-                xh[u] = a.xfrag[fi];
-                xl[u] = a.xfrag[fi + 16];
+                st.w[u] = *(const uint2*)p;
+                st.sc[u] = *(const uint2*)(sct + (int64_t)b * 16);
+                st.x[u] = frag[(b * 4 + g) * 16 + j];
             }
+        };
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        auto compute = [&](int b0, const Stage& st) {
             #pragma unroll
             for (int u = 0; u < kMbDepth; ++u) {
                 if (b0 + u >= b_hi) break;
-                const h8_t wa = weights_f16<QT>(wr[u], g);
-                h8_t bh = *(const h8_t*)&xh[u], bl = *(const h8_t*)&xl[u];
-                if (!col_ok) { bh = (h8_t)0; bl = (h8_t)0; }
-                f4_t c = {0.f, 0.f, 0.f, 0.f};
-                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa, bh, c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa, bl, c, 0, 0, 0);
-                acc[0] = fmaf(h2f((uint16_t)(sr[u].x & 0xFFFF)), c[0], acc[0]);
-                acc[1] = fmaf(h2f((uint16_t)(sr[u].x >> 16)), c[1], acc[1]);
-                acc[2] = fmaf(h2f((uint16_t)(sr[u].y & 0xFFFF)), c[2], acc[2]);
-                acc[3] = fmaf(h2f((uint16_t)(sr[u].y >> 16)), c[3], acc[3]);
+                uint2 wa = st.w[u];
+                if (QT == kQ4_0) {
+                    // columns 8g..8g+7: low nibbles (groups 0, 1) or high nibbles (2, 3) of the 8 bytes
+                    const int sh = g >= 2 ? 4 : 0;
+                    wa.x = (wa.x >> sh) & 0x0F0F0F0Fu;
+                    wa.y = (wa.y >> sh) & 0x0F0F0F0Fu;
+                }
+                const long av = (long)(((uint64_t)wa.y << 32) | wa.x);
+                const long bv = (long)(((uint64_t)st.x[u].y << 32) | st.x[u].x);
+                v4i_t c = {0, 0, 0, 0};
+                c = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, bv, c, 0, 0, 0);
+                if (QT == kQ4_0) {
+                    const int t8 = 8 * (int)st.x[u].w;       // nibble n = q + 8
+                    #pragma unroll
+                    for (int i = 0; i < 4; ++i) c[i] -= t8;
+                }
+                const float sx = __uint_as_float(st.x[u].z);
+                acc[0] = fmaf(h2f((uint16_t)(st.sc[u].x & 0xFFFF)) * sx, (float)c[0], acc[0]);
+                acc[1] = fmaf(h2f((uint16_t)(st.sc[u].x >> 16)) * sx, (float)c[1], acc[1]);
+                acc[2] = fmaf(h2f((uint16_t)(st.sc[u].y & 0xFFFF)) * sx, (float)c[2], acc[2]);
+                acc[3] = fmaf(h2f((uint16_t)(st.sc[u].y >> 16)) * sx, (float)c[3], acc[3]);
+            }
+        };
+        // two stages in flight: the next stage's loads are issued before this one computes
+        if (b_lo < b_hi) {
+            Stage sa, sb;
+            load(b_lo, sa);
+            int b0 = b_lo;
+            for (;;) {
+                const bool more = b0 + kMbDepth < b_hi;
+                if (more) load(b0 + kMbDepth, sb);
+                compute(b0, sa);
+                b0 += kMbDepth;
+                if (!more) break;
+                const bool more2 = b0 + kMbDepth < b_hi;
+                if (more2) load(b0 + kMbDepth, sa);
+                compute(b0, sb);
+                b0 += kMbDepth;
+                if (!more2) break;
             }
         }
         *(float4*)&part[wave][lane][0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
         __syncthreads();
-        if (wave == 0 && col_ok) {
-            float y[4] = {0.f, 0.f, 0.f, 0.f};
+        float y[4] = {0.f, 0.f, 0.f, 0.f};
+        if (wave == 0) {
             #pragma unroll
             for (int w = 0; w < W; ++w) {
                 const float4 v = *(const float4*)&part[w][lane][0];
                 y[0] += v.x; y[1] += v.y; y[2] += v.z; y[3] += v.w;
             }
-            const int s = j;
+            // a sequence's three digit columns sit in lanes j, j+1, j+2 of the group
+            #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float y1 = __shfl(y[i], lane + 1, 64), y2 = __shfl(y[i], lane + 2, 64);
+                y[i] = fmaf(y2, 65536.0f, fmaf(y1, 256.0f, y[i]));
+            }
+        }
+        if (wave == 0 && dg == 0 && j < 3 * a.n_seq) {
+            const int s = sq;
             #pragma unroll
             for (int pr = 0; pr < 2; ++pr) {
                 const int r0 = tile * 16 + 4 * g + 2 * pr;   // rows r0, r0 + 1 (a RoPE / gate-up pair)
@@ -656,7 +717,7 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
     }
 
     if (EPI == EPI_LOGITS) {
-        // sequence j's candidates sit in lanes j, j+16, j+32, j+48 of wavefront 0
+        // sequence s's candidates sit in lanes 3s, 3s+16, 3s+32, 3s+48 of wavefront 0
         if (wave == 0) {
             float bv = best_v;
             int bi = best_i;
@@ -666,9 +727,9 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
                 const int oi = __shfl_xor(bi, off, 64);
                 better(bv, bi, ov, oi);
             }
-            if (lane < a.n_seq) {
-                a.part_val[(int64_t)lane * gridDim.x + blockIdx.x] = bv;
-                a.part_idx[(int64_t)lane * gridDim.x + blockIdx.x] = bi;
+            if (g == 0 && dg == 0 && j < 3 * a.n_seq) {
+                a.part_val[(int64_t)sq * gridDim.x + blockIdx.x] = bv;
+                a.part_idx[(int64_t)sq * gridDim.x + blockIdx.x] = bi;
             }
         }
         __syncthreads();
@@ -736,8 +797,8 @@ hipError_t launch_gemv_batched(const GemvArgs& a0, int epi, int n_seq, int max_b
     if (n_seq < 1 || n_seq > 4 || !a0.w.sct || !a0.xfrag) return hipErrorInvalidValue;
     GemvArgs a = a0;
     a.n_seq = n_seq;
-    hipLaunchKernelGGL(k_xfrag, dim3(n_seq), dim3(kBlock), 0, st, a.xin, a.x_stride, a.norm_g, a.eps, a.w.K,
-                       a.xfrag);
+    hipLaunchKernelGGL(k_xdigits, dim3(n_seq), dim3(kBlock), 0, st, a.xin, a.x_stride, a.norm_g, a.eps, a.w.K,
+                       (uint8_t*)a.xfrag);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.qtype == kQ8_0) {
