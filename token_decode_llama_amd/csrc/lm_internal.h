@@ -24,8 +24,21 @@ struct QMat {
     const uint16_t* sc;
     const uint16_t* sct;   // scales again, transposed per 16-row tile: [N/16][nb][16]
                            // (present when the model decodes several sequences at once)
+    const uint8_t* qf;     // quants again, as matrix-core A fragments (same models; below)
     int N, K;
 };
+
+// Matrix-core fragment copy of the quants: per 16-row tile t and group of
+// qfrag_blocks consecutive blocks, 64 lane slices of 16 bytes; lane l = 16g + j
+// holds row j of the tile, columns 8g..8g+7 of each block of the group:
+//   Q8_0: 2 blocks x 8 int8;  Q4_0: 4 blocks x 4 bytes, byte i = nibble of
+//   column 8g+i (low) | nibble of column 8g+4+i (high).
+// Offset of (t, group, lane) = ((t * groups + group) * 64 + l) * 16.
+inline int qfrag_blocks(int qtype) { return qtype == kQ8_0 ? 2 : 4; }
+inline int64_t qfrag_bytes(int qtype, int64_t N, int64_t K) {
+    const int64_t nb = K / 32, per = qfrag_blocks(qtype);
+    return (N + 15) / 16 * ((nb + per - 1) / per) * 1024;
+}
 
 inline int64_t qmat_qbytes(int qtype, int64_t N, int64_t K) {
     return qtype == kQ8_0 ? N * K : N * K / 2;

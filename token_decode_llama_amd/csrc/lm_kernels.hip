@@ -571,9 +571,13 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
     const int g = lane >> 4, j = lane & 15;
     const int sq = min(j / 3, 3), dg = j - 3 * (j / 3);   // this lane's column: sequence, digit
     const int n_tiles = (N + 15) >> 4;
-    const int nbq = (nb + W - 1) / W;
+    // each wavefront's K range is whole pipeline stages (kMbDepth blocks)
+    const int nbq = ((nb + W - 1) / W + kMbDepth - 1) / kMbDepth * kMbDepth;
     const int b_lo = min(wave * nbq, nb), b_hi = min(b_lo + nbq, nb);
-    const int64_t rowq = (QT == kQ8_0) ? (int64_t)K : (int64_t)(K >> 1);
+    constexpr int PER = QT == kQ8_0 ? 2 : 4;        // blocks per 16-byte weight fragment
+    constexpr int NW = kMbDepth / PER;               // weight fragments per stage
+    static_assert(kMbDepth % 4 == 0, "a stage is whole fragments of both formats");
+    const int ngrp = (nb + PER - 1) / PER;
     const uint4* frag = (const uint4*)a.xfrag;
 
     float best_v = -FLT_MAX;
@@ -582,21 +586,24 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
     // one pipeline stage: kMbDepth blocks of this lane's row (weights, the 4
     // rows' scales of its D rows, its B column's digits with scale and sum)
     struct Stage {
-        uint2 w[kMbDepth], sc[kMbDepth];
-        uint4 x[kMbDepth];
+        uint4 w[NW];                 // this lane's weight fragments (A operands of kMbDepth blocks)
+        uint2 sc[kMbDepth];          // scales of its D rows
+        uint4 x[kMbDepth];           // its B column's digits, block scale, digit sum
     };
     for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
-        const int row = min(tile * 16 + j, N - 1);      // this lane's A row (clamped in a ragged tile)
-        const uint8_t* qrow = a.w.q + (int64_t)row * rowq;
+        // the tile's weights in fragment order: lane slices of 16 bytes, rows
+        // past N and blocks past K are zero
+        const uint4* qf = (const uint4*)a.w.qf + (int64_t)tile * ngrp * 64 + lane;
         const uint16_t* sct = a.w.sct + (int64_t)tile * nb * 16 + 4 * g;
         auto load = [&](int b0, Stage& st) {
             #pragma unroll
+            for (int f = 0; f < NW; ++f) {
+                const int grp = min(b0 / PER + f, ngrp - 1);   // clamped: always in bounds
+                st.w[f] = qf[(int64_t)grp * 64];
+            }
+            #pragma unroll
             for (int u = 0; u < kMbDepth; ++u) {
                 const int b = min(b0 + u, b_hi - 1);     // clamped: always in bounds
-                const uint8_t* p = (QT == kQ8_0)
-                    ? qrow + (int64_t)(g >> 1) * nb * 16 + (uint32_t)b * 16u + (g & 1) * 8
-                    : qrow + (uint32_t)b * 16u + (g & 1) * 8;
-                st.w[u] = *(const uint2*)p;
                 st.sc[u] = *(const uint2*)(sct + (int64_t)b * 16);
                 st.x[u] = frag[(b * 4 + g) * 16 + j];
             }
@@ -606,12 +613,15 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
             #pragma unroll
             for (int u = 0; u < kMbDepth; ++u) {
                 if (b0 + u >= b_hi) break;
-                uint2 wa = st.w[u];
-                if (QT == kQ4_0) {
-                    // columns 8g..8g+7: low nibbles (groups 0, 1) or high nibbles (2, 3) of the 8 bytes
-                    const int sh = g >= 2 ? 4 : 0;
-                    wa.x = (wa.x >> sh) & 0x0F0F0F0Fu;
-                    wa.y = (wa.y >> sh) & 0x0F0F0F0Fu;
+                uint2 wa;
+                if (QT == kQ8_0) {
+                    const uint4 f = st.w[u / 2];
+                    wa = (u & 1) ? make_uint2(f.z, f.w) : make_uint2(f.x, f.y);
+                } else {
+                    // 4 bytes: columns 8g+i in the low nibbles, 8g+4+i in the high ones
+                    const uint4 f = st.w[0];
+                    const uint32_t q = u == 0 ? f.x : u == 1 ? f.y : u == 2 ? f.z : f.w;
+                    wa = make_uint2(q & 0x0F0F0F0Fu, (q >> 4) & 0x0F0F0F0Fu);
                 }
                 const long av = (long)(((uint64_t)wa.y << 32) | wa.x);
                 const long bv = (long)(((uint64_t)st.x[u].y << 32) | st.x[u].x);
@@ -794,7 +804,7 @@ static hipError_t launch_mfma(const GemvArgs& a, int max_blocks, hipStream_t st)
 }
 
 hipError_t launch_gemv_batched(const GemvArgs& a0, int epi, int n_seq, int max_blocks, hipStream_t st) {
-    if (n_seq < 1 || n_seq > 4 || !a0.w.sct || !a0.xfrag) return hipErrorInvalidValue;
+    if (n_seq < 1 || n_seq > 4 || !a0.w.sct || !a0.w.qf || !a0.xfrag) return hipErrorInvalidValue;
     GemvArgs a = a0;
     a.n_seq = n_seq;
     hipLaunchKernelGGL(k_xdigits, dim3(n_seq), dim3(kBlock), 0, st, a.xin, a.x_stride, a.norm_g, a.eps, a.w.K,

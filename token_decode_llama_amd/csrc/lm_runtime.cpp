@@ -47,6 +47,7 @@ enum { M_QKV = 0, M_WO = 1, M_GU = 2, M_DOWN = 3, M_COUNT = 4 };
 struct MatOff {
     int64_t q, sc;   // byte offsets within the blob
     int64_t sct;     // transposed scales [ceil(N/16)][nb][16], or -1 (single-sequence models)
+    int64_t qf;      // matrix-core fragment copy of the quants (lm_internal.h), or -1
     int N, K;
 };
 
@@ -100,7 +101,7 @@ struct lm_model {
     int64_t H = 0, F = 0, V = 0, nq = 0, nkv = 0, hd = 0, qrows = 0, kvrows = 0;
     int64_t blob_bytes = 0;
     MatOff mo[M_COUNT]{};
-    int64_t lm_q_bytes = 0, lm_sc_bytes = 0, lm_sct_bytes = 0;
+    int64_t lm_q_bytes = 0, lm_sc_bytes = 0, lm_sct_bytes = 0, lm_qf_bytes = 0;
     bool batched = false;                 // max_seqs >= 2: MFMA path for 2..4 sequences
     int max_chunks = 0;
     int gemv_max_blocks = 1024;
@@ -118,6 +119,7 @@ struct lm_model {
     uint8_t* d_lm_q = nullptr;
     uint16_t* d_lm_sc = nullptr;
     uint16_t* d_lm_sct = nullptr;
+    uint8_t* d_lm_qf = nullptr;           // LM head fragment copy (several-sequence models)
     uint4* d_xfrag = nullptr;             // activation fragments of the MFMA path
     __half* d_k = nullptr;                // [L][S][nkv][max_ctx][hd]
     __half* d_v = nullptr;
@@ -345,15 +347,19 @@ static void layout(lm_model* m) {
         m->mo[i].sc = off;
         off = align_up(off + qmat_sbytes(NK[i][0], NK[i][1]));
         m->mo[i].sct = -1;
+        m->mo[i].qf = -1;
         if (m->batched) {
             m->mo[i].sct = off;
             off = align_up(off + sct_bytes(NK[i][0], NK[i][1]));
+            m->mo[i].qf = off;
+            off = align_up(off + qfrag_bytes(qt, NK[i][0], NK[i][1]));
         }
     }
     m->blob_bytes = off;
     m->lm_q_bytes = align_up(qmat_qbytes(qt, m->V, m->H));
     m->lm_sc_bytes = align_up(qmat_sbytes(m->V, m->H));
     m->lm_sct_bytes = m->batched ? align_up(sct_bytes(m->V, m->H)) : 0;
+    m->lm_qf_bytes = m->batched ? align_up(qfrag_bytes(qt, m->V, m->H)) : 0;
     m->max_chunks = (c.max_ctx + kAttnChunk - 1) / kAttnChunk;
 }
 
@@ -362,6 +368,7 @@ static QMat mat_at(const lm_model* m, const uint8_t* blob, int which) {
     w.q = blob + m->mo[which].q;
     w.sc = (const uint16_t*)(blob + m->mo[which].sc);
     w.sct = m->mo[which].sct >= 0 ? (const uint16_t*)(blob + m->mo[which].sct) : nullptr;
+    w.qf = m->mo[which].qf >= 0 ? blob + m->mo[which].qf : nullptr;
     w.N = m->mo[which].N;
     w.K = m->mo[which].K;
     return w;
@@ -372,6 +379,7 @@ static QMat lm_head_mat(const lm_model* m) {
     w.q = m->d_lm_q;
     w.sc = m->d_lm_sc;
     w.sct = m->d_lm_sct;
+    w.qf = m->d_lm_qf;
     w.N = (int)m->V;
     w.K = (int)m->H;
     return w;
@@ -454,6 +462,7 @@ extern "C" lm_status lm_model_create(const lm_config* cfg, void* hip_stream, lm_
     CREATE_TRY(dev_alloc(m, (void**)&m->d_lm_sc, m->lm_sc_bytes, "LM head scales"));
     if (m->batched) {
         CREATE_TRY(dev_alloc(m, (void**)&m->d_lm_sct, m->lm_sct_bytes, "LM head transposed scales"));
+        CREATE_TRY(dev_alloc(m, (void**)&m->d_lm_qf, m->lm_qf_bytes, "LM head matrix-core fragments"));
         const int64_t kmax = std::max<int64_t>({m->H, m->qrows, m->F});
         CREATE_TRY(dev_alloc(m, (void**)&m->d_xfrag, xfrag_bytes(kmax), "activation fragments"));
     }
@@ -701,6 +710,52 @@ static lm_status upload_sct(lm_model* m, int N, int K, RowFn src_row, uint16_t* 
     return LM_OK;
 }
 
+// The matrix-core fragment copy of a matrix's quants (layout: lm_internal.h,
+// qfrag_bytes): per 16-row tile and group of blocks, lane l = 16g + j holds
+// row j, columns 8g..8g+7 of each block of the group.  Zero past the last row
+// and past the last block.
+template <class RowFn>
+static lm_status upload_frag(lm_model* m, int N, int K, RowFn src_row, uint8_t* dst, bool dst_host) {
+    const int qt = m->cfg.qtype;
+    const int64_t nb = K / 32, tiles = (N + 15) / 16, bb = block_bytes(qt);
+    const int per = qfrag_blocks(qt);                    // blocks per 16-byte lane slice
+    const int64_t ngrp = (nb + per - 1) / per;
+    const int64_t bytes = qfrag_bytes(qt, N, K);
+    std::vector<uint8_t> tmp;
+    uint8_t* t = dst;
+    if (!dst_host) {
+        tmp.assign((size_t)bytes, 0);
+        t = tmp.data();
+    } else {
+        std::memset(t, 0, (size_t)bytes);
+    }
+    parallel_rows(tiles, [&](int64_t a, int64_t b) {
+        for (int64_t tile = a; tile < b; ++tile)
+            for (int j = 0; j < 16; ++j) {
+                const int64_t r = tile * 16 + j;
+                if (r >= N) continue;
+                const uint8_t* src = src_row(r);
+                for (int64_t blk = 0; blk < nb; ++blk) {
+                    const uint8_t* qs = src + blk * bb + 2;      // past the fp16 scale
+                    const int64_t grp = blk / per, k = blk % per;
+                    for (int g = 0; g < 4; ++g) {
+                        uint8_t* lane = t + ((tile * ngrp + grp) * 64 + 16 * g + j) * 16;
+                        if (qt == kQ8_0) {
+                            std::memcpy(lane + 8 * k, qs + 8 * g, 8);
+                        } else {
+                            // byte i: nibble of column 8g+i (low), of column 8g+4+i (high)
+                            auto nib = [&](int c) { return c < 16 ? (qs[c] & 15) : (qs[c - 16] >> 4); };
+                            for (int i = 0; i < 4; ++i)
+                                lane[4 * k + i] = (uint8_t)(nib(8 * g + i) | (nib(8 * g + 4 + i) << 4));
+                        }
+                    }
+                }
+            }
+    });
+    if (!dst_host) HIPTRY(m, hipMemcpy(dst, t, (size_t)bytes, hipMemcpyHostToDevice));
+    return LM_OK;
+}
+
 // Tile-major copy of one matrix for the persistent step (layout: lm_step.h):
 // row groups of 16 (rows past N are zero), each group's column chunks as
 // contiguous tiles: [block][row] quants, then [block][row] scales.
@@ -796,6 +851,11 @@ extern "C" lm_status lm_load_layer_weights(lm_model* m, int32_t layer, const lm_
         if ((st = upload_sct(m, (int)H, (int)m->qrows, src_wo, dt(M_WO), host)) != LM_OK) return st;
         if ((st = upload_sct(m, (int)(2 * F), (int)H, src_gu, dt(M_GU), host)) != LM_OK) return st;
         if ((st = upload_sct(m, (int)H, (int)F, src_down, dt(M_DOWN), host)) != LM_OK) return st;
+        auto df = [&](int i) { return blob + m->mo[i].qf; };
+        if ((st = upload_frag(m, m->mo[M_QKV].N, (int)H, src_qkv, df(M_QKV), host)) != LM_OK) return st;
+        if ((st = upload_frag(m, (int)H, (int)m->qrows, src_wo, df(M_WO), host)) != LM_OK) return st;
+        if ((st = upload_frag(m, (int)(2 * F), (int)H, src_gu, df(M_GU), host)) != LM_OK) return st;
+        if ((st = upload_frag(m, (int)H, (int)F, src_down, df(M_DOWN), host)) != LM_OK) return st;
     }
     if (m->step_capable) {
         uint8_t* tl = m->d_tiles + (int64_t)layer * m->tile_layer_stride;
@@ -825,6 +885,7 @@ extern "C" lm_status lm_load_global_weights(lm_model* m, const uint16_t* tok_emb
     lm_status st = upload_matrix(m, (int)m->V, (int)m->H, src_row, m->d_lm_q, m->d_lm_sc, false);
     if (st != LM_OK) return st;
     if (m->batched && (st = upload_sct(m, (int)m->V, (int)m->H, src_row, m->d_lm_sct, false)) != LM_OK) return st;
+    if (m->batched && (st = upload_frag(m, (int)m->V, (int)m->H, src_row, m->d_lm_qf, false)) != LM_OK) return st;
     if (m->step_capable && (st = upload_tiles(m, m->tgeo[4], src_row, m->d_lm_tiles)) != LM_OK) return st;
     m->global_loaded = true;
     return LM_OK;
