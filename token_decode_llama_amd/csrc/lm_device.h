@@ -1,6 +1,7 @@
 // lm_device.h - device helpers shared by the decode kernels (gfx950): the
 // integer-digit dot products of the dequant-GEMV, activation staging,
-// wavefront reductions and the lowest-index argmax rule.
+// wavefront reductions, the lowest-index argmax rule and the merge of
+// split-context attention states.
 #pragma once
 
 #include "lm_internal.h"
@@ -174,5 +175,100 @@ __device__ __forceinline__ void stage_digits(float4 v, int i, int K, int8_t* xq,
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// split-context attention
+// ---------------------------------------------------------------------------
+// Counts one more finished chunk of a (sequence, KV head) whose n_act chunks
+// publish partial states; true for the caller that completes the count (it
+// then merges).  Two levels, so that at most kCntGroup atomics meet on one
+// line: chunks count into their group's line, the chunk completing a group
+// counts into line 0.  Whoever completes a count resets it for the next launch.
+// One thread calls it, after its workgroup's partial stores have completed.
+__device__ __forceinline__ bool chunk_arrive(int* cnt, int chunk, int n_act) {
+    const int grp = chunk / kCntGroup, n_grp = (n_act + kCntGroup - 1) / kCntGroup;
+    const int in_grp = min(kCntGroup, n_act - grp * kCntGroup);
+    int* c1 = cnt + (1 + grp) * kCntStride;
+    if (__hip_atomic_fetch_add(c1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != in_grp - 1) return false;
+    __hip_atomic_store(c1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (n_grp == 1) return true;
+    if (__hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != n_grp - 1) return false;
+    __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+}
+
+// Log-sum-exp merge of the n_act chunk states of the G query heads of one KV
+// head (the split softmax of FlashDecoding-style attention; the pages' GQA
+// decode attention computes softmax(q K^T / sqrt(hd)) V over keys 0..pos):
+//   out[j][d] = sum_c o_c[d] e^(m_c - M) / sum_c l_c e^(m_c - M),  M = max_c m_c,
+// where chunk c's record (part(j) + c * (HD + 2)) holds its unnormalised
+// o[HD] = sum_t e^(s_t - m_c) v_t, then m_c and l_c = sum_t e^(s_t - m_c).
+// The merge is latency-bound, so it is laid out for memory-level parallelism:
+// a thread per (partition of the chunks, query head, 4 dimensions), each batch
+// of kB chunks loaded in full before the first is used, the partitions combined
+// in LDS.  ld2(p) returns the two floats at the 8-byte aligned p, device-
+// coherently; st4(i, v) writes out[i..i+3] (i = j * HD + d).  Cs: LDS scratch,
+// kBlock x 6 floats.  Every thread of the workgroup calls it (one barrier).
+template <int HD, class Part, class Ld2, class St4>
+__device__ __forceinline__ void merge_chunk_states(int G, int n_act, Part part, Ld2 ld2, St4 st4,
+                                                   float (*Cs)[6]) {
+    constexpr int kB = 8;                      // chunks per batch of loads
+    constexpr int64_t stride = HD + 2;
+    const int tid = threadIdx.x;
+    const int n_out = G * HD / 4;              // float4 outputs (at most kBlock)
+    const int P = kBlock / n_out;              // partitions of the chunks
+    const int p = tid / n_out, r = tid % n_out;
+    const int j = r / (HD / 4), d4 = (r % (HD / 4)) * 4;
+    const float* ph = part(j);
+    float M = -FLT_MAX, L = 0.f, O[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int base = p < P ? p * kB : n_act; base < n_act; base += P * kB) {
+        float2 ml[kB], o01[kB], o23[kB];
+        #pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            const float* pc = ph + min(base + u, n_act - 1) * stride;
+            ml[u] = ld2(pc + HD);
+            o01[u] = ld2(pc + d4);
+            o23[u] = ld2(pc + d4 + 2);
+        }
+        float bm = M;
+        #pragma unroll
+        for (int u = 0; u < kB; ++u)
+            if (base + u < n_act) bm = fmaxf(bm, ml[u].x);
+        const float rs = __expf(M - bm);
+        L *= rs;
+        #pragma unroll
+        for (int k = 0; k < 4; ++k) O[k] *= rs;
+        #pragma unroll
+        for (int u = 0; u < kB; ++u)
+            if (base + u < n_act) {
+                const float e = __expf(ml[u].x - bm);
+                L = fmaf(ml[u].y, e, L);
+                O[0] = fmaf(o01[u].x, e, O[0]);
+                O[1] = fmaf(o01[u].y, e, O[1]);
+                O[2] = fmaf(o23[u].x, e, O[2]);
+                O[3] = fmaf(o23[u].y, e, O[3]);
+            }
+        M = bm;
+    }
+    Cs[tid][0] = M;
+    Cs[tid][1] = L;
+    #pragma unroll
+    for (int k = 0; k < 4; ++k) Cs[tid][2 + k] = O[k];
+    __syncthreads();
+    if (p != 0) return;
+    float Mt = M;
+    for (int q = 1; q < P; ++q) Mt = fmaxf(Mt, Cs[q * n_out + r][0]);
+    float Lt = 0.f, Ot[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < P; ++q) {
+        const float* c = Cs[q * n_out + r];
+        if (c[0] == -FLT_MAX) continue;        // a partition that holds no chunk
+        const float e = __expf(c[0] - Mt);
+        Lt = fmaf(c[1], e, Lt);
+        #pragma unroll
+        for (int k = 0; k < 4; ++k) Ot[k] = fmaf(c[2 + k], e, Ot[k]);
+    }
+    const float inv = 1.f / Lt;
+    st4(j * HD + d4, make_float4(Ot[0] * inv, Ot[1] * inv, Ot[2] * inv, Ot[3] * inv));
+}
 
 }  // namespace lmk

@@ -34,7 +34,7 @@ struct FlowArgs {
     const float* rope_sin;
     float *x, *q, *o, *h;      // activations exchanged between workgroups
     float* attn_part;          // [nq][max_chunks][hd + 2]
-    int* attn_cnt;             // [nkv], zero between uses
+    int* attn_cnt;             // [nkv][attn_cnt_lines][kCntStride] (chunk_arrive), zero between uses
     uint32_t* done;            // [L * kFlowOps][kFlowSub + 1][kFlowLine] phase counters, one per
                                // 128-byte line: kFlowSub partial counts (workgroup index mod
                                // kFlowSub) and the count of complete partials; all grow by their

@@ -67,6 +67,10 @@ __device__ __forceinline__ void stc32(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ uint64_t ldc64(const void* p) {
     return __hip_atomic_load(gpf((uint64_t*)const_cast<void*>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void stc2(float* p, float x, float y) {
+    const uint64_t v = (uint64_t)__float_as_uint(x) | ((uint64_t)__float_as_uint(y) << 32);
+    __hip_atomic_store(gpf((uint64_t*)p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ uint32_t addc32(uint32_t* p, uint32_t v) {
     return __hip_atomic_fetch_add(gpf(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -499,54 +503,37 @@ __device__ void flow_attn(const FlowArgs& a, int l, int wg, int ph_wait, int n_p
         }
         return;
     }
-    for (int i = tid; i < G * HD; i += kBlock) {
-        float v = Os[0][i];
+    for (int i = 2 * tid; i < G * HD; i += 2 * kBlock) {
+        float v0 = Os[0][i], v1 = Os[0][i + 1];
         #pragma unroll
-        for (int w = 1; w < kWaves; ++w) v += Os[w][i];
+        for (int w = 1; w < kWaves; ++w) {
+            v0 += Os[w][i];
+            v1 += Os[w][i + 1];
+        }
         const int j = i / HD, d = i % HD;
         float* ph = a.attn_part + ((int64_t)(g * G + j) * a.max_chunks + chunk) * stride;
-        stc(ph + d, v);
-        if (d == 0) { stc(ph + HD, Ms[j]); stc(ph + HD + 1, Ls[j]); }
+        stc2(ph + d, v0, v1);
+        if (d == 0) stc2(ph + HD, Ms[j], Ls[j]);
     }
     // the last chunk of this KV head merges every chunk
     drain_vm();
     __syncthreads();
-    if (tid == 0) s_last = (addci(a.attn_cnt + g, 1) == n_act - 1);
+    if (tid == 0)
+        s_last = chunk_arrive(a.attn_cnt + (int64_t)g * attn_cnt_lines(a.max_chunks) * kCntStride, chunk, n_act);
     __syncthreads();
     if (!s_last) return;
-    constexpr int B = 16;                          // partials fetched per round trip
-    for (int idx = tid; idx < G * HD; idx += kBlock) {
-        const int j = idx / HD, d = idx % HD;
-        const float* ph = a.attn_part + (int64_t)(g * G + j) * a.max_chunks * stride;
-        float M = -FLT_MAX, L = 0.f, O = 0.f;
-        for (int base = 0; base < n_act; base += B) {
-            float mv[B], lv[B], ov[B];
-            #pragma unroll
-            for (int u = 0; u < B; ++u) {
-                const int c = min(base + u, n_act - 1);
-                mv[u] = ldc(ph + c * stride + HD);
-                lv[u] = ldc(ph + c * stride + HD + 1);
-                ov[u] = ldc(ph + c * stride + d);
-            }
-            float bm = M;
-            #pragma unroll
-            for (int u = 0; u < B; ++u)
-                if (base + u < n_act) bm = fmaxf(bm, mv[u]);
-            const float r = __expf(M - bm);
-            L *= r;
-            O *= r;
-            #pragma unroll
-            for (int u = 0; u < B; ++u)
-                if (base + u < n_act) {
-                    const float e = __expf(mv[u] - bm);
-                    L = fmaf(lv[u], e, L);
-                    O = fmaf(ov[u], e, O);
-                }
-            M = bm;
-        }
-        stc(out + idx, O / L);
-    }
-    if (tid == 0) stci(a.attn_cnt + g, 0);
+    const float* part_g = a.attn_part + (int64_t)g * G * a.max_chunks * stride;
+    merge_chunk_states<HD>(
+        G, n_act, [&](int j) { return part_g + (int64_t)j * a.max_chunks * stride; },
+        [](const float* p) {
+            const uint64_t v = ldc64(p);
+            return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+        },
+        [&](int i, float4 v) {
+            stc2(out + i, v.x, v.y);
+            stc2(out + i + 2, v.z, v.w);
+        },
+        (float (*)[6])smem);
 }
 
 // one phase of layer l for workgroup `wg` of the phase's `n_wg`

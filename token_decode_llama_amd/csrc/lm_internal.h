@@ -11,6 +11,11 @@ namespace lmk {
 constexpr int kQ4_0 = 2;
 constexpr int kQ8_0 = 8;
 constexpr int kAttnChunk = 64;     // KV positions per attention workgroup
+constexpr int kCntStride = 32;     // ints per attention chunk counter: one 128-byte line each, so
+                                   // that different counters do not serialise each other's atomics
+constexpr int kCntGroup = 16;      // chunks per first-level counter (atomics on one line serialise)
+// counter lines per (sequence, KV head): the count of complete groups, then one per group
+constexpr int attn_cnt_lines(int max_chunks) { return 1 + (max_chunks + kCntGroup - 1) / kCntGroup; }
 
 // Device layout of one quantised matrix [N rows][K cols], nb = K/32 blocks/row.
 //   Q8_0: quants row-major, each row = [first 16 bytes of every block]
@@ -86,7 +91,8 @@ struct AttnArgs {
     int nq, nkv, hd, max_ctx, max_chunks;
     float scale;           // 1/sqrt(hd)
     float* part;           // [n_seq][nq][max_chunks][hd + 2] partial o, m, l
-    int* counter;          // [n_seq][nkv] chunks finished, zero between launches
+    int* counter;          // [n_seq][nkv][attn_cnt_lines][kCntStride] chunk counts (first int of
+                           // each line, see chunk_arrive), zero between launches
     float* out;            // [n_seq][nq*hd]
 };
 

@@ -839,7 +839,7 @@ hipError_t launch_gemv_batched(const GemvArgs& a0, int epi, int n_seq, int max_b
 // over the quarters in LDS.  A context that fits one chunk writes o
 // directly; otherwise each chunk publishes its softmax state (m, l, o) with
 // device-coherent stores, and the last chunk of the (sequence, KV head) to
-// finish merges all of them (log-sum-exp) within the same launch.
+// finish merges all of them (merge_chunk_states) within the same launch.
 constexpr int kMaxGroup = 8;   // query heads per KV head
 
 __device__ __forceinline__ void st_dev(float* p, float v) {
@@ -847,6 +847,16 @@ __device__ __forceinline__ void st_dev(float* p, float v) {
 }
 __device__ __forceinline__ float ld_dev(const float* p) {
     return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// two floats at an 8-byte aligned address, device-coherent
+__device__ __forceinline__ void st_dev2(float* p, float x, float y) {
+    const uint64_t v = (uint64_t)__float_as_uint(x) | ((uint64_t)__float_as_uint(y) << 32);
+    __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 ld_dev2(const float* p) {
+    const uint64_t v = __hip_atomic_load((uint64_t*)const_cast<float*>(p), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
 }
 // this wavefront's outstanding memory operations have completed (gfx9 vmcnt(0))
 __device__ __forceinline__ void drain_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -858,6 +868,7 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
     constexpr int PCS = CH * HD / 8 / kBlock;   // 16-byte pieces per thread per tile
     // the K tile is dead once the scores are taken: the PV partial sums reuse it
     static_assert(sizeof(float) * kWaves * kMaxGroup * HD <= sizeof(__half) * CH * KP, "Os fits in Ks");
+    static_assert(sizeof(float) * 6 * kBlock <= sizeof(__half) * CH * KP, "merge scratch fits in Ks");
     __shared__ __align__(16) __half Ks[CH][KP];
     __shared__ __align__(16) __half Vs[CH][HD];
     __shared__ __align__(16) float Qs[kMaxGroup][HD];
@@ -870,7 +881,7 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int G = a.nq / a.nkv;
     const int t0 = chunk * CH;
-    const int64_t stride = HD + 2;
+    const int64_t stride = HD + 2;      // even: 8-byte aligned pairs
 
     // ---- every load first (rows clamped to the cache; masked below)
     const __half* Kg = a.kcache + (int64_t)s * a.kv_seq_stride + (int64_t)g * a.max_ctx * HD;
@@ -983,14 +994,17 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
         }
         return;
     }
-    for (int i = tid; i < G * HD; i += kBlock) {
-        float v = Os[0][i];
+    for (int i = 2 * tid; i < G * HD; i += 2 * kBlock) {
+        float v0 = Os[0][i], v1 = Os[0][i + 1];
         #pragma unroll
-        for (int w = 1; w < kWaves; ++w) v += Os[w][i];
+        for (int w = 1; w < kWaves; ++w) {
+            v0 += Os[w][i];
+            v1 += Os[w][i + 1];
+        }
         const int j = i / HD, d = i % HD;
         float* ph = part_s + ((int64_t)(g * G + j) * a.max_chunks + chunk) * stride;
-        st_dev(ph + d, v);
-        if (d == 0) { st_dev(ph + HD, Ms[j]); st_dev(ph + HD + 1, Ls[j]); }
+        st_dev2(ph + d, v0, v1);
+        if (d == 0) st_dev2(ph + HD, Ms[j], Ls[j]);
     }
 
     // ---- the last chunk of this (sequence, KV head) merges every chunk.  The
@@ -998,46 +1012,18 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
     // to complete before the count is taken.
     drain_vm();
     __syncthreads();
-    if (tid == 0) {
-        const int old = __hip_atomic_fetch_add(&a.counter[s * a.nkv + g], 1, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (old == n_act - 1);
-    }
+    if (tid == 0)
+        s_last = chunk_arrive(a.counter + (int64_t)(s * a.nkv + g) * attn_cnt_lines(a.max_chunks) * kCntStride,
+                              chunk, n_act);
     __syncthreads();
     if (!s_last) return;
-    constexpr int B = 16;                     // partials fetched per round trip
-    for (int idx = tid; idx < G * HD; idx += kBlock) {
-        const int j = idx / HD, d = idx % HD;
-        const float* ph = part_s + (int64_t)(g * G + j) * a.max_chunks * stride;
-        float M = -FLT_MAX, L = 0.f, O = 0.f;
-        for (int base = 0; base < n_act; base += B) {
-            float mv[B], lv[B], ov[B];
-            #pragma unroll
-            for (int u = 0; u < B; ++u) {
-                const int c = min(base + u, n_act - 1);
-                mv[u] = ld_dev(ph + c * stride + HD);
-                lv[u] = ld_dev(ph + c * stride + HD + 1);
-                ov[u] = ld_dev(ph + c * stride + d);
-            }
-            float bm = M;
-            #pragma unroll
-            for (int u = 0; u < B; ++u)
-                if (base + u < n_act) bm = fmaxf(bm, mv[u]);
-            const float r = __expf(M - bm);
-            L *= r;
-            O *= r;
-            #pragma unroll
-            for (int u = 0; u < B; ++u)
-                if (base + u < n_act) {
-                    const float e = __expf(mv[u] - bm);
-                    L = fmaf(lv[u], e, L);
-                    O = fmaf(ov[u], e, O);
-                }
-            M = bm;
-        }
-        out_s[idx] = O / L;
-    }
-    if (tid == 0) __hip_atomic_store(&a.counter[s * a.nkv + g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    const float* part_g = part_s + (int64_t)g * G * a.max_chunks * stride;
+    merge_chunk_states<HD>(
+        G, n_act, [&](int j) { return part_g + (int64_t)j * a.max_chunks * stride; },
+        [](const float* p) { return ld_dev2(p); },
+        [&](int i, float4 v) { *(float4*)(out_s + i) = v; },
+        reinterpret_cast<float (*)[6]>(&Ks[0][0]));
 }
 
 hipError_t launch_attention(const AttnArgs& a, int n_seq, hipStream_t st) {

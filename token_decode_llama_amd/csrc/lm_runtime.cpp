@@ -127,7 +127,7 @@ struct lm_model {
     int *d_tokens = nullptr, *d_argmax = nullptr, *d_pos = nullptr;
     float *d_cos = nullptr, *d_sin = nullptr;
     float* d_attn_part = nullptr;
-    int* d_attn_cnt = nullptr;            // [max_seqs][nkv] attention chunk counters
+    int* d_attn_cnt = nullptr;            // [max_seqs][nkv][attn_cnt_lines][kCntStride] attention chunk counters
     float* d_lm_pval = nullptr;
     int* d_lm_pidx = nullptr;
     int* d_lm_cnt = nullptr;
@@ -483,7 +483,8 @@ extern "C" lm_status lm_model_create(const lm_config* cfg, void* hip_stream, lm_
     CREATE_TRY(dev_alloc(m, (void**)&m->d_lm_pval, (int64_t)S * m->gemv_max_blocks * 4, "argmax partials"));
     CREATE_TRY(dev_alloc(m, (void**)&m->d_lm_pidx, (int64_t)S * m->gemv_max_blocks * 4, "argmax partial ids"));
     CREATE_TRY(dev_alloc(m, (void**)&m->d_lm_cnt, (int64_t)S * 4, "argmax counters"));
-    CREATE_TRY(dev_alloc(m, (void**)&m->d_attn_cnt, (int64_t)S * m->nkv * 4, "attention chunk counters"));
+    CREATE_TRY(dev_alloc(m, (void**)&m->d_attn_cnt, (int64_t)S * m->nkv * attn_cnt_lines(m->max_chunks) * kCntStride * 4,
+                         "attention chunk counters"));
     CREATE_TRY(dev_alloc(m, (void**)&m->d_sink, 4096 * 4, "sink"));
     m->dbg_floats = std::max<int64_t>({m->H, m->F, m->qrows}) * 64;
     CREATE_TRY(dev_alloc(m, (void**)&m->d_dbg, m->dbg_floats * 4, "debug rows"));
@@ -493,7 +494,8 @@ extern "C" lm_status lm_model_create(const lm_config* cfg, void* hip_stream, lm_
 
     // zero what must start at zero (counters, caches, positions)
     CREATE_HIP(hipMemsetAsync(m->d_lm_cnt, 0, (size_t)S * 4, m->stream));
-    CREATE_HIP(hipMemsetAsync(m->d_attn_cnt, 0, (size_t)(S * m->nkv * 4), m->stream));
+    CREATE_HIP(hipMemsetAsync(m->d_attn_cnt, 0, (size_t)S * m->nkv * attn_cnt_lines(m->max_chunks) * kCntStride * 4,
+                              m->stream));
     CREATE_HIP(hipMemsetAsync(m->d_pos, 0, (size_t)S * 4, m->stream));
     CREATE_HIP(hipMemsetAsync(m->d_k, 0, (size_t)(L * kv_layer_elems(m) * 2), m->stream));
     CREATE_HIP(hipMemsetAsync(m->d_v, 0, (size_t)(L * kv_layer_elems(m) * 2), m->stream));
