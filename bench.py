@@ -400,7 +400,8 @@ def run_multi(args):
 
 
 def run_70b(args):
-    """(a) resident in HBM, (b) layer streaming from pinned host memory."""
+    """(a) resident in HBM, (b) layer streaming from pinned host memory, (c) the
+    first 36 layers resident and the other 44 streamed."""
     import numpy as np
     import synth
     import token_decode_llama_amd as lm
@@ -462,7 +463,7 @@ def run_70b(args):
     overlap = (t_copy + t_comp - ms_st_timed) / min(t_copy, t_comp) if min(t_copy, t_comp) > 0 else None
     config = {"workload": WORKLOAD_TEXT[name], "name": name, "batch": 1, "ctx": cfg.ctx, "qtype": "Q4_0",
               "weights": "random N(0,0.02), quantized; (a) resident in HBM, (b) streamed per layer from "
-                         "pinned host memory"}
+                         "pinned host memory, (c) first 36 layers resident, the other 44 streamed"}
     out = base_line("decode tokens/s + achieved HBM GB/s, 70B-shape Q4_0 batch 1, weights resident in HBM",
                     1000.0 / ms_res, ms_res, args.steps, args.warmup, step_bytes, config)
     out["roofline"] = roof
@@ -479,6 +480,20 @@ def run_70b(args):
         "overlap_definition": "(sum copy + sum compute - wall) / min(sum copy, sum compute), per step, all "
                               "three from the same steps with HIP events around every copy and kernel",
         "resident_compute_ms_eager": round(compute_ms, 3)}
+    # (c) hybrid residency: the pages' 70B Q4_K_M split, 36 of 80 layers in GPU
+    # memory and 44 streamed; and what the tier sizing rule gives for a 24 GiB card
+    k_h = 36
+    log(f"hybrid: {k_h} of {cfg.n_layers} layers resident")
+    r.g.set_residency(k_h)
+    r.warm(1)
+    ms_h = r.timed(n_st)
+    copy_h = r.g.kernel_bytes("copy", 1)
+    log(f"hybrid: {ms_h:.3f} ms/step")
+    out["hybrid"] = {
+        "value": round(1000.0 / ms_h, 4), "unit": "tokens/s", "steps": n_st, "ms_per_step": round(ms_h, 2),
+        "n_resident": k_h, "n_streamed": cfg.n_layers - k_h,
+        "host_link_GBps": round(copy_h / (ms_h * 1e-3) / 1e9, 2),
+        "tier_a_for_24GiB": r.g.plan_residency(hbm_bytes=24 << 30, host_bytes=1 << 40)}
     r.close()
     if keep:
         log("oracle baseline (bounded sample)")

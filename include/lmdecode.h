@@ -130,14 +130,41 @@ lm_status lm_get_kv(lm_model* m, int32_t seq, int32_t layer, uint16_t* k, uint16
 lm_status lm_set_position(lm_model* m, int32_t seq, int32_t pos);
 lm_status lm_get_position(const lm_model* m, int32_t seq, int32_t* pos);
 
-/* Weight residency.  enable = 1: the decoder layers' weights move to a pinned
- * host arena and each step copies layer l+1 into one of two HBM layer buffers
- * on a copy stream while layer l computes from the other (events order both
- * the copy->compute and the compute->overwrite edges).  enable = 0: weights
- * move back to HBM.  Embedding, norms, LM head and KV stay in HBM either way.
- * Legal only between steps.  Outputs are bit-identical in both modes.
- * Errors: LM_E_OOM (pinned or device memory), LM_E_HIP. */
+/* Weight residency (the pages' tiered layer cache, "Llama 3.1 70B on a 24 GB
+ * GPU" write-up, sections 2.2-2.3 and 4.1-4.2: tier A in GPU memory, tier B in
+ * pinned host memory streamed through two GPU layer buffers).  Layers
+ * 0..n_resident-1 stay in HBM; layers n_resident..L-1 move to a pinned host
+ * arena, and each step copies streamed layer l+1 into one of two HBM layer
+ * buffers on a copy stream while layer l computes from the other (events order
+ * both the copy->compute and the compute->overwrite edges; the next step's
+ * first two streamed layers are copied while the LM head runs).  n_resident = L:
+ * everything resident (the state after lm_model_create); 0: every layer
+ * streamed.  Embedding, norms, LM head and KV stay in HBM always.  Legal only
+ * between steps; the weights move (device memory peaks at old + new resident
+ * arenas).  Outputs are bit-identical for every n_resident.
+ * Errors: LM_E_ARG (n_resident outside 0..L), LM_E_OOM (pinned or device
+ * memory; the model is unchanged), LM_E_HIP. */
+lm_status lm_set_residency(lm_model* m, int32_t n_resident);
+
+/* lm_set_residency(m, enable ? 0 : L): every layer streamed, or none. */
 lm_status lm_stream_mode(lm_model* m, int32_t enable);
+
+/* The pages' tier sizing (same write-up, section 4.1, compute_tier_sizes):
+ * tier_a = min(L, floor(0.9 * hbm_bytes / layer_bytes)) layers in HBM, then
+ * tier_b = min(L - tier_a, floor(0.7 * host_bytes / layer_bytes)) in pinned
+ * host memory.  Pure host arithmetic (no device needed).
+ * Returns LM_OK when tier_a + tier_b == n_layers, LM_E_OOM when layers are
+ * left over (the pages' disk tier, which this library does not have),
+ * LM_E_ARG on a NULL output or a non-positive size. */
+lm_status lm_tier_sizes(int32_t n_layers, int64_t layer_bytes, int64_t hbm_bytes, int64_t host_bytes,
+                        int32_t* tier_a, int32_t* tier_b);
+
+/* lm_tier_sizes for this model's layer blobs: hbm_bytes <= 0 means the
+ * device's free memory now plus what the resident layers hold; host_bytes <= 0
+ * the host's available memory plus what the host arena holds.  *n_resident =
+ * tier A, ready for lm_set_residency.  Errors: LM_E_OOM (the rest does not fit
+ * in host memory; *n_resident is still set), LM_E_HIP. */
+lm_status lm_plan_residency(lm_model* m, int64_t hbm_bytes, int64_t host_bytes, int32_t* n_resident);
 
 /* One decode step for sequences 0..n_seq-1 (1 <= n_seq <= max_seqs):
  * tokens host int32 [n_seq]; logits host fp32 [n_seq][vocab] or NULL;

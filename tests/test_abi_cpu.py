@@ -67,3 +67,29 @@ def test_null_arguments():
     assert L.lm_model_create(None, None, ctypes.byref(h)) == lm.LM_E_ARG
     L.lm_model_destroy(None)   # no-op
     assert L.lm_last_error(None) is not None
+
+
+# The tier sizing rule of the 70B write-up (section 4.1, compute_tier_sizes):
+# tier A = floor(0.9 * free GPU memory / layer bytes), tier B = floor(0.7 *
+# available host memory / layer bytes), clamped to the layers left.  Expected
+# values worked by hand.
+@pytest.mark.parametrize("args,expect", [
+    ((80, 10**9, 40 * 10**9, 100 * 10**9), (36, 44, True)),     # 36 of 80 in HBM, the rest fits in host memory
+    ((80, 10**9, 40 * 10**9, 50 * 10**9), (36, 35, False)),     # 9 layers would need the disk tier
+    ((80, 10**9, 10**12, 0), (80, 0, True)),                    # everything resident
+    ((80, 10**9, 0, 200 * 10**9), (0, 80, True)),               # everything streamed
+    ((32, 3, 10, 100), (3, 23, False)),                         # 0.9 * 10 / 3 = 3 exactly; 0.7 * 100 / 3 = 23.3
+    ((32, 7, 69, 10), (8, 1, False)),                           # 62.1 / 7 = 8.87; 7 / 7 = 1
+    ((4, 2**40, 2**62, 2**62), (4, 0, True)),                   # no overflow at large sizes
+])
+def test_tier_sizes(args, expect):
+    assert lm.tier_sizes(*args) == expect
+
+
+def test_tier_sizes_rejects_bad_arguments():
+    L = lm.load()
+    a, b = ctypes.c_int32(), ctypes.c_int32()
+    assert L.lm_tier_sizes(80, 0, 10, 10, ctypes.byref(a), ctypes.byref(b)) == lm.LM_E_ARG
+    assert L.lm_tier_sizes(0, 10, 10, 10, ctypes.byref(a), ctypes.byref(b)) == lm.LM_E_ARG
+    assert L.lm_tier_sizes(80, 10, -1, 10, ctypes.byref(a), ctypes.byref(b)) == lm.LM_E_ARG
+    assert L.lm_tier_sizes(80, 10, 10, 10, None, ctypes.byref(b)) == lm.LM_E_ARG

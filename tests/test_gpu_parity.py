@@ -36,6 +36,8 @@ CASES = {
     # 8B layer shapes in Q8_0; positions 127, 128, 129: the new key ends a
     # 64-position attention chunk, then is alone in a fresh chunk, then second
     "llama8b_q8_2layers_ctx127": synth.variant("llama8b_q8", n_layers=2, ctx=127, steps=3, batch=1),
+    # five layers: resident prefixes of every length, both streaming buffers in turn
+    "tiny_5layers": synth.variant("tiny", n_layers=5, steps=3),
 }
 
 # shapes the one-launch step supports (head_dim 128, hidden and FFN >= 2048)
@@ -327,6 +329,46 @@ def test_stream_mode_bit_identical(name):
         for other in (streamed, streamed2, back):
             for (a, b), (c, d) in zip(resident, other):
                 assert np.array_equal(a, c) and np.array_equal(b, d)
+    finally:
+        g.close()
+
+
+@pytest.mark.parametrize("name,plan", [("tiny_5layers", [3, 1, 0, 4, 2, 5]),
+                                       ("llama70b_q4_2layers", [1, 0, 1, 2])])
+def test_hybrid_residency_bit_identical(name, plan):
+    """The first k layers resident and the rest streamed: every k gives the
+    fully resident outputs bit for bit, through any sequence of moves."""
+    model = get_model(name)
+    cfg = model.cfg
+    g = open_gpu(model, max_seqs=1)
+    try:
+        toks = synth.start_tokens(cfg, 1)
+
+        def run():
+            g.set_position(0, cfg.ctx)
+            res = []
+            t = toks
+            for _ in range(cfg.steps):
+                lg, am = g.step(t)
+                res.append((lg.copy(), am.copy()))
+                t = am
+            return res
+
+        g.set_persistent(False)
+        g.set_dataflow(False)
+        resident = run()
+        for k in plan:
+            log(f"{name}: {k} of {cfg.n_layers} layers resident")
+            g.set_residency(k)
+            for _ in range(2):       # twice: the second starts from the previous step's prefetch
+                for (a, b), (c, d) in zip(resident, run()):
+                    assert np.array_equal(a, c) and np.array_equal(b, d), k
+        import token_decode_llama_amd as lm
+        with pytest.raises(lm.LMError):
+            g.set_residency(cfg.n_layers + 1)
+        assert g.plan_residency(hbm_bytes=1, host_bytes=1 << 40) == 0
+        assert g.plan_residency(hbm_bytes=1 << 50, host_bytes=1) == cfg.n_layers
+        assert g.plan_residency() == cfg.n_layers      # a small model fits the device
     finally:
         g.close()
 

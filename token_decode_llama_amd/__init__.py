@@ -23,6 +23,7 @@ KERNEL_KINDS = ("embed", "qkv", "attn", "wo", "gateup", "down", "lmhead", "copy"
 EXPORTS = (
     "lm_model_create", "lm_model_destroy", "lm_load_layer_weights", "lm_load_global_weights",
     "lm_load_kv", "lm_get_kv", "lm_set_position", "lm_get_position", "lm_stream_mode",
+    "lm_set_residency", "lm_tier_sizes", "lm_plan_residency",
     "lm_decode_step", "lm_decode_step_dev", "lm_set_graph", "lm_set_persistent", "lm_set_dataflow",
     "lm_check_error", "lm_stream", "lm_last_error",
     "lm_kernel_timing", "lm_kernel_stats", "lm_time_kind", "lm_kernel_bytes", "lm_debug_dequant",
@@ -74,6 +75,9 @@ def load():
         "lm_set_position": ([vp, i32, i32], st),
         "lm_get_position": ([vp, i32, ctypes.POINTER(i32)], st),
         "lm_stream_mode": ([vp, i32], st),
+        "lm_set_residency": ([vp, i32], st),
+        "lm_tier_sizes": ([i32, i64, i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)], st),
+        "lm_plan_residency": ([vp, i64, i64, ctypes.POINTER(i32)], st),
         "lm_decode_step": ([vp, vp, i32, vp, vp], st),
         "lm_decode_step_dev": ([vp, vp, i32, vp, vp], st),
         "lm_set_graph": ([vp, i32], st),
@@ -101,6 +105,15 @@ def load():
 
 def _p(a: np.ndarray) -> int:
     return a.ctypes.data
+
+
+def tier_sizes(n_layers: int, layer_bytes: int, hbm_bytes: int, host_bytes: int):
+    """(tier_a, tier_b, all_fit) by the tier sizing rule (host arithmetic in the library)."""
+    a, b = ctypes.c_int32(), ctypes.c_int32()
+    st = load().lm_tier_sizes(n_layers, layer_bytes, hbm_bytes, host_bytes, ctypes.byref(a), ctypes.byref(b))
+    if st not in (LM_OK, LM_E_OOM):
+        raise LMError(f"lm_tier_sizes: status {st}")
+    return a.value, b.value, st == LM_OK
 
 
 def make_config(cfg, max_seqs: int | None = None, max_ctx: int | None = None) -> Config:
@@ -212,6 +225,16 @@ class Model:
 
     def stream_mode(self, enable: bool):
         self._check(self._lib.lm_stream_mode(self._h, 1 if enable else 0))
+
+    def set_residency(self, n_resident: int):
+        """Layers 0..n_resident-1 in HBM, the rest streamed from pinned host memory."""
+        self._check(self._lib.lm_set_residency(self._h, n_resident))
+
+    def plan_residency(self, hbm_bytes: int = 0, host_bytes: int = 0) -> int:
+        """Tier-A layer count by the tier sizing rule (0: query the device / host)."""
+        n = ctypes.c_int32()
+        self._check(self._lib.lm_plan_residency(self._h, hbm_bytes, host_bytes, ctypes.byref(n)))
+        return n.value
 
     def set_graph(self, enable: bool):
         self._check(self._lib.lm_set_graph(self._h, 1 if enable else 0))

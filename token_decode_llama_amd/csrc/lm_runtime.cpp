@@ -26,6 +26,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <unistd.h>
 #include <cstring>
 #include <string>
 #include <thread>
@@ -108,9 +109,12 @@ struct lm_model {
     int lm_grid = 0;
 
     // device memory
-    uint8_t* d_layers = nullptr;          // resident blobs [L][blob]
+    // weight residency: layers 0..n_res-1 live in HBM, layers n_res..L-1 in a
+    // pinned host arena, each copied into one of two HBM buffers when used
+    int n_res = 0;
+    uint8_t* d_layers = nullptr;          // resident blobs [n_res][blob]
     uint8_t* d_sbuf[2] = {nullptr, nullptr};
-    uint8_t* h_arena = nullptr;           // pinned blobs (stream mode)
+    uint8_t* h_arena = nullptr;           // pinned blobs [L - n_res][blob]
     uint8_t* h_stage = nullptr;           // pinned staging for uploads
     int64_t stage_bytes = 0;
     float* d_norms = nullptr;             // [L][2][H]
@@ -159,13 +163,13 @@ struct lm_model {
     std::vector<uint8_t> layer_loaded;
     bool global_loaded = false;
     std::vector<int> pos;
-    bool streaming = false;
+    bool streaming = false;               // n_res < L
     bool use_graph = true;
 
     // streaming pipeline state
     hipEvent_t ev_copied[2] = {nullptr, nullptr};
     hipEvent_t ev_consumed[2] = {nullptr, nullptr};
-    bool prefetched[2] = {false, false};   // slot holds layer 0/1 for the next step
+    bool prefetched[2] = {false, false};   // the next step's first / second streamed layer is copied
 
     struct Pending { int kind; hipEvent_t a, b; };
     struct GraphEntry {
@@ -455,6 +459,7 @@ extern "C" lm_status lm_model_create(const lm_config* cfg, void* hip_stream, lm_
     const int S = c.max_seqs;
     const int64_t L = c.n_layers;
     CREATE_TRY(dev_alloc(m, (void**)&m->d_layers, L * m->blob_bytes, "layer weights"));
+    m->n_res = (int)L;
     CREATE_TRY(dev_alloc(m, (void**)&m->d_norms, L * 2 * m->H * 4, "norm gains"));
     CREATE_TRY(dev_alloc(m, (void**)&m->d_embd, m->V * m->H * 2, "token embedding"));
     CREATE_TRY(dev_alloc(m, (void**)&m->d_out_norm, m->H * 4, "output norm"));
@@ -800,6 +805,12 @@ static lm_status upload_tiles(lm_model* m, const TileGeom& g, RowFn src_row, uin
     return LM_OK;
 }
 
+// residency: layers n_res..L-1 are streamed through the two HBM buffers,
+// alternating between them in order
+static bool layer_streamed(const lm_model* m, int l) { return l >= m->n_res; }
+static int stream_slot(const lm_model* m, int l) { return (l - m->n_res) & 1; }
+static uint8_t* host_blob(lm_model* m, int l) { return m->h_arena + (int64_t)(l - m->n_res) * m->blob_bytes; }
+
 static void invalidate_graphs(lm_model* m) {
     for (auto& g : m->graphs) {
         (void)hipGraphExecDestroy(g.exec);
@@ -824,9 +835,8 @@ extern "C" lm_status lm_load_layer_weights(lm_model* m, int32_t layer, const lm_
     const uint8_t *wo = (const uint8_t*)w->wo, *wg = (const uint8_t*)w->w_gate, *wu = (const uint8_t*)w->w_up;
     const uint8_t* wd = (const uint8_t*)w->w_down;
     const int64_t qr = m->qrows, kr = m->kvrows;
-    uint8_t* blob = m->streaming ? m->h_arena + (int64_t)layer * m->blob_bytes
-                                 : m->d_layers + (int64_t)layer * m->blob_bytes;
-    const bool host = m->streaming;
+    const bool host = layer_streamed(m, layer);
+    uint8_t* blob = host ? host_blob(m, layer) : m->d_layers + (int64_t)layer * m->blob_bytes;
     auto dq = [&](int i) { return blob + m->mo[i].q; };
     auto ds = [&](int i) { return (uint16_t*)(blob + m->mo[i].sc); };
     auto src_qkv = [&](int64_t r) {
@@ -1109,16 +1119,16 @@ static lm_status collect_timing(lm_model* m) {
 }
 
 static const uint8_t* layer_blob(lm_model* m, int l) {
-    return m->streaming ? m->d_sbuf[l & 1] : m->d_layers + (int64_t)l * m->blob_bytes;
+    return layer_streamed(m, l) ? m->d_sbuf[stream_slot(m, l)] : m->d_layers + (int64_t)l * m->blob_bytes;
 }
 
 static lm_status stream_copy(lm_model* m, int layer) {
-    const int slot = layer & 1;
+    const int slot = stream_slot(m, layer);
     HIPTRY(m, hipStreamWaitEvent(m->copy_stream, m->ev_consumed[slot], 0));
     hipEvent_t a = m->timing ? pool_event(m) : nullptr;
     if (a) HIPTRY(m, hipEventRecord(a, m->copy_stream));
-    HIPTRY(m, hipMemcpyAsync(m->d_sbuf[slot], m->h_arena + (int64_t)layer * m->blob_bytes,
-                             (size_t)m->blob_bytes, hipMemcpyHostToDevice, m->copy_stream));
+    HIPTRY(m, hipMemcpyAsync(m->d_sbuf[slot], host_blob(m, layer), (size_t)m->blob_bytes, hipMemcpyHostToDevice,
+                             m->copy_stream));
     if (a) {
         hipEvent_t b = pool_event(m);
         if (b) {
@@ -1169,7 +1179,11 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
     const bool flow = use_flow(m, n_seq);
     if (flow) {
         KTimer t(m, LM_K_FLOW);
-        if (want(m, LM_K_FLOW)) HIPTRY(m, launch_flow(m->flow_h, c.qtype, st));
+        if (want(m, LM_K_FLOW)) {
+            FlowArgs fa = m->flow_h;
+            fa.blobs = m->d_layers;       // the resident arena as it is now
+            HIPTRY(m, launch_flow(fa, c.qtype, st));
+        }
     }
     GemvArgs base{};
     base.qtype = c.qtype;
@@ -1197,17 +1211,16 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
     at.counter = m->d_attn_cnt;
     at.out = m->d_o;
 
-    if (m->streaming) {
-        for (int l = 0; l < std::min(L, 2); ++l)
-            if (!m->prefetched[l]) {
-                lm_status s = stream_copy(m, l);
-                if (s != LM_OK) return s;
-            }
-        m->prefetched[0] = m->prefetched[1] = false;
-    }
+    const int n_str = L - m->n_res;     // streamed layers: n_res..L-1
+    for (int i = 0; i < std::min(n_str, 2); ++i)
+        if (!m->prefetched[i]) {
+            lm_status s = stream_copy(m, m->n_res + i);
+            if (s != LM_OK) return s;
+        }
+    m->prefetched[0] = m->prefetched[1] = false;
 
     for (int l = 0; l < (flow ? 0 : L); ++l) {
-        if (m->streaming) HIPTRY(m, hipStreamWaitEvent(st, m->ev_copied[l & 1], 0));
+        if (layer_streamed(m, l)) HIPTRY(m, hipStreamWaitEvent(st, m->ev_copied[stream_slot(m, l)], 0));
         const uint8_t* blob = layer_blob(m, l);
         const float* g_attn = m->d_norms + (int64_t)l * 2 * m->H;
         const float* g_ffn = g_attn + m->H;
@@ -1254,21 +1267,20 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
             a.out = m->d_x; a.out_stride = (int)m->H;
             if (want(m, LM_K_DOWN)) HIPTRY(m, gemv(m, a, EPI_RESID, n_seq, st));
         }
-        if (m->streaming) {
-            HIPTRY(m, hipEventRecord(m->ev_consumed[l & 1], st));
+        if (layer_streamed(m, l)) {
+            HIPTRY(m, hipEventRecord(m->ev_consumed[stream_slot(m, l)], st));
             if (l + 2 < L) {
                 lm_status s = stream_copy(m, l + 2);
                 if (s != LM_OK) return s;
             }
         }
     }
-    if (m->streaming) {
-        // start the next step's first two layers while the LM head runs
-        for (int l = 0; l < std::min(L, 2); ++l) {
-            lm_status s = stream_copy(m, l);
-            if (s != LM_OK) return s;
-            m->prefetched[l] = true;
-        }
+    // start the next step's first two streamed layers while the LM head (and
+    // the next step's resident layers) run
+    for (int i = 0; i < std::min(n_str, 2); ++i) {
+        lm_status s = stream_copy(m, m->n_res + i);
+        if (s != LM_OK) return s;
+        m->prefetched[i] = true;
     }
     {   // final RMSNorm -> LM head GEMV -> argmax (and positions += 1)
         KTimer t(m, LM_K_LMHEAD);
@@ -1478,6 +1490,7 @@ extern "C" lm_status lm_debug_flow_trace(lm_model* m, const int32_t* d_tokens, u
     HIPTRY(m, hipStreamSynchronize(m->stream));
     HIPTRY(m, hipMalloc(&d, (size_t)words * 8));
     FlowArgs a = m->flow_h;
+    a.blobs = m->d_layers;
     a.trace = d;
     hipError_t e = hipMemsetAsync(d, 0, (size_t)words * 8, m->stream);
     if (e == hipSuccess) e = launch_embed(m->d_embd, d_tokens, (int)m->V, (int)m->H, m->d_x, 1, m->stream);
@@ -1534,58 +1547,110 @@ extern "C" lm_status lm_set_graph(lm_model* m, int32_t enable) {
 // ---------------------------------------------------------------------------
 // streaming mode
 // ---------------------------------------------------------------------------
-extern "C" lm_status lm_stream_mode(lm_model* m, int32_t enable) {
+// The pages' tier sizing: tier A (HBM) takes floor(0.9 * free HBM / layer
+// bytes) layers, tier B (pinned host memory) floor(0.7 * available host
+// memory / layer bytes); what fits in neither would go to a disk tier, which
+// this library does not have.
+extern "C" lm_status lm_tier_sizes(int32_t n_layers, int64_t layer_bytes, int64_t hbm_bytes, int64_t host_bytes,
+                                   int32_t* tier_a, int32_t* tier_b) {
+    if (n_layers < 1 || layer_bytes < 1 || hbm_bytes < 0 || host_bytes < 0 || !tier_a || !tier_b) return LM_E_ARG;
+    // exact floors of 0.9 * hbm / layer and 0.7 * host / layer
+    const __int128 den = (__int128)10 * layer_bytes;
+    const int64_t a = (int64_t)std::min<__int128>(n_layers, (__int128)9 * hbm_bytes / den);
+    const int64_t b = (int64_t)std::min<__int128>(n_layers - a, (__int128)7 * host_bytes / den);
+    *tier_a = (int32_t)a;
+    *tier_b = (int32_t)b;
+    return a + b == n_layers ? LM_OK : LM_E_OOM;
+}
+
+extern "C" lm_status lm_plan_residency(lm_model* m, int64_t hbm_bytes, int64_t host_bytes, int32_t* n_resident) {
+    if (!m || !n_resident) return LM_E_ARG;
+    if (hbm_bytes <= 0) {
+        size_t fr = 0, tot = 0;
+        HIPTRY(m, hipMemGetInfo(&fr, &tot));
+        // the resident layers' own bytes would be free too
+        hbm_bytes = (int64_t)fr + (int64_t)m->n_res * m->blob_bytes;
+    }
+    if (host_bytes <= 0) {
+        const long pages = sysconf(_SC_AVPHYS_PAGES), psz = sysconf(_SC_PAGESIZE);
+        host_bytes = (pages > 0 && psz > 0 ? (int64_t)pages * psz : 0) +
+                    (int64_t)(m->cfg.n_layers - m->n_res) * m->blob_bytes;
+    }
+    int32_t a = 0, b = 0;
+    const lm_status st = lm_tier_sizes(m->cfg.n_layers, m->blob_bytes, hbm_bytes, host_bytes, &a, &b);
+    *n_resident = a;
+    if (st != LM_OK)
+        return fail(m, st, "lm_plan_residency: %d resident + %d host layers of %d fit (HBM %lld B, host %lld B)",
+                    a, b, m->cfg.n_layers, (long long)hbm_bytes, (long long)host_bytes);
+    return LM_OK;
+}
+
+extern "C" lm_status lm_set_residency(lm_model* m, int32_t n_resident) {
     if (!m) return LM_E_ARG;
-    const bool want = enable != 0;
-    if (want == m->streaming) return LM_OK;
+    const int L = m->cfg.n_layers;
+    if (n_resident < 0 || n_resident > L)
+        return fail(m, LM_E_ARG, "lm_set_residency: n_resident = %d; expected 0..%d", n_resident, L);
+    if (n_resident == m->n_res) return LM_OK;
     HIPTRY(m, hipStreamSynchronize(m->stream));
     HIPTRY(m, hipStreamSynchronize(m->copy_stream));
-    const int64_t L = m->cfg.n_layers;
-    if (want) {
-        uint8_t* arena = nullptr;
-        uint8_t* b0 = nullptr;
-        uint8_t* b1 = nullptr;
-        lm_status st = host_alloc(m, (void**)&arena, L * m->blob_bytes, "streaming host arena");
-        if (st != LM_OK) return st;
-        st = dev_alloc(m, (void**)&b0, m->blob_bytes, "streaming buffer 0");
-        if (st == LM_OK) st = dev_alloc(m, (void**)&b1, m->blob_bytes, "streaming buffer 1");
-        if (st == LM_OK) {
-            hipError_t e = hipMemcpy(arena, m->d_layers, (size_t)(L * m->blob_bytes), hipMemcpyDeviceToHost);
-            if (e != hipSuccess) st = fail(m, LM_E_HIP, "hipMemcpy (weights to host arena) failed: %s",
-                                           hipGetErrorString(e));
+    const int64_t B = m->blob_bytes;
+    const int old = m->n_res, nw = n_resident;
+    uint8_t *d = nullptr, *h = nullptr, *b0 = m->d_sbuf[0], *b1 = m->d_sbuf[1];
+    const bool new_bufs = nw < L && !b0;
+    lm_status st = LM_OK;
+    if (nw > 0) st = dev_alloc(m, (void**)&d, nw * B, "layer weights");
+    if (st == LM_OK && nw < L) st = host_alloc(m, (void**)&h, (L - nw) * B, "streaming host arena");
+    if (st == LM_OK && new_bufs) {
+        b0 = b1 = nullptr;
+        st = dev_alloc(m, (void**)&b0, B, "streaming buffer 0");
+        if (st == LM_OK) st = dev_alloc(m, (void**)&b1, B, "streaming buffer 1");
+    }
+    // every layer from its present home to its new one
+    for (int l = 0; l < L && st == LM_OK; ++l) {
+        const bool from_dev = l < old, to_dev = l < nw;
+        const uint8_t* src = from_dev ? m->d_layers + (int64_t)l * B : m->h_arena + (int64_t)(l - old) * B;
+        uint8_t* dst = to_dev ? d + (int64_t)l * B : h + (int64_t)(l - nw) * B;
+        if (!from_dev && !to_dev) {
+            std::memcpy(dst, src, (size_t)B);
+            continue;
         }
-        if (st != LM_OK) {
-            host_free(m, arena);
+        const hipMemcpyKind kind = from_dev ? (to_dev ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToHost)
+                                            : hipMemcpyHostToDevice;
+        const hipError_t e = hipMemcpy(dst, src, (size_t)B, kind);
+        if (e != hipSuccess)
+            st = fail(m, LM_E_HIP, "lm_set_residency: moving layer %d failed: %s", l, hipGetErrorString(e));
+    }
+    if (st != LM_OK) {
+        dev_free(m, d);
+        host_free(m, h);
+        if (new_bufs) {
             dev_free(m, b0);
             dev_free(m, b1);
-            return st;
         }
-        dev_free(m, m->d_layers);
-        m->d_layers = nullptr;
-        m->h_arena = arena;
-        m->d_sbuf[0] = b0;
-        m->d_sbuf[1] = b1;
-        m->streaming = true;
-    } else {
-        uint8_t* d = nullptr;
-        lm_status st = dev_alloc(m, (void**)&d, L * m->blob_bytes, "layer weights");
-        if (st != LM_OK) return st;
-        hipError_t e = hipMemcpy(d, m->h_arena, (size_t)(L * m->blob_bytes), hipMemcpyHostToDevice);
-        if (e != hipSuccess) {
-            dev_free(m, d);
-            return fail(m, LM_E_HIP, "hipMemcpy (weights to HBM) failed: %s", hipGetErrorString(e));
-        }
-        host_free(m, m->h_arena);
-        dev_free(m, m->d_sbuf[0]);
-        dev_free(m, m->d_sbuf[1]);
-        m->h_arena = nullptr;
-        m->d_sbuf[0] = m->d_sbuf[1] = nullptr;
-        m->d_layers = d;
-        m->streaming = false;
+        return st;
     }
+    dev_free(m, m->d_layers);
+    host_free(m, m->h_arena);
+    if (nw == L) {
+        dev_free(m, b0);
+        dev_free(m, b1);
+        b0 = b1 = nullptr;
+    }
+    m->d_layers = d;
+    m->h_arena = h;
+    m->d_sbuf[0] = b0;
+    m->d_sbuf[1] = b1;
+    m->n_res = nw;
+    m->streaming = nw < L;
+    m->flow_h.blobs = d;
     m->prefetched[0] = m->prefetched[1] = false;
     invalidate_graphs(m);
     return LM_OK;
+}
+
+extern "C" lm_status lm_stream_mode(lm_model* m, int32_t enable) {
+    if (!m) return LM_E_ARG;
+    return lm_set_residency(m, enable ? 0 : m->cfg.n_layers);
 }
 
 // ---------------------------------------------------------------------------
@@ -1690,7 +1755,7 @@ extern "C" lm_status lm_kernel_bytes(const lm_model* m, int32_t kind, int32_t n_
         case LM_K_GATEUP: b = L * (2 * F * H * bpw + H * 4 + S * (H * 4 + F * 4)); break;
         case LM_K_DOWN: b = L * (H * F * bpw + S * (F * 4 + H * 8)); break;
         case LM_K_LMHEAD: b = V * H * bpw + H * 4 + S * H * 4; break;
-        case LM_K_COPY: b = m->streaming ? L * (double)m->blob_bytes : 0.0; break;
+        case LM_K_COPY: b = (double)(L - m->n_res) * (double)m->blob_bytes; break;
         case LM_K_FLOW:
             for (int k = LM_K_QKV; k <= LM_K_DOWN; ++k) {
                 double kb = 0.0;
@@ -1736,9 +1801,8 @@ extern "C" lm_status lm_debug_dequant(lm_model* m, int32_t layer, int32_t which,
     HIPTRY(m, hipStreamSynchronize(m->copy_stream));
     QMat w;
     if (mat < 0) w = lm_head_mat(m);
-    else if (m->streaming) {
-        HIPTRY(m, hipMemcpy(m->d_sbuf[0], m->h_arena + (int64_t)layer * m->blob_bytes, (size_t)m->blob_bytes,
-                            hipMemcpyHostToDevice));
+    else if (layer_streamed(m, layer)) {
+        HIPTRY(m, hipMemcpy(m->d_sbuf[0], host_blob(m, layer), (size_t)m->blob_bytes, hipMemcpyHostToDevice));
         m->prefetched[0] = m->prefetched[1] = false;
         w = mat_at(m, m->d_sbuf[0], mat);
     } else {
@@ -1765,8 +1829,8 @@ extern "C" lm_status lm_debug_dequant(lm_model* m, int32_t layer, int32_t which,
 
 extern "C" lm_status lm_debug_read_bw(lm_model* m, int64_t n_bytes, int32_t iters, double* ms) {
     if (!m || !ms || iters < 1) return LM_E_ARG;
-    const uint8_t* buf = m->streaming ? nullptr : m->d_layers;
-    const int64_t avail = m->streaming ? 0 : (int64_t)m->cfg.n_layers * m->blob_bytes;
+    const uint8_t* buf = m->d_layers;
+    const int64_t avail = (int64_t)m->n_res * m->blob_bytes;
     if (!buf || n_bytes < 16 || n_bytes > avail || n_bytes % 16)
         return fail(m, LM_E_ARG, "lm_debug_read_bw: n_bytes = %lld; expected a multiple of 16 in 16..%lld "
                     "(resident weight arena)", (long long)n_bytes, (long long)avail);
