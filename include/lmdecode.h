@@ -130,9 +130,9 @@ lm_status lm_get_kv(lm_model* m, int32_t seq, int32_t layer, uint16_t* k, uint16
 lm_status lm_set_position(lm_model* m, int32_t seq, int32_t pos);
 lm_status lm_get_position(const lm_model* m, int32_t seq, int32_t* pos);
 
-/* Weight residency (the pages' tiered layer cache, "Llama 3.1 70B on a 24 GB
- * GPU" write-up, sections 2.2-2.3 and 4.1-4.2: tier A in GPU memory, tier B in
- * pinned host memory streamed through two GPU layer buffers).  Layers
+/* Weight residency (the C/CUDA Llama engine page's tiered layer cache, its
+ * sections 2.2-2.3, 3.2-3.3 and 4.1-4.2: tier A in GPU memory, tier B in pinned
+ * host memory streamed through two GPU layer buffers).  Layers
  * 0..n_resident-1 stay in HBM; layers n_resident..L-1 move to a pinned host
  * arena, and each step copies streamed layer l+1 into one of two HBM layer
  * buffers on a copy stream while layer l computes from the other (events order
@@ -149,7 +149,7 @@ lm_status lm_set_residency(lm_model* m, int32_t n_resident);
 /* lm_set_residency(m, enable ? 0 : L): every layer streamed, or none. */
 lm_status lm_stream_mode(lm_model* m, int32_t enable);
 
-/* The pages' tier sizing (same write-up, section 4.1, compute_tier_sizes):
+/* The engine page's tier sizing (its section 4.1, compute_tier_sizes):
  * tier_a = min(L, floor(0.9 * hbm_bytes / layer_bytes)) layers in HBM, then
  * tier_b = min(L - tier_a, floor(0.7 * host_bytes / layer_bytes)) in pinned
  * host memory.  Pure host arithmetic (no device needed).

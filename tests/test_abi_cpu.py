@@ -69,7 +69,7 @@ def test_null_arguments():
     assert L.lm_last_error(None) is not None
 
 
-# The tier sizing rule of the 70B write-up (section 4.1, compute_tier_sizes):
+# The tier sizing rule of the C/CUDA Llama engine page (section 4.1, compute_tier_sizes):
 # tier A = floor(0.9 * free GPU memory / layer bytes), tier B = floor(0.7 *
 # available host memory / layer bytes), clamped to the layers left.  Expected
 # values worked by hand.

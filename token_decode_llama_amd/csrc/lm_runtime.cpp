@@ -1547,10 +1547,10 @@ extern "C" lm_status lm_set_graph(lm_model* m, int32_t enable) {
 // ---------------------------------------------------------------------------
 // streaming mode
 // ---------------------------------------------------------------------------
-// The pages' tier sizing: tier A (HBM) takes floor(0.9 * free HBM / layer
-// bytes) layers, tier B (pinned host memory) floor(0.7 * available host
-// memory / layer bytes); what fits in neither would go to a disk tier, which
-// this library does not have.
+// The C/CUDA Llama engine page's tier sizing (its section 4.1): tier A (HBM)
+// takes floor(0.9 * free HBM / layer bytes) layers, tier B (pinned host
+// memory) floor(0.7 * available host memory / layer bytes); what fits in
+// neither would go to a disk tier, which this library does not have.
 extern "C" lm_status lm_tier_sizes(int32_t n_layers, int64_t layer_bytes, int64_t hbm_bytes, int64_t host_bytes,
                                    int32_t* tier_a, int32_t* tier_b) {
     if (n_layers < 1 || layer_bytes < 1 || hbm_bytes < 0 || host_bytes < 0 || !tier_a || !tier_b) return LM_E_ARG;
