@@ -79,7 +79,7 @@ struct GemvArgs {
     int* pos_inc;          // [n_seq] positions advanced by one after the argmax
     // several sequences at once (MFMA path)
     int n_seq;
-    uint4* xfrag;          // activation digit fragments, scales and digit sums (lm_kernels.hip)
+    uint8_t* xfrag;        // activation digits, scales and digit sums (xfrag_bytes; lm_kernels.hip)
 };
 
 struct AttnArgs {
@@ -102,7 +102,11 @@ hipError_t launch_embed(const uint16_t* tok_embd, const int* tokens, int vocab, 
 hipError_t launch_gemv(const GemvArgs& a, int epi, int n_seq, int max_blocks, hipStream_t st);
 // 2..4 sequences: activation fragments (RMSNorm applied), then the MFMA GEMV
 hipError_t launch_gemv_batched(const GemvArgs& a, int epi, int n_seq, int max_blocks, hipStream_t st);
-inline int64_t xfrag_bytes(int64_t K) { return K / 32 * 1024; }   // per block: 4 x 16 x 16 bytes
+// Activation operands of the several-sequence GEMV (nb = K/32 blocks): digit
+// pairs [ceil(nb/2)][4][16] x 16 bytes, then the table [nb][16] x 8 bytes
+// (activation scale, digit sum).
+constexpr int64_t xdig_table_offset(int64_t nb) { return (nb + 1) / 2 * 1024; }
+inline int64_t xfrag_bytes(int64_t K) { return xdig_table_offset(K / 32) + K / 32 * 128; }
 hipError_t launch_attention(const AttnArgs& a, int n_seq, hipStream_t st);
 hipError_t launch_dequant(const QMat& w, int qtype, int row0, int n_rows, float* out,
                           hipStream_t st);

@@ -477,21 +477,28 @@ hipError_t launch_gemv(const GemvArgs& a, int epi, int n_seq, int max_blocks, hi
 // sequence are combined (2^16 D2 + 2^8 D1 + D0) across lanes.
 typedef int v4i_t __attribute__((ext_vector_type(4)));
 
-// Activation fragments of the several-sequence GEMV (at a.xfrag):
-//   [nb][4 groups g][16 columns j] x 16 bytes: digit d of sequence s (j = 3s+d)
-//   for the block's columns 8g..8g+7 (8 bytes), the block's activation scale
-//   max|x_b| / (127 x 2^16) of sequence s (fp32), and the digit sum of column j
-//   over the block's 32 columns (int32); columns j >= 3 x n_seq are unused.
-// One workgroup per sequence: RMSNorm (optional), then the digits of every
-// activation.  Four consecutive threads hold one 32-column block.
+// Activation operands of the several-sequence GEMV (at a.xfrag; nb = K/32
+// blocks, np = ceil(nb/2) block pairs; layout also in lm_internal.h):
+//   digits [np][4 groups g][16 columns j] x 16 bytes: for the pair's two
+//     blocks, digit d of sequence s (column j = 3s+d) at the block's columns
+//     8g..8g+7, 8 bytes per block (the matrix-core B operand);
+//   table [nb][16 columns j] x 8 bytes (at byte np x 1024): the block's
+//     activation scale max|x_b| / (127 x 2^16) of sequence s (fp32 bits) and
+//     column j's digit sum over the block's 32 columns (int32).
+// Columns j >= 3 x n_seq are never read.
+// Grid (ceil(K / 2048), n_seq): a thread per 8 columns, four consecutive
+// threads per block.  With a gain, every workgroup first takes the whole
+// row's RMS (the row is at most 64 KB, read from L2), so no workgroup waits
+// for another.
 __global__ __launch_bounds__(kBlock) void k_xdigits(const float* __restrict__ xin, int x_stride,
                                                    const float* __restrict__ g, float eps, int K,
                                                    uint8_t* __restrict__ xb) {
     __shared__ float red[kWaves];
-    const int s = blockIdx.x, tid = threadIdx.x;
+    const int s = blockIdx.y, tid = threadIdx.x;
     const int nb = K >> 5;
     const float* x = xin + (int64_t)s * x_stride;
-    uint4* frag = (uint4*)xb;
+    uint2* dig = (uint2*)xb;
+    uint2* tab = (uint2*)(xb + xdig_table_offset(nb));
     float scale = 1.f;
     if (g) {
         float ss = 0.f;
@@ -505,62 +512,69 @@ __global__ __launch_bounds__(kBlock) void k_xdigits(const float* __restrict__ xi
         scale = 1.0f / sqrtf(block_sum(ss, red) / (float)K + eps);
     }
     // K % 32 == 0 and kBlock % 4 == 0: the four threads of a block are all in or all out
-    for (int c0 = 0; c0 < K / 8; c0 += kBlock) {
-        const int c = c0 + tid;                     // 8 columns per thread
-        const bool in = c < K / 8;
-        float v[8];
-        const int cc = in ? c : 0;
-        const float4 v0 = *(const float4*)(x + 8 * cc), v1 = *(const float4*)(x + 8 * cc + 4);
-        v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
-        v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
-        if (g) {
-            const float4 g0 = *(const float4*)(g + 8 * cc), g1 = *(const float4*)(g + 8 * cc + 4);
-            const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-            #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = v[e] * scale * gg[e];
-        }
-        float m = 0.f;
+    const int c = blockIdx.x * kBlock + tid;        // 8 columns per thread
+    const bool in = c < K / 8;
+    const int cc = in ? c : 0;
+    float v[8];
+    const float4 v0 = *(const float4*)(x + 8 * cc), v1 = *(const float4*)(x + 8 * cc + 4);
+    v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
+    v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+    if (g) {
+        const float4 g0 = *(const float4*)(g + 8 * cc), g1 = *(const float4*)(g + 8 * cc + 4);
+        const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
         #pragma unroll
-        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
-        m = fmaxf(m, __shfl_xor(m, 1, 64));         // the block's four threads
-        m = fmaxf(m, __shfl_xor(m, 2, 64));
-        const float f = m > 0.f ? 8323072.0f / m : 0.f;     // 127 * 2^16 / max|x_b|
-        uint32_t w[3][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}};
-        int t[3] = {0, 0, 0};
-        #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int X = (int)rintf(v[e] * f);
-            const int x1 = (X + 128) >> 8, x2 = (x1 + 128) >> 8;
-            const int d0 = (int)(int8_t)(X & 255), d1 = (int)(int8_t)(x1 & 255);
-            w[0][e >> 2] |= (uint32_t)(d0 & 255) << (8 * (e & 3));
-            w[1][e >> 2] |= (uint32_t)(d1 & 255) << (8 * (e & 3));
-            w[2][e >> 2] |= (uint32_t)(x2 & 255) << (8 * (e & 3));
-            t[0] += d0;
-            t[1] += d1;
-            t[2] += x2;
-        }
+        for (int e = 0; e < 8; ++e) v[e] = v[e] * scale * gg[e];
+    }
+    float m = 0.f;
+    #pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
+    m = fmaxf(m, __shfl_xor(m, 1, 64));             // the block's four threads
+    m = fmaxf(m, __shfl_xor(m, 2, 64));
+    const float f = m > 0.f ? 8323072.0f / m : 0.f;         // 127 * 2^16 / max|x_b|
+    uint32_t w[3][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}};
+    int t[3] = {0, 0, 0};
+    #pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int X = (int)rintf(v[e] * f);
+        const int x1 = (X + 128) >> 8, x2 = (x1 + 128) >> 8;
+        const int d0 = (int)(int8_t)(X & 255), d1 = (int)(int8_t)(x1 & 255);
+        w[0][e >> 2] |= (uint32_t)(d0 & 255) << (8 * (e & 3));
+        w[1][e >> 2] |= (uint32_t)(d1 & 255) << (8 * (e & 3));
+        w[2][e >> 2] |= (uint32_t)(x2 & 255) << (8 * (e & 3));
+        t[0] += d0;
+        t[1] += d1;
+        t[2] += x2;
+    }
+    #pragma unroll
+    for (int d = 0; d < 3; ++d) {
+        t[d] += __shfl_xor(t[d], 1, 64);
+        t[d] += __shfl_xor(t[d], 2, 64);
+    }
+    if (in) {
+        const int b = c >> 2, gq = c & 3;
+        const uint32_t sxb = __float_as_uint(m * (1.0f / 8323072.0f));
         #pragma unroll
         for (int d = 0; d < 3; ++d) {
-            t[d] += __shfl_xor(t[d], 1, 64);
-            t[d] += __shfl_xor(t[d], 2, 64);
-        }
-        if (in) {
-            const int b = c >> 2, gq = c & 3;
-            const uint32_t sxb = __float_as_uint(m * (1.0f / 8323072.0f));
-            #pragma unroll
-            for (int d = 0; d < 3; ++d)
-                frag[(b * 4 + gq) * 16 + 3 * s + d] = make_uint4(w[d][0], w[d][1], sxb, (uint32_t)t[d]);
+            dig[((int64_t)((b >> 1) * 4 + gq) * 16 + 3 * s + d) * 2 + (b & 1)] = make_uint2(w[d][0], w[d][1]);
+            if (gq == 0) tab[(int64_t)b * 16 + 3 * s + d] = make_uint2(sxb, (uint32_t)t[d]);
         }
     }
 }
 
-constexpr int kMbDepth = 4;   // blocks per lane per pipeline stage (two stages in flight)
+// Several-sequence GEMV: k_gemv_mfma<QT, EPI, W, T>.  A workgroup of W
+// wavefronts takes units of T consecutive 16-row tiles (grid-stride); its
+// wavefronts split K in whole pipeline stages of kMbDepth blocks and reduce
+// through LDS.  Per stage a lane loads its weight fragments (2 blocks per
+// 16 bytes for Q8_0, 4 for Q4_0, from the fragment copy: one contiguous 1 KiB
+// per wavefront and group), the scales of its D rows, and the activation
+// digit pairs, which serve all T tiles; each block's activation scale and
+// digit sum come from the table, staged in LDS once per workgroup.
+constexpr int kMbDepth = 4;    // blocks per pipeline stage
 
-// One 16-row tile per workgroup at a time (grid-stride over tiles); the W
-// wavefronts of the workgroup split the tile's K blocks and reduce through LDS.
-template <int QT, int EPI, int W>
+template <int QT, int EPI, int W, int T>
 __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
-    __shared__ __align__(16) float part[W][64][4];
+    extern __shared__ __align__(16) uint2 xtab[];           // [nb][16] (activation scale, digit sum)
+    __shared__ __align__(16) float part[W][T][64][4];
     __shared__ float wv_best[4][W];
     __shared__ int wi_best[4][W];
     __shared__ int s_last;
@@ -570,155 +584,198 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, j = lane & 15;
     const int sq = min(j / 3, 3), dg = j - 3 * (j / 3);   // this lane's column: sequence, digit
-    const int n_tiles = (N + 15) >> 4;
+    const int n_tiles = (N + 15) >> 4, n_units = (n_tiles + T - 1) / T;
     // each wavefront's K range is whole pipeline stages (kMbDepth blocks)
     const int nbq = ((nb + W - 1) / W + kMbDepth - 1) / kMbDepth * kMbDepth;
     const int b_lo = min(wave * nbq, nb), b_hi = min(b_lo + nbq, nb);
     constexpr int PER = QT == kQ8_0 ? 2 : 4;        // blocks per 16-byte weight fragment
-    constexpr int NW = kMbDepth / PER;               // weight fragments per stage
-    static_assert(kMbDepth % 4 == 0, "a stage is whole fragments of both formats");
-    const int ngrp = (nb + PER - 1) / PER;
-    const uint4* frag = (const uint4*)a.xfrag;
+    constexpr int NW = kMbDepth / PER;               // weight fragments per stage and tile
+    static_assert(kMbDepth % 4 == 0, "a stage is whole fragments of both formats and whole digit pairs");
+    const int ngrp = (nb + PER - 1) / PER, npair = (nb + 1) >> 1;
+    const uint4* xd = (const uint4*)a.xfrag + (g * 16 + j);     // this lane's digit pairs, stride 64
+    const uint2* xt = (const uint2*)(a.xfrag + xdig_table_offset(nb));
 
     float best_v = -FLT_MAX;
     int best_i = INT_MAX;
 
-    // one pipeline stage: kMbDepth blocks of this lane's row (weights, the 4
-    // rows' scales of its D rows, its B column's digits with scale and sum)
     struct Stage {
-        uint4 w[NW];                 // this lane's weight fragments (A operands of kMbDepth blocks)
-        uint2 sc[kMbDepth];          // scales of its D rows
-        uint4 x[kMbDepth];           // its B column's digits, block scale, digit sum
+        uint4 w[T][NW];              // weight fragments (A operands of kMbDepth blocks) per tile
+        uint2 sc[T][kMbDepth];       // scales of this lane's D rows per tile and block
+        uint4 x[kMbDepth / 2];       // B operands: digit pairs of this lane's column
     };
-    for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
-        // the tile's weights in fragment order: lane slices of 16 bytes, rows
-        // past N and blocks past K are zero
-        const uint4* qf = (const uint4*)a.w.qf + (int64_t)tile * ngrp * 64 + lane;
-        const uint16_t* sct = a.w.sct + (int64_t)tile * nb * 16 + 4 * g;
-        auto load = [&](int b0, Stage& st) {
+    auto load = [&](int unit, int b0, Stage& st) {
+        #pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const int tile = min(unit * T + t, n_tiles - 1);      // clamped: always in bounds
+            const uint4* qf = (const uint4*)a.w.qf + (int64_t)tile * ngrp * 64 + lane;
+            const uint16_t* sct = a.w.sct + (int64_t)tile * nb * 16 + 4 * g;
             #pragma unroll
             for (int f = 0; f < NW; ++f) {
-                const int grp = min(b0 / PER + f, ngrp - 1);   // clamped: always in bounds
-                st.w[f] = qf[(int64_t)grp * 64];
+                const int grp = min(b0 / PER + f, ngrp - 1);
+                st.w[t][f] = qf[(int64_t)grp * 64];
             }
             #pragma unroll
             for (int u = 0; u < kMbDepth; ++u) {
-                const int b = min(b0 + u, b_hi - 1);     // clamped: always in bounds
-                st.sc[u] = *(const uint2*)(sct + (int64_t)b * 16);
-                st.x[u] = frag[(b * 4 + g) * 16 + j];
+                const int b = min(b0 + u, b_hi - 1);
+                st.sc[t][u] = *(const uint2*)(sct + (int64_t)b * 16);
             }
-        };
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        auto compute = [&](int b0, const Stage& st) {
+        }
+        #pragma unroll
+        for (int h = 0; h < kMbDepth / 2; ++h) {
+            const int pr = min((b0 >> 1) + h, npair - 1);
+            st.x[h] = xd[(int64_t)pr * 64];
+        }
+    };
+    float acc[T][4];
+    auto compute = [&](int b0, const Stage& st) {
+        #pragma unroll
+        for (int u = 0; u < kMbDepth; ++u) {
+            if (b0 + u >= b_hi) break;
+            const uint4 xp = st.x[u >> 1];
+            const long bv = (u & 1) ? (long)(((uint64_t)xp.w << 32) | xp.z) : (long)(((uint64_t)xp.y << 32) | xp.x);
+            const uint2 tb = xtab[(b0 + u) * 16 + j];
+            const float sx = __uint_as_float(tb.x);
             #pragma unroll
-            for (int u = 0; u < kMbDepth; ++u) {
-                if (b0 + u >= b_hi) break;
+            for (int t = 0; t < T; ++t) {
                 uint2 wa;
                 if (QT == kQ8_0) {
-                    const uint4 f = st.w[u / 2];
+                    const uint4 f = st.w[t][u / 2];
                     wa = (u & 1) ? make_uint2(f.z, f.w) : make_uint2(f.x, f.y);
                 } else {
                     // 4 bytes: columns 8g+i in the low nibbles, 8g+4+i in the high ones
-                    const uint4 f = st.w[0];
+                    const uint4 f = st.w[t][0];
                     const uint32_t q = u == 0 ? f.x : u == 1 ? f.y : u == 2 ? f.z : f.w;
                     wa = make_uint2(q & 0x0F0F0F0Fu, (q >> 4) & 0x0F0F0F0Fu);
                 }
                 const long av = (long)(((uint64_t)wa.y << 32) | wa.x);
-                const long bv = (long)(((uint64_t)st.x[u].y << 32) | st.x[u].x);
                 v4i_t c = {0, 0, 0, 0};
                 c = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, bv, c, 0, 0, 0);
                 if (QT == kQ4_0) {
-                    const int t8 = 8 * (int)st.x[u].w;       // nibble n = q + 8
+                    const int t8 = 8 * (int)tb.y;            // nibble n = q + 8
                     #pragma unroll
                     for (int i = 0; i < 4; ++i) c[i] -= t8;
                 }
-                const float sx = __uint_as_float(st.x[u].z);
-                acc[0] = fmaf(h2f((uint16_t)(st.sc[u].x & 0xFFFF)) * sx, (float)c[0], acc[0]);
-                acc[1] = fmaf(h2f((uint16_t)(st.sc[u].x >> 16)) * sx, (float)c[1], acc[1]);
-                acc[2] = fmaf(h2f((uint16_t)(st.sc[u].y & 0xFFFF)) * sx, (float)c[2], acc[2]);
-                acc[3] = fmaf(h2f((uint16_t)(st.sc[u].y >> 16)) * sx, (float)c[3], acc[3]);
+                const uint2 sc = st.sc[t][u];
+                acc[t][0] = fmaf(h2f((uint16_t)(sc.x & 0xFFFF)) * sx, (float)c[0], acc[t][0]);
+                acc[t][1] = fmaf(h2f((uint16_t)(sc.x >> 16)) * sx, (float)c[1], acc[t][1]);
+                acc[t][2] = fmaf(h2f((uint16_t)(sc.y & 0xFFFF)) * sx, (float)c[2], acc[t][2]);
+                acc[t][3] = fmaf(h2f((uint16_t)(sc.y >> 16)) * sx, (float)c[3], acc[t][3]);
             }
-        };
+        }
+    };
+
+    // the first unit's first stage goes out before the table is staged
+    Stage sa, sb;
+    int unit = blockIdx.x;
+    const bool go0 = unit < n_units && b_lo < b_hi;
+    {
+        constexpr int XT = 8;                        // table entries per thread per round
+        uint2 tv[XT];
+        #pragma unroll
+        for (int r = 0; r < XT; ++r) {
+            const int i = min(tid + r * 64 * W, nb * 16 - 1);
+            tv[r] = xt[i];
+        }
+        if (go0) load(unit, b_lo, sa);
+        #pragma unroll
+        for (int r = 0; r < XT; ++r) {
+            const int i = tid + r * 64 * W;
+            if (i < nb * 16) xtab[i] = tv[r];
+        }
+        for (int i = tid + XT * 64 * W; i < nb * 16; i += 64 * W) xtab[i] = xt[i];
+        // LDS stores visible to the workgroup; the weight loads stay in flight
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    for (; unit < n_units; unit += gridDim.x) {
+        #pragma unroll
+        for (int t = 0; t < T; ++t)
+            #pragma unroll
+            for (int i = 0; i < 4; ++i) acc[t][i] = 0.f;
         // two stages in flight: the next stage's loads are issued before this one computes
         if (b_lo < b_hi) {
-            Stage sa, sb;
-            load(b_lo, sa);
+            if (unit != (int)blockIdx.x) load(unit, b_lo, sa);
             int b0 = b_lo;
             for (;;) {
                 const bool more = b0 + kMbDepth < b_hi;
-                if (more) load(b0 + kMbDepth, sb);
+                if (more) load(unit, b0 + kMbDepth, sb);
                 compute(b0, sa);
                 b0 += kMbDepth;
                 if (!more) break;
                 const bool more2 = b0 + kMbDepth < b_hi;
-                if (more2) load(b0 + kMbDepth, sa);
+                if (more2) load(unit, b0 + kMbDepth, sa);
                 compute(b0, sb);
                 b0 += kMbDepth;
                 if (!more2) break;
             }
         }
-        *(float4*)&part[wave][lane][0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        #pragma unroll
+        for (int t = 0; t < T; ++t)
+            *(float4*)&part[wave][t][lane][0] = make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
         __syncthreads();
-        float y[4] = {0.f, 0.f, 0.f, 0.f};
-        if (wave == 0) {
-            #pragma unroll
-            for (int w = 0; w < W; ++w) {
-                const float4 v = *(const float4*)&part[w][lane][0];
-                y[0] += v.x; y[1] += v.y; y[2] += v.z; y[3] += v.w;
+        #pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const int tile = unit * T + t;
+            float y[4] = {0.f, 0.f, 0.f, 0.f};
+            if (wave == 0) {
+                #pragma unroll
+                for (int w = 0; w < W; ++w) {
+                    const float4 v = *(const float4*)&part[w][t][lane][0];
+                    y[0] += v.x; y[1] += v.y; y[2] += v.z; y[3] += v.w;
+                }
+                // a sequence's three digit columns sit in lanes j, j+1, j+2 of the group
+                #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float y1 = __shfl(y[i], lane + 1, 64), y2 = __shfl(y[i], lane + 2, 64);
+                    y[i] = fmaf(y2, 65536.0f, fmaf(y1, 256.0f, y[i]));
+                }
             }
-            // a sequence's three digit columns sit in lanes j, j+1, j+2 of the group
-            #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float y1 = __shfl(y[i], lane + 1, 64), y2 = __shfl(y[i], lane + 2, 64);
-                y[i] = fmaf(y2, 65536.0f, fmaf(y1, 256.0f, y[i]));
-            }
-        }
-        if (wave == 0 && dg == 0 && j < 3 * a.n_seq) {
-            const int s = sq;
-            #pragma unroll
-            for (int pr = 0; pr < 2; ++pr) {
-                const int r0 = tile * 16 + 4 * g + 2 * pr;   // rows r0, r0 + 1 (a RoPE / gate-up pair)
-                const float y0 = y[2 * pr], y1 = y[2 * pr + 1];
-                if (EPI == EPI_QKV) {
-                    const int p = a.pos[s];
-                    const int hd = a.head_dim;
-                    if (r0 < a.q_rows + a.kv_rows) {
-                        const int rr = r0 < a.q_rows ? r0 : r0 - a.q_rows;
-                        const int pi = (rr % hd) >> 1;
-                        const float cs = a.rope_cos[(int64_t)p * (hd >> 1) + pi];
-                        const float sn = a.rope_sin[(int64_t)p * (hd >> 1) + pi];
-                        const float z0 = y0 * cs - y1 * sn;
-                        const float z1 = y0 * sn + y1 * cs;
-                        if (r0 < a.q_rows) {
-                            *(float2*)(a.out + (int64_t)s * a.out_stride + r0) = make_float2(z0, z1);
+            if (wave == 0 && dg == 0 && j < 3 * a.n_seq && tile < n_tiles) {
+                const int s = sq;
+                #pragma unroll
+                for (int pr = 0; pr < 2; ++pr) {
+                    const int r0 = tile * 16 + 4 * g + 2 * pr;   // rows r0, r0 + 1 (a RoPE / gate-up pair)
+                    const float y0 = y[2 * pr], y1 = y[2 * pr + 1];
+                    if (EPI == EPI_QKV) {
+                        const int p = a.pos[s];
+                        const int hd = a.head_dim;
+                        if (r0 < a.q_rows + a.kv_rows) {
+                            const int rr = r0 < a.q_rows ? r0 : r0 - a.q_rows;
+                            const int pi = (rr % hd) >> 1;
+                            const float cs = a.rope_cos[(int64_t)p * (hd >> 1) + pi];
+                            const float sn = a.rope_sin[(int64_t)p * (hd >> 1) + pi];
+                            const float z0 = y0 * cs - y1 * sn;
+                            const float z1 = y0 * sn + y1 * cs;
+                            if (r0 < a.q_rows) {
+                                *(float2*)(a.out + (int64_t)s * a.out_stride + r0) = make_float2(z0, z1);
+                            } else {
+                                __half2* dst = (__half2*)(a.kcache + (int64_t)s * a.kv_seq_stride +
+                                                          ((int64_t)(rr / hd) * a.max_ctx + p) * hd + (rr % hd));
+                                *dst = __floats2half2_rn(z0, z1);
+                            }
                         } else {
-                            __half2* dst = (__half2*)(a.kcache + (int64_t)s * a.kv_seq_stride +
+                            const int rr = r0 - a.q_rows - a.kv_rows;
+                            __half2* dst = (__half2*)(a.vcache + (int64_t)s * a.kv_seq_stride +
                                                       ((int64_t)(rr / hd) * a.max_ctx + p) * hd + (rr % hd));
-                            *dst = __floats2half2_rn(z0, z1);
+                            *dst = __floats2half2_rn(y0, y1);
                         }
-                    } else {
-                        const int rr = r0 - a.q_rows - a.kv_rows;
-                        __half2* dst = (__half2*)(a.vcache + (int64_t)s * a.kv_seq_stride +
-                                                  ((int64_t)(rr / hd) * a.max_ctx + p) * hd + (rr % hd));
-                        *dst = __floats2half2_rn(y0, y1);
-                    }
-                } else if (EPI == EPI_RESID) {
-                    float* xo = a.out + (int64_t)s * a.out_stride + r0;
-                    float2 v = *(float2*)xo;
-                    v.x += y0;
-                    v.y += y1;
-                    *(float2*)xo = v;
-                } else if (EPI == EPI_SWIGLU) {
-                    const float sg = y0 / (1.0f + __expf(-y0));
-                    a.out[(int64_t)s * a.out_stride + (r0 >> 1)] = sg * y1;
-                } else {  // EPI_LOGITS: the vocabulary may end inside a tile or a pair
-                    if (r0 < N) {
-                        if (a.out) a.out[(int64_t)s * a.out_stride + r0] = y0;
-                        better(best_v, best_i, y0, r0);
-                    }
-                    if (r0 + 1 < N) {
-                        if (a.out) a.out[(int64_t)s * a.out_stride + r0 + 1] = y1;
-                        better(best_v, best_i, y1, r0 + 1);
+                    } else if (EPI == EPI_RESID) {
+                        float* xo = a.out + (int64_t)s * a.out_stride + r0;
+                        float2 v = *(float2*)xo;
+                        v.x += y0;
+                        v.y += y1;
+                        *(float2*)xo = v;
+                    } else if (EPI == EPI_SWIGLU) {
+                        const float sg = y0 / (1.0f + __expf(-y0));
+                        a.out[(int64_t)s * a.out_stride + (r0 >> 1)] = sg * y1;
+                    } else {  // EPI_LOGITS: the vocabulary may end inside a tile or a pair
+                        if (r0 < N) {
+                            if (a.out) a.out[(int64_t)s * a.out_stride + r0] = y0;
+                            better(best_v, best_i, y0, r0);
+                        }
+                        if (r0 + 1 < N) {
+                            if (a.out) a.out[(int64_t)s * a.out_stride + r0 + 1] = y1;
+                            better(best_v, best_i, y1, r0 + 1);
+                        }
                     }
                 }
             }
@@ -780,35 +837,38 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
     }
 }
 
-template <int QT, int EPI, int W>
-static hipError_t launch_mfma_w(const GemvArgs& a, int max_blocks, hipStream_t st) {
-    const int n_tiles = (a.w.N + 15) / 16;
+template <int QT, int EPI, int W, int T>
+static hipError_t launch_mfma_wt(const GemvArgs& a, int max_blocks, hipStream_t st) {
+    const int n_tiles = (a.w.N + 15) / 16, n_units = (n_tiles + T - 1) / T;
+    const size_t lds = (size_t)(a.w.K / 32) * 16 * sizeof(uint2);
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemv_mfma<QT, EPI, W>, 64 * W, 0) != hipSuccess ||
-        per_cu < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemv_mfma<QT, EPI, W, T>, 64 * W, lds) !=
+            hipSuccess || per_cu < 1)
         per_cu = 1;
     const int cap = std::min(max_blocks, per_cu * device_cus());
-    const int grid = std::max(1, std::min(n_tiles, cap));
-    hipLaunchKernelGGL((k_gemv_mfma<QT, EPI, W>), dim3(grid), dim3(64 * W), 0, st, a);
+    const int grid = std::max(1, std::min(n_units, cap));
+    hipLaunchKernelGGL((k_gemv_mfma<QT, EPI, W, T>), dim3(grid), dim3(64 * W), lds, st, a);
     return hipGetLastError();
 }
 
-// wavefronts per tile: enough K splitting that every CU holds ~16 wavefronts
+// Shapes with many tiles take two tiles per wavefront (the activation
+// operands then serve both); the others split K over more wavefronts.
 template <int QT, int EPI>
 static hipError_t launch_mfma(const GemvArgs& a, int max_blocks, hipStream_t st) {
     const int n_tiles = (a.w.N + 15) / 16;
-    const int64_t target = (int64_t)device_cus() * 16;
-    if ((int64_t)n_tiles * 4 >= target) return launch_mfma_w<QT, EPI, 4>(a, max_blocks, st);
-    if ((int64_t)n_tiles * 8 >= target) return launch_mfma_w<QT, EPI, 8>(a, max_blocks, st);
-    return launch_mfma_w<QT, EPI, 16>(a, max_blocks, st);
+    const int64_t target = (int64_t)device_cus() * 16;       // wavefronts wanted
+    if ((int64_t)n_tiles * 2 >= target) return launch_mfma_wt<QT, EPI, 4, 2>(a, max_blocks, st);
+    if ((int64_t)n_tiles * 4 >= target) return launch_mfma_wt<QT, EPI, 4, 1>(a, max_blocks, st);
+    if ((int64_t)n_tiles * 8 >= target) return launch_mfma_wt<QT, EPI, 8, 1>(a, max_blocks, st);
+    return launch_mfma_wt<QT, EPI, 16, 1>(a, max_blocks, st);
 }
 
 hipError_t launch_gemv_batched(const GemvArgs& a0, int epi, int n_seq, int max_blocks, hipStream_t st) {
     if (n_seq < 1 || n_seq > 4 || !a0.w.sct || !a0.w.qf || !a0.xfrag) return hipErrorInvalidValue;
     GemvArgs a = a0;
     a.n_seq = n_seq;
-    hipLaunchKernelGGL(k_xdigits, dim3(n_seq), dim3(kBlock), 0, st, a.xin, a.x_stride, a.norm_g, a.eps, a.w.K,
-                       (uint8_t*)a.xfrag);
+    hipLaunchKernelGGL(k_xdigits, dim3((a.w.K + 8 * kBlock - 1) / (8 * kBlock), n_seq), dim3(kBlock), 0, st, a.xin,
+                       a.x_stride, a.norm_g, a.eps, a.w.K, a.xfrag);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.qtype == kQ8_0) {

@@ -124,7 +124,7 @@ struct lm_model {
     uint16_t* d_lm_sc = nullptr;
     uint16_t* d_lm_sct = nullptr;
     uint8_t* d_lm_qf = nullptr;           // LM head fragment copy (several-sequence models)
-    uint4* d_xfrag = nullptr;             // activation fragments of the MFMA path
+    uint8_t* d_xfrag = nullptr;           // activation operands of the MFMA path
     __half* d_k = nullptr;                // [L][S][nkv][max_ctx][hd]
     __half* d_v = nullptr;
     float *d_x = nullptr, *d_q = nullptr, *d_o = nullptr, *d_h = nullptr, *d_logits = nullptr;
@@ -470,6 +470,7 @@ extern "C" lm_status lm_model_create(const lm_config* cfg, void* hip_stream, lm_
         CREATE_TRY(dev_alloc(m, (void**)&m->d_lm_qf, m->lm_qf_bytes, "LM head matrix-core fragments"));
         const int64_t kmax = std::max<int64_t>({m->H, m->qrows, m->F});
         CREATE_TRY(dev_alloc(m, (void**)&m->d_xfrag, xfrag_bytes(kmax), "activation fragments"));
+        CREATE_HIP(hipMemsetAsync(m->d_xfrag, 0, (size_t)xfrag_bytes(kmax), m->stream));
     }
     CREATE_TRY(dev_alloc(m, (void**)&m->d_k, L * kv_layer_elems(m) * 2, "K cache"));
     CREATE_TRY(dev_alloc(m, (void**)&m->d_v, L * kv_layer_elems(m) * 2, "V cache"));
