@@ -90,7 +90,8 @@ struct AttnArgs {
     const int* pos;
     int nq, nkv, hd, max_ctx, max_chunks;
     float scale;           // 1/sqrt(hd)
-    float* part;           // [n_seq][nq][max_chunks][hd + 2] partial o, m, l
+    int tiles;             // kAttnChunk-position tiles per workgroup (attn_tiles)
+    float* part;           // [n_seq][nq][max_chunks][hd + 2] partial o, m, l (one record per workgroup)
     int* counter;          // [n_seq][nkv][attn_cnt_lines][kCntStride] chunk counts (first int of
                            // each line, see chunk_arrive), zero between launches
     float* out;            // [n_seq][nq*hd]
@@ -107,6 +108,7 @@ hipError_t launch_gemv_batched(const GemvArgs& a, int epi, int n_seq, int max_bl
 // (activation scale, digit sum).
 constexpr int64_t xdig_table_offset(int64_t nb) { return (nb + 1) / 2 * 1024; }
 inline int64_t xfrag_bytes(int64_t K) { return xdig_table_offset(K / 32) + K / 32 * 128; }
+int attn_tiles(int n_seq, int nkv, int max_chunks);
 hipError_t launch_attention(const AttnArgs& a, int n_seq, hipStream_t st);
 hipError_t launch_dequant(const QMat& w, int qtype, int row0, int n_rows, float* out,
                           hipStream_t st);

@@ -921,8 +921,9 @@ __device__ __forceinline__ float2 ld_dev2(const float* p) {
 // this wavefront's outstanding memory operations have completed (gfx9 vmcnt(0))
 __device__ __forceinline__ void drain_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// One tile per workgroup (short contexts: the straight-line form).
 template <int HD>
-__global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
+__global__ __launch_bounds__(kBlock) void k_attn1(AttnArgs a) {
     constexpr int CH = kAttnChunk;
     constexpr int KP = HD + 8;                  // padded K row (halves)
     constexpr int PCS = CH * HD / 8 / kBlock;   // 16-byte pieces per thread per tile
@@ -1086,11 +1087,250 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
         reinterpret_cast<float (*)[6]>(&Ks[0][0]));
 }
 
+// Several tiles per workgroup (TP = 2 or 4: long contexts with many
+// workgroups): the span's tiles in turn, the next tile's K/V loads in flight
+// while the current one computes, with a running maximum and sum per head.
+template <int HD, int TP>
+__global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
+    static_assert(TP >= 2, "one tile: k_attn1");
+    constexpr int CH = kAttnChunk;
+    constexpr int KP = HD + 8;                  // padded K row (halves)
+    constexpr int PCS = CH * HD / 8 / kBlock;   // 16-byte pieces per thread per tile
+    constexpr int D8 = HD / 8;
+    constexpr int NI = (kMaxGroup * D8 * kWaves + kBlock - 1) / kBlock;   // PV items per thread
+    // the K tile is dead once the last scores are taken: the PV partial sums reuse it
+    static_assert(sizeof(float) * kWaves * kMaxGroup * HD <= sizeof(__half) * CH * KP, "Os fits in Ks");
+    static_assert(sizeof(float) * 6 * kBlock <= sizeof(__half) * CH * KP, "merge scratch fits in Ks");
+    __shared__ __align__(16) __half Ks[CH][KP];
+    __shared__ __align__(16) __half Vs[CH][HD];
+    __shared__ __align__(16) float Qs[kMaxGroup][HD];
+    __shared__ __align__(16) float Ps[kMaxGroup][CH];
+    __shared__ float Ms[kMaxGroup], Ls[kMaxGroup], Rs[kMaxGroup];
+    __shared__ int s_last;
+    float (*Os)[kMaxGroup * HD] = reinterpret_cast<float (*)[kMaxGroup * HD]>(&Ks[0][0]);
+
+    // this workgroup's span: tiles span*TP .. span*TP+TP-1 of CH positions each
+    const int chunk = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int G = a.nq / a.nkv;
+    const int64_t stride = HD + 2;      // even: 8-byte aligned pairs
+
+    // ---- the first tile's loads first (rows clamped to the cache; masked below)
+    const __half* Kg = a.kcache + (int64_t)s * a.kv_seq_stride + (int64_t)g * a.max_ctx * HD;
+    const __half* Vg = a.vcache + (int64_t)s * a.kv_seq_stride + (int64_t)g * a.max_ctx * HD;
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // (native vectors: kept in registers)
+    u32x4 kr[PCS], vr[PCS];
+    const int t_first = chunk * TP;
+    #pragma unroll
+    for (int u = 0; u < PCS; ++u) {
+        const int c = tid + u * kBlock;
+        const int t = min(t_first * CH + c / (HD / 8), a.max_ctx - 1), d8 = (c % (HD / 8)) * 8;
+        kr[u] = *(const u32x4*)(Kg + (int64_t)t * HD + d8);
+        vr[u] = *(const u32x4*)(Vg + (int64_t)t * HD + d8);
+    }
+    const float* qg = a.q + (int64_t)s * a.nq * HD + (int64_t)g * G * HD;
+    constexpr int kQ = (kMaxGroup * HD / 4 + kBlock - 1) / kBlock;
+    float4 qv[kQ];
+    #pragma unroll
+    for (int u = 0; u < kQ; ++u) {
+        const int i = min((tid + u * kBlock) * 4, G * HD - 4);
+        qv[u] = *(const float4*)(qg + i);
+    }
+    const int n_ctx = a.pos[s] + 1;                       // keys 0..pos inclusive
+    const int n_tiles = (n_ctx + CH - 1) / CH;
+    const int n_act = (n_tiles + TP - 1) / TP;            // spans holding keys
+    if (chunk >= n_act) return;                           // span past the causal horizon
+
+    #pragma unroll
+    for (int u = 0; u < kQ; ++u) {
+        const int i = (tid + u * kBlock) * 4;
+        if (i < G * HD) *(float4*)&Qs[i / HD][i % HD] = qv[u];
+    }
+    if (tid < G) {
+        Ms[tid] = -FLT_MAX;
+        Ls[tid] = 0.f;
+    }
+    // PV accumulators: thread item (key quarter w, head j, 8 dimensions)
+    float o[NI][8];
+    #pragma unroll
+    for (int i = 0; i < NI; ++i)
+        #pragma unroll
+        for (int k = 0; k < 8; ++k) o[i][k] = 0.f;
+
+    // TP is a compile-time count and every tile runs (one past the context
+    // has no valid key and changes nothing): the loop unrolls without
+    // branches and K/V stay in registers
+    #pragma unroll
+    for (int ti = 0; ti < TP; ++ti) {
+        const int tile = t_first + ti;
+        const int nt = max(0, min(CH, n_ctx - tile * CH));
+        #pragma unroll
+        for (int u = 0; u < PCS; ++u) {
+            const int c = tid + u * kBlock;
+            const int t = c / (HD / 8), d8 = (c % (HD / 8)) * 8;
+            *(u32x4*)&Ks[t][d8] = kr[u];
+            *(u32x4*)&Vs[t][d8] = vr[u];
+        }
+        if (ti + 1 < TP) {                                // in flight while this tile computes
+            #pragma unroll
+            for (int u = 0; u < PCS; ++u) {
+                const int c = tid + u * kBlock;
+                const int t = min((tile + 1) * CH + c / (HD / 8), a.max_ctx - 1), d8 = (c % (HD / 8)) * 8;
+                kr[u] = *(const u32x4*)(Kg + (int64_t)t * HD + d8);
+                vr[u] = *(const u32x4*)(Vg + (int64_t)t * HD + d8);
+            }
+        }
+        __syncthreads();
+
+        // ---- scores: a wavefront per query head, a lane per key; the running
+        // maximum M and sum L of the head (online softmax over the span's tiles)
+        for (int j = wave; j < G; j += kWaves) {
+            float sc = -FLT_MAX;
+            if (lane < nt) {
+                float acc0 = 0.f, acc1 = 0.f;
+                #pragma unroll
+                for (int d = 0; d < HD; d += 8) {
+                    const uint4 kk = *(const uint4*)&Ks[lane][d];
+                    const float4 q0 = *(const float4*)&Qs[j][d];
+                    const float4 q1 = *(const float4*)&Qs[j][d + 4];
+                    const float2 k01 = __half22float2(*(const __half2*)&kk.x);
+                    const float2 k23 = __half22float2(*(const __half2*)&kk.y);
+                    const float2 k45 = __half22float2(*(const __half2*)&kk.z);
+                    const float2 k67 = __half22float2(*(const __half2*)&kk.w);
+                    acc0 = fmaf(q0.x, k01.x, acc0);
+                    acc1 = fmaf(q0.y, k01.y, acc1);
+                    acc0 = fmaf(q0.z, k23.x, acc0);
+                    acc1 = fmaf(q0.w, k23.y, acc1);
+                    acc0 = fmaf(q1.x, k45.x, acc0);
+                    acc1 = fmaf(q1.y, k45.y, acc1);
+                    acc0 = fmaf(q1.z, k67.x, acc0);
+                    acc1 = fmaf(q1.w, k67.y, acc1);
+                }
+                sc = (acc0 + acc1) * a.scale;
+            }
+            const float m_old = Ms[j];
+            const float m = fmaxf(m_old, wave_max(sc));
+            const float r = __expf(m_old - m);            // 0 on the first tile
+            const float p = lane < nt ? __expf(sc - m) : 0.f;
+            const float l = wave_sum(p);
+            Ps[j][lane] = p;
+            if (lane == 0) {
+                Ms[j] = m;
+                Ls[j] = fmaf(Ls[j], r, l);
+                Rs[j] = r;
+            }
+        }
+        __syncthreads();
+
+        // ---- o = r o + sum_t p_t v_t over this tile's keys of quarter w
+        #pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int idx = tid + i * kBlock;
+            const bool live = idx < G * D8 * kWaves;          // (no break: o stays in registers)
+            const int w = idx / (G * D8), rr = idx % (G * D8);
+            const int j = live ? rr / D8 : 0, d8 = (rr % D8) * 8;
+            const float r = Rs[j];
+            #pragma unroll
+            for (int k = 0; k < 8; ++k) o[i][k] *= r;
+            const int tb = w * (CH / kWaves), te = live ? min(tb + CH / kWaves, nt) : tb;
+            for (int t = tb; t < te; ++t) {
+                const float pt = Ps[j][t];
+                const uint4 vv = *(const uint4*)&Vs[t][d8];
+                const float2 v01 = __half22float2(*(const __half2*)&vv.x);
+                const float2 v23 = __half22float2(*(const __half2*)&vv.y);
+                const float2 v45 = __half22float2(*(const __half2*)&vv.z);
+                const float2 v67 = __half22float2(*(const __half2*)&vv.w);
+                o[i][0] = fmaf(pt, v01.x, o[i][0]);
+                o[i][1] = fmaf(pt, v01.y, o[i][1]);
+                o[i][2] = fmaf(pt, v23.x, o[i][2]);
+                o[i][3] = fmaf(pt, v23.y, o[i][3]);
+                o[i][4] = fmaf(pt, v45.x, o[i][4]);
+                o[i][5] = fmaf(pt, v45.y, o[i][5]);
+                o[i][6] = fmaf(pt, v67.x, o[i][6]);
+                o[i][7] = fmaf(pt, v67.y, o[i][7]);
+            }
+        }
+        // before the next tile overwrites K, V and P (after the last one the
+        // partial sums below overwrite only K, whose reads ended before P)
+        if (ti + 1 < TP) __syncthreads();
+    }
+    #pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int idx = tid + i * kBlock;
+        if (idx < G * D8 * kWaves) {
+            const int w = idx / (G * D8), rr = idx % (G * D8);
+            const int j = rr / D8, d8 = (rr % D8) * 8;
+            float* dst = &Os[w][j * HD + d8];
+            *(float4*)dst = make_float4(o[i][0], o[i][1], o[i][2], o[i][3]);
+            *(float4*)(dst + 4) = make_float4(o[i][4], o[i][5], o[i][6], o[i][7]);
+        }
+    }
+    __syncthreads();
+
+    float* part_s = a.part + (int64_t)s * a.nq * a.max_chunks * stride;
+    float* out_s = a.out + (int64_t)s * a.nq * HD + (int64_t)g * G * HD;
+    if (n_act == 1) {
+        for (int i = tid; i < G * HD; i += kBlock) {
+            float v = Os[0][i];
+            #pragma unroll
+            for (int w = 1; w < kWaves; ++w) v += Os[w][i];
+            out_s[i] = v / Ls[i / HD];
+        }
+        return;
+    }
+    for (int i = 2 * tid; i < G * HD; i += 2 * kBlock) {
+        float v0 = Os[0][i], v1 = Os[0][i + 1];
+        #pragma unroll
+        for (int w = 1; w < kWaves; ++w) {
+            v0 += Os[w][i];
+            v1 += Os[w][i + 1];
+        }
+        const int j = i / HD, d = i % HD;
+        float* ph = part_s + ((int64_t)(g * G + j) * a.max_chunks + chunk) * stride;
+        st_dev2(ph + d, v0, v1);
+        if (d == 0) st_dev2(ph + HD, Ms[j], Ls[j]);
+    }
+
+    // ---- the last chunk of this (sequence, KV head) merges every chunk.  The
+    // partials are device-coherent stores, each wavefront waits for its own
+    // to complete before the count is taken.
+    drain_vm();
+    __syncthreads();
+    if (tid == 0)
+        s_last = chunk_arrive(a.counter + (int64_t)(s * a.nkv + g) * attn_cnt_lines(a.max_chunks) * kCntStride,
+                              chunk, n_act);
+    __syncthreads();
+    if (!s_last) return;
+
+    const float* part_g = part_s + (int64_t)g * G * a.max_chunks * stride;
+    merge_chunk_states<HD>(
+        G, n_act, [&](int j) { return part_g + (int64_t)j * a.max_chunks * stride; },
+        [](const float* p) { return ld_dev2(p); },
+        [&](int i, float4 v) { *(float4*)(out_s + i) = v; },
+        reinterpret_cast<float (*)[6]>(&Ks[0][0]));
+}
+
+// Tiles per attention workgroup: one, unless the grid would hold more than
+// about four workgroups per CU; then up to four, so that fewer partial
+// states are merged and each workgroup's next tile loads while it computes.
+int attn_tiles(int n_seq, int nkv, int max_chunks) {
+    const int64_t wgs = (int64_t)n_seq * nkv * max_chunks, per = 4ll * device_cus();
+    return wgs >= 4 * per ? 4 : wgs >= 2 * per ? 2 : 1;
+}
+
 hipError_t launch_attention(const AttnArgs& a, int n_seq, hipStream_t st) {
-    dim3 grid(a.max_chunks, a.nkv, n_seq);
-    if (a.hd == 128) hipLaunchKernelGGL(k_attn<128>, grid, dim3(kBlock), 0, st, a);
-    else if (a.hd == 64) hipLaunchKernelGGL(k_attn<64>, grid, dim3(kBlock), 0, st, a);
-    else return hipErrorInvalidValue;
+    if (a.tiles != 1 && a.tiles != 2 && a.tiles != 4) return hipErrorInvalidValue;
+    if (a.hd != 128 && a.hd != 64) return hipErrorInvalidValue;
+    dim3 grid((a.max_chunks + a.tiles - 1) / a.tiles, a.nkv, n_seq);
+    if (a.hd == 128) {
+        if (a.tiles == 1) hipLaunchKernelGGL((k_attn1<128>), grid, dim3(kBlock), 0, st, a);
+        else if (a.tiles == 2) hipLaunchKernelGGL((k_attn<128, 2>), grid, dim3(kBlock), 0, st, a);
+        else hipLaunchKernelGGL((k_attn<128, 4>), grid, dim3(kBlock), 0, st, a);
+    } else {
+        if (a.tiles == 1) hipLaunchKernelGGL((k_attn1<64>), grid, dim3(kBlock), 0, st, a);
+        else if (a.tiles == 2) hipLaunchKernelGGL((k_attn<64, 2>), grid, dim3(kBlock), 0, st, a);
+        else hipLaunchKernelGGL((k_attn<64, 4>), grid, dim3(kBlock), 0, st, a);
+    }
     return hipGetLastError();
 }
 

@@ -1208,6 +1208,7 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
     at.max_ctx = c.max_ctx;
     at.max_chunks = m->max_chunks;
     at.scale = (float)(1.0 / std::sqrt((double)m->hd));
+    at.tiles = attn_tiles(n_seq, (int)m->nkv, m->max_chunks);
     at.part = m->d_attn_part;
     at.counter = m->d_attn_cnt;
     at.out = m->d_o;
