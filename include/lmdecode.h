@@ -67,13 +67,13 @@ typedef struct {
     int32_t hidden;      /* H, a multiple of 32 */
     int32_t n_layers;
     int32_t n_heads;     /* query heads nq */
-    int32_t n_kv_heads;  /* KV heads nkv; nq % nkv == 0 */
-    int32_t head_dim;    /* hd: even, 32 <= hd <= 256, nq*hd a multiple of 32 */
+    int32_t n_kv_heads;  /* KV heads nkv; nq % nkv == 0, nq / nkv <= 8 */
+    int32_t head_dim;    /* hd: 64 or 128 */
     int32_t ffn;         /* F, a multiple of 32 */
     double rms_eps;      /* RMSNorm epsilon (inside the square root) */
     double rope_theta;   /* RoPE base: pair i turns by p * theta^(-2i/hd) */
     int32_t max_ctx;     /* KV positions per sequence */
-    int32_t max_seqs;    /* sequences decoded together (1..4) */
+    int32_t max_seqs;    /* sequences decoded together (1..4; 2..4 need hidden <= 8192) */
     int32_t qtype;       /* LM_Q8_0 or LM_Q4_0, for every weight matrix */
 } lm_config;
 

@@ -486,41 +486,42 @@ typedef int v4i_t __attribute__((ext_vector_type(4)));
 //     activation scale max|x_b| / (127 x 2^16) of sequence s (fp32 bits) and
 //     column j's digit sum over the block's 32 columns (int32).
 // Columns j >= 3 x n_seq are never read.
-// Grid (ceil(K / 2048), n_seq): a thread per 8 columns, four consecutive
-// threads per block.  With a gain, every workgroup first takes the whole
-// row's RMS (the row is at most 64 KB, read from L2), so no workgroup waits
-// for another.
-__global__ __launch_bounds__(kBlock) void k_xdigits(const float* __restrict__ xin, int x_stride,
-                                                   const float* __restrict__ g, float eps, int K,
-                                                   uint8_t* __restrict__ xb) {
-    __shared__ float red[kWaves];
+// A thread per 8 columns, four consecutive threads per block, every input
+// loaded once.  With a gain (RMSNorm inputs) one workgroup covers the whole
+// row (K / 8 threads, up to 1024: K <= 8192), so the sum of squares comes from
+// the same registers; without one, the grid splits K into 2048-column chunks.
+template <bool GAIN>
+__global__ __launch_bounds__(1024) void k_xdigits(const float* __restrict__ xin, int x_stride,
+                                                 const float* __restrict__ g, float eps, int K,
+                                                 uint8_t* __restrict__ xb) {
+    __shared__ float red[16];
     const int s = blockIdx.y, tid = threadIdx.x;
     const int nb = K >> 5;
     const float* x = xin + (int64_t)s * x_stride;
     uint2* dig = (uint2*)xb;
     uint2* tab = (uint2*)(xb + xdig_table_offset(nb));
-    float scale = 1.f;
-    if (g) {
-        float ss = 0.f;
-        for (int i = tid * 4; i < K; i += kBlock * 4) {
-            const float4 v = *(const float4*)(x + i);
-            ss = fmaf(v.x, v.x, ss);
-            ss = fmaf(v.y, v.y, ss);
-            ss = fmaf(v.z, v.z, ss);
-            ss = fmaf(v.w, v.w, ss);
-        }
-        scale = 1.0f / sqrtf(block_sum(ss, red) / (float)K + eps);
-    }
-    // K % 32 == 0 and kBlock % 4 == 0: the four threads of a block are all in or all out
-    const int c = blockIdx.x * kBlock + tid;        // 8 columns per thread
+    // K % 32 == 0 and blockDim.x % 4 == 0: the four threads of a block are all in or all out
+    const int c = blockIdx.x * blockDim.x + tid;    // 8 columns per thread
     const bool in = c < K / 8;
     const int cc = in ? c : 0;
     float v[8];
     const float4 v0 = *(const float4*)(x + 8 * cc), v1 = *(const float4*)(x + 8 * cc + 4);
     v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
     v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
-    if (g) {
+    if (GAIN) {
         const float4 g0 = *(const float4*)(g + 8 * cc), g1 = *(const float4*)(g + 8 * cc + 4);
+        float ss = 0.f;
+        if (in) {
+            #pragma unroll
+            for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
+        }
+        // sum over the workgroup (blockDim.x / 64 wavefronts)
+        ss = wave_sum(ss);
+        if ((tid & 63) == 0) red[tid >> 6] = ss;
+        __syncthreads();
+        float tot = 0.f;
+        for (int w = 0; w < (int)(blockDim.x >> 6); ++w) tot += red[w];
+        const float scale = 1.0f / sqrtf(tot / (float)K + eps);
         const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
         #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = v[e] * scale * gg[e];
@@ -561,6 +562,20 @@ __global__ __launch_bounds__(kBlock) void k_xdigits(const float* __restrict__ xi
     }
 }
 
+static hipError_t launch_xdigits(const GemvArgs& a, int n_seq, hipStream_t st) {
+    const int K = a.w.K;
+    if (a.norm_g) {
+        const int threads = ((K / 8 + 63) / 64) * 64;   // whole wavefronts, one pass over the row
+        if (threads > 1024) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(k_xdigits<true>, dim3(1, n_seq), dim3(threads), 0, st, a.xin, a.x_stride, a.norm_g,
+                           a.eps, K, a.xfrag);
+    } else {
+        hipLaunchKernelGGL(k_xdigits<false>, dim3((K + 8 * kBlock - 1) / (8 * kBlock), n_seq), dim3(kBlock), 0, st,
+                           a.xin, a.x_stride, nullptr, a.eps, K, a.xfrag);
+    }
+    return hipGetLastError();
+}
+
 // Several-sequence GEMV: k_gemv_mfma<QT, EPI, W, T>.  A workgroup of W
 // wavefronts takes units of T consecutive 16-row tiles (grid-stride); its
 // wavefronts split K in whole pipeline stages of kMbDepth blocks and reduce
@@ -569,12 +584,21 @@ __global__ __launch_bounds__(kBlock) void k_xdigits(const float* __restrict__ xi
 // per wavefront and group), the scales of its D rows, and the activation
 // digit pairs, which serve all T tiles; each block's activation scale and
 // digit sum come from the table, staged in LDS once per workgroup.
+// PRO (inputs of at most kProMaxK columns): no separate digit launch; every
+// workgroup computes the digit pairs and the table of all sequences into LDS
+// in its prologue, while its first weight loads are in flight, from x (times
+// the gain for RMSNorm inputs); the RMS factor of each sequence is then applied
+// to the finished dot products (its sum of squares is taken in the same pass).
 constexpr int kMbDepth = 4;    // blocks per pipeline stage
+constexpr int kProMaxK = 6144; // widest input the prologue mode stages in LDS
 
-template <int QT, int EPI, int W, int T>
+template <int QT, int EPI, int W, int T, bool PRO>
 __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
-    extern __shared__ __align__(16) uint2 xtab[];           // [nb][16] (activation scale, digit sum)
+    static_assert(!PRO || W == 16, "the prologue mode runs with 16 wavefronts");
+    // LDS: PRO: digit pairs [np][4][16] x 16 B, then the table; else the table only
+    extern __shared__ __align__(16) uint4 xlds[];
     __shared__ __align__(16) float part[W][T][64][4];
+    __shared__ float ss_red[W][4];                          // PRO: per-wavefront sums of squares
     __shared__ float wv_best[4][W];
     __shared__ int wi_best[4][W];
     __shared__ int s_last;
@@ -594,6 +618,8 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
     const int ngrp = (nb + PER - 1) / PER, npair = (nb + 1) >> 1;
     const uint4* xd = (const uint4*)a.xfrag + (g * 16 + j);     // this lane's digit pairs, stride 64
     const uint2* xt = (const uint2*)(a.xfrag + xdig_table_offset(nb));
+    uint2* xtab = (uint2*)(PRO ? (uint8_t*)xlds + xdig_table_offset(nb) : (uint8_t*)xlds);
+    const uint4* xdl = xlds + (g * 16 + j);                      // PRO: digit pairs in LDS, stride 64
 
     float best_v = -FLT_MAX;
     int best_i = INT_MAX;
@@ -601,7 +627,7 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
     struct Stage {
         uint4 w[T][NW];              // weight fragments (A operands of kMbDepth blocks) per tile
         uint2 sc[T][kMbDepth];       // scales of this lane's D rows per tile and block
-        uint4 x[kMbDepth / 2];       // B operands: digit pairs of this lane's column
+        uint4 x[PRO ? 1 : kMbDepth / 2];   // B operands: digit pairs of this lane's column (PRO: LDS)
     };
     auto load = [&](int unit, int b0, Stage& st) {
         #pragma unroll
@@ -620,10 +646,12 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
                 st.sc[t][u] = *(const uint2*)(sct + (int64_t)b * 16);
             }
         }
-        #pragma unroll
-        for (int h = 0; h < kMbDepth / 2; ++h) {
-            const int pr = min((b0 >> 1) + h, npair - 1);
-            st.x[h] = xd[(int64_t)pr * 64];
+        if (!PRO) {
+            #pragma unroll
+            for (int h = 0; h < kMbDepth / 2; ++h) {
+                const int pr = min((b0 >> 1) + h, npair - 1);
+                st.x[h] = xd[(int64_t)pr * 64];
+            }
         }
     };
     float acc[T][4];
@@ -631,7 +659,7 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
         #pragma unroll
         for (int u = 0; u < kMbDepth; ++u) {
             if (b0 + u >= b_hi) break;
-            const uint4 xp = st.x[u >> 1];
+            const uint4 xp = PRO ? xdl[((b0 + u) >> 1) * 64] : st.x[PRO ? 0 : (u >> 1)];
             const long bv = (u & 1) ? (long)(((uint64_t)xp.w << 32) | xp.z) : (long)(((uint64_t)xp.y << 32) | xp.x);
             const uint2 tb = xtab[(b0 + u) * 16 + j];
             const float sx = __uint_as_float(tb.x);
@@ -668,7 +696,97 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
     Stage sa, sb;
     int unit = blockIdx.x;
     const bool go0 = unit < n_units && b_lo < b_hi;
-    {
+    if (PRO) {
+        // the digits of every sequence: an item per (sequence, 8 columns), four
+        // consecutive items per block (all active or all idle together).  Every
+        // item's inputs are requested first, then the first weight stage.
+        constexpr int MAXI = (4 * (kProMaxK / 8) + 64 * W - 1) / (64 * W);
+        const int cpr = K >> 3, n_items = a.n_seq * cpr;
+        const bool gain = a.norm_g != nullptr;
+        float4 xv[MAXI][2], gv[MAXI][2];
+        #pragma unroll
+        for (int i = 0; i < MAXI; ++i) {
+            const int it = tid + i * 64 * W;
+            const int sI = it < n_items ? it / cpr : 0, c = it < n_items ? it - sI * cpr : 0;
+            const float* xs = a.xin + (int64_t)sI * a.x_stride + 8 * c;
+            xv[i][0] = *(const float4*)xs;
+            xv[i][1] = *(const float4*)(xs + 4);
+            if (gain) {
+                gv[i][0] = *(const float4*)(a.norm_g + 8 * c);
+                gv[i][1] = *(const float4*)(a.norm_g + 8 * c + 4);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (go0) load(unit, b_lo, sa);
+        float ssq[4] = {0.f, 0.f, 0.f, 0.f};
+        uint2* dig = (uint2*)xlds;
+        #pragma unroll
+        for (int i = 0; i < MAXI; ++i) {
+            const int it = tid + i * 64 * W;
+            const bool in = it < n_items;
+            const int sI = in ? it / cpr : 0, c = in ? it - sI * cpr : 0;
+            float v[8] = {xv[i][0].x, xv[i][0].y, xv[i][0].z, xv[i][0].w,
+                          xv[i][1].x, xv[i][1].y, xv[i][1].z, xv[i][1].w};
+            if (gain) {
+                float q = 0.f;
+                #pragma unroll
+                for (int e = 0; e < 8; ++e) q = fmaf(v[e], v[e], q);
+                if (in) {
+                    ssq[0] += sI == 0 ? q : 0.f;
+                    ssq[1] += sI == 1 ? q : 0.f;
+                    ssq[2] += sI == 2 ? q : 0.f;
+                    ssq[3] += sI == 3 ? q : 0.f;
+                }
+                const float gg[8] = {gv[i][0].x, gv[i][0].y, gv[i][0].z, gv[i][0].w,
+                                     gv[i][1].x, gv[i][1].y, gv[i][1].z, gv[i][1].w};
+                #pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] *= gg[e];
+            }
+            float m = 0.f;
+            #pragma unroll
+            for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
+            m = fmaxf(m, __shfl_xor(m, 1, 64));
+            m = fmaxf(m, __shfl_xor(m, 2, 64));
+            const float f = m > 0.f ? 8323072.0f / m : 0.f;     // 127 * 2^16 / max|x_b|
+            uint32_t w[3][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}};
+            int tq[3] = {0, 0, 0};
+            #pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int X = (int)rintf(v[e] * f);
+                const int x1 = (X + 128) >> 8, x2 = (x1 + 128) >> 8;
+                const int d0 = (int)(int8_t)(X & 255), d1 = (int)(int8_t)(x1 & 255);
+                w[0][e >> 2] |= (uint32_t)(d0 & 255) << (8 * (e & 3));
+                w[1][e >> 2] |= (uint32_t)(d1 & 255) << (8 * (e & 3));
+                w[2][e >> 2] |= (uint32_t)(x2 & 255) << (8 * (e & 3));
+                tq[0] += d0;
+                tq[1] += d1;
+                tq[2] += x2;
+            }
+            #pragma unroll
+            for (int d = 0; d < 3; ++d) {
+                tq[d] += __shfl_xor(tq[d], 1, 64);
+                tq[d] += __shfl_xor(tq[d], 2, 64);
+            }
+            if (in) {
+                const int b = c >> 2, gq = c & 3;
+                const uint32_t sxb = __float_as_uint(m * (1.0f / 8323072.0f));
+                #pragma unroll
+                for (int d = 0; d < 3; ++d) {
+                    dig[(((b >> 1) * 4 + gq) * 16 + 3 * sI + d) * 2 + (b & 1)] = make_uint2(w[d][0], w[d][1]);
+                    if (gq == 0) xtab[b * 16 + 3 * sI + d] = make_uint2(sxb, (uint32_t)tq[d]);
+                }
+            }
+        }
+        if (a.norm_g) {
+            #pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float t = wave_sum(ssq[q]);
+                if (lane == 0) ss_red[wave][q] = t;
+            }
+        }
+        // LDS stores visible to the workgroup; the weight loads stay in flight
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    } else {
         constexpr int XT = 8;                        // table entries per thread per round
         uint2 tv[XT];
         #pragma unroll
@@ -685,6 +803,13 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
         for (int i = tid + XT * 64 * W; i < nb * 16; i += 64 * W) xtab[i] = xt[i];
         // LDS stores visible to the workgroup; the weight loads stay in flight
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    // PRO with a gain: RMSNorm factor of each sequence, applied to the finished sums
+    float rms = 1.f;
+    if (PRO && a.norm_g) {
+        float tot = 0.f;
+        for (int w = 0; w < W; ++w) tot += ss_red[w][sq];
+        rms = 1.0f / sqrtf(tot / (float)K + a.eps);
     }
     for (; unit < n_units; unit += gridDim.x) {
         #pragma unroll
@@ -734,7 +859,7 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
                 #pragma unroll
                 for (int pr = 0; pr < 2; ++pr) {
                     const int r0 = tile * 16 + 4 * g + 2 * pr;   // rows r0, r0 + 1 (a RoPE / gate-up pair)
-                    const float y0 = y[2 * pr], y1 = y[2 * pr + 1];
+                    const float y0 = y[2 * pr] * rms, y1 = y[2 * pr + 1] * rms;
                     if (EPI == EPI_QKV) {
                         const int p = a.pos[s];
                         const int hd = a.head_dim;
@@ -837,17 +962,22 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
     }
 }
 
-template <int QT, int EPI, int W, int T>
+template <int QT, int EPI, int W, int T, bool PRO>
 static hipError_t launch_mfma_wt(const GemvArgs& a, int max_blocks, hipStream_t st) {
     const int n_tiles = (a.w.N + 15) / 16, n_units = (n_tiles + T - 1) / T;
-    const size_t lds = (size_t)(a.w.K / 32) * 16 * sizeof(uint2);
+    const int nb = a.w.K / 32;
+    const size_t lds = (PRO ? (size_t)xdig_table_offset(nb) : 0) + (size_t)nb * 16 * sizeof(uint2);
+    if (!PRO) {
+        const hipError_t e = launch_xdigits(a, a.n_seq, st);
+        if (e != hipSuccess) return e;
+    }
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemv_mfma<QT, EPI, W, T>, 64 * W, lds) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemv_mfma<QT, EPI, W, T, PRO>, 64 * W, lds) !=
             hipSuccess || per_cu < 1)
         per_cu = 1;
     const int cap = std::min(max_blocks, per_cu * device_cus());
     const int grid = std::max(1, std::min(n_units, cap));
-    hipLaunchKernelGGL((k_gemv_mfma<QT, EPI, W, T>), dim3(grid), dim3(64 * W), lds, st, a);
+    hipLaunchKernelGGL((k_gemv_mfma<QT, EPI, W, T, PRO>), dim3(grid), dim3(64 * W), lds, st, a);
     return hipGetLastError();
 }
 
@@ -857,20 +987,19 @@ template <int QT, int EPI>
 static hipError_t launch_mfma(const GemvArgs& a, int max_blocks, hipStream_t st) {
     const int n_tiles = (a.w.N + 15) / 16;
     const int64_t target = (int64_t)device_cus() * 16;       // wavefronts wanted
-    if ((int64_t)n_tiles * 2 >= target) return launch_mfma_wt<QT, EPI, 4, 2>(a, max_blocks, st);
-    if ((int64_t)n_tiles * 4 >= target) return launch_mfma_wt<QT, EPI, 4, 1>(a, max_blocks, st);
-    if ((int64_t)n_tiles * 8 >= target) return launch_mfma_wt<QT, EPI, 8, 1>(a, max_blocks, st);
-    return launch_mfma_wt<QT, EPI, 16, 1>(a, max_blocks, st);
+    if ((int64_t)n_tiles * 2 >= target) return launch_mfma_wt<QT, EPI, 4, 2, false>(a, max_blocks, st);
+    if ((int64_t)n_tiles * 4 >= target) return launch_mfma_wt<QT, EPI, 4, 1, false>(a, max_blocks, st);
+    if ((int64_t)n_tiles * 8 >= target) return launch_mfma_wt<QT, EPI, 8, 1, false>(a, max_blocks, st);
+    // 16 wavefronts per workgroup (about one workgroup per CU): the prologue
+    // mode's LDS fits, and the digit launch disappears
+    if (a.w.K <= kProMaxK) return launch_mfma_wt<QT, EPI, 16, 1, true>(a, max_blocks, st);
+    return launch_mfma_wt<QT, EPI, 16, 1, false>(a, max_blocks, st);
 }
 
 hipError_t launch_gemv_batched(const GemvArgs& a0, int epi, int n_seq, int max_blocks, hipStream_t st) {
     if (n_seq < 1 || n_seq > 4 || !a0.w.sct || !a0.w.qf || !a0.xfrag) return hipErrorInvalidValue;
     GemvArgs a = a0;
     a.n_seq = n_seq;
-    hipLaunchKernelGGL(k_xdigits, dim3((a.w.K + 8 * kBlock - 1) / (8 * kBlock), n_seq), dim3(kBlock), 0, st, a.xin,
-                       a.x_stride, a.norm_g, a.eps, a.w.K, a.xfrag);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     if (a.qtype == kQ8_0) {
         switch (epi) {
             case EPI_QKV: return launch_mfma<kQ8_0, EPI_QKV>(a, max_blocks, st);
