@@ -27,8 +27,9 @@ constexpr int attn_cnt_lines(int max_chunks) { return 1 + (max_chunks + kCntGrou
 struct QMat {
     const uint8_t* q;
     const uint16_t* sc;
-    const uint16_t* sct;   // scales again, transposed per 16-row tile: [N/16][nb][16]
-                           // (present when the model decodes several sequences at once)
+    const uint16_t* sct;   // scales again for the matrix-core GEMV: per 16-row tile, 4-block group,
+                           // row, block (sct_bytes in lm_runtime.cpp; models that decode several
+                           // sequences at once)
     const uint8_t* qf;     // quants again, as matrix-core A fragments (same models; below)
     int N, K;
 };
@@ -104,8 +105,8 @@ hipError_t launch_gemv(const GemvArgs& a, int epi, int n_seq, int max_blocks, hi
 // 2..4 sequences: activation fragments (RMSNorm applied), then the MFMA GEMV
 hipError_t launch_gemv_batched(const GemvArgs& a, int epi, int n_seq, int max_blocks, hipStream_t st);
 // Activation operands of the several-sequence GEMV (nb = K/32 blocks): digit
-// pairs [ceil(nb/2)][4][16] x 16 bytes, then the table [nb][16] x 8 bytes
-// (activation scale, digit sum).
+// pairs [ceil(nb/2)][4][16] x 16 bytes, then the table: activation scales
+// [nb][16] fp32, then digit sums [nb][16] int32.
 constexpr int64_t xdig_table_offset(int64_t nb) { return (nb + 1) / 2 * 1024; }
 inline int64_t xfrag_bytes(int64_t K) { return xdig_table_offset(K / 32) + K / 32 * 128; }
 int attn_tiles(int n_seq, int nkv, int max_chunks);

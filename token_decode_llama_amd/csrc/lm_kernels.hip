@@ -482,9 +482,9 @@ typedef int v4i_t __attribute__((ext_vector_type(4)));
 //   digits [np][4 groups g][16 columns j] x 16 bytes: for the pair's two
 //     blocks, digit d of sequence s (column j = 3s+d) at the block's columns
 //     8g..8g+7, 8 bytes per block (the matrix-core B operand);
-//   table [nb][16 columns j] x 8 bytes (at byte np x 1024): the block's
-//     activation scale max|x_b| / (127 x 2^16) of sequence s (fp32 bits) and
-//     column j's digit sum over the block's 32 columns (int32).
+//   table (at byte np x 1024): the block's activation scale max|x_b| /
+//     (127 x 2^16) of sequence s per column j, fp32 [nb][16], then column j's
+//     digit sum over the block's 32 columns, int32 [nb][16].
 // Columns j >= 3 x n_seq are never read.
 // A thread per 8 columns, four consecutive threads per block, every input
 // loaded once.  With a gain (RMSNorm inputs) one workgroup covers the whole
@@ -499,7 +499,8 @@ __global__ __launch_bounds__(1024) void k_xdigits(const float* __restrict__ xin,
     const int nb = K >> 5;
     const float* x = xin + (int64_t)s * x_stride;
     uint2* dig = (uint2*)xb;
-    uint2* tab = (uint2*)(xb + xdig_table_offset(nb));
+    float* tsx = (float*)(xb + xdig_table_offset(nb));     // activation scales [nb][16]
+    int* tsum = (int*)(tsx + nb * 16);                     // digit sums [nb][16]
     // K % 32 == 0 and blockDim.x % 4 == 0: the four threads of a block are all in or all out
     const int c = blockIdx.x * blockDim.x + tid;    // 8 columns per thread
     const bool in = c < K / 8;
@@ -557,7 +558,10 @@ __global__ __launch_bounds__(1024) void k_xdigits(const float* __restrict__ xin,
         #pragma unroll
         for (int d = 0; d < 3; ++d) {
             dig[((int64_t)((b >> 1) * 4 + gq) * 16 + 3 * s + d) * 2 + (b & 1)] = make_uint2(w[d][0], w[d][1]);
-            if (gq == 0) tab[(int64_t)b * 16 + 3 * s + d] = make_uint2(sxb, (uint32_t)t[d]);
+            if (gq == 0) {
+                tsx[(int64_t)b * 16 + 3 * s + d] = __uint_as_float(sxb);
+                tsum[(int64_t)b * 16 + 3 * s + d] = t[d];
+            }
         }
     }
 }
@@ -576,14 +580,18 @@ static hipError_t launch_xdigits(const GemvArgs& a, int n_seq, hipStream_t st) {
     return hipGetLastError();
 }
 
-// Several-sequence GEMV: k_gemv_mfma<QT, EPI, W, T>.  A workgroup of W
+// Several-sequence GEMV: k_gemv_mfma<QT, EPI, W, T, PRO>.  A workgroup of W
 // wavefronts takes units of T consecutive 16-row tiles (grid-stride); its
 // wavefronts split K in whole pipeline stages of kMbDepth blocks and reduce
-// through LDS.  Per stage a lane loads its weight fragments (2 blocks per
-// 16 bytes for Q8_0, 4 for Q4_0, from the fragment copy: one contiguous 1 KiB
-// per wavefront and group), the scales of its D rows, and the activation
-// digit pairs, which serve all T tiles; each block's activation scale and
-// digit sum come from the table, staged in LDS once per workgroup.
+// through LDS.  The matrix op takes the activation digits as its first
+// operand (row = digit column 3s+d) and the weights as its second (column =
+// weight row), so a lane's four results are four digit columns of one weight
+// row, and each lane needs one weight scale per block.  Per stage a lane
+// loads its weight fragments (2 blocks per 16 bytes for Q8_0, 4 for Q4_0,
+// from the fragment copy: one contiguous 1 KiB per wavefront and group), its
+// row's 4 block scales (8 bytes), and the activation digit pairs, which serve
+// all T tiles; each block's activation scales and digit sums come from the
+// table, staged in LDS once per workgroup.
 // PRO (inputs of at most kProMaxK columns): no separate digit launch; every
 // workgroup computes the digit pairs and the table of all sequences into LDS
 // in its prologue, while its first weight loads are in flight, from x (times
@@ -598,6 +606,7 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
     // LDS: PRO: digit pairs [np][4][16] x 16 B, then the table; else the table only
     extern __shared__ __align__(16) uint4 xlds[];
     __shared__ __align__(16) float part[W][T][64][4];
+    __shared__ float ybuf[T][16][17];                       // wavefront 0's sums: (digit column, row)
     __shared__ float ss_red[W][4];                          // PRO: per-wavefront sums of squares
     __shared__ float wv_best[4][W];
     __shared__ int wi_best[4][W];
@@ -607,7 +616,6 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, j = lane & 15;
-    const int sq = min(j / 3, 3), dg = j - 3 * (j / 3);   // this lane's column: sequence, digit
     const int n_tiles = (N + 15) >> 4, n_units = (n_tiles + T - 1) / T;
     // each wavefront's K range is whole pipeline stages (kMbDepth blocks)
     const int nbq = ((nb + W - 1) / W + kMbDepth - 1) / kMbDepth * kMbDepth;
@@ -615,36 +623,33 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
     constexpr int PER = QT == kQ8_0 ? 2 : 4;        // blocks per 16-byte weight fragment
     constexpr int NW = kMbDepth / PER;               // weight fragments per stage and tile
     static_assert(kMbDepth % 4 == 0, "a stage is whole fragments of both formats and whole digit pairs");
-    const int ngrp = (nb + PER - 1) / PER, npair = (nb + 1) >> 1;
+    const int ngrp = (nb + PER - 1) / PER, npair = (nb + 1) >> 1, ng4 = (nb + 3) >> 2;
     const uint4* xd = (const uint4*)a.xfrag + (g * 16 + j);     // this lane's digit pairs, stride 64
     const uint2* xt = (const uint2*)(a.xfrag + xdig_table_offset(nb));
     uint2* xtab = (uint2*)(PRO ? (uint8_t*)xlds + xdig_table_offset(nb) : (uint8_t*)xlds);
+    const float* xsx = (const float*)xtab;                       // LDS table: scales, then digit sums
+    const int* xsum = (const int*)(xsx + nb * 16);
     const uint4* xdl = xlds + (g * 16 + j);                      // PRO: digit pairs in LDS, stride 64
 
     float best_v = -FLT_MAX;
     int best_i = INT_MAX;
 
     struct Stage {
-        uint4 w[T][NW];              // weight fragments (A operands of kMbDepth blocks) per tile
-        uint2 sc[T][kMbDepth];       // scales of this lane's D rows per tile and block
-        uint4 x[PRO ? 1 : kMbDepth / 2];   // B operands: digit pairs of this lane's column (PRO: LDS)
+        uint4 w[T][NW];              // weight fragments (kMbDepth blocks of this lane's row) per tile
+        uint2 sc[T];                 // this lane's row's scales of the kMbDepth blocks, per tile
+        uint4 x[PRO ? 1 : kMbDepth / 2];   // digit pairs of this lane's digit column (PRO: LDS)
     };
     auto load = [&](int unit, int b0, Stage& st) {
         #pragma unroll
         for (int t = 0; t < T; ++t) {
             const int tile = min(unit * T + t, n_tiles - 1);      // clamped: always in bounds
             const uint4* qf = (const uint4*)a.w.qf + (int64_t)tile * ngrp * 64 + lane;
-            const uint16_t* sct = a.w.sct + (int64_t)tile * nb * 16 + 4 * g;
             #pragma unroll
             for (int f = 0; f < NW; ++f) {
                 const int grp = min(b0 / PER + f, ngrp - 1);
                 st.w[t][f] = qf[(int64_t)grp * 64];
             }
-            #pragma unroll
-            for (int u = 0; u < kMbDepth; ++u) {
-                const int b = min(b0 + u, b_hi - 1);
-                st.sc[t][u] = *(const uint2*)(sct + (int64_t)b * 16);
-            }
+            st.sc[t] = *(const uint2*)(a.w.sct + (((int64_t)tile * ng4 + (b0 >> 2)) * 16 + j) * 4);
         }
         if (!PRO) {
             #pragma unroll
@@ -660,9 +665,11 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
         for (int u = 0; u < kMbDepth; ++u) {
             if (b0 + u >= b_hi) break;
             const uint4 xp = PRO ? xdl[((b0 + u) >> 1) * 64] : st.x[PRO ? 0 : (u >> 1)];
-            const long bv = (u & 1) ? (long)(((uint64_t)xp.w << 32) | xp.z) : (long)(((uint64_t)xp.y << 32) | xp.x);
-            const uint2 tb = xtab[(b0 + u) * 16 + j];
-            const float sx = __uint_as_float(tb.x);
+            const long xv = (u & 1) ? (long)(((uint64_t)xp.w << 32) | xp.z) : (long)(((uint64_t)xp.y << 32) | xp.x);
+            // activation scales (and digit sums) of this lane's four result columns 4g..4g+3
+            const float4 sx = *(const float4*)&xsx[(b0 + u) * 16 + 4 * g];
+            int4 ts = make_int4(0, 0, 0, 0);
+            if (QT == kQ4_0) ts = *(const int4*)&xsum[(b0 + u) * 16 + 4 * g];
             #pragma unroll
             for (int t = 0; t < T; ++t) {
                 uint2 wa;
@@ -675,19 +682,22 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
                     const uint32_t q = u == 0 ? f.x : u == 1 ? f.y : u == 2 ? f.z : f.w;
                     wa = make_uint2(q & 0x0F0F0F0Fu, (q >> 4) & 0x0F0F0F0Fu);
                 }
-                const long av = (long)(((uint64_t)wa.y << 32) | wa.x);
+                const long wv = (long)(((uint64_t)wa.y << 32) | wa.x);
                 v4i_t c = {0, 0, 0, 0};
-                c = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, bv, c, 0, 0, 0);
-                if (QT == kQ4_0) {
-                    const int t8 = 8 * (int)tb.y;            // nibble n = q + 8
-                    #pragma unroll
-                    for (int i = 0; i < 4; ++i) c[i] -= t8;
+                c = __builtin_amdgcn_mfma_i32_16x16x32_i8(xv, wv, c, 0, 0, 0);
+                if (QT == kQ4_0) {                           // nibble n = q + 8
+                    c[0] -= 8 * ts.x;
+                    c[1] -= 8 * ts.y;
+                    c[2] -= 8 * ts.z;
+                    c[3] -= 8 * ts.w;
                 }
-                const uint2 sc = st.sc[t][u];
-                acc[t][0] = fmaf(h2f((uint16_t)(sc.x & 0xFFFF)) * sx, (float)c[0], acc[t][0]);
-                acc[t][1] = fmaf(h2f((uint16_t)(sc.x >> 16)) * sx, (float)c[1], acc[t][1]);
-                acc[t][2] = fmaf(h2f((uint16_t)(sc.y & 0xFFFF)) * sx, (float)c[2], acc[t][2]);
-                acc[t][3] = fmaf(h2f((uint16_t)(sc.y >> 16)) * sx, (float)c[3], acc[t][3]);
+                const uint2 sc = st.sc[t];
+                const float d = h2f((uint16_t)(u == 0 ? (sc.x & 0xFFFF) : u == 1 ? (sc.x >> 16)
+                                                : u == 2 ? (sc.y & 0xFFFF) : (sc.y >> 16)));
+                acc[t][0] = fmaf(d * sx.x, (float)c[0], acc[t][0]);
+                acc[t][1] = fmaf(d * sx.y, (float)c[1], acc[t][1]);
+                acc[t][2] = fmaf(d * sx.z, (float)c[2], acc[t][2]);
+                acc[t][3] = fmaf(d * sx.w, (float)c[3], acc[t][3]);
             }
         }
     };
@@ -773,7 +783,10 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
                 #pragma unroll
                 for (int d = 0; d < 3; ++d) {
                     dig[(((b >> 1) * 4 + gq) * 16 + 3 * sI + d) * 2 + (b & 1)] = make_uint2(w[d][0], w[d][1]);
-                    if (gq == 0) xtab[b * 16 + 3 * sI + d] = make_uint2(sxb, (uint32_t)tq[d]);
+                    if (gq == 0) {
+                        ((float*)xtab)[b * 16 + 3 * sI + d] = __uint_as_float(sxb);
+                        ((int*)xtab)[nb * 16 + b * 16 + 3 * sI + d] = tq[d];
+                    }
                 }
             }
         }
@@ -805,10 +818,13 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
     // PRO with a gain: RMSNorm factor of each sequence, applied to the finished sums
+    // the epilogue lane (sequence es = lane / 16, tile row er = lane % 16; even
+    // rows take a row pair); PRO with a gain: that sequence's RMSNorm factor
+    const int es = g, er = j;
     float rms = 1.f;
     if (PRO && a.norm_g) {
         float tot = 0.f;
-        for (int w = 0; w < W; ++w) tot += ss_red[w][sq];
+        for (int w = 0; w < W; ++w) tot += ss_red[w][es];
         rms = 1.0f / sqrtf(tot / (float)K + a.eps);
     }
     for (; unit < n_units; unit += gridDim.x) {
@@ -837,29 +853,34 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
         for (int t = 0; t < T; ++t)
             *(float4*)&part[wave][t][lane][0] = make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
         __syncthreads();
-        #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const int tile = unit * T + t;
-            float y[4] = {0.f, 0.f, 0.f, 0.f};
-            if (wave == 0) {
+        if (wave == 0) {
+            // sum over the wavefronts; result i of lane (g, j) is digit column 4g+i of row j
+            #pragma unroll
+            for (int t = 0; t < T; ++t) {
+                float y[4] = {0.f, 0.f, 0.f, 0.f};
                 #pragma unroll
                 for (int w = 0; w < W; ++w) {
                     const float4 v = *(const float4*)&part[w][t][lane][0];
                     y[0] += v.x; y[1] += v.y; y[2] += v.z; y[3] += v.w;
                 }
-                // a sequence's three digit columns sit in lanes j, j+1, j+2 of the group
                 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float y1 = __shfl(y[i], lane + 1, 64), y2 = __shfl(y[i], lane + 2, 64);
-                    y[i] = fmaf(y2, 65536.0f, fmaf(y1, 256.0f, y[i]));
-                }
+                for (int i = 0; i < 4; ++i) ybuf[t][4 * g + i][j] = y[i];
             }
-            if (wave == 0 && dg == 0 && j < 3 * a.n_seq && tile < n_tiles) {
-                const int s = sq;
-                #pragma unroll
-                for (int pr = 0; pr < 2; ++pr) {
-                    const int r0 = tile * 16 + 4 * g + 2 * pr;   // rows r0, r0 + 1 (a RoPE / gate-up pair)
-                    const float y0 = y[2 * pr] * rms, y1 = y[2 * pr + 1] * rms;
+            // (one wavefront writes and reads ybuf: its LDS operations stay in order)
+        }
+        #pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const int tile = unit * T + t;
+            if (wave == 0 && es < a.n_seq && (er & 1) == 0 && tile < n_tiles) {
+                const int s = es;
+                {
+                    // a sequence's three digit columns 3s, 3s+1, 3s+2: 2^16 D2 + 2^8 D1 + D0
+                    const float* c0 = &ybuf[t][3 * s][0];
+                    const float* c1 = &ybuf[t][3 * s + 1][0];
+                    const float* c2 = &ybuf[t][3 * s + 2][0];
+                    const int r0 = tile * 16 + er;               // rows r0, r0 + 1 (a RoPE / gate-up pair)
+                    const float y0 = fmaf(c2[er], 65536.0f, fmaf(c1[er], 256.0f, c0[er])) * rms;
+                    const float y1 = fmaf(c2[er + 1], 65536.0f, fmaf(c1[er + 1], 256.0f, c0[er + 1])) * rms;
                     if (EPI == EPI_QKV) {
                         const int p = a.pos[s];
                         const int hd = a.head_dim;
@@ -909,19 +930,19 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
     }
 
     if (EPI == EPI_LOGITS) {
-        // sequence s's candidates sit in lanes 3s, 3s+16, 3s+32, 3s+48 of wavefront 0
+        // sequence s's candidates sit in lanes 16s .. 16s+15 of wavefront 0
         if (wave == 0) {
             float bv = best_v;
             int bi = best_i;
             #pragma unroll
-            for (int off = 16; off < 64; off <<= 1) {
+            for (int off = 1; off < 16; off <<= 1) {
                 const float ov = __shfl_xor(bv, off, 64);
                 const int oi = __shfl_xor(bi, off, 64);
                 better(bv, bi, ov, oi);
             }
-            if (g == 0 && dg == 0 && j < 3 * a.n_seq) {
-                a.part_val[(int64_t)sq * gridDim.x + blockIdx.x] = bv;
-                a.part_idx[(int64_t)sq * gridDim.x + blockIdx.x] = bi;
+            if (er == 0 && es < a.n_seq) {
+                a.part_val[(int64_t)es * gridDim.x + blockIdx.x] = bv;
+                a.part_idx[(int64_t)es * gridDim.x + blockIdx.x] = bi;
             }
         }
         __syncthreads();

@@ -53,7 +53,9 @@ struct MatOff {
 };
 
 // bytes of a tile-transposed scale plane
-inline int64_t sct_bytes(int64_t N, int64_t K) { return (N + 15) / 16 * 16 * (K / 32) * 2; }
+// scales for the matrix-core GEMV: [N/16 tiles][ceil(nb/4) groups][16 rows][4 blocks] fp16
+// (zero past the last row and block): a row's scales of one 4-block stage are 8 contiguous bytes
+inline int64_t sct_bytes(int64_t N, int64_t K) { return (N + 15) / 16 * ((K / 32 + 3) / 4) * 64 * 2; }
 
 template <class F>
 void parallel_rows(int64_t n, F&& fn) {
@@ -690,33 +692,31 @@ static lm_status upload_matrix(lm_model* m, int N, int K, RowFn src_row, uint8_t
     return LM_OK;
 }
 
-// The tile-transposed copy of a matrix's block scales used by the MFMA path:
-// dst[t][b][i] = scale of row 16t+i, block b (zero past the last row).
+// The grouped copy of a matrix's block scales used by the MFMA path:
+// dst[t][b/4][i][b%4] = scale of row 16t+i, block b (zero past the last row and block).
 template <class RowFn>
 static lm_status upload_sct(lm_model* m, int N, int K, RowFn src_row, uint16_t* dst, bool dst_host) {
-    const int64_t nb = K / 32, tiles = (N + 15) / 16, bb = block_bytes(m->cfg.qtype);
+    const int64_t nb = K / 32, tiles = (N + 15) / 16, bb = block_bytes(m->cfg.qtype), ng = (nb + 3) / 4;
+    const int64_t n = sct_bytes(N, K) / 2;
     std::vector<uint16_t> tmp;
     uint16_t* t = dst;
     if (!dst_host) {
-        tmp.assign((size_t)(tiles * nb * 16), 0);
+        tmp.assign((size_t)n, 0);
         t = tmp.data();
+    } else {
+        std::memset(t, 0, (size_t)n * 2);
     }
     parallel_rows(tiles, [&](int64_t a, int64_t b) {
         for (int64_t tile = a; tile < b; ++tile)
             for (int i = 0; i < 16; ++i) {
                 const int64_t r = tile * 16 + i;
-                uint16_t* col = t + tile * nb * 16 + i;
-                if (r >= N) {
-                    for (int64_t k = 0; k < nb; ++k) col[k * 16] = 0;
-                    continue;
-                }
+                if (r >= N) continue;
                 const uint8_t* src = src_row(r);
                 for (int64_t k = 0; k < nb; ++k)
-                    col[k * 16] = (uint16_t)(src[k * bb] | (src[k * bb + 1] << 8));
+                    t[((tile * ng + k / 4) * 16 + i) * 4 + k % 4] = (uint16_t)(src[k * bb] | (src[k * bb + 1] << 8));
             }
     });
-    if (!dst_host)
-        HIPTRY(m, hipMemcpy(dst, t, (size_t)(tiles * nb * 16 * 2), hipMemcpyHostToDevice));
+    if (!dst_host) HIPTRY(m, hipMemcpy(dst, t, (size_t)n * 2, hipMemcpyHostToDevice));
     return LM_OK;
 }
 
