@@ -832,9 +832,10 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
         for (int t = 0; t < T; ++t)
             #pragma unroll
             for (int i = 0; i < 4; ++i) acc[t][i] = 0.f;
-        // two stages in flight: the next stage's loads are issued before this one computes
+        // two stages in flight: the next stage's loads are issued before this one
+        // computes.  The unit's first stage is already in `sa` (requested before
+        // the prologue, or at the end of the previous unit's K loop).
         if (b_lo < b_hi) {
-            if (unit != (int)blockIdx.x) load(unit, b_lo, sa);
             int b0 = b_lo;
             for (;;) {
                 const bool more = b0 + kMbDepth < b_hi;
@@ -848,6 +849,8 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
                 b0 += kMbDepth;
                 if (!more2) break;
             }
+            // the next unit's first stage streams in during this unit's epilogue
+            if (unit + (int)gridDim.x < n_units) load(unit + gridDim.x, b_lo, sa);
         }
         #pragma unroll
         for (int t = 0; t < T; ++t)
