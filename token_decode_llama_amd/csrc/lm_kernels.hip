@@ -1463,10 +1463,9 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
         reinterpret_cast<float (*)[6]>(&Ks[0][0]));
 }
 
-// Tiles per attention workgroup: one, unless the one-tile grid would hold at
-// least eight workgroups per CU; then two (four from sixteen), so that fewer
-// partial states are merged and each workgroup's next tile loads while it
-// computes.
+// Tiles per attention workgroup: one, unless the grid would hold more than
+// about four workgroups per CU; then up to four, so that fewer partial
+// states are merged and each workgroup's next tile loads while it computes.
 int attn_tiles(int n_seq, int nkv, int max_chunks) {
     const int64_t wgs = (int64_t)n_seq * nkv * max_chunks, per = 4ll * device_cus();
     return wgs >= 4 * per ? 4 : wgs >= 2 * per ? 2 : 1;
