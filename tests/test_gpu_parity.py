@@ -373,6 +373,33 @@ def test_hybrid_residency_bit_identical(name, plan):
         g.close()
 
 
+@pytest.mark.parametrize("name", ["llama1b_2layers", "llama8b_q8_2layers_ctx127"])
+def test_long_cache_short_context_bit_identical(name):
+    """A cache far longer than the context: the attention grid follows the
+    context (64-position chunks up to the next power of two), so the outputs
+    equal those of a model whose cache ends at the context, bit for bit."""
+    import token_decode_llama_amd as lm
+    model = get_model(name)
+    cfg = model.cfg
+    toks = synth.start_tokens(cfg, 1)
+    outs = []
+    for max_ctx in (cfg.max_ctx, 8192):
+        g = lm.open_model(model, lambda s, l: synth.make_kv(cfg, s, l), max_seqs=1, max_ctx=max_ctx)
+        try:
+            g.set_persistent(False)
+            g.set_dataflow(False)
+            res, t = [], toks
+            for _ in range(cfg.steps):
+                lg, am = g.step(t)
+                res.append((lg.copy(), am.copy()))
+                t = am
+            outs.append(res)
+        finally:
+            g.close()
+    for (a, b), (c, d) in zip(*outs):
+        assert np.array_equal(a, c) and np.array_equal(b, d)
+
+
 def test_state_and_context_errors():
     import token_decode_llama_amd as lm
     cfg = CASES["tiny_q8"]

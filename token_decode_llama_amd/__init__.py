@@ -303,13 +303,14 @@ class Model:
 
 
 def open_model(model, kv_fn, max_seqs: int | None = None, kv_seqs: int | None = None,
-               stream: int | None = None) -> Model:
+               stream: int | None = None, max_ctx: int | None = None) -> Model:
     """Creates an lm_model for a model object (cfg, layers, tok_embd, out_norm,
     lm_head), loads its weights, and installs the cache that kv_fn(seq, layer)
     returns (fp16 bits [n_kv, n_pos, hd] for K and V) for sequences
-    0..kv_seqs-1 (default max_seqs)."""
+    0..kv_seqs-1 (default max_seqs).  max_ctx: cache positions (default the
+    config's ctx + steps)."""
     cfg = model.cfg
-    m = Model(cfg, max_seqs=max_seqs, stream=stream)
+    m = Model(cfg, max_seqs=max_seqs, max_ctx=max_ctx, stream=stream)
     m.load_model(model)
     n = kv_seqs if kv_seqs is not None else m.c.max_seqs
     for s in range(n):

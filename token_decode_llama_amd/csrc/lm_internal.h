@@ -91,6 +91,7 @@ struct AttnArgs {
     const int* pos;
     int nq, nkv, hd, max_ctx, max_chunks;
     float scale;           // 1/sqrt(hd)
+    int grid_chunks;       // chunks the grid covers (<= max_chunks; >= every sequence's context)
     int tiles;             // kAttnChunk-position tiles per workgroup (attn_tiles)
     float* part;           // [n_seq][nq][max_chunks][hd + 2] partial o, m, l (one record per workgroup)
     int* counter;          // [n_seq][nkv][attn_cnt_lines][kCntStride] chunk counts (first int of

@@ -1463,9 +1463,10 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
         reinterpret_cast<float (*)[6]>(&Ks[0][0]));
 }
 
-// Tiles per attention workgroup: one, unless the grid would hold more than
-// about four workgroups per CU; then up to four, so that fewer partial
-// states are merged and each workgroup's next tile loads while it computes.
+// Tiles per attention workgroup: one, unless the one-tile grid would hold at
+// least eight workgroups per CU; then two (four from sixteen), so that fewer
+// partial states are merged and each workgroup's next tile loads while it
+// computes.
 int attn_tiles(int n_seq, int nkv, int max_chunks) {
     const int64_t wgs = (int64_t)n_seq * nkv * max_chunks, per = 4ll * device_cus();
     return wgs >= 4 * per ? 4 : wgs >= 2 * per ? 2 : 1;
@@ -1474,7 +1475,8 @@ int attn_tiles(int n_seq, int nkv, int max_chunks) {
 hipError_t launch_attention(const AttnArgs& a, int n_seq, hipStream_t st) {
     if (a.tiles != 1 && a.tiles != 2 && a.tiles != 4) return hipErrorInvalidValue;
     if (a.hd != 128 && a.hd != 64) return hipErrorInvalidValue;
-    dim3 grid((a.max_chunks + a.tiles - 1) / a.tiles, a.nkv, n_seq);
+    if (a.grid_chunks < 1 || a.grid_chunks > a.max_chunks) return hipErrorInvalidValue;
+    dim3 grid((a.grid_chunks + a.tiles - 1) / a.tiles, a.nkv, n_seq);
     if (a.hd == 128) {
         if (a.tiles == 1) hipLaunchKernelGGL((k_attn1<128>), grid, dim3(kBlock), 0, st, a);
         else if (a.tiles == 2) hipLaunchKernelGGL((k_attn<128, 2>), grid, dim3(kBlock), 0, st, a);

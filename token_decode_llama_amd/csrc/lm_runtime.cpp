@@ -176,6 +176,7 @@ struct lm_model {
     struct Pending { int kind; hipEvent_t a, b; };
     struct GraphEntry {
         int n_seq;
+        int chunks;                       // attention grid (attn_grid_chunks at capture)
         const int* tok;
         float* logits;
         int* argmax;
@@ -1121,6 +1122,20 @@ static lm_status collect_timing(lm_model* m) {
     return LM_OK;
 }
 
+// Attention grid of a step: 64-position chunks up to the next power of two
+// of the longest context among the stepping sequences (at most max_chunks),
+// so a launch does not read the whole cache when the context is short.  A
+// step graph is keyed by it: a context crossing a power of two takes a new
+// graph.
+static int attn_grid_chunks(const lm_model* m, int n_seq) {
+    int need = 1;
+    for (int s = 0; s < n_seq; ++s) need = std::max(need, m->pos[s] + 1);
+    const int tiles = (need + kAttnChunk - 1) / kAttnChunk;
+    int c = 1;
+    while (c < tiles) c *= 2;
+    return std::min(c, m->max_chunks);
+}
+
 static const uint8_t* layer_blob(lm_model* m, int l) {
     return layer_streamed(m, l) ? m->d_sbuf[stream_slot(m, l)] : m->d_layers + (int64_t)l * m->blob_bytes;
 }
@@ -1210,7 +1225,8 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
     at.max_ctx = c.max_ctx;
     at.max_chunks = m->max_chunks;
     at.scale = (float)(1.0 / std::sqrt((double)m->hd));
-    at.tiles = attn_tiles(n_seq, (int)m->nkv, m->max_chunks);
+    at.grid_chunks = attn_grid_chunks(m, n_seq);
+    at.tiles = attn_tiles(n_seq, (int)m->nkv, at.grid_chunks);
     at.part = m->d_attn_part;
     at.counter = m->d_attn_cnt;
     at.out = m->d_o;
@@ -1316,8 +1332,10 @@ static lm_status launch_graph(lm_model* m, const lm_model::GraphEntry& g) {
 static lm_status run_step(lm_model* m, int n_seq, const int* d_tok, float* d_logits, int* d_argmax) {
     const bool graph_ok = m->use_graph && m->timing != 1 && !m->streaming;
     if (!graph_ok) return enqueue_step(m, n_seq, d_tok, d_logits, d_argmax);
+    const int chunks = attn_grid_chunks(m, n_seq);
     for (auto& g : m->graphs)
-        if (g.n_seq == n_seq && g.tok == d_tok && g.logits == d_logits && g.argmax == d_argmax)
+        if (g.n_seq == n_seq && g.chunks == chunks && g.tok == d_tok && g.logits == d_logits &&
+            g.argmax == d_argmax)
             return launch_graph(m, g);
     lm_status cs = collect_timing(m);
     if (cs != LM_OK) return cs;
@@ -1352,7 +1370,7 @@ static lm_status run_step(lm_model* m, int n_seq, const int* d_tok, float* d_log
         for (hipEvent_t ev : m->graphs.front().owned) (void)hipEventDestroy(ev);
         m->graphs.erase(m->graphs.begin());
     }
-    m->graphs.push_back({n_seq, d_tok, d_logits, d_argmax, exec, std::move(timers), std::move(owned)});
+    m->graphs.push_back({n_seq, chunks, d_tok, d_logits, d_argmax, exec, std::move(timers), std::move(owned)});
     return launch_graph(m, m->graphs.back());
 }
 
