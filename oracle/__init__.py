@@ -78,6 +78,9 @@ def lib():
             "orc_model_set_position": ([vp, i32, i64], i32),
             "orc_model_position": ([vp, i32], i64),
             "orc_decode_step": ([vp, vp, i32, vp, vp], i32),
+            "orc_decode_step_ex": ([vp, vp, i32, vp, vp, vp, vp], i32),
+            "orc_cosine": ([vp, vp, i64], f64),
+            "orc_skip_list": ([vp, i32, f64, vp], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -165,6 +168,18 @@ def attention(q, K: np.ndarray, V: np.ndarray, n_heads: int, n_kv: int, head_dim
     return out
 
 
+def cosine(a, b) -> float:
+    a, b = _c64(a), _c64(b)
+    return float(lib().orc_cosine(_p(a), _p(b), a.size))
+
+
+def skip_list(mean_cos, threshold: float) -> np.ndarray:
+    m = _c64(mean_cos)
+    mask = np.zeros(m.size, np.uint8)
+    lib().orc_skip_list(_p(m), m.size, float(threshold), _p(mask))
+    return mask
+
+
 def argmax_f32(v) -> int:
     v = _c64(v)
     return int(lib().orc_argmax_f32(_p(v), v.size))
@@ -234,12 +249,17 @@ class OracleModel:
     def position(self, seq: int) -> int:
         return int(lib().orc_model_position(self._h, seq))
 
-    def step(self, tokens):
-        """One decode step; returns (fp64 logits [n_seq, vocab], argmax [n_seq])."""
+    def step(self, tokens, skip=None, with_cos: bool = False):
+        """One decode step; returns (fp64 logits [n_seq, vocab], argmax [n_seq]),
+        plus the per-layer input/output cosine similarities [n_seq, n_layers]
+        with with_cos.  skip: [n_layers] mask of skipped layers."""
         t = np.ascontiguousarray(tokens, dtype=np.int32)
         n = t.size
         logits = np.empty((n, self.cfg.vocab), np.float64)
         am = np.empty(n, np.int32)
-        if lib().orc_decode_step(self._h, _p(t), n, _p(logits), _p(am)) != 0:
+        sk = None if skip is None else np.ascontiguousarray(skip, dtype=np.uint8)
+        cos = np.empty((n, self.cfg.n_layers), np.float64) if with_cos else None
+        if lib().orc_decode_step_ex(self._h, _p(t), n, _p(logits), _p(am),
+                                    None if sk is None else _p(sk), None if cos is None else _p(cos)) != 0:
             raise ValueError("oracle decode step rejected its arguments")
-        return logits, am
+        return (logits, am, cos) if with_cos else (logits, am)

@@ -25,6 +25,11 @@
  *             cache size n_layers * n_head_kv * n_ctx * head_dim * dtype * 2;
  *             section 4 step 4 says decode positions continue from the end of
  *             the prefix, or RoPE goes wrong.
+ *   [ENGINE] sections 2.5, 3.5 and 4.5 (layer skip): a layer whose output is
+ *             close to its input, by the cosine similarity of the two hidden
+ *             vectors against a threshold (0.98 by default), is skipped and its
+ *             input passed on; section 3.5 calibrates the similarities ahead
+ *             of time.
  * The block formats are the ones the workload states: Q8_0 = fp16 d then 32
  * int8 q, value d*q; Q4_0 = fp16 d then 16 bytes, byte j = element j (low
  * nibble) | element j+16 (high nibble), value (nibble - 8) * d.
@@ -38,7 +43,12 @@
  *   scale 1/sqrt(hd), keys 0..pos inclusive; query head h reads KV head
  *   floor(h / (n_heads / n_kv_heads)); RMSNorm x / sqrt(mean(x^2) + eps) * g;
  *   no biases; the LM head is its own quantised matrix; argmax picks the
- *   first index of the largest fp32-rounded logit.
+ *   first index of the largest fp32-rounded logit.  Layer skip: a skipped
+ *   layer computes nothing and writes no cache row (its input is its output);
+ *   a layer's similarity is the cosine of its input and output residual
+ *   vectors (0 when either is zero); the calibrated list skips a layer when
+ *   its similarity, averaged over the calibration steps and sequences, is
+ *   above the threshold.
  *
  * parity pins: see tests/test_oracle_pins.py (every function here has one).
  */
@@ -220,6 +230,18 @@ void orc_attention(const double* q, const uint16_t* K, const uint16_t* V, int nq
 }
 
 /* First index of the largest value after rounding each to fp32. */
+/* Cosine similarity a.b / (|a| |b|) in fp64; 0 when either vector is zero. */
+double orc_cosine(const double* a, const double* b, int64_t n) {
+    double ab = 0.0, aa = 0.0, bb = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        ab += a[i] * b[i];
+        aa += a[i] * a[i];
+        bb += b[i] * b[i];
+    }
+    if (aa == 0.0 || bb == 0.0) return 0.0;
+    return ab / (sqrt(aa) * sqrt(bb));
+}
+
 int32_t orc_argmax_f32(const double* v, int64_t n) {
     int32_t best = 0;
     float bv = (float)v[0];
@@ -330,9 +352,13 @@ int64_t orc_model_position(const orc_model* m, int s) { return m->pos[s]; }
 /*
  * One decode step for n_seq independent sequences (sequence s reads token
  * tokens[s] at position pos[s]).  logits: fp64 [n_seq][vocab] (nullable);
- * argmax: [n_seq].  Returns 0, or -1 on a bad argument / full context.
+ * argmax: [n_seq].  skip: [n_layers] nonzero = layer skipped (nullable);
+ * cos: [n_seq][n_layers] cosine similarity of each computed layer's input and
+ * output (nullable; skipped layers get 0).  Returns 0, or -1 on a bad
+ * argument / full context.
  */
-int orc_decode_step(orc_model* m, const int32_t* tokens, int n_seq, double* logits, int32_t* argmax) {
+int orc_decode_step_ex(orc_model* m, const int32_t* tokens, int n_seq, double* logits, int32_t* argmax,
+                       const uint8_t* skip, double* cos) {
     const orc_config* c = &m->c;
     const int H = c->hidden, nq = c->n_heads, nkv = c->n_kv_heads, hd = c->head_dim, F = c->ffn;
     if (n_seq < 1 || n_seq > c->max_seqs) return -1;
@@ -350,12 +376,16 @@ int orc_decode_step(orc_model* m, const int32_t* tokens, int n_seq, double* logi
     double* a = (double*)malloc(sizeof(double) * F);
     double* b = (double*)malloc(sizeof(double) * F);
     double* lg = (double*)malloc(sizeof(double) * c->vocab);
+    double* xin = (double*)malloc(sizeof(double) * H);
     int qt = c->qtype;
     for (int s = 0; s < n_seq; ++s) {
         const int64_t p = m->pos[s];
         /* embedding lookup: fp16 row -> fp64 (exact) */
         for (int i = 0; i < H; ++i) x[i] = orc_f16_to_f64(m->tok_embd[(int64_t)tokens[s] * H + i]);
         for (int l = 0; l < c->n_layers; ++l) {
+            if (cos) cos[(int64_t)s * c->n_layers + l] = 0.0;
+            if (skip && skip[l]) continue;               /* the layer's input is its output */
+            memcpy(xin, x, sizeof(double) * H);
             const orc_layer* L = &m->layers[l];
             uint16_t* Kc = m->kcache + kv_index(m, s, l);
             uint16_t* Vc = m->vcache + kv_index(m, s, l);
@@ -381,6 +411,7 @@ int orc_decode_step(orc_model* m, const int32_t* tokens, int n_seq, double* logi
             for (int i = 0; i < F; ++i) a[i] = orc_silu(a[i]) * b[i];
             orc_gemv(qt, L->w_down, H, F, a, y);
             for (int i = 0; i < H; ++i) x[i] += y[i];
+            if (cos) cos[(int64_t)s * c->n_layers + l] = orc_cosine(xin, x, H);
         }
         orc_rmsnorm(x, m->out_norm, H, c->rms_eps, xn);
         orc_gemv(qt, m->lm_head, c->vocab, H, xn, lg);
@@ -388,6 +419,20 @@ int orc_decode_step(orc_model* m, const int32_t* tokens, int n_seq, double* logi
         argmax[s] = orc_argmax_f32(lg, c->vocab);
         m->pos[s] = p + 1;
     }
-    free(x); free(xn); free(q); free(k); free(v); free(o); free(y); free(a); free(b); free(lg);
+    free(x); free(xn); free(q); free(k); free(v); free(o); free(y); free(a); free(b); free(lg); free(xin);
     return 0;
+}
+
+int orc_decode_step(orc_model* m, const int32_t* tokens, int n_seq, double* logits, int32_t* argmax) {
+    return orc_decode_step_ex(m, tokens, n_seq, logits, argmax, NULL, NULL);
+}
+
+/* The calibrated skip list: mask[l] = 1 when mean_cos[l] > threshold. */
+int orc_skip_list(const double* mean_cos, int n_layers, double threshold, uint8_t* mask) {
+    int n = 0;
+    for (int l = 0; l < n_layers; ++l) {
+        mask[l] = mean_cos[l] > threshold;
+        n += mask[l];
+    }
+    return n;
 }

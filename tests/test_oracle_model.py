@@ -226,3 +226,85 @@ def test_generator_distributions():
     W = _numpy_dequant(Q8_0, blocks, 64, 256)
     assert abs(W.std() - 0.02) < 0.001
     assert cfg.max_ctx == 20
+
+
+# ---------------------------------------------------------------------------
+# layer skip (the C/CUDA Llama engine page, sections 2.5, 3.5 and 4.5)
+# ---------------------------------------------------------------------------
+
+def test_oracle_cosine_properties():
+    rng = np.random.default_rng(7)
+    a = rng.standard_normal(97)
+    b = rng.standard_normal(97)
+    assert oracle.cosine(a, a) == pytest.approx(1.0, abs=1e-15)
+    assert oracle.cosine(a, -a) == pytest.approx(-1.0, abs=1e-15)
+    assert oracle.cosine(a, 3.0 * a) == pytest.approx(1.0, abs=1e-15)          # scale invariance
+    assert oracle.cosine(a, b) == pytest.approx(oracle.cosine(b, a), abs=0)       # symmetry
+    assert abs(oracle.cosine(a, b)) <= 1.0                                       # Cauchy-Schwarz
+    assert oracle.cosine([1.0, 0.0], [0.0, 2.0]) == 0.0                          # orthogonal
+    assert oracle.cosine([1.0, 0.0], [1.0, 3.0 ** 0.5]) == pytest.approx(0.5, abs=1e-15)   # 60 degrees
+    assert oracle.cosine([0.0, 0.0], [1.0, 2.0]) == 0.0                          # zero vector: 0
+
+
+def test_oracle_skip_list_is_strictly_above():
+    mask = oracle.skip_list([0.5, 0.98, 0.99, 0.981, float("nan")], 0.98)
+    assert mask.tolist() == [0, 0, 1, 1, 0]
+
+
+def test_skip_all_layers_closed_form():
+    """Every layer skipped: the residual stream stays E[tok], so the logits are
+    W_lm * rmsnorm(E[tok]) * g_out (the same closed form as zero W_o, W_down)."""
+    cfg = synth.variant("tiny", qtype=Q4_0)
+    model = synth.make_model(cfg)
+    om = _load_oracle(model)
+    tok = int(synth.start_tokens(cfg)[0])
+    logits, am, cos = om.step([tok], skip=np.ones(cfg.n_layers, np.uint8), with_cos=True)
+    e = model.tok_embd[tok].view(np.float16).astype(np.float64)
+    xf = torch.nn.functional.rms_norm(torch.from_numpy(e), (cfg.hidden,),
+                                      weight=torch.from_numpy(model.out_norm.astype(np.float64)),
+                                      eps=cfg.rms_eps).numpy()
+    expect = _numpy_dequant(cfg.qtype, model.lm_head, cfg.vocab, cfg.hidden) @ xf
+    assert np.allclose(logits[0], expect, rtol=1e-12, atol=1e-14)
+    assert np.all(cos == 0.0)
+    # no cache row written by a skipped layer
+    k, v = om.get_kv(0, 0, cfg.ctx + 1)
+    assert np.all(k[:, cfg.ctx] == 0) and np.all(v[:, cfg.ctx] == 0)
+
+
+def test_skip_equals_model_without_that_layer():
+    """Skipping layer 1 of three is the two-layer model made of layers 0 and 2
+    (with their caches), exactly; each computed layer's similarity is the same
+    number in both."""
+    cfg3 = synth.variant("tiny", n_layers=3)
+    m3 = synth.make_model(cfg3)
+    cfg2 = synth.variant("tiny", n_layers=2)
+    m2 = synth.Model(cfg=cfg2, tok_embd=m3.tok_embd, out_norm=m3.out_norm, lm_head=m3.lm_head,
+                     layers=[m3.layers[0], m3.layers[2]])
+    o3 = oracle.OracleModel(m3, max_seqs=2)
+    o2 = oracle.OracleModel(m2, max_seqs=2)
+    for s in range(2):
+        for l in range(3):
+            o3.load_kv(s, l, *synth.make_kv(cfg3, s, l))
+        o2.load_kv(s, 0, *synth.make_kv(cfg3, s, 0))
+        o2.load_kv(s, 1, *synth.make_kv(cfg3, s, 2))
+    toks = synth.start_tokens(cfg3, 2)
+    skip = np.array([0, 1, 0], np.uint8)
+    for _ in range(3):
+        l3, a3, c3 = o3.step(toks, skip=skip, with_cos=True)
+        l2, a2, c2 = o2.step(toks, with_cos=True)
+        assert np.array_equal(l3, l2) and np.array_equal(a3, a2)
+        assert np.array_equal(c3[:, [0, 2]], c2) and np.all(c3[:, 1] == 0.0)
+        assert np.all(np.abs(c2) <= 1.0)
+        toks = a3
+
+
+def test_zero_update_layer_similarity_is_one():
+    """A layer with W_o = W_down = 0 passes its input through: similarity 1."""
+    cfg = synth.variant("tiny")
+    model = synth.make_model(cfg)
+    model.layers[1].wo[:] = 0
+    model.layers[1].w_down[:] = 0
+    om = _load_oracle(model)
+    _, _, cos = om.step(synth.start_tokens(cfg, 1), with_cos=True)
+    assert cos[0, 1] == pytest.approx(1.0, abs=1e-15)
+    assert cos[0, 0] < 1.0
