@@ -146,6 +146,34 @@ lm_status lm_get_position(const lm_model* m, int32_t seq, int32_t* pos);
  * memory; the model is unchanged), LM_E_HIP. */
 lm_status lm_set_residency(lm_model* m, int32_t n_resident);
 
+/* Layer skip (the C/CUDA Llama engine page, sections 2.5, 3.5 and 4.5: a
+ * layer whose output is close to its input is skipped; section 3.5 calibrates
+ * which).  mask: host uint8 [n_layers], nonzero = skip the layer; NULL clears
+ * the mask.  A skipped layer computes nothing and writes no KV-cache row: its
+ * input is its output.  In streaming mode skipped layers are not copied.  The
+ * one-launch and persistent step paths are not used while layers are skipped.
+ * Changing the mask mid-sequence leaves the skipped steps' cache rows of
+ * those layers unwritten.  Legal only between steps.  Errors: LM_E_HIP. */
+lm_status lm_set_layer_skip(lm_model* m, const uint8_t* mask);
+
+/* Similarity recording for calibrating the skip list.  enable = 1 clears the
+ * accumulators; every following step (run without graphs) adds, for each
+ * computed layer and sequence, the cosine similarity a.b / (|a| |b|) of the
+ * layer's input and output hidden vectors (fp64; 0 when either is zero).
+ * enable = 0 stops recording and keeps the sums.  Errors: LM_E_HIP. */
+lm_status lm_layer_similarity(lm_model* m, int32_t enable);
+
+/* mean: host fp64 [n_layers], the recorded similarities' mean per layer (NaN
+ * for a layer with no record); count: host int32 [n_layers] records, or NULL.
+ * Synchronises the model's stream.  Errors: LM_E_ARG (NULL mean), LM_E_HIP. */
+lm_status lm_get_layer_similarity(lm_model* m, double* mean, int32_t* count);
+
+/* The calibrated skip list: skips exactly the layers whose recorded mean
+ * similarity is above threshold (the page's default is 0.98) and reports how
+ * many in *n_skipped (nullable); lm_set_layer_skip with that mask.
+ * Errors: LM_E_ARG (non-finite threshold), LM_E_HIP. */
+lm_status lm_skip_similar_layers(lm_model* m, double threshold, int32_t* n_skipped);
+
 /* lm_set_residency(m, enable ? 0 : L): every layer streamed, or none. */
 lm_status lm_stream_mode(lm_model* m, int32_t enable);
 

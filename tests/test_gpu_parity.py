@@ -400,6 +400,127 @@ def test_long_cache_short_context_bit_identical(name):
         assert np.array_equal(a, c) and np.array_equal(b, d)
 
 
+@pytest.mark.parametrize("name,n_seq,mask", [("tiny_5layers", 1, [0, 1, 0, 1, 0]),
+                                              ("tiny_5layers", 1, [1, 1, 1, 1, 1]),
+                                              ("llama1b_2layers", 1, [0, 1])])
+def test_layer_skip_parity(name, n_seq, mask):
+    """Skipped layers (the engine page's layer skip) against the oracle with the
+    same mask: logits, argmax, appended rows of computed layers; a skipped
+    layer's cache rows stay as they were."""
+    model = get_model(name)
+    cfg = model.cfg
+    g = open_gpu(model, max_seqs=n_seq)
+    om = open_oracle(model, n_seq)
+    skip = np.array(mask, np.uint8)
+    g.set_layer_skip(skip)
+    toks = synth.start_tokens(cfg, n_seq)
+    try:
+        for st in range(cfg.steps):
+            p = cfg.ctx + st
+            lg_o, am_o = om.step(toks, skip=skip)
+            lg_g, am_g = g.step(toks)
+            compare_step(lg_g, am_g, lg_o, am_o, f"{name} skip {mask} step {st}")
+            for s in range(n_seq):
+                for l in range(cfg.n_layers):
+                    kg, vg = g.get_kv(s, l, p + 1)
+                    ko, vo = om.get_kv(s, l, p + 1)
+                    if skip[l]:
+                        assert np.array_equal(kg[:, cfg.ctx:], np.zeros_like(kg[:, cfg.ctx:])), (l, "skipped K row")
+                    else:
+                        assert f16_close(kg[:, cfg.ctx:p + 1], ko[:, cfg.ctx:p + 1]), (s, l, "K append")
+                        assert f16_close(vg[:, cfg.ctx:p + 1], vo[:, cfg.ctx:p + 1]), (s, l, "V append")
+            toks = am_o
+    finally:
+        g.close()
+        om.close()
+
+
+@pytest.mark.parametrize("name", ["tiny_5layers", "llama70b_q4_2layers"])
+def test_layer_skip_streaming_bit_identical(name):
+    """Skipped layers are not copied in streaming mode; every residency gives the
+    resident outputs bit for bit with the same mask."""
+    model = get_model(name)
+    cfg = model.cfg
+    mask = np.zeros(cfg.n_layers, np.uint8)
+    mask[1] = 1
+    if cfg.n_layers >= 5:
+        mask[3] = 1
+    g = open_gpu(model, max_seqs=1)
+    try:
+        toks = synth.start_tokens(cfg, 1)
+
+        def run():
+            g.set_position(0, cfg.ctx)
+            res, t = [], toks
+            for _ in range(cfg.steps):
+                lg, am = g.step(t)
+                res.append((lg.copy(), am.copy()))
+                t = am
+            return res
+
+        g.set_persistent(False)
+        g.set_dataflow(False)
+        g.set_layer_skip(mask)
+        resident = run()
+        for k in (0, 1, cfg.n_layers - 1):
+            g.set_residency(k)
+            for _ in range(2):
+                for (a, b), (c, d) in zip(resident, run()):
+                    assert np.array_equal(a, c) and np.array_equal(b, d), k
+        g.set_residency(cfg.n_layers)
+        g.set_layer_skip(None)
+        full = run()
+        g.set_layer_skip(mask)
+        again = run()
+        for (a, b), (c, d) in zip(resident, again):
+            assert np.array_equal(a, c) and np.array_equal(b, d)
+        assert not all(np.array_equal(a, c) for (a, _), (c, _) in zip(resident, full))
+    finally:
+        g.close()
+
+
+@pytest.mark.parametrize("name,n_seq", [("tiny_5layers", 1), ("tiny_q4", 1)])
+def test_layer_similarity_and_calibrated_skip(name, n_seq):
+    """Recorded per-layer input/output cosine similarities against the oracle's,
+    and the calibrated list (mean above the threshold) equal to the oracle's."""
+    import oracle
+    model = get_model(name)
+    cfg = model.cfg
+    g = open_gpu(model, max_seqs=n_seq)
+    om = open_oracle(model, n_seq)
+    toks = synth.start_tokens(cfg, n_seq)
+    try:
+        g.layer_similarity(True)
+        sums = np.zeros(cfg.n_layers)
+        for st in range(cfg.steps):
+            lg_o, am_o, cos = om.step(toks, with_cos=True)
+            g.step(toks)
+            sums += cos.sum(axis=0)
+            toks = am_o
+        g.layer_similarity(False)
+        mean, cnt = g.get_layer_similarity()
+        ref = sums / (cfg.steps * n_seq)
+        assert np.all(cnt == cfg.steps * n_seq)
+        assert np.allclose(mean, ref, rtol=0, atol=2e-6), (mean, ref)
+        # a threshold between two recorded means: the same list on both sides
+        srt = np.sort(ref)
+        thr = float((srt[len(srt) // 2 - 1] + srt[len(srt) // 2]) / 2) if len(srt) > 1 else float(srt[0] - 1e-3)
+        n = g.skip_similar_layers(thr)
+        expect = oracle.skip_list(ref, thr)
+        assert n == int(expect.sum())
+        # the model now skips exactly those layers: compare a step with the oracle's
+        toks = synth.start_tokens(cfg, n_seq)
+        for s in range(n_seq):
+            om.set_position(s, cfg.ctx)
+            g.set_position(s, cfg.ctx)
+        lg_o, am_o = om.step(toks, skip=expect)
+        lg_g, am_g = g.step(toks)
+        compare_step(lg_g, am_g, lg_o, am_o, f"{name} calibrated skip")
+    finally:
+        g.close()
+        om.close()
+
+
 def test_state_and_context_errors():
     import token_decode_llama_amd as lm
     cfg = CASES["tiny_q8"]

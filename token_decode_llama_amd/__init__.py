@@ -23,7 +23,8 @@ KERNEL_KINDS = ("embed", "qkv", "attn", "wo", "gateup", "down", "lmhead", "copy"
 EXPORTS = (
     "lm_model_create", "lm_model_destroy", "lm_load_layer_weights", "lm_load_global_weights",
     "lm_load_kv", "lm_get_kv", "lm_set_position", "lm_get_position", "lm_stream_mode",
-    "lm_set_residency", "lm_tier_sizes", "lm_plan_residency",
+    "lm_set_residency", "lm_tier_sizes", "lm_plan_residency", "lm_set_layer_skip",
+    "lm_layer_similarity", "lm_get_layer_similarity", "lm_skip_similar_layers",
     "lm_decode_step", "lm_decode_step_dev", "lm_set_graph", "lm_set_persistent", "lm_set_dataflow",
     "lm_check_error", "lm_stream", "lm_last_error",
     "lm_kernel_timing", "lm_kernel_stats", "lm_time_kind", "lm_kernel_bytes", "lm_debug_dequant",
@@ -78,6 +79,10 @@ def load():
         "lm_set_residency": ([vp, i32], st),
         "lm_tier_sizes": ([i32, i64, i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)], st),
         "lm_plan_residency": ([vp, i64, i64, ctypes.POINTER(i32)], st),
+        "lm_set_layer_skip": ([vp, vp], st),
+        "lm_layer_similarity": ([vp, i32], st),
+        "lm_get_layer_similarity": ([vp, vp, vp], st),
+        "lm_skip_similar_layers": ([vp, dbl, ctypes.POINTER(i32)], st),
         "lm_decode_step": ([vp, vp, i32, vp, vp], st),
         "lm_decode_step_dev": ([vp, vp, i32, vp, vp], st),
         "lm_set_graph": ([vp, i32], st),
@@ -229,6 +234,31 @@ class Model:
     def set_residency(self, n_resident: int):
         """Layers 0..n_resident-1 in HBM, the rest streamed from pinned host memory."""
         self._check(self._lib.lm_set_residency(self._h, n_resident))
+
+    def set_layer_skip(self, mask=None):
+        """mask: [n_layers] of 0/1 (1 = skip), or None to compute every layer."""
+        if mask is None:
+            self._check(self._lib.lm_set_layer_skip(self._h, None))
+            return
+        m = np.ascontiguousarray(mask, dtype=np.uint8)
+        if m.size != self.cfg.n_layers:
+            raise ValueError(f"skip mask has {m.size} entries; expected {self.cfg.n_layers}")
+        self._check(self._lib.lm_set_layer_skip(self._h, _p(m)))
+
+    def layer_similarity(self, enable: bool):
+        self._check(self._lib.lm_layer_similarity(self._h, 1 if enable else 0))
+
+    def get_layer_similarity(self):
+        """(mean cosine per layer, records per layer)."""
+        mean = np.empty(self.cfg.n_layers, np.float64)
+        cnt = np.empty(self.cfg.n_layers, np.int32)
+        self._check(self._lib.lm_get_layer_similarity(self._h, _p(mean), _p(cnt)))
+        return mean, cnt
+
+    def skip_similar_layers(self, threshold: float = 0.98) -> int:
+        n = ctypes.c_int32()
+        self._check(self._lib.lm_skip_similar_layers(self._h, float(threshold), ctypes.byref(n)))
+        return n.value
 
     def plan_residency(self, hbm_bytes: int = 0, host_bytes: int = 0) -> int:
         """Tier-A layer count by the tier sizing rule (0: query the device / host)."""

@@ -1518,6 +1518,49 @@ hipError_t launch_dequant(const QMat& w, int qtype, int row0, int n_rows, float*
     return hipGetLastError();
 }
 
+// Layer similarity (the C/CUDA Llama engine page, sections 3.5 and 4.5: the
+// cosine similarity of a layer's input and output hidden vectors, calibrated
+// ahead of time): for each sequence, cos = a.b / (|a| |b|) in fp64 (0 when
+// either vector is zero); acc[0] += the cosines, acc[1] += the sequences.
+// One workgroup, sequences in order: the sums are deterministic.
+__global__ __launch_bounds__(kBlock) void k_layer_cos(const float* __restrict__ xin, const float* __restrict__ x,
+                                                     int H, int n_seq, double* __restrict__ acc) {
+    __shared__ double red[3][kWaves];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    double tot = 0.0;
+    for (int s = 0; s < n_seq; ++s) {
+        double ab = 0.0, aa = 0.0, bb = 0.0;
+        for (int i = tid; i < H; i += kBlock) {
+            const double av = xin[(int64_t)s * H + i], bv = x[(int64_t)s * H + i];
+            ab = fma(av, bv, ab);
+            aa = fma(av, av, aa);
+            bb = fma(bv, bv, bb);
+        }
+        for (int off = 32; off > 0; off >>= 1) {
+            ab += __shfl_xor(ab, off, 64);
+            aa += __shfl_xor(aa, off, 64);
+            bb += __shfl_xor(bb, off, 64);
+        }
+        if (lane == 0) { red[0][wave] = ab; red[1][wave] = aa; red[2][wave] = bb; }
+        __syncthreads();
+        if (tid == 0) {
+            double sab = 0.0, saa = 0.0, sbb = 0.0;
+            for (int w = 0; w < kWaves; ++w) { sab += red[0][w]; saa += red[1][w]; sbb += red[2][w]; }
+            tot += (saa == 0.0 || sbb == 0.0) ? 0.0 : sab / (sqrt(saa) * sqrt(sbb));
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        acc[0] += tot;
+        acc[1] += (double)n_seq;
+    }
+}
+
+hipError_t launch_layer_cos(const float* xin, const float* x, int H, int n_seq, double* acc, hipStream_t st) {
+    hipLaunchKernelGGL(k_layer_cos, dim3(1), dim3(kBlock), 0, st, xin, x, H, n_seq, acc);
+    return hipGetLastError();
+}
+
 __global__ __launch_bounds__(kBlock) void k_read_bw(const uint4* __restrict__ buf, int64_t n16,
                                                    float* __restrict__ sink) {
     uint32_t acc = 0;

@@ -166,6 +166,15 @@ struct lm_model {
     bool global_loaded = false;
     std::vector<int> pos;
     bool streaming = false;               // n_res < L
+    // layer skip: skipped layers compute nothing (their input is their output)
+    std::vector<uint8_t> skip;
+    bool any_skip = false;
+    std::vector<int> str_list;            // the streamed layers a step computes, in order
+    std::vector<int> str_idx;             // layer -> index in str_list, or -1
+    // layer similarity recording (calibration of the skip list)
+    bool sim_on = false;
+    double* d_sim = nullptr;              // [L][2]: sum of input/output cosines, records
+    float* d_xin = nullptr;               // [max_seqs][H] a layer's input
     bool use_graph = true;
 
     // streaming pipeline state
@@ -301,6 +310,8 @@ static void release_all(lm_model* m) {
     if (m->own_stream && m->stream) (void)hipStreamDestroy(m->stream);
     m->stream = nullptr;
 }
+
+static void rebuild_stream_order(lm_model* m);
 
 // ---------------------------------------------------------------------------
 // configuration checks (no HIP call before these pass)
@@ -465,6 +476,8 @@ extern "C" lm_status lm_model_create(const lm_config* cfg, void* hip_stream, lm_
     const int64_t L = c.n_layers;
     CREATE_TRY(dev_alloc(m, (void**)&m->d_layers, L * m->blob_bytes, "layer weights"));
     m->n_res = (int)L;
+    m->skip.assign((size_t)L, 0);
+    rebuild_stream_order(m);
     CREATE_TRY(dev_alloc(m, (void**)&m->d_norms, L * 2 * m->H * 4, "norm gains"));
     CREATE_TRY(dev_alloc(m, (void**)&m->d_embd, m->V * m->H * 2, "token embedding"));
     CREATE_TRY(dev_alloc(m, (void**)&m->d_out_norm, m->H * 4, "output norm"));
@@ -497,6 +510,8 @@ extern "C" lm_status lm_model_create(const lm_config* cfg, void* hip_stream, lm_
     CREATE_TRY(dev_alloc(m, (void**)&m->d_attn_cnt, (int64_t)S * m->nkv * attn_cnt_lines(m->max_chunks) * kCntStride * 4,
                          "attention chunk counters"));
     CREATE_TRY(dev_alloc(m, (void**)&m->d_sink, 4096 * 4, "sink"));
+    CREATE_TRY(dev_alloc(m, (void**)&m->d_sim, (int64_t)L * 2 * 8, "layer similarity sums"));
+    CREATE_TRY(dev_alloc(m, (void**)&m->d_xin, (int64_t)S * m->H * 4, "layer input copy"));
     m->dbg_floats = std::max<int64_t>({m->H, m->F, m->qrows}) * 64;
     CREATE_TRY(dev_alloc(m, (void**)&m->d_dbg, m->dbg_floats * 4, "debug rows"));
     m->stage_bytes = std::min<int64_t>(64ll << 20, std::max<int64_t>(m->blob_bytes, m->lm_q_bytes + m->lm_sc_bytes));
@@ -812,7 +827,18 @@ static lm_status upload_tiles(lm_model* m, const TileGeom& g, RowFn src_row, uin
 // residency: layers n_res..L-1 are streamed through the two HBM buffers,
 // alternating between them in order
 static bool layer_streamed(const lm_model* m, int l) { return l >= m->n_res; }
-static int stream_slot(const lm_model* m, int l) { return (l - m->n_res) & 1; }
+// the streamed layers a step computes take the two buffers in turn
+static int stream_slot(const lm_model* m, int l) { return m->str_idx[l] & 1; }
+static void rebuild_stream_order(lm_model* m) {
+    const int L = m->cfg.n_layers;
+    m->str_list.clear();
+    m->str_idx.assign((size_t)L, -1);
+    for (int l = m->n_res; l < L; ++l)
+        if (!m->skip[l]) {
+            m->str_idx[l] = (int)m->str_list.size();
+            m->str_list.push_back(l);
+        }
+}
 static uint8_t* host_blob(lm_model* m, int l) { return m->h_arena + (int64_t)(l - m->n_res) * m->blob_bytes; }
 
 static void invalidate_graphs(lm_model* m) {
@@ -1169,11 +1195,12 @@ static hipError_t gemv(lm_model* m, GemvArgs a, int epi, int n_seq, hipStream_t 
 }
 
 static bool use_step(const lm_model* m, int n_seq) {
-    return m->persistent && m->step_capable && n_seq == 1 && !m->streaming;
+    return m->persistent && m->step_capable && n_seq == 1 && !m->streaming && !m->any_skip && !m->sim_on;
 }
 
 static bool use_flow(const lm_model* m, int n_seq) {
-    return m->flow_mode != 0 && m->flow_capable && n_seq == 1 && !m->streaming && !use_step(m, n_seq);
+    return m->flow_mode != 0 && m->flow_capable && n_seq == 1 && !m->streaming && !m->any_skip && !m->sim_on &&
+           !use_step(m, n_seq);
 }
 
 // Launch this family's kernels?  All of them, unless a timing-only graph of
@@ -1231,16 +1258,19 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
     at.counter = m->d_attn_cnt;
     at.out = m->d_o;
 
-    const int n_str = L - m->n_res;     // streamed layers: n_res..L-1
+    const int n_str = (int)m->str_list.size();     // streamed layers this step computes
     for (int i = 0; i < std::min(n_str, 2); ++i)
         if (!m->prefetched[i]) {
-            lm_status s = stream_copy(m, m->n_res + i);
+            lm_status s = stream_copy(m, m->str_list[i]);
             if (s != LM_OK) return s;
         }
     m->prefetched[0] = m->prefetched[1] = false;
 
     for (int l = 0; l < (flow ? 0 : L); ++l) {
+        if (m->skip[l]) continue;                       // its input is its output
         if (layer_streamed(m, l)) HIPTRY(m, hipStreamWaitEvent(st, m->ev_copied[stream_slot(m, l)], 0));
+        if (m->sim_on)                                  // the layer's input, for its similarity
+            HIPTRY(m, hipMemcpyAsync(m->d_xin, m->d_x, (size_t)n_seq * m->H * 4, hipMemcpyDeviceToDevice, st));
         const uint8_t* blob = layer_blob(m, l);
         const float* g_attn = m->d_norms + (int64_t)l * 2 * m->H;
         const float* g_ffn = g_attn + m->H;
@@ -1287,10 +1317,12 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
             a.out = m->d_x; a.out_stride = (int)m->H;
             if (want(m, LM_K_DOWN)) HIPTRY(m, gemv(m, a, EPI_RESID, n_seq, st));
         }
+        if (m->sim_on) HIPTRY(m, launch_layer_cos(m->d_xin, m->d_x, (int)m->H, n_seq, m->d_sim + 2 * l, st));
         if (layer_streamed(m, l)) {
             HIPTRY(m, hipEventRecord(m->ev_consumed[stream_slot(m, l)], st));
-            if (l + 2 < L) {
-                lm_status s = stream_copy(m, l + 2);
+            const int nx = m->str_idx[l] + 2;
+            if (nx < n_str) {
+                lm_status s = stream_copy(m, m->str_list[nx]);
                 if (s != LM_OK) return s;
             }
         }
@@ -1298,7 +1330,7 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
     // start the next step's first two streamed layers while the LM head (and
     // the next step's resident layers) run
     for (int i = 0; i < std::min(n_str, 2); ++i) {
-        lm_status s = stream_copy(m, m->n_res + i);
+        lm_status s = stream_copy(m, m->str_list[i]);
         if (s != LM_OK) return s;
         m->prefetched[i] = true;
     }
@@ -1330,7 +1362,7 @@ static lm_status launch_graph(lm_model* m, const lm_model::GraphEntry& g) {
 }
 
 static lm_status run_step(lm_model* m, int n_seq, const int* d_tok, float* d_logits, int* d_argmax) {
-    const bool graph_ok = m->use_graph && m->timing != 1 && !m->streaming;
+    const bool graph_ok = m->use_graph && m->timing != 1 && !m->streaming && !m->sim_on;
     if (!graph_ok) return enqueue_step(m, n_seq, d_tok, d_logits, d_argmax);
     const int chunks = attn_grid_chunks(m, n_seq);
     for (auto& g : m->graphs)
@@ -1664,10 +1696,68 @@ extern "C" lm_status lm_set_residency(lm_model* m, int32_t n_resident) {
     m->d_sbuf[1] = b1;
     m->n_res = nw;
     m->streaming = nw < L;
+    rebuild_stream_order(m);
     m->flow_h.blobs = d;
     m->prefetched[0] = m->prefetched[1] = false;
     invalidate_graphs(m);
     return LM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// layer skip (the C/CUDA Llama engine page, sections 2.5, 3.5, 4.5)
+// ---------------------------------------------------------------------------
+extern "C" lm_status lm_set_layer_skip(lm_model* m, const uint8_t* mask) {
+    if (!m) return LM_E_ARG;
+    HIPTRY(m, hipStreamSynchronize(m->stream));
+    HIPTRY(m, hipStreamSynchronize(m->copy_stream));
+    const int L = m->cfg.n_layers;
+    m->any_skip = false;
+    for (int l = 0; l < L; ++l) {
+        m->skip[l] = mask && mask[l] ? 1 : 0;
+        m->any_skip = m->any_skip || m->skip[l];
+    }
+    rebuild_stream_order(m);
+    m->prefetched[0] = m->prefetched[1] = false;
+    invalidate_graphs(m);
+    return LM_OK;
+}
+
+extern "C" lm_status lm_layer_similarity(lm_model* m, int32_t enable) {
+    if (!m) return LM_E_ARG;
+    HIPTRY(m, hipStreamSynchronize(m->stream));
+    if (enable) HIPTRY(m, hipMemset(m->d_sim, 0, (size_t)m->cfg.n_layers * 2 * 8));
+    m->sim_on = enable != 0;
+    invalidate_graphs(m);
+    return LM_OK;
+}
+
+extern "C" lm_status lm_get_layer_similarity(lm_model* m, double* mean, int32_t* count) {
+    if (!m || !mean) return LM_E_ARG;
+    const int L = m->cfg.n_layers;
+    std::vector<double> h((size_t)L * 2);
+    HIPTRY(m, hipStreamSynchronize(m->stream));
+    HIPTRY(m, hipMemcpy(h.data(), m->d_sim, h.size() * 8, hipMemcpyDeviceToHost));
+    for (int l = 0; l < L; ++l) {
+        mean[l] = h[2 * l + 1] > 0 ? h[2 * l] / h[2 * l + 1] : std::nan("");
+        if (count) count[l] = (int32_t)h[2 * l + 1];
+    }
+    return LM_OK;
+}
+
+extern "C" lm_status lm_skip_similar_layers(lm_model* m, double threshold, int32_t* n_skipped) {
+    if (!m || !std::isfinite(threshold)) return LM_E_ARG;
+    const int L = m->cfg.n_layers;
+    std::vector<double> mean((size_t)L);
+    lm_status st = lm_get_layer_similarity(m, mean.data(), nullptr);
+    if (st != LM_OK) return st;
+    std::vector<uint8_t> mask((size_t)L);
+    int n = 0;
+    for (int l = 0; l < L; ++l) {
+        mask[l] = mean[l] > threshold;            // false for a layer with no record (NaN)
+        n += mask[l];
+    }
+    if (n_skipped) *n_skipped = n;
+    return lm_set_layer_skip(m, mask.data());
 }
 
 extern "C" lm_status lm_stream_mode(lm_model* m, int32_t enable) {
@@ -1761,8 +1851,10 @@ extern "C" lm_status lm_kernel_stats(lm_model* m, int32_t kind, int64_t* count, 
 extern "C" lm_status lm_kernel_bytes(const lm_model* m, int32_t kind, int32_t n_seq, double* bytes) {
     if (!m || !bytes || kind < 0 || kind >= LM_K_COUNT || n_seq < 1 || n_seq > m->cfg.max_seqs) return LM_E_ARG;
     const double bpw = m->cfg.qtype == LM_Q8_0 ? 34.0 / 32.0 : 18.0 / 32.0;
+    int computed = 0;                                 // layers a step computes (not skipped)
+    for (int l = 0; l < m->cfg.n_layers; ++l) computed += !m->skip[l];
     const double H = (double)m->H, F = (double)m->F, V = (double)m->V, Q = (double)m->qrows,
-                 KV = (double)m->kvrows, L = m->cfg.n_layers, S = n_seq;
+                 KV = (double)m->kvrows, L = computed, S = n_seq;
     double b = 0.0;
     switch (kind) {
         case LM_K_EMBED: b = S * H * (2 + 4); break;
@@ -1777,7 +1869,7 @@ extern "C" lm_status lm_kernel_bytes(const lm_model* m, int32_t kind, int32_t n_
         case LM_K_GATEUP: b = L * (2 * F * H * bpw + H * 4 + S * (H * 4 + F * 4)); break;
         case LM_K_DOWN: b = L * (H * F * bpw + S * (F * 4 + H * 8)); break;
         case LM_K_LMHEAD: b = V * H * bpw + H * 4 + S * H * 4; break;
-        case LM_K_COPY: b = (double)(L - m->n_res) * (double)m->blob_bytes; break;
+        case LM_K_COPY: b = (double)m->str_list.size() * (double)m->blob_bytes; break;
         case LM_K_FLOW:
             for (int k = LM_K_QKV; k <= LM_K_DOWN; ++k) {
                 double kb = 0.0;
