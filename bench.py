@@ -401,8 +401,10 @@ def run_multi(args):
 
 def run_70b(args):
     """(a) resident in HBM, (b) layer streaming from pinned host memory, (c) the
-    first 36 layers resident and the other 44 streamed."""
+    first 36 layers resident and the other 44 streamed, (d) streamed with the 20
+    most similar layers skipped."""
     import numpy as np
+    import torch
     import synth
     import token_decode_llama_amd as lm
     name = "llama70b_q4"
@@ -494,6 +496,33 @@ def run_70b(args):
         "n_resident": k_h, "n_streamed": cfg.n_layers - k_h,
         "host_link_GBps": round(copy_h / (ms_h * 1e-3) / 1e9, 2),
         "tier_a_for_24GiB": r.g.plan_residency(hbm_bytes=24 << 30, host_bytes=1 << 40)}
+    # (d) layer skip, streamed: the similarity of every layer's input and output
+    # recorded over 2 steps, then the 20 most similar of 80 layers skipped (the
+    # pages' 70B figure skips 20 of 80); skipped layers are not copied
+    r.g.set_residency(0)
+    r.rewind()
+    r.g.layer_similarity(True)
+    for _ in range(2):
+        r.step()
+    torch.cuda.synchronize()
+    r.g.layer_similarity(False)
+    mean, _ = r.g.get_layer_similarity()
+    order = np.sort(mean)[::-1]
+    n_skip = 20
+    thr = float((order[n_skip - 1] + order[n_skip]) / 2)
+    skipped = r.g.skip_similar_layers(thr)
+    r.warm(1)
+    ms_sk = r.timed(n_st)
+    copy_sk = r.g.kernel_bytes("copy", 1)
+    log(f"streaming, {skipped} layers skipped: {ms_sk:.3f} ms/step")
+    out["layer_skip"] = {
+        "value": round(1000.0 / ms_sk, 4), "unit": "tokens/s", "steps": n_st, "ms_per_step": round(ms_sk, 2),
+        "mode": "all layers streamed", "n_skipped": skipped, "threshold": round(thr, 6),
+        "similarity_min_max": [round(float(np.nanmin(mean)), 6), round(float(np.nanmax(mean)), 6)],
+        "host_link_GBps": round(copy_sk / (ms_sk * 1e-3) / 1e9, 2),
+        "calibration": "mean input/output cosine similarity per layer over 2 greedy steps; the list skips the "
+                       "layers above a threshold set between the 20th and 21st largest mean"}
+    r.g.set_layer_skip(None)
     r.close()
     if keep:
         log("oracle baseline (bounded sample)")
