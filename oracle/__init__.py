@@ -81,6 +81,7 @@ def lib():
             "orc_decode_step_ex": ([vp, vp, i32, vp, vp, vp, vp], i32),
             "orc_cosine": ([vp, vp, i64], f64),
             "orc_skip_list": ([vp, i32, f64, vp], i32),
+            "orc_spec_accept": ([vp, vp, i32, vp], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -178,6 +179,17 @@ def skip_list(mean_cos, threshold: float) -> np.ndarray:
     mask = np.zeros(m.size, np.uint8)
     lib().orc_skip_list(_p(m), m.size, float(threshold), _p(mask))
     return mask
+
+
+def spec_accept(draft, verify):
+    """Accepted tokens of one self-speculative round (len(verify) == len(draft) + 1)."""
+    d = np.ascontiguousarray(draft, dtype=np.int32)
+    v = np.ascontiguousarray(verify, dtype=np.int32)
+    if v.size != d.size + 1:
+        raise ValueError("verify holds one token more than draft")
+    out = np.empty(v.size, np.int32)
+    n = lib().orc_spec_accept(_p(d) if d.size else None, _p(v), d.size, _p(out))
+    return out[:n]
 
 
 def argmax_f32(v) -> int:

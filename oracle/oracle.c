@@ -25,6 +25,8 @@
  *             cache size n_layers * n_head_kv * n_ctx * head_dim * dtype * 2;
  *             section 4 step 4 says decode positions continue from the end of
  *             the prefix, or RoPE goes wrong.
+ *   [ENGINE] sections 3.5 and 5.3 (self-speculative decoding): the bottom
+ *             layers draft tokens, the full model verifies them.
  *   [ENGINE] sections 2.5, 3.5 and 4.5 (layer skip): a layer whose output is
  *             close to its input, by the cosine similarity of the two hidden
  *             vectors against a threshold (0.98 by default), is skipped and its
@@ -425,6 +427,25 @@ int orc_decode_step_ex(orc_model* m, const int32_t* tokens, int n_seq, double* l
 
 int orc_decode_step(orc_model* m, const int32_t* tokens, int n_seq, double* logits, int32_t* argmax) {
     return orc_decode_step_ex(m, tokens, n_seq, logits, argmax, NULL, NULL);
+}
+
+/*
+ * Self-speculative acceptance ([ENGINE] sections 3.5 and 5.3: draft tokens
+ * with the bottom layers, then verify them with the full model).  draft[0..k-1]
+ * are the drafted tokens d1..dk; verify[0..k] the full model's argmax after
+ * [t0, d1, .., dk] at positions p..p+k.  The longest prefix d1..di with
+ * verify[j] == d(j+1) for every j < i is accepted, then verify[i] (the full
+ * model's own next token) is appended: out[0..i], returns i + 1.  Greedy
+ * decoding gives the same tokens.
+ */
+int orc_spec_accept(const int32_t* draft, const int32_t* verify, int k, int32_t* out) {
+    int i = 0;
+    while (i < k && verify[i] == draft[i]) {
+        out[i] = draft[i];
+        ++i;
+    }
+    out[i] = verify[i];
+    return i + 1;
 }
 
 /* The calibrated skip list: mask[l] = 1 when mean_cos[l] > threshold. */

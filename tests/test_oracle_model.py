@@ -308,3 +308,58 @@ def test_zero_update_layer_similarity_is_one():
     _, _, cos = om.step(synth.start_tokens(cfg, 1), with_cos=True)
     assert cos[0, 1] == pytest.approx(1.0, abs=1e-15)
     assert cos[0, 0] < 1.0
+
+
+# ---------------------------------------------------------------------------
+# self-speculative decoding (the C/CUDA Llama engine page, sections 3.5 and 5.3)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("draft,verify,expect", [
+    ([5, 6, 7], [5, 6, 7, 9], [5, 6, 7, 9]),     # every draft accepted, plus the bonus token
+    ([5, 6, 7], [5, 8, 7, 9], [5, 8]),           # first mismatch at 2: d1 then the model's own token
+    ([5, 6, 7], [4, 6, 7, 9], [4]),              # nothing accepted: one token, the model's
+    ([], [3], [3]),                              # k = 0: a plain step
+    ([1, 1], [1, 1, 1], [1, 1, 1]),
+])
+def test_spec_accept_hand_cases(draft, verify, expect):
+    assert oracle.spec_accept(draft, verify).tolist() == expect
+
+
+def test_speculative_round_equals_greedy():
+    """A round drafted with the bottom layers (the other layers skipped) and
+    verified by k+1 full steps yields exactly the greedy tokens; with every
+    layer drafting, all k drafts are accepted."""
+    cfg = synth.variant("tiny", n_layers=3, steps=12)
+    model = synth.make_model(cfg)
+    tok = int(synth.start_tokens(cfg)[0])
+    greedy = _load_oracle(model)
+    g_toks, t = [], tok
+    for _ in range(8):
+        _, am = greedy.step([t])
+        t = int(am[0])
+        g_toks.append(t)
+    for d_layers, k in ((1, 3), (3, 3), (0, 2)):
+        om = _load_oracle(model)
+        p0 = om.position(0)
+        out, t = [], tok
+        while len(out) < 8:
+            p = om.position(0)
+            skip = np.array([l >= d_layers for l in range(cfg.n_layers)], np.uint8)
+            draft, dt = [], t
+            for _ in range(k):                   # draft: bottom layers only
+                _, am = om.step([dt], skip=skip)
+                dt = int(am[0])
+                draft.append(dt)
+            om.set_position(0, p)                # verify: k+1 full steps over [t, d1..dk]
+            verify = []
+            for x in [t] + draft:
+                _, am = om.step([x])
+                verify.append(int(am[0]))
+            acc = oracle.spec_accept(draft, verify).tolist()
+            if d_layers == cfg.n_layers:
+                assert len(acc) == k + 1
+            out += acc
+            t = acc[-1]
+            om.set_position(0, p + len(acc))
+        assert out[:8] == g_toks, (d_layers, k)
+        assert om.position(0) == p0 + len(out)
