@@ -174,6 +174,25 @@ lm_status lm_get_layer_similarity(lm_model* m, double* mean, int32_t* count);
  * Errors: LM_E_ARG (non-finite threshold), LM_E_HIP. */
 lm_status lm_skip_similar_layers(lm_model* m, double threshold, int32_t* n_skipped);
 
+/* One self-speculative round for sequence 0 (the C/CUDA Llama engine page,
+ * sections 3.5 and 5.3: draft with the bottom layers, verify with the full
+ * model).  token: sequence 0's next input token (at its position p, not yet
+ * processed).  k drafts d1..dk, each a step through layers 0..draft_layers-1
+ * and the LM head; then one pass of every layer over t0 = token, d1..dk at
+ * positions p..p+k (k+1 columns of the several-sequence path, all on sequence
+ * 0's cache, so column j attends to keys 0..p+j: the same as k+1 plain
+ * steps); then the longest prefix of drafts the full model agrees with, plus
+ * the full model's own token after it, go to tokens_out (host int32 [k+1]),
+ * their count to *n_out (1..k+1) and sequence 0's position becomes
+ * p + *n_out; the last output token is the next round's input.  Greedy
+ * decoding gives the same tokens.  Cache rows past the new position hold
+ * draft or rejected values until overwritten.  Needs 1 <= k <= 3, k + 1 <=
+ * max_seqs, every layer resident.  Blocks until the tokens are on the host.
+ * Errors: LM_E_ARG, LM_E_STATE (weights not loaded, streaming mode), LM_E_CTX
+ * (p + k + 1 > max_ctx), LM_E_HIP. */
+lm_status lm_speculative_step(lm_model* m, int32_t token, int32_t draft_layers, int32_t k,
+                              int32_t* tokens_out, int32_t* n_out);
+
 /* lm_set_residency(m, enable ? 0 : L): every layer streamed, or none. */
 lm_status lm_stream_mode(lm_model* m, int32_t enable);
 

@@ -24,7 +24,7 @@ EXPORTS = (
     "lm_model_create", "lm_model_destroy", "lm_load_layer_weights", "lm_load_global_weights",
     "lm_load_kv", "lm_get_kv", "lm_set_position", "lm_get_position", "lm_stream_mode",
     "lm_set_residency", "lm_tier_sizes", "lm_plan_residency", "lm_set_layer_skip",
-    "lm_layer_similarity", "lm_get_layer_similarity", "lm_skip_similar_layers",
+    "lm_layer_similarity", "lm_get_layer_similarity", "lm_skip_similar_layers", "lm_speculative_step",
     "lm_decode_step", "lm_decode_step_dev", "lm_set_graph", "lm_set_persistent", "lm_set_dataflow",
     "lm_check_error", "lm_stream", "lm_last_error",
     "lm_kernel_timing", "lm_kernel_stats", "lm_time_kind", "lm_kernel_bytes", "lm_debug_dequant",
@@ -83,6 +83,7 @@ def load():
         "lm_layer_similarity": ([vp, i32], st),
         "lm_get_layer_similarity": ([vp, vp, vp], st),
         "lm_skip_similar_layers": ([vp, dbl, ctypes.POINTER(i32)], st),
+        "lm_speculative_step": ([vp, i32, i32, i32, vp, ctypes.POINTER(i32)], st),
         "lm_decode_step": ([vp, vp, i32, vp, vp], st),
         "lm_decode_step_dev": ([vp, vp, i32, vp, vp], st),
         "lm_set_graph": ([vp, i32], st),
@@ -259,6 +260,14 @@ class Model:
         n = ctypes.c_int32()
         self._check(self._lib.lm_skip_similar_layers(self._h, float(threshold), ctypes.byref(n)))
         return n.value
+
+    def speculative_step(self, token: int, draft_layers: int, k: int) -> np.ndarray:
+        """One self-speculative round for sequence 0: the accepted tokens (1..k+1)."""
+        out = np.zeros(k + 1, np.int32)
+        n = ctypes.c_int32()
+        self._check(self._lib.lm_speculative_step(self._h, int(token), int(draft_layers), int(k), _p(out),
+                                                  ctypes.byref(n)))
+        return out[:n.value].copy()
 
     def plan_residency(self, hbm_bytes: int = 0, host_bytes: int = 0) -> int:
         """Tier-A layer count by the tier sizing rule (0: query the device / host)."""

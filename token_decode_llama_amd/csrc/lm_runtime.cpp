@@ -171,6 +171,15 @@ struct lm_model {
     bool any_skip = false;
     std::vector<int> str_list;            // the streamed layers a step computes, in order
     std::vector<int> str_idx;             // layer -> index in str_list, or -1
+    // one step's overrides (self-speculative rounds): positions from opt_pos,
+    // every column on sequence 0's cache, positions not advanced, layers from
+    // opt_limit on skipped; opt_need = the longest context among the columns
+    bool opt_active = false;
+    const int* opt_pos = nullptr;
+    bool opt_shared_kv = false, opt_advance = true;
+    int opt_limit = 0, opt_need = 0;
+    int* d_spec = nullptr;                // [8] a round's tokens t0, d1..dk; [8..15] verify argmax
+    int* d_vpos = nullptr;                // [4] verify positions
     // layer similarity recording (calibration of the skip list)
     bool sim_on = false;
     double* d_sim = nullptr;              // [L][2]: sum of input/output cosines, records
@@ -511,6 +520,8 @@ extern "C" lm_status lm_model_create(const lm_config* cfg, void* hip_stream, lm_
                          "attention chunk counters"));
     CREATE_TRY(dev_alloc(m, (void**)&m->d_sink, 4096 * 4, "sink"));
     CREATE_TRY(dev_alloc(m, (void**)&m->d_sim, (int64_t)L * 2 * 8, "layer similarity sums"));
+    CREATE_TRY(dev_alloc(m, (void**)&m->d_spec, 16 * 4, "speculative round tokens"));
+    CREATE_TRY(dev_alloc(m, (void**)&m->d_vpos, 4 * 4, "verify positions"));
     CREATE_TRY(dev_alloc(m, (void**)&m->d_xin, (int64_t)S * m->H * 4, "layer input copy"));
     m->dbg_floats = std::max<int64_t>({m->H, m->F, m->qrows}) * 64;
     CREATE_TRY(dev_alloc(m, (void**)&m->d_dbg, m->dbg_floats * 4, "debug rows"));
@@ -1153,13 +1164,17 @@ static lm_status collect_timing(lm_model* m) {
 // so a launch does not read the whole cache when the context is short.  A
 // step graph is keyed by it: a context crossing a power of two takes a new
 // graph.
-static int attn_grid_chunks(const lm_model* m, int n_seq) {
-    int need = 1;
-    for (int s = 0; s < n_seq; ++s) need = std::max(need, m->pos[s] + 1);
-    const int tiles = (need + kAttnChunk - 1) / kAttnChunk;
+static int attn_chunks_for(const lm_model* m, int need) {
+    const int tiles = (std::max(need, 1) + kAttnChunk - 1) / kAttnChunk;
     int c = 1;
     while (c < tiles) c *= 2;
     return std::min(c, m->max_chunks);
+}
+
+static int attn_grid_chunks(const lm_model* m, int n_seq) {
+    int need = 1;
+    for (int s = 0; s < n_seq; ++s) need = std::max(need, m->pos[s] + 1);
+    return attn_chunks_for(m, need);
 }
 
 static const uint8_t* layer_blob(lm_model* m, int l) {
@@ -1195,12 +1210,13 @@ static hipError_t gemv(lm_model* m, GemvArgs a, int epi, int n_seq, hipStream_t 
 }
 
 static bool use_step(const lm_model* m, int n_seq) {
-    return m->persistent && m->step_capable && n_seq == 1 && !m->streaming && !m->any_skip && !m->sim_on;
+    return m->persistent && m->step_capable && n_seq == 1 && !m->streaming && !m->any_skip && !m->sim_on &&
+           !m->opt_active;
 }
 
 static bool use_flow(const lm_model* m, int n_seq) {
     return m->flow_mode != 0 && m->flow_capable && n_seq == 1 && !m->streaming && !m->any_skip && !m->sim_on &&
-           !use_step(m, n_seq);
+           !m->opt_active && !use_step(m, n_seq);
 }
 
 // Launch this family's kernels?  All of them, unless a timing-only graph of
@@ -1237,22 +1253,24 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
     base.max_ctx = c.max_ctx;
     base.q_rows = (int)m->qrows;
     base.kv_rows = (int)m->kvrows;
-    base.kv_seq_stride = kv_seq_elems(m);
-    base.pos = m->d_pos;
+    const int* step_pos = m->opt_active && m->opt_pos ? m->opt_pos : m->d_pos;
+    const int64_t kv_stride = m->opt_active && m->opt_shared_kv ? 0 : kv_seq_elems(m);
+    base.kv_seq_stride = kv_stride;
+    base.pos = step_pos;
     base.rope_cos = m->d_cos;
     base.rope_sin = m->d_sin;
 
     AttnArgs at{};
     at.q = m->d_q;
-    at.kv_seq_stride = kv_seq_elems(m);
-    at.pos = m->d_pos;
+    at.kv_seq_stride = kv_stride;
+    at.pos = step_pos;
     at.nq = (int)m->nq;
     at.nkv = (int)m->nkv;
     at.hd = (int)m->hd;
     at.max_ctx = c.max_ctx;
     at.max_chunks = m->max_chunks;
     at.scale = (float)(1.0 / std::sqrt((double)m->hd));
-    at.grid_chunks = attn_grid_chunks(m, n_seq);
+    at.grid_chunks = m->opt_active ? attn_chunks_for(m, m->opt_need) : attn_grid_chunks(m, n_seq);
     at.tiles = attn_tiles(n_seq, (int)m->nkv, at.grid_chunks);
     at.part = m->d_attn_part;
     at.counter = m->d_attn_cnt;
@@ -1268,6 +1286,7 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
 
     for (int l = 0; l < (flow ? 0 : L); ++l) {
         if (m->skip[l]) continue;                       // its input is its output
+        if (m->opt_active && l >= m->opt_limit) continue;
         if (layer_streamed(m, l)) HIPTRY(m, hipStreamWaitEvent(st, m->ev_copied[stream_slot(m, l)], 0));
         if (m->sim_on)                                  // the layer's input, for its similarity
             HIPTRY(m, hipMemcpyAsync(m->d_xin, m->d_x, (size_t)n_seq * m->H * 4, hipMemcpyDeviceToDevice, st));
@@ -1346,7 +1365,7 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
         a.counter = m->d_lm_cnt;
         a.argmax_out = d_argmax;
         // a timing-only replay of the LM head must not advance the positions
-        a.pos_inc = m->only_kind < 0 ? m->d_pos : nullptr;
+        a.pos_inc = m->only_kind < 0 && !(m->opt_active && !m->opt_advance) ? m->d_pos : nullptr;
         if (want(m, LM_K_LMHEAD)) HIPTRY(m, gemv(m, a, EPI_LOGITS, n_seq, st));
     }
     return LM_OK;
@@ -1494,6 +1513,82 @@ extern "C" lm_status lm_decode_step_dev(lm_model* m, const int32_t* d_tokens, in
     if (st != LM_OK) return st;
     for (int s = 0; s < n_seq; ++s) m->pos[s] += 1;
     return LM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// self-speculative decoding (the C/CUDA Llama engine page, sections 3.5, 5.3)
+// ---------------------------------------------------------------------------
+// One round for sequence 0: k drafts, each one step of the layers below
+// draft_layers and the LM head; then one pass of the whole model over the k+1
+// tokens t0, d1..dk at positions p..p+k as k+1 columns of the several-sequence
+// path that all read and write sequence 0's cache (column j attends to keys
+// 0..p+j, the block's own keys included: the verify pass is exactly k+1 plain
+// steps); then the longest prefix of drafts that the full model agrees with,
+// plus the full model's token after it.
+extern "C" lm_status lm_speculative_step(lm_model* m, int32_t token, int32_t draft_layers, int32_t k,
+                                         int32_t* tokens_out, int32_t* n_out) {
+    if (!m) return LM_E_ARG;
+    lm_status st = check_ready(m, "lm_speculative_step", 1);
+    if (st != LM_OK) return st;
+    const int L = m->cfg.n_layers;
+    if (!tokens_out || !n_out) return fail(m, LM_E_ARG, "lm_speculative_step: tokens_out or n_out is NULL");
+    if (k < 1 || k > 3 || k + 1 > m->cfg.max_seqs)
+        return fail(m, LM_E_ARG, "lm_speculative_step: k = %d; expected 1..%d (k + 1 <= max_seqs <= 4)", k,
+                    std::min(3, m->cfg.max_seqs - 1));
+    if (draft_layers < 0 || draft_layers > L)
+        return fail(m, LM_E_ARG, "lm_speculative_step: draft_layers = %d; expected 0..%d", draft_layers, L);
+    if (token < 0 || token >= m->cfg.vocab)
+        return fail(m, LM_E_ARG, "lm_speculative_step: token = %d; expected 0..%d", token, m->cfg.vocab - 1);
+    if (m->streaming)
+        return fail(m, LM_E_STATE, "lm_speculative_step: not in streaming mode (every layer must be resident)");
+    const int p = m->pos[0];
+    if (p + k + 1 > m->cfg.max_ctx)
+        return fail(m, LM_E_CTX, "lm_speculative_step: position %d + %d drafts reaches max_ctx = %d", p, k,
+                    m->cfg.max_ctx);
+    hipStream_t s0 = m->stream;
+    HIPTRY(m, hipMemcpyAsync(m->d_spec, &token, 4, hipMemcpyHostToDevice, s0));
+    // drafts: the bottom layers, positions advanced on the device as a plain step does
+    m->opt_active = true;
+    m->opt_pos = nullptr;
+    m->opt_shared_kv = false;
+    m->opt_advance = true;
+    m->opt_limit = draft_layers;
+    for (int i = 0; i < k && st == LM_OK; ++i) {
+        m->opt_need = p + i + 1;
+        st = enqueue_step(m, 1, m->d_spec + i, nullptr, m->d_spec + i + 1);
+        if (st == LM_OK) m->pos[0] += 1;
+    }
+    // verify: every layer, columns j = 0..k at positions p + j on sequence 0's cache
+    int32_t vpos[4] = {p, p + 1, p + 2, p + 3};
+    int32_t h[16] = {0};
+    if (st == LM_OK) {
+        const hipError_t e = hipMemcpyAsync(m->d_vpos, vpos, 16, hipMemcpyHostToDevice, s0);
+        if (e != hipSuccess) st = fail(m, LM_E_HIP, "lm_speculative_step: %s", hipGetErrorString(e));
+    }
+    if (st == LM_OK) {
+        m->opt_pos = m->d_vpos;
+        m->opt_shared_kv = true;
+        m->opt_advance = false;
+        m->opt_limit = L;
+        m->opt_need = p + k + 1;
+        st = enqueue_step(m, k + 1, m->d_spec, nullptr, m->d_spec + 8);
+    }
+    m->opt_active = false;
+    m->opt_pos = nullptr;
+    if (st != LM_OK) return st;
+    HIPTRY(m, hipMemcpyAsync(h, m->d_spec, sizeof(h), hipMemcpyDeviceToHost, s0));
+    HIPTRY(m, hipStreamSynchronize(s0));
+    // the longest agreeing prefix of drafts, then the full model's own token
+    int n = 0;
+    while (n < k && h[8 + n] == h[1 + n]) {
+        tokens_out[n] = h[1 + n];
+        ++n;
+    }
+    tokens_out[n] = h[8 + n];
+    *n_out = n + 1;
+    m->pos[0] = p + n + 1;
+    HIPTRY(m, hipMemcpy(m->d_pos, &m->pos[0], 4, hipMemcpyHostToDevice));
+    return collect_timing(m);
 }
 
 extern "C" lm_status lm_set_persistent(lm_model* m, int32_t enable) {
