@@ -286,6 +286,40 @@ def alternatives(r, args) -> dict:
     return res
 
 
+def speculative(model, rounds: int = 12) -> dict:
+    """Self-speculative rounds on sequence 0 of the same model opened for four
+    sequences: k = 3 drafts through the bottom 8 of 32 layers, verified by one
+    pass of all layers over 4 columns; and drafts by all 32 layers (every draft
+    accepted: the verify pass's own rate).  Host-clocked, each round blocks."""
+    import synth
+    import token_decode_llama_amd as lm
+    cfg = model.cfg
+    g = lm.open_model(model, lambda s, l: synth.make_kv(cfg, s, l), max_seqs=4, kv_seqs=1)
+    res = {"k": 3}
+    try:
+        for label, d in (("draft_8_of_32", 8), ("draft_all_32", cfg.n_layers)):
+            g.set_position(0, cfg.ctx)
+            t = int(synth.start_tokens(cfg, 1)[0])
+            acc = g.speculative_step(t, d, 3)         # warm-up round
+            g.set_position(0, cfg.ctx)
+            n_tok = 0
+            t0 = time.perf_counter()
+            for _ in range(rounds):
+                acc = g.speculative_step(t, d, 3)
+                n_tok += len(acc)
+                t = int(acc[-1])
+            dt = time.perf_counter() - t0
+            res[label] = {"draft_layers": d, "rounds": rounds, "tokens": n_tok,
+                          "tokens_per_round": round(n_tok / rounds, 3), "ms_per_round": round(1e3 * dt / rounds, 3),
+                          "tokens_per_s": round(n_tok / dt, 2)}
+            log(f"speculative {label}: {n_tok} tokens in {rounds} rounds, {n_tok / dt:.1f} tok/s")
+    finally:
+        g.close()
+    res["note"] = ("random weights: the bottom layers rarely predict the full model's token, so the acceptance "
+                   "rate says nothing about trained models; the all-layer draft bounds the verify pass")
+    return res
+
+
 def run_single(args, name: str, n_seq: int):
     """llama8b_q8 (headline, batch 1) and llama8b_q4 (four sequences)."""
     import synth
@@ -333,6 +367,8 @@ def run_single(args, name: str, n_seq: int):
     if n_seq == 1 and not args.only_kernels and not args.no_alternatives:
         out["alternatives_ms_per_step"] = alternatives(r, args)
     r.close()
+    if n_seq == 1 and not args.only_kernels and not args.no_alternatives:
+        out["speculative"] = speculative(model)
     if not args.no_cpu_baseline and not args.only_kernels:
         log("oracle baseline")
         out["cpu_baseline"] = public(cpu_baseline(model, cfg, n_seq, args.cpu_budget))
