@@ -21,6 +21,8 @@ LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 Q4_0 = 2
 Q8_0 = 8
+Q4_K = 12
+Q6_K = 14
 
 
 def build() -> str:
@@ -62,6 +64,8 @@ def lib():
             "orc_f16_to_f64": ([ctypes.c_uint16], f64),
             "orc_f64_to_f16": ([f64], ctypes.c_uint16),
             "orc_block_bytes": ([i32], i32),
+            "orc_block_weights": ([i32], i32),
+            "orc_row_bytes": ([i32, i64], i64),
             "orc_dequant_row": ([i32, vp, i64, vp], i32),
             "orc_gemv": ([i32, vp, i64, i64, vp, vp], i32),
             "orc_rmsnorm": ([vp, vp, i64, f64, vp], None),
@@ -114,9 +118,9 @@ def f64_to_f16(v: float) -> int:
 
 
 def dequant(qtype: int, blocks: np.ndarray, rows: int, cols: int) -> np.ndarray:
-    """GGUF Q8_0/Q4_0 blocks [rows, cols/32*bb] -> fp64 [rows, cols]
-    (format as the workload defines it; formats named on the C/CUDA Llama
-    engine page, section 1)."""
+    """GGUF blocks [rows, row bytes] -> fp64 [rows, cols]: Q8_0/Q4_0 as the
+    workload defines them, Q4_K/Q6_K as the GGUF format publishes them (all
+    four named on the C/CUDA Llama engine page, section 1)."""
     b = np.ascontiguousarray(blocks, dtype=np.uint8).reshape(rows, -1)
     out = np.empty((rows, cols), np.float64)
     for r in range(rows):

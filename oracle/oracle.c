@@ -35,6 +35,16 @@
  * The block formats are the ones the workload states: Q8_0 = fp16 d then 32
  * int8 q, value d*q; Q4_0 = fp16 d then 16 bytes, byte j = element j (low
  * nibble) | element j+16 (high nibble), value (nibble - 8) * d.
+ * [ENGINE] section 1 also names the GGUF "K" formats Q4_K and Q6_K (the
+ * formats of its 70B figures) without defining them; their byte layout is the
+ * one the GGUF format publishes (restated in orc_dequant_row below): 256-weight
+ * super-blocks,
+ *   Q4_K (144 bytes): fp16 d, fp16 dmin, 12 bytes packing eight 6-bit scales
+ *         sc_j and eight 6-bit mins m_j (one per 32-weight sub-block j), then
+ *         128 bytes of nibbles; value d*sc_j*q - dmin*m_j, q in 0..15;
+ *   Q6_K (210 bytes): 128 bytes of low nibbles, 64 bytes of 2-bit high parts,
+ *         16 int8 scales (one per 16-weight sub-block), fp16 d; value
+ *         d*scale*(q - 32), q in 0..63.
  *
  * Readings where the pages are silent (each also listed in the design notes):
  *   RoPE rotates adjacent pairs (2i, 2i+1) by angle pos * theta^(-2i/hd), no
@@ -61,6 +71,8 @@
 
 #define ORC_Q4_0 2
 #define ORC_Q8_0 8
+#define ORC_Q4_K 12
+#define ORC_Q6_K 14
 
 /* ------------------------------------------------------------------------ */
 /* IEEE binary16 <-> fp64                                                    */
@@ -118,24 +130,88 @@ uint16_t orc_f64_to_f16(double v) {
 /* ------------------------------------------------------------------------ */
 
 int orc_block_bytes(int qtype) {
-    return qtype == ORC_Q8_0 ? 34 : (qtype == ORC_Q4_0 ? 18 : -1);
+    switch (qtype) {
+        case ORC_Q8_0: return 34;
+        case ORC_Q4_0: return 18;
+        case ORC_Q4_K: return 144;
+        case ORC_Q6_K: return 210;
+        default: return -1;
+    }
 }
 
-/* One row of `cols` weights stored as consecutive blocks -> fp64. */
+/* weights per block: 32 (Q8_0, Q4_0) or 256 (the K formats' super-blocks) */
+int orc_block_weights(int qtype) { return qtype == ORC_Q4_K || qtype == ORC_Q6_K ? 256 : 32; }
+
+/* bytes of one row of `cols` weights, or -1 for an unknown type or a ragged row */
+int64_t orc_row_bytes(int qtype, int64_t cols) {
+    int bb = orc_block_bytes(qtype), qk = orc_block_weights(qtype);
+    if (bb < 0 || cols % qk) return -1;
+    return cols / qk * bb;
+}
+
+/* Q4_K: the 6-bit scale and min of sub-block j (0..7) from the 12 packed
+ * bytes.  Sub-blocks 0..3 keep theirs in the low 6 bits of bytes j (scale) and
+ * j+4 (min); sub-blocks 4..7 keep the low 4 bits of each in byte j+4 (scale in
+ * the low nibble, min in the high one) and the top 2 bits in the spare top
+ * bits of bytes j-4 (scale) and j (min). */
+static void q4k_scale_min(const uint8_t* s, int j, int* sc, int* mn) {
+    if (j < 4) {
+        *sc = s[j] & 63;
+        *mn = s[j + 4] & 63;
+    } else {
+        *sc = (s[j + 4] & 15) | ((s[j - 4] >> 6) << 4);
+        *mn = (s[j + 4] >> 4) | ((s[j] >> 6) << 4);
+    }
+}
+
+/* One row of `cols` weights stored as consecutive blocks -> fp64 (exact). */
 int orc_dequant_row(int qtype, const uint8_t* row, int64_t cols, double* out) {
-    int bb = orc_block_bytes(qtype);
-    if (bb < 0 || cols % 32) return -1;
-    for (int64_t b = 0; b < cols / 32; ++b) {
+    const int bb = orc_block_bytes(qtype), qk = orc_block_weights(qtype);
+    if (bb < 0 || cols % qk) return -1;
+    for (int64_t b = 0; b < cols / qk; ++b) {
         const uint8_t* blk = row + b * bb;
-        uint16_t dh = (uint16_t)(blk[0] | (blk[1] << 8));
-        double d = orc_f16_to_f64(dh);
+        double* o = out + qk * b;
         if (qtype == ORC_Q8_0) {
-            for (int j = 0; j < 32; ++j) out[32 * b + j] = d * (double)(int8_t)blk[2 + j];
-        } else {
+            double d = orc_f16_to_f64((uint16_t)(blk[0] | (blk[1] << 8)));
+            for (int j = 0; j < 32; ++j) o[j] = d * (double)(int8_t)blk[2 + j];
+        } else if (qtype == ORC_Q4_0) {
+            double d = orc_f16_to_f64((uint16_t)(blk[0] | (blk[1] << 8)));
             for (int j = 0; j < 16; ++j) {
                 int lo = blk[2 + j] & 0x0F, hi = blk[2 + j] >> 4;
-                out[32 * b + j] = (double)(lo - 8) * d;
-                out[32 * b + j + 16] = (double)(hi - 8) * d;
+                o[j] = (double)(lo - 8) * d;
+                o[j + 16] = (double)(hi - 8) * d;
+            }
+        } else if (qtype == ORC_Q4_K) {
+            /* element e of the super-block: sub-block j = e / 32; the 32 bytes
+             * 32*(j/2) .. +31 of the nibble area hold sub-blocks j (even: low
+             * nibbles) and j+1 (odd: high nibbles), element e at byte e % 32 */
+            double d = orc_f16_to_f64((uint16_t)(blk[0] | (blk[1] << 8)));
+            double dmin = orc_f16_to_f64((uint16_t)(blk[2] | (blk[3] << 8)));
+            const uint8_t* scales = blk + 4;
+            const uint8_t* qs = blk + 16;
+            for (int e = 0; e < 256; ++e) {
+                int j = e / 32, sc, mn;
+                q4k_scale_min(scales, j, &sc, &mn);
+                uint8_t byte = qs[32 * (j / 2) + e % 32];
+                int q = (j % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+                o[e] = d * (double)sc * (double)q - dmin * (double)mn;
+            }
+        } else {  /* ORC_Q6_K */
+            /* element e: half h = e / 128, r = e % 128, quarter t = r / 32,
+             * l = r % 32.  Low 4 bits: byte 64h + l + 32*(t % 2), low nibble
+             * for t < 2, high nibble for t >= 2.  High 2 bits: bits 2t, 2t+1 of
+             * byte 32h + l of the high-bit area.  Scale: int8 number e / 16. */
+            const uint8_t* ql = blk;
+            const uint8_t* qh = blk + 128;
+            const int8_t* scales = (const int8_t*)(blk + 192);
+            double d = orc_f16_to_f64((uint16_t)(blk[208] | (blk[209] << 8)));
+            for (int e = 0; e < 256; ++e) {
+                int h = e / 128, r = e % 128, t = r / 32, l = r % 32;
+                uint8_t lb = ql[64 * h + l + 32 * (t % 2)];
+                int lo = t < 2 ? (lb & 0x0F) : (lb >> 4);
+                int hi = (qh[32 * h + l] >> (2 * t)) & 3;
+                int q = lo | (hi << 4);
+                o[e] = d * (double)scales[e / 16] * (double)(q - 32);
             }
         }
     }
@@ -147,9 +223,8 @@ int orc_dequant_row(int qtype, const uint8_t* row, int64_t cols, double* out) {
 /* y[r] = sum_c W[r][c] * x[c], W dequantised exactly, summed in order of c. */
 /* ------------------------------------------------------------------------ */
 int orc_gemv(int qtype, const uint8_t* w, int64_t rows, int64_t cols, const double* x, double* y) {
-    int bb = orc_block_bytes(qtype);
-    if (bb < 0 || cols % 32) return -1;
-    const int64_t row_bytes = cols / 32 * bb;
+    const int64_t row_bytes = orc_row_bytes(qtype, cols);
+    if (row_bytes < 0) return -1;
     #pragma omp parallel
     {
         double* wr = (double*)malloc(sizeof(double) * (size_t)cols);

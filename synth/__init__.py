@@ -33,7 +33,18 @@ LIB_PATH = os.path.join(_HERE, "libsynth.so")
 
 Q4_0 = 2
 Q8_0 = 8
-BLOCK_BYTES = {Q8_0: 34, Q4_0: 18}
+Q4_K = 12
+Q6_K = 14
+BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q4_K: 144, Q6_K: 210}     # bytes per block
+BLOCK_WEIGHTS = {Q8_0: 32, Q4_0: 32, Q4_K: 256, Q6_K: 256}   # weights per block
+QTYPE_NAMES = {Q8_0: "Q8_0", Q4_0: "Q4_0", Q4_K: "Q4_K", Q6_K: "Q6_K"}
+
+
+def row_bytes(qtype: int, cols: int) -> int:
+    """Bytes of one row of `cols` weights in GGUF blocks."""
+    if cols % BLOCK_WEIGHTS[qtype]:
+        raise ValueError(f"{cols} columns is not a multiple of the {QTYPE_NAMES[qtype]} block")
+    return cols // BLOCK_WEIGHTS[qtype] * BLOCK_BYTES[qtype]
 
 
 def build() -> str:
@@ -98,9 +109,9 @@ def f64_to_f16_bits(v: float) -> int:
 
 
 def quantize(w: np.ndarray, qtype: int) -> np.ndarray:
-    """Quantise fp32 values (length a multiple of 32) into GGUF blocks."""
+    """Quantise fp32 values (length a multiple of the block size) into GGUF blocks."""
     w = np.ascontiguousarray(w, dtype=np.float32).ravel()
-    out = np.zeros(w.size // 32 * BLOCK_BYTES[qtype], np.uint8)
+    out = np.zeros(row_bytes(qtype, w.size), np.uint8)
     if lib().synth_quantize(_ptr(w), w.size, qtype, _ptr(out)) != 0:
         raise ValueError("bad quantize arguments")
     return out
@@ -125,8 +136,8 @@ def uniform_int(seed, tid, n, bound) -> np.ndarray:
 
 
 def quant_matrix(seed, tid, rows, cols, std, qtype) -> np.ndarray:
-    """rows x cols matrix of (float)(std*z), quantised: uint8 [rows, cols/32*bb]."""
-    out = np.empty((rows, cols // 32 * BLOCK_BYTES[qtype]), np.uint8)
+    """rows x cols matrix of (float)(std*z), quantised: uint8 [rows, row_bytes(qtype, cols)]."""
+    out = np.empty((rows, row_bytes(qtype, cols)), np.uint8)
     if lib().synth_quant_matrix(seed, tid, rows, cols, std, qtype, _ptr(out)) != 0:
         raise ValueError("bad quant_matrix arguments")
     return out
@@ -164,11 +175,12 @@ class ModelConfig:
 
     def weight_bytes(self) -> int:
         """Quantised weight bytes read per token (all layers + LM head)."""
-        bb = BLOCK_BYTES[self.qtype]
+        qt = self.qtype
         H, F = self.hidden, self.ffn
         qkv = (self.n_heads + 2 * self.n_kv_heads) * self.head_dim
-        per_layer = (qkv * H + H * self.n_heads * self.head_dim + 2 * F * H + H * F) // 32 * bb
-        return per_layer * self.n_layers + self.vocab * H // 32 * bb
+        per_layer = (qkv * row_bytes(qt, H) + H * row_bytes(qt, self.n_heads * self.head_dim)
+                     + 2 * F * row_bytes(qt, H) + H * row_bytes(qt, F))
+        return per_layer * self.n_layers + self.vocab * row_bytes(qt, H)
 
 
 def _cfg(**kw) -> ModelConfig:

@@ -23,6 +23,23 @@
  *         j+16 in its high nibble.  18 bytes per block.
  * round() is half away from zero (C roundf); q uses the fp32 d before it is
  * rounded to fp16; an all-zero block has d = 0 and q = 0 (Q8_0) / 8 (Q4_0).
+ *
+ * The GGUF "K" formats (the same page names Q4_K and Q6_K, the formats of its
+ * 70B figures, without defining them; the byte layout is GGUF's published
+ * one): 256-weight super-blocks.  This generator's own recipe:
+ *   Q4_K (144 bytes): per 32-weight sub-block j, mn_j = max(0, -min w) and
+ *         s_j = (max w + mn_j)/15; d = max_j s_j / 63, dmin = max_j mn_j / 63
+ *         (fp32, stored fp16); sc_j = round(s_j/d), m_j = round(mn_j/dmin)
+ *         clamped to 0..63; q = clamp(round((w + dmin*m_j)/(d*sc_j)), 0, 15).
+ *         Layout: fp16 d, fp16 dmin, 12 bytes of packed 6-bit sc/m, 128 bytes
+ *         of nibbles (bytes 32g..32g+31 hold sub-block 2g in their low
+ *         nibbles and sub-block 2g+1 in their high nibbles).
+ *   Q6_K (210 bytes): per 16-weight sub-block k, s_k = max|w|/31;
+ *         d = max_k s_k / 127; sc_k = round(s_k/d) (0..127, stored int8);
+ *         q = clamp(round(w/(d*sc_k)), -32, 31) + 32.  Layout: 128 bytes of
+ *         low nibbles, 64 bytes of 2-bit high parts, 16 int8 scales, fp16 d.
+ * d, dmin and the sub-block scales use the fp32 values before any rounding;
+ * a zero scale gives q = 0 (Q4_K) / 32 (Q6_K).
  */
 #include <math.h>
 #include <stdint.h>
@@ -30,6 +47,8 @@
 
 #define SYN_Q4_0 2
 #define SYN_Q8_0 8
+#define SYN_Q4_K 12
+#define SYN_Q6_K 14
 
 /* ---- Philox4x32-10 (Salmon et al. SC'11, section 3.2 / table 2 constants) */
 static inline void mulhilo32(uint32_t a, uint32_t b, uint32_t* hi, uint32_t* lo) {
@@ -152,18 +171,112 @@ static void quant_block_q4_0(const float* w, uint8_t* out) {
     for (int j = 0; j < 16; ++j) out[2 + j] = (uint8_t)(q[j] | (q[j + 16] << 4));
 }
 
-static int block_bytes(int qtype) {
-    return qtype == SYN_Q8_0 ? 34 : (qtype == SYN_Q4_0 ? 18 : -1);
+static void quant_block_q4_k(const float* w, uint8_t* out) {
+    float s[8], mn[8], smax = 0.0f, mmax = 0.0f;
+    for (int j = 0; j < 8; ++j) {
+        float lo = w[32 * j], hi = w[32 * j];
+        for (int i = 1; i < 32; ++i) {
+            if (w[32 * j + i] < lo) lo = w[32 * j + i];
+            if (w[32 * j + i] > hi) hi = w[32 * j + i];
+        }
+        mn[j] = lo < 0.0f ? -lo : 0.0f;
+        s[j] = (hi + mn[j]) / 15.0f;
+        if (s[j] > smax) smax = s[j];
+        if (mn[j] > mmax) mmax = mn[j];
+    }
+    const float d = smax / 63.0f, dmin = mmax / 63.0f;
+    uint16_t dh = synth_f64_to_f16((double)d), mh = synth_f64_to_f16((double)dmin);
+    memcpy(out, &dh, 2);
+    memcpy(out + 2, &mh, 2);
+    int sc[8], m[8];
+    for (int j = 0; j < 8; ++j) {
+        int a = d > 0.0f ? (int)roundf(s[j] / d) : 0, b = dmin > 0.0f ? (int)roundf(mn[j] / dmin) : 0;
+        sc[j] = a < 0 ? 0 : (a > 63 ? 63 : a);
+        m[j] = b < 0 ? 0 : (b > 63 ? 63 : b);
+    }
+    uint8_t* p = out + 4;
+    for (int j = 0; j < 4; ++j) {
+        p[j] = (uint8_t)(sc[j] | ((sc[j + 4] >> 4) << 6));
+        p[j + 4] = (uint8_t)(m[j] | ((m[j + 4] >> 4) << 6));
+        p[j + 8] = (uint8_t)((sc[j + 4] & 15) | ((m[j + 4] & 15) << 4));
+    }
+    int q[256];
+    for (int e = 0; e < 256; ++e) {
+        const int j = e / 32;
+        const float es = d * (float)sc[j], em = dmin * (float)m[j];
+        int v = 0;
+        if (es > 0.0f) {
+            v = (int)roundf((w[e] + em) / es);
+            if (v < 0) v = 0;
+            if (v > 15) v = 15;
+        }
+        q[e] = v;
+    }
+    uint8_t* qs = out + 16;
+    for (int g = 0; g < 4; ++g)
+        for (int l = 0; l < 32; ++l) qs[32 * g + l] = (uint8_t)(q[64 * g + l] | (q[64 * g + 32 + l] << 4));
 }
 
-/* Quantise n fp32 values (n a multiple of 32) into consecutive blocks. */
-int synth_quantize(const float* w, int64_t n, int qtype, uint8_t* out) {
-    int bb = block_bytes(qtype);
-    if (bb < 0 || n % 32 != 0) return -1;
-    for (int64_t b = 0; b < n / 32; ++b) {
-        if (qtype == SYN_Q8_0) quant_block_q8_0(w + 32 * b, out + bb * b);
-        else quant_block_q4_0(w + 32 * b, out + bb * b);
+static void quant_block_q6_k(const float* w, uint8_t* out) {
+    float s[16], smax = 0.0f;
+    for (int k = 0; k < 16; ++k) {
+        float amax = 0.0f;
+        for (int i = 0; i < 16; ++i) { float a = fabsf(w[16 * k + i]); if (a > amax) amax = a; }
+        s[k] = amax / 31.0f;
+        if (s[k] > smax) smax = s[k];
     }
+    const float d = smax / 127.0f;
+    int sc[16];
+    for (int k = 0; k < 16; ++k) {
+        int a = d > 0.0f ? (int)roundf(s[k] / d) : 0;
+        sc[k] = a < 0 ? 0 : (a > 127 ? 127 : a);
+    }
+    uint8_t* ql = out;
+    uint8_t* qh = out + 128;
+    memset(out, 0, 192);
+    for (int e = 0; e < 256; ++e) {
+        const float es = d * (float)sc[e / 16];
+        int v = 32;
+        if (es > 0.0f) {
+            v = (int)roundf(w[e] / es);
+            if (v < -32) v = -32;
+            if (v > 31) v = 31;
+            v += 32;
+        }
+        const int h = e / 128, r = e % 128, t = r / 32, l = r % 32;
+        ql[64 * h + l + 32 * (t % 2)] |= (uint8_t)((v & 15) << (t < 2 ? 0 : 4));
+        qh[32 * h + l] |= (uint8_t)((v >> 4) << (2 * t));
+    }
+    for (int k = 0; k < 16; ++k) out[192 + k] = (uint8_t)(int8_t)sc[k];
+    uint16_t dh = synth_f64_to_f16((double)d);
+    memcpy(out + 208, &dh, 2);
+}
+
+static int block_bytes(int qtype) {
+    switch (qtype) {
+        case SYN_Q8_0: return 34;
+        case SYN_Q4_0: return 18;
+        case SYN_Q4_K: return 144;
+        case SYN_Q6_K: return 210;
+        default: return -1;
+    }
+}
+static int block_weights(int qtype) { return qtype == SYN_Q4_K || qtype == SYN_Q6_K ? 256 : 32; }
+
+static void quant_block(int qtype, const float* w, uint8_t* out) {
+    switch (qtype) {
+        case SYN_Q8_0: quant_block_q8_0(w, out); break;
+        case SYN_Q4_0: quant_block_q4_0(w, out); break;
+        case SYN_Q4_K: quant_block_q4_k(w, out); break;
+        default: quant_block_q6_k(w, out); break;
+    }
+}
+
+/* Quantise n fp32 values (n a multiple of the block size) into consecutive blocks. */
+int synth_quantize(const float* w, int64_t n, int qtype, uint8_t* out) {
+    const int bb = block_bytes(qtype), qk = block_weights(qtype);
+    if (bb < 0 || n % qk != 0) return -1;
+    for (int64_t b = 0; b < n / qk; ++b) quant_block(qtype, w + qk * b, out + bb * b);
     return 0;
 }
 
@@ -216,26 +329,25 @@ void synth_uniform_int(uint64_t seed, uint64_t tensor_id, int64_t n, uint32_t bo
  */
 int synth_quant_matrix(uint64_t seed, uint64_t tensor_id, int64_t rows, int64_t cols,
                        double std, int qtype, uint8_t* out) {
-    int bb = block_bytes(qtype);
-    if (bb < 0 || cols % 32 != 0 || rows < 0) return -1;
+    const int bb = block_bytes(qtype), qk = block_weights(qtype);
+    if (bb < 0 || cols % qk != 0 || rows < 0) return -1;
     uint32_t key[2];
     stream_key(seed, tensor_id, key);
-    const int64_t nb = cols / 32;
+    const int64_t nb = cols / qk;
     const int64_t total = rows * nb;
     #pragma omp parallel
     {
-        float w[32];
+        float w[256];
         #pragma omp for schedule(static)
         for (int64_t blk = 0; blk < total; ++blk) {
-            uint64_t base = (uint64_t)blk * 32u; /* = r*cols + b*32 */
-            /* 32 consecutive elements = 8 Philox counters, aligned to 4 */
-            for (int c4 = 0; c4 < 8; ++c4) {
+            uint64_t base = (uint64_t)blk * (uint64_t)qk; /* = r*cols + b*qk */
+            /* qk consecutive elements = qk/4 Philox counters, aligned to 4 */
+            for (int c4 = 0; c4 < qk / 4; ++c4) {
                 double z[4];
                 normals4(key, (base >> 2) + (uint64_t)c4, z);
                 for (int t = 0; t < 4; ++t) w[4 * c4 + t] = (float)(std * z[t]);
             }
-            if (qtype == SYN_Q8_0) quant_block_q8_0(w, out + bb * blk);
-            else quant_block_q4_0(w, out + bb * blk);
+            quant_block(qtype, w, out + bb * blk);
         }
     }
     return 0;
