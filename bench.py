@@ -16,7 +16,13 @@ Other workloads (--workload), each printing one JSON line of its own:
                its own HIP stream; value = aggregate tokens/s
   llama70b_q4  70B shape, Q4_0, KV context 1024, 16 steps: (a) all weights
                resident in HBM, then (b) layer streaming from pinned host
-               memory through two HBM layer buffers
+               memory through two HBM layer buffers, (c) the engine page's
+               hybrid split, (d) streaming with 20 layers skipped
+  llama8b_q4k, llama8b_q6k    8B shape in the GGUF K formats, batch 1, KV
+               context 512 (+64 steps), weights resident
+  llama70b_q4k, llama70b_q6k  70B shape in the K formats, as llama70b_q4;
+               the hybrid split is the page's for that format (Q4_K_M: 36
+               of 80 layers in GPU memory, Q6_K: 26)
 
 Every line carries:
   value           decode tokens/s over the timed steps (whole job; one GPU)
@@ -53,6 +59,13 @@ WORKLOAD_TEXT = {
     "llama70b_q4": "Llama-3.1-70B-shaped synthetic decoder (vocab 128256, hidden 8192, 80 layers, "
                    "64/8 heads, hd 128, ffn 28672), Q4_0 weights, batch 1, KV context 1024 (+steps)",
 }
+for _qt in ("q4k", "q6k"):
+    _fmt = {"q4k": "Q4_K", "q6k": "Q6_K"}[_qt]
+    WORKLOAD_TEXT[f"llama8b_{_qt}"] = (f"Llama-3.1-8B-shaped synthetic decoder ({SHAPE_8B}), {_fmt} weights "
+                                       "resident in HBM, batch 1, KV context 512 (+steps), greedy decode")
+    WORKLOAD_TEXT[f"llama70b_{_qt}"] = WORKLOAD_TEXT["llama70b_q4"].replace("Q4_0", _fmt)
+# layers in GPU memory in the engine page's 70B figures (section 1 table: Q6_K 26 of 80, Q4_K_M 36 of 80)
+HYBRID_RESIDENT = {"llama70b_q4": 36, "llama70b_q4k": 36, "llama70b_q6k": 26}
 KERNEL_NAMES = {
     "qkv": "k_gemv<QKV, RMSNorm prologue, RoPE + KV-append epilogue>",
     "attn": "k_attn + k_attn_merge (GQA decode attention)",
@@ -346,12 +359,15 @@ def run_single(args, name: str, n_seq: int):
                           "times between two HIP events on the model's stream")
     roofline["avg_launch_us_events_in_step"] = round(1e3 * kstats[dom][1] / max(kstats[dom][0], 1), 3)
     step_bytes = r.step_bytes(args.steps // 2)
-    read_ms = r.g.debug_read_bw(4 << 30, 5)
+    # plain-read ceiling over (at most) 4 GiB of the resident layer arena
+    n_read = min(4 << 30, (cfg.weight_bytes() - cfg.vocab * synth.row_bytes(cfg.qtype, cfg.hidden)) // 16 * 16)
+    read_ms = r.g.debug_read_bw(n_read, 5)
     if args.calibrate:
         r.g.debug_read_bw(1 << 30, 1)
         r.g.debug_dequant(0, 6, 0, 64, cfg.ffn)
         log(f"calibration: read {1 << 30} bytes; dequant wrote {64 * cfg.ffn * 4} bytes")
-    qt = "Q8_0" if cfg.qtype == synth.Q8_0 else "Q4_0"
+    qt = synth.QTYPE_NAMES[cfg.qtype]
+    one_launch = cfg.qtype in (synth.Q8_0, synth.Q4_0)      # the opt-in step paths and batched verify
     config = {"workload": WORKLOAD_TEXT[name], "name": name, "batch": n_seq, "ctx": base.ctx, "qtype": qt,
               "weights": "random N(0,0.02), quantized, resident in HBM"}
     metric = HEADLINE_METRIC if name == "llama8b_q8" else \
@@ -362,12 +378,12 @@ def run_single(args, name: str, n_seq: int):
     else:
         out = {"metric": metric, "config": config}
     out["roofline"] = roofline
-    out["read_ceiling_GBps"] = round((4 << 30) / (read_ms * 1e-3) / 1e9, 1)
+    out["read_ceiling_GBps"] = round(n_read / (read_ms * 1e-3) / 1e9, 1)
     out["kernels"] = kernel_table(kstats, kbytes, L)
-    if n_seq == 1 and not args.only_kernels and not args.no_alternatives:
+    if n_seq == 1 and one_launch and not args.only_kernels and not args.no_alternatives:
         out["alternatives_ms_per_step"] = alternatives(r, args)
     r.close()
-    if n_seq == 1 and not args.only_kernels and not args.no_alternatives:
+    if n_seq == 1 and one_launch and not args.only_kernels and not args.no_alternatives:
         out["speculative"] = speculative(model)
     if not args.no_cpu_baseline and not args.only_kernels:
         log("oracle baseline")
@@ -435,15 +451,15 @@ def run_multi(args):
     return out
 
 
-def run_70b(args):
+def run_70b(args, name="llama70b_q4"):
     """(a) resident in HBM, (b) layer streaming from pinned host memory, (c) the
-    first 36 layers resident and the other 44 streamed, (d) streamed with the 20
-    most similar layers skipped."""
+    engine page's split for the format (Q4_0 and Q4_K: the first 36 layers
+    resident and the other 44 streamed; Q6_K: 26 and 54), (d) streamed with the
+    20 most similar layers skipped."""
     import numpy as np
     import torch
     import synth
     import token_decode_llama_amd as lm
-    name = "llama70b_q4"
     extra = max(args.steps, args.warmup, args.timing_steps, 1)
     cfg = synth.variant(name, steps=extra)
     s, H, V = cfg.seed, cfg.hidden, cfg.vocab
@@ -499,10 +515,13 @@ def run_70b(args):
     t_copy = sk["copy"][1] / n_st
     t_comp = sum(ms for k, (n, ms) in sk.items() if k != "copy") / n_st
     overlap = (t_copy + t_comp - ms_st_timed) / min(t_copy, t_comp) if min(t_copy, t_comp) > 0 else None
-    config = {"workload": WORKLOAD_TEXT[name], "name": name, "batch": 1, "ctx": cfg.ctx, "qtype": "Q4_0",
+    qt = synth.QTYPE_NAMES[cfg.qtype]
+    k_h = HYBRID_RESIDENT[name]
+    config = {"workload": WORKLOAD_TEXT[name], "name": name, "batch": 1, "ctx": cfg.ctx, "qtype": qt,
               "weights": "random N(0,0.02), quantized; (a) resident in HBM, (b) streamed per layer from "
-                         "pinned host memory, (c) first 36 layers resident, the other 44 streamed"}
-    out = base_line("decode tokens/s + achieved HBM GB/s, 70B-shape Q4_0 batch 1, weights resident in HBM",
+                         f"pinned host memory, (c) first {k_h} layers resident, the other "
+                         f"{cfg.n_layers - k_h} streamed"}
+    out = base_line(f"decode tokens/s + achieved HBM GB/s, 70B-shape {qt} batch 1, weights resident in HBM",
                     1000.0 / ms_res, ms_res, args.steps, args.warmup, step_bytes, config)
     out["roofline"] = roof
     out["kernels"] = ktab
@@ -518,9 +537,9 @@ def run_70b(args):
         "overlap_definition": "(sum copy + sum compute - wall) / min(sum copy, sum compute), per step, all "
                               "three from the same steps with HIP events around every copy and kernel",
         "resident_compute_ms_eager": round(compute_ms, 3)}
-    # (c) hybrid residency: the pages' 70B Q4_K_M split, 36 of 80 layers in GPU
-    # memory and 44 streamed; and what the tier sizing rule gives for a 24 GiB card
-    k_h = 36
+    # (c) hybrid residency: the pages' 70B split for this format (Q4_K_M: 36 of
+    # 80 layers in GPU memory; Q6_K: 26); and what the tier sizing rule gives
+    # for a 24 GiB card
     log(f"hybrid: {k_h} of {cfg.n_layers} layers resident")
     r.g.set_residency(k_h)
     r.warm(1)
@@ -572,7 +591,8 @@ def main():
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default: the workload's own)")
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama8b_q8",
-                    choices=["llama8b_q8", "llama8b_q4", "multi", "llama70b_q4"])
+                    choices=["llama8b_q8", "llama8b_q4", "multi", "llama70b_q4", "llama8b_q4k",
+                             "llama8b_q6k", "llama70b_q4k", "llama70b_q6k"])
     ap.add_argument("--timing-steps", type=int, default=8,
                     help="eager steps with per-kernel HIP events for the roofline")
     ap.add_argument("--stream-steps", type=int, default=16, help="timed steps in layer-streaming mode (70B)")
@@ -593,7 +613,8 @@ def main():
               "(the per-GPU throughput is the --gpus 1 figure)", file=sys.stderr)
         sys.exit(2)
     if args.steps is None:
-        args.steps = {"llama8b_q8": 64, "llama8b_q4": 32, "multi": 32, "llama70b_q4": 16}[args.workload]
+        args.steps = {"llama8b_q8": 64, "llama8b_q4": 32, "multi": 32, "llama70b_q4": 16, "llama8b_q4k": 64,
+                      "llama8b_q6k": 64, "llama70b_q4k": 16, "llama70b_q6k": 16}[args.workload]
 
     import torch
     if not torch.cuda.is_available():
@@ -604,10 +625,12 @@ def main():
         out = run_single(args, "llama8b_q8", 1)
     elif args.workload == "llama8b_q4":
         out = run_single(args, "llama8b_q4", 4)
+    elif args.workload in ("llama8b_q4k", "llama8b_q6k"):
+        out = run_single(args, args.workload, 1)
     elif args.workload == "multi":
         out = run_multi(args)
     else:
-        out = run_70b(args)
+        out = run_70b(args, args.workload)
     print(json.dumps(out), flush=True)
 
 

@@ -56,11 +56,24 @@ typedef enum {
     LM_E_CTX = 5     /* the step would run past max_ctx */
 } lm_status;
 
-/* GGUF type ids of the two block formats.
+/* GGUF type ids of the block formats (the C/CUDA Llama engine page, section 1,
+ * lists Q4_0, Q8_0, Q4_K and Q6_K among the formats it reads; the K formats
+ * carry its 70B figures).
  * Q8_0: 34-byte block = fp16 d (little endian) + 32 int8 q; w = d * q.
  * Q4_0: 18-byte block = fp16 d + 16 bytes; byte j holds element j in its low
- *       nibble and element j+16 in its high nibble; w = (nibble - 8) * d. */
-typedef enum { LM_Q4_0 = 2, LM_Q8_0 = 8 } lm_qtype;
+ *       nibble and element j+16 in its high nibble; w = (nibble - 8) * d.
+ * Q4_K: 144-byte super-block of 256 weights (GGUF's published layout) = fp16
+ *       d, fp16 dmin, 12 bytes packing a 6-bit scale sc_j and a 6-bit min m_j
+ *       per 32-weight sub-block j, 128 bytes of nibbles (32-byte group g:
+ *       sub-block 2g in the low nibbles, 2g+1 in the high ones);
+ *       w = d * sc_j * q - dmin * m_j.
+ * Q6_K: 210-byte super-block of 256 weights = 128 bytes of low nibbles, 64
+ *       bytes of 2-bit high parts, 16 int8 scales (one per 16 weights), fp16
+ *       d; w = d * scale * (q - 32), q = 6 bits.
+ * The K formats need every matrix input width (hidden, ffn, n_heads *
+ * head_dim) to be a multiple of 256 and decode one sequence per step
+ * (max_seqs = 1); the one-launch step modes are not built for them. */
+typedef enum { LM_Q4_0 = 2, LM_Q8_0 = 8, LM_Q4_K = 12, LM_Q6_K = 14 } lm_qtype;
 
 typedef struct {
     int32_t vocab;       /* rows of the LM head, rows of the embedding table */
@@ -74,11 +87,12 @@ typedef struct {
     double rope_theta;   /* RoPE base: pair i turns by p * theta^(-2i/hd) */
     int32_t max_ctx;     /* KV positions per sequence */
     int32_t max_seqs;    /* sequences decoded together (1..4; 2..4 need hidden <= 8192) */
-    int32_t qtype;       /* LM_Q8_0 or LM_Q4_0, for every weight matrix */
+    int32_t qtype;       /* an lm_qtype, for every weight matrix (the LM head included) */
 } lm_config;
 
 /* One decoder layer's weights.  Norm gains: fp32 [hidden].  Matrices: GGUF
- * block bytes, row-major [out rows][in/32 blocks]:
+ * block bytes, row-major [out rows][in/32 blocks] (in/256 super-blocks for
+ * the K formats):
  *   wq [nq*hd][H], wk [nkv*hd][H], wv [nkv*hd][H], wo [H][nq*hd],
  *   w_gate [F][H], w_up [F][H], w_down [H][F]. */
 typedef struct {

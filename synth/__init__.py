@@ -1,20 +1,22 @@
 """Seeded synthetic inputs shared by the oracle and the HIP library.
 
 Only input generation lives here (random numbers, random models already in
-the GGUF Q8_0/Q4_0 block formats, fp16 tables, token ids); none of the decode
+the GGUF Q8_0/Q4_0/Q4_K/Q6_K block formats, fp16 tables, token ids); none of the decode
 step's arithmetic does.  The C core is ``synth.c``; ``build()`` compiles it.
 
 Workloads (the decode-step configurations this project is measured on):
 
-==========  ==============================================================
-tiny        vocab 512, hidden 256, 2 layers, 4/2 heads, hd 64, ffn 704,
-            Q8_0, 16 cached positions, 4 greedy steps, seed 0
-llama8b_q8  Llama-3.1-8B shape, Q8_0, ctx 512 (+64 steps), batch 1, seed 1
-llama8b_q4  Llama-3.1-8B shape, Q4_0, ctx 4096 (+32 steps), batch 4, seed 2
-multi_*     Llama-3.2-1B / Qwen2-0.5B / SmolLM2-360M shapes, Q8_0, ctx 2048,
-            32 steps each, seed 3, tensor-id namespaces 0/1/2
-llama70b_q4 Llama-3.1-70B shape, Q4_0, ctx 1024, 16 steps, seed 4
-==========  ==============================================================
+* tiny: vocab 512, hidden 256, 2 layers, 4/2 heads, hd 64, ffn 704, Q8_0,
+  16 cached positions, 4 greedy steps, seed 0
+* llama8b_q8: Llama-3.1-8B shape, Q8_0, ctx 512 (+64 steps), batch 1, seed 1
+* llama8b_q4: Llama-3.1-8B shape, Q4_0, ctx 4096 (+32 steps), batch 4, seed 2
+* multi_*: Llama-3.2-1B / Qwen2-0.5B / SmolLM2-360M shapes, Q8_0, ctx 2048,
+  32 steps each, seed 3, tensor-id namespaces 0/1/2
+* llama70b_q4: Llama-3.1-70B shape, Q4_0, ctx 1024, 16 steps, seed 4
+* llama8b_q4k / llama8b_q6k: the 8B shape in Q4_K / Q6_K, ctx 512 (+64 steps),
+  batch 1, seeds 5 / 6
+* llama70b_q4k / llama70b_q6k: the 70B shape in Q4_K / Q6_K, ctx 1024,
+  16 steps, seeds 7 / 8
 
 Distributions: weights N(0, 0.02) quantised block by block; fp16 token
 embeddings N(0, 0.02); fp32 norm gains N(1, 0.1); fp16 KV N(0, 1) for every
@@ -208,6 +210,19 @@ CONFIGS = {
     "llama70b_q4": _cfg(name="llama70b_q4", vocab=128256, hidden=8192, n_layers=80,
                         n_heads=64, n_kv_heads=8, head_dim=128, ffn=28672, qtype=Q4_0,
                         ctx=1024, steps=16, batch=1, seed=4),
+    # the GGUF K formats of the engine page's 70B figures, on the 8B and 70B shapes
+    "llama8b_q4k": _cfg(name="llama8b_q4k", vocab=128256, hidden=4096, n_layers=32, n_heads=32,
+                        n_kv_heads=8, head_dim=128, ffn=14336, qtype=Q4_K, ctx=512, steps=64,
+                        batch=1, seed=5),
+    "llama8b_q6k": _cfg(name="llama8b_q6k", vocab=128256, hidden=4096, n_layers=32, n_heads=32,
+                        n_kv_heads=8, head_dim=128, ffn=14336, qtype=Q6_K, ctx=512, steps=64,
+                        batch=1, seed=6),
+    "llama70b_q4k": _cfg(name="llama70b_q4k", vocab=128256, hidden=8192, n_layers=80,
+                         n_heads=64, n_kv_heads=8, head_dim=128, ffn=28672, qtype=Q4_K,
+                         ctx=1024, steps=16, batch=1, seed=7),
+    "llama70b_q6k": _cfg(name="llama70b_q6k", vocab=128256, hidden=8192, n_layers=80,
+                         n_heads=64, n_kv_heads=8, head_dim=128, ffn=28672, qtype=Q6_K,
+                         ctx=1024, steps=16, batch=1, seed=8),
 }
 
 

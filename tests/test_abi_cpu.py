@@ -107,3 +107,25 @@ def test_tier_sizes_rejects_bad_arguments():
     assert L.lm_tier_sizes(0, 10, 10, 10, ctypes.byref(a), ctypes.byref(b)) == lm.LM_E_ARG
     assert L.lm_tier_sizes(80, 10, -1, 10, ctypes.byref(a), ctypes.byref(b)) == lm.LM_E_ARG
     assert L.lm_tier_sizes(80, 10, 10, 10, None, ctypes.byref(b)) == lm.LM_E_ARG
+
+
+@pytest.mark.parametrize("changes,needle", [
+    (dict(ffn=704), "ffn"),                               # 704 = 2.75 super-blocks
+    (dict(hidden=288, n_heads=4, head_dim=64), "hidden"),
+    (dict(n_heads=2, n_kv_heads=2, head_dim=64, hidden=256), "n_heads * head_dim"),
+    (dict(max_seqs=2), "max_seqs"),
+])
+@pytest.mark.parametrize("qtype", [lm.LM_Q4_K, lm.LM_Q6_K])
+def test_create_rejects_k_formats_outside_their_shapes(qtype, changes, needle):
+    """Q4_K / Q6_K: 256-weight super-blocks along every GEMV input, one
+    sequence per step; checked before any device call."""
+    L = lm.load()
+    d = _good()
+    d.update(ffn=768, qtype=qtype)
+    d.update(changes)
+    c = lm.Config(**d)
+    h = ctypes.c_void_p(123)
+    assert L.lm_model_create(ctypes.byref(c), None, ctypes.byref(h)) == lm.LM_E_ARG
+    assert not h.value
+    msg = L.lm_last_error(None).decode()
+    assert needle in msg and "expected" in msg

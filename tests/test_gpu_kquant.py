@@ -1,0 +1,116 @@
+"""GGUF K formats (Q4_K, Q6_K) on the batch-1 path against the fp64 oracle.
+
+The C/CUDA Llama engine page, section 1, lists both among the formats it reads
+and quotes its 70B figures in them.  Same bar as the Q8_0 / Q4_0 parity tests:
+dequantisation bit-exact, logits within 1e-3 max|logit| per step, the argmax
+equal, appended K/V rows within one fp16 ulp plus the fp32 error.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth import Q4_K, Q6_K
+from tests.helpers import log, open_gpu
+from tests.test_gpu_parity import run_parity
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # one super-block per hidden row (8 blocks: a lane group of 8, one block each)
+    "tiny_q4k": synth.variant("tiny", qtype=Q4_K, ffn=768),
+    "tiny_q6k": synth.variant("tiny", qtype=Q6_K, ffn=768),
+    # 64 blocks per row: half of every lane's second pipeline slot is past the row end
+    "llama1b_q4k_2layers": synth.variant("multi_llama1b", n_layers=2, qtype=Q4_K, ctx=64, steps=3),
+    "llama1b_q6k_2layers": synth.variant("multi_llama1b", n_layers=2, qtype=Q6_K, ctx=64, steps=3),
+    # 8B layer shapes (down: 448 blocks per row, a ragged last chunk), context crossing a chunk
+    "llama8b_q4k_2layers_ctx127": synth.variant("llama8b_q8", n_layers=2, qtype=Q4_K, ctx=127, steps=3),
+    "llama8b_q6k_2layers_ctx127": synth.variant("llama8b_q8", n_layers=2, qtype=Q6_K, ctx=127, steps=3),
+    # the 70B shape's layers (hidden 8192, ffn 28672, 64/8 heads) at its context length
+    "llama70b_q4k_2layers": synth.variant("llama70b_q4", n_layers=2, qtype=Q4_K, steps=2),
+    "llama70b_q6k_2layers": synth.variant("llama70b_q4", n_layers=2, qtype=Q6_K, steps=2),
+}
+
+_models = {}
+
+
+def get_model(name):
+    if name not in _models:
+        log("generate", name)
+        _models[name] = synth.make_model(CASES[name])
+    return _models[name]
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_kquant_decode_parity(name):
+    run_parity(get_model(name), n_seq=1)
+
+
+@pytest.mark.parametrize("name", ["tiny_q4k", "tiny_q6k", "llama1b_q4k_2layers", "llama1b_q6k_2layers"])
+def test_kquant_dequant_bit_exact_all_rows(name):
+    model = get_model(name)
+    cfg = model.cfg
+    g = open_gpu(model, max_seqs=1)
+    try:
+        H, F, Q, KV = cfg.hidden, cfg.ffn, cfg.n_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
+        for l, w in enumerate(model.layers):
+            for which, (arr, rows, cols) in enumerate([(w.wq, Q, H), (w.wk, KV, H), (w.wv, KV, H),
+                                                       (w.wo, H, Q), (w.w_gate, F, H),
+                                                       (w.w_up, F, H), (w.w_down, H, F)]):
+                log(f"{name}: dequant layer {l} matrix {which}")
+                got = g.debug_dequant(l, which, 0, rows, cols)
+                ref = oracle.dequant(cfg.qtype, arr, rows, cols)
+                # fp32 result of the exact fp64 value (Q4_K: one rounding of d*sc*q - dmin*m)
+                assert np.array_equal(got, ref.astype(np.float32)), (l, which)
+        got = g.debug_dequant(0, 7, 0, cfg.vocab, H)
+        assert np.array_equal(got, oracle.dequant(cfg.qtype, model.lm_head, cfg.vocab, H).astype(np.float32))
+    finally:
+        g.close()
+
+
+@pytest.mark.parametrize("name", ["tiny_q4k", "llama1b_q6k_2layers"])
+def test_kquant_streaming_and_hybrid_bit_identical(name):
+    """Layer streaming and every resident prefix give the resident outputs bit for bit."""
+    model = get_model(name)
+    cfg = model.cfg
+    g = open_gpu(model, max_seqs=1)
+    try:
+        toks = synth.start_tokens(cfg, 1)
+
+        def run():
+            g.set_position(0, cfg.ctx)
+            res, t = [], toks
+            for _ in range(cfg.steps):
+                lg, am = g.step(t)
+                res.append((lg.copy(), am.copy()))
+                t = am
+            return res
+
+        ref = run()
+        g.stream_mode(True)
+        runs = [run()]
+        g.stream_mode(False)
+        for k in range(cfg.n_layers + 1):
+            g.set_residency(k)
+            runs.append(run())
+        for other in runs:
+            for (a, b), (c, d) in zip(ref, other):
+                assert np.array_equal(a, c) and np.array_equal(b, d)
+    finally:
+        g.close()
+
+
+def test_kquant_one_launch_modes_rejected():
+    """The one-launch step modes are built for Q8_0 / Q4_0 only: asking for
+    them on a K-format model is an error, and the model keeps decoding."""
+    import token_decode_llama_amd as lm
+    model = get_model("tiny_q4k")
+    g = open_gpu(model, max_seqs=1)
+    try:
+        for fn in (lambda: g.set_persistent(True), lambda: g.set_dataflow(1)):
+            with pytest.raises(lm.LMError):
+                fn()
+        lg, am = g.step(synth.start_tokens(model.cfg, 1))
+        assert np.all(np.isfinite(lg))
+    finally:
+        g.close()

@@ -17,6 +17,9 @@
 #ifndef LMK_CB_Q4
 #define LMK_CB_Q4 4
 #endif
+#ifndef LMK_CB_QK
+#define LMK_CB_QK 2     // the K formats (more registers per block: headers / high bits)
+#endif
 #ifndef LMK_WEIGHT_NT
 #define LMK_WEIGHT_NT 0     // plain loads: the measured default of the GEMV kernels
 #endif
@@ -91,15 +94,17 @@ __device__ __forceinline__ float dot_q8(const int4 A, const int4 B, const int4* 
 }
 
 // Q4_0 block: 16 bytes, byte j = element j (low nibble) | element j+16 (high).
-// The nibbles n = q + 8 enter the dot products unsigned; T = the block's digit
-// sums (T0, T1, T2) remove the 8 offset.
+// The nibbles n = q + OFF enter the dot products unsigned; T = the block's
+// digit sums (T0, T1, T2) remove the offset (Q4_0: OFF = 8; the Q4_K
+// sub-blocks, regrouped into this order, have OFF = 0: sum n x).
+template <int OFF = 8>
 __device__ __forceinline__ float dot_q4(const int4 A, const int4* D, const int4 T) {
     const int4 e0 = D[0], e1 = D[1], f0 = D[2], f1 = D[3], g0 = D[4], g1 = D[5];
     const int w[4] = {A.x, A.y, A.z, A.w};
     const int E0[4] = {e0.x, e0.y, e0.z, e0.w}, E1[4] = {e1.x, e1.y, e1.z, e1.w};
     const int F0[4] = {f0.x, f0.y, f0.z, f0.w}, F1[4] = {f1.x, f1.y, f1.z, f1.w};
     const int G0[4] = {g0.x, g0.y, g0.z, g0.w}, G1[4] = {g1.x, g1.y, g1.z, g1.w};
-    int s0 = -8 * T.x, s1 = -8 * T.y, s2 = -8 * T.z;
+    int s0 = -OFF * T.x, s1 = -OFF * T.y, s2 = -OFF * T.z;
     #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int lo = w[u] & 0x0F0F0F0F, hi = (int)(((unsigned)w[u] >> 4) & 0x0F0F0F0Fu);
@@ -107,6 +112,50 @@ __device__ __forceinline__ float dot_q4(const int4 A, const int4* D, const int4 
         s0 = sdot4(hi, E1[u], s0); s1 = sdot4(hi, F1[u], s1); s2 = sdot4(hi, G1[u], s2);
     }
     return combine_digits(s0, s1, s2);
+}
+
+// Q4_K sub-block j (0..7) of a super-block: its 6-bit scale and min from the
+// 16-byte header h (x = fp16 d | fp16 dmin << 16; y, z, w = packed bytes
+// p0..p3, p4..p7, p8..p11).  Sub-blocks 0..3: scale = p[j] & 63, min =
+// p[j+4] & 63; sub-blocks 4..7: the low 4 bits of both in p[j+4] (scale low
+// nibble, min high nibble), the top 2 bits in p[j-4] (scale) and p[j] (min).
+// Returns ds = d * scale and dm = dmin * min (both exact in fp32).
+__device__ __forceinline__ void q4k_scale_min(const int4 h, int j, float& ds, float& dm) {
+    const int sh = 8 * (j & 3);
+    const uint32_t by = ((uint32_t)h.y >> sh) & 255u, bz = ((uint32_t)h.z >> sh) & 255u,
+                   bw = ((uint32_t)h.w >> sh) & 255u;
+    const uint32_t sc = j < 4 ? (by & 63u) : ((bw & 15u) | ((by >> 6) << 4));
+    const uint32_t mn = j < 4 ? (bz & 63u) : ((bw >> 4) | ((bz >> 6) << 4));
+    ds = h2f((uint16_t)((uint32_t)h.x & 0xFFFFu)) * (float)sc;
+    dm = h2f((uint16_t)((uint32_t)h.x >> 16)) * (float)mn;
+}
+
+// Q6_K block (32 weights, two 16-weight sub-blocks): A = low nibbles in the
+// Q4_0 order, Hb = the high parts (word x: elements 0..15, y: 16..31; element
+// 4u+k's two bits at bit 8k + 2u).  q = low | high << 4 (0..63) enters the dot
+// products unsigned; the sub-blocks' digit sums T0 (elements 0..15), T1
+// (16..31) remove the 32 offset.  lo / hi = sum (q - 32) x over each sub-block.
+__device__ __forceinline__ void dot_q6(const int4 A, const uint2 Hb, const int4* D, const int4 T0,
+                                       const int4 T1, float& lo, float& hi) {
+    const int4 e0 = D[0], e1 = D[1], f0 = D[2], f1 = D[3], g0 = D[4], g1 = D[5];
+    const int w[4] = {A.x, A.y, A.z, A.w};
+    const int E0[4] = {e0.x, e0.y, e0.z, e0.w}, E1[4] = {e1.x, e1.y, e1.z, e1.w};
+    const int F0[4] = {f0.x, f0.y, f0.z, f0.w}, F1[4] = {f1.x, f1.y, f1.z, f1.w};
+    const int G0[4] = {g0.x, g0.y, g0.z, g0.w}, G1[4] = {g1.x, g1.y, g1.z, g1.w};
+    int a0 = -32 * T0.x, a1 = -32 * T0.y, a2 = -32 * T0.z;
+    int b0 = -32 * T1.x, b1 = -32 * T1.y, b2 = -32 * T1.z;
+    #pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        // move bits 8k + 2u, 8k + 2u + 1 to 8k + 4, 8k + 5
+        const uint32_t hl = u < 2 ? Hb.x << (4 - 2 * u) : Hb.x >> (2 * u - 4);
+        const uint32_t hh = u < 2 ? Hb.y << (4 - 2 * u) : Hb.y >> (2 * u - 4);
+        const int vl = (int)(((uint32_t)w[u] & 0x0F0F0F0Fu) | (hl & 0x30303030u));
+        const int vh = (int)((((uint32_t)w[u] >> 4) & 0x0F0F0F0Fu) | (hh & 0x30303030u));
+        a0 = sdot4(vl, E0[u], a0); a1 = sdot4(vl, F0[u], a1); a2 = sdot4(vl, G0[u], a2);
+        b0 = sdot4(vh, E1[u], b0); b1 = sdot4(vh, F1[u], b1); b2 = sdot4(vh, G1[u], b2);
+    }
+    lo = combine_digits(a0, a1, a2);
+    hi = combine_digits(b0, b1, b2);
 }
 
 __device__ __forceinline__ float block_sum(float v, float* red) {
@@ -134,17 +183,23 @@ __device__ __forceinline__ float max8(float v) {
     v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false))); // row_half_mirror
     return v;
 }
-__device__ __forceinline__ int sum8(int v) {
+__device__ __forceinline__ int sum4(int v) {
     v += __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
     v += __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
+    return v;
+}
+__device__ __forceinline__ int sum8(int v) {
+    v = sum4(v);
     v += __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);
     return v;
 }
 
 // Four consecutive activations (columns i..i+3 of a 32-column block) -> their
 // three digit bytes; the block maximum comes from the 8 lanes sharing the block.
+// sums: 0 none; 1 the block's digit sums at dsum[b]; 2 the sums of its two
+// 16-column halves at dsum[2b], dsum[2b+1].
 __device__ __forceinline__ void stage_digits(float4 v, int i, int K, int8_t* xq, float* xsc, int4* dsum,
-                                             bool sums) {
+                                             int sums) {
     const float m = max8(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
     if (i >= K) return;
     const float f = m > 0.f ? 8323072.0f / m : 0.f;       // 127 * 2^16 / max|x_b|
@@ -167,11 +222,16 @@ __device__ __forceinline__ void stage_digits(float4 v, int i, int K, int8_t* xq,
     dst[8 + j] = (int)w1;
     dst[16 + j] = (int)w2;
     if (j == 0) xsc[b] = m * (1.0f / 8323072.0f);
-    if (sums) {
+    if (sums == 1) {
         t0 = sum8(t0);
         t1 = sum8(t1);
         t2 = sum8(t2);
         if (j == 0) dsum[b] = make_int4(t0, t1, t2, 0);
+    } else if (sums == 2) {
+        t0 = sum4(t0);
+        t1 = sum4(t1);
+        t2 = sum4(t2);
+        if ((j & 3) == 0) dsum[2 * b + (j >> 2)] = make_int4(t0, t1, t2, 0);
     }
 }
 

@@ -10,6 +10,9 @@ namespace lmk {
 
 constexpr int kQ4_0 = 2;
 constexpr int kQ8_0 = 8;
+constexpr int kQ4_K = 12;   // GGUF K formats: 256-weight super-blocks (batch-1 GEMV only)
+constexpr int kQ6_K = 14;
+constexpr bool is_kquant(int qtype) { return qtype == kQ4_K || qtype == kQ6_K; }
 constexpr int kAttnChunk = 64;     // KV positions per attention workgroup
 constexpr int kCntStride = 32;     // ints per attention chunk counter: one 128-byte line each, so
                                    // that different counters do not serialise each other's atomics
@@ -17,13 +20,26 @@ constexpr int kCntGroup = 16;      // chunks per first-level counter (atomics on
 // counter lines per (sequence, KV head): the count of complete groups, then one per group
 constexpr int attn_cnt_lines(int max_chunks) { return 1 + (max_chunks + kCntGroup - 1) / kCntGroup; }
 
-// Device layout of one quantised matrix [N rows][K cols], nb = K/32 blocks/row.
-//   Q8_0: quants row-major, each row = [first 16 bytes of every block]
+// Device layout of one quantised matrix [N rows][K cols], nb = K/32 blocks/row,
+// nsb = K/256 super-blocks/row (K formats).  Quants and scales sit in two
+// planes, row-major, so that a row range of a matrix is a contiguous slice:
+//   Q8_0: quants, each row = [first 16 bytes of every block]
 //         [last 16 bytes of every block] (int8), so a wavefront reading
 //         block b of consecutive lanes makes fully coalesced 16-byte loads;
-//   Q4_0: quants row-major, each row = nb x 16 nibble bytes in GGUF order
+//         scales: fp16 [N][nb];
+//   Q4_0: quants, each row = nb x 16 nibble bytes in GGUF order
 //         (byte j: element j low nibble, element j+16 high nibble);
-//   scales: fp16 [N][nb] in a separate plane.
+//         scales: fp16 [N][nb];
+//   Q4_K: quants, each row = nb x 16 bytes, the 32-weight sub-blocks
+//         regrouped into the Q4_0 nibble order; scales: the super-blocks'
+//         16-byte headers as stored (fp16 d, fp16 dmin, 12 bytes of packed
+//         6-bit scale/min pairs) [N][nsb][16];
+//   Q6_K: quants, each row = nb x 16 bytes of low nibbles (Q4_0 order), then
+//         nb x 8 bytes of 2-bit high parts: words h0 (elements 0..15) and h1
+//         (16..31) of a block hold element 4u+k's (u, k < 4) two bits at bit
+//         8k + 2u; scales, each row = nb x 2 int8 (the two 16-weight
+//         sub-block scales of each block), then nsb x fp16 d.
+// Every layout holds exactly the GGUF bytes of the matrix, regrouped.
 struct QMat {
     const uint8_t* q;
     const uint16_t* sc;
@@ -46,10 +62,27 @@ inline int64_t qfrag_bytes(int qtype, int64_t N, int64_t K) {
     return (N + 15) / 16 * ((nb + per - 1) / per) * 1024;
 }
 
-inline int64_t qmat_qbytes(int qtype, int64_t N, int64_t K) {
-    return qtype == kQ8_0 ? N * K : N * K / 2;
+constexpr int64_t qmat_qbytes(int qtype, int64_t N, int64_t K) {
+    if (qtype == kQ8_0) return N * K;
+    if (qtype == kQ6_K) return N * (K / 2 + K / 4);
+    return N * K / 2;
 }
-inline int64_t qmat_sbytes(int64_t N, int64_t K) { return N * (K / 32) * 2; }
+// bytes of one row of the scale plane
+constexpr int64_t qmat_srow(int qtype, int64_t K) {
+    if (qtype == kQ4_K) return K / 256 * 16;
+    if (qtype == kQ6_K) return K / 32 * 2 + K / 256 * 2;
+    return K / 32 * 2;
+}
+constexpr int64_t qmat_sbytes(int qtype, int64_t N, int64_t K) { return N * qmat_srow(qtype, K); }
+// bytes of one GGUF row of K weights
+inline int64_t gguf_row_bytes(int qtype, int64_t K) {
+    switch (qtype) {
+        case kQ8_0: return K / 32 * 34;
+        case kQ4_0: return K / 32 * 18;
+        case kQ4_K: return K / 256 * 144;
+        default: return K / 256 * 210;
+    }
+}
 
 enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
 

@@ -62,14 +62,19 @@ hipError_t launch_embed(const uint16_t* tok_embd, const int* tokens, int vocab, 
 // Weight blocks one lane loads per pipeline stage (per row of its row pair).
 template <int QT> struct ChunkBlocks { static constexpr int value = LMK_CB_Q8; };
 template <> struct ChunkBlocks<kQ4_0> { static constexpr int value = LMK_CB_Q4; };
+template <> struct ChunkBlocks<kQ4_K> { static constexpr int value = LMK_CB_QK; };
+template <> struct ChunkBlocks<kQ6_K> { static constexpr int value = LMK_CB_QK; };
 
 // One pipeline stage of a lane: CB blocks of both rows of its row pair.
 template <int QT>
 struct WChunk {
     static constexpr int CB = ChunkBlocks<QT>::value;
-    int4 a0[CB], a1[CB];          // first 16 bytes (Q8_0) / all 16 bytes (Q4_0) of row 0 / row 1
+    int4 a0[CB], a1[CB];          // first 16 bytes (Q8_0) / the 16 nibble bytes (others) of row 0 / row 1
     int4 b0[QT == kQ8_0 ? CB : 1], b1[QT == kQ8_0 ? CB : 1];   // Q8_0 second halves
-    uint16_t d0[CB], d1[CB];
+    int4 h0[QT == kQ4_K ? CB : 1], h1[QT == kQ4_K ? CB : 1];   // Q4_K super-block headers
+    uint2 e0[QT == kQ6_K ? CB : 1], e1[QT == kQ6_K ? CB : 1];  // Q6_K high bits
+    uint16_t d0[CB], d1[CB];      // block scale (Q8_0, Q4_0) / sub-block scale pair (Q6_K)
+    uint16_t f0[QT == kQ6_K ? CB : 1], f1[QT == kQ6_K ? CB : 1];   // Q6_K super-block d
 };
 
 #ifndef LMK_GEMV_MIN_BLOCKS
@@ -93,17 +98,21 @@ __global__ __launch_bounds__(kBlock, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a
 
     const int K = a.w.K, N = a.w.N, nb = K >> 5;
     // LDS: per 32-column block, the activation digit planes (96 bytes), its
-    // scale, and (Q4_0) the digit sums
+    // scale, and the digit sums (Q4_0, Q4_K: per block; Q6_K: per 16-column half)
+    constexpr int kSums = (QT == kQ4_0 || QT == kQ4_K) ? 1 : (QT == kQ6_K ? 2 : 0);
     int8_t* xq = (int8_t*)smem;                       // [nb][3][32] int8
     float* xsc = (float*)(xq + nb * 96);              // [nb]
-    int4* dsum = (int4*)(xsc + ((nb + 3) & ~3));      // [nb] (T0, T1, T2, 0)
+    int4* dsum = (int4*)(xsc + ((nb + 3) & ~3));      // [nb or 2 nb] (T0, T1, T2, 0)
     const int tid = threadIdx.x, lane = tid & 63;
     // wave-uniform by construction; readfirstlane lets the row bases live in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int s = blockIdx.y;
     const float* x = a.xin + (int64_t)s * a.x_stride;
     const int rg = lane / LPR, li = lane % LPR;
-    const int64_t rowq = (QT == kQ8_0) ? (int64_t)K : (int64_t)(K >> 1);
+    const int64_t rowq = (QT == kQ8_0) ? (int64_t)K : (QT == kQ6_K ? (int64_t)(K >> 1) + (K >> 2) : (int64_t)(K >> 1));
+    // scale-plane row in 16-bit words (layouts in lm_internal.h)
+    const int srow = QT == kQ4_K ? (K >> 8) * 8 : (QT == kQ6_K ? nb + (K >> 8) : nb);
+    const int jsub = li & 7;   // Q4_K: sub-block of every block this lane reads (LPR is a multiple of 8)
 
     // this wavefront's steps: step0, step0 + sstride, ... ; each step is split
     // into `cps` chunks of CB blocks per lane
@@ -125,7 +134,7 @@ __global__ __launch_bounds__(kBlock, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a
         const int r0 = min((step0 + i * sstride) * kRowsPerStep + rg * 2, N - 2);
         const uint8_t* q0 = a.w.q + (int64_t)r0 * rowq;
         const uint8_t* q1 = q0 + rowq;
-        const uint16_t* s0 = a.w.sc + (int64_t)r0 * nb;
+        const uint16_t* s0 = a.w.sc + (int64_t)r0 * srow;
         #pragma unroll
         for (int u = 0; u < CB; ++u) {
             const int b = li + LPR * (k * CB + u);
@@ -136,8 +145,20 @@ __global__ __launch_bounds__(kBlock, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a
                 w.b0[u] = ld16_stream(q0 + (uint32_t)nb * 16u + bc * 16u);
                 w.b1[u] = ld16_stream(q1 + (uint32_t)nb * 16u + bc * 16u);
             }
-            w.d0[u] = s0[bc];          // used only in compute(): consuming a load here
-            w.d1[u] = s0[(uint32_t)nb + bc];     // would wait on every load issued before it
+            if (QT == kQ4_K) {
+                w.h0[u] = *(const int4*)(s0 + (bc >> 3) * 8u);
+                w.h1[u] = *(const int4*)(s0 + (uint32_t)srow + (bc >> 3) * 8u);
+            } else if (QT == kQ6_K) {
+                w.e0[u] = *(const uint2*)(q0 + (uint32_t)nb * 16u + bc * 8u);
+                w.e1[u] = *(const uint2*)(q1 + (uint32_t)nb * 16u + bc * 8u);
+                w.d0[u] = s0[bc];
+                w.d1[u] = s0[(uint32_t)srow + bc];
+                w.f0[u] = s0[(uint32_t)nb + (bc >> 3)];
+                w.f1[u] = s0[(uint32_t)(srow + nb) + (bc >> 3)];
+            } else {
+                w.d0[u] = s0[bc];          // used only in compute(): consuming a load here
+                w.d1[u] = s0[(uint32_t)srow + bc];   // would wait on every load issued before it
+            }
         }
     };
 
@@ -148,17 +169,40 @@ __global__ __launch_bounds__(kBlock, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a
         for (int u = 0; u < CB; ++u) {
             const int braw = li + LPR * (k * CB + u);
             const int b = min(braw, nb - 1);
-            const float d0 = braw < nb ? h2f(w.d0[u]) : 0.f;   // past the row end: no contribution
-            const float d1 = braw < nb ? h2f(w.d1[u]) : 0.f;
+            const bool in_row = braw < nb;                     // past the row end: no contribution
             const int4* D = (const int4*)(xq + b * 96);
             const float sx = xsc[b];
             if (QT == kQ8_0) {
+                const float d0 = in_row ? h2f(w.d0[u]) : 0.f, d1 = in_row ? h2f(w.d1[u]) : 0.f;
                 acc0 = fmaf(d0 * sx, dot_q8(w.a0[u], w.b0[u], D), acc0);
                 acc1 = fmaf(d1 * sx, dot_q8(w.a1[u], w.b1[u], D), acc1);
-            } else {
+            } else if (QT == kQ4_0) {
+                const float d0 = in_row ? h2f(w.d0[u]) : 0.f, d1 = in_row ? h2f(w.d1[u]) : 0.f;
                 const int4 T = dsum[b];
                 acc0 = fmaf(d0 * sx, dot_q4(w.a0[u], D, T), acc0);
                 acc1 = fmaf(d1 * sx, dot_q4(w.a1[u], D, T), acc1);
+            } else if (QT == kQ4_K) {
+                // sum (ds q - dm) x = ds sum q x - dm sum x over the sub-block
+                float ds0, dm0, ds1, dm1;
+                q4k_scale_min(w.h0[u], jsub, ds0, dm0);
+                q4k_scale_min(w.h1[u], jsub, ds1, dm1);
+                const float f = in_row ? sx : 0.f;
+                const int4 T = dsum[b];
+                const float tx = combine_digits(T.x, T.y, T.z);
+                acc0 = fmaf(ds0 * f, dot_q4<0>(w.a0[u], D, T), acc0);
+                acc0 = fmaf(-dm0 * f, tx, acc0);
+                acc1 = fmaf(ds1 * f, dot_q4<0>(w.a1[u], D, T), acc1);
+                acc1 = fmaf(-dm1 * f, tx, acc1);
+            } else {  // Q6_K
+                const int4 T0 = dsum[2 * b], T1 = dsum[2 * b + 1];
+                float lo0, hi0, lo1, hi1;
+                dot_q6(w.a0[u], w.e0[u], D, T0, T1, lo0, hi0);
+                dot_q6(w.a1[u], w.e1[u], D, T0, T1, lo1, hi1);
+                const float g0 = in_row ? h2f(w.f0[u]) * sx : 0.f, g1 = in_row ? h2f(w.f1[u]) * sx : 0.f;
+                const float c00 = (float)(int8_t)(w.d0[u] & 255), c01 = (float)(int8_t)(w.d0[u] >> 8);
+                const float c10 = (float)(int8_t)(w.d1[u] & 255), c11 = (float)(int8_t)(w.d1[u] >> 8);
+                acc0 = fmaf(g0, fmaf(c00, lo0, c01 * hi0), acc0);
+                acc1 = fmaf(g1, fmaf(c10, lo1, c11 * hi1), acc1);
             }
         }
     };
@@ -272,7 +316,7 @@ __global__ __launch_bounds__(kBlock, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a
                 v.z *= gv.z;
                 v.w *= gv.w;
             }
-            stage_digits(v, i, K, xq, xsc, dsum, QT == kQ4_0);
+            stage_digits(v, i, K, xq, xsc, dsum, kSums);
         }
     }
     // block_sum's barriers also order the LDS stores above before any reads
@@ -453,9 +497,19 @@ hipError_t launch_gemv(const GemvArgs& a, int epi, int n_seq, int max_blocks, hi
     if (epi == EPI_RESID && a.norm_g) return hipErrorInvalidValue;   // the residual products take no gain
     const int nb = a.w.K / 32;
     const int lpr = pick_lpr(nb);
-    const size_t lds = (size_t)nb * 96 + (size_t)((nb + 3) & ~3) * 4 + (a.qtype == kQ4_0 ? (size_t)nb * 16 : 0);
-    if (a.qtype == kQ8_0) return launch_gemv_epi<kQ8_0>(a, epi, lpr, n_seq, max_blocks, lds, st);
-    return launch_gemv_epi<kQ4_0>(a, epi, lpr, n_seq, max_blocks, lds, st);
+    const size_t sums = a.qtype == kQ4_0 || a.qtype == kQ4_K ? (size_t)nb * 16 : (a.qtype == kQ6_K ? (size_t)nb * 32 : 0);
+    const size_t lds = (size_t)nb * 96 + (size_t)((nb + 3) & ~3) * 4 + sums;
+    switch (a.qtype) {
+        case kQ8_0: return launch_gemv_epi<kQ8_0>(a, epi, lpr, n_seq, max_blocks, lds, st);
+        case kQ4_0: return launch_gemv_epi<kQ4_0>(a, epi, lpr, n_seq, max_blocks, lds, st);
+        case kQ4_K:
+            if (a.w.K % 256) return hipErrorInvalidValue;
+            return launch_gemv_epi<kQ4_K>(a, epi, lpr, n_seq, max_blocks, lds, st);
+        case kQ6_K:
+            if (a.w.K % 256) return hipErrorInvalidValue;
+            return launch_gemv_epi<kQ6_K>(a, epi, lpr, n_seq, max_blocks, lds, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1495,19 +1549,33 @@ hipError_t launch_attention(const AttnArgs& a, int n_seq, hipStream_t st) {
 __global__ __launch_bounds__(kBlock) void k_dequant(QMat w, int qtype, int row0, float* __restrict__ out) {
     const int r = row0 + blockIdx.x;
     const int K = w.K, nb = K >> 5;
-    const int64_t rowq = qtype == kQ8_0 ? (int64_t)K : (int64_t)(K >> 1);
+    const int64_t rowq = qmat_qbytes(qtype, 1, K);
+    const int64_t srow = qmat_srow(qtype, K) / 2;     // 16-bit words
     const uint8_t* q = w.q + (int64_t)r * rowq;
+    const uint16_t* sc = w.sc + (int64_t)r * srow;
     for (int c = threadIdx.x; c < K; c += kBlock) {
         const int b = c >> 5, e = c & 31;
-        const float d = h2f(w.sc[(int64_t)r * nb + b]);
         float v;
         if (qtype == kQ8_0) {
+            const float d = h2f(sc[b]);
             const int8_t qi = (int8_t)(e < 16 ? q[b * 16 + e] : q[(int64_t)nb * 16 + b * 16 + (e - 16)]);
             v = d * (float)qi;
         } else {
             const uint8_t byte = q[b * 16 + (e & 15)];
             const int nib = e < 16 ? (byte & 0xF) : (byte >> 4);
-            v = (float)(nib - 8) * d;
+            if (qtype == kQ4_0) {
+                v = (float)(nib - 8) * h2f(sc[b]);
+            } else if (qtype == kQ4_K) {
+                float ds, dm;
+                q4k_scale_min(*(const int4*)(sc + (b >> 3) * 8), b & 7, ds, dm);
+                v = fmaf(ds, (float)nib, -dm);                  // one rounding of the exact value
+            } else {  // Q6_K
+                const int ii = e & 15;
+                const uint8_t hb = q[(int64_t)nb * 16 + b * 8 + 4 * (e >> 4) + (ii & 3)];
+                const int q6 = nib | (((hb >> (2 * (ii >> 2))) & 3) << 4);
+                const int8_t s6 = (int8_t)(e < 16 ? (sc[b] & 255) : (sc[b] >> 8));
+                v = h2f(sc[nb + (b >> 3)]) * (float)s6 * (float)(q6 - 32);   // exact in fp32
+            }
         }
         out[(int64_t)blockIdx.x * K + c] = v;
     }

@@ -71,25 +71,60 @@ void parallel_rows(int64_t n, F&& fn) {
     for (auto& t : th) t.join();
 }
 
-// GGUF row (nb blocks) -> device layout row (quants + scales)
-void repack_row(int qtype, const uint8_t* src, int K, uint8_t* dq, uint16_t* dsc) {
+// GGUF row -> device layout row (quants + scales; lm_internal.h).  The K
+// formats (GGUF's published layout; the C/CUDA Llama engine page, section 1,
+// names them): Q4_K super-block = fp16 d, fp16 dmin, 12 bytes of 6-bit
+// scale/min pairs, 128 bytes whose 32-byte group g holds sub-block 2g in the
+// low nibbles and 2g+1 in the high ones; Q6_K super-block = 128 bytes of low
+// nibbles (element 128h + 32t + l at byte 64h + 32(t%2) + l, high nibble when
+// t >= 2), 64 bytes of 2-bit high parts (bits 2t, 2t+1 of byte 32h + l),
+// 16 int8 sub-block scales, fp16 d.
+void repack_row(int qtype, const uint8_t* src, int K, uint8_t* dq, uint8_t* dsc) {
     const int nb = K / 32;
     if (qtype == kQ8_0) {
         for (int b = 0; b < nb; ++b) {
             const uint8_t* blk = src + (int64_t)b * 34;
-            dsc[b] = (uint16_t)(blk[0] | (blk[1] << 8));
+            std::memcpy(dsc + 2 * b, blk, 2);
             std::memcpy(dq + (int64_t)b * 16, blk + 2, 16);
             std::memcpy(dq + (int64_t)nb * 16 + (int64_t)b * 16, blk + 18, 16);
         }
-    } else {
+    } else if (qtype == kQ4_0) {
         for (int b = 0; b < nb; ++b) {
             const uint8_t* blk = src + (int64_t)b * 18;
-            dsc[b] = (uint16_t)(blk[0] | (blk[1] << 8));
+            std::memcpy(dsc + 2 * b, blk, 2);
             std::memcpy(dq + (int64_t)b * 16, blk + 2, 16);
+        }
+    } else if (qtype == kQ4_K) {
+        for (int sb = 0; sb < K / 256; ++sb) {
+            const uint8_t* blk = src + (int64_t)sb * 144;
+            std::memcpy(dsc + 16 * sb, blk, 16);
+            for (int j = 0; j < 8; ++j) {
+                const uint8_t* g = blk + 16 + 32 * (j / 2);
+                const int sh = 4 * (j % 2);
+                uint8_t* o = dq + (int64_t)(8 * sb + j) * 16;
+                for (int i = 0; i < 16; ++i)
+                    o[i] = (uint8_t)(((g[i] >> sh) & 15) | (((g[i + 16] >> sh) & 15) << 4));
+            }
+        }
+    } else {  // kQ6_K
+        std::memset(dq, 0, (size_t)nb * 24);
+        for (int sb = 0; sb < K / 256; ++sb) {
+            const uint8_t* blk = src + (int64_t)sb * 210;
+            for (int e = 0; e < 256; ++e) {
+                const int h = e / 128, t = (e % 128) / 32, l = e % 32;
+                const int lo = (blk[64 * h + 32 * (t % 2) + l] >> (4 * (t / 2))) & 15;
+                const int hi = (blk[128 + 32 * h + l] >> (2 * t)) & 3;
+                const int b = 8 * sb + e / 32, i = e % 32, ii = i & 15;
+                dq[(int64_t)b * 16 + ii] |= (uint8_t)(lo << (i < 16 ? 0 : 4));
+                dq[(int64_t)nb * 16 + (int64_t)b * 8 + 4 * (i / 16) + (ii & 3)] |= (uint8_t)(hi << (2 * (ii >> 2)));
+            }
+            std::memcpy(dsc + 16 * sb, blk + 192, 16);                 // scales of blocks 8sb..8sb+7
+            std::memcpy(dsc + 2 * nb + 2 * sb, blk + 208, 2);          // d
         }
     }
 }
 
+// bytes of one block for the several-sequence layouts (Q8_0 / Q4_0 only)
 int block_bytes(int qtype) { return qtype == kQ8_0 ? 34 : 18; }
 
 }  // namespace
@@ -330,7 +365,16 @@ static lm_status check_config(const lm_config* c) {
         return fail(nullptr, LM_E_ARG, "bad config: %s = %lld; expected %s", what, got, expect);
     };
     if (!c) return fail(nullptr, LM_E_ARG, "bad config: NULL pointer");
-    if (c->qtype != LM_Q8_0 && c->qtype != LM_Q4_0) return bad("qtype", c->qtype, "2 (Q4_0) or 8 (Q8_0)");
+    if (c->qtype != LM_Q8_0 && c->qtype != LM_Q4_0 && c->qtype != LM_Q4_K && c->qtype != LM_Q6_K)
+        return bad("qtype", c->qtype, "2 (Q4_0), 8 (Q8_0), 12 (Q4_K) or 14 (Q6_K)");
+    if (is_kquant(c->qtype)) {
+        // 256-weight super-blocks along every GEMV input; one sequence per step
+        if (c->hidden % 256) return bad("hidden", c->hidden, "a multiple of 256 for Q4_K / Q6_K");
+        if (c->ffn % 256) return bad("ffn", c->ffn, "a multiple of 256 for Q4_K / Q6_K");
+        if ((int64_t)c->n_heads * c->head_dim % 256)
+            return bad("n_heads * head_dim", (long long)c->n_heads * c->head_dim, "a multiple of 256 for Q4_K / Q6_K");
+        if (c->max_seqs != 1) return bad("max_seqs", c->max_seqs, "1 for Q4_K / Q6_K (one sequence per step)");
+    }
     if (c->vocab < 2 || c->vocab % 2) return bad("vocab", c->vocab, "an even number >= 2");
     if (c->hidden < 32 || c->hidden % 32) return bad("hidden", c->hidden, "a positive multiple of 32");
     if (c->n_layers < 1) return bad("n_layers", c->n_layers, ">= 1");
@@ -374,7 +418,7 @@ static void layout(lm_model* m) {
         m->mo[i].q = off;
         off = align_up(off + qmat_qbytes(qt, NK[i][0], NK[i][1]));
         m->mo[i].sc = off;
-        off = align_up(off + qmat_sbytes(NK[i][0], NK[i][1]));
+        off = align_up(off + qmat_sbytes(qt, NK[i][0], NK[i][1]));
         m->mo[i].sct = -1;
         m->mo[i].qf = -1;
         if (m->batched) {
@@ -386,7 +430,7 @@ static void layout(lm_model* m) {
     }
     m->blob_bytes = off;
     m->lm_q_bytes = align_up(qmat_qbytes(qt, m->V, m->H));
-    m->lm_sc_bytes = align_up(qmat_sbytes(m->V, m->H));
+    m->lm_sc_bytes = align_up(qmat_sbytes(qt, m->V, m->H));
     m->lm_sct_bytes = m->batched ? align_up(sct_bytes(m->V, m->H)) : 0;
     m->lm_qf_bytes = m->batched ? align_up(qfrag_bytes(qt, m->V, m->H)) : 0;
     m->max_chunks = (c.max_ctx + kAttnChunk - 1) / kAttnChunk;
@@ -598,7 +642,7 @@ extern "C" lm_status lm_model_create(const lm_config* cfg, void* hip_stream, lm_
     }
     // persistent one-kernel step (one sequence): tile-major weight copies,
     // its argument block in device memory, barrier counts
-    if (S == 1) {
+    if (S == 1 && !is_kquant(c.qtype)) {
         const int qt = c.qtype;
         const int64_t kmax = std::max<int64_t>({m->H, m->F, m->qrows});
         const int xb = step_xbytes(qt, (int)kmax, (int)m->hd);
@@ -697,10 +741,11 @@ template <class RowFn>
 static lm_status upload_matrix(lm_model* m, int N, int K, RowFn src_row, uint8_t* dq, uint16_t* dsc,
                                bool dst_host) {
     const int qt = m->cfg.qtype;
-    const int64_t rq = qmat_qbytes(qt, 1, K), rs = (K / 32) * 2;
+    const int64_t rq = qmat_qbytes(qt, 1, K), rs = qmat_srow(qt, K);
+    uint8_t* dsb = (uint8_t*)dsc;
     if (dst_host) {
         parallel_rows(N, [&](int64_t a, int64_t b) {
-            for (int64_t r = a; r < b; ++r) repack_row(qt, src_row(r), K, dq + r * rq, dsc + r * (K / 32));
+            for (int64_t r = a; r < b; ++r) repack_row(qt, src_row(r), K, dq + r * rq, dsb + r * rs);
         });
         return LM_OK;
     }
@@ -708,12 +753,12 @@ static lm_status upload_matrix(lm_model* m, int N, int K, RowFn src_row, uint8_t
     for (int64_t r0 = 0; r0 < N; r0 += rows_per) {
         const int64_t n = std::min<int64_t>(rows_per, N - r0);
         uint8_t* sq = m->h_stage;
-        uint16_t* ss = (uint16_t*)(m->h_stage + n * rq);
+        uint8_t* ss = m->h_stage + n * rq;
         parallel_rows(n, [&](int64_t a, int64_t b) {
-            for (int64_t r = a; r < b; ++r) repack_row(qt, src_row(r0 + r), K, sq + r * rq, ss + r * (K / 32));
+            for (int64_t r = a; r < b; ++r) repack_row(qt, src_row(r0 + r), K, sq + r * rq, ss + r * rs);
         });
         HIPTRY(m, hipMemcpyAsync(dq + r0 * rq, sq, (size_t)(n * rq), hipMemcpyHostToDevice, m->stream));
-        HIPTRY(m, hipMemcpyAsync(dsc + r0 * (K / 32), ss, (size_t)(n * rs), hipMemcpyHostToDevice, m->stream));
+        HIPTRY(m, hipMemcpyAsync(dsb + r0 * rs, ss, (size_t)(n * rs), hipMemcpyHostToDevice, m->stream));
         HIPTRY(m, hipStreamSynchronize(m->stream));
     }
     return LM_OK;
@@ -869,9 +914,9 @@ extern "C" lm_status lm_load_layer_weights(lm_model* m, int32_t layer, const lm_
         return fail(m, LM_E_ARG, "lm_load_layer_weights: a weight pointer is NULL (layer %d)", layer);
     HIPTRY(m, hipStreamSynchronize(m->stream));
     HIPTRY(m, hipStreamSynchronize(m->copy_stream));
-    const int qt = m->cfg.qtype, bb = block_bytes(qt);
+    const int qt = m->cfg.qtype;
     const int64_t H = m->H, F = m->F;
-    const int64_t rowH = H / 32 * bb, rowQ = m->qrows / 32 * bb, rowF = F / 32 * bb;
+    const int64_t rowH = gguf_row_bytes(qt, H), rowQ = gguf_row_bytes(qt, m->qrows), rowF = gguf_row_bytes(qt, F);
     const uint8_t *wq = (const uint8_t*)w->wq, *wk = (const uint8_t*)w->wk, *wv = (const uint8_t*)w->wv;
     const uint8_t *wo = (const uint8_t*)w->wo, *wg = (const uint8_t*)w->w_gate, *wu = (const uint8_t*)w->w_up;
     const uint8_t* wd = (const uint8_t*)w->w_down;
@@ -932,7 +977,7 @@ extern "C" lm_status lm_load_global_weights(lm_model* m, const uint16_t* tok_emb
     HIPTRY(m, hipStreamSynchronize(m->stream));
     HIPTRY(m, hipMemcpy(m->d_embd, tok_embd_f16, (size_t)(m->V * m->H * 2), hipMemcpyHostToDevice));
     HIPTRY(m, hipMemcpy(m->d_out_norm, out_norm, (size_t)(m->H * 4), hipMemcpyHostToDevice));
-    const int64_t rowH = m->H / 32 * block_bytes(m->cfg.qtype);
+    const int64_t rowH = gguf_row_bytes(m->cfg.qtype, m->H);
     const uint8_t* src = (const uint8_t*)lm_head_blocks;
     auto src_row = [&](int64_t r) { return src + r * rowH; };
     lm_status st = upload_matrix(m, (int)m->V, (int)m->H, src_row, m->d_lm_q, m->d_lm_sc, false);
@@ -1945,7 +1990,7 @@ extern "C" lm_status lm_kernel_stats(lm_model* m, int32_t kind, int64_t* count, 
 
 extern "C" lm_status lm_kernel_bytes(const lm_model* m, int32_t kind, int32_t n_seq, double* bytes) {
     if (!m || !bytes || kind < 0 || kind >= LM_K_COUNT || n_seq < 1 || n_seq > m->cfg.max_seqs) return LM_E_ARG;
-    const double bpw = m->cfg.qtype == LM_Q8_0 ? 34.0 / 32.0 : 18.0 / 32.0;
+    const double bpw = (double)gguf_row_bytes(m->cfg.qtype, 256) / 256.0;   // bytes per weight
     int computed = 0;                                 // layers a step computes (not skipped)
     for (int l = 0; l < m->cfg.n_layers; ++l) computed += !m->skip[l];
     const double H = (double)m->H, F = (double)m->F, V = (double)m->V, Q = (double)m->qrows,
