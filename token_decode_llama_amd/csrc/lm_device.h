@@ -18,7 +18,7 @@
 #define LMK_CB_Q4 4
 #endif
 #ifndef LMK_CB_QK
-#define LMK_CB_QK 2     // the K formats (more registers per block: headers / high bits)
+#define LMK_CB_QK 1     // the K formats (more registers per block: headers / high bits)
 #endif
 #ifndef LMK_WEIGHT_NT
 #define LMK_WEIGHT_NT 0     // plain loads: the measured default of the GEMV kernels

@@ -151,7 +151,8 @@ struct lm_model {
     int n_res = 0;
     uint8_t* d_layers = nullptr;          // resident blobs [n_res][blob]
     uint8_t* d_sbuf[2] = {nullptr, nullptr};
-    uint8_t* h_arena = nullptr;           // pinned blobs [L - n_res][blob]
+    uint8_t* h_arena = nullptr;           // pinned blobs [L - n_res][blob] (layer n_res first)
+    uint8_t* h_arena_alloc = nullptr;     // the allocation h_arena lies in (it may start later in it)
     uint8_t* h_stage = nullptr;           // pinned staging for uploads
     int64_t stage_bytes = 0;
     float* d_norms = nullptr;             // [L][2][H]
@@ -1791,9 +1792,19 @@ extern "C" lm_status lm_set_residency(lm_model* m, int32_t n_resident) {
     const int old = m->n_res, nw = n_resident;
     uint8_t *d = nullptr, *h = nullptr, *b0 = m->d_sbuf[0], *b1 = m->d_sbuf[1];
     const bool new_bufs = nw < L && !b0;
+    // The layers that stay streamed keep their place in the present pinned
+    // arena when it can hold the new set: more layers resident (the front of
+    // the allocation is left unused), or fewer when that unused front is large
+    // enough for the layers coming back.  Otherwise a new arena is allocated
+    // before the old one is freed.
+    const bool keep_arena = m->h_arena && nw < L &&
+                            (nw > old || (int64_t)(m->h_arena - m->h_arena_alloc) >= (int64_t)(old - nw) * B);
     lm_status st = LM_OK;
     if (nw > 0) st = dev_alloc(m, (void**)&d, nw * B, "layer weights");
-    if (st == LM_OK && nw < L) st = host_alloc(m, (void**)&h, (L - nw) * B, "streaming host arena");
+    if (st == LM_OK && nw < L) {
+        if (keep_arena) h = m->h_arena + (int64_t)(nw - old) * B;
+        else st = host_alloc(m, (void**)&h, (L - nw) * B, "streaming host arena");
+    }
     if (st == LM_OK && new_bufs) {
         b0 = b1 = nullptr;
         st = dev_alloc(m, (void**)&b0, B, "streaming buffer 0");
@@ -1805,7 +1816,7 @@ extern "C" lm_status lm_set_residency(lm_model* m, int32_t n_resident) {
         const uint8_t* src = from_dev ? m->d_layers + (int64_t)l * B : m->h_arena + (int64_t)(l - old) * B;
         uint8_t* dst = to_dev ? d + (int64_t)l * B : h + (int64_t)(l - nw) * B;
         if (!from_dev && !to_dev) {
-            std::memcpy(dst, src, (size_t)B);
+            if (dst != src) std::memcpy(dst, src, (size_t)B);
             continue;
         }
         const hipMemcpyKind kind = from_dev ? (to_dev ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToHost)
@@ -1816,7 +1827,7 @@ extern "C" lm_status lm_set_residency(lm_model* m, int32_t n_resident) {
     }
     if (st != LM_OK) {
         dev_free(m, d);
-        host_free(m, h);
+        if (!keep_arena) host_free(m, h);
         if (new_bufs) {
             dev_free(m, b0);
             dev_free(m, b1);
@@ -1824,7 +1835,10 @@ extern "C" lm_status lm_set_residency(lm_model* m, int32_t n_resident) {
         return st;
     }
     dev_free(m, m->d_layers);
-    host_free(m, m->h_arena);
+    if (!keep_arena) {
+        host_free(m, m->h_arena_alloc);
+        m->h_arena_alloc = nw < L ? h : nullptr;
+    }
     if (nw == L) {
         dev_free(m, b0);
         dev_free(m, b1);
