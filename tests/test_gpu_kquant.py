@@ -114,3 +114,25 @@ def test_kquant_one_launch_modes_rejected():
         assert np.all(np.isfinite(lg))
     finally:
         g.close()
+
+
+@pytest.mark.parametrize("name,mask", [("tiny_q6k", [1, 0]), ("llama1b_q4k_2layers", [0, 1])])
+def test_kquant_layer_skip_parity(name, mask):
+    """Layer skip on K-format models: the oracle with the same mask."""
+    from tests.helpers import compare_step, open_oracle
+    model = get_model(name)
+    cfg = model.cfg
+    g = open_gpu(model, max_seqs=1)
+    om = open_oracle(model, 1)
+    skip = np.array(mask, np.uint8)
+    g.set_layer_skip(skip)
+    toks = synth.start_tokens(cfg, 1)
+    try:
+        for st in range(cfg.steps):
+            lg_o, am_o = om.step(toks, skip=skip)
+            lg_g, am_g = g.step(toks)
+            compare_step(lg_g, am_g, lg_o, am_o, f"{name} skip {mask} step {st}")
+            toks = am_o
+    finally:
+        g.close()
+        om.close()

@@ -77,10 +77,6 @@ struct WChunk {
     uint16_t f0[QT == kQ6_K ? CB : 1], f1[QT == kQ6_K ? CB : 1];   // Q6_K super-block d
 };
 
-#ifndef LMK_KLPR_SHIFT
-#define LMK_KLPR_SHIFT 0    // K formats: lane groups sized for nb >> shift blocks per row
-#endif
-
 #ifndef LMK_GEMV_MIN_BLOCKS
 #define LMK_GEMV_MIN_BLOCKS 1     // workgroups per CU the register budget must allow
 #endif
@@ -500,7 +496,7 @@ static hipError_t launch_gemv_epi(const GemvArgs& a, int epi, int lpr, int n_seq
 hipError_t launch_gemv(const GemvArgs& a, int epi, int n_seq, int max_blocks, hipStream_t st) {
     if (epi == EPI_RESID && a.norm_g) return hipErrorInvalidValue;   // the residual products take no gain
     const int nb = a.w.K / 32;
-    const int lpr = pick_lpr(is_kquant(a.qtype) ? nb >> LMK_KLPR_SHIFT : nb);
+    const int lpr = pick_lpr(nb);
     const size_t sums = a.qtype == kQ4_0 || a.qtype == kQ4_K ? (size_t)nb * 16 : (a.qtype == kQ6_K ? (size_t)nb * 32 : 0);
     const size_t lds = (size_t)nb * 96 + (size_t)((nb + 3) & ~3) * 4 + sums;
     switch (a.qtype) {
