@@ -202,8 +202,9 @@ lm_status lm_skip_similar_layers(lm_model* m, double threshold, int32_t* n_skipp
  * decoding gives the same tokens.  Cache rows past the new position hold
  * draft or rejected values until overwritten.  Needs 1 <= k <= 3, k + 1 <=
  * max_seqs, every layer resident.  Blocks until the tokens are on the host.
- * Errors: LM_E_ARG, LM_E_STATE (weights not loaded, streaming mode), LM_E_CTX
- * (p + k + 1 > max_ctx), LM_E_HIP. */
+ * Errors: LM_E_ARG, LM_E_STATE (weights not loaded, streaming mode, a model
+ * created for one sequence - the K formats are), LM_E_CTX (p + k + 1 >
+ * max_ctx), LM_E_HIP. */
 lm_status lm_speculative_step(lm_model* m, int32_t token, int32_t draft_layers, int32_t k,
                               int32_t* tokens_out, int32_t* n_out);
 

@@ -101,8 +101,9 @@ def test_kquant_streaming_and_hybrid_bit_identical(name):
 
 
 def test_kquant_one_launch_modes_rejected():
-    """The one-launch step modes are built for Q8_0 / Q4_0 only: asking for
-    them on a K-format model is an error, and the model keeps decoding."""
+    """The one-launch step modes and the speculative verify pass are built for
+    Q8_0 / Q4_0 only: asking for them on a K-format model is an error, and the
+    model keeps decoding."""
     import token_decode_llama_amd as lm
     model = get_model("tiny_q4k")
     g = open_gpu(model, max_seqs=1)
@@ -110,6 +111,9 @@ def test_kquant_one_launch_modes_rejected():
         for fn in (lambda: g.set_persistent(True), lambda: g.set_dataflow(1)):
             with pytest.raises(lm.LMError):
                 fn()
+        with pytest.raises(lm.LMError) as e:           # the verify pass needs the several-sequence path
+            g.speculative_step(1, 1, 1)
+        assert e.value.status == lm.LM_E_STATE
         lg, am = g.step(synth.start_tokens(model.cfg, 1))
         assert np.all(np.isfinite(lg))
     finally:

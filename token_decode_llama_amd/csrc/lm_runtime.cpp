@@ -1578,6 +1578,9 @@ extern "C" lm_status lm_speculative_step(lm_model* m, int32_t token, int32_t dra
     if (st != LM_OK) return st;
     const int L = m->cfg.n_layers;
     if (!tokens_out || !n_out) return fail(m, LM_E_ARG, "lm_speculative_step: tokens_out or n_out is NULL");
+    if (m->cfg.max_seqs < 2)
+        return fail(m, LM_E_STATE, "lm_speculative_step: the verify pass runs k + 1 tokens as sequences of the "
+                    "several-sequence path; max_seqs = %d; expected 2..4 (Q8_0 / Q4_0 models)", m->cfg.max_seqs);
     if (k < 1 || k > 3 || k + 1 > m->cfg.max_seqs)
         return fail(m, LM_E_ARG, "lm_speculative_step: k = %d; expected 1..%d (k + 1 <= max_seqs <= 4)", k,
                     std::min(3, m->cfg.max_seqs - 1));
