@@ -195,6 +195,22 @@ class Runner:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
+    def step_percentiles(self, n: int) -> dict:
+        """Per-step durations (ms) from an event pair around each of n steps on
+        the model's stream (a separate pass: the events add their own cost)."""
+        import torch
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(self.stream)
+        for i in range(n):
+            self.step()
+            ev[i + 1].record(self.stream)
+        torch.cuda.synchronize()
+        d = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(n))
+        pick = lambda q: d[min(n - 1, int(q * (n - 1) + 0.5))]
+        return {"p10": round(pick(0.1), 4), "median": round(pick(0.5), 4), "p90": round(pick(0.9), 4),
+                "steps": n}
+
     def kernel_profile(self, timing_steps: int):
         """Per-kind (launches, total ms) over graph-replayed steps with HIP events
         captured around every kernel inside the step graph, and the algorithmic
@@ -379,6 +395,11 @@ def run_single(args, name: str, n_seq: int):
         out = {"metric": metric, "config": config}
     out["roofline"] = roofline
     out["read_ceiling_GBps"] = round(n_read / (read_ms * 1e-3) / 1e9, 1)
+    if ms_per_step is not None:
+        out["pct_read_ceiling"] = round(100.0 * out["achieved_hbm_GBps"] / out["read_ceiling_GBps"], 2)
+        r.rewind()
+        out["step_ms_percentiles"] = r.step_percentiles(min(args.steps, 32))
+        r.rewind()
     out["kernels"] = kernel_table(kstats, kbytes, L)
     if n_seq == 1 and one_launch and not args.only_kernels and not args.no_alternatives:
         out["alternatives_ms_per_step"] = alternatives(r, args)
