@@ -140,3 +140,33 @@ def test_kquant_layer_skip_parity(name, mask):
     finally:
         g.close()
         om.close()
+
+
+@pytest.mark.parametrize("name", ["llama8b_q4k", "llama8b_q6k"])
+def test_kquant_full_size_parity(name):
+    """The full 8B-shape K-format models at context 512, the launch
+    configuration the benchmark times: two teacher-forced steps against the
+    oracle, plus sampled rows of every matrix dequantised bit-exactly."""
+    cfg = synth.CONFIGS[name]
+    log(f"generate {name}")
+    model = synth.make_model(cfg)
+    log("run parity")
+    run_parity(model, n_seq=1, steps=2)
+    g = open_gpu(model, max_seqs=1)
+    try:
+        H, F, Q, KV = cfg.hidden, cfg.ffn, cfg.n_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
+        rng = np.random.default_rng(0)
+        for l in (0, cfg.n_layers - 1):
+            w = model.layers[l]
+            for which, (arr, rows, cols) in enumerate([(w.wq, Q, H), (w.wk, KV, H), (w.wv, KV, H),
+                                                       (w.wo, H, Q), (w.w_gate, F, H),
+                                                       (w.w_up, F, H), (w.w_down, H, F)]):
+                for r in (0, rows - 1, int(rng.integers(rows))):
+                    got = g.debug_dequant(l, which, r, 1, cols)
+                    ref = oracle.dequant(cfg.qtype, arr[r:r + 1], 1, cols).astype(np.float32)
+                    assert np.array_equal(got, ref), (l, which, r)
+        for r in (0, cfg.vocab - 1, 77777):
+            got = g.debug_dequant(0, 7, r, 1, H)
+            assert np.array_equal(got, oracle.dequant(cfg.qtype, model.lm_head[r:r + 1], 1, H).astype(np.float32))
+    finally:
+        g.close()
