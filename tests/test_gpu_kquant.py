@@ -20,6 +20,8 @@ CASES = {
     # one super-block per hidden row (8 blocks: a lane group of 8, one block each)
     "tiny_q4k": synth.variant("tiny", qtype=Q4_K, ffn=768),
     "tiny_q6k": synth.variant("tiny", qtype=Q6_K, ffn=768),
+    # an empty prefilled cache (first token at position 0)
+    "tiny_q4k_ctx0": synth.variant("tiny", qtype=Q4_K, ffn=768, ctx=0, steps=3),
     # 64 blocks per row: half of every lane's second pipeline slot is past the row end
     "llama1b_q4k_2layers": synth.variant("multi_llama1b", n_layers=2, qtype=Q4_K, ctx=64, steps=3),
     "llama1b_q6k_2layers": synth.variant("multi_llama1b", n_layers=2, qtype=Q6_K, ctx=64, steps=3),

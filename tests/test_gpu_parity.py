@@ -38,6 +38,8 @@ CASES = {
     "llama8b_q8_2layers_ctx127": synth.variant("llama8b_q8", n_layers=2, ctx=127, steps=3, batch=1),
     # five layers: resident prefixes of every length, both streaming buffers in turn
     "tiny_5layers": synth.variant("tiny", n_layers=5, steps=3),
+    # an empty prefilled cache: the first token sits at position 0 and attends to itself only
+    "tiny_ctx0": synth.variant("tiny", ctx=0, steps=3),
 }
 
 # shapes the one-launch step supports (head_dim 128, hidden and FFN >= 2048)
@@ -539,6 +541,9 @@ def test_state_and_context_errors():
         assert e.value.status == lm.LM_E_ARG
         with pytest.raises(lm.LMError) as e:
             m.step([1, 2])
+        assert e.value.status == lm.LM_E_ARG
+        with pytest.raises(lm.LMError) as e:      # an empty batch
+            m.step([])
         assert e.value.status == lm.LM_E_ARG
         first = m.step([5])
         for _ in range(cfg.steps - 1):
