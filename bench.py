@@ -637,7 +637,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: measures one GPU; --gpus {args.gpus} is not supported "
               "(the per-GPU throughput is the --gpus 1 figure)", file=sys.stderr)
         sys.exit(2)
     if args.steps is None:
