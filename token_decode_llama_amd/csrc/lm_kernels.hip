@@ -112,7 +112,8 @@ __global__ __launch_bounds__(kBlock, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a
     const int64_t rowq = (QT == kQ8_0) ? (int64_t)K : (QT == kQ6_K ? (int64_t)(K >> 1) + (K >> 2) : (int64_t)(K >> 1));
     // scale-plane row in 16-bit words (layouts in lm_internal.h)
     const int srow = QT == kQ4_K ? (K >> 8) * 8 : (QT == kQ6_K ? nb + (K >> 8) : nb);
-    const int jsub = li & 7;   // Q4_K: sub-block of every block this lane reads (LPR is a multiple of 8)
+    static_assert(LPR % 8 == 0, "a lane's blocks must share their position in the 8-block super-block");
+    const int jsub = li & 7;   // Q4_K: sub-block of every block this lane reads
 
     // this wavefront's steps: step0, step0 + sstride, ... ; each step is split
     // into `cps` chunks of CB blocks per lane
