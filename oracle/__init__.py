@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(_HERE, "liboracle.so")
 Q4_0 = 2
 Q8_0 = 8
 Q4_K = 12
+Q5_K = 13
 Q6_K = 14
 
 
@@ -119,7 +120,7 @@ def f64_to_f16(v: float) -> int:
 
 def dequant(qtype: int, blocks: np.ndarray, rows: int, cols: int) -> np.ndarray:
     """GGUF blocks [rows, row bytes] -> fp64 [rows, cols]: Q8_0/Q4_0 as the
-    workload defines them, Q4_K/Q6_K as the GGUF format publishes them (all
+    workload defines them, Q4_K/Q5_K/Q6_K as the GGUF format publishes them (all
     four named on the C/CUDA Llama engine page, section 1)."""
     b = np.ascontiguousarray(blocks, dtype=np.uint8).reshape(rows, -1)
     out = np.empty((rows, cols), np.float64)

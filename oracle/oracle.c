@@ -42,6 +42,10 @@
  *   Q4_K (144 bytes): fp16 d, fp16 dmin, 12 bytes packing eight 6-bit scales
  *         sc_j and eight 6-bit mins m_j (one per 32-weight sub-block j), then
  *         128 bytes of nibbles; value d*sc_j*q - dmin*m_j, q in 0..15;
+ *   Q5_K (176 bytes): the Q4_K header (fp16 d, fp16 dmin, 12 bytes of 6-bit
+ *         scale/min pairs), 32 bytes of high bits (byte l, bit j: element
+ *         32j + l), 128 bytes of low nibbles grouped as in Q4_K; value
+ *         d*sc_j*q - dmin*m_j, q in 0..31;
  *   Q6_K (210 bytes): 128 bytes of low nibbles, 64 bytes of 2-bit high parts,
  *         16 int8 scales (one per 16-weight sub-block), fp16 d; value
  *         d*scale*(q - 32), q in 0..63.
@@ -72,6 +76,7 @@
 #define ORC_Q4_0 2
 #define ORC_Q8_0 8
 #define ORC_Q4_K 12
+#define ORC_Q5_K 13
 #define ORC_Q6_K 14
 
 /* ------------------------------------------------------------------------ */
@@ -134,13 +139,16 @@ int orc_block_bytes(int qtype) {
         case ORC_Q8_0: return 34;
         case ORC_Q4_0: return 18;
         case ORC_Q4_K: return 144;
+        case ORC_Q5_K: return 176;
         case ORC_Q6_K: return 210;
         default: return -1;
     }
 }
 
 /* weights per block: 32 (Q8_0, Q4_0) or 256 (the K formats' super-blocks) */
-int orc_block_weights(int qtype) { return qtype == ORC_Q4_K || qtype == ORC_Q6_K ? 256 : 32; }
+int orc_block_weights(int qtype) {
+    return qtype == ORC_Q4_K || qtype == ORC_Q5_K || qtype == ORC_Q6_K ? 256 : 32;
+}
 
 /* bytes of one row of `cols` weights, or -1 for an unknown type or a ragged row */
 int64_t orc_row_bytes(int qtype, int64_t cols) {
@@ -194,6 +202,22 @@ int orc_dequant_row(int qtype, const uint8_t* row, int64_t cols, double* out) {
                 q4k_scale_min(scales, j, &sc, &mn);
                 uint8_t byte = qs[32 * (j / 2) + e % 32];
                 int q = (j % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+                o[e] = d * (double)sc * (double)q - dmin * (double)mn;
+            }
+        } else if (qtype == ORC_Q5_K) {
+            /* as Q4_K, the nibble area after 32 bytes of high bits: element e
+             * of sub-block j = e / 32 takes bit j of high-bit byte e % 32 as
+             * its fifth bit */
+            double d = orc_f16_to_f64((uint16_t)(blk[0] | (blk[1] << 8)));
+            double dmin = orc_f16_to_f64((uint16_t)(blk[2] | (blk[3] << 8)));
+            const uint8_t* scales = blk + 4;
+            const uint8_t* qh = blk + 16;
+            const uint8_t* qs = blk + 48;
+            for (int e = 0; e < 256; ++e) {
+                int j = e / 32, sc, mn;
+                q4k_scale_min(scales, j, &sc, &mn);
+                uint8_t byte = qs[32 * (j / 2) + e % 32];
+                int q = ((j % 2 == 0) ? (byte & 0x0F) : (byte >> 4)) | (((qh[e % 32] >> j) & 1) << 4);
                 o[e] = d * (double)sc * (double)q - dmin * (double)mn;
             }
         } else {  /* ORC_Q6_K */

@@ -1,7 +1,7 @@
 """Seeded synthetic inputs shared by the oracle and the HIP library.
 
 Only input generation lives here (random numbers, random models already in
-the GGUF Q8_0/Q4_0/Q4_K/Q6_K block formats, fp16 tables, token ids); none of the decode
+the GGUF Q8_0/Q4_0/Q4_K/Q5_K/Q6_K block formats, fp16 tables, token ids); none of the decode
 step's arithmetic does.  The C core is ``synth.c``; ``build()`` compiles it.
 
 Workloads (the decode-step configurations this project is measured on):
@@ -36,10 +36,11 @@ LIB_PATH = os.path.join(_HERE, "libsynth.so")
 Q4_0 = 2
 Q8_0 = 8
 Q4_K = 12
+Q5_K = 13
 Q6_K = 14
-BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q4_K: 144, Q6_K: 210}     # bytes per block
-BLOCK_WEIGHTS = {Q8_0: 32, Q4_0: 32, Q4_K: 256, Q6_K: 256}   # weights per block
-QTYPE_NAMES = {Q8_0: "Q8_0", Q4_0: "Q4_0", Q4_K: "Q4_K", Q6_K: "Q6_K"}
+BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q4_K: 144, Q5_K: 176, Q6_K: 210}     # bytes per block
+BLOCK_WEIGHTS = {Q8_0: 32, Q4_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256}   # weights per block
+QTYPE_NAMES = {Q8_0: "Q8_0", Q4_0: "Q4_0", Q4_K: "Q4_K", Q5_K: "Q5_K", Q6_K: "Q6_K"}
 
 
 def row_bytes(qtype: int, cols: int) -> int:

@@ -34,6 +34,10 @@
  *         Layout: fp16 d, fp16 dmin, 12 bytes of packed 6-bit sc/m, 128 bytes
  *         of nibbles (bytes 32g..32g+31 hold sub-block 2g in their low
  *         nibbles and sub-block 2g+1 in their high nibbles).
+ *   Q5_K (176 bytes): as Q4_K with 31 steps per sub-block instead of 15
+ *         (q = clamp(round((w + dmin*m_j)/(d*sc_j)), 0, 31)).  Layout: the
+ *         Q4_K header, 32 bytes of fifth bits (bit j of byte l: element
+ *         32j + l), 128 bytes of low nibbles grouped as in Q4_K.
  *   Q6_K (210 bytes): per 16-weight sub-block k, s_k = max|w|/31;
  *         d = max_k s_k / 127; sc_k = round(s_k/d) (0..127, stored int8);
  *         q = clamp(round(w/(d*sc_k)), -32, 31) + 32.  Layout: 128 bytes of
@@ -48,6 +52,7 @@
 #define SYN_Q4_0 2
 #define SYN_Q8_0 8
 #define SYN_Q4_K 12
+#define SYN_Q5_K 13
 #define SYN_Q6_K 14
 
 /* ---- Philox4x32-10 (Salmon et al. SC'11, section 3.2 / table 2 constants) */
@@ -171,7 +176,12 @@ static void quant_block_q4_0(const float* w, uint8_t* out) {
     for (int j = 0; j < 16; ++j) out[2 + j] = (uint8_t)(q[j] | (q[j + 16] << 4));
 }
 
-static void quant_block_q4_k(const float* w, uint8_t* out) {
+/* Q4_K (levels 15) and Q5_K (levels 31): shared header recipe */
+static void quant_block_kmin(const float* w, uint8_t* out, int levels);
+static void quant_block_q4_k(const float* w, uint8_t* out) { quant_block_kmin(w, out, 15); }
+static void quant_block_q5_k(const float* w, uint8_t* out) { quant_block_kmin(w, out, 31); }
+
+static void quant_block_kmin(const float* w, uint8_t* out, int levels) {
     float s[8], mn[8], smax = 0.0f, mmax = 0.0f;
     for (int j = 0; j < 8; ++j) {
         float lo = w[32 * j], hi = w[32 * j];
@@ -180,7 +190,7 @@ static void quant_block_q4_k(const float* w, uint8_t* out) {
             if (w[32 * j + i] > hi) hi = w[32 * j + i];
         }
         mn[j] = lo < 0.0f ? -lo : 0.0f;
-        s[j] = (hi + mn[j]) / 15.0f;
+        s[j] = (hi + mn[j]) / (float)levels;
         if (s[j] > smax) smax = s[j];
         if (mn[j] > mmax) mmax = mn[j];
     }
@@ -208,13 +218,19 @@ static void quant_block_q4_k(const float* w, uint8_t* out) {
         if (es > 0.0f) {
             v = (int)roundf((w[e] + em) / es);
             if (v < 0) v = 0;
-            if (v > 15) v = 15;
+            if (v > levels) v = levels;
         }
         q[e] = v;
     }
-    uint8_t* qs = out + 16;
+    uint8_t* qs = out + (levels == 15 ? 16 : 48);
     for (int g = 0; g < 4; ++g)
-        for (int l = 0; l < 32; ++l) qs[32 * g + l] = (uint8_t)(q[64 * g + l] | (q[64 * g + 32 + l] << 4));
+        for (int l = 0; l < 32; ++l)
+            qs[32 * g + l] = (uint8_t)((q[64 * g + l] & 15) | ((q[64 * g + 32 + l] & 15) << 4));
+    if (levels == 31) {
+        uint8_t* qh = out + 16;
+        memset(qh, 0, 32);
+        for (int e = 0; e < 256; ++e) qh[e % 32] |= (uint8_t)(((q[e] >> 4) & 1) << (e / 32));
+    }
 }
 
 static void quant_block_q6_k(const float* w, uint8_t* out) {
@@ -257,17 +273,21 @@ static int block_bytes(int qtype) {
         case SYN_Q8_0: return 34;
         case SYN_Q4_0: return 18;
         case SYN_Q4_K: return 144;
+        case SYN_Q5_K: return 176;
         case SYN_Q6_K: return 210;
         default: return -1;
     }
 }
-static int block_weights(int qtype) { return qtype == SYN_Q4_K || qtype == SYN_Q6_K ? 256 : 32; }
+static int block_weights(int qtype) {
+    return qtype == SYN_Q4_K || qtype == SYN_Q5_K || qtype == SYN_Q6_K ? 256 : 32;
+}
 
 static void quant_block(int qtype, const float* w, uint8_t* out) {
     switch (qtype) {
         case SYN_Q8_0: quant_block_q8_0(w, out); break;
         case SYN_Q4_0: quant_block_q4_0(w, out); break;
         case SYN_Q4_K: quant_block_q4_k(w, out); break;
+        case SYN_Q5_K: quant_block_q5_k(w, out); break;
         default: quant_block_q6_k(w, out); break;
     }
 }

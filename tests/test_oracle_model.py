@@ -22,7 +22,7 @@ import torch
 
 import oracle
 import synth
-from synth import Q4_0, Q4_K, Q6_K, Q8_0
+from synth import Q4_0, Q4_K, Q5_K, Q6_K, Q8_0
 from tests.test_oracle_pins import _numpy_dequant
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -100,7 +100,7 @@ def _hf_model(model):
 
 # the K formats' 256-weight super-blocks need every input width a multiple of 256
 @pytest.mark.parametrize("name,qtype,ffn", [("tiny", Q8_0, 704), ("tiny", Q4_0, 704),
-                                            ("tiny", Q4_K, 768), ("tiny", Q6_K, 768)])
+                                            ("tiny", Q4_K, 768), ("tiny", Q5_K, 768), ("tiny", Q6_K, 768)])
 def test_oracle_matches_transformers_llama(name, qtype, ffn):
     from transformers.cache_utils import DynamicCache
     cfg = synth.variant(name, qtype=qtype, ffn=ffn)

@@ -15,7 +15,7 @@ import torch.nn.functional as F
 
 import oracle
 import synth
-from synth import Q4_0, Q4_K, Q6_K, Q8_0
+from synth import Q4_0, Q4_K, Q5_K, Q6_K, Q8_0
 
 RNG = np.random.default_rng(1234)
 
@@ -218,6 +218,40 @@ def _encode_q4_k(d_bits, dmin_bits, sc, mn, q):
     return blk
 
 
+def _encode_q5_k(d_bits, dmin_bits, sc, mn, q):
+    """Q4_K's encoding of the low four bits, then the fifth bits after the header."""
+    b4 = _encode_q4_k(d_bits, dmin_bits, sc, mn, np.asarray(q) & 15)
+    blk = np.zeros(176, np.uint8)
+    blk[0:16] = b4[0:16]
+    blk[48:176] = b4[16:144]
+    for e in range(256):
+        blk[16 + e % 32] |= ((q[e] >> 4) & 1) << (e // 32)
+    return blk
+
+
+def test_q5_k_hand_worked_superblock():
+    # the Q4_K header of the hand-worked Q4_K case (d 1.0, dmin 0.25, the same
+    # eight (scale, min) pairs); fifth bits set for elements 33 (byte 1, bit 1),
+    # 130 (byte 2, bit 4) and 255 (byte 31, bit 7)
+    blk = np.zeros(176, np.uint8)
+    blk[0:4] = [0x00, 0x3C, 0x00, 0x34]
+    blk[4:16] = [65, 130, 255, 0, 128, 68, 193, 127, 129, 81, 240, 5]
+    qh, qs = blk[16:48], blk[48:]
+    qh[1] = 0x02
+    qh[2] = 0x10
+    qh[31] = 0x80
+    qs[1] = 0x90      # element 33 (sub-block 1, high nibble): q = 9 + 16 = 25
+    qs[66] = 0x03     # element 130 (sub-block 4, low nibble): q = 3 + 16 = 19
+    qs[0] = 0x07      # element 0 (sub-block 0): q = 7, no fifth bit
+    expect = np.repeat([0.0, -1.0, -0.25, -15.75, -10.0, -5.25, -15.75, -4.0], 32)
+    expect[0] = 7.0          # 1 * 7
+    expect[33] = 49.0        # 2 * 25 - 0.25 * 4
+    expect[130] = 313.0      # 17 * 19 - 0.25 * 40
+    expect[255] = 76.0       # 5 * 16 - 0.25 * 16 (nibble 0, fifth bit set)
+    got = oracle.dequant(Q5_K, blk, 1, 256)[0]
+    assert np.array_equal(got, expect), np.nonzero(got != expect)
+
+
 def _encode_q6_k(d_bits, sc, q):
     blk = np.zeros(210, np.uint8)
     for e in range(256):
@@ -242,13 +276,17 @@ def test_k_formats_decode_random_fields(seed):
     blk = _encode_q4_k(_f16_bits(d), _f16_bits(dmin), sc, mn, q)
     want = float(d) * np.repeat(sc, 32) * q - float(dmin) * np.repeat(mn, 32)
     assert np.array_equal(oracle.dequant(Q4_K, blk, 1, 256)[0], want)
+    q5 = r.integers(0, 32, 256)
+    blk5 = _encode_q5_k(_f16_bits(d), _f16_bits(dmin), sc, mn, q5)
+    want5 = float(d) * np.repeat(sc, 32) * q5 - float(dmin) * np.repeat(mn, 32)
+    assert np.array_equal(oracle.dequant(Q5_K, blk5, 1, 256)[0], want5)
     d6, sc6, q6 = np.float16(r.uniform(-1, 1)), r.integers(-128, 128, 16), r.integers(0, 64, 256)
     blk6 = _encode_q6_k(_f16_bits(d6), sc6, q6)
     want6 = float(d6) * np.repeat(sc6, 16) * (q6 - 32)
     assert np.array_equal(oracle.dequant(Q6_K, blk6, 1, 256)[0], want6)
 
 
-@pytest.mark.parametrize("qtype,step_bound", [(Q4_K, 0.55), (Q6_K, 0.55)])
+@pytest.mark.parametrize("qtype,step_bound", [(Q4_K, 0.55), (Q5_K, 0.55), (Q6_K, 0.55)])
 def test_k_quantizer_round_trip(qtype, step_bound):
     # the generator's K blocks dequantise to within about half a quantisation
     # step of the drawn values (clamping can only widen the extreme bins)
@@ -256,13 +294,13 @@ def test_k_quantizer_round_trip(qtype, step_bound):
     blk = synth.quantize(w, qtype)
     assert blk.size == 16 * synth.BLOCK_BYTES[qtype]
     got = oracle.dequant(qtype, blk, 1, w.size)[0]
-    span = 15 if qtype == Q4_K else 62
-    sub = 32 if qtype == Q4_K else 16
+    span = {Q4_K: 15, Q5_K: 31, Q6_K: 62}[qtype]
+    sub = 16 if qtype == Q6_K else 32
     ws = w.reshape(-1, sub).astype(np.float64)
-    step = (ws.max(1) - np.minimum(ws.min(1), 0)) / span if qtype == Q4_K else np.abs(ws).max(1) * 2 / span
+    step = (ws.max(1) - np.minimum(ws.min(1), 0)) / span if qtype != Q6_K else np.abs(ws).max(1) * 2 / span
     err = np.abs(got.reshape(-1, sub) - ws)
     assert np.all(err <= step_bound * step[:, None] * 1.2 + 1e-9)
-    assert np.corrcoef(got, w)[0, 1] > (0.99 if qtype == Q4_K else 0.999)
+    assert np.corrcoef(got, w)[0, 1] > {Q4_K: 0.99, Q5_K: 0.998, Q6_K: 0.999}[qtype]
     z = synth.quantize(np.zeros(512, np.float32), qtype)
     assert np.all(oracle.dequant(qtype, z, 1, 512) == 0)
 
@@ -270,7 +308,7 @@ def test_k_quantizer_round_trip(qtype, step_bound):
 def _numpy_dequant(qtype, blocks, rows, cols):
     """Independent dequantiser written from the format definition (vectorised
     over whole planes, where the oracle walks element by element)."""
-    if qtype in (Q4_K, Q6_K):
+    if qtype in (Q4_K, Q5_K, Q6_K):
         return _numpy_dequant_k(qtype, blocks, rows, cols)
     bb = synth.BLOCK_BYTES[qtype]
     b = np.ascontiguousarray(blocks, np.uint8).reshape(rows, cols // 32, bb)
@@ -288,14 +326,18 @@ def _numpy_dequant_k(qtype, blocks, rows, cols):
     """GGUF K formats, 256-weight super-blocks, from the published layout."""
     nsb = cols // 256
     b = np.ascontiguousarray(blocks, np.uint8).reshape(rows, nsb, synth.BLOCK_BYTES[qtype])
-    if qtype == Q4_K:
+    if qtype in (Q4_K, Q5_K):
         d = b[..., 0:2].copy().view(np.float16)[..., 0].astype(np.float64)
         dmin = b[..., 2:4].copy().view(np.float16)[..., 0].astype(np.float64)
         s = b[..., 4:16].astype(np.int64)
         sc = np.concatenate([s[..., 0:4] & 63, (s[..., 8:12] & 15) | ((s[..., 0:4] >> 6) << 4)], axis=-1)
         mn = np.concatenate([s[..., 4:8] & 63, (s[..., 8:12] >> 4) | ((s[..., 4:8] >> 6) << 4)], axis=-1)
-        qs = b[..., 16:144].reshape(rows, nsb, 4, 32).astype(np.int64)
+        off = 16 if qtype == Q4_K else 48
+        qs = b[..., off:off + 128].reshape(rows, nsb, 4, 32).astype(np.int64)
         q = np.stack([qs & 15, qs >> 4], axis=3).reshape(rows, nsb, 8, 32)   # sub-blocks 2g, 2g+1
+        if qtype == Q5_K:
+            qh = b[..., 16:48].astype(np.int64)                               # [l], bit j: sub-block j
+            q = q | (((qh[:, :, None, :] >> np.arange(8)[None, None, :, None]) & 1) << 4)
         w = d[..., None, None] * sc[..., None] * q - dmin[..., None, None] * mn[..., None]
         return w.reshape(rows, cols)
     ql = b[..., 0:128].reshape(rows, nsb, 2, 2, 32).astype(np.int64)   # [half][which 32 bytes][l]
@@ -312,7 +354,8 @@ def _numpy_dequant_k(qtype, blocks, rows, cols):
     return w.reshape(rows, cols)
 
 
-@pytest.mark.parametrize("qtype,cols", [(Q8_0, 32 * 13), (Q4_0, 32 * 13), (Q4_K, 256 * 3), (Q6_K, 256 * 3)])
+@pytest.mark.parametrize("qtype,cols", [(Q8_0, 32 * 13), (Q4_0, 32 * 13), (Q4_K, 256 * 3), (Q5_K, 256 * 3),
+                                        (Q6_K, 256 * 3)])
 def test_dequant_matches_format_definition(qtype, cols):
     rows = 37
     blocks = synth.quant_matrix(7, 99, rows, cols, 0.02, qtype)
@@ -325,7 +368,7 @@ def test_dequant_matches_format_definition(qtype, cols):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("qtype,rows,cols", [(Q8_0, 8, 64), (Q4_0, 6, 96), (Q8_0, 3, 32),
-                                             (Q4_K, 3, 512), (Q6_K, 3, 256)])
+                                             (Q4_K, 3, 512), (Q5_K, 2, 512), (Q6_K, 3, 256)])
 def test_gemv_brute_force_fraction(qtype, rows, cols):
     blocks = synth.quant_matrix(5, 17 + rows, rows, cols, 0.02, qtype)
     x = RNG.standard_normal(cols)
