@@ -18,7 +18,7 @@ Other workloads (--workload), each printing one JSON line of its own:
                resident in HBM, then (b) layer streaming from pinned host
                memory through two HBM layer buffers, (c) the engine page's
                hybrid split, (d) streaming with 20 layers skipped
-  llama8b_q4k, llama8b_q6k    8B shape in the GGUF K formats, batch 1, KV
+  llama8b_q4k, llama8b_q5k, llama8b_q6k   8B shape in the GGUF K formats, batch 1, KV
                context 512 (+64 steps), weights resident
   llama70b_q4k, llama70b_q6k  70B shape in the K formats, as llama70b_q4;
                the hybrid split is the page's for that format (Q4_K_M: 36
@@ -60,8 +60,8 @@ WORKLOAD_TEXT = {
     "llama70b_q4": "Llama-3.1-70B-shaped synthetic decoder (vocab 128256, hidden 8192, 80 layers, "
                    "64/8 heads, hd 128, ffn 28672), Q4_0 weights, batch 1, KV context 1024 (+steps)",
 }
-for _qt in ("q4k", "q6k"):
-    _fmt = {"q4k": "Q4_K", "q6k": "Q6_K"}[_qt]
+for _qt in ("q4k", "q5k", "q6k"):
+    _fmt = {"q4k": "Q4_K", "q5k": "Q5_K", "q6k": "Q6_K"}[_qt]
     WORKLOAD_TEXT[f"llama8b_{_qt}"] = (f"Llama-3.1-8B-shaped synthetic decoder ({SHAPE_8B}), {_fmt} weights "
                                        "resident in HBM, batch 1, KV context 512 (+steps), greedy decode")
     WORKLOAD_TEXT[f"llama70b_{_qt}"] = WORKLOAD_TEXT["llama70b_q4"].replace("Q4_0", _fmt)
@@ -620,7 +620,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama8b_q8",
                     choices=["llama8b_q8", "llama8b_q4", "multi", "llama70b_q4", "llama8b_q4k",
-                             "llama8b_q6k", "llama70b_q4k", "llama70b_q6k"])
+                             "llama8b_q5k", "llama8b_q6k", "llama70b_q4k", "llama70b_q6k"])
     ap.add_argument("--timing-steps", type=int, default=8,
                     help="eager steps with per-kernel HIP events for the roofline")
     ap.add_argument("--stream-steps", type=int, default=16, help="timed steps in layer-streaming mode (70B)")
@@ -642,7 +642,7 @@ def main():
         sys.exit(2)
     if args.steps is None:
         args.steps = {"llama8b_q8": 64, "llama8b_q4": 32, "multi": 32, "llama70b_q4": 16, "llama8b_q4k": 64,
-                      "llama8b_q6k": 64, "llama70b_q4k": 16, "llama70b_q6k": 16}[args.workload]
+                      "llama8b_q5k": 64, "llama8b_q6k": 64, "llama70b_q4k": 16, "llama70b_q6k": 16}[args.workload]
 
     import torch
     if not torch.cuda.is_available():
@@ -653,7 +653,7 @@ def main():
         out = run_single(args, "llama8b_q8", 1)
     elif args.workload == "llama8b_q4":
         out = run_single(args, "llama8b_q4", 4)
-    elif args.workload in ("llama8b_q4k", "llama8b_q6k"):
+    elif args.workload in ("llama8b_q4k", "llama8b_q5k", "llama8b_q6k"):
         out = run_single(args, args.workload, 1)
     elif args.workload == "multi":
         out = run_multi(args)

@@ -57,7 +57,7 @@ typedef enum {
 } lm_status;
 
 /* GGUF type ids of the block formats (the C/CUDA Llama engine page, section 1,
- * lists Q4_0, Q8_0, Q4_K and Q6_K among the formats it reads; the K formats
+ * lists Q4_0, Q8_0, Q4_K, Q5_K and Q6_K among the formats it reads; the K formats
  * carry its 70B figures).
  * Q8_0: 34-byte block = fp16 d (little endian) + 32 int8 q; w = d * q.
  * Q4_0: 18-byte block = fp16 d + 16 bytes; byte j holds element j in its low
@@ -67,13 +67,17 @@ typedef enum {
  *       per 32-weight sub-block j, 128 bytes of nibbles (32-byte group g:
  *       sub-block 2g in the low nibbles, 2g+1 in the high ones);
  *       w = d * sc_j * q - dmin * m_j.
+ * Q5_K: 176-byte super-block = the Q4_K header (d, dmin, 12 bytes of 6-bit
+ *       pairs), 32 bytes of fifth bits (bit j of byte l: element 32j + l), 128
+ *       bytes of low nibbles grouped as in Q4_K; w = d * sc_j * q - dmin * m_j,
+ *       q = 5 bits.
  * Q6_K: 210-byte super-block of 256 weights = 128 bytes of low nibbles, 64
  *       bytes of 2-bit high parts, 16 int8 scales (one per 16 weights), fp16
  *       d; w = d * scale * (q - 32), q = 6 bits.
  * The K formats need every matrix input width (hidden, ffn, n_heads *
  * head_dim) to be a multiple of 256 and decode one sequence per step
  * (max_seqs = 1); the one-launch step modes are not built for them. */
-typedef enum { LM_Q4_0 = 2, LM_Q8_0 = 8, LM_Q4_K = 12, LM_Q6_K = 14 } lm_qtype;
+typedef enum { LM_Q4_0 = 2, LM_Q8_0 = 8, LM_Q4_K = 12, LM_Q5_K = 13, LM_Q6_K = 14 } lm_qtype;
 
 typedef struct {
     int32_t vocab;       /* rows of the LM head, rows of the embedding table */

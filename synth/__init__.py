@@ -17,6 +17,7 @@ Workloads (the decode-step configurations this project is measured on):
   batch 1, seeds 5 / 6
 * llama70b_q4k / llama70b_q6k: the 70B shape in Q4_K / Q6_K, ctx 1024,
   16 steps, seeds 7 / 8
+* llama8b_q5k: the 8B shape in Q5_K, ctx 512 (+64 steps), batch 1, seed 9
 
 Distributions: weights N(0, 0.02) quantised block by block; fp16 token
 embeddings N(0, 0.02); fp32 norm gains N(1, 0.1); fp16 KV N(0, 1) for every
@@ -218,6 +219,9 @@ CONFIGS = {
     "llama8b_q6k": _cfg(name="llama8b_q6k", vocab=128256, hidden=4096, n_layers=32, n_heads=32,
                         n_kv_heads=8, head_dim=128, ffn=14336, qtype=Q6_K, ctx=512, steps=64,
                         batch=1, seed=6),
+    "llama8b_q5k": _cfg(name="llama8b_q5k", vocab=128256, hidden=4096, n_layers=32, n_heads=32,
+                        n_kv_heads=8, head_dim=128, ffn=14336, qtype=Q5_K, ctx=512, steps=64,
+                        batch=1, seed=9),
     "llama70b_q4k": _cfg(name="llama70b_q4k", vocab=128256, hidden=8192, n_layers=80,
                          n_heads=64, n_kv_heads=8, head_dim=128, ffn=28672, qtype=Q4_K,
                          ctx=1024, steps=16, batch=1, seed=7),

@@ -115,7 +115,7 @@ def test_tier_sizes_rejects_bad_arguments():
     (dict(n_heads=2, n_kv_heads=2, head_dim=64, hidden=256), "n_heads * head_dim"),
     (dict(max_seqs=2), "max_seqs"),
 ])
-@pytest.mark.parametrize("qtype", [lm.LM_Q4_K, lm.LM_Q6_K])
+@pytest.mark.parametrize("qtype", [lm.LM_Q4_K, lm.LM_Q5_K, lm.LM_Q6_K])
 def test_create_rejects_k_formats_outside_their_shapes(qtype, changes, needle):
     """Q4_K / Q6_K: 256-weight super-blocks along every GEMV input, one
     sequence per step; checked before any device call."""

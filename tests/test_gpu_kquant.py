@@ -1,6 +1,6 @@
-"""GGUF K formats (Q4_K, Q6_K) on the batch-1 path against the fp64 oracle.
+"""GGUF K formats (Q4_K, Q5_K, Q6_K) on the batch-1 path against the fp64 oracle.
 
-The C/CUDA Llama engine page, section 1, lists both among the formats it reads
+The C/CUDA Llama engine page, section 1, lists them among the formats it reads
 and quotes its 70B figures in them.  Same bar as the Q8_0 / Q4_0 parity tests:
 dequantisation bit-exact, logits within 1e-3 max|logit| per step, the argmax
 equal, appended K/V rows within one fp16 ulp plus the fp32 error.
@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import synth
-from synth import Q4_K, Q6_K
+from synth import Q4_K, Q5_K, Q6_K
 from tests.helpers import log, open_gpu
 from tests.test_gpu_parity import run_parity
 
@@ -20,17 +20,21 @@ CASES = {
     # one super-block per hidden row (8 blocks: a lane group of 8, one block each)
     "tiny_q4k": synth.variant("tiny", qtype=Q4_K, ffn=768),
     "tiny_q6k": synth.variant("tiny", qtype=Q6_K, ffn=768),
+    "tiny_q5k": synth.variant("tiny", qtype=Q5_K, ffn=768),
     # an empty prefilled cache (first token at position 0)
     "tiny_q4k_ctx0": synth.variant("tiny", qtype=Q4_K, ffn=768, ctx=0, steps=3),
     # 64 blocks per row: half of every lane's second pipeline slot is past the row end
     "llama1b_q4k_2layers": synth.variant("multi_llama1b", n_layers=2, qtype=Q4_K, ctx=64, steps=3),
     "llama1b_q6k_2layers": synth.variant("multi_llama1b", n_layers=2, qtype=Q6_K, ctx=64, steps=3),
+    "llama1b_q5k_2layers": synth.variant("multi_llama1b", n_layers=2, qtype=Q5_K, ctx=64, steps=3),
     # 8B layer shapes (down: 448 blocks per row, a ragged last chunk), context crossing a chunk
     "llama8b_q4k_2layers_ctx127": synth.variant("llama8b_q8", n_layers=2, qtype=Q4_K, ctx=127, steps=3),
     "llama8b_q6k_2layers_ctx127": synth.variant("llama8b_q8", n_layers=2, qtype=Q6_K, ctx=127, steps=3),
+    "llama8b_q5k_2layers_ctx127": synth.variant("llama8b_q8", n_layers=2, qtype=Q5_K, ctx=127, steps=3),
     # the 70B shape's layers (hidden 8192, ffn 28672, 64/8 heads) at its context length
     "llama70b_q4k_2layers": synth.variant("llama70b_q4", n_layers=2, qtype=Q4_K, steps=2),
     "llama70b_q6k_2layers": synth.variant("llama70b_q4", n_layers=2, qtype=Q6_K, steps=2),
+    "llama70b_q5k_2layers": synth.variant("llama70b_q4", n_layers=2, qtype=Q5_K, steps=2),
 }
 
 _models = {}
@@ -48,7 +52,8 @@ def test_kquant_decode_parity(name):
     run_parity(get_model(name), n_seq=1)
 
 
-@pytest.mark.parametrize("name", ["tiny_q4k", "tiny_q6k", "llama1b_q4k_2layers", "llama1b_q6k_2layers"])
+@pytest.mark.parametrize("name", ["tiny_q4k", "tiny_q6k", "tiny_q5k", "llama1b_q4k_2layers",
+                                  "llama1b_q6k_2layers", "llama1b_q5k_2layers"])
 def test_kquant_dequant_bit_exact_all_rows(name):
     model = get_model(name)
     cfg = model.cfg
@@ -144,7 +149,7 @@ def test_kquant_layer_skip_parity(name, mask):
         om.close()
 
 
-@pytest.mark.parametrize("name", ["llama8b_q4k", "llama8b_q6k"])
+@pytest.mark.parametrize("name", ["llama8b_q4k", "llama8b_q5k", "llama8b_q6k"])
 def test_kquant_full_size_parity(name):
     """The full 8B-shape K-format models at context 512, the launch
     configuration the benchmark times: two teacher-forced steps against the

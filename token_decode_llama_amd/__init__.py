@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblmdecode.so")
 
 LM_OK, LM_E_ARG, LM_E_STATE, LM_E_OOM, LM_E_HIP, LM_E_CTX = range(6)
-LM_Q4_0, LM_Q8_0, LM_Q4_K, LM_Q6_K = 2, 8, 12, 14
+LM_Q4_0, LM_Q8_0, LM_Q4_K, LM_Q5_K, LM_Q6_K = 2, 8, 12, 13, 14
 KERNEL_KINDS = ("embed", "qkv", "attn", "wo", "gateup", "down", "lmhead", "copy", "step", "flow")
 
 # every symbol include/lmdecode.h declares

@@ -130,6 +130,27 @@ __device__ __forceinline__ void q4k_scale_min(const int4 h, int j, float& ds, fl
     dm = h2f((uint16_t)((uint32_t)h.x >> 16)) * (float)mn;
 }
 
+// Q5_K sub-block (32 weights): A = low nibbles in the Q4_0 order, H = the
+// fifth bits (element 4u+k's at bit 8k + u, element 16+4u+k's at bit
+// 8k + 4 + u).  Returns sum q x over the sub-block, q = nibble | bit << 4
+// (0..31, unsigned in the dot products).
+__device__ __forceinline__ float dot_q5(const int4 A, const uint32_t H, const int4* D) {
+    const int4 e0 = D[0], e1 = D[1], f0 = D[2], f1 = D[3], g0 = D[4], g1 = D[5];
+    const int w[4] = {A.x, A.y, A.z, A.w};
+    const int E0[4] = {e0.x, e0.y, e0.z, e0.w}, E1[4] = {e1.x, e1.y, e1.z, e1.w};
+    const int F0[4] = {f0.x, f0.y, f0.z, f0.w}, F1[4] = {f1.x, f1.y, f1.z, f1.w};
+    const int G0[4] = {g0.x, g0.y, g0.z, g0.w}, G1[4] = {g1.x, g1.y, g1.z, g1.w};
+    int s0 = 0, s1 = 0, s2 = 0;
+    #pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int lo = (int)(((uint32_t)w[u] & 0x0F0F0F0Fu) | ((H << (4 - u)) & 0x10101010u));
+        const int hi = (int)((((uint32_t)w[u] >> 4) & 0x0F0F0F0Fu) | ((H >> u) & 0x10101010u));
+        s0 = sdot4(lo, E0[u], s0); s1 = sdot4(lo, F0[u], s1); s2 = sdot4(lo, G0[u], s2);
+        s0 = sdot4(hi, E1[u], s0); s1 = sdot4(hi, F1[u], s1); s2 = sdot4(hi, G1[u], s2);
+    }
+    return combine_digits(s0, s1, s2);
+}
+
 // Q6_K block (32 weights, two 16-weight sub-blocks): A = low nibbles in the
 // Q4_0 order, Hb = the high parts (word x: elements 0..15, y: 16..31; element
 // 4u+k's two bits at bit 8k + 2u).  q = low | high << 4 (0..63) enters the dot

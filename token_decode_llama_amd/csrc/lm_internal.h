@@ -11,8 +11,9 @@ namespace lmk {
 constexpr int kQ4_0 = 2;
 constexpr int kQ8_0 = 8;
 constexpr int kQ4_K = 12;   // GGUF K formats: 256-weight super-blocks (batch-1 GEMV only)
+constexpr int kQ5_K = 13;
 constexpr int kQ6_K = 14;
-constexpr bool is_kquant(int qtype) { return qtype == kQ4_K || qtype == kQ6_K; }
+constexpr bool is_kquant(int qtype) { return qtype == kQ4_K || qtype == kQ5_K || qtype == kQ6_K; }
 constexpr int kAttnChunk = 64;     // KV positions per attention workgroup
 constexpr int kCntStride = 32;     // ints per attention chunk counter: one 128-byte line each, so
                                    // that different counters do not serialise each other's atomics
@@ -34,6 +35,9 @@ constexpr int attn_cnt_lines(int max_chunks) { return 1 + (max_chunks + kCntGrou
 //         regrouped into the Q4_0 nibble order; scales: the super-blocks'
 //         16-byte headers as stored (fp16 d, fp16 dmin, 12 bytes of packed
 //         6-bit scale/min pairs) [N][nsb][16];
+//   Q5_K: as Q4_K, each quant row followed by nb x 4 bytes of fifth bits: the
+//         32-bit word of a block holds element 4u+k's bit at bit 8k + u and
+//         element 16+4u+k's at bit 8k + 4 + u (u, k < 4);
 //   Q6_K: quants, each row = nb x 16 bytes of low nibbles (Q4_0 order), then
 //         nb x 8 bytes of 2-bit high parts: words h0 (elements 0..15) and h1
 //         (16..31) of a block hold element 4u+k's (u, k < 4) two bits at bit
@@ -65,11 +69,12 @@ inline int64_t qfrag_bytes(int qtype, int64_t N, int64_t K) {
 constexpr int64_t qmat_qbytes(int qtype, int64_t N, int64_t K) {
     if (qtype == kQ8_0) return N * K;
     if (qtype == kQ6_K) return N * (K / 2 + K / 4);
+    if (qtype == kQ5_K) return N * (K / 2 + K / 8);
     return N * K / 2;
 }
 // bytes of one row of the scale plane
 constexpr int64_t qmat_srow(int qtype, int64_t K) {
-    if (qtype == kQ4_K) return K / 256 * 16;
+    if (qtype == kQ4_K || qtype == kQ5_K) return K / 256 * 16;
     if (qtype == kQ6_K) return K / 32 * 2 + K / 256 * 2;
     return K / 32 * 2;
 }
@@ -80,6 +85,7 @@ inline int64_t gguf_row_bytes(int qtype, int64_t K) {
         case kQ8_0: return K / 32 * 34;
         case kQ4_0: return K / 32 * 18;
         case kQ4_K: return K / 256 * 144;
+        case kQ5_K: return K / 256 * 176;
         default: return K / 256 * 210;
     }
 }

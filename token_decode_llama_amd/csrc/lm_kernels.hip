@@ -63,6 +63,7 @@ hipError_t launch_embed(const uint16_t* tok_embd, const int* tokens, int vocab, 
 template <int QT> struct ChunkBlocks { static constexpr int value = LMK_CB_Q8; };
 template <> struct ChunkBlocks<kQ4_0> { static constexpr int value = LMK_CB_Q4; };
 template <> struct ChunkBlocks<kQ4_K> { static constexpr int value = LMK_CB_QK; };
+template <> struct ChunkBlocks<kQ5_K> { static constexpr int value = LMK_CB_QK; };
 template <> struct ChunkBlocks<kQ6_K> { static constexpr int value = LMK_CB_QK; };
 
 // One pipeline stage of a lane: CB blocks of both rows of its row pair.
@@ -71,7 +72,9 @@ struct WChunk {
     static constexpr int CB = ChunkBlocks<QT>::value;
     int4 a0[CB], a1[CB];          // first 16 bytes (Q8_0) / the 16 nibble bytes (others) of row 0 / row 1
     int4 b0[QT == kQ8_0 ? CB : 1], b1[QT == kQ8_0 ? CB : 1];   // Q8_0 second halves
-    int4 h0[QT == kQ4_K ? CB : 1], h1[QT == kQ4_K ? CB : 1];   // Q4_K super-block headers
+    static constexpr bool kHdr = QT == kQ4_K || QT == kQ5_K;
+    int4 h0[kHdr ? CB : 1], h1[kHdr ? CB : 1];                 // Q4_K / Q5_K super-block headers
+    uint32_t p0[QT == kQ5_K ? CB : 1], p1[QT == kQ5_K ? CB : 1];   // Q5_K fifth bits
     uint2 e0[QT == kQ6_K ? CB : 1], e1[QT == kQ6_K ? CB : 1];  // Q6_K high bits
     uint16_t d0[CB], d1[CB];      // block scale (Q8_0, Q4_0) / sub-block scale pair (Q6_K)
     uint16_t f0[QT == kQ6_K ? CB : 1], f1[QT == kQ6_K ? CB : 1];   // Q6_K super-block d
@@ -99,7 +102,7 @@ __global__ __launch_bounds__(kBlock, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a
     const int K = a.w.K, N = a.w.N, nb = K >> 5;
     // LDS: per 32-column block, the activation digit planes (96 bytes), its
     // scale, and the digit sums (Q4_0, Q4_K: per block; Q6_K: per 16-column half)
-    constexpr int kSums = (QT == kQ4_0 || QT == kQ4_K) ? 1 : (QT == kQ6_K ? 2 : 0);
+    constexpr int kSums = (QT == kQ4_0 || QT == kQ4_K || QT == kQ5_K) ? 1 : (QT == kQ6_K ? 2 : 0);
     int8_t* xq = (int8_t*)smem;                       // [nb][3][32] int8
     float* xsc = (float*)(xq + nb * 96);              // [nb]
     int4* dsum = (int4*)(xsc + ((nb + 3) & ~3));      // [nb or 2 nb] (T0, T1, T2, 0)
@@ -109,9 +112,9 @@ __global__ __launch_bounds__(kBlock, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a
     const int s = blockIdx.y;
     const float* x = a.xin + (int64_t)s * a.x_stride;
     const int rg = lane / LPR, li = lane % LPR;
-    const int64_t rowq = (QT == kQ8_0) ? (int64_t)K : (QT == kQ6_K ? (int64_t)(K >> 1) + (K >> 2) : (int64_t)(K >> 1));
+    const int64_t rowq = qmat_qbytes(QT, 1, K);
     // scale-plane row in 16-bit words (layouts in lm_internal.h)
-    const int srow = QT == kQ4_K ? (K >> 8) * 8 : (QT == kQ6_K ? nb + (K >> 8) : nb);
+    const int srow = (int)(qmat_srow(QT, K) / 2);
     static_assert(LPR % 8 == 0, "a lane's blocks must share their position in the 8-block super-block");
     const int jsub = li & 7;   // Q4_K: sub-block of every block this lane reads
 
@@ -146,9 +149,13 @@ __global__ __launch_bounds__(kBlock, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a
                 w.b0[u] = ld16_stream(q0 + (uint32_t)nb * 16u + bc * 16u);
                 w.b1[u] = ld16_stream(q1 + (uint32_t)nb * 16u + bc * 16u);
             }
-            if (QT == kQ4_K) {
+            if (QT == kQ4_K || QT == kQ5_K) {
                 w.h0[u] = *(const int4*)(s0 + (bc >> 3) * 8u);
                 w.h1[u] = *(const int4*)(s0 + (uint32_t)srow + (bc >> 3) * 8u);
+                if (QT == kQ5_K) {
+                    w.p0[u] = *(const uint32_t*)(q0 + (uint32_t)nb * 16u + bc * 4u);
+                    w.p1[u] = *(const uint32_t*)(q1 + (uint32_t)nb * 16u + bc * 4u);
+                }
             } else if (QT == kQ6_K) {
                 w.e0[u] = *(const uint2*)(q0 + (uint32_t)nb * 16u + bc * 8u);
                 w.e1[u] = *(const uint2*)(q1 + (uint32_t)nb * 16u + bc * 8u);
@@ -182,7 +189,7 @@ __global__ __launch_bounds__(kBlock, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a
                 const int4 T = dsum[b];
                 acc0 = fmaf(d0 * sx, dot_q4(w.a0[u], D, T), acc0);
                 acc1 = fmaf(d1 * sx, dot_q4(w.a1[u], D, T), acc1);
-            } else if (QT == kQ4_K) {
+            } else if (QT == kQ4_K || QT == kQ5_K) {
                 // sum (ds q - dm) x = ds sum q x - dm sum x over the sub-block
                 float ds0, dm0, ds1, dm1;
                 q4k_scale_min(w.h0[u], jsub, ds0, dm0);
@@ -190,9 +197,11 @@ __global__ __launch_bounds__(kBlock, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a
                 const float f = in_row ? sx : 0.f;
                 const int4 T = dsum[b];
                 const float tx = combine_digits(T.x, T.y, T.z);
-                acc0 = fmaf(ds0 * f, dot_q4<0>(w.a0[u], D, T), acc0);
+                const float q0x = QT == kQ5_K ? dot_q5(w.a0[u], w.p0[u], D) : dot_q4<0>(w.a0[u], D, T);
+                const float q1x = QT == kQ5_K ? dot_q5(w.a1[u], w.p1[u], D) : dot_q4<0>(w.a1[u], D, T);
+                acc0 = fmaf(ds0 * f, q0x, acc0);
                 acc0 = fmaf(-dm0 * f, tx, acc0);
-                acc1 = fmaf(ds1 * f, dot_q4<0>(w.a1[u], D, T), acc1);
+                acc1 = fmaf(ds1 * f, q1x, acc1);
                 acc1 = fmaf(-dm1 * f, tx, acc1);
             } else {  // Q6_K
                 const int4 T0 = dsum[2 * b], T1 = dsum[2 * b + 1];
@@ -498,7 +507,8 @@ hipError_t launch_gemv(const GemvArgs& a, int epi, int n_seq, int max_blocks, hi
     if (epi == EPI_RESID && a.norm_g) return hipErrorInvalidValue;   // the residual products take no gain
     const int nb = a.w.K / 32;
     const int lpr = pick_lpr(nb);
-    const size_t sums = a.qtype == kQ4_0 || a.qtype == kQ4_K ? (size_t)nb * 16 : (a.qtype == kQ6_K ? (size_t)nb * 32 : 0);
+    const size_t sums = a.qtype == kQ4_0 || a.qtype == kQ4_K || a.qtype == kQ5_K ? (size_t)nb * 16
+                      : (a.qtype == kQ6_K ? (size_t)nb * 32 : 0);
     const size_t lds = (size_t)nb * 96 + (size_t)((nb + 3) & ~3) * 4 + sums;
     switch (a.qtype) {
         case kQ8_0: return launch_gemv_epi<kQ8_0>(a, epi, lpr, n_seq, max_blocks, lds, st);
@@ -506,6 +516,9 @@ hipError_t launch_gemv(const GemvArgs& a, int epi, int n_seq, int max_blocks, hi
         case kQ4_K:
             if (a.w.K % 256) return hipErrorInvalidValue;
             return launch_gemv_epi<kQ4_K>(a, epi, lpr, n_seq, max_blocks, lds, st);
+        case kQ5_K:
+            if (a.w.K % 256) return hipErrorInvalidValue;
+            return launch_gemv_epi<kQ5_K>(a, epi, lpr, n_seq, max_blocks, lds, st);
         case kQ6_K:
             if (a.w.K % 256) return hipErrorInvalidValue;
             return launch_gemv_epi<kQ6_K>(a, epi, lpr, n_seq, max_blocks, lds, st);
@@ -1566,10 +1579,16 @@ __global__ __launch_bounds__(kBlock) void k_dequant(QMat w, int qtype, int row0,
             const int nib = e < 16 ? (byte & 0xF) : (byte >> 4);
             if (qtype == kQ4_0) {
                 v = (float)(nib - 8) * h2f(sc[b]);
-            } else if (qtype == kQ4_K) {
+            } else if (qtype == kQ4_K || qtype == kQ5_K) {
                 float ds, dm;
                 q4k_scale_min(*(const int4*)(sc + (b >> 3) * 8), b & 7, ds, dm);
-                v = fmaf(ds, (float)nib, -dm);                  // one rounding of the exact value
+                int q5 = nib;
+                if (qtype == kQ5_K) {
+                    const int ii = e & 15;
+                    const uint8_t hb = q[(int64_t)nb * 16 + b * 4 + (ii & 3)];
+                    q5 |= ((hb >> ((ii >> 2) + (e < 16 ? 0 : 4))) & 1) << 4;
+                }
+                v = fmaf(ds, (float)q5, -dm);                   // one rounding of the exact value
             } else {  // Q6_K
                 const int ii = e & 15;
                 const uint8_t hb = q[(int64_t)nb * 16 + b * 8 + 4 * (e >> 4) + (ii & 3)];

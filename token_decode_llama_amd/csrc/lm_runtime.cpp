@@ -94,12 +94,23 @@ void repack_row(int qtype, const uint8_t* src, int K, uint8_t* dq, uint8_t* dsc)
             std::memcpy(dsc + 2 * b, blk, 2);
             std::memcpy(dq + (int64_t)b * 16, blk + 2, 16);
         }
-    } else if (qtype == kQ4_K) {
+    } else if (qtype == kQ4_K || qtype == kQ5_K) {
+        // Q5_K: the Q4_K header, 32 bytes of fifth bits (bit j of byte l: element 32j + l), the nibbles
+        const bool five = qtype == kQ5_K;
+        const int bytes = five ? 176 : 144, nib = five ? 48 : 16;
+        if (five) std::memset(dq + (int64_t)nb * 16, 0, (size_t)nb * 4);
         for (int sb = 0; sb < K / 256; ++sb) {
-            const uint8_t* blk = src + (int64_t)sb * 144;
+            const uint8_t* blk = src + (int64_t)sb * bytes;
             std::memcpy(dsc + 16 * sb, blk, 16);
+            for (int j = 0; five && j < 8; ++j) {
+                uint8_t* h = dq + (int64_t)nb * 16 + (int64_t)(8 * sb + j) * 4;
+                for (int i = 0; i < 32; ++i) {
+                    const int bit = (blk[16 + i] >> j) & 1, ii = i & 15;
+                    h[(ii & 3)] |= (uint8_t)(bit << ((ii >> 2) + (i < 16 ? 0 : 4)));
+                }
+            }
             for (int j = 0; j < 8; ++j) {
-                const uint8_t* g = blk + 16 + 32 * (j / 2);
+                const uint8_t* g = blk + nib + 32 * (j / 2);
                 const int sh = 4 * (j % 2);
                 uint8_t* o = dq + (int64_t)(8 * sb + j) * 16;
                 for (int i = 0; i < 16; ++i)
@@ -366,15 +377,16 @@ static lm_status check_config(const lm_config* c) {
         return fail(nullptr, LM_E_ARG, "bad config: %s = %lld; expected %s", what, got, expect);
     };
     if (!c) return fail(nullptr, LM_E_ARG, "bad config: NULL pointer");
-    if (c->qtype != LM_Q8_0 && c->qtype != LM_Q4_0 && c->qtype != LM_Q4_K && c->qtype != LM_Q6_K)
-        return bad("qtype", c->qtype, "2 (Q4_0), 8 (Q8_0), 12 (Q4_K) or 14 (Q6_K)");
+    if (c->qtype != LM_Q8_0 && c->qtype != LM_Q4_0 && c->qtype != LM_Q4_K && c->qtype != LM_Q5_K &&
+        c->qtype != LM_Q6_K)
+        return bad("qtype", c->qtype, "2 (Q4_0), 8 (Q8_0), 12 (Q4_K), 13 (Q5_K) or 14 (Q6_K)");
     if (is_kquant(c->qtype)) {
         // 256-weight super-blocks along every GEMV input; one sequence per step
-        if (c->hidden % 256) return bad("hidden", c->hidden, "a multiple of 256 for Q4_K / Q6_K");
-        if (c->ffn % 256) return bad("ffn", c->ffn, "a multiple of 256 for Q4_K / Q6_K");
+        if (c->hidden % 256) return bad("hidden", c->hidden, "a multiple of 256 for the K formats");
+        if (c->ffn % 256) return bad("ffn", c->ffn, "a multiple of 256 for the K formats");
         if ((int64_t)c->n_heads * c->head_dim % 256)
-            return bad("n_heads * head_dim", (long long)c->n_heads * c->head_dim, "a multiple of 256 for Q4_K / Q6_K");
-        if (c->max_seqs != 1) return bad("max_seqs", c->max_seqs, "1 for Q4_K / Q6_K (one sequence per step)");
+            return bad("n_heads * head_dim", (long long)c->n_heads * c->head_dim, "a multiple of 256 for the K formats");
+        if (c->max_seqs != 1) return bad("max_seqs", c->max_seqs, "1 for the K formats (one sequence per step)");
     }
     if (c->vocab < 2 || c->vocab % 2) return bad("vocab", c->vocab, "an even number >= 2");
     if (c->hidden < 32 || c->hidden % 32) return bad("hidden", c->hidden, "a positive multiple of 32");
