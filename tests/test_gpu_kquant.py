@@ -177,3 +177,26 @@ def test_kquant_full_size_parity(name):
             assert np.array_equal(got, oracle.dequant(cfg.qtype, model.lm_head[r:r + 1], 1, H).astype(np.float32))
     finally:
         g.close()
+
+
+def test_kquant_algorithmic_bytes_follow_the_format():
+    """The benchmark's algorithmic bytes (lm_kernel_bytes) differ between two
+    formats of the same shape by exactly the weight-byte difference of the
+    GGUF rows (the activation terms are the same)."""
+    base_cfg = synth.variant("tiny", ffn=768)
+    H, F, V = base_cfg.hidden, base_cfg.ffn, base_cfg.vocab
+    Q, KV, L = base_cfg.n_heads * base_cfg.head_dim, base_cfg.n_kv_heads * base_cfg.head_dim, base_cfg.n_layers
+    shapes = {"qkv": (L * (Q + 2 * KV), H), "wo": (L * H, Q), "gateup": (L * 2 * F, H),
+              "down": (L * H, F), "lmhead": (V, H)}
+    got = {}
+    for qt in (synth.Q8_0, Q4_K, Q5_K, Q6_K):
+        model = synth.make_model(synth.variant("tiny", ffn=768, qtype=qt))
+        g = open_gpu(model, max_seqs=1)
+        try:
+            got[qt] = {k: g.kernel_bytes(k, 1) for k in shapes}
+        finally:
+            g.close()
+    for qt in (Q4_K, Q5_K, Q6_K):
+        for k, (rows, cols) in shapes.items():
+            want = rows * (synth.row_bytes(qt, cols) - synth.row_bytes(synth.Q8_0, cols))
+            assert got[qt][k] - got[synth.Q8_0][k] == want, (qt, k)
