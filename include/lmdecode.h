@@ -159,7 +159,11 @@ lm_status lm_get_position(const lm_model* m, int32_t seq, int32_t* pos);
  * everything resident (the state after lm_model_create); 0: every layer
  * streamed.  Embedding, norms, LM head and KV stay in HBM always.  Legal only
  * between steps; the weights move (device memory peaks at old + new resident
- * arenas).  Outputs are bit-identical for every n_resident.
+ * arenas).  The pinned arena is kept when it can hold the new streamed set
+ * (more layers resident, or fewer when the front it freed before is large
+ * enough; that front stays allocated until the arena is replaced); otherwise a
+ * new one is allocated before the old one is freed.  Outputs are
+ * bit-identical for every n_resident.
  * Errors: LM_E_ARG (n_resident outside 0..L), LM_E_OOM (pinned or device
  * memory; the model is unchanged), LM_E_HIP. */
 lm_status lm_set_residency(lm_model* m, int32_t n_resident);
