@@ -29,6 +29,8 @@ Every line carries:
   roofline        the dominant kernel: algorithmic bytes per launch / average
                   launch duration from HIP events on the model's stream
   cpu_baseline    the fp64 oracle on this host's cores, on a bounded sample
+Side legs (--extras: the opt-in step paths, self-speculative rounds) only add
+fields; a failure in one becomes an "error" entry and never drops the line.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 from __future__ import annotations
@@ -140,6 +142,40 @@ def cpu_baseline(model, cfg, n_seq: int, budget_s: float, max_steps: int = 64):
 
 def public(d):
     return {k: v for k, v in d.items() if not k.startswith("_")}
+
+
+def side_leg(name: str, fn):
+    """Runs an optional measurement; an exception becomes {"error": ...}."""
+    try:
+        return fn()
+    except Exception as e:  # noqa: BLE001 - reported in the line, never fatal
+        log(f"{name} failed: {type(e).__name__}: {e}")
+        return {"error": f"{type(e).__name__}: {e}"}
+
+
+def input_digests(model, n_seq: int) -> dict:
+    """SHA-256 of every input tensor kind: the global tensors one by one, each
+    per-layer kind over its layers' bytes concatenated in layer order, and the
+    prefilled KV of every (sequence, layer) in order (K then V)."""
+    import synth
+    cfg = model.cfg
+    out = {"tok_embd": hashlib.sha256(model.tok_embd.tobytes()).hexdigest(),
+           "out_norm": hashlib.sha256(model.out_norm.tobytes()).hexdigest(),
+           "lm_head": hashlib.sha256(model.lm_head.tobytes()).hexdigest()}
+    for kind in ("attn_norm", "ffn_norm", "wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down"):
+        h = hashlib.sha256()
+        for lw in model.layers:
+            h.update(memoryview(getattr(lw, kind)).cast("B"))
+        out[f"layers.{kind}"] = h.hexdigest()
+    h = hashlib.sha256()
+    for s in range(n_seq):
+        for l in range(cfg.n_layers):
+            k, v = synth.make_kv(cfg, s, l)
+            h.update(k.tobytes())
+            h.update(v.tobytes())
+    out["kv_prefill"] = h.hexdigest()
+    out["start_tokens"] = [int(t) for t in synth.start_tokens(cfg, n_seq)]
+    return out
 
 
 class Runner:
@@ -281,7 +317,13 @@ def dominant(kstats):
     return max((k for k in kstats if k not in ("copy", "embed")), key=lambda k: kstats[k][1])
 
 
-def base_line(metric, tps, ms_per_step, steps, warmup, step_bytes, config, dtype="f32"):
+# The arithmetic of the GEMVs: int8 (or 4-bit) weights times the activations'
+# 24-bit fixed-point digits in exact int32 block sums, the two block scales
+# and the sums combined in fp32; attention, norms and softmax in fp32.
+DTYPE = "int8 weights x int24 activation digits -> int32 block sums, fp32 accumulation"
+
+
+def base_line(metric, tps, ms_per_step, steps, warmup, step_bytes, config, dtype=DTYPE):
     gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
     return {"metric": metric, "value": round(tps, 2), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
             "warmup": warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
@@ -316,26 +358,29 @@ def alternatives(r, args) -> dict:
     return res
 
 
-def speculative(model, rounds: int = 12) -> dict:
+def speculative(model, rounds: int = 12, k: int = 3) -> dict:
     """Self-speculative rounds on sequence 0 of the same model opened for four
     sequences: k = 3 drafts through the bottom 8 of 32 layers, verified by one
     pass of all layers over 4 columns; and drafts by all 32 layers (every draft
-    accepted: the verify pass's own rate).  Host-clocked, each round blocks."""
+    accepted: the verify pass's own rate).  Host-clocked, each round blocks.
+    The model is opened with room for every round: a round advances the
+    position by at most k + 1, and the warm-up round comes on top."""
     import synth
     import token_decode_llama_amd as lm
     cfg = model.cfg
-    g = lm.open_model(model, lambda s, l: synth.make_kv(cfg, s, l), max_seqs=4, kv_seqs=1)
-    res = {"k": 3}
+    max_ctx = cfg.ctx + (rounds + 1) * (k + 1)
+    g = lm.open_model(model, lambda s, l: synth.make_kv(cfg, s, l), max_seqs=4, kv_seqs=1, max_ctx=max_ctx)
+    res = {"k": k, "max_ctx": max_ctx}
     try:
         for label, d in (("draft_8_of_32", 8), ("draft_all_32", cfg.n_layers)):
             g.set_position(0, cfg.ctx)
             t = int(synth.start_tokens(cfg, 1)[0])
-            acc = g.speculative_step(t, d, 3)         # warm-up round
+            acc = g.speculative_step(t, d, k)         # warm-up round
             g.set_position(0, cfg.ctx)
             n_tok = 0
             t0 = time.perf_counter()
             for _ in range(rounds):
-                acc = g.speculative_step(t, d, 3)
+                acc = g.speculative_step(t, d, k)
                 n_tok += len(acc)
                 t = int(acc[-1])
             dt = time.perf_counter() - t0
@@ -408,14 +453,20 @@ def run_single(args, name: str, n_seq: int):
         out["step_ms_percentiles"] = r.step_percentiles(min(args.steps, 32))
         r.rewind()
     out["kernels"] = kernel_table(kstats, kbytes, L)
-    if n_seq == 1 and one_launch and not args.only_kernels and not args.no_alternatives:
-        out["alternatives_ms_per_step"] = alternatives(r, args)
+    out["inputs_sha256"] = input_digests(model, n_seq)
+    # The headline fields are complete here.  The CPU baseline and the opt-in
+    # side legs below only add fields: a failure in one of them becomes an
+    # "error" entry of its own and never discards the headline.
+    extras = n_seq == 1 and one_launch and not args.only_kernels and args.extras
+    if extras:
+        out["alternatives_ms_per_step"] = side_leg("alternatives", lambda: alternatives(r, args))
     r.close()
-    if n_seq == 1 and one_launch and not args.only_kernels and not args.no_alternatives:
-        out["speculative"] = speculative(model)
+    if extras:
+        out["speculative"] = side_leg("speculative", lambda: speculative(model))
     if not args.no_cpu_baseline and not args.only_kernels:
         log("oracle baseline")
-        out["cpu_baseline"] = public(cpu_baseline(model, cfg, n_seq, args.cpu_budget))
+        out["cpu_baseline"] = side_leg("cpu_baseline",
+                                       lambda: public(cpu_baseline(model, cfg, n_seq, args.cpu_budget)))
     return out
 
 
@@ -626,8 +677,9 @@ def main():
     ap.add_argument("--stream-steps", type=int, default=16, help="timed steps in layer-streaming mode (70B)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-alternatives", action="store_true",
-                    help="skip timing the opt-in one-launch and persistent step paths")
+    ap.add_argument("--extras", action="store_true",
+                    help="also time the opt-in one-launch / persistent step paths and self-speculative "
+                         "rounds (batch-1 Q8_0/Q4_0 workloads)")
     ap.add_argument("--only-kernels", action="store_true",
                     help="skip the timed loop: run the per-kernel timing steps only (for profilers)")
     ap.add_argument("--calibrate", action="store_true",
