@@ -29,7 +29,7 @@ Every line carries:
   roofline        the dominant kernel: algorithmic bytes per launch / average
                   launch duration from HIP events on the model's stream
   cpu_baseline    the fp64 oracle on this host's cores, on a bounded sample
-Side legs (--extras: the opt-in step paths, self-speculative rounds) only add
+Side legs (--extras: self-speculative rounds) only add
 fields; a failure in one becomes an "error" entry and never drops the line.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -76,8 +76,6 @@ KERNEL_NAMES = {
     "gateup": "k_gemv<gate/up, RMSNorm prologue, SwiGLU epilogue>",
     "down": "k_gemv<down, residual epilogue>",
     "lmhead": "k_gemv<LM head, RMSNorm prologue, argmax epilogue>",
-    "step": "k_step (persistent one-kernel decode step: LDS weight ring + operator chain)",
-    "flow": "k_flow (dataflow launch of all layers: QKV, attention, Wo, gate/up, down workgroups in dependency order)",
 }
 
 
@@ -87,8 +85,7 @@ def log(*a):
 
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("lm_kernels.hip", "lm_internal.h", "lm_step.hip", "lm_step.h", "lm_device.h", "lm_flow.hip",
-              "lm_flow.h"):
+    for f in ("lm_kernels.hip", "lm_internal.h", "lm_device.h"):
         with open(os.path.join(ROOT, "token_decode_llama_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -272,7 +269,7 @@ class Runner:
         import token_decode_llama_amd as lm
         for s in range(self.n_seq):
             self.g.set_position(s, self.cfg.ctx + at_step)
-        b = sum(self.g.kernel_bytes(k, self.n_seq) for k in lm.KERNEL_KINDS if k not in ("copy", "step", "flow"))
+        b = sum(self.g.kernel_bytes(k, self.n_seq) for k in lm.KERNEL_KINDS if k != "copy")
         self.rewind()
         return b
 
@@ -281,7 +278,7 @@ class Runner:
 
 
 def per_launch(kind: str, n_layers: int) -> int:
-    return 1 if kind in ("embed", "lmhead", "step", "flow") else n_layers
+    return 1 if kind in ("embed", "lmhead") else n_layers
 
 
 def kernel_table(kstats, kbytes, n_layers):
@@ -333,31 +330,6 @@ def base_line(metric, tps, ms_per_step, steps, warmup, step_bytes, config, dtype
 
 
 # ---------------------------------------------------------------------------
-def alternatives(r, args) -> dict:
-    """The same workload through the library's other one-sequence step paths
-    (opt-in; the headline uses the default per-operator kernels), timed the
-    same way, for comparison."""
-    import token_decode_llama_amd as lm
-    res = {}
-    for label, on, off in (("one_launch_dataflow", lambda: r.g.set_dataflow(1), lambda: r.g.set_dataflow(0)),
-                           ("one_launch_resident", lambda: r.g.set_dataflow(2), lambda: r.g.set_dataflow(0)),
-                           ("persistent_step", lambda: r.g.set_persistent(True), lambda: r.g.set_persistent(False))):
-        try:
-            on()
-        except lm.LMError as e:
-            res[label] = None
-            log(f"{label}: not available ({e})")
-            continue
-        r.rewind()
-        r.warm(args.warmup)
-        res[label] = round(r.timed(min(args.steps, 32)), 4)
-        r.g.check_error()
-        off()
-        r.rewind()
-        log(f"{label}: {res[label]:.4f} ms/step")
-    return res
-
-
 def speculative(model, rounds: int = 12, k: int = 3) -> dict:
     """Self-speculative rounds on sequence 0 of the same model opened for four
     sequences: k = 3 drafts through the bottom 8 of 32 layers, verified by one
@@ -429,7 +401,7 @@ def run_single(args, name: str, n_seq: int):
         r.g.debug_dequant(0, 6, 0, 64, cfg.ffn)
         log(f"calibration: read {1 << 30} bytes; dequant wrote {64 * cfg.ffn * 4} bytes")
     qt = synth.QTYPE_NAMES[cfg.qtype]
-    one_launch = cfg.qtype in (synth.Q8_0, synth.Q4_0)      # the opt-in step paths and batched verify
+    spec_ok = cfg.qtype in (synth.Q8_0, synth.Q4_0)      # the verify pass runs on the several-sequence path
     config = {"workload": WORKLOAD_TEXT[name], "name": name, "batch": n_seq, "ctx": base.ctx, "qtype": qt,
               "weights": "random N(0,0.02), quantized, resident in HBM"}
     metric = HEADLINE_METRIC if name == "llama8b_q8" else \
@@ -457,9 +429,7 @@ def run_single(args, name: str, n_seq: int):
     # The headline fields are complete here.  The CPU baseline and the opt-in
     # side legs below only add fields: a failure in one of them becomes an
     # "error" entry of its own and never discards the headline.
-    extras = n_seq == 1 and one_launch and not args.only_kernels and args.extras
-    if extras:
-        out["alternatives_ms_per_step"] = side_leg("alternatives", lambda: alternatives(r, args))
+    extras = n_seq == 1 and spec_ok and not args.only_kernels and args.extras
     r.close()
     if extras:
         out["speculative"] = side_leg("speculative", lambda: speculative(model))
@@ -482,9 +452,6 @@ def run_multi(args):
         log(f"generating {c.name} ({c.weight_bytes() / 1e9:.2f} GB)")
         models.append(synth.make_model(c))
         runners.append(Runner(models[-1], 1))
-        # the models' steps overlap on the GPU: per-operator kernels (the
-        # persistent step needs every CU for itself)
-        runners[-1].g.set_persistent(False)
     for r in runners:
         r.warm(args.warmup)
     # each model alone
@@ -678,8 +645,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extras", action="store_true",
-                    help="also time the opt-in one-launch / persistent step paths and self-speculative "
-                         "rounds (batch-1 Q8_0/Q4_0 workloads)")
+                    help="also time self-speculative rounds (batch-1 Q8_0/Q4_0 workloads)")
     ap.add_argument("--only-kernels", action="store_true",
                     help="skip the timed loop: run the per-kernel timing steps only (for profilers)")
     ap.add_argument("--calibrate", action="store_true",

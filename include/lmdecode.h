@@ -76,11 +76,12 @@ typedef enum {
  *       d; w = d * scale * (q - 32), q = 6 bits.
  * The K formats need every matrix input width (hidden, ffn, n_heads *
  * head_dim) to be a multiple of 256 and decode one sequence per step
- * (max_seqs = 1); the one-launch step modes are not built for them. */
+ * (max_seqs = 1). */
 typedef enum { LM_Q4_0 = 2, LM_Q8_0 = 8, LM_Q4_K = 12, LM_Q5_K = 13, LM_Q6_K = 14 } lm_qtype;
 
 typedef struct {
-    int32_t vocab;       /* rows of the LM head, rows of the embedding table */
+    int32_t vocab;       /* rows of the LM head, rows of the embedding table; even and >= 2
+                            (the GEMV finishes its rows in adjacent pairs) */
     int32_t hidden;      /* H, a multiple of 32 */
     int32_t n_layers;
     int32_t n_heads;     /* query heads nq */
@@ -112,7 +113,11 @@ typedef struct {
 } lm_layer_weights;
 
 /* Validates cfg, then allocates every device buffer the model needs (KV
- * cache for max_seqs x max_ctx, weights, scratch).  hip_stream: a hipStream_t
+ * cache for max_seqs x max_ctx, weights, scratch).  The KV cache holds
+ * n_layers x n_kv_heads x max_ctx x head_dim x 2 (K and V) fp16 values per
+ * sequence, the size the SwarmKV page ("Prefill once, fan out", section 3)
+ * gives; the model shapes are the Llama features of the C/CUDA Llama engine
+ * page (section 1: RoPE, GQA, SwiGLU, RMSNorm).  hip_stream: a hipStream_t
  * the model launches on (borrowed, never destroyed), or NULL for a stream the
  * library creates.  On failure *out is NULL and nothing is left allocated.
  * Errors: LM_E_ARG (bad config, with the offending field), LM_E_OOM, LM_E_HIP. */
@@ -122,8 +127,10 @@ lm_status lm_model_create(const lm_config* cfg, void* hip_stream, lm_model** out
 void lm_model_destroy(lm_model* m);
 
 /* Copies one layer's weights (host memory) into the model, repacking the
- * blocks into the library's device layout.  Byte counts follow from the
- * config.  Errors: LM_E_ARG (layer out of range, NULL pointer), LM_E_HIP. */
+ * blocks into the library's device layout.  The blocks are GGUF's (the C/CUDA
+ * Llama engine page, section 1, reads GGUF files in these formats); byte
+ * counts follow from the config.  Errors: LM_E_ARG (layer out of range, NULL
+ * pointer), LM_E_OOM, LM_E_HIP. */
 lm_status lm_load_layer_weights(lm_model* m, int32_t layer, const lm_layer_weights* w);
 
 /* Embedding table fp16 bits [vocab][hidden], output norm gain fp32 [hidden],
@@ -172,8 +179,7 @@ lm_status lm_set_residency(lm_model* m, int32_t n_resident);
  * layer whose output is close to its input is skipped; section 3.5 calibrates
  * which).  mask: host uint8 [n_layers], nonzero = skip the layer; NULL clears
  * the mask.  A skipped layer computes nothing and writes no KV-cache row: its
- * input is its output.  In streaming mode skipped layers are not copied.  The
- * one-launch and persistent step paths are not used while layers are skipped.
+ * input is its output.  In streaming mode skipped layers are not copied.
  * Changing the mask mid-sequence leaves the skipped steps' cache rows of
  * those layers unwritten.  Legal only between steps.  Errors: LM_E_HIP. */
 lm_status lm_set_layer_skip(lm_model* m, const uint8_t* mask);
@@ -236,7 +242,12 @@ lm_status lm_tier_sizes(int32_t n_layers, int64_t layer_bytes, int64_t hbm_bytes
  * in host memory; *n_resident is still set), LM_E_HIP. */
 lm_status lm_plan_residency(lm_model* m, int64_t hbm_bytes, int64_t host_bytes, int32_t* n_resident);
 
-/* One decode step for sequences 0..n_seq-1 (1 <= n_seq <= max_seqs):
+/* One decode step for sequences 0..n_seq-1 (1 <= n_seq <= max_seqs): the
+ * operator chain at the top of this file, i.e. the C/CUDA Llama engine page's
+ * section 4.4 operators (single-token GEMV, fused RMSNorm, RoPE from a
+ * precomputed table, causal-masked softmax attention, SwiGLU fused with the FC
+ * product) over the model of its section 1, each sequence at its own position
+ * (positions continue after the cached prefix: the SwarmKV page, section 4).
  * tokens host int32 [n_seq]; logits host fp32 [n_seq][vocab] or NULL;
  * argmax host int32 [n_seq].  Blocks until the results are on the host.
  * Every sequence advances by one position.
@@ -257,47 +268,6 @@ lm_status lm_decode_step_dev(lm_model* m, const int32_t* d_tokens, int32_t n_seq
 /* 1 (default): replay each step from a captured HIP graph; 0: launch eagerly. */
 lm_status lm_set_graph(lm_model* m, int32_t enable);
 
-/* One-sequence steps as one persistent kernel (available on models created
- * with max_seqs = 1 whose widest GEMV input fits the kernel's LDS plan;
- * weights resident, not in streaming mode; off by default).  One workgroup per CU
- * streams that CU's share of every weight matrix through an LDS ring while
- * its other wavefronts follow the step's operator chain (the C/CUDA Llama
- * engine page, section 4.4: GEMV, RMSNorm, RoPE + KV append, causal softmax
- * attention, SwiGLU, LM head, argmax), with grid-wide barriers between
- * operators.  It keeps a tile-major copy of the weights in HBM (made at load).
- * The kernel needs every CU: steps of two models must not overlap on one GPU
- * while it is on (a wait that times out fails the step with LM_E_HIP when the
- * step is synchronous).  enable = 0 selects the per-operator kernels; enable =
- * 1 on a model without the kernel returns LM_E_STATE.  Results agree with the
- * per-operator kernels within the same logit bound (different summation
- * order), not bit for bit. */
-lm_status lm_set_persistent(lm_model* m, int32_t enable);
-
-/* One-sequence steps with every layer in one launch (mode 1 or 2; off by
- * default; available for Q8_0/Q4_0, head_dim 128, at most 8 query heads per KV
- * head, hidden and FFN widths >= 2048; weights resident, not in streaming mode).
- * The same operators as the per-operator kernels (the C/CUDA Llama engine
- * page, section 4.4), computed the same way: the launch's workgroups are the
- * operators' workgroups in dependency order, and each waits for the operator
- * before it through a device counter instead of a kernel boundary, after
- * requesting the weights it multiplies.  The embedding and the LM head stay
- * separate launches.  A wait that times out (seconds) fails the step with
- * LM_E_HIP (lm_decode_step; lm_check_error after lm_decode_step_dev).
- * Mode 1 (dataflow): one workgroup per (operator, share); workgroups are
- * dispatched in index order, so the chain always progresses, also beside
- * other work on the GPU.  Mode 2 (resident): two workgroups per CU take their
- * share of every operator in turn; it needs every CU (steps of two models
- * must not overlap on one GPU).  enable = 0 selects the per-operator kernels;
- * enable = 1 or 2 on a model without it returns LM_E_STATE.
- * lm_set_persistent(m, 1) takes precedence.  Measured on the 8B shape it is
- * slower than the per-operator kernels: a device-wide count across XCDs costs
- * more than a kernel boundary. */
-lm_status lm_set_dataflow(lm_model* m, int32_t enable);
-
-/* Waits for the model's stream, then reports (LM_E_HIP) and clears a timed-out
- * wait of the dataflow or persistent step since the last check. */
-lm_status lm_check_error(lm_model* m);
-
 /* The hipStream_t the model launches on. */
 void* lm_stream(const lm_model* m);
 
@@ -310,13 +280,10 @@ const char* lm_last_error(const lm_model* m);
 /* Kernel families of one step (for timing and profiling).  LM_K_COPY is the
  * host-to-HBM copy of one layer blob on the copy stream in streaming mode
  * (its durations are those copies' events; its bytes are the blobs copied per
- * step, zero when the weights are resident).  LM_K_STEP is the persistent
- * one-kernel step (lm_set_persistent); its bytes are those of the whole step.
- * LM_K_FLOW is the dataflow launch of all layers (lm_set_dataflow); its bytes
- * are those of the QKV .. down kinds together. */
+ * step, zero when the weights are resident). */
 typedef enum {
     LM_K_EMBED = 0, LM_K_QKV = 1, LM_K_ATTN = 2, LM_K_WO = 3, LM_K_GATEUP = 4,
-    LM_K_DOWN = 5, LM_K_LMHEAD = 6, LM_K_COPY = 7, LM_K_STEP = 8, LM_K_FLOW = 9, LM_K_COUNT = 10
+    LM_K_DOWN = 5, LM_K_LMHEAD = 6, LM_K_COPY = 7, LM_K_COUNT = 8
 } lm_kernel_kind;
 
 /* enable = 1: eager steps record HIP events around every kernel of every
@@ -355,28 +322,26 @@ lm_status lm_kernel_bytes(const lm_model* m, int32_t kind, int32_t n_seq, double
 lm_status lm_debug_dequant(lm_model* m, int32_t layer, int32_t which, int32_t row0,
                            int32_t n_rows, float* out);
 
-/* One persistent step (as lm_decode_step_dev with d_argmax internal, no
- * logits) that records timestamps of the 100 MHz constant clock into
- * out[cu][phase][8] (host, capacity in uint64 words): [0] the phase starts
- * (after the barrier), [1] the input vector is staged, [2] the first consumer
- * wavefront has finished its tiles, [3] every consumer has finished (barrier
- * arrival), [4] the first producer wavefront stores the phase's first tile;
- * unused words are 0.  Phases: 5 per layer (QKV, attention, Wo, gate/up,
- * down), then the LM head.  *n_cus and *n_phases give the extents.  Advances
- * the position like a step.  For profiling the persistent kernel. */
-lm_status lm_debug_step_trace(lm_model* m, const int32_t* d_tokens, uint64_t* out, int64_t capacity,
-                              int32_t* n_cus, int32_t* n_phases);
+/* The step's dequant-GEMV kernel on a given input: y = W x with no RMSNorm
+ * gain and no epilogue (W from a resident layer, or the LM head).  which: 0
+ * the QKV matrix (rows: the nq*hd query rows, then nkv*hd key rows, then
+ * nkv*hd value rows; input hidden), 1 Wo (input nq*hd), 2 gate/up (row 2i =
+ * gate row i, row 2i+1 = up row i; input hidden), 3 down (input ffn), 4 the LM
+ * head (layer ignored).  x: host fp32 [n_seq][K]; y: host fp32 [n_seq][N].
+ * n_seq = 1 runs the one-sequence kernel, 2..max_seqs the matrix-core path.
+ * It allocates and frees a device buffer of its own.  For checking the
+ * products against a reference.  Errors: LM_E_ARG, LM_E_STATE (the layer is
+ * streamed), LM_E_HIP. */
+lm_status lm_debug_gemv(lm_model* m, int32_t layer, int32_t which, int32_t n_seq, const float* x,
+                        float* y);
 
-/* The embedding and the dataflow launch of one step (lm_set_dataflow; no LM
- * head, the position is not advanced; the K/V row of the current position is
- * written as a step writes it), recording per workgroup into
- * out[wg][4] (host, capacity in uint64 words): [0] start, [1] its wait passed
- * (0 for workgroups that do not wait), [2] its work is done (100 MHz constant
- * clock), [3] hardware ids (HW_ID in the high half, XCC_ID in the low half).
- * Workgroups are layer-major, phases QKV, attention, Wo, gate/up, down with
- * wg_per_phase[5] workgroups each; *n_wg gives the total.  For profiling. */
-lm_status lm_debug_flow_trace(lm_model* m, const int32_t* d_tokens, uint64_t* out, int64_t capacity,
-                              int32_t* n_wg, int32_t* wg_per_phase);
+/* Fault injection for the all-or-nothing contract: the n-th device or
+ * pinned-host allocation the library makes from now on (in any model of the
+ * process) fails as if memory were exhausted (LM_E_OOM); n <= 0 disarms it.
+ * lm_debug_alloc_count: the number of allocations the library has attempted
+ * in this process. */
+void lm_debug_fail_alloc(int64_t n);
+int64_t lm_debug_alloc_count(void);
 
 /* A plain read-only kernel over n_bytes of device memory (sum of 16-byte
  * words), for calibrating HBM counters and the read ceiling; *ms = average

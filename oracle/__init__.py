@@ -18,6 +18,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# another build of the same source (the sanitizer test loads one)
+LOAD_PATH = os.environ.get("LM_ORACLE_LIB") or LIB_PATH
 
 Q4_0 = 2
 Q8_0 = 8
@@ -57,9 +59,9 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
-        L = ctypes.CDLL(LIB_PATH)
+        if not os.path.exists(LOAD_PATH):
+            raise RuntimeError(f"{LOAD_PATH} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(LOAD_PATH)
         vp, i64, i32, f64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
         sig = {
             "orc_f16_to_f64": ([ctypes.c_uint16], f64),

@@ -330,7 +330,6 @@ void orc_attention(const double* q, const uint16_t* K, const uint16_t* V, int nq
     }
 }
 
-/* First index of the largest value after rounding each to fp32. */
 /* Cosine similarity a.b / (|a| |b|) in fp64; 0 when either vector is zero. */
 double orc_cosine(const double* a, const double* b, int64_t n) {
     double ab = 0.0, aa = 0.0, bb = 0.0;
@@ -343,6 +342,8 @@ double orc_cosine(const double* a, const double* b, int64_t n) {
     return ab / (sqrt(aa) * sqrt(bb));
 }
 
+/* First index of the largest value after rounding each to fp32 (ties: the
+ * lowest index, as the decode step's argmax takes them). */
 int32_t orc_argmax_f32(const double* v, int64_t n) {
     int32_t best = 0;
     float bv = (float)v[0];

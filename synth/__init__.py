@@ -33,6 +33,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsynth.so")
+# another build of the same source (the sanitizer test loads one)
+LOAD_PATH = os.environ.get("LM_SYNTH_LIB") or LIB_PATH
 
 Q4_0 = 2
 Q8_0 = 8
@@ -68,9 +70,9 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
-        L = ctypes.CDLL(LIB_PATH)
+        if not os.path.exists(LOAD_PATH):
+            raise RuntimeError(f"{LOAD_PATH} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(LOAD_PATH)
         u64, i64, f64, i32, u32 = (ctypes.c_uint64, ctypes.c_int64, ctypes.c_double,
                                    ctypes.c_int32, ctypes.c_uint32)
         vp = ctypes.c_void_p

@@ -85,14 +85,12 @@ def test_batch_matches_single_sequence(name, qtype):
 
 def test_batched_model_single_sequence_bit_identical():
     """A model created for four sequences, stepped with one, runs the
-    one-sequence per-operator kernels on the same data: identical to a
-    one-sequence model with the persistent step switched off."""
+    one-sequence kernels on the same data: identical to a one-sequence model."""
     cfg = synth.variant("tiny", batch=1)
     model = synth.make_model(cfg)
     toks = synth.start_tokens(cfg, 1)
     g1 = open_gpu(model, max_seqs=1)
     g4 = open_gpu(model, max_seqs=4, kv_seqs=1)
-    g1.set_persistent(False)      # the per-operator kernels, as a 4-sequence model uses
     try:
         a = _steps(g1, toks, cfg.steps)
         b = _steps(g4, toks, cfg.steps)

@@ -107,17 +107,14 @@ def test_kquant_streaming_and_hybrid_bit_identical(name):
         g.close()
 
 
-def test_kquant_one_launch_modes_rejected():
-    """The one-launch step modes and the speculative verify pass are built for
-    Q8_0 / Q4_0 only: asking for them on a K-format model is an error, and the
+def test_kquant_speculative_rejected():
+    """The speculative verify pass runs on the several-sequence path, built for
+    Q8_0 / Q4_0 only: asking for it on a K-format model is an error, and the
     model keeps decoding."""
     import token_decode_llama_amd as lm
     model = get_model("tiny_q4k")
     g = open_gpu(model, max_seqs=1)
     try:
-        for fn in (lambda: g.set_persistent(True), lambda: g.set_dataflow(1)):
-            with pytest.raises(lm.LMError):
-                fn()
         with pytest.raises(lm.LMError) as e:           # the verify pass needs the several-sequence path
             g.speculative_step(1, 1, 1)
         assert e.value.status == lm.LM_E_STATE

@@ -20,12 +20,8 @@ def _cfgs():
 
 def _open(model, stream):
     import token_decode_llama_amd as lm
-    g = lm.open_model(model, lambda s, l: synth.make_kv(model.cfg, s, l), max_seqs=1, kv_seqs=1,
-                      stream=stream)
-    # steps of several models overlap on the GPU: the per-operator kernels
-    # (the persistent step needs every CU for itself)
-    g.set_persistent(False)
-    return g
+    return lm.open_model(model, lambda s, l: synth.make_kv(model.cfg, s, l), max_seqs=1, kv_seqs=1,
+                         stream=stream)
 
 
 def test_round_robin_on_streams_bit_identical_to_solo():

@@ -42,9 +42,6 @@ CASES = {
     "tiny_ctx0": synth.variant("tiny", ctx=0, steps=3),
 }
 
-# shapes the one-launch step supports (head_dim 128, hidden and FFN >= 2048)
-FLOW_CASES = ["llama8b_q8_2layers_ctx127", "llama8b_q4_2layers_ctx4k", "llama70b_q4_2layers"]
-
 _models = {}
 
 
@@ -55,23 +52,13 @@ def get_model(name):
     return _models[name]
 
 
-def set_mode(g, mode):
-    """default | ops (per-operator kernels) | flow (dataflow step) | persistent"""
-    if mode == "persistent":
-        g.set_persistent(True)
-    elif mode == "ops":
-        g.set_dataflow(False)
-    elif mode == "flow":
-        g.set_dataflow(1)
-    elif mode == "resident":
-        g.set_dataflow(2)
-
-
-def run_parity(model, n_seq, steps=None, mode="default"):
+def run_parity(model, n_seq, steps=None, setup=None):
+    """setup(g): puts the GPU model in the mode under test (residency) first."""
     cfg = model.cfg
     steps = steps or cfg.steps
     g = open_gpu(model, max_seqs=n_seq)
-    set_mode(g, mode)
+    if setup:
+        setup(g)
     om = open_oracle(model, n_seq)
     toks = synth.start_tokens(cfg, n_seq)
     worst = 0.0
@@ -106,29 +93,14 @@ def test_decode_parity(name):
     run_parity(get_model(name), n_seq=1)
 
 
-@pytest.mark.parametrize("name", list(CASES))
-def test_decode_parity_persistent(name):
-    """The same steps through the persistent one-kernel step."""
-    run_parity(get_model(name), n_seq=1, mode="persistent")
-
-
-@pytest.mark.parametrize("name", FLOW_CASES)
-def test_decode_parity_flow(name):
-    """The dataflow step (all layers in one launch) against the oracle."""
-    run_parity(get_model(name), n_seq=1, mode="flow")
-
-
-@pytest.mark.parametrize("name", FLOW_CASES)
-def test_decode_parity_resident(name):
-    """The resident variant of the one-launch step (two workgroups per CU
-    through every operator) against the oracle."""
-    run_parity(get_model(name), n_seq=1, mode="resident")
-
-
-@pytest.mark.parametrize("name", FLOW_CASES)
-def test_decode_parity_ops(name):
-    """The per-operator kernels, selected explicitly, on the one-launch shapes."""
-    run_parity(get_model(name), n_seq=1, mode="ops")
+@pytest.mark.parametrize("name,k", [("llama70b_q4_2layers", 0), ("llama70b_q4_2layers", 1),
+                                    ("tiny_5layers", 0), ("tiny_5layers", 2)])
+def test_decode_parity_streamed(name, k):
+    """Layers k..L-1 streamed from pinned host memory through the two HBM layer
+    buffers (k = 0: every layer; the engine page's double-buffered streaming and
+    tier split), checked against the oracle itself, not only against resident
+    runs."""
+    run_parity(get_model(name), n_seq=1, setup=lambda g: g.set_residency(k))
 
 
 def _steps(g, cfg, n):
@@ -140,50 +112,6 @@ def _steps(g, cfg, n):
         out.append((lg.copy(), am.copy()))
         t = am
     return out
-
-
-@pytest.mark.parametrize("name", ["llama8b_q8_2layers_ctx127", "llama8b_q4_2layers_ctx4k"])
-@pytest.mark.parametrize("mode", [1, 2])
-def test_flow_equals_ops_bitwise(name, mode):
-    """The one-launch step (dataflow grid or resident workgroups) runs the
-    per-operator arithmetic in the same order (same per-row lane split, digit
-    staging, reductions and merge order), so its logits equal the per-operator
-    kernels' bit for bit."""
-    model = get_model(name)
-    cfg = model.cfg
-    g = open_gpu(model, max_seqs=1)
-    try:
-        g.set_dataflow(0)
-        ops = _steps(g, cfg, cfg.steps)
-        g.set_dataflow(mode)
-        flow = _steps(g, cfg, cfg.steps)
-        for st, ((a, b), (c, d)) in enumerate(zip(ops, flow)):
-            assert np.array_equal(b, d), (st, b, d)
-            assert np.array_equal(a, c), (st, float(np.max(np.abs(a - c))))
-    finally:
-        g.close()
-
-
-@pytest.mark.parametrize("mode", [1, 2])
-def test_flow_graph_and_eager_launches_agree(mode):
-    """Launch counting across graph replays and eager launches: the phase
-    counters grow every launch, so a wrong launch number would either hang a
-    wait (reported as an error) or let a phase start early (different logits)."""
-    model = get_model("llama8b_q8_2layers_ctx127")
-    cfg = model.cfg
-    g = open_gpu(model, max_seqs=1)
-    try:
-        g.set_dataflow(mode)
-        runs = []
-        for mode in (True, False, True, True, False):
-            g.set_graph(mode)
-            runs.append(_steps(g, cfg, 3))
-        g.check_error()
-        for other in runs[1:]:
-            for (a, b), (c, d) in zip(runs[0], other):
-                assert np.array_equal(a, c) and np.array_equal(b, d)
-    finally:
-        g.close()
 
 
 @pytest.mark.parametrize("mode", [1, 2])
@@ -229,18 +157,6 @@ def test_time_kind_graph_replay():
         again = _steps(g, cfg, 2)
         for (a, b), (c, d) in zip(ref, again):
             assert np.array_equal(a, c) and np.array_equal(b, d)
-    finally:
-        g.close()
-
-
-def test_flow_unsupported_shape_is_rejected():
-    import token_decode_llama_amd as lm
-    g = open_gpu(get_model("tiny_q8"), max_seqs=1)
-    try:
-        with pytest.raises(lm.LMError) as e:
-            g.set_dataflow(True)
-        assert e.value.status == lm.LM_E_STATE
-        g.set_dataflow(False)
     finally:
         g.close()
 
@@ -319,9 +235,6 @@ def test_stream_mode_bit_identical(name):
                 t = am
             return res
 
-        # streaming uses the per-operator kernels: compare against the same kernels resident
-        g.set_persistent(False)
-        g.set_dataflow(False)
         resident = run()
         g.stream_mode(True)
         streamed = run()
@@ -356,8 +269,6 @@ def test_hybrid_residency_bit_identical(name, plan):
                 t = am
             return res
 
-        g.set_persistent(False)
-        g.set_dataflow(False)
         resident = run()
         for k in plan:
             log(f"{name}: {k} of {cfg.n_layers} layers resident")
@@ -388,8 +299,6 @@ def test_long_cache_short_context_bit_identical(name):
     for max_ctx in (cfg.max_ctx, 8192):
         g = lm.open_model(model, lambda s, l: synth.make_kv(cfg, s, l), max_seqs=1, max_ctx=max_ctx)
         try:
-            g.set_persistent(False)
-            g.set_dataflow(False)
             res, t = [], toks
             for _ in range(cfg.steps):
                 lg, am = g.step(t)
@@ -460,8 +369,6 @@ def test_layer_skip_streaming_bit_identical(name):
                 t = am
             return res
 
-        g.set_persistent(False)
-        g.set_dataflow(False)
         g.set_layer_skip(mask)
         resident = run()
         for k in (0, 1, cfg.n_layers - 1):

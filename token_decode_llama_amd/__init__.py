@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(HERE, "liblmdecode.so")
 
 LM_OK, LM_E_ARG, LM_E_STATE, LM_E_OOM, LM_E_HIP, LM_E_CTX = range(6)
 LM_Q4_0, LM_Q8_0, LM_Q4_K, LM_Q5_K, LM_Q6_K = 2, 8, 12, 13, 14
-KERNEL_KINDS = ("embed", "qkv", "attn", "wo", "gateup", "down", "lmhead", "copy", "step", "flow")
+KERNEL_KINDS = ("embed", "qkv", "attn", "wo", "gateup", "down", "lmhead", "copy")
 
 # every symbol include/lmdecode.h declares
 EXPORTS = (
@@ -25,10 +25,9 @@ EXPORTS = (
     "lm_load_kv", "lm_get_kv", "lm_set_position", "lm_get_position", "lm_stream_mode",
     "lm_set_residency", "lm_tier_sizes", "lm_plan_residency", "lm_set_layer_skip",
     "lm_layer_similarity", "lm_get_layer_similarity", "lm_skip_similar_layers", "lm_speculative_step",
-    "lm_decode_step", "lm_decode_step_dev", "lm_set_graph", "lm_set_persistent", "lm_set_dataflow",
-    "lm_check_error", "lm_stream", "lm_last_error",
+    "lm_decode_step", "lm_decode_step_dev", "lm_set_graph", "lm_stream", "lm_last_error",
     "lm_kernel_timing", "lm_kernel_stats", "lm_time_kind", "lm_kernel_bytes", "lm_debug_dequant",
-    "lm_debug_read_bw", "lm_debug_step_trace", "lm_debug_flow_trace",
+    "lm_debug_read_bw", "lm_debug_gemv", "lm_debug_fail_alloc", "lm_debug_alloc_count",
 )
 
 
@@ -87,9 +86,6 @@ def load():
         "lm_decode_step": ([vp, vp, i32, vp, vp], st),
         "lm_decode_step_dev": ([vp, vp, i32, vp, vp], st),
         "lm_set_graph": ([vp, i32], st),
-        "lm_set_persistent": ([vp, i32], st),
-        "lm_set_dataflow": ([vp, i32], st),
-        "lm_check_error": ([vp], st),
         "lm_stream": ([vp], vp),
         "lm_last_error": ([vp], ctypes.c_char_p),
         "lm_kernel_timing": ([vp, i32], st),
@@ -98,8 +94,9 @@ def load():
         "lm_time_kind": ([vp, i32, i32, i32, ctypes.POINTER(dbl)], st),
         "lm_debug_dequant": ([vp, i32, i32, i32, i32, vp], st),
         "lm_debug_read_bw": ([vp, i64, i32, ctypes.POINTER(dbl)], st),
-        "lm_debug_step_trace": ([vp, vp, vp, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)], st),
-        "lm_debug_flow_trace": ([vp, vp, vp, i64, ctypes.POINTER(i32), vp], st),
+        "lm_debug_gemv": ([vp, i32, i32, i32, vp, vp], st),
+        "lm_debug_fail_alloc": ([i64], None),
+        "lm_debug_alloc_count": ([], i64),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -278,16 +275,6 @@ class Model:
     def set_graph(self, enable: bool):
         self._check(self._lib.lm_set_graph(self._h, 1 if enable else 0))
 
-    def set_persistent(self, enable: bool):
-        self._check(self._lib.lm_set_persistent(self._h, 1 if enable else 0))
-
-    def set_dataflow(self, mode):
-        """False/0: per-operator kernels; True/1: dataflow grid; 2: resident workgroups."""
-        self._check(self._lib.lm_set_dataflow(self._h, int(mode)))
-
-    def check_error(self):
-        self._check(self._lib.lm_check_error(self._h))
-
     # -- measurement ---------------------------------------------------------
     def kernel_timing(self, mode):
         """0/False off; 1/True eager steps with events; 2 events inside the replayed graph."""
@@ -316,29 +303,31 @@ class Model:
         self._check(self._lib.lm_debug_dequant(self._h, layer, which, row0, n_rows, _p(out)))
         return out
 
-    def debug_step_trace(self, d_tokens) -> np.ndarray:
-        """Timestamps (100 MHz ticks) of one traced persistent step: [cu][phase][8]."""
-        ncu, nph = ctypes.c_int32(), ctypes.c_int32()
-        cap = 1024 * (5 * self.cfg.n_layers + 1) * 8
-        out = np.zeros(cap, np.uint64)
-        ptr = d_tokens if isinstance(d_tokens, int) else d_tokens.data_ptr()
-        self._check(self._lib.lm_debug_step_trace(self._h, ptr, _p(out), cap, ctypes.byref(ncu),
-                                                  ctypes.byref(nph)))
-        return out[:ncu.value * nph.value * 8].reshape(ncu.value, nph.value, 8)
-
-    def debug_flow_trace(self, d_tokens, max_wg: int = 1 << 20):
-        """One traced dataflow launch: ([wg][4] uint64 trace, workgroups per phase)."""
-        n = ctypes.c_int32()
-        per = np.zeros(5, np.int32)
-        out = np.zeros(max_wg * 4, np.uint64)
-        ptr = d_tokens if isinstance(d_tokens, int) else d_tokens.data_ptr()
-        self._check(self._lib.lm_debug_flow_trace(self._h, ptr, _p(out), out.size, ctypes.byref(n), _p(per)))
-        return out[:n.value * 4].reshape(n.value, 4), per
+    def debug_gemv(self, layer: int, which: int, x: np.ndarray) -> np.ndarray:
+        """y = W x through the step's GEMV kernel (which: 0 QKV, 1 Wo, 2 gate/up
+        interleaved, 3 down, 4 LM head); x fp32 [n_seq, K] -> y fp32 [n_seq, N]."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        if x.ndim == 1:
+            x = x[None]
+        n = {0: self.cfg.n_heads * self.cfg.head_dim + 2 * self.cfg.n_kv_heads * self.cfg.head_dim,
+             1: self.cfg.hidden, 2: 2 * self.cfg.ffn, 3: self.cfg.hidden, 4: self.cfg.vocab}[which]
+        y = np.empty((x.shape[0], n), np.float32)
+        self._check(self._lib.lm_debug_gemv(self._h, layer, which, x.shape[0], _p(x), _p(y)))
+        return y
 
     def debug_read_bw(self, n_bytes: int, iters: int = 10) -> float:
         ms = ctypes.c_double()
         self._check(self._lib.lm_debug_read_bw(self._h, n_bytes, iters, ctypes.byref(ms)))
         return ms.value
+
+
+def fail_alloc(n: int):
+    """The n-th library allocation from now on fails (LM_E_OOM); 0 disarms."""
+    load().lm_debug_fail_alloc(int(n))
+
+
+def alloc_count() -> int:
+    return int(load().lm_debug_alloc_count())
 
 
 def open_model(model, kv_fn, max_seqs: int | None = None, kv_seqs: int | None = None,

@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "liblmdecode.so")
 
-SOURCES = ["lm_kernels.hip", "lm_step.hip", "lm_flow.hip", "lm_runtime.cpp"]
+SOURCES = ["lm_kernels.hip", "lm_runtime.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -266,14 +266,18 @@ __device__ __forceinline__ void stage_digits(float4 v, int i, int K, int8_t* xq,
 // line: chunks count into their group's line, the chunk completing a group
 // counts into line 0.  Whoever completes a count resets it for the next launch.
 // One thread calls it, after its workgroup's partial stores have completed.
+// The counts are release/acquire at device scope: each arrival releases its
+// workgroup's partial states, and the caller that completes the count
+// acquires every earlier arrival's (through the first-level count and then
+// the second), so the merge that follows reads them all.
 __device__ __forceinline__ bool chunk_arrive(int* cnt, int chunk, int n_act) {
     const int grp = chunk / kCntGroup, n_grp = (n_act + kCntGroup - 1) / kCntGroup;
     const int in_grp = min(kCntGroup, n_act - grp * kCntGroup);
     int* c1 = cnt + (1 + grp) * kCntStride;
-    if (__hip_atomic_fetch_add(c1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != in_grp - 1) return false;
+    if (__hip_atomic_fetch_add(c1, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) != in_grp - 1) return false;
     __hip_atomic_store(c1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (n_grp == 1) return true;
-    if (__hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != n_grp - 1) return false;
+    if (__hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) != n_grp - 1) return false;
     __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return true;
 }

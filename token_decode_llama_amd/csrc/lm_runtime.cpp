@@ -15,8 +15,6 @@
 // layer's compute waits for its copy, and the copy that overwrites a buffer
 // waits for the compute that last read it.
 #include "lm_internal.h"
-#include "lm_step.h"
-#include "lm_flow.h"
 
 #include "../../include/lmdecode.h"
 
@@ -38,6 +36,7 @@ namespace {
 
 thread_local std::string g_create_error;
 std::atomic<long> g_alloc_count{0};
+std::atomic<long> g_fail_at{0};
 
 constexpr int64_t kAlign = 256;
 inline int64_t align_up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -187,26 +186,7 @@ struct lm_model {
     float* d_sink = nullptr;
     float* d_dbg = nullptr;               // debug dequant rows
 
-    // dataflow step (one sequence, weights resident): every layer in one launch
-    bool flow_capable = false;
-    int flow_mode = 0;                    // 0 off (per-operator kernels: measured faster), 1 dataflow
-                                          // grid, 2 resident workgroups (lm_set_dataflow)
-    FlowArgs flow_h{};
-    uint32_t* d_flow_ctl = nullptr;       // [L * 5] phase counts, then epoch, error flag
-
-    // persistent one-kernel step (one sequence, weights resident)
-    bool step_capable = false;            // the step kernel's LDS plan fits this shape
-    bool persistent = false;              // use it for one-sequence steps
     int n_cus = 0;
-    TileGeom tgeo[5]{};                   // QKV, Wo, gate/up, down, LM head
-    int64_t tile_layer_stride = 0;
-    int64_t tile_off[4] = {};
-    uint8_t* d_tiles = nullptr;           // tile-major layer matrices [L][...]
-    uint8_t* d_lm_tiles = nullptr;
-    StepArgs step_h{};
-    StepArgs* d_step_args = nullptr;      // the step kernel's arguments
-    uint32_t* d_bar = nullptr;            // grid-barrier counts
-    uint32_t* d_step_misc = nullptr;      // [0] epoch [1] error [2] argmax count [3] pad [4..] attention counts
     int64_t dbg_floats = 0;
 
     std::vector<uint8_t> layer_loaded;
@@ -291,13 +271,12 @@ static lm_status fail(lm_model* m, lm_status st, const char* fmt, ...) {
                         (int)_e);                                                          \
     } while (0)
 
+// Allocation fault injection (lm_debug_fail_alloc): the allocation whose
+// process-wide number equals g_fail_at fails as if the memory were exhausted.
 static bool fault_alloc_now() {
-    static long at = [] {
-        const char* s = std::getenv("LM_FAULT_ALLOC_AT");
-        return s ? std::atol(s) : 0L;
-    }();
     const long n = ++g_alloc_count;
-    return at > 0 && n == at;
+    long at = g_fail_at.load();
+    return at > 0 && n == at && g_fail_at.compare_exchange_strong(at, 0L);
 }
 
 static lm_status dev_alloc(lm_model* m, void** p, int64_t bytes, const char* what) {
@@ -608,122 +587,6 @@ extern "C" lm_status lm_model_create(const lm_config* cfg, void* hip_stream, lm_
         CREATE_HIP(hipMemcpy(m->d_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice));
         CREATE_HIP(hipMemcpy(m->d_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice));
     }
-    // dataflow step: its phase counters and arguments
-    if (flow_supported(c.qtype, (int)m->H, (int)m->F, (int)m->hd, (int)m->nq, (int)m->nkv) && m->n_cus >= 1) {
-        const int64_t words = flow_ctl_words(c.n_layers);
-        CREATE_TRY(dev_alloc(m, (void**)&m->d_flow_ctl, words * 4, "dataflow step counters"));
-        CREATE_HIP(hipMemsetAsync(m->d_flow_ctl, 0, (size_t)(words * 4), m->stream));
-        FlowArgs& a = m->flow_h;
-        a.L = c.n_layers;
-        a.H = (int)m->H;
-        a.F = (int)m->F;
-        a.nq = (int)m->nq;
-        a.nkv = (int)m->nkv;
-        a.hd = (int)m->hd;
-        a.max_ctx = c.max_ctx;
-        a.max_chunks = m->max_chunks;
-        a.eps = (float)c.rms_eps;
-        a.scale = (float)(1.0 / std::sqrt((double)m->hd));
-        a.blobs = m->d_layers;
-        a.blob_stride = m->blob_bytes;
-        const int which[4] = {M_QKV, M_WO, M_GU, M_DOWN};
-        for (int i = 0; i < 4; ++i) {
-            a.mat[i].q_off = m->mo[which[i]].q;
-            a.mat[i].sc_off = m->mo[which[i]].sc;
-            a.mat[i].N = m->mo[which[i]].N;
-            a.mat[i].K = m->mo[which[i]].K;
-        }
-        a.norms = m->d_norms;
-        a.kcache = m->d_k;
-        a.vcache = m->d_v;
-        a.kv_layer = kv_layer_elems(m);
-        a.pos = m->d_pos;
-        a.rope_cos = m->d_cos;
-        a.rope_sin = m->d_sin;
-        a.x = m->d_x;
-        a.q = m->d_q;
-        a.o = m->d_o;
-        a.h = m->d_h;
-        a.attn_part = m->d_attn_part;
-        a.attn_cnt = m->d_attn_cnt;
-        a.done = m->d_flow_ctl;
-        a.epoch = m->d_flow_ctl + (int64_t)c.n_layers * kFlowOps * (kFlowSub + 1) * kFlowLine;
-        a.err = a.epoch + kFlowLine;
-        a.resident = m->flow_mode == 2;
-        flow_plan(a, c.qtype, m->n_cus);
-        m->flow_capable = true;
-    }
-    // persistent one-kernel step (one sequence): tile-major weight copies,
-    // its argument block in device memory, barrier counts
-    if (S == 1 && !is_kquant(c.qtype)) {
-        const int qt = c.qtype;
-        const int64_t kmax = std::max<int64_t>({m->H, m->F, m->qrows});
-        const int xb = step_xbytes(qt, (int)kmax, (int)m->hd);
-        const int slots = step_ring_slots(xb);
-        if (slots >= 4 && m->n_cus >= 1) {
-            m->tgeo[0] = tile_geom(qt, (int)(m->qrows + 2 * m->kvrows), (int)m->H);
-            m->tgeo[1] = tile_geom(qt, (int)m->H, (int)m->qrows);
-            m->tgeo[2] = tile_geom(qt, (int)(2 * m->F), (int)m->H);
-            m->tgeo[3] = tile_geom(qt, (int)m->H, (int)m->F);
-            m->tgeo[4] = tile_geom(qt, (int)m->V, (int)m->H);
-            int64_t off = 0;
-            for (int i = 0; i < 4; ++i) {
-                m->tile_off[i] = off;
-                off = align_up(off + tile_matrix_bytes(m->tgeo[i]));
-            }
-            m->tile_layer_stride = off;
-            CREATE_TRY(dev_alloc(m, (void**)&m->d_tiles, L * off, "tile-major layer weights"));
-            CREATE_TRY(dev_alloc(m, (void**)&m->d_lm_tiles, tile_matrix_bytes(m->tgeo[4]), "tile-major LM head"));
-            CREATE_TRY(dev_alloc(m, (void**)&m->d_step_args, sizeof(StepArgs), "step arguments"));
-            CREATE_TRY(dev_alloc(m, (void**)&m->d_bar, step_bar_words(c.n_layers) * 4, "step barrier counts"));
-            CREATE_TRY(dev_alloc(m, (void**)&m->d_step_misc, (4 + m->nkv) * 4, "step counters"));
-            CREATE_HIP(hipMemsetAsync(m->d_bar, 0, (size_t)(step_bar_words(c.n_layers) * 4), m->stream));
-            CREATE_HIP(hipMemsetAsync(m->d_step_misc, 0, (size_t)((4 + m->nkv) * 4), m->stream));
-            StepArgs& a = m->step_h;
-            a.L = c.n_layers;
-            a.H = (int)m->H;
-            a.F = (int)m->F;
-            a.V = (int)m->V;
-            a.nq = (int)m->nq;
-            a.nkv = (int)m->nkv;
-            a.hd = (int)m->hd;
-            a.max_ctx = c.max_ctx;
-            a.eps = (float)c.rms_eps;
-            a.scale = (float)(1.0 / std::sqrt((double)m->hd));
-            a.tiles = m->d_tiles;
-            a.layer_stride = m->tile_layer_stride;
-            for (int i = 0; i < 4; ++i) a.mat_off[i] = m->tile_off[i];
-            a.lm_tiles = m->d_lm_tiles;
-            for (int i = 0; i < 5; ++i) a.geo[i] = m->tgeo[i];
-            a.embd = m->d_embd;
-            a.norms = m->d_norms;
-            a.out_norm = m->d_out_norm;
-            a.kcache = m->d_k;
-            a.vcache = m->d_v;
-            a.kv_layer = kv_layer_elems(m);
-            a.rope_cos = m->d_cos;
-            a.rope_sin = m->d_sin;
-            a.pos = m->d_pos;
-            a.x = m->d_x;
-            a.q = m->d_q;
-            a.o = m->d_o;
-            a.h = m->d_h;
-            a.attn_part = m->d_attn_part;
-            a.attn_cnt = m->d_step_misc + 4;
-            a.max_chunks = m->max_chunks;
-            a.part_val = m->d_lm_pval;
-            a.part_idx = m->d_lm_pidx;
-            a.done_cnt = m->d_step_misc + 2;
-            a.bar = m->d_bar;
-            a.epoch = m->d_step_misc + 0;
-            a.err = (int*)(m->d_step_misc + 1);
-            a.ring_slots = slots;
-            a.xbytes = xb;
-            CREATE_HIP(hipMemcpy(m->d_step_args, &a, sizeof a, hipMemcpyHostToDevice));
-            m->step_capable = true;
-            m->persistent = false;        // opt-in (lm_set_persistent) until it beats the per-operator kernels
-        }
-    }
     CREATE_HIP(hipStreamSynchronize(m->stream));
 #undef CREATE_TRY
 #undef CREATE_HIP
@@ -851,48 +714,6 @@ static lm_status upload_frag(lm_model* m, int N, int K, RowFn src_row, uint8_t* 
     return LM_OK;
 }
 
-// Tile-major copy of one matrix for the persistent step (layout: lm_step.h):
-// row groups of 16 (rows past N are zero), each group's column chunks as
-// contiguous tiles: [block][row] quants, then [block][row] scales.
-template <class RowFn>
-static lm_status upload_tiles(lm_model* m, const TileGeom& g, RowFn src_row, uint8_t* dst) {
-    const int qt = m->cfg.qtype, bb = block_bytes(qt);
-    const int NBK = qt == kQ8_0 ? kTileBlocksQ8 : kTileBlocksQ4;
-    const int QBB = qt == kQ8_0 ? 512 : 256;      // quant bytes of one block of 16 rows
-    const int64_t per = std::max<int64_t>(1, m->stage_bytes / g.gbytes);
-    for (int64_t g0 = 0; g0 < g.ng; g0 += per) {
-        const int64_t n = std::min<int64_t>(per, g.ng - g0);
-        uint8_t* stg = m->h_stage;
-        parallel_rows(n, [&](int64_t a, int64_t b) {
-            for (int64_t gi = a; gi < b; ++gi) {
-                uint8_t* gd = stg + gi * g.gbytes;
-                std::memset(gd, 0, (size_t)g.gbytes);
-                for (int ch = 0; ch < g.nch; ++ch) {
-                    const int nbk = ch == g.nch - 1 ? g.nbk_last : NBK;
-                    uint8_t* t = gd + (int64_t)ch * g.tfull;
-                    uint8_t* sc = t + (int64_t)nbk * QBB;
-                    for (int j = 0; j < kTileRows; ++j) {
-                        const int64_t row = (g0 + gi) * kTileRows + j;
-                        if (row >= g.N) continue;
-                        const uint8_t* src = src_row(row);
-                        for (int bk = 0; bk < nbk; ++bk) {
-                            const uint8_t* blk = src + (int64_t)(ch * NBK + bk) * bb;
-                            sc[(bk * kTileRows + j) * 2] = blk[0];
-                            sc[(bk * kTileRows + j) * 2 + 1] = blk[1];
-                            const int qb = qt == kQ8_0 ? 32 : 16;    // quant bytes of one row's block
-                            std::memcpy(t + (int64_t)bk * QBB + j * qb, blk + 2, qb);
-                        }
-                    }
-                }
-            }
-        });
-        HIPTRY(m, hipMemcpyAsync(dst + g0 * g.gbytes, stg, (size_t)(n * g.gbytes), hipMemcpyHostToDevice,
-                                 m->stream));
-        HIPTRY(m, hipStreamSynchronize(m->stream));
-    }
-    return LM_OK;
-}
-
 // residency: layers n_res..L-1 are streamed through the two HBM buffers,
 // alternating between them in order
 static bool layer_streamed(const lm_model* m, int l) { return l >= m->n_res; }
@@ -968,13 +789,6 @@ extern "C" lm_status lm_load_layer_weights(lm_model* m, int32_t layer, const lm_
         if ((st = upload_frag(m, (int)(2 * F), (int)H, src_gu, df(M_GU), host)) != LM_OK) return st;
         if ((st = upload_frag(m, (int)H, (int)F, src_down, df(M_DOWN), host)) != LM_OK) return st;
     }
-    if (m->step_capable) {
-        uint8_t* tl = m->d_tiles + (int64_t)layer * m->tile_layer_stride;
-        if ((st = upload_tiles(m, m->tgeo[0], src_qkv, tl + m->tile_off[0])) != LM_OK) return st;
-        if ((st = upload_tiles(m, m->tgeo[1], src_wo, tl + m->tile_off[1])) != LM_OK) return st;
-        if ((st = upload_tiles(m, m->tgeo[2], src_gu, tl + m->tile_off[2])) != LM_OK) return st;
-        if ((st = upload_tiles(m, m->tgeo[3], src_down, tl + m->tile_off[3])) != LM_OK) return st;
-    }
     HIPTRY(m, hipMemcpy(m->d_norms + (int64_t)layer * 2 * H, w->attn_norm, H * 4, hipMemcpyHostToDevice));
     HIPTRY(m, hipMemcpy(m->d_norms + ((int64_t)layer * 2 + 1) * H, w->ffn_norm, H * 4, hipMemcpyHostToDevice));
     m->layer_loaded[layer] = 1;
@@ -997,7 +811,6 @@ extern "C" lm_status lm_load_global_weights(lm_model* m, const uint16_t* tok_emb
     if (st != LM_OK) return st;
     if (m->batched && (st = upload_sct(m, (int)m->V, (int)m->H, src_row, m->d_lm_sct, false)) != LM_OK) return st;
     if (m->batched && (st = upload_frag(m, (int)m->V, (int)m->H, src_row, m->d_lm_qf, false)) != LM_OK) return st;
-    if (m->step_capable && (st = upload_tiles(m, m->tgeo[4], src_row, m->d_lm_tiles)) != LM_OK) return st;
     m->global_loaded = true;
     return LM_OK;
 }
@@ -1267,16 +1080,6 @@ static hipError_t gemv(lm_model* m, GemvArgs a, int epi, int n_seq, hipStream_t 
     return launch_gemv(a, epi, n_seq, m->gemv_max_blocks, st);
 }
 
-static bool use_step(const lm_model* m, int n_seq) {
-    return m->persistent && m->step_capable && n_seq == 1 && !m->streaming && !m->any_skip && !m->sim_on &&
-           !m->opt_active;
-}
-
-static bool use_flow(const lm_model* m, int n_seq) {
-    return m->flow_mode != 0 && m->flow_capable && n_seq == 1 && !m->streaming && !m->any_skip && !m->sim_on &&
-           !m->opt_active && !use_step(m, n_seq);
-}
-
 // Launch this family's kernels?  All of them, unless a timing-only graph of
 // one family is being captured (lm_time_kind).
 static bool want(const lm_model* m, int kind) { return m->only_kind < 0 || m->only_kind == kind; }
@@ -1285,24 +1088,9 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
     const lm_config& c = m->cfg;
     const int L = c.n_layers;
     hipStream_t st = m->stream;
-    if (use_step(m, n_seq)) {
-        KTimer t(m, LM_K_STEP);
-        if (want(m, LM_K_STEP))
-            HIPTRY(m, launch_step(m->step_h, m->d_step_args, c.qtype, d_tok, d_logits, d_argmax, m->n_cus, st));
-        return LM_OK;
-    }
     {
         KTimer t(m, LM_K_EMBED);
         if (want(m, LM_K_EMBED)) HIPTRY(m, launch_embed(m->d_embd, d_tok, (int)m->V, (int)m->H, m->d_x, n_seq, st));
-    }
-    const bool flow = use_flow(m, n_seq);
-    if (flow) {
-        KTimer t(m, LM_K_FLOW);
-        if (want(m, LM_K_FLOW)) {
-            FlowArgs fa = m->flow_h;
-            fa.blobs = m->d_layers;       // the resident arena as it is now
-            HIPTRY(m, launch_flow(fa, c.qtype, st));
-        }
     }
     GemvArgs base{};
     base.qtype = c.qtype;
@@ -1342,7 +1130,7 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
         }
     m->prefetched[0] = m->prefetched[1] = false;
 
-    for (int l = 0; l < (flow ? 0 : L); ++l) {
+    for (int l = 0; l < L; ++l) {
         if (m->skip[l]) continue;                       // its input is its output
         if (m->opt_active && l >= m->opt_limit) continue;
         if (layer_streamed(m, l)) HIPTRY(m, hipStreamWaitEvent(st, m->ev_copied[stream_slot(m, l)], 0));
@@ -1483,40 +1271,6 @@ static lm_status run_step(lm_model* m, int n_seq, const int* d_tok, float* d_log
     return launch_graph(m, m->graphs.back());
 }
 
-// The step kernel sets an error flag when a wait between workgroups times
-// out (another kernel holding CUs for seconds); its counts are then reset.
-static lm_status check_step_error(lm_model* m) {
-    uint32_t err = 0;
-    HIPTRY(m, hipMemcpy(&err, m->d_step_misc + 1, 4, hipMemcpyDeviceToHost));
-    if (!err) return LM_OK;
-    HIPTRY(m, hipMemset(m->d_bar, 0, (size_t)(step_bar_words(m->cfg.n_layers) * 4)));
-    HIPTRY(m, hipMemset(m->d_step_misc, 0, (size_t)((4 + m->nkv) * 4)));
-    return fail(m, LM_E_HIP, "persistent decode step: a wait between workgroups timed out (every CU must be "
-                "free for the step kernel); the step's outputs are invalid");
-}
-
-// The dataflow step sets its error flag when a wait between workgroups timed
-// out; the counters are then reset so the next step starts clean.
-static lm_status check_flow_error(lm_model* m) {
-    uint32_t err = 0;
-    HIPTRY(m, hipMemcpy(&err, m->flow_h.err, 4, hipMemcpyDeviceToHost));
-    if (!err) return LM_OK;
-    HIPTRY(m, hipMemset(m->d_flow_ctl, 0, (size_t)(flow_ctl_words(m->cfg.n_layers) * 4)));
-    return fail(m, LM_E_HIP, "dataflow decode step: a wait between workgroups timed out; the step's outputs "
-                "are invalid");
-}
-
-extern "C" lm_status lm_check_error(lm_model* m) {
-    if (!m) return LM_E_ARG;
-    HIPTRY(m, hipStreamSynchronize(m->stream));
-    if (m->flow_capable) {
-        lm_status s = check_flow_error(m);
-        if (s != LM_OK) return s;
-    }
-    if (m->step_capable) return check_step_error(m);
-    return LM_OK;
-}
-
 static lm_status check_ready(lm_model* m, const char* fn, int n_seq) {
     if (!m->global_loaded)
         return fail(m, LM_E_STATE, "%s: global weights not loaded (lm_load_global_weights)", fn);
@@ -1550,14 +1304,6 @@ extern "C" lm_status lm_decode_step(lm_model* m, const int32_t* tokens, int32_t 
         HIPTRY(m, hipMemcpyAsync(logits, m->d_logits, (size_t)(n_seq * m->V * 4), hipMemcpyDeviceToHost,
                                  m->stream));
     HIPTRY(m, hipStreamSynchronize(m->stream));
-    if (use_step(m, n_seq)) {
-        lm_status es = check_step_error(m);
-        if (es != LM_OK) return es;
-    }
-    if (use_flow(m, n_seq)) {
-        lm_status es = check_flow_error(m);
-        if (es != LM_OK) return es;
-    }
     return collect_timing(m);
 }
 
@@ -1650,98 +1396,6 @@ extern "C" lm_status lm_speculative_step(lm_model* m, int32_t token, int32_t dra
     m->pos[0] = p + n + 1;
     HIPTRY(m, hipMemcpy(m->d_pos, &m->pos[0], 4, hipMemcpyHostToDevice));
     return collect_timing(m);
-}
-
-extern "C" lm_status lm_set_persistent(lm_model* m, int32_t enable) {
-    if (!m) return LM_E_ARG;
-    if (enable && !m->step_capable)
-        return fail(m, LM_E_STATE, "lm_set_persistent: the one-kernel step is not available for this model "
-                    "(it needs max_seqs = 1 and an LDS plan that fits: widest GEMV input %lld columns)",
-                    (long long)std::max<int64_t>({m->H, m->F, m->qrows}));
-    HIPTRY(m, hipStreamSynchronize(m->stream));
-    m->persistent = enable != 0;
-    invalidate_graphs(m);
-    return LM_OK;
-}
-
-extern "C" lm_status lm_set_dataflow(lm_model* m, int32_t enable) {
-    if (!m) return LM_E_ARG;
-    if (enable && !m->flow_capable)
-        return fail(m, LM_E_STATE, "lm_set_dataflow: the dataflow step is not available for this model (it needs "
-                    "Q8_0/Q4_0, head_dim 128, at most 8 query heads per KV head, hidden and FFN widths >= 2048)");
-    if (enable < 0 || enable > 2) return fail(m, LM_E_ARG, "lm_set_dataflow: mode = %d; expected 0, 1 or 2", enable);
-    HIPTRY(m, hipStreamSynchronize(m->stream));
-    if (m->flow_capable && (enable == 2) != (m->flow_h.resident != 0)) {
-        // the counters' launch totals depend on the plan: start them afresh
-        m->flow_h.resident = enable == 2;
-        flow_plan(m->flow_h, m->cfg.qtype, m->n_cus);
-        HIPTRY(m, hipMemset(m->d_flow_ctl, 0, (size_t)(flow_ctl_words(m->cfg.n_layers) * 4)));
-    }
-    m->flow_mode = enable;
-    invalidate_graphs(m);
-    return LM_OK;
-}
-
-extern "C" lm_status lm_debug_flow_trace(lm_model* m, const int32_t* d_tokens, uint64_t* out, int64_t capacity,
-                                         int32_t* n_wg, int32_t* wg_per_phase) {
-    if (!m || !d_tokens || !out || !n_wg || !wg_per_phase) return LM_E_ARG;
-    if (!use_flow(m, 1)) return fail(m, LM_E_STATE, "lm_debug_flow_trace: the dataflow step is not in use");
-    lm_status st = check_ready(m, "lm_debug_flow_trace", 1);
-    if (st != LM_OK) return st;
-    const int64_t grid = m->flow_h.resident ? (int64_t)m->cfg.n_layers * kFlowOps * m->flow_h.wg[0]
-                                            : (int64_t)m->cfg.n_layers * m->flow_h.wg_off[kFlowOps];
-    const int64_t words = grid * kFlowTraceWords;
-    *n_wg = (int32_t)grid;
-    for (int i = 0; i < kFlowOps; ++i) wg_per_phase[i] = m->flow_h.wg[i];
-    if (capacity < words)
-        return fail(m, LM_E_ARG, "lm_debug_flow_trace: capacity = %lld words; expected >= %lld", (long long)capacity,
-                    (long long)words);
-    uint64_t* d = nullptr;
-    HIPTRY(m, hipStreamSynchronize(m->stream));
-    HIPTRY(m, hipMalloc(&d, (size_t)words * 8));
-    FlowArgs a = m->flow_h;
-    a.blobs = m->d_layers;
-    a.trace = d;
-    hipError_t e = hipMemsetAsync(d, 0, (size_t)words * 8, m->stream);
-    if (e == hipSuccess) e = launch_embed(m->d_embd, d_tokens, (int)m->V, (int)m->H, m->d_x, 1, m->stream);
-    if (e == hipSuccess) e = launch_flow(a, m->cfg.qtype, m->stream);
-    if (e == hipSuccess) e = hipStreamSynchronize(m->stream);
-    if (e == hipSuccess) e = hipMemcpy(out, d, (size_t)words * 8, hipMemcpyDeviceToHost);
-    (void)hipFree(d);
-    if (e != hipSuccess) return fail(m, LM_E_HIP, "lm_debug_flow_trace: %s", hipGetErrorString(e));
-    return check_flow_error(m);
-}
-
-extern "C" lm_status lm_debug_step_trace(lm_model* m, const int32_t* d_tokens, uint64_t* out, int64_t capacity,
-                                         int32_t* n_cus, int32_t* n_phases) {
-    if (!m || !d_tokens || !out || !n_cus || !n_phases) return LM_E_ARG;
-    if (!m->step_capable || !m->persistent || m->streaming)
-        return fail(m, LM_E_STATE, "lm_debug_step_trace: the persistent step is not in use");
-    lm_status st = check_ready(m, "lm_debug_step_trace", 1);
-    if (st != LM_OK) return st;
-    const int64_t np = 5 * (int64_t)m->cfg.n_layers + 1;
-    const int64_t words = (int64_t)m->n_cus * np * kTraceWords;
-    *n_cus = m->n_cus;
-    *n_phases = (int32_t)np;
-    if (capacity < words)
-        return fail(m, LM_E_ARG, "lm_debug_step_trace: capacity = %lld words; expected >= %lld", (long long)capacity,
-                    (long long)words);
-    uint64_t* d = nullptr;
-    HIPTRY(m, hipStreamSynchronize(m->stream));
-    HIPTRY(m, hipMalloc(&d, (size_t)words * 8));
-    StepArgs a = m->step_h;
-    a.trace = d;
-    hipError_t e = hipMemsetAsync(d, 0, (size_t)words * 8, m->stream);
-    if (e == hipSuccess) e = hipMemcpyAsync(m->d_step_args, &a, sizeof a, hipMemcpyHostToDevice, m->stream);
-    if (e == hipSuccess)
-        e = launch_step(a, m->d_step_args, m->cfg.qtype, d_tokens, nullptr, m->d_argmax, m->n_cus, m->stream);
-    if (e == hipSuccess) e = hipStreamSynchronize(m->stream);
-    if (e == hipSuccess) e = hipMemcpy(out, d, (size_t)words * 8, hipMemcpyDeviceToHost);
-    (void)hipMemcpy(m->d_step_args, &m->step_h, sizeof m->step_h, hipMemcpyHostToDevice);
-    (void)hipFree(d);
-    if (e != hipSuccess) return fail(m, LM_E_HIP, "lm_debug_step_trace: %s", hipGetErrorString(e));
-    m->pos[0] += 1;
-    return check_step_error(m);
 }
 
 extern "C" lm_status lm_set_graph(lm_model* m, int32_t enable) {
@@ -1866,7 +1520,6 @@ extern "C" lm_status lm_set_residency(lm_model* m, int32_t n_resident) {
     m->n_res = nw;
     m->streaming = nw < L;
     rebuild_stream_order(m);
-    m->flow_h.blobs = d;
     m->prefetched[0] = m->prefetched[1] = false;
     invalidate_graphs(m);
     return LM_OK;
@@ -2002,7 +1655,7 @@ extern "C" lm_status lm_time_kind(lm_model* m, int32_t kind, int32_t n_seq, int3
     if (e != hipSuccess) return fail(m, LM_E_HIP, "lm_time_kind: %s", hipGetErrorString(e));
     // launches of the family per step (a launch may be more than one graph node:
     // the several-sequence GEMV stages its activations first)
-    const bool once = kind == LM_K_EMBED || kind == LM_K_LMHEAD || kind == LM_K_FLOW || kind == LM_K_STEP;
+    const bool once = kind == LM_K_EMBED || kind == LM_K_LMHEAD;
     const double launches = once ? 1.0 : (double)m->cfg.n_layers;
     *us_per_launch = 1e3 * (double)ms / ((double)reps * launches);
     return LM_OK;
@@ -2039,20 +1692,6 @@ extern "C" lm_status lm_kernel_bytes(const lm_model* m, int32_t kind, int32_t n_
         case LM_K_DOWN: b = L * (H * F * bpw + S * (F * 4 + H * 8)); break;
         case LM_K_LMHEAD: b = V * H * bpw + H * 4 + S * H * 4; break;
         case LM_K_COPY: b = (double)m->str_list.size() * (double)m->blob_bytes; break;
-        case LM_K_FLOW:
-            for (int k = LM_K_QKV; k <= LM_K_DOWN; ++k) {
-                double kb = 0.0;
-                (void)lm_kernel_bytes(m, k, n_seq, &kb);
-                b += kb;
-            }
-            break;
-        case LM_K_STEP:
-            for (int k = LM_K_EMBED; k <= LM_K_LMHEAD; ++k) {
-                double kb = 0.0;
-                (void)lm_kernel_bytes(m, k, n_seq, &kb);
-                b += kb;
-            }
-            break;
     }
     *bytes = b;
     return LM_OK;
@@ -2107,6 +1746,46 @@ extern "C" lm_status lm_debug_dequant(lm_model* m, int32_t layer, int32_t which,
             std::memcpy(out + (r + i) * K, tmp.data() + i * stride * K, (size_t)K * 4);
         r += n;
     }
+    return LM_OK;
+}
+
+extern "C" void lm_debug_fail_alloc(int64_t n) {
+    g_fail_at.store(n > 0 ? g_alloc_count.load() + (long)n : 0L);
+}
+
+extern "C" int64_t lm_debug_alloc_count(void) { return g_alloc_count.load(); }
+
+extern "C" lm_status lm_debug_gemv(lm_model* m, int32_t layer, int32_t which, int32_t n_seq, const float* x,
+                                   float* y) {
+    if (!m || !x || !y) return LM_E_ARG;
+    if (which < 0 || which > 4) return fail(m, LM_E_ARG, "lm_debug_gemv: which = %d; expected 0..4", which);
+    if (which < 4 && (layer < 0 || layer >= m->cfg.n_layers))
+        return fail(m, LM_E_ARG, "lm_debug_gemv: layer = %d; expected 0..%d", layer, m->cfg.n_layers - 1);
+    if (n_seq < 1 || n_seq > m->cfg.max_seqs)
+        return fail(m, LM_E_ARG, "lm_debug_gemv: n_seq = %d; expected 1..%d (max_seqs)", n_seq, m->cfg.max_seqs);
+    if (which < 4 && layer_streamed(m, layer))
+        return fail(m, LM_E_STATE, "lm_debug_gemv: layer %d is streamed (make it resident first)", layer);
+    const int mats[4] = {M_QKV, M_WO, M_GU, M_DOWN};
+    const QMat w = which == 4 ? lm_head_mat(m) : mat_at(m, m->d_layers + (int64_t)layer * m->blob_bytes, mats[which]);
+    const int64_t K = w.K, N = w.N;
+    HIPTRY(m, hipStreamSynchronize(m->stream));
+    float* d = nullptr;
+    HIPTRY(m, hipMalloc(&d, (size_t)(n_seq * (K + N)) * 4));
+    GemvArgs a{};
+    a.w = w;
+    a.qtype = m->cfg.qtype;
+    a.xin = d;
+    a.x_stride = (int)K;
+    a.out = d + n_seq * K;
+    a.out_stride = (int)N;
+    a.n_seq = n_seq;
+    hipError_t e = hipMemcpyAsync(d, x, (size_t)(n_seq * K) * 4, hipMemcpyHostToDevice, m->stream);
+    if (e == hipSuccess) e = hipMemsetAsync(d + n_seq * K, 0, (size_t)(n_seq * N) * 4, m->stream);
+    if (e == hipSuccess) e = gemv(m, a, EPI_RESID, n_seq, m->stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(y, d + n_seq * K, (size_t)(n_seq * N) * 4, hipMemcpyDeviceToHost, m->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(m->stream);
+    (void)hipFree(d);
+    if (e != hipSuccess) return fail(m, LM_E_HIP, "lm_debug_gemv: %s", hipGetErrorString(e));
     return LM_OK;
 }
 
