@@ -28,6 +28,12 @@ namespace lmk {
 
 constexpr int kBlock = 256;   // threads per workgroup (4 wavefronts)
 constexpr int kWaves = kBlock / 64;
+// The one-sequence GEMV runs one 8-wavefront workgroup per CU: the input is
+// staged into LDS once per CU, by twice the threads of a 4-wavefront group.
+#ifndef LMK_GEMV_NT
+#define LMK_GEMV_NT 512
+#endif
+constexpr int kGemvThreads = LMK_GEMV_NT;
 
 // ---------------------------------------------------------------------------
 // helpers
@@ -179,6 +185,8 @@ __device__ __forceinline__ void dot_q6(const int4 A, const uint2 Hb, const int4*
     hi = combine_digits(b0, b1, b2);
 }
 
+// Sum over a workgroup of NW wavefronts (red: NW floats of LDS).
+template <int NW = kWaves>
 __device__ __forceinline__ float block_sum(float v, float* red) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     v = wave_sum(v);
@@ -187,7 +195,7 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
     __syncthreads();
     float t = 0.f;
     #pragma unroll
-    for (int w = 0; w < kWaves; ++w) t += red[w];
+    for (int w = 0; w < NW; ++w) t += red[w];
     return t;
 }
 

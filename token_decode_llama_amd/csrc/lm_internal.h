@@ -27,10 +27,12 @@ constexpr int attn_cnt_lines(int max_chunks) { return 1 + (max_chunks + kCntGrou
 //   Q8_0: quants, each row = [first 16 bytes of every block]
 //         [last 16 bytes of every block] (int8), so a wavefront reading
 //         block b of consecutive lanes makes fully coalesced 16-byte loads;
-//         scales: fp16 [N][nb];
+//         scales: fp16 [N/2][nb][2], the two rows of a row pair interleaved
+//         (one 32-bit load gives both rows' scale of a block; kScPairs),
+//         else fp16 [N][nb];
 //   Q4_0: quants, each row = nb x 16 nibble bytes in GGUF order
 //         (byte j: element j low nibble, element j+16 high nibble);
-//         scales: fp16 [N][nb];
+//         scales: fp16 [N/2][nb][2] as Q8_0;
 //   Q4_K: quants, each row = nb x 16 bytes, the 32-weight sub-blocks
 //         regrouped into the Q4_0 nibble order; scales: the super-blocks'
 //         16-byte headers as stored (fp16 d, fp16 dmin, 12 bytes of packed
@@ -91,6 +93,13 @@ inline int64_t gguf_row_bytes(int qtype, int64_t K) {
 }
 
 enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
+
+// Q8_0 / Q4_0 scale plane: 1 = the two rows of a row pair interleaved per
+// block (one 32-bit load per block for both rows), 0 = row-major [N][nb].
+#ifndef LMK_SC_PAIRS
+#define LMK_SC_PAIRS 1
+#endif
+constexpr bool kScPairs = LMK_SC_PAIRS != 0;
 
 struct GemvArgs {
     QMat w;

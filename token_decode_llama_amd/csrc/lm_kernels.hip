@@ -76,7 +76,10 @@ struct WChunk {
     int4 h0[kHdr ? CB : 1], h1[kHdr ? CB : 1];                 // Q4_K / Q5_K super-block headers
     uint32_t p0[QT == kQ5_K ? CB : 1], p1[QT == kQ5_K ? CB : 1];   // Q5_K fifth bits
     uint2 e0[QT == kQ6_K ? CB : 1], e1[QT == kQ6_K ? CB : 1];  // Q6_K high bits
-    uint16_t d0[CB], d1[CB];      // block scale (Q8_0, Q4_0) / sub-block scale pair (Q6_K)
+    static constexpr bool kPair = (QT == kQ8_0 || QT == kQ4_0) && kScPairs;
+    uint16_t d0[kPair ? 1 : CB], d1[kPair ? 1 : CB];   // block scales of row 0 / 1 (Q8_0, Q4_0) or the
+                                                       // sub-block scale pairs (Q6_K)
+    uint32_t dd[kPair ? CB : 1];   // Q8_0 / Q4_0 with paired scales: both rows' block scale (row 0 low)
     uint16_t f0[QT == kQ6_K ? CB : 1], f1[QT == kQ6_K ? CB : 1];   // Q6_K super-block d
 };
 
@@ -84,15 +87,20 @@ struct WChunk {
 #define LMK_GEMV_MIN_BLOCKS 1     // workgroups per CU the register budget must allow
 #endif
 
-// XR: float4s of the input each thread requests per prologue batch (4, 8 or
-// 16: K up to 4096, 8192 or 16384 columns in one round trip); a template
-// parameter so the register budget of the short-K kernels stays small.
-template <int QT, int LPR, int EPI, int XR>
-__global__ __launch_bounds__(kBlock, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a) {
+// XR: float4s of the input each thread requests per prologue batch (2, 4 or
+// 8: K up to 4096, 8192 or 16384 columns in one round trip with 512 threads);
+// a template parameter so the register budget of the short-K kernels stays
+// small.
+// NT threads per workgroup: 512 (one workgroup per CU, the input staged once
+// per CU); the LM head keeps two 256-thread workgroups per CU (its staging is
+// amortised over ~30 row pairs per wavefront; measured faster so).
+template <int QT, int LPR, int EPI, int XR, int NT>
+__global__ __launch_bounds__(NT, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a) {
+    constexpr int NW = NT / 64;
     extern __shared__ __align__(16) float smem[];
-    __shared__ float red[kWaves];
-    __shared__ float wv_best[kWaves];
-    __shared__ int wi_best[kWaves];
+    __shared__ float red[NW];
+    __shared__ float wv_best[NW];
+    __shared__ int wi_best[NW];
     __shared__ int s_last;
 
     constexpr int CB = ChunkBlocks<QT>::value;
@@ -121,7 +129,7 @@ __global__ __launch_bounds__(kBlock, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a
     // this wavefront's steps: step0, step0 + sstride, ... ; each step is split
     // into `cps` chunks of CB blocks per lane
     const int n_steps = (N + kRowsPerStep - 1) / kRowsPerStep;
-    const int step0 = blockIdx.x * kWaves + wave, sstride = gridDim.x * kWaves;
+    const int step0 = blockIdx.x * NW + wave, sstride = gridDim.x * NW;
     const int my_steps = step0 < n_steps ? (n_steps - 1 - step0) / sstride + 1 : 0;
     const int bpl = (nb + LPR - 1) / LPR;        // blocks per lane per row (upper bound)
     const int cps = (bpl + CB - 1) / CB;
@@ -138,6 +146,7 @@ __global__ __launch_bounds__(kBlock, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a
         const int r0 = min((step0 + i * sstride) * kRowsPerStep + rg * 2, N - 2);
         const uint8_t* q0 = a.w.q + (int64_t)r0 * rowq;
         const uint8_t* q1 = q0 + rowq;
+        // Q8_0 / Q4_0: the row pair's scales interleaved, (row r0, row r0+1) per block
         const uint16_t* s0 = a.w.sc + (int64_t)r0 * srow;
         #pragma unroll
         for (int u = 0; u < CB; ++u) {
@@ -163,9 +172,13 @@ __global__ __launch_bounds__(kBlock, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a
                 w.d1[u] = s0[(uint32_t)srow + bc];
                 w.f0[u] = s0[(uint32_t)nb + (bc >> 3)];
                 w.f1[u] = s0[(uint32_t)(srow + nb) + (bc >> 3)];
+            } else if (WChunk<QT>::kPair) {
+                // both rows' block scales in one 32-bit load; consumed only in compute():
+                // consuming a load here would wait on every load issued before it
+                w.dd[u] = *(const uint32_t*)(s0 + bc * 2u);
             } else {
-                w.d0[u] = s0[bc];          // used only in compute(): consuming a load here
-                w.d1[u] = s0[(uint32_t)srow + bc];   // would wait on every load issued before it
+                w.d0[u] = s0[bc];
+                w.d1[u] = s0[(uint32_t)srow + bc];
             }
         }
     };
@@ -180,12 +193,16 @@ __global__ __launch_bounds__(kBlock, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a
             const bool in_row = braw < nb;                     // past the row end: no contribution
             const int4* D = (const int4*)(xq + b * 96);
             const float sx = xsc[b];
+            const uint16_t h0 = WChunk<QT>::kPair ? (uint16_t)(w.dd[u] & 0xFFFFu) : w.d0[u];
+            const uint16_t h1 = WChunk<QT>::kPair ? (uint16_t)(w.dd[u] >> 16) : w.d1[u];
             if (QT == kQ8_0) {
-                const float d0 = in_row ? h2f(w.d0[u]) : 0.f, d1 = in_row ? h2f(w.d1[u]) : 0.f;
+                const float d0 = in_row ? h2f(h0) : 0.f;
+                const float d1 = in_row ? h2f(h1) : 0.f;
                 acc0 = fmaf(d0 * sx, dot_q8(w.a0[u], w.b0[u], D), acc0);
                 acc1 = fmaf(d1 * sx, dot_q8(w.a1[u], w.b1[u], D), acc1);
             } else if (QT == kQ4_0) {
-                const float d0 = in_row ? h2f(w.d0[u]) : 0.f, d1 = in_row ? h2f(w.d1[u]) : 0.f;
+                const float d0 = in_row ? h2f(h0) : 0.f;
+                const float d1 = in_row ? h2f(h1) : 0.f;
                 const int4 T = dsum[b];
                 acc0 = fmaf(d0 * sx, dot_q4(w.a0[u], D, T), acc0);
                 acc1 = fmaf(d1 * sx, dot_q4(w.a1[u], D, T), acc1);
@@ -292,7 +309,7 @@ __global__ __launch_bounds__(kBlock, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a
     auto fetch = [&](int base) {
         #pragma unroll
         for (int u = 0; u < XR; ++u) {
-            const int i = min(base + (tid + u * kBlock) * 4, K - 4);
+            const int i = min(base + (tid + u * NT) * 4, K - 4);
             xr[u] = *(const float4*)(x + i);
             if (kGain && has_g) gr[u % GR] = *(const float4*)(a.norm_g + i);
         }
@@ -305,13 +322,13 @@ __global__ __launch_bounds__(kBlock, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a
     load(0, wa);          // unconditional: rows are clamped, so these are always in bounds
     load(1, wb);
     float ss = 0.f;
-    for (int base = 0; base < K; base += XR * kBlock * 4) {
+    for (int base = 0; base < K; base += XR * NT * 4) {
         if (base > 0) fetch(base);
         #pragma unroll
         for (int u = 0; u < XR; ++u) {
             // the 8 threads tid..tid|7 hold one 32-column block (K % 32 == 0, so a
             // block is either wholly inside K or wholly past it: uniform per group)
-            const int i = base + (tid + u * kBlock) * 4;
+            const int i = base + (tid + u * NT) * 4;
             float4 v = xr[u];
             if (kGain && has_g) {
                 if (i < K) {
@@ -330,7 +347,7 @@ __global__ __launch_bounds__(kBlock, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a
         }
     }
     // block_sum's barriers also order the LDS stores above before any reads
-    if (has_g) rscale = 1.0f / sqrtf(block_sum(ss, red) / (float)K + a.eps);
+    if (has_g) rscale = 1.0f / sqrtf(block_sum<NW>(ss, red) / (float)K + a.eps);
     __syncthreads();
 
     // ---- the position and the RoPE inputs of this wavefront's first row pair.
@@ -387,7 +404,7 @@ __global__ __launch_bounds__(kBlock, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a
         if (tid == 0) {
             float bv = wv_best[0];
             int bi = wi_best[0];
-            for (int w = 1; w < kWaves; ++w) better(bv, bi, wv_best[w], wi_best[w]);
+            for (int w = 1; w < NW; ++w) better(bv, bi, wv_best[w], wi_best[w]);
             a.part_val[(int64_t)s * gridDim.x + blockIdx.x] = bv;
             a.part_idx[(int64_t)s * gridDim.x + blockIdx.x] = bi;
             __threadfence();
@@ -400,7 +417,7 @@ __global__ __launch_bounds__(kBlock, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a
             __syncthreads();
             float bv = -FLT_MAX;
             int bi = INT_MAX;
-            for (int i = tid; i < (int)gridDim.x; i += kBlock)
+            for (int i = tid; i < (int)gridDim.x; i += NT)
                 better(bv, bi, a.part_val[(int64_t)s * gridDim.x + i],
                        a.part_idx[(int64_t)s * gridDim.x + i]);
             #pragma unroll
@@ -412,7 +429,7 @@ __global__ __launch_bounds__(kBlock, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a
             if (lane == 0) { wv_best[wave] = bv; wi_best[wave] = bi; }
             __syncthreads();
             if (tid == 0) {
-                for (int w = 1; w < kWaves; ++w) better(wv_best[0], wi_best[0], wv_best[w], wi_best[w]);
+                for (int w = 1; w < NW; ++w) better(wv_best[0], wi_best[0], wv_best[w], wi_best[w]);
                 a.argmax_out[s] = wi_best[0];
                 if (a.pos_inc) a.pos_inc[s] += 1;
                 a.counter[s] = 0;
@@ -439,56 +456,43 @@ static int device_cus() {
     return cached_cus;
 }
 
-template <int QT, int LPR, int EPI, int XR>
-static int resident_blocks(size_t lds) {
-    // workgroups of this instantiation that fit on the whole device at once
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemv<QT, LPR, EPI, XR>, kBlock, lds) != hipSuccess ||
-        per_cu < 1)
-        per_cu = 1;
-    return per_cu * device_cus();
-}
+#ifndef LMK_LMHEAD_NT
+#define LMK_LMHEAD_NT 256
+#endif
+#ifndef LMK_GEMV_WPC
+#define LMK_GEMV_WPC 1      // workgroups per CU
+#endif
+template <int EPI> constexpr int gemv_threads() { return EPI == EPI_LOGITS ? LMK_LMHEAD_NT : kGemvThreads; }
 
 template <int QT, int LPR, int EPI, int XR>
 static hipError_t launch_one(const GemvArgs& a, int n_seq, int max_blocks, size_t lds, hipStream_t st) {
+    constexpr int NT = gemv_threads<EPI>();
     constexpr int rows_per_step = 2 * (64 / LPR);
+    constexpr int nw = NT / 64;
     const int n_steps = (a.w.N + rows_per_step - 1) / rows_per_step;
-    const int need = (n_steps + kWaves - 1) / kWaves;
-    const int cus = device_cus();
-    const int cap = std::min(max_blocks, resident_blocks<QT, LPR, EPI, XR>(lds));
-    int g = need;
-    if (need > cap) {
-        // Several rounds per wavefront.  Busiest CU decides: cost = (row-pair rounds
-        // per wavefront) x (workgroups on the busiest CU), over whole multiples of the
-        // CU count.  Measured on gfx950: beyond two workgroups per CU a long GEMV
-        // slows down (the 128256-row LM head: 101 us at 1-2 per CU, 131 us at 3-4),
-        // so at most two.
-        int64_t best = -1;
-        for (int per = 1; per <= 2 && per * cus <= cap; ++per) {
-            const int cand = per * cus;
-            const int64_t rounds = ((int64_t)n_steps + (int64_t)cand * kWaves - 1) / ((int64_t)cand * kWaves);
-            const int64_t cost = rounds * per;
-            if (best < 0 || cost <= best) { best = cost; g = cand; }
-        }
-        if (best < 0) g = cap;
-    }
+    const int need = (n_steps + nw - 1) / nw;
+    // Eight GEMV wavefronts per CU (measured on gfx950: more slow a long GEMV
+    // down); a longer matrix takes several row-pair rounds per wavefront.
+    int g = std::min({need, device_cus() * LMK_GEMV_WPC, max_blocks});
     if (g < 1) g = 1;
-    hipLaunchKernelGGL((k_gemv<QT, LPR, EPI, XR>), dim3(g, n_seq), dim3(kBlock), lds, st, a);
+    hipLaunchKernelGGL((k_gemv<QT, LPR, EPI, XR, NT>), dim3(g, n_seq), dim3(NT), lds, st, a);
     return hipGetLastError();
 }
 
 template <int QT, int EPI>
 static hipError_t launch_gemv_lpr(const GemvArgs& a, int lpr, int n_seq, int max_blocks, size_t lds,
                                   hipStream_t st) {
-    // K < 2048 (the narrower lane groups) always fits the 4-float4 batch
+    // XR float4s per thread cover K = XR x 4 x NT columns in one input batch;
+    // K < 2048 (the narrower lane groups) always fits the 2-float4 batch
+    constexpr int NT = gemv_threads<EPI>();
     switch (lpr) {
         case 64:
-            if (a.w.K <= 4 * kBlock * 4) return launch_one<QT, 64, EPI, 4>(a, n_seq, max_blocks, lds, st);
-            if (a.w.K <= 8 * kBlock * 4) return launch_one<QT, 64, EPI, 8>(a, n_seq, max_blocks, lds, st);
-            return launch_one<QT, 64, EPI, 16>(a, n_seq, max_blocks, lds, st);
-        case 32: return launch_one<QT, 32, EPI, 4>(a, n_seq, max_blocks, lds, st);
-        case 16: return launch_one<QT, 16, EPI, 4>(a, n_seq, max_blocks, lds, st);
-        default: return launch_one<QT, 8, EPI, 4>(a, n_seq, max_blocks, lds, st);
+            if (a.w.K <= 2 * NT * 4) return launch_one<QT, 64, EPI, 2>(a, n_seq, max_blocks, lds, st);
+            if (a.w.K <= 4 * NT * 4) return launch_one<QT, 64, EPI, 4>(a, n_seq, max_blocks, lds, st);
+            return launch_one<QT, 64, EPI, 8>(a, n_seq, max_blocks, lds, st);
+        case 32: return launch_one<QT, 32, EPI, 2>(a, n_seq, max_blocks, lds, st);
+        case 16: return launch_one<QT, 16, EPI, 2>(a, n_seq, max_blocks, lds, st);
+        default: return launch_one<QT, 8, EPI, 2>(a, n_seq, max_blocks, lds, st);
     }
 }
 
@@ -1567,18 +1571,21 @@ __global__ __launch_bounds__(kBlock) void k_dequant(QMat w, int qtype, int row0,
     const int64_t srow = qmat_srow(qtype, K) / 2;     // 16-bit words
     const uint8_t* q = w.q + (int64_t)r * rowq;
     const uint16_t* sc = w.sc + (int64_t)r * srow;
+    // Q8_0 / Q4_0: with paired scales, this row's at every other word of its row pair's
+    const uint16_t* sp = kScPairs ? w.sc + (int64_t)(r & ~1) * srow + (r & 1) : sc;
+    const int sstep = kScPairs ? 2 : 1;
     for (int c = threadIdx.x; c < K; c += kBlock) {
         const int b = c >> 5, e = c & 31;
         float v;
         if (qtype == kQ8_0) {
-            const float d = h2f(sc[b]);
+            const float d = h2f(sp[sstep * b]);
             const int8_t qi = (int8_t)(e < 16 ? q[b * 16 + e] : q[(int64_t)nb * 16 + b * 16 + (e - 16)]);
             v = d * (float)qi;
         } else {
             const uint8_t byte = q[b * 16 + (e & 15)];
             const int nib = e < 16 ? (byte & 0xF) : (byte >> 4);
             if (qtype == kQ4_0) {
-                v = (float)(nib - 8) * h2f(sc[b]);
+                v = (float)(nib - 8) * h2f(sp[sstep * b]);
             } else if (qtype == kQ4_K || qtype == kQ5_K) {
                 float ds, dm;
                 q4k_scale_min(*(const int4*)(sc + (b >> 3) * 8), b & 7, ds, dm);

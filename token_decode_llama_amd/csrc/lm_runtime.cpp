@@ -78,19 +78,22 @@ void parallel_rows(int64_t n, F&& fn) {
 // nibbles (element 128h + 32t + l at byte 64h + 32(t%2) + l, high nibble when
 // t >= 2), 64 bytes of 2-bit high parts (bits 2t, 2t+1 of byte 32h + l),
 // 16 int8 sub-block scales, fp16 d.
+// Q8_0 / Q4_0 block scales are interleaved per row pair when kScPairs (row
+// 2i's scale of block b, then row 2i+1's): the caller points dsc at this
+// row's first one, and consecutive blocks are 4 bytes apart (else 2).
 void repack_row(int qtype, const uint8_t* src, int K, uint8_t* dq, uint8_t* dsc) {
     const int nb = K / 32;
     if (qtype == kQ8_0) {
         for (int b = 0; b < nb; ++b) {
             const uint8_t* blk = src + (int64_t)b * 34;
-            std::memcpy(dsc + 2 * b, blk, 2);
+            std::memcpy(dsc + (kScPairs ? 4 : 2) * b, blk, 2);
             std::memcpy(dq + (int64_t)b * 16, blk + 2, 16);
             std::memcpy(dq + (int64_t)nb * 16 + (int64_t)b * 16, blk + 18, 16);
         }
     } else if (qtype == kQ4_0) {
         for (int b = 0; b < nb; ++b) {
             const uint8_t* blk = src + (int64_t)b * 18;
-            std::memcpy(dsc + 2 * b, blk, 2);
+            std::memcpy(dsc + (kScPairs ? 4 : 2) * b, blk, 2);
             std::memcpy(dq + (int64_t)b * 16, blk + 2, 16);
         }
     } else if (qtype == kQ4_K || qtype == kQ5_K) {
@@ -618,20 +621,23 @@ static lm_status upload_matrix(lm_model* m, int N, int K, RowFn src_row, uint8_t
                                bool dst_host) {
     const int qt = m->cfg.qtype;
     const int64_t rq = qmat_qbytes(qt, 1, K), rs = qmat_srow(qt, K);
+    // Q8_0 / Q4_0: scales of a row pair interleaved (N is even); the K formats: a row's scales contiguous
+    const bool pairs = (qt == kQ8_0 || qt == kQ4_0) && kScPairs;
+    auto srow_at = [&](uint8_t* base, int64_t r) { return pairs ? base + (r >> 1) * 2 * rs + (r & 1) * 2 : base + r * rs; };
     uint8_t* dsb = (uint8_t*)dsc;
     if (dst_host) {
         parallel_rows(N, [&](int64_t a, int64_t b) {
-            for (int64_t r = a; r < b; ++r) repack_row(qt, src_row(r), K, dq + r * rq, dsb + r * rs);
+            for (int64_t r = a; r < b; ++r) repack_row(qt, src_row(r), K, dq + r * rq, srow_at(dsb, r));
         });
         return LM_OK;
     }
-    const int64_t rows_per = std::max<int64_t>(1, m->stage_bytes / (rq + rs));
+    const int64_t rows_per = std::max<int64_t>(2, m->stage_bytes / (rq + rs)) & ~(int64_t)1;   // whole row pairs
     for (int64_t r0 = 0; r0 < N; r0 += rows_per) {
         const int64_t n = std::min<int64_t>(rows_per, N - r0);
         uint8_t* sq = m->h_stage;
         uint8_t* ss = m->h_stage + n * rq;
         parallel_rows(n, [&](int64_t a, int64_t b) {
-            for (int64_t r = a; r < b; ++r) repack_row(qt, src_row(r0 + r), K, sq + r * rq, ss + r * rs);
+            for (int64_t r = a; r < b; ++r) repack_row(qt, src_row(r0 + r), K, sq + r * rq, srow_at(ss, r));
         });
         HIPTRY(m, hipMemcpyAsync(dq + r0 * rq, sq, (size_t)(n * rq), hipMemcpyHostToDevice, m->stream));
         HIPTRY(m, hipMemcpyAsync(dsb + r0 * rs, ss, (size_t)(n * rs), hipMemcpyHostToDevice, m->stream));
