@@ -1036,16 +1036,14 @@ static lm_status collect_timing(lm_model* m) {
     return LM_OK;
 }
 
-// Attention grid of a step: 64-position chunks up to the next power of two
-// of the longest context among the stepping sequences (at most max_chunks),
-// so a launch does not read the whole cache when the context is short.  A
-// step graph is keyed by it: a context crossing a power of two takes a new
-// graph.
+// Attention grid of a step: 64-position chunks up to the next multiple of
+// four (256 positions) of the longest context among the stepping sequences
+// (at most max_chunks), so a launch reads at most three chunks past the
+// context (their K/V loads are issued before the position is known).  A step
+// graph is keyed by it: a context crossing a multiple of 256 takes a new graph.
 static int attn_chunks_for(const lm_model* m, int need) {
     const int tiles = (std::max(need, 1) + kAttnChunk - 1) / kAttnChunk;
-    int c = 1;
-    while (c < tiles) c *= 2;
-    return std::min(c, m->max_chunks);
+    return std::min((tiles + 3) / 4 * 4, m->max_chunks);
 }
 
 static int attn_grid_chunks(const lm_model* m, int n_seq) {
