@@ -265,6 +265,57 @@ __device__ __forceinline__ void stage_digits(float4 v, int i, int K, int8_t* xq,
 }
 
 
+// Cross-workgroup hand-off within one launch.  Each XCD has its own L2,
+// which is not coherent with the others', and an acquire or release at device
+// scope makes the compiler write back (buffer_wbl2) and invalidate
+// (buffer_inv) that whole L2 at every use: once per workgroup this cost the
+// 4096-position batch-4 attention more than half its time.  The hand-offs
+// below get the same ordering from the memory operations themselves instead:
+//   * the data crosses in device-coherent stores and loads (relaxed atomics
+//     at device scope, which the hardware issues with the sc1 bit: the store
+//     is written through to memory-side coherence, the load is not served
+//     from a non-coherent cache);
+//   * every wavefront waits for its stores to complete (vmcnt(0)) and the
+//     workgroup meets at a barrier before one thread counts its arrival, so
+//     the data is visible device-wide before the count moves;
+//   * the caller that completes the count reads the data only after the
+//     count's returned value and a barrier, so those loads are issued after
+//     every earlier arrival was counted.
+// The barriers also keep the compiler from moving these memory operations
+// across the count.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(int* p, int v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_dev(const int* p) {
+    return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// two floats at an 8-byte aligned address, device-coherent
+__device__ __forceinline__ void st_dev2(float* p, float x, float y) {
+    const uint64_t v = (uint64_t)__float_as_uint(x) | ((uint64_t)__float_as_uint(y) << 32);
+    __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 ld_dev2(const float* p) {
+    const uint64_t v = __hip_atomic_load((uint64_t*)const_cast<float*>(p), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+// this wavefront's outstanding memory operations have completed (gfx9 vmcnt(0))
+__device__ __forceinline__ void drain_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// one arrival of n on a device-scope count; true for the caller that makes it
+// n, which also resets it to zero for the next launch.  One thread calls it,
+// between the barriers described above.
+__device__ __forceinline__ bool count_arrive(int* c, int n) {
+    if (__hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != n - 1) return false;
+    __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+}
+
 // ---------------------------------------------------------------------------
 // split-context attention
 // ---------------------------------------------------------------------------
@@ -273,21 +324,14 @@ __device__ __forceinline__ void stage_digits(float4 v, int i, int K, int8_t* xq,
 // then merges).  Two levels, so that at most kCntGroup atomics meet on one
 // line: chunks count into their group's line, the chunk completing a group
 // counts into line 0.  Whoever completes a count resets it for the next launch.
-// One thread calls it, after its workgroup's partial stores have completed.
-// The counts are release/acquire at device scope: each arrival releases its
-// workgroup's partial states, and the caller that completes the count
-// acquires every earlier arrival's (through the first-level count and then
-// the second), so the merge that follows reads them all.
+// One thread calls it, after its workgroup's partial stores have completed
+// (the hand-off above; the second level is reached only after the first
+// level's count has returned).
 __device__ __forceinline__ bool chunk_arrive(int* cnt, int chunk, int n_act) {
     const int grp = chunk / kCntGroup, n_grp = (n_act + kCntGroup - 1) / kCntGroup;
     const int in_grp = min(kCntGroup, n_act - grp * kCntGroup);
-    int* c1 = cnt + (1 + grp) * kCntStride;
-    if (__hip_atomic_fetch_add(c1, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) != in_grp - 1) return false;
-    __hip_atomic_store(c1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (n_grp == 1) return true;
-    if (__hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) != n_grp - 1) return false;
-    __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return true;
+    if (!count_arrive(cnt + (1 + grp) * kCntStride, in_grp)) return false;
+    return n_grp == 1 || count_arrive(cnt, n_grp);
 }
 
 // Log-sum-exp merge of the n_act chunk states of the G query heads of one KV

@@ -405,21 +405,20 @@ __global__ __launch_bounds__(NT, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a) {
             float bv = wv_best[0];
             int bi = wi_best[0];
             for (int w = 1; w < NW; ++w) better(bv, bi, wv_best[w], wi_best[w]);
-            a.part_val[(int64_t)s * gridDim.x + blockIdx.x] = bv;
-            a.part_idx[(int64_t)s * gridDim.x + blockIdx.x] = bi;
-            __threadfence();
-            const int old = atomicAdd(&a.counter[s], 1);
-            s_last = (old == (int)gridDim.x - 1);
+            // the workgroup's candidate, handed to the last workgroup as the
+            // attention chunks hand over their states (lm_device.h)
+            st_dev(&a.part_val[(int64_t)s * gridDim.x + blockIdx.x], bv);
+            st_dev(&a.part_idx[(int64_t)s * gridDim.x + blockIdx.x], bi);
+            drain_vm();
+            s_last = count_arrive(&a.counter[s], (int)gridDim.x);
         }
         __syncthreads();
         if (s_last) {
-            if (tid == 0) __threadfence();
-            __syncthreads();
             float bv = -FLT_MAX;
             int bi = INT_MAX;
             for (int i = tid; i < (int)gridDim.x; i += NT)
-                better(bv, bi, a.part_val[(int64_t)s * gridDim.x + i],
-                       a.part_idx[(int64_t)s * gridDim.x + i]);
+                better(bv, bi, ld_dev(&a.part_val[(int64_t)s * gridDim.x + i]),
+                       ld_dev(&a.part_idx[(int64_t)s * gridDim.x + i]));
             #pragma unroll
             for (int off = 32; off > 0; off >>= 1) {
                 const float ov = __shfl_xor(bv, off, 64);
@@ -432,7 +431,6 @@ __global__ __launch_bounds__(NT, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a) {
                 for (int w = 1; w < NW; ++w) better(wv_best[0], wi_best[0], wv_best[w], wi_best[w]);
                 a.argmax_out[s] = wi_best[0];
                 if (a.pos_inc) a.pos_inc[s] += 1;
-                a.counter[s] = 0;
             }
         }
     }
@@ -1015,26 +1013,22 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
                 const int oi = __shfl_xor(bi, off, 64);
                 better(bv, bi, ov, oi);
             }
-            if (er == 0 && es < a.n_seq) {
-                a.part_val[(int64_t)es * gridDim.x + blockIdx.x] = bv;
-                a.part_idx[(int64_t)es * gridDim.x + blockIdx.x] = bi;
+            if (er == 0 && es < a.n_seq) {      // handed over as in lm_device.h
+                st_dev(&a.part_val[(int64_t)es * gridDim.x + blockIdx.x], bv);
+                st_dev(&a.part_idx[(int64_t)es * gridDim.x + blockIdx.x], bi);
             }
         }
+        drain_vm();
         __syncthreads();
-        if (tid == 0) {
-            __threadfence();
-            const int old = atomicAdd(&a.counter[0], 1);
-            s_last = (old == (int)gridDim.x - 1);
-        }
+        if (tid == 0) s_last = count_arrive(&a.counter[0], (int)gridDim.x);
         __syncthreads();
         if (s_last) {
-            if (tid == 0) __threadfence();
-            __syncthreads();
             for (int s = 0; s < a.n_seq; ++s) {
                 float bv = -FLT_MAX;
                 int bi = INT_MAX;
                 for (int i = tid; i < (int)gridDim.x; i += 64 * W)
-                    better(bv, bi, a.part_val[(int64_t)s * gridDim.x + i], a.part_idx[(int64_t)s * gridDim.x + i]);
+                    better(bv, bi, ld_dev(&a.part_val[(int64_t)s * gridDim.x + i]),
+                           ld_dev(&a.part_idx[(int64_t)s * gridDim.x + i]));
                 #pragma unroll
                 for (int off = 32; off > 0; off >>= 1) {
                     const float ov = __shfl_xor(bv, off, 64);
@@ -1052,7 +1046,6 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
                     a.argmax_out[s] = bi;
                     if (a.pos_inc) a.pos_inc[s] += 1;
                 }
-                a.counter[0] = 0;
             }
         }
     }
@@ -1126,25 +1119,6 @@ hipError_t launch_gemv_batched(const GemvArgs& a0, int epi, int n_seq, int max_b
 // device-coherent stores, and the last chunk of the (sequence, KV head) to
 // finish merges all of them (merge_chunk_states) within the same launch.
 constexpr int kMaxGroup = 8;   // query heads per KV head
-
-__device__ __forceinline__ void st_dev(float* p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_dev(const float* p) {
-    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// two floats at an 8-byte aligned address, device-coherent
-__device__ __forceinline__ void st_dev2(float* p, float x, float y) {
-    const uint64_t v = (uint64_t)__float_as_uint(x) | ((uint64_t)__float_as_uint(y) << 32);
-    __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float2 ld_dev2(const float* p) {
-    const uint64_t v = __hip_atomic_load((uint64_t*)const_cast<float*>(p), __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-    return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
-}
-// this wavefront's outstanding memory operations have completed (gfx9 vmcnt(0))
-__device__ __forceinline__ void drain_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // One tile per workgroup (short contexts: the straight-line form).
 template <int HD>
