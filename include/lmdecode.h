@@ -265,6 +265,25 @@ lm_status lm_decode_step(lm_model* m, const int32_t* tokens, int32_t n_seq, floa
 lm_status lm_decode_step_dev(lm_model* m, const int32_t* d_tokens, int32_t n_seq,
                              float* d_logits, int32_t* d_argmax);
 
+/* lm_decode_step_dev for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, kernels and results; it calls no hipMalloc,
+ * hipFree or allocating routine and instantiates no graph (its kernels are
+ * launched one by one on the model's stream, so a caller may capture them).
+ * The step's working memory (residual, q, attention output, FFN hidden,
+ * activation digits, attention partial states and counts, argmax candidates
+ * and counts) lives in a fixed 32 MiB device array inside the library, one
+ * per GPU, held until the process ends.  Each call clears the counts it
+ * uses; every call on a GPU shares that GPU's array, so calls that overlap on
+ * one GPU (two streams, two threads) race and must be serialised by the
+ * caller.  Errors: those of lm_decode_step_dev; LM_E_ARG when n_seq
+ * sequences at this model's max_ctx need more than the array holds (the
+ * attention partial states grow with n_seq * n_heads * max_ctx; the message
+ * gives the size); LM_E_STATE when a layer is streamed (every layer must be
+ * resident). */
+lm_status lm_decode_step_dev_noalloc(lm_model* m, const int32_t* d_tokens, int32_t n_seq,
+                                     float* d_logits, int32_t* d_argmax);
+
 /* 1 (default): replay each step from a captured HIP graph; 0: launch eagerly. */
 lm_status lm_set_graph(lm_model* m, int32_t enable);
 

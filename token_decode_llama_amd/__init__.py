@@ -25,7 +25,7 @@ EXPORTS = (
     "lm_load_kv", "lm_get_kv", "lm_set_position", "lm_get_position", "lm_stream_mode",
     "lm_set_residency", "lm_tier_sizes", "lm_plan_residency", "lm_set_layer_skip",
     "lm_layer_similarity", "lm_get_layer_similarity", "lm_skip_similar_layers", "lm_speculative_step",
-    "lm_decode_step", "lm_decode_step_dev", "lm_set_graph", "lm_stream", "lm_last_error",
+    "lm_decode_step", "lm_decode_step_dev", "lm_decode_step_dev_noalloc", "lm_set_graph", "lm_stream", "lm_last_error",
     "lm_kernel_timing", "lm_kernel_stats", "lm_time_kind", "lm_kernel_bytes", "lm_debug_dequant",
     "lm_debug_read_bw", "lm_debug_gemv", "lm_debug_fail_alloc", "lm_debug_alloc_count",
 )
@@ -85,6 +85,7 @@ def load():
         "lm_speculative_step": ([vp, i32, i32, i32, vp, ctypes.POINTER(i32)], st),
         "lm_decode_step": ([vp, vp, i32, vp, vp], st),
         "lm_decode_step_dev": ([vp, vp, i32, vp, vp], st),
+        "lm_decode_step_dev_noalloc": ([vp, vp, i32, vp, vp], st),
         "lm_set_graph": ([vp, i32], st),
         "lm_stream": ([vp], vp),
         "lm_last_error": ([vp], ctypes.c_char_p),
@@ -225,6 +226,12 @@ class Model:
         ptr = lambda x: x if isinstance(x, int) or x is None else x.data_ptr()
         self._check(self._lib.lm_decode_step_dev(self._h, ptr(d_tokens), n_seq, ptr(d_logits),
                                                  ptr(d_argmax)))
+
+    def step_dev_noalloc(self, d_tokens, n_seq: int, d_argmax, d_logits=None):
+        """step_dev without any device allocation (working memory in the library's fixed scratch array)."""
+        ptr = lambda x: x if isinstance(x, int) or x is None else x.data_ptr()
+        self._check(self._lib.lm_decode_step_dev_noalloc(self._h, ptr(d_tokens), n_seq, ptr(d_logits),
+                                                         ptr(d_argmax)))
 
     def stream_mode(self, enable: bool):
         self._check(self._lib.lm_stream_mode(self._h, 1 if enable else 0))

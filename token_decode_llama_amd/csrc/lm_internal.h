@@ -163,6 +163,12 @@ hipError_t launch_attention(const AttnArgs& a, int n_seq, hipStream_t st);
 hipError_t launch_dequant(const QMat& w, int qtype, int row0, int n_rows, float* out,
                           hipStream_t st);
 hipError_t launch_read_bw(const void* buf, int64_t n_bytes, float* sink, hipStream_t st);
+// The allocation-free step's scratch (lm_kernels.hip): a fixed device array of
+// kNoAllocScratchBytes per device, its address looked up once per device.
+constexpr int64_t kNoAllocScratchBytes = 32ll << 20;
+hipError_t noalloc_scratch(int device, uint8_t** ptr);
+// p[0..n) = 0 with a kernel (a graph under capture gets a kernel node, not a memset node)
+hipError_t launch_zero(void* p, int64_t n_bytes, hipStream_t st);
 // acc[0] += cosine similarity of xin and x ([n_seq][H] each) summed over the sequences, acc[1] += n_seq
 hipError_t launch_layer_cos(const float* xin, const float* x, int H, int n_seq, double* acc, hipStream_t st);
 

@@ -29,6 +29,7 @@
 #include <limits.h>
 
 #include <algorithm>
+#include <mutex>
 
 namespace lmk {
 
@@ -1645,6 +1646,55 @@ __global__ __launch_bounds__(kBlock) void k_read_bw(const uint4* __restrict__ bu
 hipError_t launch_read_bw(const void* buf, int64_t n_bytes, float* sink, hipStream_t st) {
     hipLaunchKernelGGL(k_read_bw, dim3(2048), dim3(kBlock), 0, st, (const uint4*)buf, n_bytes / 16, sink);
     return hipGetLastError();
+}
+
+__global__ __launch_bounds__(kBlock) void k_zero(uint32_t* __restrict__ p, int64_t n4) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n4; i += stride) p[i] = 0u;
+}
+
+hipError_t launch_zero(void* p, int64_t n_bytes, hipStream_t st) {
+    if (n_bytes < 0 || n_bytes % 4 || ((uintptr_t)p & 3)) return hipErrorInvalidValue;
+    if (n_bytes == 0) return hipSuccess;
+    const int64_t n4 = n_bytes / 4;
+    const int grid = (int)std::min<int64_t>(1024, (n4 + kBlock - 1) / kBlock);
+    hipLaunchKernelGGL(k_zero, dim3(grid), dim3(kBlock), 0, st, (uint32_t*)p, n4);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// scratch of the allocation-free step
+// ---------------------------------------------------------------------------
+// A fixed array in the code object: every device the library runs on holds
+// its own copy, from when the code object is loaded there until the process
+// ends, and every call on that device shares it.  In host code its name is
+// not a device address; the address comes from hipGetSymbolAddress, taken
+// once per device with that device current and kept.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(int device, uint8_t** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static uint8_t* addr[kMaxDevices] = {};
+    if (device < 0 || device >= kMaxDevices || !ptr) return hipErrorInvalidValue;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[device]) {
+        int cur = -1;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+        void* a = nullptr;
+        e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+        if (cur != device) {
+            const hipError_t r = hipSetDevice(cur);
+            if (e == hipSuccess) e = r;
+        }
+        if (e != hipSuccess) return e;
+        if (!a) return hipErrorInvalidSymbol;
+        addr[device] = (uint8_t*)a;
+    }
+    *ptr = addr[device];
+    return hipSuccess;
 }
 
 }  // namespace lmk

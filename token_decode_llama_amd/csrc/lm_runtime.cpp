@@ -142,6 +142,21 @@ int block_bytes(int qtype) { return qtype == kQ8_0 ? 34 : 18; }
 
 }  // namespace
 
+// Working memory of one step: the residual stream, q, the attention output,
+// the FFN hidden vector, the matrix-core path's activation digits, the
+// attention chunks' partial states and counts, and the LM head's per-workgroup
+// argmax candidates and counts.  The model's own buffers, or (the
+// allocation-free step) slices of the device scratch array.
+struct StepBufs {
+    float *x = nullptr, *q = nullptr, *o = nullptr, *h = nullptr;
+    uint8_t* xfrag = nullptr;
+    float* attn_part = nullptr;
+    int* attn_cnt = nullptr;
+    float* lm_pval = nullptr;
+    int* lm_pidx = nullptr;
+    int* lm_cnt = nullptr;
+};
+
 struct lm_model {
     lm_config cfg{};
     hipStream_t stream = nullptr;
@@ -190,7 +205,9 @@ struct lm_model {
     float* d_dbg = nullptr;               // debug dequant rows
 
     int n_cus = 0;
+    int device = 0;                       // the device current at creation
     int64_t dbg_floats = 0;
+    StepBufs sb;                          // the buffers the step being enqueued uses
 
     std::vector<uint8_t> layer_loaded;
     bool global_loaded = false;
@@ -517,6 +534,7 @@ extern "C" lm_status lm_model_create(const lm_config* cfg, void* hip_stream, lm_
         CREATE_HIP(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
         m->gemv_max_blocks = std::max(64, ncu * 4);
         m->n_cus = ncu;
+        m->device = dev;
     }
 
     const lm_config& c = *cfg;
@@ -567,6 +585,17 @@ extern "C" lm_status lm_model_create(const lm_config* cfg, void* hip_stream, lm_
     m->stage_bytes = std::min<int64_t>(64ll << 20, std::max<int64_t>(m->blob_bytes, m->lm_q_bytes + m->lm_sc_bytes));
     m->stage_bytes = std::max<int64_t>(m->stage_bytes, 4 * (m->H * 34 / 32 + 64));
     CREATE_TRY(host_alloc(m, (void**)&m->h_stage, m->stage_bytes, "upload staging"));
+
+    m->sb.x = m->d_x;
+    m->sb.q = m->d_q;
+    m->sb.o = m->d_o;
+    m->sb.h = m->d_h;
+    m->sb.xfrag = m->d_xfrag;
+    m->sb.attn_part = m->d_attn_part;
+    m->sb.attn_cnt = m->d_attn_cnt;
+    m->sb.lm_pval = m->d_lm_pval;
+    m->sb.lm_pidx = m->d_lm_pidx;
+    m->sb.lm_cnt = m->d_lm_cnt;
 
     // zero what must start at zero (counters, caches, positions)
     CREATE_HIP(hipMemsetAsync(m->d_lm_cnt, 0, (size_t)S * 4, m->stream));
@@ -1078,7 +1107,7 @@ static lm_status stream_copy(lm_model* m, int layer) {
 // fragments plus the MFMA GEMV (one read of the weights for all sequences).
 static hipError_t gemv(lm_model* m, GemvArgs a, int epi, int n_seq, hipStream_t st) {
     if (n_seq >= 2) {
-        a.xfrag = m->d_xfrag;
+        a.xfrag = m->sb.xfrag;
         return launch_gemv_batched(a, epi, n_seq, m->gemv_max_blocks, st);
     }
     return launch_gemv(a, epi, n_seq, m->gemv_max_blocks, st);
@@ -1094,7 +1123,7 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
     hipStream_t st = m->stream;
     {
         KTimer t(m, LM_K_EMBED);
-        if (want(m, LM_K_EMBED)) HIPTRY(m, launch_embed(m->d_embd, d_tok, (int)m->V, (int)m->H, m->d_x, n_seq, st));
+        if (want(m, LM_K_EMBED)) HIPTRY(m, launch_embed(m->d_embd, d_tok, (int)m->V, (int)m->H, m->sb.x, n_seq, st));
     }
     GemvArgs base{};
     base.qtype = c.qtype;
@@ -1111,7 +1140,7 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
     base.rope_sin = m->d_sin;
 
     AttnArgs at{};
-    at.q = m->d_q;
+    at.q = m->sb.q;
     at.kv_seq_stride = kv_stride;
     at.pos = step_pos;
     at.nq = (int)m->nq;
@@ -1122,9 +1151,9 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
     at.scale = (float)(1.0 / std::sqrt((double)m->hd));
     at.grid_chunks = m->opt_active ? attn_chunks_for(m, m->opt_need) : attn_grid_chunks(m, n_seq);
     at.tiles = attn_tiles(n_seq, (int)m->nkv, at.grid_chunks);
-    at.part = m->d_attn_part;
-    at.counter = m->d_attn_cnt;
-    at.out = m->d_o;
+    at.part = m->sb.attn_part;
+    at.counter = m->sb.attn_cnt;
+    at.out = m->sb.o;
 
     const int n_str = (int)m->str_list.size();     // streamed layers this step computes
     for (int i = 0; i < std::min(n_str, 2); ++i)
@@ -1139,7 +1168,7 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
         if (m->opt_active && l >= m->opt_limit) continue;
         if (layer_streamed(m, l)) HIPTRY(m, hipStreamWaitEvent(st, m->ev_copied[stream_slot(m, l)], 0));
         if (m->sim_on)                                  // the layer's input, for its similarity
-            HIPTRY(m, hipMemcpyAsync(m->d_xin, m->d_x, (size_t)n_seq * m->H * 4, hipMemcpyDeviceToDevice, st));
+            HIPTRY(m, hipMemcpyAsync(m->d_xin, m->sb.x, (size_t)n_seq * m->H * 4, hipMemcpyDeviceToDevice, st));
         const uint8_t* blob = layer_blob(m, l);
         const float* g_attn = m->d_norms + (int64_t)l * 2 * m->H;
         const float* g_ffn = g_attn + m->H;
@@ -1149,9 +1178,9 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
             KTimer t(m, LM_K_QKV);
             GemvArgs a = base;
             a.w = mat_at(m, blob, M_QKV);
-            a.xin = m->d_x; a.x_stride = (int)m->H;
+            a.xin = m->sb.x; a.x_stride = (int)m->H;
             a.norm_g = g_attn;
-            a.out = m->d_q; a.out_stride = (int)m->qrows;
+            a.out = m->sb.q; a.out_stride = (int)m->qrows;
             a.kcache = kc; a.vcache = vc;
             if (want(m, LM_K_QKV)) HIPTRY(m, gemv(m, a, EPI_QKV, n_seq, st));
         }
@@ -1165,28 +1194,28 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
             KTimer t(m, LM_K_WO);
             GemvArgs a = base;
             a.w = mat_at(m, blob, M_WO);
-            a.xin = m->d_o; a.x_stride = (int)m->qrows;
-            a.out = m->d_x; a.out_stride = (int)m->H;
+            a.xin = m->sb.o; a.x_stride = (int)m->qrows;
+            a.out = m->sb.x; a.out_stride = (int)m->H;
             if (want(m, LM_K_WO)) HIPTRY(m, gemv(m, a, EPI_RESID, n_seq, st));
         }
         {   // RMSNorm -> gate/up GEMV -> SwiGLU
             KTimer t(m, LM_K_GATEUP);
             GemvArgs a = base;
             a.w = mat_at(m, blob, M_GU);
-            a.xin = m->d_x; a.x_stride = (int)m->H;
+            a.xin = m->sb.x; a.x_stride = (int)m->H;
             a.norm_g = g_ffn;
-            a.out = m->d_h; a.out_stride = (int)m->F;
+            a.out = m->sb.h; a.out_stride = (int)m->F;
             if (want(m, LM_K_GATEUP)) HIPTRY(m, gemv(m, a, EPI_SWIGLU, n_seq, st));
         }
         {   // x += Wdown h
             KTimer t(m, LM_K_DOWN);
             GemvArgs a = base;
             a.w = mat_at(m, blob, M_DOWN);
-            a.xin = m->d_h; a.x_stride = (int)m->F;
-            a.out = m->d_x; a.out_stride = (int)m->H;
+            a.xin = m->sb.h; a.x_stride = (int)m->F;
+            a.out = m->sb.x; a.out_stride = (int)m->H;
             if (want(m, LM_K_DOWN)) HIPTRY(m, gemv(m, a, EPI_RESID, n_seq, st));
         }
-        if (m->sim_on) HIPTRY(m, launch_layer_cos(m->d_xin, m->d_x, (int)m->H, n_seq, m->d_sim + 2 * l, st));
+        if (m->sim_on) HIPTRY(m, launch_layer_cos(m->d_xin, m->sb.x, (int)m->H, n_seq, m->d_sim + 2 * l, st));
         if (layer_streamed(m, l)) {
             HIPTRY(m, hipEventRecord(m->ev_consumed[stream_slot(m, l)], st));
             const int nx = m->str_idx[l] + 2;
@@ -1207,12 +1236,12 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
         KTimer t(m, LM_K_LMHEAD);
         GemvArgs a = base;
         a.w = lm_head_mat(m);
-        a.xin = m->d_x; a.x_stride = (int)m->H;
+        a.xin = m->sb.x; a.x_stride = (int)m->H;
         a.norm_g = m->d_out_norm;
         a.out = d_logits; a.out_stride = (int)m->V;
-        a.part_val = m->d_lm_pval;
-        a.part_idx = m->d_lm_pidx;
-        a.counter = m->d_lm_cnt;
+        a.part_val = m->sb.lm_pval;
+        a.part_idx = m->sb.lm_pidx;
+        a.counter = m->sb.lm_cnt;
         a.argmax_out = d_argmax;
         // a timing-only replay of the LM head must not advance the positions
         a.pos_inc = m->only_kind < 0 && !(m->opt_active && !m->opt_advance) ? m->d_pos : nullptr;
@@ -1318,6 +1347,72 @@ extern "C" lm_status lm_decode_step_dev(lm_model* m, const int32_t* d_tokens, in
     if (st != LM_OK) return st;
     if (!d_tokens || !d_argmax) return fail(m, LM_E_ARG, "lm_decode_step_dev: d_tokens or d_argmax is NULL");
     st = run_step(m, n_seq, d_tokens, d_logits, d_argmax);
+    if (st != LM_OK) return st;
+    for (int s = 0; s < n_seq; ++s) m->pos[s] += 1;
+    return LM_OK;
+}
+
+// The step's working buffers for n_seq sequences as slices of one region at
+// base, each 256-byte aligned; returns the bytes they need (base == nullptr:
+// the size only).  The counts and the activation digits come first, so that
+// one clear covers what must start at zero: [0, *zero_bytes).
+static int64_t scratch_layout(const lm_model* m, int n_seq, uint8_t* base, StepBufs* b, int64_t* zero_bytes) {
+    int64_t off = 0;
+    auto take = [&](int64_t bytes) {
+        uint8_t* p = base ? base + off : nullptr;
+        off += (bytes + 255) / 256 * 256;
+        return p;
+    };
+    const int64_t S = n_seq;
+    StepBufs t;
+    t.attn_cnt = (int*)take(S * m->nkv * attn_cnt_lines(m->max_chunks) * kCntStride * 4);
+    t.lm_cnt = (int*)take(S * 4);
+    if (m->batched && n_seq >= 2) t.xfrag = take(xfrag_bytes(std::max<int64_t>({m->H, m->qrows, m->F})));
+    const int64_t zeroed = off;
+    t.x = (float*)take(S * m->H * 4);
+    t.q = (float*)take(S * m->qrows * 4);
+    t.o = (float*)take(S * m->qrows * 4);
+    t.h = (float*)take(S * m->F * 4);
+    t.attn_part = (float*)take(S * m->nq * m->max_chunks * (m->hd + 2) * 4);
+    t.lm_pval = (float*)take(S * m->gemv_max_blocks * 4);
+    t.lm_pidx = (int*)take(S * m->gemv_max_blocks * 4);
+    if (b) *b = t;
+    if (zero_bytes) *zero_bytes = zeroed;
+    return off;
+}
+
+extern "C" lm_status lm_decode_step_dev_noalloc(lm_model* m, const int32_t* d_tokens, int32_t n_seq,
+                                                float* d_logits, int32_t* d_argmax) {
+    if (!m) return LM_E_ARG;
+    lm_status st = check_ready(m, "lm_decode_step_dev_noalloc", n_seq);
+    if (st != LM_OK) return st;
+    if (!d_tokens || !d_argmax)
+        return fail(m, LM_E_ARG, "lm_decode_step_dev_noalloc: d_tokens or d_argmax is NULL");
+    if (m->streaming)
+        return fail(m, LM_E_STATE, "lm_decode_step_dev_noalloc: layers %d..%d are streamed; every layer must be "
+                    "resident (lm_set_residency with n_layers)", m->n_res, m->cfg.n_layers - 1);
+    const int64_t need = scratch_layout(m, n_seq, nullptr, nullptr, nullptr);
+    if (need > kNoAllocScratchBytes)
+        return fail(m, LM_E_ARG, "lm_decode_step_dev_noalloc: %d sequences with max_ctx %d need %lld bytes of "
+                    "scratch; the allocation-free step has %lld (use lm_decode_step_dev)", n_seq, m->cfg.max_ctx,
+                    (long long)need, (long long)kNoAllocScratchBytes);
+    uint8_t* base = nullptr;
+    const hipError_t e = noalloc_scratch(m->device, &base);
+    if (e != hipSuccess)
+        return fail(m, LM_E_HIP, "lm_decode_step_dev_noalloc: scratch address: %s", hipGetErrorString(e));
+    StepBufs sb;
+    int64_t zero_bytes = 0;
+    scratch_layout(m, n_seq, base, &sb, &zero_bytes);
+    // the array keeps the last call's contents (possibly another model's)
+    HIPTRY(m, launch_zero(base, zero_bytes, m->stream));
+    // eager launches (instantiating a graph would allocate), no timing events
+    const StepBufs own = m->sb;
+    const int timing = m->timing;
+    m->sb = sb;
+    m->timing = 0;
+    st = enqueue_step(m, n_seq, d_tokens, d_logits, d_argmax);
+    m->sb = own;
+    m->timing = timing;
     if (st != LM_OK) return st;
     for (int s = 0; s < n_seq; ++s) m->pos[s] += 1;
     return LM_OK;
