@@ -151,13 +151,13 @@ struct AttnArgs {
 hipError_t launch_embed(const uint16_t* tok_embd, const int* tokens, int vocab, int hidden,
                         float* x, int n_seq, hipStream_t st);
 hipError_t launch_gemv(const GemvArgs& a, int epi, int n_seq, int max_blocks, hipStream_t st);
-// 2..4 sequences: activation fragments (RMSNorm applied), then the MFMA GEMV
+// 2..4 sequences: the matrix-core GEMV (its activation digits computed in each
+// workgroup's prologue, or for wide inputs by a digit kernel into a.xfrag first)
 hipError_t launch_gemv_batched(const GemvArgs& a, int epi, int n_seq, int max_blocks, hipStream_t st);
-// Activation operands of the several-sequence GEMV (nb = K/32 blocks): digit
-// pairs [ceil(nb/2)][4][16] x 16 bytes, then the table: activation scales
-// [nb][16] fp32, then digit sums [nb][16] int32.
-constexpr int64_t xdig_table_offset(int64_t nb) { return (nb + 1) / 2 * 1024; }
-inline int64_t xfrag_bytes(int64_t K) { return xdig_table_offset(K / 32) + K / 32 * 128; }
+// Activation operands of the several-sequence GEMV for nb = K/32 blocks:
+// digits uint2 [nb][4 column groups][16 rows 4s+d], then activation scales
+// fp32 [nb][4 sequences], then digit sums int4 [nb][4 sequences].
+inline int64_t xfrag_bytes(int64_t K) { return K / 32 * (512 + 16 + 64); }
 int attn_tiles(int n_seq, int nkv, int max_chunks);
 hipError_t launch_attention(const AttnArgs& a, int n_seq, hipStream_t st);
 hipError_t launch_dequant(const QMat& w, int qtype, int row0, int n_rows, float* out,

@@ -532,88 +532,48 @@ hipError_t launch_gemv(const GemvArgs& a, int epi, int n_seq, int max_blocks, hi
 // ---------------------------------------------------------------------------
 // 2..4 sequences: dequant-GEMV as a dense contraction on the matrix cores
 // ---------------------------------------------------------------------------
-// v_mfma_i32_16x16x32_i8 contracts a 16-row x 32-column weight tile (one quant
-// block, its int8 quants - or Q4_0 nibbles as unsigned bytes - taken as they
-// are in HBM) with a 32 x 16 int8 activation tile.  The activations enter as
-// the integer digits of the one-sequence GEMV (per block b and sequence s,
-// X = rint(x * 127 * 2^16 / max|x_b|) = D2 * 2^16 + D1 * 2^8 + D0, signed
-// bytes), and the tile's 16 columns are (sequence, digit) pairs: column
-// j = 3 s + d, so one MFMA gives every digit's exact int32 dot product for up
-// to four sequences.  Operand layout (lane l, group g = l/16, index j = l%16):
-//   A: row j, columns 8g..8g+7;  B: column j, rows 8g..8g+7;
-//   D: rows 4g..4g+3, column j.
-// Each lane keeps an fp32 sum per (row, column): the block's int32 result
-// (Q4_0: minus 8 x the block's digit sum) times the row's block scale and the
-// block's activation scale.  After the K loop the three digit columns of a
-// sequence are combined (2^16 D2 + 2^8 D1 + D0) across lanes.
+// v_mfma_i32_16x16x32_i8 contracts a 16 x 32 int8 activation tile with a
+// 32-column x 16-row weight tile (one quant block of 16 weight rows, its int8
+// quants - or Q4_0 nibbles as unsigned bytes - as they are in HBM).  The
+// activations enter as the integer digits of the one-sequence GEMV (per block
+// b and sequence s, X = rint(x * 127 * 2^16 / max|x_b|) = D2 2^16 + D1 2^8 +
+// D0, signed bytes), and the activation tile's 16 rows are (sequence, digit)
+// slots: row 4s + d, slot d = 3 unused.  Operand layout (lane l, group
+// g = l/16, index j = l%16):
+//   A (digits): row j, block columns 8g..8g+7;
+//   B (weights): weight row j of the tile, block columns 8g..8g+7;
+//   D: rows 4g..4g+3 (sequence g's three digit sums and the unused slot),
+//      column j (weight row j).
+// So each lane holds one sequence's digit sums of one weight row and folds
+// them itself, block by block: y += d_b * sx_b * (2^16 S2 + 2^8 S1 + S0)
+// (Q4_0: S_k minus 8 times the block's digit sum, exactly, in int32 first).
 typedef int v4i_t __attribute__((ext_vector_type(4)));
 
-// Activation operands of the several-sequence GEMV (at a.xfrag; nb = K/32
-// blocks, np = ceil(nb/2) block pairs; layout also in lm_internal.h):
-//   digits [np][4 groups g][16 columns j] x 16 bytes: for the pair's two
-//     blocks, digit d of sequence s (column j = 3s+d) at the block's columns
-//     8g..8g+7, 8 bytes per block (the matrix-core B operand);
-//   table (at byte np x 1024): the block's activation scale max|x_b| /
-//     (127 x 2^16) of sequence s per column j, fp32 [nb][16], then column j's
-//     digit sum over the block's 32 columns, int32 [nb][16].
-// Columns j >= 3 x n_seq are never read.
-// A thread per 8 columns, four consecutive threads per block, every input
-// loaded once.  With a gain (RMSNorm inputs) one workgroup covers the whole
-// row (K / 8 threads, up to 1024: K <= 8192), so the sum of squares comes from
-// the same registers; without one, the grid splits K into 2048-column chunks.
-template <bool GAIN>
-__global__ __launch_bounds__(1024) void k_xdigits(const float* __restrict__ xin, int x_stride,
-                                                 const float* __restrict__ g, float eps, int K,
-                                                 uint8_t* __restrict__ xb) {
-    __shared__ float red[16];
-    const int s = blockIdx.y, tid = threadIdx.x;
-    const int nb = K >> 5;
-    const float* x = xin + (int64_t)s * x_stride;
-    uint2* dig = (uint2*)xb;
-    float* tsx = (float*)(xb + xdig_table_offset(nb));     // activation scales [nb][16]
-    int* tsum = (int*)(tsx + nb * 16);                     // digit sums [nb][16]
-    // K % 32 == 0 and blockDim.x % 4 == 0: the four threads of a block are all in or all out
-    const int c = blockIdx.x * blockDim.x + tid;    // 8 columns per thread
-    const bool in = c < K / 8;
-    const int cc = in ? c : 0;
-    float v[8];
-    const float4 v0 = *(const float4*)(x + 8 * cc), v1 = *(const float4*)(x + 8 * cc + 4);
-    v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
-    v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
-    if (GAIN) {
-        const float4 g0 = *(const float4*)(g + 8 * cc), g1 = *(const float4*)(g + 8 * cc + 4);
-        float ss = 0.f;
-        if (in) {
-            #pragma unroll
-            for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
-        }
-        // sum over the workgroup (blockDim.x / 64 wavefronts)
-        ss = wave_sum(ss);
-        if ((tid & 63) == 0) red[tid >> 6] = ss;
-        __syncthreads();
-        float tot = 0.f;
-        for (int w = 0; w < (int)(blockDim.x >> 6); ++w) tot += red[w];
-        const float scale = 1.0f / sqrtf(tot / (float)K + eps);
-        const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-        #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = v[e] * scale * gg[e];
-    }
+constexpr int kMbWaves = 8;        // wavefronts per workgroup (one workgroup per CU)
+constexpr int kMbGroup = 4;        // blocks per pipeline stage (whole fragments of both formats)
+constexpr int kMbLdsMaxK = 6144;   // widest input whose digits a workgroup computes into LDS
+
+// The digits of 8 consecutive inputs v (a quarter of a 32-column block; the
+// block's four quarters sit in lanes 4k..4k+3 of one wavefront): the three
+// digit planes packed 8 bytes each, the block's digit sums t[d] (over all 32
+// columns) and max|x_b| as the return value.
+__device__ __forceinline__ float block_digits(const float (&v)[8], uint2 (&w)[3], int (&t)[3]) {
     float m = 0.f;
     #pragma unroll
     for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
-    m = fmaxf(m, __shfl_xor(m, 1, 64));             // the block's four threads
+    m = fmaxf(m, __shfl_xor(m, 1, 64));
     m = fmaxf(m, __shfl_xor(m, 2, 64));
     const float f = m > 0.f ? 8323072.0f / m : 0.f;         // 127 * 2^16 / max|x_b|
-    uint32_t w[3][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}};
-    int t[3] = {0, 0, 0};
+    uint32_t p[3][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}};
+    t[0] = t[1] = t[2] = 0;
     #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int X = (int)rintf(v[e] * f);
         const int x1 = (X + 128) >> 8, x2 = (x1 + 128) >> 8;
         const int d0 = (int)(int8_t)(X & 255), d1 = (int)(int8_t)(x1 & 255);
-        w[0][e >> 2] |= (uint32_t)(d0 & 255) << (8 * (e & 3));
-        w[1][e >> 2] |= (uint32_t)(d1 & 255) << (8 * (e & 3));
-        w[2][e >> 2] |= (uint32_t)(x2 & 255) << (8 * (e & 3));
+        p[0][e >> 2] |= (uint32_t)(d0 & 255) << (8 * (e & 3));
+        p[1][e >> 2] |= (uint32_t)(d1 & 255) << (8 * (e & 3));
+        p[2][e >> 2] |= (uint32_t)(x2 & 255) << (8 * (e & 3));
         t[0] += d0;
         t[1] += d1;
         t[2] += x2;
@@ -622,130 +582,144 @@ __global__ __launch_bounds__(1024) void k_xdigits(const float* __restrict__ xin,
     for (int d = 0; d < 3; ++d) {
         t[d] += __shfl_xor(t[d], 1, 64);
         t[d] += __shfl_xor(t[d], 2, 64);
+        w[d] = make_uint2(p[d][0], p[d][1]);
     }
-    if (in) {
-        const int b = c >> 2, gq = c & 3;
-        const uint32_t sxb = __float_as_uint(m * (1.0f / 8323072.0f));
-        #pragma unroll
-        for (int d = 0; d < 3; ++d) {
-            dig[((int64_t)((b >> 1) * 4 + gq) * 16 + 3 * s + d) * 2 + (b & 1)] = make_uint2(w[d][0], w[d][1]);
-            if (gq == 0) {
-                tsx[(int64_t)b * 16 + 3 * s + d] = __uint_as_float(sxb);
-                tsum[(int64_t)b * 16 + 3 * s + d] = t[d];
-            }
-        }
+    return m;
+}
+
+// Activation operands (layout also in lm_internal.h, xfrag_bytes), for nb
+// blocks: digits uint2 [nb][4 groups g][16 rows 4s+d] (rows 4s+3 unused),
+// then the activation scales max|x_b| / (127 * 2^16) fp32 [nb][4 sequences],
+// then the digit sums int4 [nb][4 sequences] (S0, S1, S2, 0).
+__host__ __device__ constexpr int64_t mb_scales_offset(int64_t nb) { return nb * 512; }
+__host__ __device__ constexpr int64_t mb_sums_offset(int64_t nb) { return nb * 512 + nb * 16; }
+
+// Stores one item's digits (sequence s, columns 8c..8c+7) into the operand
+// layout at base (LDS or global).
+__device__ __forceinline__ void put_digits(uint8_t* base, int nb, int s, int c, const uint2 (&w)[3],
+                                           const int (&t)[3], float m) {
+    const int b = c >> 2, gq = c & 3;
+    uint2* dig = (uint2*)base;
+    #pragma unroll
+    for (int d = 0; d < 3; ++d) dig[(b * 4 + gq) * 16 + 4 * s + d] = w[d];
+    if (gq == 0) {
+        ((float*)(base + mb_scales_offset(nb)))[b * 4 + s] = m * (1.0f / 8323072.0f);
+        ((int4*)(base + mb_sums_offset(nb)))[b * 4 + s] = make_int4(t[0], t[1], t[2], 0);
     }
 }
 
-static hipError_t launch_xdigits(const GemvArgs& a, int n_seq, hipStream_t st) {
-    const int K = a.w.K;
-    if (a.norm_g) {
-        const int threads = ((K / 8 + 63) / 64) * 64;   // whole wavefronts, one pass over the row
-        if (threads > 1024) return hipErrorInvalidValue;
-        hipLaunchKernelGGL(k_xdigits<true>, dim3(1, n_seq), dim3(threads), 0, st, a.xin, a.x_stride, a.norm_g,
-                           a.eps, K, a.xfrag);
-    } else {
-        hipLaunchKernelGGL(k_xdigits<false>, dim3((K + 8 * kBlock - 1) / (8 * kBlock), n_seq), dim3(kBlock), 0, st,
-                           a.xin, a.x_stride, nullptr, a.eps, K, a.xfrag);
+// Digits of inputs wider than kMbLdsMaxK (the down projection's hidden
+// vector, no gain) into a.xfrag, for the four sequence slots (slots past
+// n_seq get zeros).  A thread per 8 columns and sequence slot.
+__global__ __launch_bounds__(kBlock) void k_xdigits(const float* __restrict__ xin, int x_stride, int K, int n_seq,
+                                                   uint8_t* __restrict__ xb) {
+    const int s = blockIdx.y, nb = K >> 5;
+    const int c = blockIdx.x * kBlock + threadIdx.x;       // 8 columns per thread
+    const bool in = c < K / 8;                             // K % 32 == 0: a block's four threads agree
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (in && s < n_seq) {
+        const float* x = xin + (int64_t)s * x_stride + 8 * c;
+        const float4 v0 = *(const float4*)x, v1 = *(const float4*)(x + 4);
+        v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
+        v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
     }
-    return hipGetLastError();
+    uint2 w[3];
+    int t[3];
+    const float m = block_digits(v, w, t);
+    if (in) put_digits(xb, nb, s, c, w, t, m);
 }
 
-// Several-sequence GEMV: k_gemv_mfma<QT, EPI, W, T, PRO>.  A workgroup of W
-// wavefronts takes units of T consecutive 16-row tiles (grid-stride); its
-// wavefronts split K in whole pipeline stages of kMbDepth blocks and reduce
-// through LDS.  The matrix op takes the activation digits as its first
-// operand (row = digit column 3s+d) and the weights as its second (column =
-// weight row), so a lane's four results are four digit columns of one weight
-// row, and each lane needs one weight scale per block.  Per stage a lane
-// loads its weight fragments (2 blocks per 16 bytes for Q8_0, 4 for Q4_0,
-// from the fragment copy: one contiguous 1 KiB per wavefront and group), its
-// row's 4 block scales (8 bytes), and the activation digit pairs, which serve
-// all T tiles; each block's activation scales and digit sums come from the
-// table, staged in LDS once per workgroup.
-// PRO (inputs of at most kProMaxK columns): no separate digit launch; every
-// workgroup computes the digit pairs and the table of all sequences into LDS
-// in its prologue, while its first weight loads are in flight, from x (times
-// the gain for RMSNorm inputs); the RMS factor of each sequence is then applied
-// to the finished dot products (its sum of squares is taken in the same pass).
-constexpr int kMbDepth = 4;    // blocks per pipeline stage
-constexpr int kProMaxK = 6144; // widest input the prologue mode stages in LDS
-
-template <int QT, int EPI, int W, int T, bool PRO>
-__global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
-    static_assert(!PRO || W == 16, "the prologue mode runs with 16 wavefronts");
-    // LDS: PRO: digit pairs [np][4][16] x 16 B, then the table; else the table only
-    extern __shared__ __align__(16) uint4 xlds[];
-    __shared__ __align__(16) float part[W][T][64][4];
-    __shared__ float ybuf[T][16][17];                       // wavefront 0's sums: (digit column, row)
-    __shared__ float ss_red[W][4];                          // PRO: per-wavefront sums of squares
-    __shared__ float wv_best[4][W];
-    __shared__ int wi_best[4][W];
+// Several-sequence GEMV: k_gemv_mb<QT, EPI, TW, XL>.  One workgroup of eight
+// wavefronts per CU owns a contiguous run of 16-row tiles; its wavefronts
+// split K (whole stages of kMbGroup blocks) and take the run TW tiles at a
+// time: per stage a lane loads, for each of the TW tiles, its weight
+// fragments (from the fragment copy: 1 KiB per wavefront, tile and fragment
+// group, contiguous) and its row's four block scales, and one activation
+// digit fragment per block that serves all TW tiles.  Two stages stay in
+// flight; the next round's first stage is requested before the round's
+// results are reduced.  A round ends with one LDS reduction over the
+// wavefronts, and wavefront t finishes tile t of the round (epilogue lane:
+// sequence g, tile row j; even rows take the row pair j, j+1).
+// XL: the workgroup computes the digits of every sequence into LDS in its
+// prologue (K <= kMbLdsMaxK), while its first stage is in flight, from x
+// (times the gain for RMSNorm inputs; the RMS factor of each sequence then
+// scales the finished dot products); else they come from a.xfrag (k_xdigits).
+template <int QT, int EPI, int TW, bool XL>
+__global__ __launch_bounds__(64 * kMbWaves) void k_gemv_mb(GemvArgs a) {
+    constexpr int NT = 64 * kMbWaves;
+    extern __shared__ __align__(16) uint8_t mb_lds[];
+    __shared__ float part[2][kMbWaves][TW][64];
+    __shared__ float ss_red[kMbWaves][4];
+    __shared__ float wv_best[kMbWaves][4];
+    __shared__ int wi_best[kMbWaves][4];
     __shared__ int s_last;
 
     const int K = a.w.K, N = a.w.N, nb = K >> 5;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, j = lane & 15;
-    const int n_tiles = (N + 15) >> 4, n_units = (n_tiles + T - 1) / T;
-    // each wavefront's K range is whole pipeline stages (kMbDepth blocks)
-    const int nbq = ((nb + W - 1) / W + kMbDepth - 1) / kMbDepth * kMbDepth;
-    const int b_lo = min(wave * nbq, nb), b_hi = min(b_lo + nbq, nb);
-    constexpr int PER = QT == kQ8_0 ? 2 : 4;        // blocks per 16-byte weight fragment
-    constexpr int NW = kMbDepth / PER;               // weight fragments per stage and tile
-    static_assert(kMbDepth % 4 == 0, "a stage is whole fragments of both formats and whole digit pairs");
-    const int ngrp = (nb + PER - 1) / PER, npair = (nb + 1) >> 1, ng4 = (nb + 3) >> 2;
-    const uint4* xd = (const uint4*)a.xfrag + (g * 16 + j);     // this lane's digit pairs, stride 64
-    const uint2* xt = (const uint2*)(a.xfrag + xdig_table_offset(nb));
-    uint2* xtab = (uint2*)(PRO ? (uint8_t*)xlds + xdig_table_offset(nb) : (uint8_t*)xlds);
-    const float* xsx = (const float*)xtab;                       // LDS table: scales, then digit sums
-    const int* xsum = (const int*)(xsx + nb * 16);
-    const uint4* xdl = xlds + (g * 16 + j);                      // PRO: digit pairs in LDS, stride 64
+    const int n_tiles = (N + 15) >> 4;
+    const int G = gridDim.x;
+    // this workgroup's tiles: blockIdx.x + G i for i = 0 .. t_end-1, so that at
+    // any time the workgroups read neighbouring tiles (one window of the matrix)
+    const int t_begin = 0;
+    const int t_end = ((int)blockIdx.x < n_tiles) ? (n_tiles - 1 - (int)blockIdx.x) / G + 1 : 0;
+    auto tile_at = [&](int i) { return (int)blockIdx.x + G * i; };
+    const int ng4 = (nb + kMbGroup - 1) / kMbGroup;
+    const int k_lo = wave * ng4 / kMbWaves, k_hi = (wave + 1) * ng4 / kMbWaves;
+    constexpr int PER = QT == kQ8_0 ? 2 : 4;         // blocks per 16-byte weight fragment
+    constexpr int NF = kMbGroup / PER;               // fragments per stage and tile
+    const int ngrp = (nb + PER - 1) / PER;
 
-    float best_v = -FLT_MAX;
-    int best_i = INT_MAX;
+    // LDS: XL: digits, scales, sums (the xfrag layout); else the scales and sums only
+    const int64_t tab_off = XL ? mb_scales_offset(nb) : 0;
 
+    constexpr int XS = XL ? 1 : kMbGroup;              // digit operands a stage carries (global digits)
     struct Stage {
-        uint4 w[T][NW];              // weight fragments (kMbDepth blocks of this lane's row) per tile
-        uint2 sc[T];                 // this lane's row's scales of the kMbDepth blocks, per tile
-        uint4 x[PRO ? 1 : kMbDepth / 2];   // digit pairs of this lane's digit column (PRO: LDS)
+        uint4 w[TW][NF];    // weight fragments of this lane's row, per tile
+        uint2 sc[TW];       // the row's scales of the stage's four blocks, per tile
+        uint2 x[XS];        // (digits from a.xfrag) this lane's digit fragment of each block
     };
-    auto load = [&](int unit, int b0, Stage& st) {
+    // tiles t0.. t0+TW-1 of the run (clamped to its last tile), stage k.
+    // Every address is clamped, so a stage's loads are issued unconditionally
+    // and the compiler's in-order load counters stay exact.
+    auto load = [&](int t0, int k, Stage& st) {
         #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const int tile = min(unit * T + t, n_tiles - 1);      // clamped: always in bounds
+        for (int t = 0; t < TW; ++t) {
+            const int tile = tile_at(min(t0 + t, t_end - 1));
             const uint4* qf = (const uint4*)a.w.qf + (int64_t)tile * ngrp * 64 + lane;
             #pragma unroll
-            for (int f = 0; f < NW; ++f) {
-                const int grp = min(b0 / PER + f, ngrp - 1);
-                st.w[t][f] = qf[(int64_t)grp * 64];
-            }
-            st.sc[t] = *(const uint2*)(a.w.sct + (((int64_t)tile * ng4 + (b0 >> 2)) * 16 + j) * 4);
+            for (int f = 0; f < NF; ++f) st.w[t][f] = qf[(int64_t)min(k * NF + f, ngrp - 1) * 64];
+            st.sc[t] = *(const uint2*)(a.w.sct + (((int64_t)tile * ng4 + k) * 16 + j) * 4);
         }
-        if (!PRO) {
+        if constexpr (!XL) {
             #pragma unroll
-            for (int h = 0; h < kMbDepth / 2; ++h) {
-                const int pr = min((b0 >> 1) + h, npair - 1);
-                st.x[h] = xd[(int64_t)pr * 64];
+            for (int u = 0; u < XS; ++u) {
+                const int b = min(k * kMbGroup + u, nb - 1);
+                st.x[u] = ((const uint2*)a.xfrag)[(b * 4 + g) * 16 + j];
             }
         }
     };
-    float acc[T][4];
-    auto compute = [&](int b0, const Stage& st) {
+    float acc[TW];
+    auto compute = [&](int k, const Stage& st) {
         #pragma unroll
-        for (int u = 0; u < kMbDepth; ++u) {
-            if (b0 + u >= b_hi) break;
-            const uint4 xp = PRO ? xdl[((b0 + u) >> 1) * 64] : st.x[PRO ? 0 : (u >> 1)];
-            const long xv = (u & 1) ? (long)(((uint64_t)xp.w << 32) | xp.z) : (long)(((uint64_t)xp.y << 32) | xp.x);
-            // activation scales (and digit sums) of this lane's four result columns 4g..4g+3
-            const float4 sx = *(const float4*)&xsx[(b0 + u) * 16 + 4 * g];
-            int4 ts = make_int4(0, 0, 0, 0);
-            if (QT == kQ4_0) ts = *(const int4*)&xsum[(b0 + u) * 16 + 4 * g];
+        for (int u = 0; u < kMbGroup; ++u) {
+            const int b = k * kMbGroup + u;
+            if (b >= nb) break;
+            uint2 xp;
+            float sx;
+            int4 T = make_int4(0, 0, 0, 0);
+            if constexpr (XL) xp = ((const uint2*)mb_lds)[(b * 4 + g) * 16 + j];
+            else xp = st.x[u % XS];
+            // the scales and sums sit in LDS in both modes (XL: past the digits)
+            sx = ((const float*)(mb_lds + tab_off))[b * 4 + g];
+            if (QT == kQ4_0) T = ((const int4*)(mb_lds + tab_off + (int64_t)nb * 16))[b * 4 + g];
+            const long xv = (long)(((uint64_t)xp.y << 32) | xp.x);
             #pragma unroll
-            for (int t = 0; t < T; ++t) {
+            for (int t = 0; t < TW; ++t) {
                 uint2 wa;
                 if (QT == kQ8_0) {
-                    const uint4 f = st.w[t][u / 2];
+                    const uint4 f = st.w[t][u >> 1];
                     wa = (u & 1) ? make_uint2(f.z, f.w) : make_uint2(f.x, f.y);
                 } else {
                     // 4 bytes: columns 8g+i in the low nibbles, 8g+4+i in the high ones
@@ -757,293 +731,242 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
                 v4i_t c = {0, 0, 0, 0};
                 c = __builtin_amdgcn_mfma_i32_16x16x32_i8(xv, wv, c, 0, 0, 0);
                 if (QT == kQ4_0) {                           // nibble n = q + 8
-                    c[0] -= 8 * ts.x;
-                    c[1] -= 8 * ts.y;
-                    c[2] -= 8 * ts.z;
-                    c[3] -= 8 * ts.w;
+                    c[0] -= 8 * T.x;
+                    c[1] -= 8 * T.y;
+                    c[2] -= 8 * T.z;
                 }
                 const uint2 sc = st.sc[t];
                 const float d = h2f((uint16_t)(u == 0 ? (sc.x & 0xFFFF) : u == 1 ? (sc.x >> 16)
                                                 : u == 2 ? (sc.y & 0xFFFF) : (sc.y >> 16)));
-                acc[t][0] = fmaf(d * sx.x, (float)c[0], acc[t][0]);
-                acc[t][1] = fmaf(d * sx.y, (float)c[1], acc[t][1]);
-                acc[t][2] = fmaf(d * sx.z, (float)c[2], acc[t][2]);
-                acc[t][3] = fmaf(d * sx.w, (float)c[3], acc[t][3]);
+                acc[t] = fmaf(d * sx, combine_digits(c[0], c[1], c[2]), acc[t]);
             }
         }
     };
 
-    // the first unit's first stage goes out before the table is staged
     Stage sa, sb;
-    int unit = blockIdx.x;
-    const bool go0 = unit < n_units && b_lo < b_hi;
-    if (PRO) {
-        // the digits of every sequence: an item per (sequence, 8 columns), four
-        // consecutive items per block (all active or all idle together).  Every
-        // item's inputs are requested first, then the first weight stage.
-        constexpr int MAXI = (4 * (kProMaxK / 8) + 64 * W - 1) / (64 * W);
-        const int cpr = K >> 3, n_items = a.n_seq * cpr;
+    const bool has_k = k_lo < k_hi;
+    if (has_k && t_begin < t_end) load(t_begin, k_lo, sa);
+
+    if constexpr (!XL) {
+        // the activation scales and digit sums of every block (nb x 80 bytes,
+        // written by k_xdigits) into LDS; the first stage stays in flight
+        const int n16 = nb * 5;                             // 16-byte pieces
+        const uint4* src = (const uint4*)(a.xfrag + mb_scales_offset(nb));
+        for (int i = tid; i < n16; i += NT) ((uint4*)mb_lds)[i] = src[i];
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+
+    // ---- prologue (XL): an item per (8 columns, sequence slot); the four
+    // slots of a column group in one thread, so the gain is read once
+    float rms = 1.f;            // the RMS factor of this lane's sequence g
+    if constexpr (XL) {
+        constexpr int MAXI = (kMbLdsMaxK / 8 + NT - 1) / NT;
+        const int cpr = K >> 3;
         const bool gain = a.norm_g != nullptr;
-        float4 xv[MAXI][2], gv[MAXI][2];
-        #pragma unroll
-        for (int i = 0; i < MAXI; ++i) {
-            const int it = tid + i * 64 * W;
-            const int sI = it < n_items ? it / cpr : 0, c = it < n_items ? it - sI * cpr : 0;
-            const float* xs = a.xin + (int64_t)sI * a.x_stride + 8 * c;
-            xv[i][0] = *(const float4*)xs;
-            xv[i][1] = *(const float4*)(xs + 4);
-            if (gain) {
-                gv[i][0] = *(const float4*)(a.norm_g + 8 * c);
-                gv[i][1] = *(const float4*)(a.norm_g + 8 * c + 4);
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        if (go0) load(unit, b_lo, sa);
         float ssq[4] = {0.f, 0.f, 0.f, 0.f};
-        uint2* dig = (uint2*)xlds;
         #pragma unroll
         for (int i = 0; i < MAXI; ++i) {
-            const int it = tid + i * 64 * W;
-            const bool in = it < n_items;
-            const int sI = in ? it / cpr : 0, c = in ? it - sI * cpr : 0;
-            float v[8] = {xv[i][0].x, xv[i][0].y, xv[i][0].z, xv[i][0].w,
-                          xv[i][1].x, xv[i][1].y, xv[i][1].z, xv[i][1].w};
+            const int c = tid + i * NT;
+            if (i > 0 && c - (tid & 3) >= cpr) break;       // (whole blocks, uniform per block)
+            const bool in = c < cpr;
+            const int cc = in ? c : 0;
+            float4 gv0 = make_float4(1.f, 1.f, 1.f, 1.f), gv1 = gv0;
             if (gain) {
-                float q = 0.f;
-                #pragma unroll
-                for (int e = 0; e < 8; ++e) q = fmaf(v[e], v[e], q);
-                if (in) {
-                    ssq[0] += sI == 0 ? q : 0.f;
-                    ssq[1] += sI == 1 ? q : 0.f;
-                    ssq[2] += sI == 2 ? q : 0.f;
-                    ssq[3] += sI == 3 ? q : 0.f;
+                gv0 = *(const float4*)(a.norm_g + 8 * cc);
+                gv1 = *(const float4*)(a.norm_g + 8 * cc + 4);
+            }
+            float4 xv[4][2];
+            #pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const float* xs = a.xin + (int64_t)min(s, a.n_seq - 1) * a.x_stride + 8 * cc;
+                xv[s][0] = *(const float4*)xs;
+                xv[s][1] = *(const float4*)(xs + 4);
+            }
+            #pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const bool live = in && s < a.n_seq;
+                float v[8] = {xv[s][0].x, xv[s][0].y, xv[s][0].z, xv[s][0].w,
+                              xv[s][1].x, xv[s][1].y, xv[s][1].z, xv[s][1].w};
+                if (!live) {
+                    #pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = 0.f;
                 }
-                const float gg[8] = {gv[i][0].x, gv[i][0].y, gv[i][0].z, gv[i][0].w,
-                                     gv[i][1].x, gv[i][1].y, gv[i][1].z, gv[i][1].w};
-                #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] *= gg[e];
-            }
-            float m = 0.f;
-            #pragma unroll
-            for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
-            m = fmaxf(m, __shfl_xor(m, 1, 64));
-            m = fmaxf(m, __shfl_xor(m, 2, 64));
-            const float f = m > 0.f ? 8323072.0f / m : 0.f;     // 127 * 2^16 / max|x_b|
-            uint32_t w[3][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}};
-            int tq[3] = {0, 0, 0};
-            #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int X = (int)rintf(v[e] * f);
-                const int x1 = (X + 128) >> 8, x2 = (x1 + 128) >> 8;
-                const int d0 = (int)(int8_t)(X & 255), d1 = (int)(int8_t)(x1 & 255);
-                w[0][e >> 2] |= (uint32_t)(d0 & 255) << (8 * (e & 3));
-                w[1][e >> 2] |= (uint32_t)(d1 & 255) << (8 * (e & 3));
-                w[2][e >> 2] |= (uint32_t)(x2 & 255) << (8 * (e & 3));
-                tq[0] += d0;
-                tq[1] += d1;
-                tq[2] += x2;
-            }
-            #pragma unroll
-            for (int d = 0; d < 3; ++d) {
-                tq[d] += __shfl_xor(tq[d], 1, 64);
-                tq[d] += __shfl_xor(tq[d], 2, 64);
-            }
-            if (in) {
-                const int b = c >> 2, gq = c & 3;
-                const uint32_t sxb = __float_as_uint(m * (1.0f / 8323072.0f));
-                #pragma unroll
-                for (int d = 0; d < 3; ++d) {
-                    dig[(((b >> 1) * 4 + gq) * 16 + 3 * sI + d) * 2 + (b & 1)] = make_uint2(w[d][0], w[d][1]);
-                    if (gq == 0) {
-                        ((float*)xtab)[b * 16 + 3 * sI + d] = __uint_as_float(sxb);
-                        ((int*)xtab)[nb * 16 + b * 16 + 3 * sI + d] = tq[d];
-                    }
+                if (gain) {
+                    #pragma unroll
+                    for (int e = 0; e < 8; ++e) ssq[s] = fmaf(v[e], v[e], ssq[s]);
+                    v[0] *= gv0.x; v[1] *= gv0.y; v[2] *= gv0.z; v[3] *= gv0.w;
+                    v[4] *= gv1.x; v[5] *= gv1.y; v[6] *= gv1.z; v[7] *= gv1.w;
                 }
+                uint2 w[3];
+                int t[3];
+                const float m = block_digits(v, w, t);
+                if (in) put_digits(mb_lds, nb, s, c, w, t, m);
             }
         }
-        if (a.norm_g) {
+        if (gain) {
             #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float t = wave_sum(ssq[q]);
-                if (lane == 0) ss_red[wave][q] = t;
+            for (int s = 0; s < 4; ++s) {
+                const float t = wave_sum(ssq[s]);
+                if (lane == 0) ss_red[wave][s] = t;
             }
         }
         // LDS stores visible to the workgroup; the weight loads stay in flight
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    } else {
-        constexpr int XT = 8;                        // table entries per thread per round
-        uint2 tv[XT];
-        #pragma unroll
-        for (int r = 0; r < XT; ++r) {
-            const int i = min(tid + r * 64 * W, nb * 16 - 1);
-            tv[r] = xt[i];
-        }
-        if (go0) load(unit, b_lo, sa);
-        #pragma unroll
-        for (int r = 0; r < XT; ++r) {
-            const int i = tid + r * 64 * W;
-            if (i < nb * 16) xtab[i] = tv[r];
-        }
-        for (int i = tid + XT * 64 * W; i < nb * 16; i += 64 * W) xtab[i] = xt[i];
-        // LDS stores visible to the workgroup; the weight loads stay in flight
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    }
-    // PRO with a gain: RMSNorm factor of each sequence, applied to the finished sums
-    // the epilogue lane (sequence es = lane / 16, tile row er = lane % 16; even
-    // rows take a row pair); PRO with a gain: that sequence's RMSNorm factor
-    const int es = g, er = j;
-    float rms = 1.f;
-    if (PRO && a.norm_g) {
-        float tot = 0.f;
-        for (int w = 0; w < W; ++w) tot += ss_red[w][es];
-        rms = 1.0f / sqrtf(tot / (float)K + a.eps);
-    }
-    for (; unit < n_units; unit += gridDim.x) {
-        #pragma unroll
-        for (int t = 0; t < T; ++t)
+        if (gain) {
+            float tot = 0.f;
             #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[t][i] = 0.f;
-        // two stages in flight: the next stage's loads are issued before this one
-        // computes.  The unit's first stage is already in `sa` (requested before
-        // the prologue, or at the end of the previous unit's K loop).
-        if (b_lo < b_hi) {
-            int b0 = b_lo;
-            for (;;) {
-                const bool more = b0 + kMbDepth < b_hi;
-                if (more) load(unit, b0 + kMbDepth, sb);
-                compute(b0, sa);
-                b0 += kMbDepth;
-                if (!more) break;
-                const bool more2 = b0 + kMbDepth < b_hi;
-                if (more2) load(unit, b0 + kMbDepth, sa);
-                compute(b0, sb);
-                b0 += kMbDepth;
-                if (!more2) break;
-            }
-            // the next unit's first stage streams in during this unit's epilogue
-            if (unit + (int)gridDim.x < n_units) load(unit + gridDim.x, b_lo, sa);
+            for (int w = 0; w < kMbWaves; ++w) tot += ss_red[w][g];
+            rms = 1.0f / sqrtf(tot / (float)K + a.eps);
         }
+    }
+
+    float best_v = -FLT_MAX;
+    int best_i = INT_MAX;
+    #pragma unroll
+    for (int t = 0; t < TW; ++t) acc[t] = 0.f;
+    // end of round rq (tiles t0..t0+TW-1): one LDS reduction over the
+    // wavefronts, wavefront t finishes tile t.  Two partial buffers: round
+    // rq+1 writes the other one, and round rq+2 this one only after every
+    // wavefront has passed round rq+1's barrier, its reduction done.
+    auto end_round = [&](int rq, int t0) {
         #pragma unroll
-        for (int t = 0; t < T; ++t)
-            *(float4*)&part[wave][t][lane][0] = make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+        for (int t = 0; t < TW; ++t) {
+            part[rq & 1][wave][t][lane] = acc[t];
+            acc[t] = 0.f;
+        }
         __syncthreads();
-        if (wave == 0) {
-            // sum over the wavefronts; result i of lane (g, j) is digit column 4g+i of row j
+        if (wave < TW && t0 + wave < t_end) {
+            const int tile = tile_at(t0 + wave);
+            float y = 0.f;
             #pragma unroll
-            for (int t = 0; t < T; ++t) {
-                float y[4] = {0.f, 0.f, 0.f, 0.f};
-                #pragma unroll
-                for (int w = 0; w < W; ++w) {
-                    const float4 v = *(const float4*)&part[w][t][lane][0];
-                    y[0] += v.x; y[1] += v.y; y[2] += v.z; y[3] += v.w;
-                }
-                #pragma unroll
-                for (int i = 0; i < 4; ++i) ybuf[t][4 * g + i][j] = y[i];
-            }
-            // (one wavefront writes and reads ybuf: its LDS operations stay in order)
-        }
-        #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const int tile = unit * T + t;
-            if (wave == 0 && es < a.n_seq && (er & 1) == 0 && tile < n_tiles) {
-                const int s = es;
-                {
-                    // a sequence's three digit columns 3s, 3s+1, 3s+2: 2^16 D2 + 2^8 D1 + D0
-                    const float* c0 = &ybuf[t][3 * s][0];
-                    const float* c1 = &ybuf[t][3 * s + 1][0];
-                    const float* c2 = &ybuf[t][3 * s + 2][0];
-                    const int r0 = tile * 16 + er;               // rows r0, r0 + 1 (a RoPE / gate-up pair)
-                    const float y0 = fmaf(c2[er], 65536.0f, fmaf(c1[er], 256.0f, c0[er])) * rms;
-                    const float y1 = fmaf(c2[er + 1], 65536.0f, fmaf(c1[er + 1], 256.0f, c0[er + 1])) * rms;
-                    if (EPI == EPI_QKV) {
-                        const int p = a.pos[s];
-                        const int hd = a.head_dim;
-                        if (r0 < a.q_rows + a.kv_rows) {
-                            const int rr = r0 < a.q_rows ? r0 : r0 - a.q_rows;
-                            const int pi = (rr % hd) >> 1;
-                            const float cs = a.rope_cos[(int64_t)p * (hd >> 1) + pi];
-                            const float sn = a.rope_sin[(int64_t)p * (hd >> 1) + pi];
-                            const float z0 = y0 * cs - y1 * sn;
-                            const float z1 = y0 * sn + y1 * cs;
-                            if (r0 < a.q_rows) {
-                                *(float2*)(a.out + (int64_t)s * a.out_stride + r0) = make_float2(z0, z1);
-                            } else {
-                                __half2* dst = (__half2*)(a.kcache + (int64_t)s * a.kv_seq_stride +
-                                                          ((int64_t)(rr / hd) * a.max_ctx + p) * hd + (rr % hd));
-                                *dst = __floats2half2_rn(z0, z1);
-                            }
+            for (int w = 0; w < kMbWaves; ++w) y += part[rq & 1][w][wave][lane];
+            y *= rms;
+            const float y1 = __shfl_down(y, 1, 16);           // row j + 1 of the same sequence
+            const int s = g, r0 = tile * 16 + j;               // rows r0, r0 + 1 (a RoPE / gate-up pair)
+            if (s < a.n_seq && (j & 1) == 0) {
+                const float y0 = y;
+                if (EPI == EPI_QKV) {
+                    const int p = a.pos[s];
+                    const int hd = a.head_dim;
+                    if (r0 < a.q_rows + a.kv_rows) {
+                        const int rr = r0 < a.q_rows ? r0 : r0 - a.q_rows;
+                        const int pi = (rr % hd) >> 1;
+                        const float cs = a.rope_cos[(int64_t)p * (hd >> 1) + pi];
+                        const float sn = a.rope_sin[(int64_t)p * (hd >> 1) + pi];
+                        const float z0 = y0 * cs - y1 * sn;
+                        const float z1 = y0 * sn + y1 * cs;
+                        if (r0 < a.q_rows) {
+                            *(float2*)(a.out + (int64_t)s * a.out_stride + r0) = make_float2(z0, z1);
                         } else {
-                            const int rr = r0 - a.q_rows - a.kv_rows;
-                            __half2* dst = (__half2*)(a.vcache + (int64_t)s * a.kv_seq_stride +
+                            __half2* dst = (__half2*)(a.kcache + (int64_t)s * a.kv_seq_stride +
                                                       ((int64_t)(rr / hd) * a.max_ctx + p) * hd + (rr % hd));
-                            *dst = __floats2half2_rn(y0, y1);
+                            *dst = __floats2half2_rn(z0, z1);
                         }
-                    } else if (EPI == EPI_RESID) {
-                        float* xo = a.out + (int64_t)s * a.out_stride + r0;
-                        float2 v = *(float2*)xo;
-                        v.x += y0;
-                        v.y += y1;
-                        *(float2*)xo = v;
-                    } else if (EPI == EPI_SWIGLU) {
-                        const float sg = y0 / (1.0f + __expf(-y0));
-                        a.out[(int64_t)s * a.out_stride + (r0 >> 1)] = sg * y1;
-                    } else {  // EPI_LOGITS: the vocabulary may end inside a tile or a pair
-                        if (r0 < N) {
-                            if (a.out) a.out[(int64_t)s * a.out_stride + r0] = y0;
-                            better(best_v, best_i, y0, r0);
-                        }
-                        if (r0 + 1 < N) {
-                            if (a.out) a.out[(int64_t)s * a.out_stride + r0 + 1] = y1;
-                            better(best_v, best_i, y1, r0 + 1);
-                        }
+                    } else {
+                        const int rr = r0 - a.q_rows - a.kv_rows;
+                        __half2* dst = (__half2*)(a.vcache + (int64_t)s * a.kv_seq_stride +
+                                                  ((int64_t)(rr / hd) * a.max_ctx + p) * hd + (rr % hd));
+                        *dst = __floats2half2_rn(y0, y1);
+                    }
+                } else if (EPI == EPI_RESID) {
+                    float* xo = a.out + (int64_t)s * a.out_stride + r0;
+                    float2 v = *(float2*)xo;
+                    v.x += y0;
+                    v.y += y1;
+                    *(float2*)xo = v;
+                } else if (EPI == EPI_SWIGLU) {
+                    const float sg = y0 / (1.0f + __expf(-y0));
+                    a.out[(int64_t)s * a.out_stride + (r0 >> 1)] = sg * y1;
+                } else {  // EPI_LOGITS: the vocabulary may end inside a tile or a pair
+                    if (r0 < N) {
+                        if (a.out) a.out[(int64_t)s * a.out_stride + r0] = y0;
+                        better(best_v, best_i, y0, r0);
+                    }
+                    if (r0 + 1 < N) {
+                        if (a.out) a.out[(int64_t)s * a.out_stride + r0 + 1] = y1;
+                        better(best_v, best_i, y1, r0 + 1);
                     }
                 }
             }
         }
-        __syncthreads();
+    };
+
+    const int n_rounds = (t_end - t_begin + TW - 1) / TW;
+    if (has_k) {
+        // steps i = 0 .. S-1: round i / n_k, stage k_lo + i % n_k; the next
+        // step's stage is requested before this one computes (the last
+        // step's request repeats it: clamped, so the load count is exact)
+        const int n_k = k_hi - k_lo, S = n_rounds * n_k;
+        auto issue = [&](int i, Stage& st) {
+            const int ic = min(i, S - 1);
+            const int rq = ic / n_k;
+            load(t_begin + rq * TW, k_lo + (ic - rq * n_k), st);
+        };
+        auto run = [&](int i, const Stage& st) {
+            const int rq = i / n_k, k = k_lo + (i - rq * n_k);
+            compute(k, st);
+            if (k == k_hi - 1) end_round(rq, t_begin + rq * TW);
+        };
+        for (int i = 0; i < S; i += 2) {
+            issue(i + 1, sb);
+            run(i, sa);
+            if (i + 1 >= S) break;
+            issue(i + 2, sa);
+            run(i + 1, sb);
+        }
+    } else {
+        for (int rq = 0; rq < n_rounds; ++rq) end_round(rq, t_begin + rq * TW);
     }
 
     if (EPI == EPI_LOGITS) {
-        // sequence s's candidates sit in lanes 16s .. 16s+15 of wavefront 0
-        if (wave == 0) {
-            float bv = best_v;
-            int bi = best_i;
-            #pragma unroll
-            for (int off = 1; off < 16; off <<= 1) {
-                const float ov = __shfl_xor(bv, off, 64);
-                const int oi = __shfl_xor(bi, off, 64);
-                better(bv, bi, ov, oi);
-            }
-            if (er == 0 && es < a.n_seq) {      // handed over as in lm_device.h
-                st_dev(&a.part_val[(int64_t)es * gridDim.x + blockIdx.x], bv);
-                st_dev(&a.part_idx[(int64_t)es * gridDim.x + blockIdx.x], bi);
-            }
+        // this workgroup's best row per sequence: over the tile rows (lanes j
+        // of group g), then the wavefronts; handed to the last workgroup as the
+        // attention chunks hand over their states (lm_device.h)
+        #pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+            const float ov = __shfl_xor(best_v, off, 64);
+            const int oi = __shfl_xor(best_i, off, 64);
+            better(best_v, best_i, ov, oi);
+        }
+        if (j == 0) {
+            wv_best[wave][g] = best_v;
+            wi_best[wave][g] = best_i;
+        }
+        __syncthreads();
+        if (tid < a.n_seq) {
+            float bv = wv_best[0][tid];
+            int bi = wi_best[0][tid];
+            for (int w = 1; w < kMbWaves; ++w) better(bv, bi, wv_best[w][tid], wi_best[w][tid]);
+            st_dev(&a.part_val[(int64_t)tid * G + blockIdx.x], bv);
+            st_dev(&a.part_idx[(int64_t)tid * G + blockIdx.x], bi);
         }
         drain_vm();
         __syncthreads();
-        if (tid == 0) s_last = count_arrive(&a.counter[0], (int)gridDim.x);
+        if (tid == 0) s_last = count_arrive(&a.counter[0], G);
         __syncthreads();
         if (s_last) {
             for (int s = 0; s < a.n_seq; ++s) {
                 float bv = -FLT_MAX;
                 int bi = INT_MAX;
-                for (int i = tid; i < (int)gridDim.x; i += 64 * W)
-                    better(bv, bi, ld_dev(&a.part_val[(int64_t)s * gridDim.x + i]),
-                           ld_dev(&a.part_idx[(int64_t)s * gridDim.x + i]));
+                for (int i = tid; i < G; i += NT)
+                    better(bv, bi, ld_dev(&a.part_val[(int64_t)s * G + i]), ld_dev(&a.part_idx[(int64_t)s * G + i]));
                 #pragma unroll
                 for (int off = 32; off > 0; off >>= 1) {
                     const float ov = __shfl_xor(bv, off, 64);
                     const int oi = __shfl_xor(bi, off, 64);
                     better(bv, bi, ov, oi);
                 }
-                if (lane == 0) { wv_best[s][wave] = bv; wi_best[s][wave] = bi; }
+                if (lane == 0) {
+                    wv_best[wave][s] = bv;
+                    wi_best[wave][s] = bi;
+                }
             }
             __syncthreads();
             if (tid == 0) {
                 for (int s = 0; s < a.n_seq; ++s) {
-                    float bv = wv_best[s][0];
-                    int bi = wi_best[s][0];
-                    for (int w = 1; w < W; ++w) better(bv, bi, wv_best[s][w], wi_best[s][w]);
+                    float bv = wv_best[0][s];
+                    int bi = wi_best[0][s];
+                    for (int w = 1; w < kMbWaves; ++w) better(bv, bi, wv_best[w][s], wi_best[w][s]);
                     a.argmax_out[s] = bi;
                     if (a.pos_inc) a.pos_inc[s] += 1;
                 }
@@ -1052,57 +975,58 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(GemvArgs a) {
     }
 }
 
-template <int QT, int EPI, int W, int T, bool PRO>
-static hipError_t launch_mfma_wt(const GemvArgs& a, int max_blocks, hipStream_t st) {
-    const int n_tiles = (a.w.N + 15) / 16, n_units = (n_tiles + T - 1) / T;
-    const int nb = a.w.K / 32;
-    const size_t lds = (PRO ? (size_t)xdig_table_offset(nb) : 0) + (size_t)nb * 16 * sizeof(uint2);
-    if (!PRO) {
-        const hipError_t e = launch_xdigits(a, a.n_seq, st);
+template <int QT, int EPI, int TW, bool XL>
+static hipError_t launch_mb(const GemvArgs& a, int max_blocks, hipStream_t st) {
+    const int n_tiles = (a.w.N + 15) / 16, nb = a.w.K / 32;
+    if (!XL) {
+        hipLaunchKernelGGL(k_xdigits, dim3((a.w.K / 8 + kBlock - 1) / kBlock, 4), dim3(kBlock), 0, st, a.xin,
+                           a.x_stride, a.w.K, a.n_seq, a.xfrag);
+        const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemv_mfma<QT, EPI, W, T, PRO>, 64 * W, lds) !=
-            hipSuccess || per_cu < 1)
-        per_cu = 1;
-    const int cap = std::min(max_blocks, per_cu * device_cus());
-    const int grid = std::max(1, std::min(n_units, cap));
-    hipLaunchKernelGGL((k_gemv_mfma<QT, EPI, W, T, PRO>), dim3(grid), dim3(64 * W), lds, st, a);
+    // XL: digits, scales, sums; else scales and sums
+    const size_t lds = XL ? (size_t)mb_sums_offset(nb) + (size_t)nb * 64 : (size_t)nb * 80;
+    const int grid = std::max(1, std::min({n_tiles, device_cus(), max_blocks}));
+    hipLaunchKernelGGL((k_gemv_mb<QT, EPI, TW, XL>), dim3(grid), dim3(64 * kMbWaves), lds, st, a);
     return hipGetLastError();
 }
 
-// Shapes with many tiles take two tiles per wavefront (the activation
-// operands then serve both); the others split K over more wavefronts.
+// TW from the tiles per workgroup (one workgroup per CU): up to four tiles
+// per round share each digit fragment
 template <int QT, int EPI>
-static hipError_t launch_mfma(const GemvArgs& a, int max_blocks, hipStream_t st) {
+static hipError_t launch_mb_shape(const GemvArgs& a, int max_blocks, hipStream_t st) {
     const int n_tiles = (a.w.N + 15) / 16;
-    const int64_t target = (int64_t)device_cus() * 16;       // wavefronts wanted
-    if ((int64_t)n_tiles * 2 >= target) return launch_mfma_wt<QT, EPI, 4, 2, false>(a, max_blocks, st);
-    if ((int64_t)n_tiles * 4 >= target) return launch_mfma_wt<QT, EPI, 4, 1, false>(a, max_blocks, st);
-    if ((int64_t)n_tiles * 8 >= target) return launch_mfma_wt<QT, EPI, 8, 1, false>(a, max_blocks, st);
-    // 16 wavefronts per workgroup (about one workgroup per CU): the prologue
-    // mode's LDS fits, and the digit launch disappears
-    if (a.w.K <= kProMaxK) return launch_mfma_wt<QT, EPI, 16, 1, true>(a, max_blocks, st);
-    return launch_mfma_wt<QT, EPI, 16, 1, false>(a, max_blocks, st);
+    const int per = (n_tiles + device_cus() - 1) / device_cus();
+    if (a.w.K > kMbLdsMaxK) {
+        if (a.norm_g) return hipErrorInvalidValue;           // (the wide inputs take no gain)
+        if (per >= 4) return launch_mb<QT, EPI, 4, false>(a, max_blocks, st);
+        if (per >= 2) return launch_mb<QT, EPI, 2, false>(a, max_blocks, st);
+        return launch_mb<QT, EPI, 1, false>(a, max_blocks, st);
+    }
+    if (per >= 4) return launch_mb<QT, EPI, 4, true>(a, max_blocks, st);
+    if (per >= 2) return launch_mb<QT, EPI, 2, true>(a, max_blocks, st);
+    return launch_mb<QT, EPI, 1, true>(a, max_blocks, st);
 }
 
 hipError_t launch_gemv_batched(const GemvArgs& a0, int epi, int n_seq, int max_blocks, hipStream_t st) {
     if (n_seq < 1 || n_seq > 4 || !a0.w.sct || !a0.w.qf || !a0.xfrag) return hipErrorInvalidValue;
+    if (a0.w.K % 32) return hipErrorInvalidValue;
     GemvArgs a = a0;
     a.n_seq = n_seq;
     if (a.qtype == kQ8_0) {
         switch (epi) {
-            case EPI_QKV: return launch_mfma<kQ8_0, EPI_QKV>(a, max_blocks, st);
-            case EPI_RESID: return launch_mfma<kQ8_0, EPI_RESID>(a, max_blocks, st);
-            case EPI_SWIGLU: return launch_mfma<kQ8_0, EPI_SWIGLU>(a, max_blocks, st);
-            default: return launch_mfma<kQ8_0, EPI_LOGITS>(a, max_blocks, st);
+            case EPI_QKV: return launch_mb_shape<kQ8_0, EPI_QKV>(a, max_blocks, st);
+            case EPI_RESID: return launch_mb_shape<kQ8_0, EPI_RESID>(a, max_blocks, st);
+            case EPI_SWIGLU: return launch_mb_shape<kQ8_0, EPI_SWIGLU>(a, max_blocks, st);
+            default: return launch_mb_shape<kQ8_0, EPI_LOGITS>(a, max_blocks, st);
         }
     }
+    if (a.qtype != kQ4_0) return hipErrorInvalidValue;
     switch (epi) {
-        case EPI_QKV: return launch_mfma<kQ4_0, EPI_QKV>(a, max_blocks, st);
-        case EPI_RESID: return launch_mfma<kQ4_0, EPI_RESID>(a, max_blocks, st);
-        case EPI_SWIGLU: return launch_mfma<kQ4_0, EPI_SWIGLU>(a, max_blocks, st);
-        default: return launch_mfma<kQ4_0, EPI_LOGITS>(a, max_blocks, st);
+        case EPI_QKV: return launch_mb_shape<kQ4_0, EPI_QKV>(a, max_blocks, st);
+        case EPI_RESID: return launch_mb_shape<kQ4_0, EPI_RESID>(a, max_blocks, st);
+        case EPI_SWIGLU: return launch_mb_shape<kQ4_0, EPI_SWIGLU>(a, max_blocks, st);
+        default: return launch_mb_shape<kQ4_0, EPI_LOGITS>(a, max_blocks, st);
     }
 }
 
