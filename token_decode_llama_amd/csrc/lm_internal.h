@@ -140,7 +140,7 @@ struct AttnArgs {
     int nq, nkv, hd, max_ctx, max_chunks;
     float scale;           // 1/sqrt(hd)
     int grid_chunks;       // chunks the grid covers (<= max_chunks; >= every sequence's context)
-    int tiles;             // kAttnChunk-position tiles per workgroup (attn_tiles)
+    int tiles;             // kAttnChunk-position tiles per workgroup (attn_tiles), >= 1
     float* part;           // [n_seq][nq][max_chunks][hd + 2] partial o, m, l (one record per workgroup)
     int* counter;          // [n_seq][nkv][attn_cnt_lines][kCntStride] chunk counts (first int of
                            // each line, see chunk_arrive), zero between launches
@@ -158,7 +158,7 @@ hipError_t launch_gemv_batched(const GemvArgs& a, int epi, int n_seq, int max_bl
 // digits uint2 [nb][4 column groups][16 rows 4s+d], then activation scales
 // fp32 [nb][4 sequences], then digit sums int4 [nb][4 sequences].
 inline int64_t xfrag_bytes(int64_t K) { return K / 32 * (512 + 16 + 64); }
-int attn_tiles(int n_seq, int nkv, int max_chunks);
+int attn_tiles(int n_seq, int nkv, int max_chunks, int hd);
 hipError_t launch_attention(const AttnArgs& a, int n_seq, hipStream_t st);
 hipError_t launch_dequant(const QMat& w, int qtype, int row0, int n_rows, float* out,
                           hipStream_t st);

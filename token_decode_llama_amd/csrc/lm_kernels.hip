@@ -1033,217 +1033,59 @@ hipError_t launch_gemv_batched(const GemvArgs& a0, int epi, int n_seq, int max_b
 // ---------------------------------------------------------------------------
 // GQA decode attention with causal softmax, split over context
 // ---------------------------------------------------------------------------
-// One workgroup per (64-position chunk, KV head, sequence).  The chunk's K and
-// V tiles are read with coalesced 16-byte loads (issued before anything
-// else), staged in LDS (K rows padded so that a lane per key reads
-// conflict-free), and every query head of the group is scored against them:
-// a wavefront per head, a lane per key, causal mask = keys 0..pos.  PV runs
-// as thread = (head, 8 dimensions, quarter of the keys) with a reduction
-// over the quarters in LDS.  A context that fits one chunk writes o
-// directly; otherwise each chunk publishes its softmax state (m, l, o) with
-// device-coherent stores, and the last chunk of the (sequence, KV head) to
-// finish merges all of them (merge_chunk_states) within the same launch.
+// One workgroup of four wavefronts per (span of TP 64-position tiles, KV
+// head, sequence).  The span's K and V tiles are read with coalesced 16-byte
+// loads, the next tile's while the current one computes, and staged in LDS
+// (padded rows, V rows past the context zeroed); the group's G query heads
+// (at most kMaxGroup, padded to 16 rows) are scored against them and the
+// probabilities applied to V on the matrix cores (v_mfma_f32_16x16x16f16):
+//   scores S[head][key] = sum_d q[head][d] K[key][d]: wavefront w takes keys
+//     16w..16w+15; q enters as two fp16 terms, hi = fp16(q), lo = fp16(q - hi)
+//     (q to about 2^-22 relative; K is fp16 already), fp32 accumulation;
+//   online softmax over the span's tiles, causal mask = keys 0..pos: one LDS
+//     exchange of the per-wavefront maxima per tile, a running maximum M per
+//     head; p = exp(s - M) is written to LDS as fp16 hi + lo;
+//   o[head][d] = sum_key p V[key][d]: wavefront w takes the 16-column tiles
+//     of d in turn (HD / 64 of them), with every key of the tile.
+// In both products a lane's four results are four heads (rows 4(l/16)..+3) of
+// one key or one dimension (column l%16), so the per-head rescale factors a
+// lane computes in the softmax are the ones its o accumulators need.  A
+// context that fits one span writes o directly; otherwise each span
+// publishes its softmax state (m, l, o) with device-coherent stores, and the
+// last span of the (sequence, KV head) to finish merges all of them
+// (merge_chunk_states) within the same launch.
 constexpr int kMaxGroup = 8;   // query heads per KV head
+typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
 
-// One tile per workgroup (short contexts: the straight-line form).
 template <int HD>
-__global__ __launch_bounds__(kBlock) void k_attn1(AttnArgs a) {
-    constexpr int CH = kAttnChunk;
-    constexpr int KP = HD + 8;                  // padded K row (halves)
-    constexpr int PCS = CH * HD / 8 / kBlock;   // 16-byte pieces per thread per tile
-    // the K tile is dead once the scores are taken: the PV partial sums reuse it
-    static_assert(sizeof(float) * kWaves * kMaxGroup * HD <= sizeof(__half) * CH * KP, "Os fits in Ks");
-    static_assert(sizeof(float) * 6 * kBlock <= sizeof(__half) * CH * KP, "merge scratch fits in Ks");
-    __shared__ __align__(16) __half Ks[CH][KP];
-    __shared__ __align__(16) __half Vs[CH][HD];
-    __shared__ __align__(16) float Qs[kMaxGroup][HD];
-    __shared__ __align__(16) float Ps[kMaxGroup][CH];
-    __shared__ float Ms[kMaxGroup], Ls[kMaxGroup];
-    __shared__ int s_last;
-    float (*Os)[kMaxGroup * HD] = reinterpret_cast<float (*)[kMaxGroup * HD]>(&Ks[0][0]);
-
-    const int chunk = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int G = a.nq / a.nkv;
-    const int t0 = chunk * CH;
-    const int64_t stride = HD + 2;      // even: 8-byte aligned pairs
-
-    // ---- every load first (rows clamped to the cache; masked below)
-    const __half* Kg = a.kcache + (int64_t)s * a.kv_seq_stride + (int64_t)g * a.max_ctx * HD;
-    const __half* Vg = a.vcache + (int64_t)s * a.kv_seq_stride + (int64_t)g * a.max_ctx * HD;
-    uint4 kr[PCS], vr[PCS];
-    #pragma unroll
-    for (int u = 0; u < PCS; ++u) {
-        const int c = tid + u * kBlock;
-        const int t = min(t0 + c / (HD / 8), a.max_ctx - 1), d8 = (c % (HD / 8)) * 8;
-        kr[u] = *(const uint4*)(Kg + (int64_t)t * HD + d8);
-        vr[u] = *(const uint4*)(Vg + (int64_t)t * HD + d8);
-    }
-    const float* qg = a.q + (int64_t)s * a.nq * HD + (int64_t)g * G * HD;
-    constexpr int kQ = (kMaxGroup * HD / 4 + kBlock - 1) / kBlock;
-    float4 qv[kQ];
-    #pragma unroll
-    for (int u = 0; u < kQ; ++u) {
-        const int i = min((tid + u * kBlock) * 4, G * HD - 4);
-        qv[u] = *(const float4*)(qg + i);
-    }
-    const int n_ctx = a.pos[s] + 1;                       // keys 0..pos inclusive
-    const int n_act = (n_ctx + CH - 1) / CH;
-    if (chunk >= n_act) return;                           // chunk past the causal horizon
-    const int nt = min(CH, n_ctx - t0);
-
-    #pragma unroll
-    for (int u = 0; u < PCS; ++u) {
-        const int c = tid + u * kBlock;
-        const int t = c / (HD / 8), d8 = (c % (HD / 8)) * 8;
-        *(uint4*)&Ks[t][d8] = kr[u];
-        *(uint4*)&Vs[t][d8] = vr[u];
-    }
-    #pragma unroll
-    for (int u = 0; u < kQ; ++u) {
-        const int i = (tid + u * kBlock) * 4;
-        if (i < G * HD) *(float4*)&Qs[i / HD][i % HD] = qv[u];
-    }
-    __syncthreads();
-
-    // ---- scores: a wavefront per query head, a lane per key
-    for (int j = wave; j < G; j += kWaves) {
-        float sc = -FLT_MAX;
-        if (lane < nt) {
-            float acc0 = 0.f, acc1 = 0.f;
-            #pragma unroll
-            for (int d = 0; d < HD; d += 8) {
-                const uint4 kk = *(const uint4*)&Ks[lane][d];
-                const float4 q0 = *(const float4*)&Qs[j][d];
-                const float4 q1 = *(const float4*)&Qs[j][d + 4];
-                const float2 k01 = __half22float2(*(const __half2*)&kk.x);
-                const float2 k23 = __half22float2(*(const __half2*)&kk.y);
-                const float2 k45 = __half22float2(*(const __half2*)&kk.z);
-                const float2 k67 = __half22float2(*(const __half2*)&kk.w);
-                acc0 = fmaf(q0.x, k01.x, acc0);
-                acc1 = fmaf(q0.y, k01.y, acc1);
-                acc0 = fmaf(q0.z, k23.x, acc0);
-                acc1 = fmaf(q0.w, k23.y, acc1);
-                acc0 = fmaf(q1.x, k45.x, acc0);
-                acc1 = fmaf(q1.y, k45.y, acc1);
-                acc0 = fmaf(q1.z, k67.x, acc0);
-                acc1 = fmaf(q1.w, k67.y, acc1);
-            }
-            sc = (acc0 + acc1) * a.scale;
-        }
-        const float m = wave_max(sc);
-        const float p = lane < nt ? __expf(sc - m) : 0.f;
-        const float l = wave_sum(p);
-        Ps[j][lane] = p;
-        if (lane == 0) { Ms[j] = m; Ls[j] = l; }
-    }
-    __syncthreads();
-
-    // ---- o = sum_t p_t v_t: thread (head j, 8 dims, quarter w of the keys)
-    constexpr int D8 = HD / 8;
-    for (int idx = tid; idx < G * D8 * kWaves; idx += kBlock) {
-        const int w = idx / (G * D8), r = idx % (G * D8);
-        const int j = r / D8, d8 = (r % D8) * 8;
-        float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        const int tb = w * (CH / kWaves), te = min(tb + CH / kWaves, nt);
-        for (int t = tb; t < te; ++t) {
-            const float pt = Ps[j][t];
-            const uint4 vv = *(const uint4*)&Vs[t][d8];
-            const float2 v01 = __half22float2(*(const __half2*)&vv.x);
-            const float2 v23 = __half22float2(*(const __half2*)&vv.y);
-            const float2 v45 = __half22float2(*(const __half2*)&vv.z);
-            const float2 v67 = __half22float2(*(const __half2*)&vv.w);
-            o[0] = fmaf(pt, v01.x, o[0]);
-            o[1] = fmaf(pt, v01.y, o[1]);
-            o[2] = fmaf(pt, v23.x, o[2]);
-            o[3] = fmaf(pt, v23.y, o[3]);
-            o[4] = fmaf(pt, v45.x, o[4]);
-            o[5] = fmaf(pt, v45.y, o[5]);
-            o[6] = fmaf(pt, v67.x, o[6]);
-            o[7] = fmaf(pt, v67.y, o[7]);
-        }
-        float* dst = &Os[w][j * HD + d8];
-        *(float4*)dst = make_float4(o[0], o[1], o[2], o[3]);
-        *(float4*)(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
-    }
-    __syncthreads();
-
-    float* part_s = a.part + (int64_t)s * a.nq * a.max_chunks * stride;
-    float* out_s = a.out + (int64_t)s * a.nq * HD + (int64_t)g * G * HD;
-    if (n_act == 1) {
-        for (int i = tid; i < G * HD; i += kBlock) {
-            float v = Os[0][i];
-            #pragma unroll
-            for (int w = 1; w < kWaves; ++w) v += Os[w][i];
-            out_s[i] = v / Ls[i / HD];
-        }
-        return;
-    }
-    for (int i = 2 * tid; i < G * HD; i += 2 * kBlock) {
-        float v0 = Os[0][i], v1 = Os[0][i + 1];
-        #pragma unroll
-        for (int w = 1; w < kWaves; ++w) {
-            v0 += Os[w][i];
-            v1 += Os[w][i + 1];
-        }
-        const int j = i / HD, d = i % HD;
-        float* ph = part_s + ((int64_t)(g * G + j) * a.max_chunks + chunk) * stride;
-        st_dev2(ph + d, v0, v1);
-        if (d == 0) st_dev2(ph + HD, Ms[j], Ls[j]);
-    }
-
-    // ---- the last chunk of this (sequence, KV head) merges every chunk.  The
-    // partials are device-coherent stores, each wavefront waits for its own
-    // to complete before the count is taken.
-    drain_vm();
-    __syncthreads();
-    if (tid == 0)
-        s_last = chunk_arrive(a.counter + (int64_t)(s * a.nkv + g) * attn_cnt_lines(a.max_chunks) * kCntStride,
-                              chunk, n_act);
-    __syncthreads();
-    if (!s_last) return;
-
-    const float* part_g = part_s + (int64_t)g * G * a.max_chunks * stride;
-    merge_chunk_states<HD>(
-        G, n_act, [&](int j) { return part_g + (int64_t)j * a.max_chunks * stride; },
-        [](const float* p) { return ld_dev2(p); },
-        [&](int i, float4 v) { *(float4*)(out_s + i) = v; },
-        reinterpret_cast<float (*)[6]>(&Ks[0][0]));
-}
-
-// Several tiles per workgroup (TP = 2 or 4: long contexts with many
-// workgroups): the span's tiles in turn, the next tile's K/V loads in flight
-// while the current one computes, with a running maximum and sum per head.
-template <int HD, int TP>
 __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
-    static_assert(TP >= 2, "one tile: k_attn1");
+    static_assert(kBlock == 256 && kAttnChunk == 64, "four wavefronts, sixteen keys each");
     constexpr int CH = kAttnChunk;
-    constexpr int KP = HD + 8;                  // padded K row (halves)
+    constexpr int KP = HD + 8;                  // padded K / V row (halves): conflict-free operand reads
+    constexpr int PP = CH + 8;                  // padded P row (halves)
     constexpr int PCS = CH * HD / 8 / kBlock;   // 16-byte pieces per thread per tile
-    constexpr int D8 = HD / 8;
-    constexpr int NI = (kMaxGroup * D8 * kWaves + kBlock - 1) / kBlock;   // PV items per thread
-    // the K tile is dead once the last scores are taken: the PV partial sums reuse it
-    static_assert(sizeof(float) * kWaves * kMaxGroup * HD <= sizeof(__half) * CH * KP, "Os fits in Ks");
+    constexpr int KS = HD / 16;                 // 16-dimension steps of the score product
+    constexpr int DT = HD / 64;                 // 16-column tiles of o per wavefront
     static_assert(sizeof(float) * 6 * kBlock <= sizeof(__half) * CH * KP, "merge scratch fits in Ks");
     __shared__ __align__(16) __half Ks[CH][KP];
-    __shared__ __align__(16) __half Vs[CH][HD];
-    __shared__ __align__(16) float Qs[kMaxGroup][HD];
-    __shared__ __align__(16) float Ps[kMaxGroup][CH];
-    __shared__ float Ms[kMaxGroup], Ls[kMaxGroup], Rs[kMaxGroup];
+    __shared__ __align__(16) __half Vs[CH][KP];
+    __shared__ __align__(16) _Float16 Ph[16][PP], Pl[16][PP];
+    __shared__ float Mx[4][16], Lx[4][16];
     __shared__ int s_last;
-    float (*Os)[kMaxGroup * HD] = reinterpret_cast<float (*)[kMaxGroup * HD]>(&Ks[0][0]);
 
-    // this workgroup's span: tiles span*TP .. span*TP+TP-1 of CH positions each
     const int chunk = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 15, lq = lane >> 4;   // operand row / column index, lane group
     const int G = a.nq / a.nkv;
-    const int64_t stride = HD + 2;      // even: 8-byte aligned pairs
+    const int64_t stride = HD + 2;              // partial record (even: 8-byte aligned pairs)
 
     // ---- the first tile's loads first (rows clamped to the cache; masked below)
     const __half* Kg = a.kcache + (int64_t)s * a.kv_seq_stride + (int64_t)g * a.max_ctx * HD;
     const __half* Vg = a.vcache + (int64_t)s * a.kv_seq_stride + (int64_t)g * a.max_ctx * HD;
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // (native vectors: kept in registers)
     u32x4 kr[PCS], vr[PCS];
+    const int TP = a.tiles;                     // tiles of this workgroup's span
     const int t_first = chunk * TP;
     #pragma unroll
     for (int u = 0; u < PCS; ++u) {
@@ -1252,48 +1094,50 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
         kr[u] = *(const u32x4*)(Kg + (int64_t)t * HD + d8);
         vr[u] = *(const u32x4*)(Vg + (int64_t)t * HD + d8);
     }
+    // this lane's q operands: head lr (zero past G), dimensions 16k + 4lq .. +3
     const float* qg = a.q + (int64_t)s * a.nq * HD + (int64_t)g * G * HD;
-    constexpr int kQ = (kMaxGroup * HD / 4 + kBlock - 1) / kBlock;
-    float4 qv[kQ];
+    float4 qv[KS];
     #pragma unroll
-    for (int u = 0; u < kQ; ++u) {
-        const int i = min((tid + u * kBlock) * 4, G * HD - 4);
-        qv[u] = *(const float4*)(qg + i);
-    }
+    for (int k = 0; k < KS; ++k) qv[k] = *(const float4*)(qg + (int64_t)min(lr, G - 1) * HD + 16 * k + 4 * lq);
     const int n_ctx = a.pos[s] + 1;                       // keys 0..pos inclusive
     const int n_tiles = (n_ctx + CH - 1) / CH;
     const int n_act = (n_tiles + TP - 1) / TP;            // spans holding keys
     if (chunk >= n_act) return;                           // span past the causal horizon
 
+    h4_t qh[KS], ql[KS];
     #pragma unroll
-    for (int u = 0; u < kQ; ++u) {
-        const int i = (tid + u * kBlock) * 4;
-        if (i < G * HD) *(float4*)&Qs[i / HD][i % HD] = qv[u];
-    }
-    if (tid < G) {
-        Ms[tid] = -FLT_MAX;
-        Ls[tid] = 0.f;
-    }
-    // PV accumulators: thread item (key quarter w, head j, 8 dimensions)
-    float o[NI][8];
-    #pragma unroll
-    for (int i = 0; i < NI; ++i)
+    for (int k = 0; k < KS; ++k) {
+        const float v[4] = {qv[k].x, qv[k].y, qv[k].z, qv[k].w};
         #pragma unroll
-        for (int k = 0; k < 8; ++k) o[i][k] = 0.f;
-
-    // TP is a compile-time count and every tile runs (one past the context
-    // has no valid key and changes nothing): the loop unrolls without
-    // branches and K/V stay in registers
+        for (int e = 0; e < 4; ++e) {
+            const float x = lr < G ? v[e] : 0.f;
+            const _Float16 hi = (_Float16)x;
+            qh[k][e] = hi;
+            ql[k][e] = (_Float16)(x - (float)hi);
+        }
+    }
+    // running state of this lane's four heads 4lq + i
+    float M[4], Lw[4];                // maximum (common to the wavefronts), this wavefront's sum
+    f4_t o[DT];                       // o[dt][i]: head 4lq + i, dimension 16 (DT wave + dt) + lr
     #pragma unroll
+    for (int i = 0; i < 4; ++i) { M[i] = -FLT_MAX; Lw[i] = 0.f; }
+    #pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f4_t{0.f, 0.f, 0.f, 0.f};
+
+    // every tile of the span runs (one past the context has no valid key and
+    // changes nothing)
     for (int ti = 0; ti < TP; ++ti) {
         const int tile = t_first + ti;
         const int nt = max(0, min(CH, n_ctx - tile * CH));
+        if (ti > 0) __syncthreads();                      // the previous tile's readers are done
         #pragma unroll
         for (int u = 0; u < PCS; ++u) {
             const int c = tid + u * kBlock;
             const int t = c / (HD / 8), d8 = (c % (HD / 8)) * 8;
             *(u32x4*)&Ks[t][d8] = kr[u];
-            *(u32x4*)&Vs[t][d8] = vr[u];
+            // V rows past the context are zeroed: their probability is 0, and
+            // 0 times a stale cache value must stay 0
+            *(u32x4*)&Vs[t][d8] = t < nt ? vr[u] : u32x4{0u, 0u, 0u, 0u};
         }
         if (ti + 1 < TP) {                                // in flight while this tile computes
             #pragma unroll
@@ -1306,117 +1150,112 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
         }
         __syncthreads();
 
-        // ---- scores: a wavefront per query head, a lane per key; the running
-        // maximum M and sum L of the head (online softmax over the span's tiles)
-        for (int j = wave; j < G; j += kWaves) {
-            float sc = -FLT_MAX;
-            if (lane < nt) {
-                float acc0 = 0.f, acc1 = 0.f;
-                #pragma unroll
-                for (int d = 0; d < HD; d += 8) {
-                    const uint4 kk = *(const uint4*)&Ks[lane][d];
-                    const float4 q0 = *(const float4*)&Qs[j][d];
-                    const float4 q1 = *(const float4*)&Qs[j][d + 4];
-                    const float2 k01 = __half22float2(*(const __half2*)&kk.x);
-                    const float2 k23 = __half22float2(*(const __half2*)&kk.y);
-                    const float2 k45 = __half22float2(*(const __half2*)&kk.z);
-                    const float2 k67 = __half22float2(*(const __half2*)&kk.w);
-                    acc0 = fmaf(q0.x, k01.x, acc0);
-                    acc1 = fmaf(q0.y, k01.y, acc1);
-                    acc0 = fmaf(q0.z, k23.x, acc0);
-                    acc1 = fmaf(q0.w, k23.y, acc1);
-                    acc0 = fmaf(q1.x, k45.x, acc0);
-                    acc1 = fmaf(q1.y, k45.y, acc1);
-                    acc0 = fmaf(q1.z, k67.x, acc0);
-                    acc1 = fmaf(q1.w, k67.y, acc1);
-                }
-                sc = (acc0 + acc1) * a.scale;
-            }
-            const float m_old = Ms[j];
-            const float m = fmaxf(m_old, wave_max(sc));
-            const float r = __expf(m_old - m);            // 0 on the first tile
-            const float p = lane < nt ? __expf(sc - m) : 0.f;
-            const float l = wave_sum(p);
-            Ps[j][lane] = p;
-            if (lane == 0) {
-                Ms[j] = m;
-                Ls[j] = fmaf(Ls[j], r, l);
-                Rs[j] = r;
-            }
+        // ---- scores of keys 16 wave + lr, heads 4lq + i
+        f4_t sc = {0.f, 0.f, 0.f, 0.f};
+        #pragma unroll
+        for (int k = 0; k < KS; ++k) {
+            const h4_t kb = *(const h4_t*)&Ks[16 * wave + lr][16 * k + 4 * lq];
+            sc = __builtin_amdgcn_mfma_f32_16x16x16f16(qh[k], kb, sc, 0, 0, 0);
+            sc = __builtin_amdgcn_mfma_f32_16x16x16f16(ql[k], kb, sc, 0, 0, 0);
+        }
+        const bool live = 16 * wave + lr < nt;
+        float sv[4], mw[4];
+        #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sv[i] = live ? sc[i] * a.scale : -FLT_MAX;
+            mw[i] = sv[i];
+        }
+        #pragma unroll
+        for (int off = 1; off < 16; off <<= 1)
+            #pragma unroll
+            for (int i = 0; i < 4; ++i) mw[i] = fmaxf(mw[i], __shfl_xor(mw[i], off, 64));
+        if (lr == 0) {
+            #pragma unroll
+            for (int i = 0; i < 4; ++i) Mx[wave][4 * lq + i] = mw[i];
         }
         __syncthreads();
 
-        // ---- o = r o + sum_t p_t v_t over this tile's keys of quarter w
+        // ---- online softmax: the tile's maximum, p, the rescale of the running state
+        float r[4];
         #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int idx = tid + i * kBlock;
-            const bool live = idx < G * D8 * kWaves;          // (no break: o stays in registers)
-            const int w = idx / (G * D8), rr = idx % (G * D8);
-            const int j = live ? rr / D8 : 0, d8 = (rr % D8) * 8;
-            const float r = Rs[j];
+        for (int i = 0; i < 4; ++i) {
+            const int h = 4 * lq + i;
+            const float mt = fmaxf(fmaxf(Mx[0][h], Mx[1][h]), fmaxf(Mx[2][h], Mx[3][h]));
+            const float mn = fmaxf(M[i], mt);
+            r[i] = __expf(M[i] - mn);                     // 0 on the first tile
+            M[i] = mn;
+            const float p = live ? __expf(sv[i] - mn) : 0.f;
+            const _Float16 ph = (_Float16)p;
+            Ph[h][16 * wave + lr] = ph;
+            Pl[h][16 * wave + lr] = (_Float16)(p - (float)ph);
+            float ps = p;
             #pragma unroll
-            for (int k = 0; k < 8; ++k) o[i][k] *= r;
-            const int tb = w * (CH / kWaves), te = live ? min(tb + CH / kWaves, nt) : tb;
-            for (int t = tb; t < te; ++t) {
-                const float pt = Ps[j][t];
-                const uint4 vv = *(const uint4*)&Vs[t][d8];
-                const float2 v01 = __half22float2(*(const __half2*)&vv.x);
-                const float2 v23 = __half22float2(*(const __half2*)&vv.y);
-                const float2 v45 = __half22float2(*(const __half2*)&vv.z);
-                const float2 v67 = __half22float2(*(const __half2*)&vv.w);
-                o[i][0] = fmaf(pt, v01.x, o[i][0]);
-                o[i][1] = fmaf(pt, v01.y, o[i][1]);
-                o[i][2] = fmaf(pt, v23.x, o[i][2]);
-                o[i][3] = fmaf(pt, v23.y, o[i][3]);
-                o[i][4] = fmaf(pt, v45.x, o[i][4]);
-                o[i][5] = fmaf(pt, v45.y, o[i][5]);
-                o[i][6] = fmaf(pt, v67.x, o[i][6]);
-                o[i][7] = fmaf(pt, v67.y, o[i][7]);
+            for (int off = 1; off < 16; off <<= 1) ps += __shfl_xor(ps, off, 64);
+            Lw[i] = fmaf(Lw[i], r[i], ps);
+        }
+        #pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+            #pragma unroll
+            for (int i = 0; i < 4; ++i) o[dt][i] *= r[i];
+        __syncthreads();
+
+        // ---- o += p V over the tile's keys: column tiles DT wave .. DT wave + DT - 1
+        #pragma unroll
+        for (int kq = 0; kq < CH / 16; ++kq) {
+            const h4_t pa = *(const h4_t*)&Ph[lr][16 * kq + 4 * lq];
+            const h4_t pb = *(const h4_t*)&Pl[lr][16 * kq + 4 * lq];
+            #pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const int d = 16 * (DT * wave + dt) + lr;
+                h4_t vb;
+                #pragma unroll
+                for (int e = 0; e < 4; ++e) vb[e] = *(const _Float16*)&Vs[16 * kq + 4 * lq + e][d];
+                o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vb, o[dt], 0, 0, 0);
+                o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(pb, vb, o[dt], 0, 0, 0);
             }
         }
-        // before the next tile overwrites K, V and P (after the last one the
-        // partial sums below overwrite only K, whose reads ended before P)
-        if (ti + 1 < TP) __syncthreads();
     }
-    #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        const int idx = tid + i * kBlock;
-        if (idx < G * D8 * kWaves) {
-            const int w = idx / (G * D8), rr = idx % (G * D8);
-            const int j = rr / D8, d8 = (rr % D8) * 8;
-            float* dst = &Os[w][j * HD + d8];
-            *(float4*)dst = make_float4(o[i][0], o[i][1], o[i][2], o[i][3]);
-            *(float4*)(dst + 4) = make_float4(o[i][4], o[i][5], o[i][6], o[i][7]);
-        }
+
+    // ---- the span's l per head: the four wavefronts' sums
+    if (lr == 0) {
+        #pragma unroll
+        for (int i = 0; i < 4; ++i) Lx[wave][4 * lq + i] = Lw[i];
     }
     __syncthreads();
+    float L[4];
+    #pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int h = 4 * lq + i;
+        L[i] = Lx[0][h] + Lx[1][h] + Lx[2][h] + Lx[3][h];
+    }
 
     float* part_s = a.part + (int64_t)s * a.nq * a.max_chunks * stride;
     float* out_s = a.out + (int64_t)s * a.nq * HD + (int64_t)g * G * HD;
     if (n_act == 1) {
-        for (int i = tid; i < G * HD; i += kBlock) {
-            float v = Os[0][i];
-            #pragma unroll
-            for (int w = 1; w < kWaves; ++w) v += Os[w][i];
-            out_s[i] = v / Ls[i / HD];
+        #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int h = 4 * lq + i;
+            if (h < G) {
+                const float inv = 1.f / L[i];
+                #pragma unroll
+                for (int dt = 0; dt < DT; ++dt) out_s[h * HD + 16 * (DT * wave + dt) + lr] = o[dt][i] * inv;
+            }
         }
         return;
     }
-    for (int i = 2 * tid; i < G * HD; i += 2 * kBlock) {
-        float v0 = Os[0][i], v1 = Os[0][i + 1];
-        #pragma unroll
-        for (int w = 1; w < kWaves; ++w) {
-            v0 += Os[w][i];
-            v1 += Os[w][i + 1];
+    #pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int h = 4 * lq + i;
+        if (h < G) {
+            float* ph = part_s + ((int64_t)(g * G + h) * a.max_chunks + chunk) * stride;
+            #pragma unroll
+            for (int dt = 0; dt < DT; ++dt) st_dev(ph + 16 * (DT * wave + dt) + lr, o[dt][i]);
+            if (wave == 0 && lr == 0) st_dev2(ph + HD, M[i], L[i]);
         }
-        const int j = i / HD, d = i % HD;
-        float* ph = part_s + ((int64_t)(g * G + j) * a.max_chunks + chunk) * stride;
-        st_dev2(ph + d, v0, v1);
-        if (d == 0) st_dev2(ph + HD, Ms[j], Ls[j]);
     }
 
-    // ---- the last chunk of this (sequence, KV head) merges every chunk.  The
-    // partials are device-coherent stores, each wavefront waits for its own
+    // ---- the last span of this (sequence, KV head) merges every span.  The
+    // partials are device-coherent stores; each wavefront waits for its own
     // to complete before the count is taken.
     drain_vm();
     __syncthreads();
@@ -1434,29 +1273,29 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
         reinterpret_cast<float (*)[6]>(&Ks[0][0]));
 }
 
-// Tiles per attention workgroup: one, unless the one-tile grid would hold at
-// least eight workgroups per CU; then two (four from sixteen), so that fewer
-// partial states are merged and each workgroup's next tile loads while it
-// computes.
-int attn_tiles(int n_seq, int nkv, int max_chunks) {
-    const int64_t wgs = (int64_t)n_seq * nkv * max_chunks, per = 4ll * device_cus();
-    return wgs >= 4 * per ? 4 : wgs >= 2 * per ? 2 : 1;
+// Tiles per attention workgroup: as few as keep the whole grid resident at
+// once (the workgroups one CU holds, from the kernel's registers and LDS,
+// times the CUs), so no workgroup waits for another to finish, and longer
+// spans leave fewer partial states to merge.
+int attn_tiles(int n_seq, int nkv, int max_chunks, int hd) {
+    static int per_cu[2] = {0, 0};
+    int& pc = per_cu[hd == 128 ? 1 : 0];
+    if (!pc) {
+        const void* f = hd == 128 ? (const void*)k_attn<128> : (const void*)k_attn<64>;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&pc, f, kBlock, 0) != hipSuccess || pc < 1) pc = 1;
+    }
+    const int64_t tiles = (int64_t)n_seq * nkv * max_chunks, slots = (int64_t)pc * device_cus();
+    return (int)std::max<int64_t>(1, (tiles + slots - 1) / slots);
 }
 
 hipError_t launch_attention(const AttnArgs& a, int n_seq, hipStream_t st) {
-    if (a.tiles != 1 && a.tiles != 2 && a.tiles != 4) return hipErrorInvalidValue;
+    if (a.tiles < 1) return hipErrorInvalidValue;
     if (a.hd != 128 && a.hd != 64) return hipErrorInvalidValue;
     if (a.grid_chunks < 1 || a.grid_chunks > a.max_chunks) return hipErrorInvalidValue;
+    if (a.nq % a.nkv || a.nq / a.nkv > kMaxGroup) return hipErrorInvalidValue;
     dim3 grid((a.grid_chunks + a.tiles - 1) / a.tiles, a.nkv, n_seq);
-    if (a.hd == 128) {
-        if (a.tiles == 1) hipLaunchKernelGGL((k_attn1<128>), grid, dim3(kBlock), 0, st, a);
-        else if (a.tiles == 2) hipLaunchKernelGGL((k_attn<128, 2>), grid, dim3(kBlock), 0, st, a);
-        else hipLaunchKernelGGL((k_attn<128, 4>), grid, dim3(kBlock), 0, st, a);
-    } else {
-        if (a.tiles == 1) hipLaunchKernelGGL((k_attn1<64>), grid, dim3(kBlock), 0, st, a);
-        else if (a.tiles == 2) hipLaunchKernelGGL((k_attn<64, 2>), grid, dim3(kBlock), 0, st, a);
-        else hipLaunchKernelGGL((k_attn<64, 4>), grid, dim3(kBlock), 0, st, a);
-    }
+    if (a.hd == 128) hipLaunchKernelGGL((k_attn<128>), grid, dim3(kBlock), 0, st, a);
+    else hipLaunchKernelGGL((k_attn<64>), grid, dim3(kBlock), 0, st, a);
     return hipGetLastError();
 }
 

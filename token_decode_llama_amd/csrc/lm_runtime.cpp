@@ -1150,7 +1150,7 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
     at.max_chunks = m->max_chunks;
     at.scale = (float)(1.0 / std::sqrt((double)m->hd));
     at.grid_chunks = m->opt_active ? attn_chunks_for(m, m->opt_need) : attn_grid_chunks(m, n_seq);
-    at.tiles = attn_tiles(n_seq, (int)m->nkv, at.grid_chunks);
+    at.tiles = attn_tiles(n_seq, (int)m->nkv, at.grid_chunks, (int)m->hd);
     at.part = m->sb.attn_part;
     at.counter = m->sb.attn_cnt;
     at.out = m->sb.o;
