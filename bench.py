@@ -71,7 +71,7 @@ for _qt in ("q4k", "q5k", "q6k"):
 HYBRID_RESIDENT = {"llama70b_q4": 36, "llama70b_q4k": 36, "llama70b_q6k": 26}
 KERNEL_NAMES = {
     "qkv": "k_gemv<QKV, RMSNorm prologue, RoPE + KV-append epilogue>",
-    "attn": "k_attn + k_attn_merge (GQA decode attention)",
+    "attn": "k_attn (GQA decode attention on the matrix cores, split over context, in-launch merge)",
     "wo": "k_gemv<Wo, residual epilogue>",
     "gateup": "k_gemv<gate/up, RMSNorm prologue, SwiGLU epilogue>",
     "down": "k_gemv<down, residual epilogue>",
@@ -92,9 +92,10 @@ def kernel_source_digest() -> str:
 
 
 def traffic_from_profiles(kind: str, workload: str):
-    """HBM bytes per launch from the committed counter summary, if it was
-    taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"pmc_{kind}_{workload}.json")
+    """HBM bytes (fetched + written) per launch of one operator from the
+    committed counter summary of the workload, if it was taken on the current
+    kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{workload}.json")
     if not os.path.exists(path):
         return None
     try:
@@ -102,9 +103,125 @@ def traffic_from_profiles(kind: str, workload: str):
             d = json.load(fh)
         if d.get("kernel_source_sha256_16") != kernel_source_digest():
             return None
-        return float(d["hbm_bytes_per_launch"])
+        e = d["per_launch_bytes"][kind]
+        return float(e["fetch"] + e["write"])
     except Exception:
         return None
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries (--summarize): the kernel trace and the two HBM counter
+# runs of this script, reduced to the per-operator tables under profiles/
+# ---------------------------------------------------------------------------
+def kind_of(kernel: str):
+    """The step operator a kernel symbol belongs to, from its template
+    arguments (the residual GEMVs: Wo takes inputs of up to 8192 columns, the
+    down projection wider ones - the 8B and 70B shapes)."""
+    import re
+    m = re.search(r"k_gemv<(\d+), (\d+), (\d+), (\d+), (\d+)>", kernel)
+    if m:
+        epi, xr = int(m.group(3)), int(m.group(4))
+        return {0: "qkv", 2: "gateup", 3: "lmhead"}.get(epi, "down" if xr == 8 else "wo")
+    m = re.search(r"k_gemv_mb<(\d+), (\d+), (\d+), (true|false)>", kernel)
+    if m:
+        epi, xl = int(m.group(2)), m.group(4) == "true"
+        return {0: "qkv", 2: "gateup", 3: "lmhead"}.get(epi, "wo" if xl else "down")
+    for key, kind in (("k_attn", "attn"), ("k_embed", "embed"), ("k_xdigits", "digits"),
+                      ("k_read_bw", "read_bw"), ("k_dequant", "dequant"), ("k_layer_cos", "layer_cos"),
+                      ("k_zero", "zero")):
+        if key in kernel:
+            return kind
+    return None
+
+
+def _counter_rows(d: str):
+    import csv
+    import glob
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f) as fh:
+            yield from csv.DictReader(fh)
+
+
+def summarize(d: str, workload: str, commands: list):
+    """Reads <d>/trace (kernel trace + stats), <d>/fetch and <d>/write
+    (FETCH_SIZE / WRITE_SIZE runs with --calibrate) and writes
+    profiles/kernels_<workload>.md and profiles/pmc_<workload>.json."""
+    import csv
+    import glob
+    import statistics
+    stats = glob.glob(os.path.join(d, "trace", "**", "*kernel_stats.csv"), recursive=True)
+    trace = glob.glob(os.path.join(d, "trace", "**", "*kernel_trace.csv"), recursive=True)
+    if not stats or not trace:
+        raise SystemExit(f"no kernel trace under {d}/trace")
+    rows = list(csv.DictReader(open(stats[0])))
+    durs = {}
+    for r in csv.DictReader(open(trace[0])):
+        k = kind_of(r["Kernel_Name"]) or r["Kernel_Name"]
+        durs.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    # HBM counters per dispatch, KiB
+    per = {}
+    for which, counter in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        for r in _counter_rows(os.path.join(d, which)):
+            if r["Counter_Name"] != counter:
+                continue
+            k = kind_of(r["Kernel_Name"]) or r["Kernel_Name"]
+            per.setdefault(k, {}).setdefault(which, []).append(float(r["Counter_Value"]) * 1024.0)
+    # calibration: a plain read of 1 GiB, a dequant writing 64 down-projection rows of fp32
+    import synth
+    cfg = synth.CONFIGS[workload]
+    read_ref, write_ref = float(1 << 30), float(64 * cfg.ffn * 4)
+    # (the read-ceiling probe reads more than 1 GiB: the calibration read is the smallest)
+    reads = per.get("read_bw", {}).get("fetch", [])
+    writes = per.get("dequant", {}).get("write", [])
+    if not reads or not writes:
+        raise SystemExit("calibration dispatches missing (run the counter passes with --calibrate)")
+    ff = read_ref / min(reads)
+    wf = write_ref / statistics.median(writes)
+    table = {}
+    for k, e in per.items():
+        if k in ("read_bw", "dequant"):
+            continue
+        f = e.get("fetch", [0.0])
+        w = e.get("write", [0.0])
+        table[k] = {"fetch": int(ff * statistics.mean(f)), "write": int(wf * statistics.mean(w)),
+                    "launches": max(len(f), len(w))}
+    out = {"kernel_source_sha256_16": kernel_source_digest(), "workload": workload,
+           "calibration": {"fetch_factor": round(ff, 5), "fetch_ref": "k_read_bw over 1 GiB",
+                           "write_factor": round(wf, 5),
+                           "write_ref": f"k_dequant writing 64*{cfg.ffn}*4 bytes"},
+           "per_launch_bytes": table, "commands": commands}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"pmc_{workload}.json"), "w") as fh:
+        json.dump(out, fh, indent=1)
+    lines = [f"# Kernel time and HBM traffic: {workload} ({WORKLOAD_TEXT[workload]})", "",
+             "Commands (repository root, MI355X host; one run each):", ""]
+    lines += [f"    {c}" for c in commands]
+    lines += ["", "rocprofv3 `kernel_stats` of the trace run (warm-up, the timed graph-replayed steps, the "
+              "timing steps with HIP events in the step graph, the one-family timing graphs, the "
+              "read-ceiling probe):", "",
+              "| operator | kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        k = kind_of(r["Name"]) or "-"
+        lines.append(f"| {k} | `{r['Name'][:70]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.1f}% |")
+    lines += ["", "Median dispatch duration per operator (kernel trace):", "",
+              "| operator | dispatches | median us |", "|---|---|---|"]
+    for k in sorted(durs, key=lambda k: -statistics.median(durs[k])):
+        if k in KERNEL_NAMES or k in ("embed", "digits"):
+            lines.append(f"| {k} | {len(durs[k])} | {statistics.median(durs[k]):.2f} |")
+    lines += ["", f"HBM counters (FETCH_SIZE and WRITE_SIZE runs; KiB per dispatch x calibration: fetch factor "
+              f"{ff:.4f} from k_read_bw reading 1 GiB, write factor {wf:.4f} from k_dequant writing "
+              f"{int(write_ref)} bytes):", "",
+              "| operator | launches | HBM fetch bytes / launch | HBM write bytes / launch |", "|---|---|---|---|"]
+    for k in sorted(table, key=lambda k: -table[k]["fetch"]):
+        lines.append(f"| {k} | {table[k]['launches']} | {table[k]['fetch']:,} | {table[k]['write']:,} |")
+    lines += ["", f"Kernel sources hashed (lm_kernels.hip, lm_internal.h, lm_device.h): "
+              f"{kernel_source_digest()}; bench.py reports `roofline.traffic` from this file only while "
+              "that hash matches."]
+    with open(os.path.join(ROOT, "profiles", f"kernels_{workload}.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(f"wrote profiles/pmc_{workload}.json and profiles/kernels_{workload}.md")
 
 
 def host_threads() -> int:
@@ -652,8 +769,16 @@ def main():
                     help="also run two calibration dispatches of known traffic for HBM counters: "
                          "a plain read of 1 GiB (k_read_bw) and a dequant of 64 down-projection rows "
                          "that writes 64*ffn*4 bytes (k_dequant)")
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="no GPU: reduce rocprofv3 output of this script under DIR (trace/, fetch/, write/) "
+                         "to profiles/kernels_<workload>.md and profiles/pmc_<workload>.json")
+    ap.add_argument("--command", action="append", default=[],
+                    help="(with --summarize) a command that produced DIR, recorded in the summary")
     args = ap.parse_args()
 
+    if args.summarize:
+        summarize(args.summarize, args.workload, args.command)
+        return
     if args.gpus != 1:
         print(f"bench.py: measures one GPU; --gpus {args.gpus} is not supported "
               "(the per-GPU throughput is the --gpus 1 figure)", file=sys.stderr)
