@@ -222,7 +222,13 @@ lm_status lm_skip_similar_layers(lm_model* m, double threshold, int32_t* n_skipp
 lm_status lm_speculative_step(lm_model* m, int32_t token, int32_t draft_layers, int32_t k,
                               int32_t* tokens_out, int32_t* n_out);
 
-/* lm_set_residency(m, enable ? 0 : L): every layer streamed, or none. */
+/* 0: every layer resident (lm_set_residency(m, L)); 1: every layer streamed
+ * (lm_set_residency(m, 0)), each layer's copy overlapping the compute of the
+ * layers before it; 2: every layer streamed serially, as the baseline of the
+ * two-buffer pipeline of the "3 Agents" page's layer-loading section: a
+ * layer's copy starts only when every kernel before it has finished, and its
+ * kernels wait for it (copy, compute, copy, compute).  Outputs are the same
+ * in every mode.  Errors: those of lm_set_residency; LM_E_ARG (mode). */
 lm_status lm_stream_mode(lm_model* m, int32_t enable);
 
 /* The engine page's tier sizing (its section 4.1, compute_tier_sizes):

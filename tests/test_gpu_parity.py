@@ -239,9 +239,13 @@ def test_stream_mode_bit_identical(name):
         g.stream_mode(True)
         streamed = run()
         streamed2 = run()
+        g.stream_mode(2)                       # serial: copy, then compute, per layer
+        serial = run()
+        g.stream_mode(True)
+        streamed3 = run()
         g.stream_mode(False)
         back = run()
-        for other in (streamed, streamed2, back):
+        for other in (streamed, streamed2, serial, streamed3, back):
             for (a, b), (c, d) in zip(resident, other):
                 assert np.array_equal(a, c) and np.array_equal(b, d)
     finally:

@@ -233,8 +233,9 @@ class Model:
         self._check(self._lib.lm_decode_step_dev_noalloc(self._h, ptr(d_tokens), n_seq, ptr(d_logits),
                                                          ptr(d_argmax)))
 
-    def stream_mode(self, enable: bool):
-        self._check(self._lib.lm_stream_mode(self._h, 1 if enable else 0))
+    def stream_mode(self, enable):
+        """False / 0: resident; True / 1: streamed (pipelined); 2: streamed, copy then compute per layer."""
+        self._check(self._lib.lm_stream_mode(self._h, int(enable)))
 
     def set_residency(self, n_resident: int):
         """Layers 0..n_resident-1 in HBM, the rest streamed from pinned host memory."""

@@ -237,6 +237,11 @@ struct lm_model {
     hipEvent_t ev_copied[2] = {nullptr, nullptr};
     hipEvent_t ev_consumed[2] = {nullptr, nullptr};
     bool prefetched[2] = {false, false};   // the next step's first / second streamed layer is copied
+    // serial streaming (lm_stream_mode 2): a layer's copy starts when every
+    // kernel before it has finished (ev_serial on the compute stream), and
+    // nothing is copied ahead: copy, compute, copy, compute
+    bool stream_serial = false;
+    hipEvent_t ev_serial = nullptr;
 
     struct Pending { int kind; hipEvent_t a, b; };
     struct GraphEntry {
@@ -356,6 +361,8 @@ static void release_all(lm_model* m) {
         if (m->ev_consumed[i]) (void)hipEventDestroy(m->ev_consumed[i]);
         m->ev_copied[i] = m->ev_consumed[i] = nullptr;
     }
+    if (m->ev_serial) (void)hipEventDestroy(m->ev_serial);
+    m->ev_serial = nullptr;
     for (void* p : m->dev_allocs) (void)hipFree(p);
     m->dev_allocs.clear();
     for (void* p : m->host_allocs) (void)hipHostFree(p);
@@ -528,6 +535,7 @@ extern "C" lm_status lm_model_create(const lm_config* cfg, void* hip_stream, lm_
         CREATE_HIP(hipEventCreateWithFlags(&m->ev_copied[i], hipEventDisableTiming));
         CREATE_HIP(hipEventCreateWithFlags(&m->ev_consumed[i], hipEventDisableTiming));
     }
+    CREATE_HIP(hipEventCreateWithFlags(&m->ev_serial, hipEventDisableTiming));
     {
         int dev = 0, ncu = 0;
         CREATE_HIP(hipGetDevice(&dev));
@@ -1156,7 +1164,8 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
     at.out = m->sb.o;
 
     const int n_str = (int)m->str_list.size();     // streamed layers this step computes
-    for (int i = 0; i < std::min(n_str, 2); ++i)
+    const bool serial = m->stream_serial;
+    for (int i = 0; i < std::min(n_str, 2) && !serial; ++i)
         if (!m->prefetched[i]) {
             lm_status s = stream_copy(m, m->str_list[i]);
             if (s != LM_OK) return s;
@@ -1166,6 +1175,13 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
     for (int l = 0; l < L; ++l) {
         if (m->skip[l]) continue;                       // its input is its output
         if (m->opt_active && l >= m->opt_limit) continue;
+        if (layer_streamed(m, l) && serial) {
+            // everything before this layer has finished, then its copy alone
+            HIPTRY(m, hipEventRecord(m->ev_serial, st));
+            HIPTRY(m, hipStreamWaitEvent(m->copy_stream, m->ev_serial, 0));
+            lm_status s = stream_copy(m, l);
+            if (s != LM_OK) return s;
+        }
         if (layer_streamed(m, l)) HIPTRY(m, hipStreamWaitEvent(st, m->ev_copied[stream_slot(m, l)], 0));
         if (m->sim_on)                                  // the layer's input, for its similarity
             HIPTRY(m, hipMemcpyAsync(m->d_xin, m->sb.x, (size_t)n_seq * m->H * 4, hipMemcpyDeviceToDevice, st));
@@ -1219,7 +1235,7 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
         if (layer_streamed(m, l)) {
             HIPTRY(m, hipEventRecord(m->ev_consumed[stream_slot(m, l)], st));
             const int nx = m->str_idx[l] + 2;
-            if (nx < n_str) {
+            if (nx < n_str && !serial) {
                 lm_status s = stream_copy(m, m->str_list[nx]);
                 if (s != LM_OK) return s;
             }
@@ -1227,7 +1243,7 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
     }
     // start the next step's first two streamed layers while the LM head (and
     // the next step's resident layers) run
-    for (int i = 0; i < std::min(n_str, 2); ++i) {
+    for (int i = 0; i < std::min(n_str, 2) && !serial; ++i) {
         lm_status s = stream_copy(m, m->str_list[i]);
         if (s != LM_OK) return s;
         m->prefetched[i] = true;
@@ -1553,7 +1569,10 @@ extern "C" lm_status lm_set_residency(lm_model* m, int32_t n_resident) {
     const int L = m->cfg.n_layers;
     if (n_resident < 0 || n_resident > L)
         return fail(m, LM_E_ARG, "lm_set_residency: n_resident = %d; expected 0..%d", n_resident, L);
-    if (n_resident == m->n_res) return LM_OK;
+    if (n_resident == m->n_res) {
+        m->stream_serial = false;               // (serial streaming only through lm_stream_mode 2)
+        return LM_OK;
+    }
     HIPTRY(m, hipStreamSynchronize(m->stream));
     HIPTRY(m, hipStreamSynchronize(m->copy_stream));
     const int64_t B = m->blob_bytes;
@@ -1621,6 +1640,7 @@ extern "C" lm_status lm_set_residency(lm_model* m, int32_t n_resident) {
     rebuild_stream_order(m);
     m->prefetched[0] = m->prefetched[1] = false;
     invalidate_graphs(m);
+    m->stream_serial = false;
     return LM_OK;
 }
 
@@ -1683,7 +1703,15 @@ extern "C" lm_status lm_skip_similar_layers(lm_model* m, double threshold, int32
 
 extern "C" lm_status lm_stream_mode(lm_model* m, int32_t enable) {
     if (!m) return LM_E_ARG;
-    return lm_set_residency(m, enable ? 0 : m->cfg.n_layers);
+    if (enable < 0 || enable > 2) return fail(m, LM_E_ARG, "lm_stream_mode: mode = %d; expected 0, 1 or 2", enable);
+    lm_status st = lm_set_residency(m, enable ? 0 : m->cfg.n_layers);
+    if (st != LM_OK) return st;
+    HIPTRY(m, hipStreamSynchronize(m->stream));
+    HIPTRY(m, hipStreamSynchronize(m->copy_stream));
+    // nothing is left copied ahead of a step, whichever mode follows
+    m->prefetched[0] = m->prefetched[1] = false;
+    m->stream_serial = enable == 2;
+    return LM_OK;
 }
 
 // ---------------------------------------------------------------------------
