@@ -677,7 +677,10 @@ __global__ __launch_bounds__(64 * kMbWaves) void k_gemv_mb(GemvArgs a) {
     constexpr int XS = XL ? 1 : kMbGroup;              // digit operands a stage carries (global digits)
     struct Stage {
         uint4 w[TW][NF];    // weight fragments of this lane's row, per tile
-        uint2 sc[TW];       // the row's scales of the stage's four blocks, per tile
+        // scales of the stage's four blocks: TW = 1: this lane's row; else lane l
+        // holds those of row l % 16 of tile (l / 16) % TW, each read once per
+        // wavefront and handed to the lanes that need them (sc_of)
+        uint2 sc;
         uint2 x[XS];        // (digits from a.xfrag) this lane's digit fragment of each block
     };
     // tiles t0.. t0+TW-1 of the run (clamped to its last tile), stage k.
@@ -690,7 +693,10 @@ __global__ __launch_bounds__(64 * kMbWaves) void k_gemv_mb(GemvArgs a) {
             const uint4* qf = (const uint4*)a.w.qf + (int64_t)tile * ngrp * 64 + lane;
             #pragma unroll
             for (int f = 0; f < NF; ++f) st.w[t][f] = qf[(int64_t)min(k * NF + f, ngrp - 1) * 64];
-            st.sc[t] = *(const uint2*)(a.w.sct + (((int64_t)tile * ng4 + k) * 16 + j) * 4);
+        }
+        {
+            const int tile = tile_at(min(t0 + (TW == 1 ? 0 : (lane >> 4) % TW), t_end - 1));
+            st.sc = *(const uint2*)(a.w.sct + (((int64_t)tile * ng4 + k) * 16 + j) * 4);
         }
         if constexpr (!XL) {
             #pragma unroll
@@ -702,6 +708,17 @@ __global__ __launch_bounds__(64 * kMbWaves) void k_gemv_mb(GemvArgs a) {
     };
     float acc[TW];
     auto compute = [&](int k, const Stage& st) {
+        // this lane's row's scales for each tile: from lane 16 t + j (TW > 1)
+        uint2 sc_of[TW];
+        #pragma unroll
+        for (int t = 0; t < TW; ++t) {
+            if (TW == 1) {
+                sc_of[t] = st.sc;
+            } else {
+                sc_of[t].x = (uint32_t)__shfl((int)st.sc.x, 16 * t + j, 64);
+                sc_of[t].y = (uint32_t)__shfl((int)st.sc.y, 16 * t + j, 64);
+            }
+        }
         #pragma unroll
         for (int u = 0; u < kMbGroup; ++u) {
             const int b = k * kMbGroup + u;
@@ -735,7 +752,7 @@ __global__ __launch_bounds__(64 * kMbWaves) void k_gemv_mb(GemvArgs a) {
                     c[1] -= 8 * T.y;
                     c[2] -= 8 * T.z;
                 }
-                const uint2 sc = st.sc[t];
+                const uint2 sc = sc_of[t];
                 const float d = h2f((uint16_t)(u == 0 ? (sc.x & 0xFFFF) : u == 1 ? (sc.x >> 16)
                                                 : u == 2 ? (sc.y & 0xFFFF) : (sc.y >> 16)));
                 acc[t] = fmaf(d * sx, combine_digits(c[0], c[1], c[2]), acc[t]);
