@@ -398,16 +398,33 @@ def per_launch(kind: str, n_layers: int) -> int:
     return 1 if kind in ("embed", "lmhead") else n_layers
 
 
-def kernel_table(kstats, kbytes, n_layers):
+def graph_times(r, kstats, n_seq: int) -> dict:
+    """µs per launch of every kernel family, its launches of one step replayed
+    alone as a HIP graph (lm_time_kind) - without the cost of event nodes."""
+    out = {}
+    for k, (n, _) in kstats.items():
+        if n and k != "copy":
+            r.rewind()
+            out[k] = r.g.time_kind(k, n_seq, 20)
+    r.rewind()
+    return out
+
+
+def kernel_table(kstats, kbytes, n_layers, us_graph=None):
+    """Per family: launches in the timing steps, µs per launch (graph replay of
+    the family alone when given, else the events around each launch in the
+    step graph), algorithmic GB/s at that duration."""
     out = {}
     for k, (n, ms) in kstats.items():
         if not n:
             continue
-        avg_ms = ms / n
+        ev_us = 1e3 * ms / n
+        us = us_graph.get(k, ev_us) if us_graph else ev_us
         launches_per_step = per_launch(k, n_layers)
-        out[k] = {"launches": n, "avg_us": round(1e3 * avg_ms, 3),
-                  "algorithmic_GBps": round((kbytes[k] / launches_per_step) / (avg_ms * 1e-3) / 1e9, 1)
-                  if kbytes[k] else None}
+        out[k] = {"launches": n, "avg_us": round(us, 3),
+                  "algorithmic_GBps": round((kbytes[k] / launches_per_step) / (us * 1e-6) / 1e9, 1)
+                  if kbytes[k] else None,
+                  "avg_us_events_in_step": round(ev_us, 3)}
     return out
 
 
@@ -502,10 +519,8 @@ def run_single(args, name: str, n_seq: int):
     kstats, kbytes = r.kernel_profile(args.timing_steps)
     L = cfg.n_layers
     dom = dominant(kstats)
-    r.rewind()
-    us_graph = r.g.time_kind(dom, n_seq, 20)
-    r.rewind()
-    roofline = roofline_for(dom, kstats, kbytes, L, name, us_graph)
+    ug = graph_times(r, kstats, n_seq)
+    roofline = roofline_for(dom, kstats, kbytes, L, name, ug[dom])
     roofline["timing"] = ("the family's launches of one step captured alone as a HIP graph and replayed 20 "
                           "times between two HIP events on the model's stream")
     roofline["avg_launch_us_events_in_step"] = round(1e3 * kstats[dom][1] / max(kstats[dom][0], 1), 3)
@@ -541,7 +556,7 @@ def run_single(args, name: str, n_seq: int):
         r.rewind()
         out["step_ms_percentiles"] = r.step_percentiles(min(args.steps, 32))
         r.rewind()
-    out["kernels"] = kernel_table(kstats, kbytes, L)
+    out["kernels"] = kernel_table(kstats, kbytes, L, ug)
     out["inputs_sha256"] = input_digests(model, n_seq)
     # The headline fields are complete here.  The CPU baseline and the opt-in
     # side legs below only add fields: a failure in one of them becomes an
@@ -592,15 +607,16 @@ def run_multi(args):
     # kernel profile of the largest model (eager, alone)
     kstats, kbytes = runners[0].kernel_profile(args.timing_steps)
     dom = dominant(kstats)
+    ug = graph_times(runners[0], kstats, 1)
     config = {"workload": WORKLOAD_TEXT["multi"], "name": "multi", "batch": 1, "ctx": 2048, "qtype": "Q8_0",
               "models": names, "weights": "random N(0,0.02), quantized, resident in HBM"}
     out = base_line("decode tokens/s aggregate over three concurrently resident Q8_0 models "
                     "(round-robin, one HIP stream each)", 3000.0 / ms_per_round, ms_per_round, args.steps,
                     args.warmup, round_bytes, config)
     out["per_model_solo_tokens_per_s"] = {k: round(1000.0 / v, 2) for k, v in solo.items()}
-    out["roofline"] = roofline_for(dom, kstats, kbytes, cfgs[0].n_layers, "multi_llama1b")
+    out["roofline"] = roofline_for(dom, kstats, kbytes, cfgs[0].n_layers, "multi_llama1b", ug[dom])
     out["roofline"]["model"] = names[0]
-    out["kernels"] = kernel_table(kstats, kbytes, cfgs[0].n_layers)
+    out["kernels"] = kernel_table(kstats, kbytes, cfgs[0].n_layers, ug)
     for r in runners:
         r.close()
     if not args.no_cpu_baseline:
@@ -656,8 +672,9 @@ def run_70b(args, name="llama70b_q4"):
     kstats, kbytes = r.kernel_profile(args.timing_steps)
     step_bytes = r.step_bytes(args.steps // 2)
     dom = dominant(kstats)
-    roof = roofline_for(dom, kstats, kbytes, cfg.n_layers, name)
-    ktab = kernel_table(kstats, kbytes, cfg.n_layers)
+    ug = graph_times(r, kstats, 1)
+    roof = roofline_for(dom, kstats, kbytes, cfg.n_layers, name, ug[dom])
+    ktab = kernel_table(kstats, kbytes, cfg.n_layers, ug)
     # the resident step's compute time per step (eager, from the kernel events)
     compute_ms = sum(ms for k, (n, ms) in kstats.items() if k != "copy") / args.timing_steps
 

@@ -324,8 +324,9 @@ lm_status lm_kernel_timing(lm_model* m, int32_t enable);
 /* Average duration of one launch of kernel family `kind` as the step graph
  * runs it: the step's launches of that family alone (same arguments and
  * order; an LM-head-only replay does not advance positions) are captured as
- * one graph and replayed `reps` times between two HIP events on the model's
- * stream; result = elapsed / (reps x the family's launches per step).  It
+ * one graph (a family launched once per step: 32 copies of it) and replayed
+ * `reps` times between two HIP events on the model's stream; result =
+ * elapsed / (reps x the launches in the graph).  It
  * overwrites activations
  * and the current position's K/V row like a step (the next step rewrites
  * them).  Resident weights only.  For the roofline of a kernel family. */

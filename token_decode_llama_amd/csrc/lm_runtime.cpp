@@ -1743,10 +1743,15 @@ extern "C" lm_status lm_time_kind(lm_model* m, int32_t kind, int32_t n_seq, int3
     const int saved_timing = m->timing;
     m->timing = 0;
     m->only_kind = kind;
+    // a family launched once per step is captured 32 times over, so that one
+    // graph launch's own cost is spread as thinly as over a per-layer family
+    const bool once = kind == LM_K_EMBED || kind == LM_K_LMHEAD;
+    const int inner = once ? 32 : 1;
     hipGraph_t graph = nullptr;
     hipError_t e = hipStreamBeginCapture(m->stream, hipStreamCaptureModeThreadLocal);
     if (e == hipSuccess) {
-        st = enqueue_step(m, n_seq, m->d_tokens, nullptr, m->d_argmax);
+        for (int i = 0; i < inner && st == LM_OK; ++i)
+            st = enqueue_step(m, n_seq, m->d_tokens, nullptr, m->d_argmax);
         e = hipStreamEndCapture(m->stream, &graph);
     }
     m->only_kind = -1;
@@ -1782,8 +1787,7 @@ extern "C" lm_status lm_time_kind(lm_model* m, int32_t kind, int32_t n_seq, int3
     if (e != hipSuccess) return fail(m, LM_E_HIP, "lm_time_kind: %s", hipGetErrorString(e));
     // launches of the family per step (a launch may be more than one graph node:
     // the several-sequence GEMV stages its activations first)
-    const bool once = kind == LM_K_EMBED || kind == LM_K_LMHEAD;
-    const double launches = once ? 1.0 : (double)m->cfg.n_layers;
+    const double launches = once ? (double)inner : (double)m->cfg.n_layers;
     *us_per_launch = 1e3 * (double)ms / ((double)reps * launches);
     return LM_OK;
 }
