@@ -1051,26 +1051,27 @@ hipError_t launch_gemv_batched(const GemvArgs& a0, int epi, int n_seq, int max_b
 // GQA decode attention with causal softmax, split over context
 // ---------------------------------------------------------------------------
 // One workgroup of four wavefronts per (span of TP 64-position tiles, KV
-// head, sequence).  The span's K and V tiles are read with coalesced 16-byte
-// loads, the next tile's while the current one computes, and staged in LDS
-// (padded rows, V rows past the context zeroed); the group's G query heads
-// (at most kMaxGroup, padded to 16 rows) are scored against them and the
-// probabilities applied to V on the matrix cores (v_mfma_f32_16x16x16f16):
-//   scores S[head][key] = sum_d q[head][d] K[key][d]: wavefront w takes keys
-//     16w..16w+15; q enters as two fp16 terms, hi = fp16(q), lo = fp16(q - hi)
-//     (q to about 2^-22 relative; K is fp16 already), fp32 accumulation;
-//   online softmax over the span's tiles, causal mask = keys 0..pos: one LDS
-//     exchange of the per-wavefront maxima per tile, a running maximum M per
-//     head; p = exp(s - M) is written to LDS as fp16 hi + lo;
-//   o[head][d] = sum_key p V[key][d]: wavefront w takes the 16-column tiles
-//     of d in turn (HD / 64 of them), with every key of the tile.
-// In both products a lane's four results are four heads (rows 4(l/16)..+3) of
-// one key or one dimension (column l%16), so the per-head rescale factors a
-// lane computes in the softmax are the ones its o accumulators need.  A
-// context that fits one span writes o directly; otherwise each span
-// publishes its softmax state (m, l, o) with device-coherent stores, and the
-// last span of the (sequence, KV head) to finish merges all of them
-// (merge_chunk_states) within the same launch.
+// head, sequence); wavefront w takes keys 16w..16w+15 of every tile of the
+// span and runs its own online softmax over them, so a tile needs no
+// exchange between wavefronts.  The group's G query heads (at most
+// kMaxGroup, padded to 16) go through v_mfma_f32_16x16x16f16 twice per tile:
+//   scores, transposed: S^T[key][head] = sum_d K[key][d] q[head][d], with K
+//     as the first operand straight from the loaded registers (lane: key l%16,
+//     dimension pieces 8(4u + l/16) .. +7 of its row, 16-byte loads) and q as
+//     the second in the same dimension order; q enters as two fp16 terms,
+//     hi = fp16(q), lo = fp16(q - hi) (q to about 2^-22 relative; K is fp16
+//     already), fp32 accumulation.  A lane's four results are keys
+//     4(l/16)..+3 of head l%16: the layout of the probabilities as the first
+//     operand of the next product, so they never leave the lane;
+//   o[head][d] += sum_key p[head][key] V[key][d]: the wavefront's 16 V rows
+//     pass through its own LDS rows (read back by columns; rows past the
+//     context written as zeros, so a probability of 0 never meets a stale
+//     cache value), p as fp16 hi + lo.
+// At the end of the span the four wavefronts' states (maximum, sum, o) are
+// combined in LDS.  A context that fits one span writes o directly;
+// otherwise each span publishes its softmax state (m, l, o) with device-
+// coherent stores, and the last span of the (sequence, KV head) to finish
+// merges all of them (merge_chunk_states) within the same launch.
 constexpr int kMaxGroup = 8;   // query heads per KV head
 typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
@@ -1079,17 +1080,18 @@ template <int HD>
 __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
     static_assert(kBlock == 256 && kAttnChunk == 64, "four wavefronts, sixteen keys each");
     constexpr int CH = kAttnChunk;
-    constexpr int KP = HD + 8;                  // padded K / V row (halves): conflict-free operand reads
-    constexpr int PP = CH + 8;                  // padded P row (halves)
-    constexpr int PCS = CH * HD / 8 / kBlock;   // 16-byte pieces per thread per tile
+    constexpr int KP = HD + 8;                  // padded V row (halves): conflict-free column reads
+    constexpr int KL = HD / 32;                 // 16-byte pieces of a K (and of a V) row per lane
     constexpr int KS = HD / 16;                 // 16-dimension steps of the score product
-    constexpr int DT = HD / 64;                 // 16-column tiles of o per wavefront
-    static_assert(sizeof(float) * 6 * kBlock <= sizeof(__half) * CH * KP, "merge scratch fits in Ks");
-    __shared__ __align__(16) __half Ks[CH][KP];
-    __shared__ __align__(16) __half Vs[CH][KP];
-    __shared__ __align__(16) _Float16 Ph[16][PP], Pl[16][PP];
-    __shared__ float Mx[4][16], Lx[4][16];
+    constexpr int DT = HD / 16;                 // 16-column tiles of o
+    __shared__ __align__(16) __half Vw[4][16][KP];   // each wavefront's own V rows
+    __shared__ __align__(16) float Mw[4][16];
+    __shared__ float Lw[4][16];
     __shared__ int s_last;
+    // after the tiles: the wavefronts' o, then the merge scratch
+    float* xs = reinterpret_cast<float*>(&Vw[0][0][0]);
+    static_assert(sizeof(float) * 4 * kMaxGroup * HD <= sizeof(Vw), "o exchange fits in Vw");
+    static_assert(sizeof(float) * 6 * kBlock <= sizeof(Vw), "merge scratch fits in Vw");
 
     const int chunk = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1101,21 +1103,30 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
     const __half* Kg = a.kcache + (int64_t)s * a.kv_seq_stride + (int64_t)g * a.max_ctx * HD;
     const __half* Vg = a.vcache + (int64_t)s * a.kv_seq_stride + (int64_t)g * a.max_ctx * HD;
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // (native vectors: kept in registers)
-    u32x4 kr[PCS], vr[PCS];
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
     const int TP = a.tiles;                     // tiles of this workgroup's span
     const int t_first = chunk * TP;
-    #pragma unroll
-    for (int u = 0; u < PCS; ++u) {
-        const int c = tid + u * kBlock;
-        const int t = min(t_first * CH + c / (HD / 8), a.max_ctx - 1), d8 = (c % (HD / 8)) * 8;
-        kr[u] = *(const u32x4*)(Kg + (int64_t)t * HD + d8);
-        vr[u] = *(const u32x4*)(Vg + (int64_t)t * HD + d8);
-    }
-    // this lane's q operands: head lr (zero past G), dimensions 16k + 4lq .. +3
-    const float* qg = a.q + (int64_t)s * a.nq * HD + (int64_t)g * G * HD;
+    // this lane's K and V row of tile t: key 64t + 16 wave + lr, pieces 4u + lq
+    auto load = [&](int t, u32x4 (&kr)[KL], u32x4 (&vr)[KL]) {
+        const int64_t row = min(t * CH + 16 * wave + lr, a.max_ctx - 1);
+        #pragma unroll
+        for (int u = 0; u < KL; ++u) {
+            const int64_t off = row * HD + 8 * (4 * u + lq);
+            kr[u] = *(const u32x4*)(Kg + off);
+            vr[u] = *(const u32x4*)(Vg + off);
+        }
+    };
+    // this lane's q operands: head lr (zero past G), at step k the dimensions
+    // 32(k/2) + 8lq + 4(k%2) .. +3 (the order of its K pieces).  Requested
+    // first (needed first: the load counters are in order), then the first
+    // tile's K and V, all before any wait: one round trip.
+    const float* qg = a.q + (int64_t)s * a.nq * HD + (int64_t)g * G * HD + (int64_t)min(lr, G - 1) * HD;
     float4 qv[KS];
     #pragma unroll
-    for (int k = 0; k < KS; ++k) qv[k] = *(const float4*)(qg + (int64_t)min(lr, G - 1) * HD + 16 * k + 4 * lq);
+    for (int k = 0; k < KS; ++k) qv[k] = *(const float4*)(qg + 32 * (k >> 1) + 8 * lq + 4 * (k & 1));
+    u32x4 ka[KL], va[KL], kb[KL], vb[KL];
+    load(t_first, ka, va);
+    __builtin_amdgcn_sched_barrier(0);   // (the scheduler would otherwise hold V back behind the waits)
     const int n_ctx = a.pos[s] + 1;                       // keys 0..pos inclusive
     const int n_tiles = (n_ctx + CH - 1) / CH;
     const int n_act = (n_tiles + TP - 1) / TP;            // spans holding keys
@@ -1133,143 +1144,145 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
             ql[k][e] = (_Float16)(x - (float)hi);
         }
     }
-    // running state of this lane's four heads 4lq + i
-    float M[4], Lw[4];                // maximum (common to the wavefronts), this wavefront's sum
-    f4_t o[DT];                       // o[dt][i]: head 4lq + i, dimension 16 (DT wave + dt) + lr
-    #pragma unroll
-    for (int i = 0; i < 4; ++i) { M[i] = -FLT_MAX; Lw[i] = 0.f; }
+    // running state of this wavefront: maximum and sum of head lr (the same
+    // in the four lane groups), o[dt][i]: head 4lq + i, dimension 16dt + lr
+    float M = -FLT_MAX, L = 0.f;
+    f4_t o[DT];
     #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[dt] = f4_t{0.f, 0.f, 0.f, 0.f};
 
-    // every tile of the span runs (one past the context has no valid key and
-    // changes nothing)
-    for (int ti = 0; ti < TP; ++ti) {
-        const int tile = t_first + ti;
-        const int nt = max(0, min(CH, n_ctx - tile * CH));
-        if (ti > 0) __syncthreads();                      // the previous tile's readers are done
-        #pragma unroll
-        for (int u = 0; u < PCS; ++u) {
-            const int c = tid + u * kBlock;
-            const int t = c / (HD / 8), d8 = (c % (HD / 8)) * 8;
-            *(u32x4*)&Ks[t][d8] = kr[u];
-            // V rows past the context are zeroed: their probability is 0, and
-            // 0 times a stale cache value must stay 0
-            *(u32x4*)&Vs[t][d8] = t < nt ? vr[u] : u32x4{0u, 0u, 0u, 0u};
-        }
-        if (ti + 1 < TP) {                                // in flight while this tile computes
-            #pragma unroll
-            for (int u = 0; u < PCS; ++u) {
-                const int c = tid + u * kBlock;
-                const int t = min((tile + 1) * CH + c / (HD / 8), a.max_ctx - 1), d8 = (c % (HD / 8)) * 8;
-                kr[u] = *(const u32x4*)(Kg + (int64_t)t * HD + d8);
-                vr[u] = *(const u32x4*)(Vg + (int64_t)t * HD + d8);
-            }
-        }
-        __syncthreads();
-
-        // ---- scores of keys 16 wave + lr, heads 4lq + i
-        f4_t sc = {0.f, 0.f, 0.f, 0.f};
+    // one tile (a tile past the context has no valid key and changes nothing)
+    auto step = [&](int tile, const u32x4 (&kr)[KL], const u32x4 (&vr)[KL]) {
+        // scores of keys 4lq + i (of this wavefront's 16), head lr
+        f4_t sh = {0.f, 0.f, 0.f, 0.f}, sl = {0.f, 0.f, 0.f, 0.f};
         #pragma unroll
         for (int k = 0; k < KS; ++k) {
-            const h4_t kb = *(const h4_t*)&Ks[16 * wave + lr][16 * k + 4 * lq];
-            sc = __builtin_amdgcn_mfma_f32_16x16x16f16(qh[k], kb, sc, 0, 0, 0);
-            sc = __builtin_amdgcn_mfma_f32_16x16x16f16(ql[k], kb, sc, 0, 0, 0);
+            const u32x4 pc = kr[k >> 1];
+            const h4_t kk = __builtin_bit_cast(h4_t, (k & 1) ? u32x2{pc.z, pc.w} : u32x2{pc.x, pc.y});
+            sh = __builtin_amdgcn_mfma_f32_16x16x16f16(kk, qh[k], sh, 0, 0, 0);
+            sl = __builtin_amdgcn_mfma_f32_16x16x16f16(kk, ql[k], sl, 0, 0, 0);
         }
-        const bool live = 16 * wave + lr < nt;
-        float sv[4], mw[4];
+        // this wavefront's V rows into its LDS rows (past the context: zeros)
+        const bool vlive = tile * CH + 16 * wave + lr < n_ctx;
+        #pragma unroll
+        for (int u = 0; u < KL; ++u)
+            *(u32x4*)&Vw[wave][lr][8 * (4 * u + lq)] = vlive ? vr[u] : u32x4{0u, 0u, 0u, 0u};
+        // online softmax of head lr over this wavefront's keys
+        const int key0 = tile * CH + 16 * wave + 4 * lq;
+        float sv[4], mt = -FLT_MAX;
         #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            sv[i] = live ? sc[i] * a.scale : -FLT_MAX;
-            mw[i] = sv[i];
+            sv[i] = key0 + i < n_ctx ? (sh[i] + sl[i]) * a.scale : -FLT_MAX;
+            mt = fmaxf(mt, sv[i]);
         }
-        #pragma unroll
-        for (int off = 1; off < 16; off <<= 1)
-            #pragma unroll
-            for (int i = 0; i < 4; ++i) mw[i] = fmaxf(mw[i], __shfl_xor(mw[i], off, 64));
-        if (lr == 0) {
-            #pragma unroll
-            for (int i = 0; i < 4; ++i) Mx[wave][4 * lq + i] = mw[i];
-        }
-        __syncthreads();
-
-        // ---- online softmax: the tile's maximum, p, the rescale of the running state
-        float r[4];
+        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const float mn = fmaxf(M, mt);
+        const float r = __expf(M - mn);                   // 0 on the first live tile
+        M = mn;
+        h4_t pa, pb;
+        float ps = 0.f;
         #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int h = 4 * lq + i;
-            const float mt = fmaxf(fmaxf(Mx[0][h], Mx[1][h]), fmaxf(Mx[2][h], Mx[3][h]));
-            const float mn = fmaxf(M[i], mt);
-            r[i] = __expf(M[i] - mn);                     // 0 on the first tile
-            M[i] = mn;
-            const float p = live ? __expf(sv[i] - mn) : 0.f;
+            const float p = key0 + i < n_ctx ? __expf(sv[i] - mn) : 0.f;
             const _Float16 ph = (_Float16)p;
-            Ph[h][16 * wave + lr] = ph;
-            Pl[h][16 * wave + lr] = (_Float16)(p - (float)ph);
-            float ps = p;
-            #pragma unroll
-            for (int off = 1; off < 16; off <<= 1) ps += __shfl_xor(ps, off, 64);
-            Lw[i] = fmaf(Lw[i], r[i], ps);
+            pa[i] = ph;
+            pb[i] = (_Float16)(p - (float)ph);
+            ps += p;
         }
+        ps += __shfl_xor(ps, 16, 64);
+        ps += __shfl_xor(ps, 32, 64);
+        L = fmaf(L, r, ps);
+        // the rescale of o's heads 4lq + i: r of head h sits in lane h
         #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+        for (int i = 0; i < 4; ++i) {
+            const float ri = __shfl(r, 4 * lq + i, 64);
             #pragma unroll
-            for (int i = 0; i < 4; ++i) o[dt][i] *= r[i];
-        __syncthreads();
-
-        // ---- o += p V over the tile's keys: column tiles DT wave .. DT wave + DT - 1
-        #pragma unroll
-        for (int kq = 0; kq < CH / 16; ++kq) {
-            const h4_t pa = *(const h4_t*)&Ph[lr][16 * kq + 4 * lq];
-            const h4_t pb = *(const h4_t*)&Pl[lr][16 * kq + 4 * lq];
-            #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const int d = 16 * (DT * wave + dt) + lr;
-                h4_t vb;
-                #pragma unroll
-                for (int e = 0; e < 4; ++e) vb[e] = *(const _Float16*)&Vs[16 * kq + 4 * lq + e][d];
-                o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vb, o[dt], 0, 0, 0);
-                o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(pb, vb, o[dt], 0, 0, 0);
-            }
+            for (int dt = 0; dt < DT; ++dt) o[dt][i] *= ri;
         }
+        // the V rows written above, read by columns (this wavefront's own
+        // rows: its LDS operations complete in order once counted)
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        #pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            h4_t vv;
+            #pragma unroll
+            for (int e = 0; e < 4; ++e) vv[e] = *(const _Float16*)&Vw[wave][4 * lq + e][16 * dt + lr];
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vv, o[dt], 0, 0, 0);
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(pb, vv, o[dt], 0, 0, 0);
+        }
+        // the next tile's V stores come after these reads
+        asm volatile("" ::: "memory");
+    };
+    // the next tile's loads are requested before this one computes (the
+    // scheduling barriers keep them there)
+    for (int ti = 0; ti < TP; ti += 2) {
+        if (ti + 1 < TP) load(t_first + ti + 1, kb, vb);
+        __builtin_amdgcn_sched_barrier(0);
+        step(t_first + ti, ka, va);
+        if (ti + 1 >= TP) break;
+        if (ti + 2 < TP) load(t_first + ti + 2, ka, va);
+        __builtin_amdgcn_sched_barrier(0);
+        step(t_first + ti + 1, kb, vb);
     }
 
-    // ---- the span's l per head: the four wavefronts' sums
-    if (lr == 0) {
-        #pragma unroll
-        for (int i = 0; i < 4; ++i) Lx[wave][4 * lq + i] = Lw[i];
+    // ---- the four wavefronts' states: the span's maximum per head, each
+    // wavefront's o scaled to it, summed in LDS
+    if (lq == 0) {
+        Mw[wave][lr] = M;
+        Lw[wave][lr] = L;
     }
     __syncthreads();
-    float L[4];
-    #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int h = 4 * lq + i;
-        L[i] = Lx[0][h] + Lx[1][h] + Lx[2][h] + Lx[3][h];
-    }
-
-    float* part_s = a.part + (int64_t)s * a.nq * a.max_chunks * stride;
-    float* out_s = a.out + (int64_t)s * a.nq * HD + (int64_t)g * G * HD;
-    if (n_act == 1) {
+    {
+        // heads 4lq .. 4lq + 3 of this lane's o: the four wavefronts' maxima
+        float4 mw[4];
+        #pragma unroll
+        for (int w = 0; w < 4; ++w) mw[w] = *(const float4*)&Mw[w][4 * lq];
+        const float4 own = *(const float4*)&Mw[wave][4 * lq];
+        const float mo[4] = {own.x, own.y, own.z, own.w};
         #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int h = 4 * lq + i;
-            if (h < G) {
-                const float inv = 1.f / L[i];
+            const float m0 = i == 0 ? mw[0].x : i == 1 ? mw[0].y : i == 2 ? mw[0].z : mw[0].w;
+            const float m1 = i == 0 ? mw[1].x : i == 1 ? mw[1].y : i == 2 ? mw[1].z : mw[1].w;
+            const float m2 = i == 0 ? mw[2].x : i == 1 ? mw[2].y : i == 2 ? mw[2].z : mw[2].w;
+            const float m3 = i == 0 ? mw[3].x : i == 1 ? mw[3].y : i == 2 ? mw[3].z : mw[3].w;
+            const float f = __expf(mo[i] - fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)));
+            if (4 * lq + i < G) {
                 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) out_s[h * HD + 16 * (DT * wave + dt) + lr] = o[dt][i] * inv;
+                for (int dt = 0; dt < DT; ++dt) xs[(wave * G + 4 * lq + i) * HD + 16 * dt + lr] = o[dt][i] * f;
             }
         }
-        return;
     }
-    #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int h = 4 * lq + i;
-        if (h < G) {
+    __syncthreads();
+
+    // a thread per (head, 4 dimensions): the sum over the wavefronts
+    float* part_s = a.part + (int64_t)s * a.nq * a.max_chunks * stride;
+    float* out_s = a.out + (int64_t)s * a.nq * HD + (int64_t)g * G * HD;
+    for (int idx = tid; idx < G * HD / 4; idx += kBlock) {
+        const int h = idx / (HD / 4), d = (idx % (HD / 4)) * 4;
+        const float mt = fmaxf(fmaxf(Mw[0][h], Mw[1][h]), fmaxf(Mw[2][h], Mw[3][h]));
+        float lt = 0.f;
+        float4 ot = make_float4(0.f, 0.f, 0.f, 0.f);
+        #pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            lt = fmaf(Lw[w][h], __expf(Mw[w][h] - mt), lt);
+            const float4 v = *(const float4*)&xs[(w * G + h) * HD + d];
+            ot.x += v.x;
+            ot.y += v.y;
+            ot.z += v.z;
+            ot.w += v.w;
+        }
+        if (n_act == 1) {
+            const float inv = 1.f / lt;
+            *(float4*)(out_s + h * HD + d) = make_float4(ot.x * inv, ot.y * inv, ot.z * inv, ot.w * inv);
+        } else {
             float* ph = part_s + ((int64_t)(g * G + h) * a.max_chunks + chunk) * stride;
-            #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) st_dev(ph + 16 * (DT * wave + dt) + lr, o[dt][i]);
-            if (wave == 0 && lr == 0) st_dev2(ph + HD, M[i], L[i]);
+            st_dev2(ph + d, ot.x, ot.y);
+            st_dev2(ph + d + 2, ot.z, ot.w);
+            if (d == 0) st_dev2(ph + HD, mt, lt);
         }
     }
+    if (n_act == 1) return;
 
     // ---- the last span of this (sequence, KV head) merges every span.  The
     // partials are device-coherent stores; each wavefront waits for its own
@@ -1287,7 +1300,7 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
         G, n_act, [&](int j) { return part_g + (int64_t)j * a.max_chunks * stride; },
         [](const float* p) { return ld_dev2(p); },
         [&](int i, float4 v) { *(float4*)(out_s + i) = v; },
-        reinterpret_cast<float (*)[6]>(&Ks[0][0]));
+        reinterpret_cast<float (*)[6]>(xs));
 }
 
 // Tiles per attention workgroup: as few as keep the whole grid resident at
