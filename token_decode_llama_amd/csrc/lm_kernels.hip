@@ -138,6 +138,7 @@ __global__ __launch_bounds__(NT, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a) {
 
     int rope_p = 0;                       // the position (read after the weight requests)
     float pre_cs = 1.f, pre_sn = 0.f;     // RoPE cos/sin of the first row pair (below)
+    float2 pre_res = make_float2(0.f, 0.f);   // residual of the first row pair (below)
 
     // Branch-free loads (clamped addresses; a block past the row end gets
     // scale 0) so the compiler's in-order load counters stay exact and the
@@ -244,11 +245,8 @@ __global__ __launch_bounds__(NT, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a) {
         if (c % cps != cps - 1) return;
         const int i = c / cps;
         const int r0 = (step0 + i * sstride) * kRowsPerStep + rg * 2;
-        #pragma unroll
-        for (int off = LPR / 2; off > 0; off >>= 1) {
-            acc0 += __shfl_xor(acc0, off, 64);
-            acc1 += __shfl_xor(acc1, off, 64);
-        }
+        acc0 = group_sum<LPR>(acc0);
+        acc1 = group_sum<LPR>(acc1);
         const float y0 = acc0 * rscale, y1 = acc1 * rscale;
         acc0 = 0.f;
         acc1 = 0.f;
@@ -281,7 +279,7 @@ __global__ __launch_bounds__(NT, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a) {
             }
         } else if (EPI == EPI_RESID) {
             float* xo = a.out + (int64_t)s * a.out_stride + r0;
-            float2 v = *(float2*)xo;
+            float2 v = i == 0 ? pre_res : *(float2*)xo;
             v.x += y0;
             v.y += y1;
             *(float2*)xo = v;
@@ -363,6 +361,16 @@ __global__ __launch_bounds__(NT, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a) {
         const int pi = (rr % a.head_dim) >> 1;
         pre_cs = a.rope_cos[(int64_t)rope_p * (a.head_dim >> 1) + pi];
         pre_sn = a.rope_sin[(int64_t)rope_p * (a.head_dim >> 1) + pi];
+    }
+    // the residual the first row pair adds to, likewise behind the weights
+    // (only this row pair's lanes write it, after the read).  A vector load:
+    // the address is uniform, and a scalar load in flight would make the
+    // main loop's LDS waits wait for it too.
+    if (EPI == EPI_RESID) {
+        int vzero;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(vzero));
+        const int r0 = min(step0 * kRowsPerStep + rg * 2, N - 2) + vzero;
+        pre_res = *(const float2*)(a.out + (int64_t)s * a.out_stride + r0);
     }
 
     // ---- pipeline: a chunk's registers are refilled (chunk c+2) as soon as
