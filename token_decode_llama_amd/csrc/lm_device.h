@@ -54,11 +54,6 @@ __device__ __forceinline__ float h2f(uint16_t h) {
     return __half2float(__ushort_as_half(h));
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-    #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
 // Sum over aligned groups of N lanes (N = 8, 16, 32 or 64), the result in
 // every lane of the group, without an LDS round trip: DPP moves inside a quad
 // (xor 1, xor 2), the mirrors inside each half row and row (8, 16 lanes), then
@@ -81,11 +76,44 @@ __device__ __forceinline__ float group_sum(float v) {
     }
     return v;
 }
-__device__ __forceinline__ float wave_max(float v) {
-    #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
+// The four rows (16 lanes each) of x, each broadcast to every lane: out[r]
+// in lane l = x in lane 16 r + l % 16.  v_permlane16_swap of x with itself
+// gives rows (0, 0, 2, 2) and (1, 1, 3, 3); v_permlane32_swap of each of
+// those with itself splits them into single rows.
+__device__ __forceinline__ void row_bcast4(uint32_t x, uint32_t (&out)[4]) {
+    const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(a[0], a[0], false, false);
+    const auto c = __builtin_amdgcn_permlane32_swap(a[1], a[1], false, false);
+    out[0] = b[0];
+    out[1] = c[0];
+    out[2] = b[1];
+    out[3] = c[1];
 }
+// Rows (0, 0, 2, 2) and (1, 1, 3, 3) of x: out[0] in lane l = x in lane
+// 32 (l / 32) + l % 16, out[1] = x in lane 32 (l / 32) + 16 + l % 16.
+__device__ __forceinline__ void row_bcast2(uint32_t x, uint32_t (&out)[2]) {
+    const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    out[0] = a[0];
+    out[1] = a[1];
+}
+// max / sum with the lane 16 and 32 apart (all lanes get the result)
+__device__ __forceinline__ float max_xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 
 // (value, index) maximum with the lowest index winning ties
 __device__ __forceinline__ void better(float& bv, int& bi, float v, int i) {

@@ -569,8 +569,9 @@ __device__ __forceinline__ float block_digits(const float (&v)[8], uint2 (&w)[3]
     float m = 0.f;
     #pragma unroll
     for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
-    m = fmaxf(m, __shfl_xor(m, 1, 64));
-    m = fmaxf(m, __shfl_xor(m, 2, 64));
+    // (the block's four lanes are a quad: DPP moves, no LDS round trip)
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1, 0xF, 0xF, false)));  // quad_perm [1,0,3,2]
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xF, 0xF, false)));  // quad_perm [2,3,0,1]
     const float f = m > 0.f ? 8323072.0f / m : 0.f;         // 127 * 2^16 / max|x_b|
     uint32_t p[3][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}};
     t[0] = t[1] = t[2] = 0;
@@ -588,8 +589,7 @@ __device__ __forceinline__ float block_digits(const float (&v)[8], uint2 (&w)[3]
     }
     #pragma unroll
     for (int d = 0; d < 3; ++d) {
-        t[d] += __shfl_xor(t[d], 1, 64);
-        t[d] += __shfl_xor(t[d], 2, 64);
+        t[d] = sum4(t[d]);
         w[d] = make_uint2(p[d][0], p[d][1]);
     }
     return m;
@@ -717,15 +717,22 @@ __global__ __launch_bounds__(64 * kMbWaves) void k_gemv_mb(GemvArgs a) {
     float acc[TW];
     auto compute = [&](int k, const Stage& st) {
         // this lane's row's scales for each tile: from lane 16 t + j (TW > 1)
+        // (rows 16 t .. 16 t + 15 hold tile t's: broadcast with row swaps)
         uint2 sc_of[TW];
-        #pragma unroll
-        for (int t = 0; t < TW; ++t) {
-            if (TW == 1) {
-                sc_of[t] = st.sc;
-            } else {
-                sc_of[t].x = (uint32_t)__shfl((int)st.sc.x, 16 * t + j, 64);
-                sc_of[t].y = (uint32_t)__shfl((int)st.sc.y, 16 * t + j, 64);
-            }
+        if constexpr (TW == 1) {
+            sc_of[0] = st.sc;
+        } else if constexpr (TW == 2) {
+            uint32_t bx[2], by[2];
+            row_bcast2(st.sc.x, bx);
+            row_bcast2(st.sc.y, by);
+            sc_of[0] = make_uint2(bx[0], by[0]);
+            sc_of[1] = make_uint2(bx[1], by[1]);
+        } else {
+            uint32_t bx[4], by[4];
+            row_bcast4(st.sc.x, bx);
+            row_bcast4(st.sc.y, by);
+            #pragma unroll
+            for (int t = 0; t < TW; ++t) sc_of[t] = make_uint2(bx[t], by[t]);
         }
         #pragma unroll
         for (int u = 0; u < kMbGroup; ++u) {
@@ -866,7 +873,8 @@ __global__ __launch_bounds__(64 * kMbWaves) void k_gemv_mb(GemvArgs a) {
             #pragma unroll
             for (int w = 0; w < kMbWaves; ++w) y += part[rq & 1][w][wave][lane];
             y *= rms;
-            const float y1 = __shfl_down(y, 1, 16);           // row j + 1 of the same sequence
+            // row j + 1 of the same sequence (row_shl:1; lane 15's value is unused)
+            const float y1 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y), 0x101, 0xF, 0xF, false));
             const int s = g, r0 = tile * 16 + j;               // rows r0, r0 + 1 (a RoPE / gate-up pair)
             if (s < a.n_seq && (j & 1) == 0) {
                 const float y0 = y;
@@ -1183,8 +1191,7 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
             sv[i] = key0 + i < n_ctx ? (sh[i] + sl[i]) * a.scale : -FLT_MAX;
             mt = fmaxf(mt, sv[i]);
         }
-        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        mt = max_xor32(max_xor16(mt));
         const float mn = fmaxf(M, mt);
         const float r = __expf(M - mn);                   // 0 on the first live tile
         M = mn;
@@ -1198,13 +1205,16 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
             pb[i] = (_Float16)(p - (float)ph);
             ps += p;
         }
-        ps += __shfl_xor(ps, 16, 64);
-        ps += __shfl_xor(ps, 32, 64);
+        ps = sum_xor32(sum_xor16(ps));
         L = fmaf(L, r, ps);
-        // the rescale of o's heads 4lq + i: r of head h sits in lane h
+        // the rescale of o's heads 4lq + i: r of head h sits in lane h (heads
+        // past kMaxGroup are padding: lanes lq >= 2 take any finite factor)
+        float rh[8];
+        #pragma unroll
+        for (int h = 0; h < 8; ++h) rh[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), h));
         #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float ri = __shfl(r, 4 * lq + i, 64);
+            const float ri = lq == 0 ? rh[i] : rh[4 + i];
             #pragma unroll
             for (int dt = 0; dt < DT; ++dt) o[dt][i] *= ri;
         }
