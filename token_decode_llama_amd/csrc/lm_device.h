@@ -120,6 +120,37 @@ __device__ __forceinline__ void better(float& bv, int& bi, float v, int i) {
     if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
 }
 
+// (value, index) maximum over aligned groups of N lanes (N = 16 or 64), the
+// result in every lane of the group: the steps of group_sum, applied to the
+// value and its index alike.
+template <int N>
+__device__ __forceinline__ void group_argmax(float& bv, int& bi) {
+    static_assert(N == 16 || N == 64, "group of 16 or 64 lanes");
+    #define LMK_DPP_STEP(ctrl)                                                                         \
+        {                                                                                              \
+            const float ov = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(bv), ctrl, 0xF, 0xF, false)); \
+            const int oi = __builtin_amdgcn_mov_dpp(bi, ctrl, 0xF, 0xF, false);                        \
+            better(bv, bi, ov, oi);                                                                    \
+        }
+    LMK_DPP_STEP(0xB1)    // quad_perm [1,0,3,2]
+    LMK_DPP_STEP(0x4E)    // quad_perm [2,3,0,1]
+    LMK_DPP_STEP(0x141)   // row_half_mirror
+    LMK_DPP_STEP(0x140)   // row_mirror
+    #undef LMK_DPP_STEP
+    if (N == 64) {
+        const auto v16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
+        const auto i16 = __builtin_amdgcn_permlane16_swap((uint32_t)bi, (uint32_t)bi, false, false);
+        bv = __uint_as_float(v16[0]);
+        bi = (int)i16[0];
+        better(bv, bi, __uint_as_float(v16[1]), (int)i16[1]);
+        const auto v32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
+        const auto i32 = __builtin_amdgcn_permlane32_swap((uint32_t)bi, (uint32_t)bi, false, false);
+        bv = __uint_as_float(v32[0]);
+        bi = (int)i32[0];
+        better(bv, bi, __uint_as_float(v32[1]), (int)i32[1]);
+    }
+}
+
 // Activations enter the integer dot products as 24-bit fixed point: per
 // 32-column block b, X_i = rint(x_i * 127*2^16 / max|x_b|), split into three
 // balanced signed 8-bit digits X = D2*2^16 + D1*2^8 + D0 (two's-complement

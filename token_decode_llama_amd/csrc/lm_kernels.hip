@@ -402,12 +402,7 @@ __global__ __launch_bounds__(NT, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a) {
     }
     if (EPI == EPI_LOGITS) {
         // workgroup maximum, then the last workgroup of the sequence reduces
-        #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const float ov = __shfl_xor(best_v, off, 64);
-            const int oi = __shfl_xor(best_i, off, 64);
-            better(best_v, best_i, ov, oi);
-        }
+        group_argmax<64>(best_v, best_i);
         if (lane == 0) { wv_best[wave] = best_v; wi_best[wave] = best_i; }
         __syncthreads();
         if (tid == 0) {
@@ -428,12 +423,7 @@ __global__ __launch_bounds__(NT, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a) {
             for (int i = tid; i < (int)gridDim.x; i += NT)
                 better(bv, bi, ld_dev(&a.part_val[(int64_t)s * gridDim.x + i]),
                        ld_dev(&a.part_idx[(int64_t)s * gridDim.x + i]));
-            #pragma unroll
-            for (int off = 32; off > 0; off >>= 1) {
-                const float ov = __shfl_xor(bv, off, 64);
-                const int oi = __shfl_xor(bi, off, 64);
-                better(bv, bi, ov, oi);
-            }
+            group_argmax<64>(bv, bi);
             if (lane == 0) { wv_best[wave] = bv; wi_best[wave] = bi; }
             __syncthreads();
             if (tid == 0) {
@@ -778,6 +768,15 @@ __global__ __launch_bounds__(64 * kMbWaves) void k_gemv_mb(GemvArgs a) {
     Stage sa, sb;
     const bool has_k = k_lo < k_hi;
     if (has_k && t_begin < t_end) load(t_begin, k_lo, sa);
+    // EPI_RESID: the residual that round 0's finishing lane adds to,
+    // requested right behind the first stage (clamped; every workgroup holds
+    // at least one tile)
+    float2 pre_res = make_float2(0.f, 0.f);
+    if (EPI == EPI_RESID) {
+        const int tile = tile_at(min(t_begin + min(wave, TW - 1), t_end - 1));
+        pre_res = *(const float2*)(a.out + (int64_t)min(g, a.n_seq - 1) * a.out_stride +
+                                   min(tile * 16 + (j & ~1), N - 2));
+    }
 
     if constexpr (!XL) {
         // the activation scales and digit sums of every block (nb x 80 bytes,
@@ -903,7 +902,7 @@ __global__ __launch_bounds__(64 * kMbWaves) void k_gemv_mb(GemvArgs a) {
                     }
                 } else if (EPI == EPI_RESID) {
                     float* xo = a.out + (int64_t)s * a.out_stride + r0;
-                    float2 v = *(float2*)xo;
+                    float2 v = rq == 0 ? pre_res : *(float2*)xo;
                     v.x += y0;
                     v.y += y1;
                     *(float2*)xo = v;
@@ -955,12 +954,7 @@ __global__ __launch_bounds__(64 * kMbWaves) void k_gemv_mb(GemvArgs a) {
         // this workgroup's best row per sequence: over the tile rows (lanes j
         // of group g), then the wavefronts; handed to the last workgroup as the
         // attention chunks hand over their states (lm_device.h)
-        #pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-            const float ov = __shfl_xor(best_v, off, 64);
-            const int oi = __shfl_xor(best_i, off, 64);
-            better(best_v, best_i, ov, oi);
-        }
+        group_argmax<16>(best_v, best_i);
         if (j == 0) {
             wv_best[wave][g] = best_v;
             wi_best[wave][g] = best_i;
@@ -983,12 +977,7 @@ __global__ __launch_bounds__(64 * kMbWaves) void k_gemv_mb(GemvArgs a) {
                 int bi = INT_MAX;
                 for (int i = tid; i < G; i += NT)
                     better(bv, bi, ld_dev(&a.part_val[(int64_t)s * G + i]), ld_dev(&a.part_idx[(int64_t)s * G + i]));
-                #pragma unroll
-                for (int off = 32; off > 0; off >>= 1) {
-                    const float ov = __shfl_xor(bv, off, 64);
-                    const int oi = __shfl_xor(bi, off, 64);
-                    better(bv, bi, ov, oi);
-                }
+                group_argmax<64>(bv, bi);
                 if (lane == 0) {
                     wv_best[wave][s] = bv;
                     wi_best[wave][s] = bi;
