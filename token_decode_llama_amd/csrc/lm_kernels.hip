@@ -765,9 +765,45 @@ __global__ __launch_bounds__(64 * kMbWaves) void k_gemv_mb(GemvArgs a) {
         }
     };
 
-    Stage sa, sb;
+    // steps i = 0 .. S-1: round i / n_k, stage k_lo + i % n_k.  D stages in
+    // flight (deeper measured slower): step i + D - 1 is requested before step i computes (requests
+    // past the last step repeat it: clamped, so the load counts the compiler
+    // tracks are exact); the first D - 1 go out before the prologue.
+    constexpr int D = 2;
     const bool has_k = k_lo < k_hi;
-    if (has_k && t_begin < t_end) load(t_begin, k_lo, sa);
+    const int n_rounds = (t_end - t_begin + TW - 1) / TW;
+    const int n_k = k_hi - k_lo, S = n_rounds * n_k;
+    auto issue = [&](int i, Stage& st) {
+        const int ic = min(i, S - 1);
+        const int rq = ic / n_k;
+        load(t_begin + rq * TW, k_lo + (ic - rq * n_k), st);
+    };
+    // XL: the prologue's first batch of the input (and the gain) is requested
+    // before any weight: the load counters are in order, so the digits can
+    // then be computed while the weights are still arriving
+    constexpr int MAXI = (kMbLdsMaxK / 8 + NT - 1) / NT;   // prologue batches
+    const int cpr = K >> 3;                                   // 8-column items per sequence
+    const bool gain = XL && a.norm_g != nullptr;
+    float4 xv0[4][2], gv00 = make_float4(1.f, 1.f, 1.f, 1.f), gv01 = gv00;
+    if constexpr (XL) {
+        const int cc = tid < cpr ? tid : 0;
+        if (gain) {
+            gv00 = *(const float4*)(a.norm_g + 8 * cc);
+            gv01 = *(const float4*)(a.norm_g + 8 * cc + 4);
+        }
+        #pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const float* xs = a.xin + (int64_t)min(s, a.n_seq - 1) * a.x_stride + 8 * cc;
+            xv0[s][0] = *(const float4*)xs;
+            xv0[s][1] = *(const float4*)(xs + 4);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    Stage st[D];
+    if (has_k && t_begin < t_end) {
+        #pragma unroll
+        for (int p = 0; p < D - 1; ++p) issue(p, st[p]);
+    }
     // EPI_RESID: the residual that round 0's finishing lane adds to,
     // requested right behind the first stage (clamped; every workgroup holds
     // at least one tile)
@@ -791,9 +827,6 @@ __global__ __launch_bounds__(64 * kMbWaves) void k_gemv_mb(GemvArgs a) {
     // slots of a column group in one thread, so the gain is read once
     float rms = 1.f;            // the RMS factor of this lane's sequence g
     if constexpr (XL) {
-        constexpr int MAXI = (kMbLdsMaxK / 8 + NT - 1) / NT;
-        const int cpr = K >> 3;
-        const bool gain = a.norm_g != nullptr;
         float ssq[4] = {0.f, 0.f, 0.f, 0.f};
         #pragma unroll
         for (int i = 0; i < MAXI; ++i) {
@@ -801,17 +834,25 @@ __global__ __launch_bounds__(64 * kMbWaves) void k_gemv_mb(GemvArgs a) {
             if (i > 0 && c - (tid & 3) >= cpr) break;       // (whole blocks, uniform per block)
             const bool in = c < cpr;
             const int cc = in ? c : 0;
-            float4 gv0 = make_float4(1.f, 1.f, 1.f, 1.f), gv1 = gv0;
-            if (gain) {
-                gv0 = *(const float4*)(a.norm_g + 8 * cc);
-                gv1 = *(const float4*)(a.norm_g + 8 * cc + 4);
-            }
+            float4 gv0 = gv00, gv1 = gv01;
             float4 xv[4][2];
-            #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const float* xs = a.xin + (int64_t)min(s, a.n_seq - 1) * a.x_stride + 8 * cc;
-                xv[s][0] = *(const float4*)xs;
-                xv[s][1] = *(const float4*)(xs + 4);
+            if (i == 0) {
+                #pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    xv[s][0] = xv0[s][0];
+                    xv[s][1] = xv0[s][1];
+                }
+            } else {
+                if (gain) {
+                    gv0 = *(const float4*)(a.norm_g + 8 * cc);
+                    gv1 = *(const float4*)(a.norm_g + 8 * cc + 4);
+                }
+                #pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const float* xs = a.xin + (int64_t)min(s, a.n_seq - 1) * a.x_stride + 8 * cc;
+                    xv[s][0] = *(const float4*)xs;
+                    xv[s][1] = *(const float4*)(xs + 4);
+                }
             }
             #pragma unroll
             for (int s = 0; s < 4; ++s) {
@@ -923,29 +964,25 @@ __global__ __launch_bounds__(64 * kMbWaves) void k_gemv_mb(GemvArgs a) {
         }
     };
 
-    const int n_rounds = (t_end - t_begin + TW - 1) / TW;
     if (has_k) {
-        // steps i = 0 .. S-1: round i / n_k, stage k_lo + i % n_k; the next
-        // step's stage is requested before this one computes (the last
-        // step's request repeats it: clamped, so the load count is exact)
-        const int n_k = k_hi - k_lo, S = n_rounds * n_k;
-        auto issue = [&](int i, Stage& st) {
-            const int ic = min(i, S - 1);
-            const int rq = ic / n_k;
-            load(t_begin + rq * TW, k_lo + (ic - rq * n_k), st);
-        };
-        auto run = [&](int i, const Stage& st) {
+        auto run = [&](int i, const Stage& sg) {
             const int rq = i / n_k, k = k_lo + (i - rq * n_k);
-            compute(k, st);
+            compute(k, sg);
             if (k == k_hi - 1) end_round(rq, t_begin + rq * TW);
         };
-        for (int i = 0; i < S; i += 2) {
-            issue(i + 1, sb);
-            run(i, sa);
-            if (i + 1 >= S) break;
-            issue(i + 2, sa);
-            run(i + 1, sb);
+        // whole groups of D steps (no exit inside a group, so each stage
+        // keeps its registers), then the last < D steps, already requested
+        int i = 0;
+        for (; i + D <= S; i += D) {
+            #pragma unroll
+            for (int u = 0; u < D; ++u) {
+                issue(i + u + D - 1, st[(u + D - 1) % D]);
+                run(i + u, st[u]);
+            }
         }
+        #pragma unroll
+        for (int u = 0; u < D - 1; ++u)
+            if (i + u < S) run(i + u, st[u]);
     } else {
         for (int rq = 0; rq < n_rounds; ++rq) end_round(rq, t_begin + rq * TW);
     }
@@ -1222,16 +1259,23 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
         asm volatile("" ::: "memory");
     };
     // the next tile's loads are requested before this one computes (the
-    // scheduling barriers keep them there)
-    for (int ti = 0; ti < TP; ti += 2) {
-        if (ti + 1 < TP) load(t_first + ti + 1, kb, vb);
+    // scheduling barriers keep them there).  Whole pairs of tiles first (no
+    // exit inside a pair, so each buffer keeps its registers), then the last
+    // one or two.
+    int ti = 0;
+    for (; ti + 2 < TP; ti += 2) {
+        load(t_first + ti + 1, kb, vb);
         __builtin_amdgcn_sched_barrier(0);
         step(t_first + ti, ka, va);
-        if (ti + 1 >= TP) break;
-        if (ti + 2 < TP) load(t_first + ti + 2, ka, va);
+        load(t_first + ti + 2, ka, va);
         __builtin_amdgcn_sched_barrier(0);
         step(t_first + ti + 1, kb, vb);
     }
+    const bool two = ti + 1 < TP;
+    if (two) load(t_first + ti + 1, kb, vb);
+    __builtin_amdgcn_sched_barrier(0);
+    step(t_first + ti, ka, va);
+    if (two) step(t_first + ti + 1, kb, vb);
 
     // ---- the four wavefronts' states: the span's maximum per head, each
     // wavefront's o scaled to it, summed in LDS
