@@ -130,7 +130,9 @@ __global__ __launch_bounds__(NT, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a) {
     // this wavefront's steps: step0, step0 + sstride, ... ; each step is split
     // into `cps` chunks of CB blocks per lane
     const int n_steps = (N + kRowsPerStep - 1) / kRowsPerStep;
-    const int step0 = blockIdx.x * NW + wave, sstride = gridDim.x * NW;
+    // (dealt round-robin over the workgroups first, so every CU holds an equal
+    // share, within one, whatever the number of steps)
+    const int step0 = wave * (int)gridDim.x + (int)blockIdx.x, sstride = gridDim.x * NW;
     const int my_steps = step0 < n_steps ? (n_steps - 1 - step0) / sstride + 1 : 0;
     const int bpl = (nb + LPR - 1) / LPR;        // blocks per lane per row (upper bound)
     const int cps = (bpl + CB - 1) / CB;
@@ -461,19 +463,47 @@ static int device_cus() {
 #endif
 template <int EPI> constexpr int gemv_threads() { return EPI == EPI_LOGITS ? LMK_LMHEAD_NT : kGemvThreads; }
 
-template <int QT, int LPR, int EPI, int XR>
+template <int QT, int LPR, int EPI, int XR, int NT = gemv_threads<EPI>()>
 static hipError_t launch_one(const GemvArgs& a, int n_seq, int max_blocks, size_t lds, hipStream_t st) {
-    constexpr int NT = gemv_threads<EPI>();
     constexpr int rows_per_step = 2 * (64 / LPR);
     constexpr int nw = NT / 64;
     const int n_steps = (a.w.N + rows_per_step - 1) / rows_per_step;
-    const int need = (n_steps + nw - 1) / nw;
-    // Eight GEMV wavefronts per CU (measured on gfx950: more slow a long GEMV
-    // down); a longer matrix takes several row-pair rounds per wavefront.
-    int g = std::min({need, device_cus() * LMK_GEMV_WPC, max_blocks});
+    (void)nw;
+    // One workgroup per CU (NT / 64 wavefronts: eight measured best for a
+    // long GEMV on gfx950); a longer matrix takes several row-pair rounds
+    // per wavefront.
+    int g = std::min({n_steps, device_cus() * LMK_GEMV_WPC, max_blocks});
     if (g < 1) g = 1;
     hipLaunchKernelGGL((k_gemv<QT, LPR, EPI, XR, NT>), dim3(g, n_seq), dim3(NT), lds, st, a);
     return hipGetLastError();
+}
+
+// A matrix whose row-pair steps fill every CU in one round of 4 to 16
+// wavefronts takes a workgroup of exactly that many wavefronts per CU (each
+// wavefront one step, the whole matrix in flight at once); others keep eight
+// wavefronts and take several rounds.  XR covers K in one input batch where
+// it can (the prologue loops over batches otherwise).
+template <int QT, int EPI>
+static hipError_t launch_wide_rows(const GemvArgs& a, int n_seq, int max_blocks, size_t lds, hipStream_t st) {
+    const int n_steps = (a.w.N + 1) / 2;
+    const int per_cu = (n_steps + device_cus() - 1) / device_cus();
+    const int K = a.w.K;
+    if (per_cu <= 4) {
+        if (K <= 2 * 256 * 4) return launch_one<QT, 64, EPI, 2, 256>(a, n_seq, max_blocks, lds, st);
+        if (K <= 4 * 256 * 4) return launch_one<QT, 64, EPI, 4, 256>(a, n_seq, max_blocks, lds, st);
+        return launch_one<QT, 64, EPI, 8, 256>(a, n_seq, max_blocks, lds, st);
+    }
+    if (per_cu > 8 && per_cu <= 12) {
+        if (K <= 2 * 768 * 4) return launch_one<QT, 64, EPI, 2, 768>(a, n_seq, max_blocks, lds, st);
+        return launch_one<QT, 64, EPI, 4, 768>(a, n_seq, max_blocks, lds, st);
+    }
+    if (per_cu > 12 && per_cu <= 16) {
+        if (K <= 2 * 1024 * 4) return launch_one<QT, 64, EPI, 2, 1024>(a, n_seq, max_blocks, lds, st);
+        return launch_one<QT, 64, EPI, 4, 1024>(a, n_seq, max_blocks, lds, st);
+    }
+    if (K <= 2 * 512 * 4) return launch_one<QT, 64, EPI, 2>(a, n_seq, max_blocks, lds, st);
+    if (K <= 4 * 512 * 4) return launch_one<QT, 64, EPI, 4>(a, n_seq, max_blocks, lds, st);
+    return launch_one<QT, 64, EPI, 8>(a, n_seq, max_blocks, lds, st);
 }
 
 template <int QT, int EPI>
@@ -484,6 +514,7 @@ static hipError_t launch_gemv_lpr(const GemvArgs& a, int lpr, int n_seq, int max
     constexpr int NT = gemv_threads<EPI>();
     switch (lpr) {
         case 64:
+            if (EPI != EPI_LOGITS) return launch_wide_rows<QT, EPI>(a, n_seq, max_blocks, lds, st);
             if (a.w.K <= 2 * NT * 4) return launch_one<QT, 64, EPI, 2>(a, n_seq, max_blocks, lds, st);
             if (a.w.K <= 4 * NT * 4) return launch_one<QT, 64, EPI, 4>(a, n_seq, max_blocks, lds, st);
             return launch_one<QT, 64, EPI, 8>(a, n_seq, max_blocks, lds, st);
