@@ -91,7 +91,7 @@ typedef struct {
     double rms_eps;      /* RMSNorm epsilon (inside the square root) */
     double rope_theta;   /* RoPE base: pair i turns by p * theta^(-2i/hd) */
     int32_t max_ctx;     /* KV positions per sequence */
-    int32_t max_seqs;    /* sequences decoded together (1..4; 2..4 need hidden <= 8192) */
+    int32_t max_seqs;    /* sequences decoded together (1..4; 2..4 need hidden <= 6144) */
     int32_t qtype;       /* an lm_qtype, for every weight matrix (the LM head included) */
 } lm_config;
 

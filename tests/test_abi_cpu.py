@@ -60,18 +60,20 @@ def test_create_rejects_bad_config_before_any_device_call(field, value, needle):
     assert needle in msg and "expected" in msg
 
 
-def test_create_rejects_wide_hidden_for_several_sequences():
-    """2..4 sequences: the activation-digit kernel takes an RMSNorm row in one
-    workgroup pass, so hidden is at most 8192 there (one sequence: no limit)."""
+@pytest.mark.parametrize("hidden", [6176, 8192])
+def test_create_rejects_wide_hidden_for_several_sequences(hidden):
+    """2..4 sequences: each GEMV workgroup stages the digits of an
+    RMSNorm-gained input (K = hidden) in LDS, at most 6144 columns, so hidden
+    is at most 6144 there (one sequence: no limit)."""
     L = lm.load()
     d = _good()
-    d.update(hidden=8224, max_seqs=2)
+    d.update(hidden=hidden, max_seqs=2)
     c = lm.Config(**d)
     h = ctypes.c_void_p(123)
     assert L.lm_model_create(ctypes.byref(c), None, ctypes.byref(h)) == lm.LM_E_ARG
     assert not h.value
     msg = L.lm_last_error(None).decode()
-    assert "hidden" in msg and "8192" in msg
+    assert "hidden" in msg and "6144" in msg
 
 
 def test_null_arguments():

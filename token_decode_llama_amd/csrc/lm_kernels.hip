@@ -482,24 +482,29 @@ static hipError_t launch_one(const GemvArgs& a, int n_seq, int max_blocks, size_
 // wavefronts takes a workgroup of exactly that many wavefronts per CU (each
 // wavefront one step, the whole matrix in flight at once); others keep eight
 // wavefronts and take several rounds.  XR covers K in one input batch where
-// it can (the prologue loops over batches otherwise).
+// it can (the prologue loops over batches otherwise).  The 12 and 16
+// wavefront sizes only where a stage is one block per row (Q4_0's four-block
+// stages need more registers than 12 or 16 wavefronts per CU leave).
 template <int QT, int EPI>
 static hipError_t launch_wide_rows(const GemvArgs& a, int n_seq, int max_blocks, size_t lds, hipStream_t st) {
     const int n_steps = (a.w.N + 1) / 2;
     const int per_cu = (n_steps + device_cus() - 1) / device_cus();
     const int K = a.w.K;
+    constexpr bool kWide = ChunkBlocks<QT>::value == 1;
     if (per_cu <= 4) {
         if (K <= 2 * 256 * 4) return launch_one<QT, 64, EPI, 2, 256>(a, n_seq, max_blocks, lds, st);
         if (K <= 4 * 256 * 4) return launch_one<QT, 64, EPI, 4, 256>(a, n_seq, max_blocks, lds, st);
         return launch_one<QT, 64, EPI, 8, 256>(a, n_seq, max_blocks, lds, st);
     }
-    if (per_cu > 8 && per_cu <= 12) {
-        if (K <= 2 * 768 * 4) return launch_one<QT, 64, EPI, 2, 768>(a, n_seq, max_blocks, lds, st);
-        return launch_one<QT, 64, EPI, 4, 768>(a, n_seq, max_blocks, lds, st);
-    }
-    if (per_cu > 12 && per_cu <= 16) {
-        if (K <= 2 * 1024 * 4) return launch_one<QT, 64, EPI, 2, 1024>(a, n_seq, max_blocks, lds, st);
-        return launch_one<QT, 64, EPI, 4, 1024>(a, n_seq, max_blocks, lds, st);
+    if constexpr (kWide) {
+        if (per_cu > 8 && per_cu <= 12) {
+            if (K <= 2 * 768 * 4) return launch_one<QT, 64, EPI, 2, 768>(a, n_seq, max_blocks, lds, st);
+            return launch_one<QT, 64, EPI, 4, 768>(a, n_seq, max_blocks, lds, st);
+        }
+        if (per_cu > 12 && per_cu <= 16) {
+            if (K <= 2 * 1024 * 4) return launch_one<QT, 64, EPI, 2, 1024>(a, n_seq, max_blocks, lds, st);
+            return launch_one<QT, 64, EPI, 4, 1024>(a, n_seq, max_blocks, lds, st);
+        }
     }
     if (K <= 2 * 512 * 4) return launch_one<QT, 64, EPI, 2>(a, n_seq, max_blocks, lds, st);
     if (K <= 4 * 512 * 4) return launch_one<QT, 64, EPI, 4>(a, n_seq, max_blocks, lds, st);

@@ -405,8 +405,11 @@ static lm_status check_config(const lm_config* c) {
     if (c->ffn < 32 || c->ffn % 32) return bad("ffn", c->ffn, "a positive multiple of 32");
     if (c->max_ctx < 1) return bad("max_ctx", c->max_ctx, ">= 1");
     if (c->max_seqs < 1 || c->max_seqs > 4) return bad("max_seqs", c->max_seqs, "1..4");
-    if (c->max_seqs >= 2 && c->hidden > 8192)       // the activation-digit kernel takes a row in one pass
-        return bad("hidden", c->hidden, "<= 8192 when max_seqs >= 2");
+    // 2..4 sequences: an RMSNorm-gained input (QKV, gate/up, LM head: K =
+    // hidden) has its digits staged by each GEMV workgroup in LDS, at most
+    // 6144 columns (lm_kernels.hip, kMbLdsMaxK)
+    if (c->max_seqs >= 2 && c->hidden > 6144)
+        return bad("hidden", c->hidden, "<= 6144 when max_seqs >= 2");
     if (!(c->rms_eps >= 0.0) || !std::isfinite(c->rms_eps))
         return fail(nullptr, LM_E_ARG, "bad config: rms_eps = %g; expected a finite value >= 0", c->rms_eps);
     if (!(c->rope_theta > 0.0) || !std::isfinite(c->rope_theta))
