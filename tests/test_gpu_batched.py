@@ -28,9 +28,10 @@ BATCH_CASES = {
     "qwen05b_2layers_b2": (synth.variant("multi_qwen05b", n_layers=2, ctx=130, steps=3, batch=2), 2),
     "smol360m_2layers_b3": (synth.variant("multi_smol360m", n_layers=2, ctx=70, steps=3, batch=3), 3),
     # the 8B Q4_0 four-sequence workload's layer shapes at its context length
-    # (attention: two 64-position tiles per workgroup)
+    # (attention: several 64-position tiles per workgroup, partial states merged)
     "llama8b_q4_2layers_b4": (synth.variant("llama8b_q4", n_layers=2, steps=2), 4),
-    # 4 x 8 KV heads x 128 chunks: four tiles per attention workgroup (head_dim 64);
+    # 4 x 8 KV heads x 128 chunks: four tiles per attention workgroup (head_dim 64, the
+    # resident-grid choice);
     # 127 tiles (the last span has a tile past the context), then a lone key in tile 128
     "llama1b_2layers_b4_ctx8k": (synth.variant("multi_llama1b", n_layers=2, ctx=8127, steps=2, batch=4), 4),
 }
