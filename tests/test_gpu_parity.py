@@ -40,6 +40,10 @@ CASES = {
     "tiny_5layers": synth.variant("tiny", n_layers=5, steps=3),
     # an empty prefilled cache: the first token sits at position 0 and attends to itself only
     "tiny_ctx0": synth.variant("tiny", ctx=0, steps=3),
+    # down projection of 48 blocks per row: 32-lane groups per row (every other
+    # lane-group width, 8, 16 and 64, is in the shapes above), Q8_0 and Q4_0
+    "tiny_ffn1536_q8": synth.variant("tiny", ffn=1536, steps=3),
+    "tiny_ffn1536_q4": synth.variant("tiny", ffn=1536, qtype=Q4_0, steps=3),
 }
 
 _models = {}
