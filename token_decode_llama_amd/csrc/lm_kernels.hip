@@ -8,20 +8,22 @@
 // Llama features (GQA, KV cache) are listed in section 1 of the same page.
 //
 // MI355X design (CDNA4, 64-lane wavefronts, 160 KB LDS per CU):
-//  * dequant-GEMV: a wavefront owns two adjacent output rows at a time
-//    (so a RoPE pair or a gate/up pair ends in the same lanes); 64/LPR row
-//    pairs share a wavefront when K is short.  Quants arrive as coalesced
-//    16-byte loads from the repacked half-block planes; the activation vector
-//    sits in LDS in fp32, XOR-swizzled per 32-column block so lanes reading
-//    consecutive blocks hit distinct banks.  fp32 accumulation; int8 -> fp32
-//    through the SDWA sign-extending convert; partial sums reduced across
-//    lanes with cross-lane shuffles.  The RMSNorm of the input is computed
-//    by every workgroup while it stages x (prologue); RoPE + fp16 KV append,
-//    SwiGLU, residual add, or logits + argmax run in the epilogue.
-//  * attention: one workgroup per (64-position chunk, KV head, sequence)
-//    stages its K/V tile in LDS once for all query heads of the group; the
-//    last workgroup of a (sequence, KV head) to finish merges the chunks'
-//    partial softmax states (log-sum-exp) - no second launch.
+//  * one-sequence dequant-GEMV: one workgroup per CU stages the input as
+//    24-bit integer digits in LDS (its RMSNorm folded in); a wavefront owns
+//    two adjacent output rows at a time (so a RoPE pair or a gate/up pair
+//    ends in the same lanes) and its lanes split the row's blocks; quants
+//    arrive as coalesced 16-byte loads from the repacked half-block planes,
+//    v_dot4_i32_i8 gives each digit plane's exact int32 block sum, fp32
+//    accumulation, row sums by DPP moves and row/half-wave swaps.  RoPE +
+//    fp16 KV append, SwiGLU, residual add, or logits + argmax run in the
+//    epilogue.
+//  * 2-4 sequences: the same digits as the first operand of the int8 matrix
+//    core (v_mfma_i32_16x16x32_i8), the weights' fragment copy as the second.
+//  * attention: one workgroup per (span of 64-position tiles, KV head,
+//    sequence) scores all query heads of the group on the matrix cores, each
+//    wavefront keeping its own online softmax; the last workgroup of a
+//    (sequence, KV head) to finish merges the spans' partial softmax states
+//    (log-sum-exp) - no second launch.
 #include "lm_internal.h"
 #include "lm_device.h"
 
@@ -92,9 +94,10 @@ struct WChunk {
 // 8: K up to 4096, 8192 or 16384 columns in one round trip with 512 threads);
 // a template parameter so the register budget of the short-K kernels stays
 // small.
-// NT threads per workgroup: 512 (one workgroup per CU, the input staged once
-// per CU); the LM head keeps two 256-thread workgroups per CU (its staging is
-// amortised over ~30 row pairs per wavefront; measured faster so).
+// NT threads per workgroup, one workgroup per CU (the input staged once per
+// CU): 512 by default; 256, 768 or 1024 for a matrix whose row pairs fill the
+// chip in one round of that many wavefronts (launch_wide_rows); the LM head
+// 256 (about 60 row pairs per wavefront; measured faster than 512).
 template <int QT, int LPR, int EPI, int XR, int NT>
 __global__ __launch_bounds__(NT, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a) {
     constexpr int NW = NT / 64;
@@ -664,9 +667,9 @@ __global__ __launch_bounds__(kBlock) void k_xdigits(const float* __restrict__ xi
 }
 
 // Several-sequence GEMV: k_gemv_mb<QT, EPI, TW, XL>.  One workgroup of eight
-// wavefronts per CU owns a contiguous run of 16-row tiles; its wavefronts
-// split K (whole stages of kMbGroup blocks) and take the run TW tiles at a
-// time: per stage a lane loads, for each of the TW tiles, its weight
+// wavefronts per CU takes every G-th 16-row tile (G workgroups); its
+// wavefronts split K (whole stages of kMbGroup blocks) and take its tiles TW
+// at a time: per stage a lane loads, for each of the TW tiles, its weight
 // fragments (from the fragment copy: 1 KiB per wavefront, tile and fragment
 // group, contiguous) and its row's four block scales, and one activation
 // digit fragment per block that serves all TW tiles.  Two stages stay in
@@ -717,7 +720,7 @@ __global__ __launch_bounds__(64 * kMbWaves) void k_gemv_mb(GemvArgs a) {
         uint2 sc;
         uint2 x[XS];        // (digits from a.xfrag) this lane's digit fragment of each block
     };
-    // tiles t0.. t0+TW-1 of the run (clamped to its last tile), stage k.
+    // this workgroup's tiles t0.. t0+TW-1 (clamped to its last tile), stage k.
     // Every address is clamped, so a stage's loads are issued unconditionally
     // and the compiler's in-order load counters stay exact.
     auto load = [&](int t0, int k, Stage& st) {
