@@ -44,6 +44,10 @@ CASES = {
     # lane-group width, 8, 16 and 64, is in the shapes above), Q8_0 and Q4_0
     "tiny_ffn1536_q8": synth.variant("tiny", ffn=1536, steps=3),
     "tiny_ffn1536_q4": synth.variant("tiny", ffn=1536, qtype=Q4_0, steps=3),
+    # down projection of 9216 columns on 256 rows: four-wavefront workgroups,
+    # whose input batch holds 8192 columns, so its prologue takes two batches
+    "tiny_ffn9216_q8": synth.variant("tiny", ffn=9216, steps=3),
+    "tiny_ffn9216_q4": synth.variant("tiny", ffn=9216, qtype=Q4_0, steps=3),
 }
 
 _models = {}
