@@ -22,6 +22,10 @@ BATCH_CASES = {
     "tiny_q8_b2": (synth.variant("tiny", batch=2), 2),
     "tiny_q8_b3": (synth.variant("tiny", batch=3), 3),
     "tiny_q4_b4": (synth.variant("tiny", qtype=Q4_0, batch=4), 4),
+    # down projection of 5120 columns: the digits staged by each workgroup in
+    # two batches (the first requested before the weights, the second after)
+    "tiny_ffn5120_q8_b2": (synth.variant("tiny", ffn=5120, batch=2), 2),
+    "tiny_ffn5120_q4_b3": (synth.variant("tiny", ffn=5120, qtype=Q4_0, batch=3), 3),
     # vocabulary that ends inside a 16-row tile (498 = 31 * 16 + 2)
     "tiny_q8_vocab498_b2": (synth.variant("tiny", vocab=498, batch=2), 2),
     # ragged block counts (28 and 30 blocks/row), GQA groups of 7 and 3
