@@ -118,7 +118,7 @@ def kind_of(kernel: str):
     arguments (the residual GEMVs: Wo takes inputs of up to 8192 columns, the
     down projection wider ones - the 8B and 70B shapes)."""
     import re
-    m = re.search(r"k_gemv<(\d+), (\d+), (\d+), (\d+), (\d+)>", kernel)
+    m = re.search(r"k_gemv<(\d+), (\d+), (\d+), (\d+), (\d+), (?:true|false)>", kernel)
     if m:
         epi, xr = int(m.group(3)), int(m.group(4))
         return {0: "qkv", 2: "gateup", 3: "lmhead"}.get(epi, "down" if xr == 8 else "wo")
@@ -525,7 +525,7 @@ def run_single(args, name: str, n_seq: int):
                           "times between two HIP events on the model's stream")
     roofline["avg_launch_us_events_in_step"] = round(1e3 * kstats[dom][1] / max(kstats[dom][0], 1), 3)
     step_bytes = r.step_bytes(args.steps // 2)
-    # plain-read ceiling over (at most) 4 GiB of the resident layer arena
+    # read ceiling (the GEMVs' non-temporal 16-byte loads) over (at most) 4 GiB of the resident layer arena
     n_read = min(4 << 30, (cfg.weight_bytes() - cfg.vocab * synth.row_bytes(cfg.qtype, cfg.hidden)) // 16 * 16)
     read_ms = r.g.debug_read_bw(n_read, 5)
     if args.calibrate:

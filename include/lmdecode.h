@@ -369,9 +369,10 @@ lm_status lm_debug_gemv(lm_model* m, int32_t layer, int32_t which, int32_t n_seq
 void lm_debug_fail_alloc(int64_t n);
 int64_t lm_debug_alloc_count(void);
 
-/* A plain read-only kernel over n_bytes of device memory (sum of 16-byte
- * words), for calibrating HBM counters and the read ceiling; *ms = average
- * duration over iters launches. */
+/* A read-only kernel over n_bytes of device memory (sum of 16-byte words,
+ * with the non-temporal loads the GEMVs read their weights with), for
+ * calibrating HBM counters and the read ceiling; *ms = average duration over
+ * iters launches. */
 lm_status lm_debug_read_bw(lm_model* m, int64_t n_bytes, int32_t iters, double* ms);
 
 #ifdef __cplusplus

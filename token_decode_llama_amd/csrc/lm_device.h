@@ -20,9 +20,6 @@
 #ifndef LMK_CB_QK
 #define LMK_CB_QK 1     // the K formats (more registers per block: headers / high bits)
 #endif
-#ifndef LMK_WEIGHT_NT
-#define LMK_WEIGHT_NT 0     // plain loads: the measured default of the GEMV kernels
-#endif
 
 namespace lmk {
 
@@ -39,15 +36,40 @@ constexpr int kGemvThreads = LMK_GEMV_NT;
 // helpers
 // ---------------------------------------------------------------------------
 
-// 16-byte weight load (optionally with the non-temporal hint)
+// Weight loads (quants, block scales, K-format headers and high bits) carry
+// the non-temporal hint: every such byte is read once per step.  Measured
+// faster for the 8B and 70B matrices (8B Q8_0 step 1.92 -> 1.82 ms, Q4_K /
+// Q5_K 2-3 %) but slower for small ones (a 1B model's QKV 4.6 -> 5.5 us), so
+// the one-sequence Q8_0 / Q4_0 GEMV takes it only for matrices of at least
+// kStreamBytes; the KV cache made attention slower with it and keeps plain
+// loads.
 typedef int v4i_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ int4 ld16_stream(const uint8_t* p) {
-#if LMK_WEIGHT_NT
     const v4i_t v = __builtin_nontemporal_load((const v4i_t*)p);
-#else
-    const v4i_t v = *(const v4i_t*)p;
-#endif
     return make_int4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 ld16_stream(const uint4* p) {
+    const v4i_t v = __builtin_nontemporal_load((const v4i_t*)p);
+    return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+}
+typedef unsigned int u2v_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 ld8_stream(const void* p) {
+    const u2v_t v = __builtin_nontemporal_load((const u2v_t*)p);
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint32_t ld4_stream(const void* p) {
+    return __builtin_nontemporal_load((const uint32_t*)p);
+}
+constexpr int64_t kStreamBytes = 16ll << 20;   // quant bytes of a matrix that takes the hint
+// the same loads without the hint (WNT = false) or with it
+template <bool WNT> __device__ __forceinline__ int4 ld16_w(const uint8_t* p) {
+    if constexpr (WNT) return ld16_stream(p);
+    const v4i_t v = *(const v4i_t*)p;
+    return make_int4(v.x, v.y, v.z, v.w);
+}
+template <bool WNT> __device__ __forceinline__ uint32_t ld4_w(const void* p) {
+    if constexpr (WNT) return ld4_stream(p);
+    return *(const uint32_t*)p;
 }
 
 __device__ __forceinline__ float h2f(uint16_t h) {

@@ -98,7 +98,7 @@ struct WChunk {
 // CU): 512 by default; 256, 768 or 1024 for a matrix whose row pairs fill the
 // chip in one round of that many wavefronts (launch_wide_rows); the LM head
 // 256 (about 60 row pairs per wavefront; measured faster than 512).
-template <int QT, int LPR, int EPI, int XR, int NT>
+template <int QT, int LPR, int EPI, int XR, int NT, bool WNT>
 __global__ __launch_bounds__(NT, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a) {
     constexpr int NW = NT / 64;
     extern __shared__ __align__(16) float smem[];
@@ -159,22 +159,22 @@ __global__ __launch_bounds__(NT, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a) {
         for (int u = 0; u < CB; ++u) {
             const int b = li + LPR * (k * CB + u);
             const uint32_t bc = (uint32_t)min(b, nb - 1);   // unsigned 32-bit offsets: scalar base + vector offset
-            w.a0[u] = ld16_stream(q0 + bc * 16u);
-            w.a1[u] = ld16_stream(q1 + bc * 16u);
+            w.a0[u] = ld16_w<WNT>(q0 + bc * 16u);
+            w.a1[u] = ld16_w<WNT>(q1 + bc * 16u);
             if (QT == kQ8_0) {
-                w.b0[u] = ld16_stream(q0 + (uint32_t)nb * 16u + bc * 16u);
-                w.b1[u] = ld16_stream(q1 + (uint32_t)nb * 16u + bc * 16u);
+                w.b0[u] = ld16_w<WNT>(q0 + (uint32_t)nb * 16u + bc * 16u);
+                w.b1[u] = ld16_w<WNT>(q1 + (uint32_t)nb * 16u + bc * 16u);
             }
             if (QT == kQ4_K || QT == kQ5_K) {
-                w.h0[u] = *(const int4*)(s0 + (bc >> 3) * 8u);
-                w.h1[u] = *(const int4*)(s0 + (uint32_t)srow + (bc >> 3) * 8u);
+                w.h0[u] = ld16_stream((const uint8_t*)(s0 + (bc >> 3) * 8u));
+                w.h1[u] = ld16_stream((const uint8_t*)(s0 + (uint32_t)srow + (bc >> 3) * 8u));
                 if (QT == kQ5_K) {
-                    w.p0[u] = *(const uint32_t*)(q0 + (uint32_t)nb * 16u + bc * 4u);
-                    w.p1[u] = *(const uint32_t*)(q1 + (uint32_t)nb * 16u + bc * 4u);
+                    w.p0[u] = ld4_stream(q0 + (uint32_t)nb * 16u + bc * 4u);
+                    w.p1[u] = ld4_stream(q1 + (uint32_t)nb * 16u + bc * 4u);
                 }
             } else if (QT == kQ6_K) {
-                w.e0[u] = *(const uint2*)(q0 + (uint32_t)nb * 16u + bc * 8u);
-                w.e1[u] = *(const uint2*)(q1 + (uint32_t)nb * 16u + bc * 8u);
+                w.e0[u] = ld8_stream(q0 + (uint32_t)nb * 16u + bc * 8u);
+                w.e1[u] = ld8_stream(q1 + (uint32_t)nb * 16u + bc * 8u);
                 w.d0[u] = s0[bc];
                 w.d1[u] = s0[(uint32_t)srow + bc];
                 w.f0[u] = s0[(uint32_t)nb + (bc >> 3)];
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(NT, LMK_GEMV_MIN_BLOCKS) void k_gemv(GemvArgs a) {
             } else if (WChunk<QT>::kPair) {
                 // both rows' block scales in one 32-bit load; consumed only in compute():
                 // consuming a load here would wait on every load issued before it
-                w.dd[u] = *(const uint32_t*)(s0 + bc * 2u);
+                w.dd[u] = ld4_w<WNT>(s0 + bc * 2u);
             } else {
                 w.d0[u] = s0[bc];
                 w.d1[u] = s0[(uint32_t)srow + bc];
@@ -477,7 +477,15 @@ static hipError_t launch_one(const GemvArgs& a, int n_seq, int max_blocks, size_
     // per wavefront.
     int g = std::min({n_steps, device_cus() * LMK_GEMV_WPC, max_blocks});
     if (g < 1) g = 1;
-    hipLaunchKernelGGL((k_gemv<QT, LPR, EPI, XR, NT>), dim3(g, n_seq), dim3(NT), lds, st, a);
+    // the non-temporal hint for large matrices only (lm_device.h); the K
+    // formats take it at every size
+    if constexpr (QT == kQ8_0 || QT == kQ4_0) {
+        if ((int64_t)a.w.N * qmat_qbytes(QT, 1, a.w.K) < kStreamBytes) {
+            hipLaunchKernelGGL((k_gemv<QT, LPR, EPI, XR, NT, false>), dim3(g, n_seq), dim3(NT), lds, st, a);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((k_gemv<QT, LPR, EPI, XR, NT, true>), dim3(g, n_seq), dim3(NT), lds, st, a);
     return hipGetLastError();
 }
 
@@ -729,11 +737,11 @@ __global__ __launch_bounds__(64 * kMbWaves) void k_gemv_mb(GemvArgs a) {
             const int tile = tile_at(min(t0 + t, t_end - 1));
             const uint4* qf = (const uint4*)a.w.qf + (int64_t)tile * ngrp * 64 + lane;
             #pragma unroll
-            for (int f = 0; f < NF; ++f) st.w[t][f] = qf[(int64_t)min(k * NF + f, ngrp - 1) * 64];
+            for (int f = 0; f < NF; ++f) st.w[t][f] = ld16_stream(qf + (int64_t)min(k * NF + f, ngrp - 1) * 64);
         }
         {
             const int tile = tile_at(min(t0 + (TW == 1 ? 0 : (lane >> 4) % TW), t_end - 1));
-            st.sc = *(const uint2*)(a.w.sct + (((int64_t)tile * ng4 + k) * 16 + j) * 4);
+            st.sc = ld8_stream(a.w.sct + (((int64_t)tile * ng4 + k) * 16 + j) * 4);
         }
         if constexpr (!XL) {
             #pragma unroll
@@ -1523,7 +1531,7 @@ __global__ __launch_bounds__(kBlock) void k_read_bw(const uint4* __restrict__ bu
     uint32_t acc = 0;
     const int64_t stride = (int64_t)gridDim.x * kBlock;
     for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n16; i += stride) {
-        const uint4 v = buf[i];
+        const uint4 v = ld16_stream(buf + i);     // the loads the GEMVs stream their weights with
         acc ^= v.x ^ v.y ^ v.z ^ v.w;
     }
     acc = (uint32_t)wave_sum((float)(acc & 0xFFFF));
