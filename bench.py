@@ -122,7 +122,7 @@ def kind_of(kernel: str):
     if m:
         epi, xr = int(m.group(3)), int(m.group(4))
         return {0: "qkv", 2: "gateup", 3: "lmhead"}.get(epi, "down" if xr == 8 else "wo")
-    m = re.search(r"k_gemv_mb<(\d+), (\d+), (\d+), (true|false)>", kernel)
+    m = re.search(r"k_gemv_mb<(\d+), (\d+), (\d+), (true|false), (?:true|false)>", kernel)
     if m:
         epi, xl = int(m.group(2)), m.group(4) == "true"
         return {0: "qkv", 2: "gateup", 3: "lmhead"}.get(epi, "wo" if xl else "down")

@@ -26,6 +26,12 @@ BATCH_CASES = {
     # two batches (the first requested before the weights, the second after)
     "tiny_ffn5120_q8_b2": (synth.variant("tiny", ffn=5120, batch=2), 2),
     "tiny_ffn5120_q4_b3": (synth.variant("tiny", ffn=5120, qtype=Q4_0, batch=3), 3),
+    # down projection of 6400 columns, wider than a workgroup's prologue digits:
+    # the gate/up kernel writes h's digits in its epilogue, four consecutive
+    # tiles (one 32-column block of h) per round, 200 blocks (fewer than the
+    # CUs); an empty sequence slot at three sequences
+    "tiny_ffn6400_q8_b3": (synth.variant("tiny", ffn=6400, batch=3), 3),
+    "tiny_ffn6400_q4_b2": (synth.variant("tiny", ffn=6400, qtype=Q4_0, batch=2), 2),
     # vocabulary that ends inside a 16-row tile (498 = 31 * 16 + 2)
     "tiny_q8_vocab498_b2": (synth.variant("tiny", vocab=498, batch=2), 2),
     # ragged block counts (28 and 30 blocks/row), GQA groups of 7 and 3

@@ -129,6 +129,8 @@ struct GemvArgs {
     // several sequences at once (MFMA path)
     int n_seq;
     uint8_t* xfrag;        // activation digits, scales and digit sums (xfrag_bytes; lm_kernels.hip)
+    int xfrag_ready;       // wide-input GEMV: xfrag already holds this input's digits (written by
+                           // the gate/up kernel's epilogue), so no digit kernel runs first
 };
 
 struct AttnArgs {
@@ -154,6 +156,10 @@ hipError_t launch_gemv(const GemvArgs& a, int epi, int n_seq, int max_blocks, hi
 // 2..4 sequences: the matrix-core GEMV (its activation digits computed in each
 // workgroup's prologue, or for wide inputs by a digit kernel into a.xfrag first)
 hipError_t launch_gemv_batched(const GemvArgs& a, int epi, int n_seq, int max_blocks, hipStream_t st);
+// The several-sequence gate/up GEMV of an FFN of width ffn writes the digits
+// of its output h into a.xfrag itself (the down projection then sets
+// xfrag_ready) when h is too wide for the down GEMV's own prologue.
+bool gateup_writes_digits(int64_t ffn);
 // Activation operands of the several-sequence GEMV for nb = K/32 blocks:
 // digits uint2 [nb][4 column groups][16 rows 4s+d], then activation scales
 // fp32 [nb][4 sequences], then digit sums int4 [nb][4 sequences].

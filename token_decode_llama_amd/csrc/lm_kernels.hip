@@ -598,6 +598,8 @@ constexpr int kMbWaves = 8;        // wavefronts per workgroup (one workgroup pe
 constexpr int kMbGroup = 4;        // blocks per pipeline stage (whole fragments of both formats)
 constexpr int kMbLdsMaxK = 6144;   // widest input whose digits a workgroup computes into LDS
 
+bool gateup_writes_digits(int64_t ffn) { return ffn > kMbLdsMaxK && ffn % 32 == 0; }
+
 // The digits of 8 consecutive inputs v (a quarter of a 32-column block; the
 // block's four quarters sit in lanes 4k..4k+3 of one wavefront): the three
 // digit planes packed 8 bytes each, the block's digit sums t[d] (over all 32
@@ -689,7 +691,7 @@ __global__ __launch_bounds__(kBlock) void k_xdigits(const float* __restrict__ xi
 // prologue (K <= kMbLdsMaxK), while its first stage is in flight, from x
 // (times the gain for RMSNorm inputs; the RMS factor of each sequence then
 // scales the finished dot products); else they come from a.xfrag (k_xdigits).
-template <int QT, int EPI, int TW, bool XL>
+template <int QT, int EPI, int TW, bool XL, bool DG>
 __global__ __launch_bounds__(64 * kMbWaves) void k_gemv_mb(GemvArgs a) {
     constexpr int NT = 64 * kMbWaves;
     extern __shared__ __align__(16) uint8_t mb_lds[];
@@ -698,6 +700,7 @@ __global__ __launch_bounds__(64 * kMbWaves) void k_gemv_mb(GemvArgs a) {
     __shared__ float wv_best[kMbWaves][4];
     __shared__ int wi_best[kMbWaves][4];
     __shared__ int s_last;
+    __shared__ float h_blk[DG ? 4 : 1][32];   // DG: a round's SwiGLU outputs, per sequence
 
     const int K = a.w.K, N = a.w.N, nb = K >> 5;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -706,10 +709,15 @@ __global__ __launch_bounds__(64 * kMbWaves) void k_gemv_mb(GemvArgs a) {
     const int n_tiles = (N + 15) >> 4;
     const int G = gridDim.x;
     // this workgroup's tiles: blockIdx.x + G i for i = 0 .. t_end-1, so that at
-    // any time the workgroups read neighbouring tiles (one window of the matrix)
+    // any time the workgroups read neighbouring tiles (one window of the matrix).
+    // DG (gate/up whose output feeds a wide-input GEMV): groups of four
+    // consecutive tiles instead, group blockIdx.x + G r in round r, so that a
+    // round's outputs are one whole 32-column block of h (N % 64 == 0)
+    static_assert(!DG || (EPI == EPI_SWIGLU && TW == 4 && XL), "digits from the gate/up rounds");
     const int t_begin = 0;
-    const int t_end = ((int)blockIdx.x < n_tiles) ? (n_tiles - 1 - (int)blockIdx.x) / G + 1 : 0;
-    auto tile_at = [&](int i) { return (int)blockIdx.x + G * i; };
+    const int n_units = DG ? n_tiles >> 2 : n_tiles;
+    const int t_end = ((int)blockIdx.x < n_units ? (n_units - 1 - (int)blockIdx.x) / G + 1 : 0) * (DG ? 4 : 1);
+    auto tile_at = [&](int i) { return DG ? 4 * ((int)blockIdx.x + G * (i >> 2)) + (i & 3) : (int)blockIdx.x + G * i; };
     const int ng4 = (nb + kMbGroup - 1) / kMbGroup;
     const int k_lo = wave * ng4 / kMbWaves, k_hi = (wave + 1) * ng4 / kMbWaves;
     constexpr int PER = QT == kQ8_0 ? 2 : 4;         // blocks per 16-byte weight fragment
@@ -997,6 +1005,7 @@ __global__ __launch_bounds__(64 * kMbWaves) void k_gemv_mb(GemvArgs a) {
                 } else if (EPI == EPI_SWIGLU) {
                     const float sg = y0 / (1.0f + __expf(-y0));
                     a.out[(int64_t)s * a.out_stride + (r0 >> 1)] = sg * y1;
+                    if (DG) h_blk[s][8 * wave + (j >> 1)] = sg * y1;
                 } else {  // EPI_LOGITS: the vocabulary may end inside a tile or a pair
                     if (r0 < N) {
                         if (a.out) a.out[(int64_t)s * a.out_stride + r0] = y0;
@@ -1007,6 +1016,26 @@ __global__ __launch_bounds__(64 * kMbWaves) void k_gemv_mb(GemvArgs a) {
                         better(best_v, best_i, y1, r0 + 1);
                     }
                 }
+            }
+        }
+        if constexpr (DG) {
+            // the round's 32 outputs of every sequence are h's block
+            // t0 / 4 + ... (its group): its digits for the wide GEMV that reads
+            // h next, as k_xdigits would compute them from the same fp32
+            // values (sequence slots past n_seq get zeros).  Round rq + 1
+            // writes h_blk only after its own first barrier, which the
+            // digit lanes reach after these reads.
+            __syncthreads();
+            if (tid < 16) {
+                const int sq = tid >> 2, qd = tid & 3;        // sequence slot, 8-column quarter
+                float v[8];
+                #pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = sq < a.n_seq ? h_blk[sq][8 * qd + e] : 0.f;
+                uint2 w[3];
+                int tq[3];
+                const float m = block_digits(v, w, tq);
+                const int blk = tile_at(t0) >> 2;
+                put_digits(a.xfrag, N >> 6, sq, 4 * blk + qd, w, tq, m);
             }
         }
     };
@@ -1081,10 +1110,10 @@ __global__ __launch_bounds__(64 * kMbWaves) void k_gemv_mb(GemvArgs a) {
     }
 }
 
-template <int QT, int EPI, int TW, bool XL>
+template <int QT, int EPI, int TW, bool XL, bool DG = false>
 static hipError_t launch_mb(const GemvArgs& a, int max_blocks, hipStream_t st) {
     const int n_tiles = (a.w.N + 15) / 16, nb = a.w.K / 32;
-    if (!XL) {
+    if (!XL && !a.xfrag_ready) {
         hipLaunchKernelGGL(k_xdigits, dim3((a.w.K / 8 + kBlock - 1) / kBlock, 4), dim3(kBlock), 0, st, a.xin,
                            a.x_stride, a.w.K, a.n_seq, a.xfrag);
         const hipError_t e = hipGetLastError();
@@ -1092,8 +1121,8 @@ static hipError_t launch_mb(const GemvArgs& a, int max_blocks, hipStream_t st) {
     }
     // XL: digits, scales, sums; else scales and sums
     const size_t lds = XL ? (size_t)mb_sums_offset(nb) + (size_t)nb * 64 : (size_t)nb * 80;
-    const int grid = std::max(1, std::min({n_tiles, device_cus(), max_blocks}));
-    hipLaunchKernelGGL((k_gemv_mb<QT, EPI, TW, XL>), dim3(grid), dim3(64 * kMbWaves), lds, st, a);
+    const int grid = std::max(1, std::min({DG ? n_tiles / 4 : n_tiles, device_cus(), max_blocks}));
+    hipLaunchKernelGGL((k_gemv_mb<QT, EPI, TW, XL, DG>), dim3(grid), dim3(64 * kMbWaves), lds, st, a);
     return hipGetLastError();
 }
 
@@ -1109,6 +1138,10 @@ static hipError_t launch_mb_shape(const GemvArgs& a, int max_blocks, hipStream_t
         if (per >= 2) return launch_mb<QT, EPI, 2, false>(a, max_blocks, st);
         return launch_mb<QT, EPI, 1, false>(a, max_blocks, st);
     }
+    // gate/up whose output h is wider than the prologue digits: its rounds
+    // write h's digits for the down projection (k_xdigits not launched)
+    if constexpr (EPI == EPI_SWIGLU)
+        if (gateup_writes_digits(a.w.N / 2)) return launch_mb<QT, EPI, 4, true, true>(a, max_blocks, st);
     if (per >= 4) return launch_mb<QT, EPI, 4, true>(a, max_blocks, st);
     if (per >= 2) return launch_mb<QT, EPI, 2, true>(a, max_blocks, st);
     return launch_mb<QT, EPI, 1, true>(a, max_blocks, st);

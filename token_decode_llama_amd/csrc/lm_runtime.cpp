@@ -1232,6 +1232,7 @@ static lm_status enqueue_step(lm_model* m, int n_seq, const int* d_tok, float* d
             a.w = mat_at(m, blob, M_DOWN);
             a.xin = m->sb.h; a.x_stride = (int)m->F;
             a.out = m->sb.x; a.out_stride = (int)m->H;
+            a.xfrag_ready = n_seq >= 2 && gateup_writes_digits(m->F);   // h's digits came with h
             if (want(m, LM_K_DOWN)) HIPTRY(m, gemv(m, a, EPI_RESID, n_seq, st));
         }
         if (m->sim_on) HIPTRY(m, launch_layer_cos(m->d_xin, m->sb.x, (int)m->H, n_seq, m->d_sim + 2 * l, st));
