@@ -1186,9 +1186,9 @@ hipError_t launch_gemv_batched(const GemvArgs& a0, int epi, int n_seq, int max_b
 //     4(l/16)..+3 of head l%16: the layout of the probabilities as the first
 //     operand of the next product, so they never leave the lane;
 //   o[head][d] += sum_key p[head][key] V[key][d]: the wavefront's 16 V rows
-//     pass through its own LDS rows (read back by columns; rows past the
-//     context written as zeros, so a probability of 0 never meets a stale
-//     cache value), p as fp16 hi + lo.
+//     pass through its own LDS rows (loaded as whole 128-byte lines, read
+//     back by columns; rows past the context written as zeros, so a
+//     probability of 0 never meets a stale cache value), p as fp16 hi + lo.
 // At the end of the span the four wavefronts' states (maximum, sum, o) are
 // combined in LDS.  A context that fits one span writes o directly;
 // otherwise each span publishes its softmax state (m, l, o) with device-
@@ -1228,14 +1228,21 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
     typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
     const int TP = a.tiles;                     // tiles of this workgroup's span
     const int t_first = chunk * TP;
-    // this lane's K and V row of tile t: key 64t + 16 wave + lr, pieces 4u + lq
+    // tile t's K and V pieces of this lane.  K: key 64t + 16 wave + lr,
+    // pieces 4u + lq (the matrix-op operand layout).  V, which passes through
+    // LDS: whole 128-byte lines per load instruction (eight rows: row
+    // vrow_of(u), dimensions 64 (u % (HD / 64)) + 8 (lane % 8) .. +7), with the
+    // non-temporal hint (the hint helps only whole-line requests; K keeps
+    // plain loads)
+    auto vrow_of = [&](int u) { return 8 * (u / (HD / 64)) + (lane >> 3); };
+    auto vcol_of = [&](int u) { return 64 * (u % (HD / 64)) + 8 * (lane & 7); };
     auto load = [&](int t, u32x4 (&kr)[KL], u32x4 (&vr)[KL]) {
         const int64_t row = min(t * CH + 16 * wave + lr, a.max_ctx - 1);
         #pragma unroll
         for (int u = 0; u < KL; ++u) {
-            const int64_t off = row * HD + 8 * (4 * u + lq);
-            kr[u] = *(const u32x4*)(Kg + off);
-            vr[u] = *(const u32x4*)(Vg + off);
+            kr[u] = *(const u32x4*)(Kg + row * HD + 8 * (4 * u + lq));
+            const int64_t vrow = min(t * CH + 16 * wave + vrow_of(u), a.max_ctx - 1);
+            vr[u] = __builtin_nontemporal_load((const u32x4*)(Vg + vrow * HD + vcol_of(u)));
         }
     };
     // this lane's q operands: head lr (zero past G), at step k the dimensions
@@ -1285,10 +1292,11 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
             sl = __builtin_amdgcn_mfma_f32_16x16x16f16(kk, ql[k], sl, 0, 0, 0);
         }
         // this wavefront's V rows into its LDS rows (past the context: zeros)
-        const bool vlive = tile * CH + 16 * wave + lr < n_ctx;
         #pragma unroll
-        for (int u = 0; u < KL; ++u)
-            *(u32x4*)&Vw[wave][lr][8 * (4 * u + lq)] = vlive ? vr[u] : u32x4{0u, 0u, 0u, 0u};
+        for (int u = 0; u < KL; ++u) {
+            const bool vlive = tile * CH + 16 * wave + vrow_of(u) < n_ctx;
+            *(u32x4*)&Vw[wave][vrow_of(u)][vcol_of(u)] = vlive ? vr[u] : u32x4{0u, 0u, 0u, 0u};
+        }
         // online softmax of head lr over this wavefront's keys
         const int key0 = tile * CH + 16 * wave + 4 * lq;
         float sv[4], mt = -FLT_MAX;
